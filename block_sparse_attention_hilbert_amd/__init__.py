@@ -1,0 +1,265 @@
+"""Python binding of libsparse_attn.so: block-sparse video attention on MI355X.
+
+Argument marshalling only.  Every step of the path (pooling, scoring,
+selection, CSR construction, attention, Hilbert reordering) runs in the HIP
+kernels of the C library; PyTorch provides device memory and the current
+stream.  The functions mirror the C ABI in ``include/sparse_attn.h``:
+
+* :func:`hilbert_perm_build` -- host Hilbert order of a latent grid
+* :func:`hilbert_permute`, :func:`hilbert_unpermute` -- token reordering
+* :func:`select` -- ``sparse_attn_select``: keep lists as CSR
+* :func:`fwd` -- ``sparse_attn_fwd``: block-sparse attention (+ compensation)
+* :func:`workspace_size`
+
+If the shared library is missing the import fails loudly; there is no
+fallback implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from dataclasses import dataclass
+from typing import Optional, Sequence
+
+import numpy as np
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libsparse_attn.so")
+
+SA_OK, SA_ERR_INVALID_ARG, SA_ERR_UNSUPPORTED, SA_ERR_WORKSPACE, SA_ERR_HIP = range(5)
+SA_RULE_NONE, SA_RULE_TOPK, SA_RULE_MASS = range(3)
+RULES = {"none": SA_RULE_NONE, "topk": SA_RULE_TOPK, "mass": SA_RULE_MASS}
+
+EXPORTS = ("sparse_attn_workspace_size", "hilbert_perm_build", "hilbert_permute",
+           "hilbert_unpermute", "sparse_attn_select", "sparse_attn_fwd",
+           "sparse_attn_last_error")
+
+
+class SaProblem(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("H", ctypes.c_int32), ("N", ctypes.c_int32),
+                ("d", ctypes.c_int32), ("T", ctypes.c_int32), ("Hg", ctypes.c_int32),
+                ("W", ctypes.c_int32), ("block", ctypes.c_int32), ("scale", ctypes.c_float)]
+
+
+class SaSelectSpec(ctypes.Structure):
+    _fields_ = [("rule", ctypes.c_int32), ("sub_block", ctypes.c_int32),
+                ("topk", ctypes.POINTER(ctypes.c_int32)),
+                ("density", ctypes.POINTER(ctypes.c_float)),
+                ("mass", ctypes.c_float), ("diag", ctypes.c_int32),
+                ("window_frames", ctypes.c_int32), ("n_anchors", ctypes.c_int32),
+                ("anchor_offset", ctypes.c_int64), ("want_comp", ctypes.c_int32)]
+
+
+class SparseAttnError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"sparse_attn status {status}: {msg}")
+        self.status = status
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run "
+                          "`python -m block_sparse_attention_hilbert_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, sz = ctypes.c_void_p, ctypes.c_size_t
+    P = ctypes.POINTER
+    lib.sparse_attn_workspace_size.argtypes = [P(SaProblem), P(SaSelectSpec), P(sz)]
+    lib.hilbert_perm_build.argtypes = [ctypes.c_int32] * 3 + [vp, vp]
+    lib.hilbert_permute.argtypes = [P(SaProblem), vp, vp, vp, vp]
+    lib.hilbert_unpermute.argtypes = [P(SaProblem), vp, vp, vp, vp]
+    lib.sparse_attn_select.argtypes = [P(SaProblem), P(SaSelectSpec), vp, vp, vp, vp, vp, vp,
+                                       vp, vp, vp, sz, vp]
+    lib.sparse_attn_fwd.argtypes = [P(SaProblem), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    for name in EXPORTS[:-1]:
+        getattr(lib, name).restype = ctypes.c_int
+    lib.sparse_attn_last_error.argtypes = []
+    lib.sparse_attn_last_error.restype = ctypes.c_char_p
+    return lib
+
+
+lib = _load()
+
+
+def _check(status: int):
+    if status != SA_OK:
+        raise SparseAttnError(status, lib.sparse_attn_last_error().decode())
+
+
+@dataclass
+class Problem:
+    B: int
+    H: int
+    N: int
+    d: int
+    T: int
+    Hg: int
+    W: int
+    block: int
+    scale: float = 0.0
+
+    @property
+    def nb(self) -> int:
+        return -(-self.N // self.block)
+
+    @property
+    def rows(self) -> int:
+        return self.B * self.H * self.nb
+
+    def c(self) -> SaProblem:
+        return SaProblem(self.B, self.H, self.N, self.d, self.T, self.Hg, self.W, self.block,
+                         self.scale)
+
+
+@dataclass
+class SelectSpec:
+    rule: str = "topk"
+    sub_block: int = 0
+    topk: Optional[Sequence[int]] = None
+    density: Optional[Sequence[float]] = None
+    mass: float = 0.9
+    diag: bool = False
+    window_frames: int = -1
+    n_anchors: int = 0
+    anchor_offset: int = 0
+    want_comp: bool = False
+
+    def c(self):
+        """ctypes struct plus the host arrays it points to (kept alive by the caller)."""
+        keep = []
+        topk = density = None
+        if self.topk is not None:
+            arr = np.ascontiguousarray(self.topk, dtype=np.int32)
+            keep.append(arr)
+            topk = arr.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+        if self.density is not None:
+            arr = np.ascontiguousarray(self.density, dtype=np.float32)
+            keep.append(arr)
+            density = arr.ctypes.data_as(ctypes.POINTER(ctypes.c_float))
+        s = SaSelectSpec(RULES[self.rule], self.sub_block, topk, density, self.mass,
+                         int(self.diag), self.window_frames, self.n_anchors,
+                         int(self.anchor_offset), int(self.want_comp))
+        return s, keep
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def workspace_size(prob: Problem, spec: Optional[SelectSpec] = None) -> int:
+    n = ctypes.c_size_t(0)
+    if spec is None:
+        _check(lib.sparse_attn_workspace_size(ctypes.byref(prob.c()), None, ctypes.byref(n)))
+    else:
+        cs, keep = spec.c()
+        _check(lib.sparse_attn_workspace_size(ctypes.byref(prob.c()), ctypes.byref(cs),
+                                              ctypes.byref(n)))
+    return int(n.value)
+
+
+def alloc_workspace(nbytes: int, device) -> Optional[torch.Tensor]:
+    """A 256-byte aligned device buffer (torch's caching allocator aligns to 512)."""
+    if nbytes == 0:
+        return None
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+def hilbert_perm_build(T: int, Hg: int, W: int):
+    """(perm, inv) int32 numpy arrays of the 3D Hilbert order of a T x Hg x W grid."""
+    N = T * Hg * W
+    perm = np.empty(N, np.int32)
+    inv = np.empty(N, np.int32)
+    _check(lib.hilbert_perm_build(T, Hg, W, perm.ctypes.data, inv.ctypes.data))
+    return perm, inv
+
+
+def hilbert_permute(prob: Problem, src: torch.Tensor, perm_dev: torch.Tensor,
+                    dst: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    dst = torch.empty_like(src) if dst is None else dst
+    _check(lib.hilbert_permute(ctypes.byref(prob.c()), _ptr(src), _ptr(dst), _ptr(perm_dev),
+                               _stream(stream)))
+    return dst
+
+
+def hilbert_unpermute(prob: Problem, src: torch.Tensor, perm_dev: torch.Tensor,
+                      dst: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    dst = torch.empty_like(src) if dst is None else dst
+    _check(lib.hilbert_unpermute(ctypes.byref(prob.c()), _ptr(src), _ptr(dst), _ptr(perm_dev),
+                                 _stream(stream)))
+    return dst
+
+
+@dataclass
+class Selection:
+    row_ptr: torch.Tensor
+    col_idx: torch.Tensor
+    scores: Optional[torch.Tensor] = None
+    k_mean: Optional[torch.Tensor] = None
+    v_sum: Optional[torch.Tensor] = None
+
+
+def select(prob: Problem, spec: SelectSpec, Q: torch.Tensor, K: torch.Tensor,
+           V: Optional[torch.Tensor] = None, *, want_scores: bool = False,
+           out: Optional[Selection] = None, workspace: Optional[torch.Tensor] = None,
+           stream=None) -> Selection:
+    """sparse_attn_select.  Output buffers are allocated unless ``out`` is given."""
+    dev = (Q if Q is not None else K).device
+    nb, rows = prob.nb, prob.rows
+    if out is None:
+        out = Selection(torch.empty(rows + 1, dtype=torch.int32, device=dev),
+                        torch.empty(rows * nb, dtype=torch.int32, device=dev))
+        if want_scores:
+            out.scores = torch.empty(rows * nb, dtype=torch.float32, device=dev)
+        if spec.want_comp:
+            out.k_mean = torch.empty(prob.B, prob.H, nb, prob.d, dtype=torch.float32, device=dev)
+            out.v_sum = torch.empty_like(out.k_mean)
+    if workspace is None:
+        workspace = alloc_workspace(workspace_size(prob, spec), dev)
+    cs, keep = spec.c()
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.sparse_attn_select(ctypes.byref(prob.c()), ctypes.byref(cs), _ptr(Q), _ptr(K),
+                                  _ptr(V), _ptr(out.row_ptr), _ptr(out.col_idx),
+                                  _ptr(out.scores), _ptr(out.k_mean), _ptr(out.v_sum),
+                                  _ptr(workspace), ws_bytes, _stream(stream)))
+    return out
+
+
+def fwd(prob: Problem, Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor,
+        row_ptr: torch.Tensor, col_idx: torch.Tensor, k_mean: Optional[torch.Tensor] = None,
+        v_sum: Optional[torch.Tensor] = None, *, O: Optional[torch.Tensor] = None,
+        lse: Optional[torch.Tensor] = None, want_lse: bool = False,
+        workspace: Optional[torch.Tensor] = None, stream=None):
+    """sparse_attn_fwd.  Returns O (and lse when requested or given)."""
+    O = torch.empty_like(Q) if O is None else O
+    if want_lse and lse is None:
+        lse = torch.empty(prob.B, prob.H, prob.N, dtype=torch.float32, device=Q.device)
+    if k_mean is not None and workspace is None:
+        workspace = alloc_workspace(workspace_size(prob, None), Q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.sparse_attn_fwd(ctypes.byref(prob.c()), _ptr(Q), _ptr(K), _ptr(V), _ptr(row_ptr),
+                               _ptr(col_idx), _ptr(k_mean), _ptr(v_sum), _ptr(O), _ptr(lse),
+                               _ptr(workspace), ws_bytes, _stream(stream)))
+    return (O, lse) if lse is not None else O
+
+
+def problem_for(wl, scale: float = 0.0) -> Problem:
+    """Problem statement of a workload description (duck-typed: B, H, N, d, T, Hg, W, block)."""
+    return Problem(wl.B, wl.H, wl.N, wl.d, wl.T, wl.Hg, wl.W, wl.block, scale)
+
+
+def spec_for(wl, anchor_offset: int = 0) -> SelectSpec:
+    """Selection spec of a workload description."""
+    dens = wl.densities()
+    topk = wl.topks()
+    return SelectSpec(rule=wl.rule, sub_block=wl.sub_block,
+                      topk=None if topk is None else list(topk),
+                      density=None if dens is None or topk is not None else list(dens),
+                      mass=wl.mass, diag=wl.diag, window_frames=wl.window_frames,
+                      n_anchors=wl.n_anchors, anchor_offset=anchor_offset,
+                      want_comp=wl.comp)

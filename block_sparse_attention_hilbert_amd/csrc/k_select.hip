@@ -1,0 +1,525 @@
+// Block selection kernels for gfx950 (wave64).
+//
+//   k_pool    block / sub-block means of Q and K, block means of K and block
+//             sums of V (DFSAttn page, trick 2: a block is summarised by its
+//             mean; SVG-EAR page, section 2A: the centroid of a skipped block).
+//             HBM-bound: one pass over the tensors with 16-byte loads staged
+//             through LDS; sums are exact in fp64, so any reduction order gives
+//             the same fp32 result.
+//   k_score   pooled scores S[i,j] = fl32(scale * dot(qbar_i, kbar_j)), the dot
+//             a sequential fp32 FMA chain over the channels (one lane per block
+//             pair, so the chain order is fixed); with sub-blocks the score is
+//             the max over the sub-block pairs (DFSAttn page, trick 2).
+//   k_select  one workgroup per query block: LDS bitonic sort by (score desc,
+//             index asc), top-k or cumulative-mass cut (SVG-EAR page, sections
+//             2B and 4; SVOO page, section 2A), union with the diagonal, the
+//             temporal window and the rotating anchors (LVSA abstract); writes
+//             a kept-block bitmap and count.
+//   k_scan    exclusive scan of the counts -> CSR row pointers.
+//   k_expand  bitmap -> ascending column indices.
+#include <math.h>
+
+#include "sa_internal.h"
+
+namespace sa {
+namespace {
+
+constexpr int kThreads = 256;
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+    return __uint_as_float((uint32_t)b << 16);
+}
+
+// ----------------------------------------------------------------------------
+// k_pool
+// ----------------------------------------------------------------------------
+// role 0: Q -> unit means qm            (unit = sub_block or block)
+// role 1: K -> unit means km, and block means k_mean when k_mean != nullptr
+// role 2: V -> block sums v_sum
+struct PoolArgs {
+    const uint16_t* src[3];
+    float* unit_out[3];      // [BH][n_units][D] or nullptr
+    float* block_out[3];     // [BH][nb][D] or nullptr
+    int32_t roles[3];
+    int32_t N, nb, unit, n_units;
+};
+
+template <int D, int BLK>
+__global__ __launch_bounds__(kThreads) void k_pool(PoolArgs a) {
+    constexpr int CH = D / 8;             // 16-byte chunks per row
+    constexpr int SEG = 16;               // rows per partial sum
+    constexpr int NSEG = BLK / SEG;
+    __shared__ uint4 tile[BLK * CH];      // BLK x D bf16
+    __shared__ double seg[NSEG][D];
+
+    const int blk = blockIdx.x;
+    const int64_t bh = blockIdx.y;
+    const int role = a.roles[blockIdx.z];
+    const int tid = threadIdx.x;
+    const int row0 = blk * BLK;
+    const int n = min(BLK, a.N - row0);
+    const uint4* src = reinterpret_cast<const uint4*>(a.src[role] + (bh * a.N + row0) * D);
+
+    for (int c = tid; c < n * CH; c += kThreads) tile[c] = src[c];
+    __syncthreads();
+
+    // partial sums over 16-row segments (exact in fp64)
+    const uint16_t* t16 = reinterpret_cast<const uint16_t*>(tile);
+    const int nseg = (n + SEG - 1) / SEG;
+    for (int p = tid; p < nseg * D; p += kThreads) {
+        const int s = p / D, c = p % D;
+        const int r1 = min(n, (s + 1) * SEG);
+        double acc = 0.0;
+        for (int r = s * SEG; r < r1; ++r) acc += (double)bf16_to_f32(t16[r * D + c]);
+        seg[s][c] = acc;
+    }
+    __syncthreads();
+
+    float* uo = a.unit_out[role];
+    if (uo) {
+        const int spb = BLK / a.unit;
+        const int segs_per_unit = a.unit / SEG;
+        const int nunit = (n + a.unit - 1) / a.unit;
+        for (int p = tid; p < nunit * D; p += kThreads) {
+            const int u = p / D, c = p % D;
+            double acc = 0.0;
+            for (int s = u * segs_per_unit; s < min(nseg, (u + 1) * segs_per_unit); ++s)
+                acc += seg[s][c];
+            const int cnt = min(a.unit, n - u * a.unit);
+            uo[((int64_t)bh * a.n_units + (int64_t)blk * spb + u) * D + c] =
+                (float)(acc / (double)cnt);
+        }
+    }
+    float* bo = a.block_out[role];
+    if (bo) {
+        for (int c = tid; c < D; c += kThreads) {
+            double acc = 0.0;
+            for (int s = 0; s < nseg; ++s) acc += seg[s][c];
+            const float v = role == 2 ? (float)acc : (float)(acc / (double)n);
+            bo[((int64_t)bh * a.nb + blk) * D + c] = v;
+        }
+    }
+}
+
+// ----------------------------------------------------------------------------
+// k_score
+// ----------------------------------------------------------------------------
+constexpr int kTile = 16;   // 16 x 16 block pairs per workgroup
+
+template <int D, int SPB>
+__global__ __launch_bounds__(kThreads) void k_score(const float* __restrict__ qm,
+                                                    const float* __restrict__ km,
+                                                    float* __restrict__ S, int nb,
+                                                    int n_units, float scale) {
+    constexpr int ROW = SPB * D + 4;      // floats per block row in LDS (+4: bank shift)
+    extern __shared__ float lds[];
+    float* qs = lds;                      // [kTile][ROW]
+    float* ks = lds + kTile * ROW;        // [kTile][ROW]
+
+    const int64_t bh = blockIdx.z;
+    const int i0 = blockIdx.y * kTile, j0 = blockIdx.x * kTile;
+    const int tid = threadIdx.x;
+    const float* qb = qm + bh * (int64_t)n_units * D;
+    const float* kb = km + bh * (int64_t)n_units * D;
+
+    // stage the unit means of 16 query blocks and 16 key blocks (float4)
+    constexpr int V4 = SPB * D / 4;
+    for (int p = tid; p < kTile * V4; p += kThreads) {
+        const int b = p / V4, o = p % V4;
+        const int u = o / (D / 4);                      // unit within the block
+        float4 qv = make_float4(0.f, 0.f, 0.f, 0.f), kv = qv;
+        if (i0 + b < nb && (i0 + b) * SPB + u < n_units)
+            qv = reinterpret_cast<const float4*>(qb + (int64_t)(i0 + b) * SPB * D)[o];
+        if (j0 + b < nb && (j0 + b) * SPB + u < n_units)
+            kv = reinterpret_cast<const float4*>(kb + (int64_t)(j0 + b) * SPB * D)[o];
+        *reinterpret_cast<float4*>(qs + b * ROW + o * 4) = qv;
+        *reinterpret_cast<float4*>(ks + b * ROW + o * 4) = kv;
+    }
+    __syncthreads();
+
+    const int ti = tid / kTile, tj = tid % kTile;
+    const int i = i0 + ti, j = j0 + tj;
+    if (i >= nb || j >= nb) return;
+    const int nu_i = min(SPB, n_units - i * SPB);       // units that exist
+    const int nu_j = min(SPB, n_units - j * SPB);
+    const float* q = qs + ti * ROW;
+    const float* k = ks + tj * ROW;
+
+    float acc[SPB][SPB];
+#pragma unroll
+    for (int x = 0; x < SPB; ++x)
+#pragma unroll
+        for (int y = 0; y < SPB; ++y) acc[x][y] = 0.f;
+    for (int c = 0; c < D; c += 4) {
+        float4 qv[SPB], kv[SPB];
+#pragma unroll
+        for (int x = 0; x < SPB; ++x) {
+            qv[x] = *reinterpret_cast<const float4*>(q + x * D + c);
+            kv[x] = *reinterpret_cast<const float4*>(k + x * D + c);
+        }
+#pragma unroll
+        for (int x = 0; x < SPB; ++x)
+#pragma unroll
+            for (int y = 0; y < SPB; ++y) {
+                float s = acc[x][y];
+                s = __builtin_fmaf(qv[x].x, kv[y].x, s);
+                s = __builtin_fmaf(qv[x].y, kv[y].y, s);
+                s = __builtin_fmaf(qv[x].z, kv[y].z, s);
+                s = __builtin_fmaf(qv[x].w, kv[y].w, s);
+                acc[x][y] = s;
+            }
+    }
+    float best = -INFINITY;
+#pragma unroll
+    for (int x = 0; x < SPB; ++x)
+#pragma unroll
+        for (int y = 0; y < SPB; ++y)
+            if (x < nu_i && y < nu_j) best = fmaxf(best, scale * acc[x][y]);
+    S[(bh * nb + i) * (int64_t)nb + j] = best;
+}
+
+// ----------------------------------------------------------------------------
+// k_select
+// ----------------------------------------------------------------------------
+struct SelectArgs {
+    const float* S;           // [rows][nb] scores (scored rules)
+    const int32_t* k_head;    // [H] blocks kept per head (TOPK)
+    uint32_t* bits;           // [rows][words]
+    int32_t* counts;          // [rows]
+    int32_t H, N, nb, nb_pad, words, block, HgW;
+    int32_t rule;
+    float mass;
+    int32_t diag, window_frames, n_anchors;
+    int64_t anchor_offset;
+};
+
+// Monotone map of fp32 to uint32 (ascending), with -0 and +0 equal.
+__device__ __forceinline__ uint32_t ordered_bits(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u << 1) == 0) u = 0;                     // -0 -> +0
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__global__ __launch_bounds__(kThreads) void k_select(SelectArgs a) {
+    extern __shared__ unsigned char smem[];
+    const int nb = a.nb, P = a.nb_pad;
+    unsigned long long* key = reinterpret_cast<unsigned long long*>(smem);  // [P]
+    double* cum = reinterpret_cast<double*>(smem);                         // aliases key
+    int32_t* ord = reinterpret_cast<int32_t*>(smem + (size_t)P * 8);       // [P]
+    unsigned char* keep = smem + (a.rule != SA_RULE_NONE ? (size_t)P * 12 : 0);  // [words*32]
+    __shared__ int32_t s_cut;
+    __shared__ int32_t s_count;
+
+    const int64_t row = blockIdx.x;
+    const int i = (int)(row % nb);
+    const int h = (int)((row / nb) % a.H);
+    const int tid = threadIdx.x;
+
+    for (int j = tid; j < a.words * 32; j += kThreads) keep[j] = 0;
+    if (tid == 0) { s_cut = nb; s_count = 0; }
+
+    if (a.rule != SA_RULE_NONE) {
+        const float* S = a.S + row * (int64_t)nb;
+        // sort keys: (score descending, index ascending) as one ascending uint64
+        for (int j = tid; j < P; j += kThreads) {
+            key[j] = j < nb ? ((unsigned long long)(~ordered_bits(S[j])) << 32) | (uint32_t)j
+                            : ~0ull;
+        }
+        __syncthreads();
+        for (int size = 2; size <= P; size <<= 1) {
+            for (int stride = size >> 1; stride > 0; stride >>= 1) {
+                for (int t = tid; t < P / 2; t += kThreads) {
+                    const int lo = 2 * t - (t & (stride - 1));
+                    const int hi = lo + stride;
+                    const bool up = (lo & size) == 0;
+                    const unsigned long long x = key[lo], y = key[hi];
+                    if ((x > y) == up) { key[lo] = y; key[hi] = x; }
+                }
+                __syncthreads();
+            }
+        }
+        for (int r = tid; r < nb; r += kThreads) ord[r] = (int32_t)(key[r] & 0xffffffffu);
+        __syncthreads();
+
+        int m;
+        if (a.rule == SA_RULE_TOPK) {
+            m = a.k_head[h];
+        } else {
+            // p_r = exp(S_r - S_max) in fp64, summed sequentially in rank order
+            const double smax = (double)S[ord[0]];
+            for (int r = tid; r < nb; r += kThreads) cum[r] = exp((double)S[ord[r]] - smax);
+            __syncthreads();
+            if (tid == 0) {
+                double run = 0.0;
+                for (int r = 0; r < nb; ++r) { run += cum[r]; cum[r] = run; }
+            }
+            __syncthreads();
+            const double thr = (double)a.mass * cum[nb - 1];
+            for (int r = tid; r < nb; r += kThreads)
+                if (cum[r] >= thr) atomicMin(&s_cut, r + 1);
+            __syncthreads();
+            m = s_cut;
+        }
+        for (int r = tid; r < m; r += kThreads) keep[ord[r]] = 1;
+    }
+    __syncthreads();
+
+    if (a.diag && tid == 0) keep[i] = 1;
+    if (a.window_frames >= 0) {
+        const int r = a.window_frames;
+        const int lo_i = (i * a.block) / a.HgW;
+        const int hi_i = (min(a.N, (i + 1) * a.block) - 1) / a.HgW;
+        for (int j = tid; j < nb; j += kThreads) {
+            const int lo_j = (j * a.block) / a.HgW;
+            const int hi_j = (min(a.N, (j + 1) * a.block) - 1) / a.HgW;
+            if (lo_j <= hi_i + r && hi_j >= lo_i - r) keep[j] = 1;
+        }
+    }
+    if (a.n_anchors > 0) {
+        const int64_t step = nb / a.n_anchors;
+        for (int m = tid; m < a.n_anchors; m += kThreads)
+            keep[(int)((a.anchor_offset + m * step) % nb)] = 1;
+    }
+    __syncthreads();
+
+    uint32_t* out = a.bits + row * (int64_t)a.words;
+    int local = 0;
+    for (int w = tid; w < a.words; w += kThreads) {
+        uint32_t word = 0;
+        for (int b = 0; b < 32; ++b) word |= (uint32_t)keep[w * 32 + b] << b;
+        out[w] = word;
+        local += __popc(word);
+    }
+    if (local) atomicAdd(&s_count, local);
+    __syncthreads();
+    if (tid == 0) a.counts[row] = s_count;
+}
+
+// ----------------------------------------------------------------------------
+// k_scan: exclusive scan of counts[R] -> row_ptr[R+1], one workgroup
+// ----------------------------------------------------------------------------
+constexpr int kScanThreads = 1024;
+constexpr int kScanItems = 16;
+
+__global__ __launch_bounds__(kScanThreads) void k_scan(const int32_t* __restrict__ counts,
+                                                       int32_t* __restrict__ row_ptr,
+                                                       int64_t R) {
+    __shared__ int32_t wsum[kScanThreads / 64];
+    __shared__ int32_t s_carry;
+    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    if (tid == 0) s_carry = 0;
+    __syncthreads();
+    for (int64_t base = 0; base < R; base += (int64_t)kScanThreads * kScanItems) {
+        int32_t v[kScanItems];
+        int32_t sum = 0;
+        const int64_t my = base + (int64_t)tid * kScanItems;
+#pragma unroll
+        for (int k = 0; k < kScanItems; ++k) {
+            v[k] = (my + k < R) ? counts[my + k] : 0;
+            sum += v[k];
+        }
+        // inclusive scan of per-thread sums within the wave
+        int32_t x = sum;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const int32_t y = __shfl_up(x, off, 64);
+            if (lane >= off) x += y;
+        }
+        if (lane == 63) wsum[wid] = x;
+        __syncthreads();
+        if (wid == 0) {
+            int32_t w = lane < kScanThreads / 64 ? wsum[lane] : 0;
+#pragma unroll
+            for (int off = 1; off < kScanThreads / 64; off <<= 1) {
+                const int32_t y = __shfl_up(w, off, 64);
+                if (lane >= off) w += y;
+            }
+            if (lane < kScanThreads / 64) wsum[lane] = w;
+        }
+        __syncthreads();
+        int32_t run = s_carry + (wid ? wsum[wid - 1] : 0) + (x - sum);
+#pragma unroll
+        for (int k = 0; k < kScanItems; ++k) {
+            if (my + k < R) row_ptr[my + k] = run;
+            run += v[k];
+        }
+        __syncthreads();
+        if (tid == kScanThreads - 1) s_carry = run;
+        __syncthreads();
+    }
+    if (tid == 0) row_ptr[R] = s_carry;
+}
+
+// ----------------------------------------------------------------------------
+// k_expand: one wave per row, bitmap -> ascending column list
+// ----------------------------------------------------------------------------
+__global__ __launch_bounds__(kThreads) void k_expand(const uint32_t* __restrict__ bits,
+                                                     const int32_t* __restrict__ row_ptr,
+                                                     int32_t* __restrict__ col_idx,
+                                                     int64_t R, int words) {
+    const int lane = threadIdx.x & 63;
+    const int64_t row = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+    if (row >= R) return;
+    const uint32_t* b = bits + row * (int64_t)words;
+    int32_t base = row_ptr[row];
+    for (int w0 = 0; w0 < words; w0 += 64) {
+        const int w = w0 + lane;
+        uint32_t word = w < words ? b[w] : 0u;
+        const int cnt = __popc(word);
+        int x = cnt;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const int y = __shfl_up(x, off, 64);
+            if (lane >= off) x += y;
+        }
+        int pos = base + x - cnt;
+        while (word) {
+            const int bit = __ffs(word) - 1;
+            col_idx[pos++] = w * 32 + bit;
+            word &= word - 1;
+        }
+        base += __shfl(x, 63, 64);
+    }
+}
+
+template <int D, int BLK>
+void launch_pool_t(const PoolArgs& a, int nroles, int64_t BH, int nb, hipStream_t s) {
+    hipLaunchKernelGGL((k_pool<D, BLK>), dim3(nb, (unsigned)BH, nroles), dim3(kThreads), 0, s, a);
+}
+
+template <int D, int SPB>
+sa_status launch_score_t(const float* qm, const float* km, float* S, int nb, int n_units,
+                         float scale, int64_t BH, hipStream_t s) {
+    const dim3 grid((nb + kTile - 1) / kTile, (nb + kTile - 1) / kTile, (unsigned)BH);
+    const size_t lds = 2 * kTile * (SPB * D + 4) * sizeof(float);
+    if (lds > 65536) {
+        sa_status st = hip_check(hipFuncSetAttribute((const void*)k_score<D, SPB>,
+                                                     hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                     (int)lds),
+                                 "k_score shared memory");
+        if (st != SA_OK) return st;
+    }
+    hipLaunchKernelGGL((k_score<D, SPB>), grid, dim3(kThreads), lds, s, qm, km, S, nb, n_units,
+                       scale);
+    return hip_check(hipGetLastError(), "k_score launch");
+}
+
+template <int D>
+sa_status launch_score_d(int spb, const float* qm, const float* km, float* S, int nb,
+                         int n_units, float scale, int64_t BH, hipStream_t s) {
+    switch (spb) {
+    case 1: return launch_score_t<D, 1>(qm, km, S, nb, n_units, scale, BH, s);
+    case 2: return launch_score_t<D, 2>(qm, km, S, nb, n_units, scale, BH, s);
+    case 4: return launch_score_t<D, 4>(qm, km, S, nb, n_units, scale, BH, s);
+    default: return launch_score_t<D, 8>(qm, km, S, nb, n_units, scale, BH, s);
+    }
+}
+
+}  // namespace
+
+SelectPlan make_select_plan(const Geometry& g, const sa_select_spec& s) {
+    SelectPlan p{};
+    p.rule = s.rule;
+    p.unit = s.sub_block ? s.sub_block : g.block;
+    p.n_units = (int32_t)ceil_div(g.N, p.unit);
+    p.spb = g.block / p.unit;
+    p.nb_pad = 1;
+    while (p.nb_pad < g.nb) p.nb_pad <<= 1;
+    if (p.nb_pad < 2) p.nb_pad = 2;
+    p.words = (int32_t)ceil_div(g.nb, 32);
+    p.mass = s.mass;
+    p.diag = s.diag;
+    p.window_frames = s.window_frames;
+    p.n_anchors = s.n_anchors;
+    p.anchor_offset = s.anchor_offset;
+    p.want_comp = s.want_comp;
+    size_t off = 0;
+    const bool scored = s.rule != SA_RULE_NONE;
+    const size_t means = scored ? (size_t)g.BH() * p.n_units * g.d * sizeof(float) : 0;
+    p.off_qm = off; off = align_up(off + means, 256);
+    p.off_km = off; off = align_up(off + means, 256);
+    p.off_scores = off;
+    off = align_up(off + (scored ? (size_t)g.rows() * g.nb * sizeof(float) : 0), 256);
+    p.off_bits = off; off = align_up(off + (size_t)g.rows() * p.words * sizeof(uint32_t), 256);
+    p.off_counts = off; off = align_up(off + (size_t)g.rows() * sizeof(int32_t), 256);
+    p.off_k = off; off = align_up(off + (size_t)g.H * sizeof(int32_t), 256);
+    p.total = off;
+    return p;
+}
+
+sa_status launch_select(const Geometry& g, const SelectPlan& p, const int32_t* k_host,
+                        const uint16_t* Q, const uint16_t* K, const uint16_t* V,
+                        int32_t* row_ptr, int32_t* col_idx, float* scores, float* k_mean,
+                        float* v_sum, char* ws, hipStream_t stream) {
+    const bool scored = p.rule != SA_RULE_NONE;
+    float* qm = reinterpret_cast<float*>(ws + p.off_qm);
+    float* km = reinterpret_cast<float*>(ws + p.off_km);
+    float* S = scores ? scores : reinterpret_cast<float*>(ws + p.off_scores);
+    uint32_t* bits = reinterpret_cast<uint32_t*>(ws + p.off_bits);
+    int32_t* counts = reinterpret_cast<int32_t*>(ws + p.off_counts);
+    int32_t* k_dev = reinterpret_cast<int32_t*>(ws + p.off_k);
+    sa_status st;
+
+    // 1. pooling
+    PoolArgs pa{};
+    pa.src[0] = Q; pa.src[1] = K; pa.src[2] = V;
+    pa.N = g.N; pa.nb = g.nb; pa.unit = p.unit; pa.n_units = p.n_units;
+    int nroles = 0;
+    if (scored) {
+        pa.unit_out[0] = qm;
+        pa.roles[nroles++] = 0;
+    }
+    if (scored || p.want_comp) {
+        pa.unit_out[1] = scored ? km : nullptr;
+        pa.block_out[1] = p.want_comp ? k_mean : nullptr;
+        pa.roles[nroles++] = 1;
+    }
+    if (p.want_comp) {
+        pa.block_out[2] = v_sum;
+        pa.roles[nroles++] = 2;
+    }
+    if (nroles) {
+        if (g.d == 128) {
+            if (g.block == 128) launch_pool_t<128, 128>(pa, nroles, g.BH(), g.nb, stream);
+            else launch_pool_t<128, 64>(pa, nroles, g.BH(), g.nb, stream);
+        } else {
+            if (g.block == 128) launch_pool_t<64, 128>(pa, nroles, g.BH(), g.nb, stream);
+            else launch_pool_t<64, 64>(pa, nroles, g.BH(), g.nb, stream);
+        }
+        if ((st = hip_check(hipGetLastError(), "k_pool launch")) != SA_OK) return st;
+    }
+
+    // 2. scores
+    if (scored) {
+        st = g.d == 128
+                 ? launch_score_d<128>(p.spb, qm, km, S, g.nb, p.n_units, g.scale, g.BH(), stream)
+                 : launch_score_d<64>(p.spb, qm, km, S, g.nb, p.n_units, g.scale, g.BH(), stream);
+        if (st != SA_OK) return st;
+    }
+
+    // 3. selection
+    if (p.rule == SA_RULE_TOPK) {
+        st = hip_check(hipMemcpyAsync(k_dev, k_host, (size_t)g.H * sizeof(int32_t),
+                                      hipMemcpyHostToDevice, stream), "copy k per head");
+        if (st != SA_OK) return st;
+    }
+    SelectArgs sa{};
+    sa.S = S; sa.k_head = k_dev; sa.bits = bits; sa.counts = counts;
+    sa.H = g.H; sa.N = g.N; sa.nb = g.nb; sa.nb_pad = p.nb_pad; sa.words = p.words;
+    sa.block = g.block; sa.HgW = g.Hg * g.W; sa.rule = p.rule; sa.mass = p.mass;
+    sa.diag = p.diag; sa.window_frames = p.window_frames; sa.n_anchors = p.n_anchors;
+    sa.anchor_offset = p.anchor_offset;
+    const size_t lds = scored ? (size_t)p.nb_pad * 12 + (size_t)p.words * 32
+                              : (size_t)p.words * 32 + 16;
+    hipLaunchKernelGGL(k_select, dim3((unsigned)g.rows()), dim3(kThreads), lds, stream, sa);
+    if ((st = hip_check(hipGetLastError(), "k_select launch")) != SA_OK) return st;
+
+    // 4. CSR
+    hipLaunchKernelGGL(k_scan, dim3(1), dim3(kScanThreads), 0, stream, counts, row_ptr, g.rows());
+    if ((st = hip_check(hipGetLastError(), "k_scan launch")) != SA_OK) return st;
+    hipLaunchKernelGGL(k_expand, dim3((unsigned)ceil_div(g.rows(), kThreads / 64)), dim3(kThreads),
+                       0, stream, bits, row_ptr, col_idx, g.rows(), p.words);
+    return hip_check(hipGetLastError(), "k_expand launch");
+}
+
+}  // namespace sa

@@ -1,0 +1,249 @@
+// Public C ABI of libsparse_attn.so: argument validation, workspace sizing and
+// dispatch to the gfx950 kernels.  Every check runs on the host before any
+// HIP call, so a rejected call enqueues nothing.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <string>
+
+#include "sa_internal.h"
+
+#define SA_API extern "C" __attribute__((visibility("default")))
+
+namespace sa {
+
+static thread_local std::string g_last_error;
+
+sa_status fail(sa_status st, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return st;
+}
+
+sa_status hip_check(hipError_t e, const char* what) {
+    if (e == hipSuccess) return SA_OK;
+    return fail(SA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+static void clear_error() { g_last_error.clear(); }
+
+static bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Validates the problem statement and fills the derived geometry.
+static sa_status check_problem(const sa_problem* p, Geometry* g) {
+    if (!p) return fail(SA_ERR_INVALID_ARG, "prob is NULL");
+    if (p->B < 1 || p->H < 1 || p->N < 1)
+        return fail(SA_ERR_INVALID_ARG, "B, H, N must be >= 1 (got %d, %d, %d)", p->B, p->H, p->N);
+    if (p->T < 1 || p->Hg < 1 || p->W < 1)
+        return fail(SA_ERR_INVALID_ARG, "latent grid sides must be >= 1 (got %d x %d x %d)",
+                    p->T, p->Hg, p->W);
+    if ((int64_t)p->T * p->Hg * p->W != (int64_t)p->N)
+        return fail(SA_ERR_INVALID_ARG, "T*Hg*W = %lld does not equal N = %d",
+                    (long long)p->T * p->Hg * p->W, p->N);
+    if (p->d != 64 && p->d != 128)
+        return fail(SA_ERR_UNSUPPORTED, "head dim d = %d (supported: 64, 128)", p->d);
+    if (p->block != 64 && p->block != 128)
+        return fail(SA_ERR_UNSUPPORTED, "block = %d (supported: 64, 128)", p->block);
+    if (!isfinite(p->scale))
+        return fail(SA_ERR_INVALID_ARG, "scale is not finite");
+    if ((int64_t)p->B * p->H * p->N * p->d > ((int64_t)1 << 40))
+        return fail(SA_ERR_UNSUPPORTED, "tensor too large");
+    g->B = p->B; g->H = p->H; g->N = p->N; g->d = p->d; g->block = p->block;
+    g->T = p->T; g->Hg = p->Hg; g->W = p->W;
+    g->nb = (int32_t)ceil_div(p->N, p->block);
+    g->scale = p->scale > 0.f ? p->scale : (float)(1.0 / sqrt((double)p->d));
+    return SA_OK;
+}
+
+static sa_status check_spec(const Geometry& g, const sa_select_spec* s) {
+    if (!s) return fail(SA_ERR_INVALID_ARG, "spec is NULL");
+    if (s->rule != SA_RULE_NONE && s->rule != SA_RULE_TOPK && s->rule != SA_RULE_MASS)
+        return fail(SA_ERR_INVALID_ARG, "unknown rule %d", s->rule);
+    if (s->rule != SA_RULE_NONE && g.nb > 4096)
+        return fail(SA_ERR_UNSUPPORTED, "scored rules support nb <= 4096 (got %d)", g.nb);
+    if (g.rows() * (int64_t)g.nb > (int64_t)INT32_MAX)
+        return fail(SA_ERR_UNSUPPORTED, "B*H*nb*nb exceeds the int32 range of row_ptr");
+    if (s->sub_block != 0) {
+        const int sb = s->sub_block;
+        if (sb < 16 || (sb & (sb - 1)) != 0 || g.block % sb != 0)
+            return fail(SA_ERR_INVALID_ARG,
+                        "sub_block = %d must be 0 or a power of two >= 16 dividing block = %d",
+                        sb, g.block);
+    }
+    if (s->rule == SA_RULE_TOPK) {
+        if (s->topk) {
+            for (int h = 0; h < g.H; ++h)
+                if (s->topk[h] < 1)
+                    return fail(SA_ERR_INVALID_ARG, "topk[%d] = %d must be >= 1", h, s->topk[h]);
+        } else if (s->density) {
+            for (int h = 0; h < g.H; ++h)
+                if (!(s->density[h] > 0.f && s->density[h] <= 1.f))
+                    return fail(SA_ERR_INVALID_ARG, "density[%d] = %g must be in (0, 1]", h,
+                                (double)s->density[h]);
+        } else {
+            return fail(SA_ERR_INVALID_ARG, "SA_RULE_TOPK needs topk or density");
+        }
+    }
+    if (s->rule == SA_RULE_MASS && !(s->mass > 0.f && s->mass <= 1.f))
+        return fail(SA_ERR_INVALID_ARG, "mass = %g must be in (0, 1]", (double)s->mass);
+    if (s->window_frames < -1)
+        return fail(SA_ERR_INVALID_ARG, "window_frames = %d must be >= -1", s->window_frames);
+    if (s->n_anchors < 0 || s->n_anchors > g.nb)
+        return fail(SA_ERR_INVALID_ARG, "n_anchors = %d must be in [0, nb = %d]", s->n_anchors, g.nb);
+    if (s->anchor_offset < 0)
+        return fail(SA_ERR_INVALID_ARG, "anchor_offset must be >= 0");
+    if (s->diag != 0 && s->diag != 1)
+        return fail(SA_ERR_INVALID_ARG, "diag must be 0 or 1");
+    if (s->want_comp != 0 && s->want_comp != 1)
+        return fail(SA_ERR_INVALID_ARG, "want_comp must be 0 or 1");
+    return SA_OK;
+}
+
+}  // namespace sa
+
+using namespace sa;
+
+SA_API sa_status sparse_attn_workspace_size(const sa_problem* prob,
+                                            const sa_select_spec* spec, size_t* bytes) {
+    clear_error();
+    Geometry g;
+    sa_status st = check_problem(prob, &g);
+    if (st != SA_OK) return st;
+    if (!bytes) return fail(SA_ERR_INVALID_ARG, "bytes is NULL");
+    if (spec) {
+        if ((st = check_spec(g, spec)) != SA_OK) return st;
+        *bytes = make_select_plan(g, *spec).total;
+    } else {
+        *bytes = fwd_workspace_bytes(g);
+    }
+    return SA_OK;
+}
+
+SA_API sa_status hilbert_perm_build(int32_t T, int32_t Hg, int32_t W, int32_t* perm,
+                                    int32_t* inv) {
+    clear_error();
+    if (T < 1 || Hg < 1 || W < 1)
+        return fail(SA_ERR_INVALID_ARG, "grid sides must be >= 1 (got %d x %d x %d)", T, Hg, W);
+    if (T > 256 || Hg > 256 || W > 256)
+        return fail(SA_ERR_UNSUPPORTED, "grid sides must be <= 256");
+    if ((int64_t)T * Hg * W > (int64_t)INT32_MAX)
+        return fail(SA_ERR_UNSUPPORTED, "grid too large");
+    if (!perm) return fail(SA_ERR_INVALID_ARG, "perm is NULL");
+    return build_hilbert_order(T, Hg, W, perm, inv);
+}
+
+static sa_status permute_common(const sa_problem* prob, const void* src, void* dst,
+                                const int32_t* perm, void* stream, bool inverse) {
+    clear_error();
+    Geometry g;
+    sa_status st = check_problem(prob, &g);
+    if (st != SA_OK) return st;
+    if (!src || !dst || !perm) return fail(SA_ERR_INVALID_ARG, "src, dst and perm must be non-NULL");
+    if (!aligned16(src) || !aligned16(dst))
+        return fail(SA_ERR_INVALID_ARG, "src and dst must be 16-byte aligned");
+    const size_t bytes = (size_t)g.BH() * g.N * g.d * 2;
+    const char* s = (const char*)src;
+    const char* d = (const char*)dst;
+    if (s < d + bytes && d < s + bytes) return fail(SA_ERR_INVALID_ARG, "src and dst overlap");
+    return launch_permute(g, (const uint16_t*)src, (uint16_t*)dst, perm, inverse,
+                          (hipStream_t)stream);
+}
+
+SA_API sa_status hilbert_permute(const sa_problem* prob, const void* src, void* dst,
+                                 const int32_t* perm_dev, void* stream) {
+    return permute_common(prob, src, dst, perm_dev, stream, false);
+}
+
+SA_API sa_status hilbert_unpermute(const sa_problem* prob, const void* src, void* dst,
+                                   const int32_t* perm_dev, void* stream) {
+    return permute_common(prob, src, dst, perm_dev, stream, true);
+}
+
+SA_API sa_status sparse_attn_select(const sa_problem* prob, const sa_select_spec* spec,
+                                    const void* Q, const void* K, const void* V,
+                                    int32_t* row_ptr, int32_t* col_idx, float* scores,
+                                    float* k_mean, float* v_sum, void* workspace,
+                                    size_t ws_bytes, void* stream) {
+    clear_error();
+    Geometry g;
+    sa_status st = check_problem(prob, &g);
+    if (st != SA_OK) return st;
+    if ((st = check_spec(g, spec)) != SA_OK) return st;
+    const bool scored = spec->rule != SA_RULE_NONE;
+    if (scored && (!Q || !K)) return fail(SA_ERR_INVALID_ARG, "Q and K are required by the rule");
+    if ((Q && !aligned16(Q)) || (K && !aligned16(K)) || (V && !aligned16(V)))
+        return fail(SA_ERR_INVALID_ARG, "Q, K, V must be 16-byte aligned");
+    if (!row_ptr || !col_idx) return fail(SA_ERR_INVALID_ARG, "row_ptr and col_idx are required");
+    if (spec->want_comp) {
+        if (!K || !V) return fail(SA_ERR_INVALID_ARG, "want_comp needs K and V");
+        if (!k_mean || !v_sum) return fail(SA_ERR_INVALID_ARG, "want_comp needs k_mean and v_sum");
+    }
+    const SelectPlan plan = make_select_plan(g, *spec);
+    if (plan.total > 0) {
+        if (!workspace) return fail(SA_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", plan.total);
+        if (((uintptr_t)workspace & 255u) != 0)
+            return fail(SA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+        if (ws_bytes < plan.total)
+            return fail(SA_ERR_WORKSPACE, "workspace too small: %zu < %zu bytes", ws_bytes, plan.total);
+    }
+    // blocks kept per head, resolved on the host
+    int32_t k_host[4096];
+    int32_t* kh = k_host;
+    std::string kbuf;
+    if (g.H > 4096) {
+        kbuf.resize((size_t)g.H * sizeof(int32_t));
+        kh = (int32_t*)&kbuf[0];
+    }
+    for (int h = 0; h < g.H; ++h) {
+        int64_t k = 0;
+        if (spec->rule == SA_RULE_TOPK) {
+            if (spec->topk) {
+                k = spec->topk[h];
+            } else {
+                k = (int64_t)ceil((double)spec->density[h] * (double)g.nb * (1.0 - 1e-6));
+            }
+            if (k < 1) k = 1;
+            if (k > g.nb) k = g.nb;
+        }
+        kh[h] = (int32_t)k;
+    }
+    return launch_select(g, plan, kh, (const uint16_t*)Q, (const uint16_t*)K,
+                         (const uint16_t*)V, row_ptr, col_idx, scores, k_mean, v_sum,
+                         (char*)workspace, (hipStream_t)stream);
+}
+
+SA_API sa_status sparse_attn_fwd(const sa_problem* prob, const void* Q, const void* K,
+                                 const void* V, const int32_t* row_ptr,
+                                 const int32_t* col_idx, const float* k_mean,
+                                 const float* v_sum, void* O, float* lse, void* workspace,
+                                 size_t ws_bytes, void* stream) {
+    clear_error();
+    Geometry g;
+    sa_status st = check_problem(prob, &g);
+    if (st != SA_OK) return st;
+    if (!Q || !K || !V || !O) return fail(SA_ERR_INVALID_ARG, "Q, K, V and O are required");
+    if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O))
+        return fail(SA_ERR_INVALID_ARG, "Q, K, V, O must be 16-byte aligned");
+    if (!row_ptr || !col_idx) return fail(SA_ERR_INVALID_ARG, "row_ptr and col_idx are required");
+    if ((k_mean == nullptr) != (v_sum == nullptr))
+        return fail(SA_ERR_INVALID_ARG, "k_mean and v_sum must be given together");
+    if (k_mean) {
+        const size_t need = fwd_workspace_bytes(g);
+        if (!workspace) return fail(SA_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", need);
+        if (((uintptr_t)workspace & 255u) != 0)
+            return fail(SA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+        if (ws_bytes < need)
+            return fail(SA_ERR_WORKSPACE, "workspace too small: %zu < %zu bytes", ws_bytes, need);
+    }
+    return launch_fwd(g, (const uint16_t*)Q, (const uint16_t*)K, (const uint16_t*)V, row_ptr,
+                      col_idx, k_mean, v_sum, (uint16_t*)O, lse, (char*)workspace,
+                      (hipStream_t)stream);
+}
+
+SA_API const char* sparse_attn_last_error(void) { return g_last_error.c_str(); }

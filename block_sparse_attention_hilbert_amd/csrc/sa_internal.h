@@ -1,0 +1,81 @@
+// Internal declarations shared by the host API and the kernel launchers of
+// libsparse_attn.so.  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/sparse_attn.h"
+
+namespace sa {
+
+// Records a failure message for sparse_attn_last_error() and returns `st`.
+sa_status fail(sa_status st, const char* fmt, ...);
+
+// Checks a HIP call / the last launch and converts a failure to SA_ERR_HIP.
+sa_status hip_check(hipError_t e, const char* what);
+
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Geometry derived from a validated sa_problem.
+struct Geometry {
+    int32_t B, H, N, d, block, nb;
+    int32_t T, Hg, W;
+    float scale;
+    int64_t BH() const { return (int64_t)B * H; }
+    int64_t rows() const { return BH() * nb; }
+};
+
+// ----------------------------------------------------------------------------
+// selection (k_select.hip)
+// ----------------------------------------------------------------------------
+struct SelectPlan {
+    int32_t rule;            // SA_RULE_*
+    int32_t unit;            // tokens per pooled unit: sub_block or block
+    int32_t n_units;         // ceil(N / unit)
+    int32_t spb;             // units per block
+    int32_t nb_pad;          // sort length: next power of two >= nb
+    int32_t words;           // bitmap words per row: ceil(nb / 32)
+    float mass;
+    int32_t diag, window_frames, n_anchors;
+    int64_t anchor_offset;
+    int32_t want_comp;
+    // workspace carve-up (byte offsets)
+    size_t off_qm, off_km, off_scores, off_bits, off_counts, off_k, total;
+};
+
+SelectPlan make_select_plan(const Geometry& g, const sa_select_spec& s);
+
+sa_status launch_select(const Geometry& g, const SelectPlan& p,
+                        const int32_t* k_host, const uint16_t* Q,
+                        const uint16_t* K, const uint16_t* V, int32_t* row_ptr,
+                        int32_t* col_idx, float* scores, float* k_mean,
+                        float* v_sum, char* ws, hipStream_t stream);
+
+// ----------------------------------------------------------------------------
+// attention (k_attn.hip)
+// ----------------------------------------------------------------------------
+size_t fwd_workspace_bytes(const Geometry& g);
+
+sa_status launch_fwd(const Geometry& g, const uint16_t* Q, const uint16_t* K,
+                     const uint16_t* V, const int32_t* row_ptr,
+                     const int32_t* col_idx, const float* k_mean,
+                     const float* v_sum, uint16_t* O, float* lse, char* ws,
+                     hipStream_t stream);
+
+// ----------------------------------------------------------------------------
+// token reordering (k_permute.hip)
+// ----------------------------------------------------------------------------
+sa_status launch_permute(const Geometry& g, const uint16_t* src, uint16_t* dst,
+                         const int32_t* perm, bool inverse, hipStream_t stream);
+
+// ----------------------------------------------------------------------------
+// Hilbert order (hilbert.cpp)
+// ----------------------------------------------------------------------------
+sa_status build_hilbert_order(int32_t T, int32_t Hg, int32_t W, int32_t* perm,
+                              int32_t* inv);
+
+}  // namespace sa

@@ -1,0 +1,94 @@
+"""One block-sparse attention call with preallocated buffers.
+
+The call is the whole hot path: optional Hilbert reordering of Q, K, V
+(DFSAttn page, trick 1), block selection (pooling, scores, keep lists as CSR),
+block-sparse attention with optional centroid compensation (SVG-EAR page,
+section 2A), and the inverse reordering of O.  Every step is one or more HIP
+kernels of libsparse_attn.so enqueued on the current stream; this class only
+owns the buffers so that repeated calls allocate nothing.
+"""
+from __future__ import annotations
+
+from typing import Optional
+
+import numpy as np
+import torch
+
+from . import (Problem, Selection, SelectSpec, alloc_workspace, fwd, hilbert_perm_build,
+               hilbert_permute, hilbert_unpermute, select, workspace_size)
+
+
+class BlockSparseAttention:
+    def __init__(self, prob: Problem, spec: SelectSpec, hilbert: bool = False,
+                 device="cuda", want_scores: bool = False, want_lse: bool = False):
+        self.prob, self.spec, self.hilbert = prob, spec, hilbert
+        self.device = torch.device(device)
+        nb, rows = prob.nb, prob.rows
+        shape = (prob.B, prob.H, prob.N, prob.d)
+        self.sel = Selection(torch.empty(rows + 1, dtype=torch.int32, device=self.device),
+                             torch.empty(rows * nb, dtype=torch.int32, device=self.device))
+        if want_scores:
+            self.sel.scores = torch.empty(rows * nb, dtype=torch.float32, device=self.device)
+        if spec.want_comp:
+            self.sel.k_mean = torch.empty(prob.B, prob.H, nb, prob.d, dtype=torch.float32,
+                                          device=self.device)
+            self.sel.v_sum = torch.empty_like(self.sel.k_mean)
+        self.ws_select = alloc_workspace(workspace_size(prob, spec), self.device)
+        self.ws_fwd = alloc_workspace(workspace_size(prob, None), self.device) \
+            if spec.want_comp else None
+        self.O = torch.empty(shape, dtype=torch.bfloat16, device=self.device)
+        self.lse = torch.empty(prob.B, prob.H, prob.N, dtype=torch.float32,
+                               device=self.device) if want_lse else None
+        self.perm_dev = None
+        if hilbert:
+            perm, _ = hilbert_perm_build(prob.T, prob.Hg, prob.W)
+            self.perm = perm
+            self.perm_dev = torch.from_numpy(perm).to(self.device)
+            self.Qp = torch.empty(shape, dtype=torch.bfloat16, device=self.device)
+            self.Kp = torch.empty_like(self.Qp)
+            self.Vp = torch.empty_like(self.Qp)
+            self.Op = torch.empty_like(self.Qp)
+
+    def permute_inputs(self, Q, K, V):
+        if not self.hilbert:
+            return Q, K, V
+        hilbert_permute(self.prob, Q, self.perm_dev, self.Qp)
+        hilbert_permute(self.prob, K, self.perm_dev, self.Kp)
+        hilbert_permute(self.prob, V, self.perm_dev, self.Vp)
+        return self.Qp, self.Kp, self.Vp
+
+    def run_select(self, Q, K, V, anchor_offset: Optional[int] = None) -> Selection:
+        spec = self.spec
+        if anchor_offset is not None:
+            spec = SelectSpec(**{**spec.__dict__, "anchor_offset": int(anchor_offset)})
+        return select(self.prob, spec, Q, K, V if spec.want_comp else None,
+                      out=self.sel, workspace=self.ws_select)
+
+    def run_fwd(self, Q, K, V, row_ptr=None, col_idx=None):
+        rp = self.sel.row_ptr if row_ptr is None else row_ptr
+        ci = self.sel.col_idx if col_idx is None else col_idx
+        out = self.Op if self.hilbert else self.O
+        fwd(self.prob, Q, K, V, rp, ci, self.sel.k_mean, self.sel.v_sum, O=out, lse=self.lse,
+            workspace=self.ws_fwd)
+        return out
+
+    def unpermute_output(self):
+        if self.hilbert:
+            hilbert_unpermute(self.prob, self.Op, self.perm_dev, self.O)
+        return self.O
+
+    def __call__(self, Q, K, V, anchor_offset: Optional[int] = None) -> torch.Tensor:
+        Qp, Kp, Vp = self.permute_inputs(Q, K, V)
+        self.run_select(Qp, Kp, Vp, anchor_offset)
+        self.run_fwd(Qp, Kp, Vp)
+        return self.unpermute_output()
+
+    def keep_mask(self) -> np.ndarray:
+        """Kept-block mask [B, H, nb, nb] of the last selection (host copy)."""
+        p = self.prob
+        rp = self.sel.row_ptr.cpu().numpy()
+        ci = self.sel.col_idx[: int(rp[-1])].cpu().numpy()
+        keep = np.zeros((p.rows, p.nb), dtype=bool)
+        rows = np.repeat(np.arange(p.rows), np.diff(rp))
+        keep[rows, ci] = True
+        return keep.reshape(p.B, p.H, p.nb, p.nb)

@@ -1,0 +1,200 @@
+/*
+ * sparse_attn.h -- C ABI of the MI355X (gfx950) block-sparse video attention
+ * library (libsparse_attn.so).
+ *
+ * The library computes training-free dynamic block-sparse self-attention for
+ * video diffusion transformers in two stages:
+ *
+ *   1. selection  -- optional 3D Hilbert token reordering, block means of Q
+ *                    and K, pooled block scores, and a per-query-block keep
+ *                    list (top-k or cumulative softmax mass) unioned with a
+ *                    temporal window and rotating global anchor blocks;
+ *   2. attention  -- a streaming (online-softmax) forward pass over the kept
+ *                    KV blocks only, optionally adding every skipped KV block
+ *                    back as one centroid term.
+ *
+ * Sources, by page title and section:
+ *   [DFS]  "DFSAttn: Dynamic Fine-grained Sparse Attention for Efficient Video
+ *          Generation": trick 1 (3D Hilbert reordering), trick 2 (block and
+ *          sub-block scores from block means).
+ *   [EAR]  "SVG-EAR: Parameter-Free Linear Compensation for Sparse Video
+ *          Generation via Error-aware Routing": section 2A (skipped blocks
+ *          replaced by their centroid), 2B (selection under a fixed density
+ *          budget; streaming update without materialised logits), section 4
+ *          (top-p selection).
+ *   [SVOO] "SVOO: Training-Free Sparse Attention for Fast Video Generation ...":
+ *          section 2A (density covering a share of cumulative attention mass).
+ *   [LVSA] "LVSA: Training-Free Sparse Attention for Long Video Diffusion",
+ *          abstract (structured window pattern plus rotating global anchors).
+ *   [SPADE]"SPADE: An Input-Adaptive Sparse Attention Engine for Fast Video
+ *          Diffusion Models Inference", part 2 (keep decision per head) and
+ *          part 3 (head-wise sparse attention kernel).
+ *
+ * Conventions shared by every entry point
+ *   - Tensors Q, K, V, O are bf16, shape [B, H, N, d], contiguous, 16-byte
+ *     aligned device pointers.  Token n of the latent grid (T, Hg, W) is
+ *     n = (t*Hg + y)*W + x in raster order.
+ *   - Blocks are contiguous runs of `block` tokens of the sequence as given
+ *     (raster or Hilbert order); nb = ceil(N / block); the last block holds
+ *     N - (nb-1)*block tokens.
+ *   - Ownership: the caller allocates and frees every buffer (device memory
+ *     for tensors, masks and workspace; host memory for host arrays).  The
+ *     library allocates nothing, keeps no state between calls and never
+ *     synchronises the stream.
+ *   - Ordering: device work is enqueued on `stream` (a hipStream_t; NULL is
+ *     the default stream) and is asynchronous.
+ *   - Errors: arguments are validated on the host before any launch; a
+ *     failed check returns SA_ERR_INVALID_ARG, SA_ERR_UNSUPPORTED or
+ *     SA_ERR_WORKSPACE and enqueues nothing.  A failed launch returns
+ *     SA_ERR_HIP.  sparse_attn_last_error() then describes the failure.
+ *     Non-finite input values are not checked (undefined results).
+ */
+#ifndef SPARSE_ATTN_H
+#define SPARSE_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    SA_OK = 0,
+    SA_ERR_INVALID_ARG = 1,   /* malformed argument (null, size, range)         */
+    SA_ERR_UNSUPPORTED = 2,   /* well-formed but outside what is implemented     */
+    SA_ERR_WORKSPACE = 3,     /* workspace missing, misaligned or too small      */
+    SA_ERR_HIP = 4            /* a HIP runtime call or kernel launch failed      */
+} sa_status;
+
+/* Problem statement: the dense 3D self-attention the sparse call replaces. */
+typedef struct {
+    int32_t B, H, N, d;   /* batch, heads, tokens, head dim (d: 64 or 128)     */
+    int32_t T, Hg, W;     /* latent grid; T*Hg*W must equal N                   */
+    int32_t block;        /* tokens per Q block and per KV block: 64 or 128     */
+    float scale;          /* softmax scale; <= 0 selects (float)(1/sqrt(d))     */
+} sa_problem;
+
+enum {
+    SA_RULE_NONE = 0,     /* structural blocks only (window, anchors, diagonal) */
+    SA_RULE_TOPK = 1,     /* k highest pooled scores per query block  [EAR 2B] */
+    SA_RULE_MASS = 2      /* shortest score-ranked prefix reaching `mass` of the
+                             softmax mass of the pooled scores  [EAR 4, SVOO 2A] */
+};
+
+/* Selection rule.  Host-side struct; `topk` and `density` are host arrays. */
+typedef struct {
+    int32_t rule;            /* SA_RULE_*                                         */
+    int32_t sub_block;       /* 0, or a power of two >= 16 dividing `block`:
+                                score = max over sub-block pairs  [DFS trick 2]  */
+    const int32_t* topk;     /* host [H] blocks kept per head (clamped to 1..nb),
+                                or NULL to derive k from `density`               */
+    const float* density;    /* host [H] in (0,1]: k = clamp(ceil(rho*nb*(1-1e-6)),
+                                1, nb); used when topk == NULL                   */
+    float mass;              /* SA_RULE_MASS threshold tau in (0, 1]              */
+    int32_t diag;            /* 1: always keep KV block j == i                    */
+    int32_t window_frames;   /* -1: off.  r >= 0: keep KV block j when the latent
+                                frames it covers come within r frames of those of
+                                query block i (raster order)  [LVSA]             */
+    int32_t n_anchors;       /* A in [0, nb]: anchors a_m = (anchor_offset +
+                                m*floor(nb/A)) mod nb kept for every row  [LVSA] */
+    int64_t anchor_offset;   /* rotation of the anchors for this call (>= 0)      */
+    int32_t want_comp;       /* 1: also write k_mean and v_sum for compensation   */
+} sa_select_spec;
+
+/*
+ * Workspace bytes needed by sparse_attn_select (spec != NULL) or by
+ * sparse_attn_fwd with compensation (spec == NULL).  The same buffer may be
+ * reused by consecutive calls on one stream.
+ */
+sa_status sparse_attn_workspace_size(const sa_problem* prob,
+                                     const sa_select_spec* spec, size_t* bytes);
+
+/*
+ * 3D Hilbert token order [DFS trick 1], host only.  The grid is placed in the
+ * cube of side 2^b (b = ceil(log2(max(T, Hg, W))), at least 1), the cube's
+ * cells are walked along the Hilbert curve (J. Skilling's construction,
+ * "Programming the Hilbert curve", 2004; x on the curve's first-step axis, t
+ * and y on the other two in order) and cells outside the grid are dropped.
+ * perm[r] = raster index of the r-th kept cell; inv[perm[r]] = r.
+ * perm and inv: caller-owned host arrays of T*Hg*W int32 each (inv may be NULL).
+ * Returns SA_ERR_UNSUPPORTED when max(T,Hg,W) > 256.
+ */
+sa_status hilbert_perm_build(int32_t T, int32_t Hg, int32_t W,
+                             int32_t* perm, int32_t* inv);
+
+/*
+ * Token reordering of one [B,H,N,d] bf16 tensor [DFS trick 1]:
+ *   hilbert_permute:   dst[b,h,n,:]       = src[b,h,perm[n],:]
+ *   hilbert_unpermute: dst[b,h,perm[n],:] = src[b,h,n,:]
+ * perm_dev: device int32 [N], a permutation of 0..N-1 (not checked on the
+ * host; entries outside [0, N) are skipped by the kernel, and a
+ * non-permutation leaves rows of dst unwritten).  src and dst must not overlap.
+ */
+sa_status hilbert_permute(const sa_problem* prob, const void* src, void* dst,
+                          const int32_t* perm_dev, void* stream);
+sa_status hilbert_unpermute(const sa_problem* prob, const void* src, void* dst,
+                            const int32_t* perm_dev, void* stream);
+
+/*
+ * Block selection [DFS trick 2, EAR 2B/4, SVOO 2A, LVSA, SPADE part 2].
+ * For every (b, h, query block i) the row of kept KV blocks is the union of
+ *   - the rule's set: blocks ranked by pooled score S[i,j] (descending; ties by
+ *     lower j), the first k (TOPK) or the shortest prefix whose softmax mass
+ *     sum_{first m} exp(S - S_max) reaches mass * (sum over all j) (MASS);
+ *   - j == i when diag; the window blocks; the anchor blocks.
+ * Pooled score: S[i,j] = fl32(scale * dot(qbar_i, kbar_j)) where qbar, kbar are
+ * block means (fp32 rounding of the exact mean) and dot is a sequential fp32
+ * fused-multiply-add chain over the d channels; with sub_block, qbar/kbar are
+ * sub-block means and S[i,j] is the max over the sub-block pairs of (i, j).
+ *
+ * Q, K: device bf16 [B,H,N,d] (ignored for SA_RULE_NONE).  V: device bf16, used
+ *   only when want_comp (else may be NULL).
+ * row_ptr: device int32 [B*H*nb + 1]; col_idx: device int32, capacity
+ *   B*H*nb*nb.  Row r = (b*H + h)*nb + i lists its kept KV blocks in
+ *   col_idx[row_ptr[r] .. row_ptr[r+1]), strictly ascending.
+ * scores: optional device fp32 [B*H*nb*nb] receiving S (NULL: not written;
+ *   never written for SA_RULE_NONE).
+ * k_mean, v_sum: device fp32 [B,H,nb,d] when want_comp (block means of K;
+ *   fp32 block sums of V), else NULL.
+ * workspace: device, 256-byte aligned, >= sparse_attn_workspace_size(prob, spec).
+ * Limits: nb <= 4096 for the scored rules (SA_ERR_UNSUPPORTED above).
+ */
+sa_status sparse_attn_select(const sa_problem* prob, const sa_select_spec* spec,
+                             const void* Q, const void* K, const void* V,
+                             int32_t* row_ptr, int32_t* col_idx, float* scores,
+                             float* k_mean, float* v_sum,
+                             void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * Block-sparse attention forward [EAR 2B streaming update; SPADE part 3].
+ * For a query token n of block i:
+ *   O[n] = sum_t exp(l_t - m) v_t / sum_t exp(l_t - m),  l_t = scale * q_n.k_t,
+ * over the tokens t of the KV blocks listed in row i of (row_ptr, col_idx).
+ * With compensation (k_mean and v_sum both non-NULL) [EAR 2A] every KV block j
+ * NOT listed adds one centroid term: logit scale*q_n.k_mean_j, weight n_j
+ * (its token count), value v_sum_j / n_j.
+ * Q, K, V: device bf16 [B,H,N,d].  row_ptr/col_idx: as written by
+ *   sparse_attn_select (strictly ascending rows, indices in [0, nb); not
+ *   checked).  O: device bf16 [B,H,N,d].  lse: optional device fp32 [B,H,N],
+ *   natural-log log-sum-exp of the logits (including compensation terms).
+ * A row with no kept block and no compensation gives O = 0, lse = -inf.
+ * workspace: needed only with compensation (size from
+ *   sparse_attn_workspace_size(prob, NULL)); may be NULL otherwise.
+ * Precision: QK^T and PV on bf16 matrix cores with fp32 accumulation, softmax
+ *   in fp32, output rounded to bf16.
+ */
+sa_status sparse_attn_fwd(const sa_problem* prob, const void* Q, const void* K,
+                          const void* V, const int32_t* row_ptr,
+                          const int32_t* col_idx, const float* k_mean,
+                          const float* v_sum, void* O, float* lse,
+                          void* workspace, size_t ws_bytes, void* stream);
+
+/* Text of the last failure on the calling thread ("" after success). */
+const char* sparse_attn_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPARSE_ATTN_H */

@@ -208,10 +208,20 @@ def unpermute_tokens(X: np.ndarray, perm: np.ndarray) -> np.ndarray:
 # ---------------------------------------------------------------------------
 
 def block_sums_f64(X: np.ndarray, block: int) -> np.ndarray:
-    """Exact float64 sums of each block of tokens: [..., N, d] -> [..., nb, d]."""
-    N = X.shape[-2]
-    b = block_bounds(N, block)
-    return np.add.reduceat(np.asarray(X, dtype=np.float64), b[:-1], axis=-2)
+    """Exact float64 sums of each block of tokens: [..., N, d] -> [..., nb, d].
+
+    Sums of at most a few hundred bf16 values are exact in float64 (their
+    significands span far fewer than 53 bits), so the order of the additions
+    does not matter.
+    """
+    X = np.asarray(X, dtype=np.float64)
+    N, d = X.shape[-2], X.shape[-1]
+    nfull = N // block
+    lead = X.shape[:-2]
+    parts = [X[..., : nfull * block, :].reshape(*lead, nfull, block, d).sum(axis=-2)]
+    if nfull * block < N:
+        parts.append(X[..., nfull * block:, :].sum(axis=-2, keepdims=True))
+    return np.concatenate(parts, axis=-2)
 
 
 def block_means(X: np.ndarray, block: int) -> np.ndarray:

@@ -1,0 +1,127 @@
+"""Helpers of the GPU parity tests: oracle side of a workload, mask comparison
+with near-tie accounting, and attention comparison on sampled query blocks."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+
+import oracle
+import workloads as W
+
+ATOL_MAX = 2e-2      # attention output, max |GPU - oracle|
+ATOL_MEAN = 2e-3     # attention output, mean |GPU - oracle|
+LSE_ATOL = 2e-2      # log-sum-exp (natural log)
+TIE_REL = 1e-6       # near-tie band, relative to the row's largest |score|
+
+
+def log(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def to_dev(bits: np.ndarray):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def from_dev(t) -> np.ndarray:
+    import torch
+    return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+class OracleCase:
+    """Oracle view of one workload: inputs, permutation, masks and scores."""
+
+    def __init__(self, wl: W.Workload, Q, K, V, anchor_offset: int = 0, heads=None):
+        self.wl = wl
+        self.Q, self.K, self.V = Q, K, V
+        self.heads = list(range(wl.H)) if heads is None else list(heads)
+        self.perm = oracle.hilbert_perm(wl.T, wl.Hg, wl.W)[0] if wl.hilbert else None
+        self.keep, self.S = oracle.select_workload(wl, Q, K, heads=self.heads,
+                                                   anchor_offset=anchor_offset, perm=self.perm)
+
+    def head_inputs(self, b, hi):
+        q = oracle.bf16_to_f64(self.Q[b, hi])
+        k = oracle.bf16_to_f64(self.K[b, hi])
+        v = oracle.bf16_to_f64(self.V[b, hi])
+        if self.perm is not None:
+            q, k, v = (oracle.permute_tokens(x, self.perm) for x in (q, k, v))
+        return q, k, v
+
+    def attention(self, b, hi, q_blocks=None):
+        """Oracle O (float64, in the order blocks are formed in) and lse."""
+        q, k, v = self.head_inputs(b, hi)
+        return oracle.attention_head(q, k, v, self.keep[b, hi], self.wl.block, self.wl.scale,
+                                     comp=self.wl.comp, q_blocks=q_blocks)
+
+
+def mask_report(keep_gpu, case: OracleCase):
+    """Compare masks row by row; returns (mismatched rows, excused rows, failures)."""
+    wl = case.wl
+    bad, excused, failures = 0, 0, []
+    B, nh, nb, _ = keep_gpu.shape
+    diff_rows = np.argwhere(np.any(keep_gpu != case.keep, axis=-1))
+    for b, hi, i in diff_rows:
+        bad += 1
+        g, o = keep_gpu[b, hi, i], case.keep[b, hi, i]
+        s = case.S[b, hi, i].astype(np.float64)
+        tol = TIE_REL * np.max(np.abs(s))
+        only_g, only_o = np.nonzero(g & ~o)[0], np.nonzero(o & ~g)[0]
+        ok = False
+        if wl.rule != "none" and only_g.size + only_o.size > 0:
+            # (a) every swapped pair of blocks is a near tie of the oracle scores
+            if only_g.size and only_o.size:
+                ok = all(abs(s[x] - s[y]) <= tol for x in only_g for y in only_o)
+            if wl.rule == "mass" and not ok:
+                # (b) the cumulative mass at the cutoff sits within 1e-6 Z of tau Z
+                order = oracle.rank_order(s[None, :].astype(np.float32))[0]
+                p = np.exp(s[order] - s[order[0]])
+                cum = np.cumsum(p)
+                m = int(oracle.mass_cutoff(s[None, :].astype(np.float32), wl.mass)[0])
+                thr = float(np.float32(wl.mass)) * cum[-1]
+                near = [abs(cum[m - 1] - thr)]
+                if m >= 2:
+                    near.append(abs(cum[m - 2] - thr))
+                ok = min(near) <= TIE_REL * cum[-1]
+        if ok:
+            excused += 1
+        else:
+            failures.append((int(b), int(hi), int(i), only_g.tolist(), only_o.tolist()))
+    return bad, excused, failures
+
+
+def compare_attention(O_gpu_bits, case: OracleCase, blocks_per_head, lse_gpu=None,
+                      rng_seed=0, heads_sample=None):
+    """Max / mean abs error of the GPU output against the oracle on sampled
+    query blocks (GPU output in raster order)."""
+    wl = case.wl
+    rng = np.random.default_rng(rng_seed)
+    errs, lse_errs, count = [], [], 0
+    hs = range(len(case.heads)) if heads_sample is None else heads_sample
+    for b in range(wl.B):
+        for hi in hs:
+            if blocks_per_head is None or blocks_per_head >= wl.nb:
+                qb = list(range(wl.nb))
+            else:
+                qb = sorted(set([0, wl.nb - 1] + list(rng.choice(wl.nb, blocks_per_head, replace=False))))
+            O, lse = case.attention(b, hi, q_blocks=qb)
+            og = oracle.bf16_to_f64(O_gpu_bits[b, hi])
+            lg = None if lse_gpu is None else lse_gpu[b, hi].astype(np.float64)
+            if case.perm is not None:
+                og = oracle.permute_tokens(og, case.perm)
+                if lg is not None:
+                    lg = lg[case.perm]
+            bounds = oracle.block_bounds(wl.N, wl.block)
+            for i in qb:
+                sl = slice(bounds[i], bounds[i + 1])
+                errs.append(np.abs(og[sl] - O[sl]))
+                count += 1
+                if lg is not None:
+                    finite = np.isfinite(lse[sl])
+                    assert np.array_equal(finite, np.isfinite(lg[sl]))
+                    if finite.any():
+                        lse_errs.append(np.abs(lg[sl][finite] - lse[sl][finite]))
+    e = np.concatenate([x.ravel() for x in errs])
+    le = np.concatenate(lse_errs) if lse_errs else np.zeros(1)
+    return float(e.max()), float(e.mean()), float(le.max()), count

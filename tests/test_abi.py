@@ -1,0 +1,135 @@
+"""The C ABI on a host without a GPU: the library loads, exports every entry
+point the header declares, rejects malformed calls before any HIP call, and
+its host-side Hilbert order equals the oracle's."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import block_sparse_attention_hilbert_amd as sa
+import oracle
+from conftest import ROOT
+
+
+def _header_functions():
+    text = open(os.path.join(ROOT, "include", "sparse_attn.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:sa_status|const char\*)\s+(\w+)\s*\(", text, flags=re.M)))
+
+
+def test_exports_every_declared_symbol():
+    names = _header_functions()
+    assert set(names) == set(sa.EXPORTS)
+    lib = ctypes.CDLL(sa.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+@pytest.mark.parametrize("grid", [(21, 30, 52), (4, 8, 8), (3, 10, 13), (1, 1, 1),
+                                  (126, 30, 52), (5, 1, 9), (21, 45, 80)])
+def test_hilbert_order_matches_oracle(grid):
+    perm, inv = sa.hilbert_perm_build(*grid)
+    operm, oinv = oracle.hilbert_perm(*grid)
+    assert np.array_equal(perm, operm) and np.array_equal(inv, oinv)
+
+
+def _err(fn, *a, **k):
+    with pytest.raises(sa.SparseAttnError) as e:
+        fn(*a, **k)
+    return e.value.status
+
+
+GOOD = dict(B=1, H=2, N=390, d=128, T=3, Hg=10, W=13, block=128)
+
+
+def _prob(**kw):
+    p = dict(GOOD)
+    p.update(kw)
+    return sa.Problem(**p)
+
+
+def test_problem_validation():
+    assert _err(sa.workspace_size, _prob(d=96)) == sa.SA_ERR_UNSUPPORTED
+    assert _err(sa.workspace_size, _prob(block=32)) == sa.SA_ERR_UNSUPPORTED
+    assert _err(sa.workspace_size, _prob(N=391)) == sa.SA_ERR_INVALID_ARG
+    assert _err(sa.workspace_size, _prob(B=0)) == sa.SA_ERR_INVALID_ARG
+    assert _err(sa.workspace_size, _prob(T=0, N=0)) == sa.SA_ERR_INVALID_ARG
+    assert _err(sa.workspace_size, _prob(scale=float("inf"))) == sa.SA_ERR_INVALID_ARG
+    with pytest.raises(sa.SparseAttnError, match="d = 96"):
+        sa.workspace_size(_prob(d=96))
+    n = ctypes.c_size_t(0)
+    assert sa.lib.sparse_attn_workspace_size(None, None, ctypes.byref(n)) == sa.SA_ERR_INVALID_ARG
+    assert b"prob is NULL" in sa.lib.sparse_attn_last_error()
+
+
+def test_spec_validation():
+    p = _prob()
+    bad = [sa.SelectSpec(rule="topk"),                               # no k, no density
+           sa.SelectSpec(rule="topk", topk=[0, 1]),
+           sa.SelectSpec(rule="topk", density=[0.0, 0.5]),
+           sa.SelectSpec(rule="topk", density=[0.5, 1.5]),
+           sa.SelectSpec(rule="mass", mass=0.0),
+           sa.SelectSpec(rule="mass", mass=1.5),
+           sa.SelectSpec(rule="mass", sub_block=48),
+           sa.SelectSpec(rule="mass", sub_block=8),
+           sa.SelectSpec(rule="mass", sub_block=256),
+           sa.SelectSpec(rule="none", window_frames=-2),
+           sa.SelectSpec(rule="none", n_anchors=5),               # nb = 4
+           sa.SelectSpec(rule="none", n_anchors=1, anchor_offset=-1)]
+    for s in bad:
+        assert _err(sa.workspace_size, p, s) == sa.SA_ERR_INVALID_ARG, s
+    big = sa.Problem(1, 1, 4097 * 64, 64, 4097, 1, 64, 64)
+    assert _err(sa.workspace_size, big, sa.SelectSpec(rule="mass")) == sa.SA_ERR_UNSUPPORTED
+    assert sa.workspace_size(big, sa.SelectSpec(rule="none", window_frames=1)) > 0
+
+
+def test_workspace_sizes_are_consistent():
+    p = _prob()
+    a = sa.workspace_size(p, sa.SelectSpec(rule="mass"))
+    b = sa.workspace_size(p, sa.SelectSpec(rule="mass", sub_block=16))
+    c = sa.workspace_size(p, sa.SelectSpec(rule="none", window_frames=1))
+    assert 0 < c < a < b
+    # compensation: bf16 centroid keys and values, [B*H*nb*d] each
+    assert sa.workspace_size(p) == 2 * (1 * 2 * 4 * 128 * 2)
+
+
+def test_select_and_fwd_reject_before_any_launch():
+    """Null / misaligned pointers and small workspaces fail on the host."""
+    p = _prob().c()
+    spec, keep = sa.SelectSpec(rule="mass").c()
+    vp = ctypes.c_void_p
+    fake = vp(1 << 20)                 # never dereferenced: validation fails first
+    odd = vp((1 << 20) + 8)
+    st = sa.lib.sparse_attn_select(ctypes.byref(p), ctypes.byref(spec), None, None, None,
+                                   fake, fake, None, None, None, fake, 1 << 30, None)
+    assert st == sa.SA_ERR_INVALID_ARG
+    st = sa.lib.sparse_attn_select(ctypes.byref(p), ctypes.byref(spec), odd, fake, None,
+                                   fake, fake, None, None, None, fake, 1 << 30, None)
+    assert st == sa.SA_ERR_INVALID_ARG
+    st = sa.lib.sparse_attn_select(ctypes.byref(p), ctypes.byref(spec), fake, fake, None,
+                                   fake, fake, None, None, None, fake, 16, None)
+    assert st == sa.SA_ERR_WORKSPACE
+    st = sa.lib.sparse_attn_select(ctypes.byref(p), ctypes.byref(spec), fake, fake, None,
+                                   fake, fake, None, None, None, vp((1 << 20) + 64), 1 << 30, None)
+    assert st == sa.SA_ERR_WORKSPACE
+    comp, keep2 = sa.SelectSpec(rule="mass", want_comp=True).c()
+    st = sa.lib.sparse_attn_select(ctypes.byref(p), ctypes.byref(comp), fake, fake, None,
+                                   fake, fake, None, None, None, fake, 1 << 30, None)
+    assert st == sa.SA_ERR_INVALID_ARG
+    # fwd
+    st = sa.lib.sparse_attn_fwd(ctypes.byref(p), fake, fake, fake, fake, fake, fake, None,
+                                fake, None, fake, 1 << 30, None)
+    assert st == sa.SA_ERR_INVALID_ARG                     # k_mean without v_sum
+    st = sa.lib.sparse_attn_fwd(ctypes.byref(p), fake, fake, fake, fake, fake, fake, fake,
+                                fake, None, None, 0, None)
+    assert st == sa.SA_ERR_WORKSPACE
+    st = sa.lib.sparse_attn_fwd(ctypes.byref(p), fake, fake, fake, None, fake, None, None,
+                                fake, None, None, 0, None)
+    assert st == sa.SA_ERR_INVALID_ARG
+    # permute: overlap
+    st = sa.lib.hilbert_permute(ctypes.byref(p), fake, vp((1 << 20) + 16), fake, None)
+    assert st == sa.SA_ERR_INVALID_ARG
+    assert sa.lib.hilbert_perm_build(0, 1, 1, None, None) == sa.SA_ERR_INVALID_ARG
+    assert sa.lib.hilbert_perm_build(300, 1, 1, None, None) == sa.SA_ERR_UNSUPPORTED

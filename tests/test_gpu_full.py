@@ -1,0 +1,81 @@
+"""GPU parity at the five full workload sizes, in the launch configuration the
+benchmark times (the same pipeline object and kernels).
+
+For every workload: the full keep mask of every (batch, head, query block)
+against the oracle (bit-exact up to counted near ties), pooled scores and
+compensation statistics bit-exact, and the attention output on sampled query
+blocks (first, last and random ones of sampled heads) against the float64
+oracle given the oracle's mask.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import workloads as W
+from parity_util import (ATOL_MAX, ATOL_MEAN, LSE_ATOL, OracleCase, compare_attention,
+                         from_dev, log, mask_report, to_dev)
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+# sampled heads and query blocks per workload (the oracle computes these rows)
+SAMPLE = {1: (None, None), 2: ([0, 5, 11], 6), 3: ([0, 17, 39], 4), 4: ([0, 11], 4),
+          5: ([0, 6, 11], 6)}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    yield
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
+def test_full_workload(cfg):
+    import block_sparse_attention_hilbert_amd as sa
+    from block_sparse_attention_hilbert_amd.pipeline import BlockSparseAttention
+    wl = W.CONFIGS[cfg]
+    log(f"[full] {wl.name}: B={wl.B} H={wl.H} N={wl.N} d={wl.d} block={wl.block} nb={wl.nb}")
+    Q, K, V = W.make_qkv(wl, progress=None)
+    log(f"[full] {wl.name}: inputs generated")
+    off = W.anchor_offset(wl.seed, 0, wl.nb)
+    pipe = BlockSparseAttention(sa.problem_for(wl), sa.spec_for(wl), hilbert=wl.hilbert,
+                                want_scores=wl.rule != "none", want_lse=True)
+    Qd, Kd, Vd = to_dev(Q), to_dev(K), to_dev(V)
+    O = pipe(Qd, Kd, Vd, anchor_offset=off)
+    torch.cuda.synchronize()
+    log(f"[full] {wl.name}: GPU call done")
+
+    case = OracleCase(wl, Q, K, V, anchor_offset=off)
+    log(f"[full] {wl.name}: oracle selection done")
+    if wl.rule != "none":
+        S = pipe.sel.scores.view(wl.B, wl.H, wl.nb, wl.nb).cpu().numpy()
+        assert np.array_equal(S, case.S), "pooled scores differ"
+    if wl.comp:
+        km = pipe.sel.k_mean.cpu().numpy()
+        vs = pipe.sel.v_sum.cpu().numpy()
+        for h in SAMPLE[cfg][0]:
+            q, k, v = case.head_inputs(0, h)
+            assert np.array_equal(km[0, h], oracle.block_means(k, wl.block))
+            assert np.array_equal(vs[0, h], oracle.block_sums_f32(v, wl.block))
+    keep = pipe.keep_mask()
+    bad, excused, failures = mask_report(keep, case)
+    log(f"[full] {wl.name}: density={keep.mean():.4f} mismatched rows={bad} near-ties={excused}")
+    assert not failures, failures[:5]
+
+    if bad:
+        # rerun attention with the oracle's mask so the outputs are comparable
+        rp, ci = oracle.keep_to_csr(case.keep.reshape(-1, wl.nb))
+        Qp, Kp, Vp = pipe.permute_inputs(Qd, Kd, Vd)
+        pipe.run_fwd(Qp, Kp, Vp, torch.from_numpy(rp).cuda(), torch.from_numpy(ci).cuda())
+        O = pipe.unpermute_output()
+    lse = pipe.lse.cpu().numpy()
+    if wl.hilbert:
+        lse = lse[..., np.argsort(pipe.perm)]
+    heads, nblk = SAMPLE[cfg]
+    emax, emean, lmax, n = compare_attention(from_dev(O), case, nblk, lse_gpu=lse,
+                                             rng_seed=cfg, heads_sample=heads)
+    log(f"[full] {wl.name}: attention on {n} query blocks max={emax:.2e} mean={emean:.2e} "
+        f"lse={lmax:.2e}")
+    assert emax <= ATOL_MAX and emean <= ATOL_MEAN and lmax <= LSE_ATOL

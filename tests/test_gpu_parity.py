@@ -1,0 +1,185 @@
+"""GPU parity: the HIP path (through the C ABI) against the oracle.
+
+Bar (stated here, derived in the design notes):
+* block means, block sums and pooled scores: bit-exact (same fp32 definition);
+* keep masks: bit-exact, except rows excused as near ties (counted, reported);
+* Hilbert order and token reordering: bit-exact;
+* attention output given the oracle's mask: max |err| <= 2e-2 and mean |err|
+  <= 2e-3 against the float64 oracle; lse within 2e-2.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import workloads as W
+from parity_util import (ATOL_MAX, ATOL_MEAN, LSE_ATOL, OracleCase, compare_attention,
+                         from_dev, log, mask_report, to_dev)
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import block_sparse_attention_hilbert_amd as sa  # noqa: F401  (fails loudly if unbuilt)
+    yield
+
+
+def _sa():
+    import block_sparse_attention_hilbert_amd as sa
+    return sa
+
+
+def _pipeline(wl, want_scores=True, want_lse=True):
+    sa = _sa()
+    from block_sparse_attention_hilbert_amd.pipeline import BlockSparseAttention
+    return BlockSparseAttention(sa.problem_for(wl), sa.spec_for(wl), hilbert=wl.hilbert,
+                                want_scores=want_scores, want_lse=want_lse)
+
+
+# small workloads: several tiles and a ragged last block (390 = 3*128 + 6 = 6*64 + 6)
+SMALL = {
+    "mass_d128_b128": W.CONFIGS[2].replace(T=3, Hg=10, W=13, H=3),
+    "topk_d128_b128": W.CONFIGS[3].replace(T=3, Hg=10, W=13, H=4),
+    "topk_diag_d64_b64": W.CONFIGS[1].replace(T=3, Hg=10, W=13, H=2),
+    "window_anchor_d128_b128": W.CONFIGS[4].replace(T=6, Hg=10, W=13, H=2),
+    "hilbert_comp_d128_b64": W.CONFIGS[5].replace(T=3, Hg=10, W=13, H=3),
+    "mass_sub32_d64_b128": W.CONFIGS[2].replace(T=3, Hg=10, W=13, H=2, d=64, sub_block=32),
+    "mass_comp_d64_b128": W.CONFIGS[2].replace(T=5, Hg=7, W=11, H=2, d=64, comp=True, mass=0.5),
+    "topk_d128_b64_wide": W.CONFIGS[3].replace(T=5, Hg=9, W=29, H=2, block=64, density=0.3),
+}
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_small_workload_parity(name):
+    wl = SMALL[name]
+    log(f"[parity] {name}: N={wl.N} nb={wl.nb} H={wl.H} d={wl.d} block={wl.block}")
+    Q, K, V = W.make_qkv(wl)
+    off = W.anchor_offset(wl.seed, 0, wl.nb)
+    case = OracleCase(wl, Q, K, V, anchor_offset=off)
+    pipe = _pipeline(wl)
+    O = pipe(to_dev(Q), to_dev(K), to_dev(V), anchor_offset=off)
+    torch.cuda.synchronize()
+
+    if wl.rule != "none":
+        S = pipe.sel.scores.view(wl.B, wl.H, wl.nb, wl.nb).cpu().numpy()
+        assert np.array_equal(S, case.S), "pooled scores differ"
+    if wl.comp:
+        km = pipe.sel.k_mean.cpu().numpy()
+        vs = pipe.sel.v_sum.cpu().numpy()
+        for b in range(wl.B):
+            for h in range(wl.H):
+                q, k, v = case.head_inputs(b, h)
+                assert np.array_equal(km[b, h], oracle.block_means(k, wl.block))
+                assert np.array_equal(vs[b, h], oracle.block_sums_f32(v, wl.block))
+    keep = pipe.keep_mask()
+    bad, excused, failures = mask_report(keep, case)
+    log(f"[parity] {name}: density={keep.mean():.3f} mismatched rows={bad} near-ties={excused}")
+    assert not failures, failures[:5]
+
+    # attention given the oracle's mask
+    rp, ci = oracle.keep_to_csr(case.keep.reshape(-1, wl.nb))
+    Qp, Kp, Vp = pipe.permute_inputs(to_dev(Q), to_dev(K), to_dev(V))
+    pipe.run_fwd(Qp, Kp, Vp, torch.from_numpy(rp).cuda(), torch.from_numpy(ci).cuda())
+    O = pipe.unpermute_output()
+    lse = pipe.lse.cpu().numpy()
+    if wl.hilbert:
+        lse = lse[..., np.argsort(pipe.perm)]            # back to raster order
+    torch.cuda.synchronize()
+    emax, emean, lmax, n = compare_attention(from_dev(O), case, None, lse_gpu=lse)
+    log(f"[parity] {name}: attention max={emax:.2e} mean={emean:.2e} lse={lmax:.2e}")
+    assert emax <= ATOL_MAX and emean <= ATOL_MEAN and lmax <= LSE_ATOL
+
+
+def test_hilbert_permute_kernels():
+    sa = _sa()
+    wl = W.CONFIGS[5].replace(H=2)
+    prob = sa.problem_for(wl)
+    perm, _ = sa.hilbert_perm_build(wl.T, wl.Hg, wl.W)
+    rng = np.random.default_rng(0)
+    X = rng.integers(0, 1 << 16, size=(1, 2, wl.N, wl.d), dtype=np.uint16)
+    pd = torch.from_numpy(perm).cuda()
+    Xp = sa.hilbert_permute(prob, to_dev(X), pd)
+    Xb = sa.hilbert_unpermute(prob, Xp, pd)
+    torch.cuda.synchronize()
+    assert np.array_equal(from_dev(Xp), oracle.permute_tokens(X, oracle.hilbert_perm(wl.T, wl.Hg, wl.W)[0]))
+    assert np.array_equal(from_dev(Xb), X)
+
+
+def test_edge_single_token_and_empty_rows():
+    sa = _sa()
+    # N = 1: one block of one token; attention to itself is exactly v
+    wl = W.CONFIGS[1].replace(T=1, Hg=1, W=1, H=1, rule="topk", topk=1, diag=False)
+    Q, K, V = W.make_qkv(wl)
+    O = _pipeline(wl)(to_dev(Q), to_dev(K), to_dev(V))
+    torch.cuda.synchronize()
+    assert np.array_equal(from_dev(O), V)
+    # structural rule with no structure: every row empty -> O = 0, lse = -inf
+    wl = W.CONFIGS[4].replace(T=2, Hg=8, W=8, H=2, window_frames=-1, n_anchors=0)
+    Q, K, V = W.make_qkv(wl)
+    pipe = _pipeline(wl)
+    O = pipe(to_dev(Q), to_dev(K), to_dev(V))
+    torch.cuda.synchronize()
+    assert int(pipe.sel.row_ptr[-1]) == 0
+    assert np.all(from_dev(O) == 0) and np.all(np.isneginf(pipe.lse.cpu().numpy()))
+
+
+def test_edge_full_budget_is_dense_attention():
+    """mass = 1 and k = nb keep every block: the result is dense attention."""
+    for wl in (SMALL["mass_d128_b128"].replace(mass=1.0),
+               SMALL["topk_d128_b128"].replace(density=None, topk=10 ** 6)):
+        Q, K, V = W.make_qkv(wl)
+        pipe = _pipeline(wl)
+        O = pipe(to_dev(Q), to_dev(K), to_dev(V))
+        torch.cuda.synchronize()
+        assert pipe.keep_mask().all()
+        case = OracleCase(wl, Q, K, V)
+        assert case.keep.all()
+        emax, emean, _, _ = compare_attention(from_dev(O), case, None)
+        assert emax <= ATOL_MAX and emean <= ATOL_MEAN
+
+
+def test_edge_compensation_limits():
+    """Compensation with every block kept adds nothing; with nothing kept the
+    output is attention over the centroids (oracle, same mask)."""
+    base = SMALL["hilbert_comp_d128_b64"]
+    for wl in (base.replace(head_density=False, density=1.0),
+               base.replace(rule="none", head_density=False, hilbert=False)):
+        Q, K, V = W.make_qkv(wl)
+        case = OracleCase(wl, Q, K, V)
+        pipe = _pipeline(wl)
+        O = pipe(to_dev(Q), to_dev(K), to_dev(V))
+        torch.cuda.synchronize()
+        assert np.array_equal(pipe.keep_mask(), case.keep)
+        emax, emean, _, _ = compare_attention(from_dev(O), case, None)
+        log(f"[parity] comp limit rule={wl.rule}: max={emax:.2e} mean={emean:.2e}")
+        assert emax <= ATOL_MAX and emean <= ATOL_MEAN
+
+
+def test_largest_sort_length():
+    """nb = 4096 (the largest scored row) with the mass rule and sub-blocks."""
+    wl = W.CONFIGS[2].replace(T=64, Hg=64, W=64, H=1, block=64, d=64, sub_block=32, mass=0.5)
+    assert wl.nb == 4096
+    Q, K, V = W.make_qkv(wl)
+    case = OracleCase(wl, Q, K, V)
+    pipe = _pipeline(wl, want_lse=False)
+    pipe.run_select(to_dev(Q), to_dev(K), None)
+    torch.cuda.synchronize()
+    S = pipe.sel.scores.view(1, 1, wl.nb, wl.nb).cpu().numpy()
+    assert np.array_equal(S, case.S)
+    bad, excused, failures = mask_report(pipe.keep_mask(), case)
+    log(f"[parity] nb=4096: mismatched rows={bad} near-ties={excused}")
+    assert not failures
+
+
+def test_determinism():
+    wl = SMALL["hilbert_comp_d128_b64"]
+    Q, K, V = (to_dev(x) for x in W.make_qkv(wl))
+    pipe = _pipeline(wl)
+    a = pipe(Q, K, V).clone()
+    b = pipe(Q, K, V).clone()
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))

@@ -38,8 +38,10 @@ stream per (seed, batch, head) so any head can be generated alone):
 """
 from __future__ import annotations
 
+import concurrent.futures
 import dataclasses
 import math
+import threading
 from typing import Optional, Tuple
 
 import numpy as np
@@ -169,17 +171,21 @@ def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
 # generators
 # ---------------------------------------------------------------------------
 
-_SCRATCH = {}
+_TLS = threading.local()
 
 
 def _scratch(name: str, shape, dtype) -> np.ndarray:
-    """Reused work buffers: first-touch page faults dominate fresh allocations."""
+    """Reused per-thread work buffers: first-touch page faults dominate fresh
+    allocations of large arrays."""
+    cache = getattr(_TLS, "cache", None)
+    if cache is None:
+        cache = _TLS.cache = {}
     key = (name, tuple(shape), np.dtype(dtype).str)
-    buf = _SCRATCH.get(key)
+    buf = cache.get(key)
     if buf is None:
-        if len(_SCRATCH) > 16:
-            _SCRATCH.clear()
-        buf = _SCRATCH[key] = np.empty(shape, dtype)
+        if len(cache) > 16:
+            cache.clear()
+        buf = cache[key] = np.empty(shape, dtype)
     return buf
 
 
@@ -207,15 +213,21 @@ def _smooth_field(rng: np.random.Generator, T: int, Hg: int, W: int, d: int,
     g1 = coef @ ex.T                                    # [d, ft, fy, W]
     g2 = np.einsum("cabx,yb->caxy", g1, ey)             # [d, ft, W, Hg]
     g2 = g2.transpose(1, 3, 2, 0).reshape(nf, Hg * W * d)  # [ft, (y, x, c)]
-    # Re(et @ g2) = et.re @ g2.re - et.im @ g2.im, into reused buffers
-    acc = _scratch("field", (T, Hg * W * d), np.float64)
-    tmp = _scratch("field_tmp", (T, Hg * W * d), np.float64)
-    np.matmul(et.real, np.ascontiguousarray(g2.real), out=acc)
-    np.matmul(et.imag, np.ascontiguousarray(g2.imag), out=tmp)
-    np.subtract(acc, tmp, out=acc)
-    out = _scratch("field32", (T * Hg * W, d), np.float32)
-    np.copyto(out, acc.reshape(T * Hg * W, d), casting="same_kind")
-    return out
+    # Re(et @ g2) = et.re @ g2.re - et.im @ g2.im, a few frames at a time
+    g2r = np.ascontiguousarray(g2.real)
+    g2i = np.ascontiguousarray(g2.imag)
+    out = _scratch("field32", (T, Hg * W * d), np.float32)
+    step = 8
+    acc = _scratch("field", (step, Hg * W * d), np.float64)
+    tmp = _scratch("field_tmp", (step, Hg * W * d), np.float64)
+    for t0 in range(0, T, step):
+        t1 = min(T, t0 + step)
+        a, b = acc[: t1 - t0], tmp[: t1 - t0]
+        np.matmul(et.real[t0:t1], g2r, out=a)
+        np.matmul(et.imag[t0:t1], g2i, out=b)
+        np.subtract(a, b, out=a)
+        np.copyto(out[t0:t1], a, casting="same_kind")
+    return out.reshape(T * Hg * W, d)
 
 
 def make_head(wl: Workload, b: int, h: int, alpha: float = None, out=None):
@@ -249,14 +261,31 @@ def make_head(wl: Workload, b: int, h: int, alpha: float = None, out=None):
     return out
 
 
-def make_qkv(wl: Workload, heads=None, alpha: float = None):
-    """Q, K, V as bf16 bits [B, len(heads), N, d] (all heads by default)."""
+def make_qkv(wl: Workload, heads=None, alpha: float = None, workers: int = 8,
+             progress=None):
+    """Q, K, V as bf16 bits [B, len(heads), N, d] (all heads by default).
+
+    Heads are generated on ``workers`` threads; every head has its own random
+    stream, so the result does not depend on the thread count.  ``progress``,
+    if given, is called with a message after every head.
+    """
     heads = list(range(wl.H)) if heads is None else list(heads)
     shape = (wl.B, len(heads), wl.N, wl.d)
     Q = np.empty(shape, np.uint16)
     K = np.empty(shape, np.uint16)
     V = np.empty(shape, np.uint16)
-    for b in range(wl.B):
-        for i, h in enumerate(heads):
-            make_head(wl, b, h, alpha, out=(Q[b, i], K[b, i], V[b, i]))
+    jobs = [(b, i, h) for b in range(wl.B) for i, h in enumerate(heads)]
+
+    def one(job):
+        b, i, h = job
+        make_head(wl, b, h, alpha, out=(Q[b, i], K[b, i], V[b, i]))
+        if progress is not None:
+            progress(f"generated {wl.name} b={b} h={h}")
+
+    if workers <= 1 or len(jobs) == 1:
+        for j in jobs:
+            one(j)
+    else:
+        with concurrent.futures.ThreadPoolExecutor(min(workers, len(jobs))) as ex:
+            list(ex.map(one, jobs))
     return Q, K, V
