@@ -1,0 +1,218 @@
+#!/usr/bin/env python3
+"""Benchmark of one block-sparse attention call on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2]
+
+A step is one full call of the hot path on the workload's synthetic inputs
+(already resident in HBM): Hilbert reordering when the workload uses it,
+block selection (pooling, scores, keep lists), block-sparse attention with
+compensation when the workload uses it, inverse reordering.  The default
+workload is the 1.3B-sized video layer (B=1, H=12, N=32760 tokens of a
+21x30x52 latent grid, d=128, 128-token blocks, cumulative-mass 0.9 rule).
+
+Printed: one JSON line.  ``value`` is the effective attention throughput in
+TFLOP/s over the kept blocks (4*d*sum over kept block pairs of n_i*n_j)
+divided by the whole step time; ``ms_per_step`` is that step time.
+``roofline`` reports the attention kernel alone against the bf16 matrix-core
+peak, timed with HIP events on the stream it is launched on.
+``cpu_baseline`` times the CPU oracle on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16 matrix-core peak (256 CU x 2.4 GHz x 4096)
+PEAK_HBM_GBS = 8000.0
+ATTN_KERNEL = "k_bsattn_fwd"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_bsattn_fwd_wan13b_traffic.md")
+ATTN_SOURCE = os.path.join(ROOT, "block_sparse_attention_hilbert_amd", "csrc", "k_attn.hip")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    with open(ATTN_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def read_traffic(workload: str):
+    """HBM bytes per attention launch from the committed counter summary, or
+    None when it is missing, for another workload or for older kernel source."""
+    try:
+        text = open(TRAFFIC_FILE).read()
+    except OSError:
+        return None
+    fields = dict(re.findall(r"^- (\w+): (\S+)", text, flags=re.M))
+    if fields.get("workload") != workload or fields.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    try:
+        return float(fields["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(wl, Q, K, V, budget_s: float = 12.0):
+    """The oracle (as it stands) on a bounded sample: selection of head 0, then
+    float64 attention of head 0's query blocks until the time budget is spent.
+    Reported as kept-block TFLOP/s of the sample."""
+    import oracle
+    import workloads as W
+    from threadpoolctl import threadpool_info
+
+    t0 = time.perf_counter()
+    perm = oracle.hilbert_perm(wl.T, wl.Hg, wl.W)[0] if wl.hilbert else None
+    off = W.anchor_offset(wl.seed, 0, wl.nb)
+    keep, _ = oracle.select_workload(wl, Q[:, :1], K[:, :1], heads=[0], anchor_offset=off,
+                                     perm=perm)
+    q, k, v = (oracle.bf16_to_f64(x[0, 0]) for x in (Q, K, V))
+    if perm is not None:
+        q, k, v = (oracle.permute_tokens(x, perm) for x in (q, k, v))
+    n = np.diff(oracle.block_bounds(wl.N, wl.block)).astype(np.float64)
+    flops = 0.0
+    done = 0
+    order = np.random.default_rng(0).permutation(wl.nb)
+    for i in order:
+        oracle.attention_head(q, k, v, keep[0, 0], wl.block, wl.scale, comp=wl.comp,
+                              q_blocks=[int(i)])
+        flops += 4.0 * wl.d * n[i] * float((keep[0, 0, i] * n).sum())
+        done += 1
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"head 0 of {wl.H}: full selection + float64 attention of {done} of "
+                      f"{wl.nb} query blocks ({dt:.1f} s wall)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", type=int, default=2, help="workload number 1..5")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="only run a plain 1 GiB device copy (counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the path is data-parallel per head and query block; see the design notes)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import block_sparse_attention_hilbert_amd as sa
+    from block_sparse_attention_hilbert_amd.pipeline import BlockSparseAttention
+    import workloads as W
+
+    if args.calib_copy:
+        n = 1 << 30
+        a = torch.empty(n, dtype=torch.uint8, device="cuda")
+        b = torch.empty_like(a)
+        a.fill_(1)
+        for _ in range(5):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"calib_copy_bytes": n, "launches": 5}))
+        return
+
+    wl = W.CONFIGS[args.config]
+    log(f"[bench] workload {wl.name}: generating inputs")
+    Q, K, V = W.make_qkv(wl)
+
+    def dev(x):
+        return torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).cuda()
+
+    Qd, Kd, Vd = dev(Q), dev(K), dev(V)
+    pipe = BlockSparseAttention(sa.problem_for(wl), sa.spec_for(wl), hilbert=wl.hilbert)
+    stream = torch.cuda.current_stream()
+
+    def step(call_idx, ev):
+        off = W.anchor_offset(wl.seed, call_idx, wl.nb) if wl.n_anchors else None
+        Qp, Kp, Vp = pipe.permute_inputs(Qd, Kd, Vd)
+        ev[0].record(stream)
+        pipe.run_select(Qp, Kp, Vp, off)
+        ev[1].record(stream)
+        pipe.run_fwd(Qp, Kp, Vp)
+        ev[2].record(stream)
+        pipe.unpermute_output()
+
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)]
+              for _ in range(max(args.steps, 1))]
+    log(f"[bench] warmup {args.warmup}")
+    for i in range(args.warmup):
+        step(i, events[0])
+    torch.cuda.synchronize()
+
+    # timed region: exactly K back-to-back calls, synchronised on both sides;
+    # HIP events on the launch stream bracket selection and attention per call
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + i, events[i])
+    torch.cuda.synchronize()
+    step_s = (time.perf_counter() - t0) / args.steps
+    sel_ms = [e[0].elapsed_time(e[1]) for e in events[: args.steps]]
+    fwd_ms = [e[1].elapsed_time(e[2]) for e in events[: args.steps]]
+    log(f"[bench] {args.steps} steps: {step_s * 1e3:.3f} ms/step")
+    # kept work of the last call's mask (only the rotating anchors change it
+    # from call to call)
+    keep = pipe.keep_mask()
+    n = np.diff(np.append(np.arange(wl.nb) * wl.block, wl.N)).astype(np.float64)
+    F_kept = 4.0 * wl.d * float((keep * np.outer(n, n)).sum())
+
+    fwd_s = float(np.mean(fwd_ms)) / 1e3
+    sel_s = float(np.mean(sel_ms)) / 1e3
+    achieved = F_kept / fwd_s / 1e12
+    traffic = read_traffic(wl.name)
+    out = {
+        "metric": "ms/attn call + effective TFLOP/s (kept blocks) at N=32760, H=12, d=128, 1 GPU",
+        "value": round(F_kept / step_s / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_s * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded smooth-field video-latent Q/K, N(0,1) V)",
+        "config": {"workload": wl.name, "B": wl.B, "H": wl.H, "N": wl.N, "d": wl.d,
+                   "latent_grid": [wl.T, wl.Hg, wl.W], "block": wl.block, "rule": wl.rule,
+                   "mass": wl.mass if wl.rule == "mass" else None,
+                   "density_kept": round(float(keep.mean()), 4),
+                   "hilbert": wl.hilbert, "compensation": wl.comp,
+                   "parallelism": "single GPU"},
+        "ms_select": round(sel_s * 1e3, 4),
+        "ms_attention": round(fwd_s * 1e3, 4),
+        "select_over_attention": round(sel_s / fwd_s, 4),
+        "kept_tflop_per_call": round(F_kept / 1e12, 4),
+        "roofline": {"bound": "mfma", "kernel": ATTN_KERNEL, "achieved": round(achieved, 2),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic},
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] cpu baseline (oracle, bounded sample)")
+        out["cpu_baseline"] = cpu_baseline(wl, Q, K, V)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

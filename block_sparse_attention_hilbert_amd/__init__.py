@@ -239,7 +239,7 @@ def fwd(prob: Problem, Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor,
     O = torch.empty_like(Q) if O is None else O
     if want_lse and lse is None:
         lse = torch.empty(prob.B, prob.H, prob.N, dtype=torch.float32, device=Q.device)
-    if k_mean is not None and workspace is None:
+    if workspace is None:
         workspace = alloc_workspace(workspace_size(prob, None), Q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib.sparse_attn_fwd(ctypes.byref(prob.c()), _ptr(Q), _ptr(K), _ptr(V), _ptr(row_ptr),

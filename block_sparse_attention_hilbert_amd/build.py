@@ -33,10 +33,17 @@ def common_flags():
             "-I", os.path.join(ROOT, "include")]
 
 
+# Per-source extra flags.  The attention kernel keeps its softmax operands in
+# VGPRs: the matrix-core accumulators of S are read by VALU code every tile, so
+# the VGPR form of the MFMA instructions avoids AGPR<->VGPR copies.
+EXTRA = {"k_attn.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=true"]}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
     lang = ["-x", "hip"] if src.endswith(".hip") else []
-    cmd = [_hipcc()] + common_flags() + lang + ["-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = ([_hipcc()] + common_flags() + EXTRA.get(src, []) + lang +
+           ["-c", os.path.join(CSRC, src), "-o", obj])
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")

@@ -6,18 +6,28 @@
 // weight = the block's token count (a logit bias of log n_j).
 //
 // Mapping onto CDNA4
-//   * one workgroup = one (batch, head, query block); wave w owns 32 queries.
-//   * S^T = K Q^T on v_mfma_f32_32x32x16_bf16: the B operand (Q^T) stays in
-//     registers for the whole row, the A operand (K) is read from LDS.  In the
+//   * one workgroup = one (batch, head, query block).  Wave (qg, kh) owns 64
+//     queries (query group qg) and one half of the keys of every KV tile (kh);
+//     the two key halves are merged once at the end, like two KV splits.
+//     64 queries per wave means every K / V operand read from LDS feeds two
+//     matrix-core instructions, halving LDS traffic per flop.
+//   * S^T = K Q^T on v_mfma_f32_32x32x16_bf16: Q^T (B operand) stays in
+//     registers for the whole row, K (A operand) is read from LDS.  In the
 //     32x32 accumulator layout a lane holds one query column, so the softmax
-//     statistics of a query are lane-local; the two lane halves that share a
-//     query exchange their maximum once per tile (xor 32).
+//     statistics are lane-local; the two lane halves sharing a query exchange
+//     their maximum once per tile (xor 32).
 //   * O^T = V^T P^T on the same instruction: P goes from the S^T accumulators
-//     straight into the B operand.  K rows are loaded in an order that swaps
-//     bits 2 and 3 of the row index inside every 16 rows, which makes the 8
-//     probabilities a lane holds per k-step 8 consecutive keys; V is stored
-//     transposed in LDS so those 8 keys are one 16-byte LDS read.
-//   * online softmax in the log2 domain (scale*log2(e) folded into one FMA).
+//     into the B operand.  K rows are read in an order that swaps bits 2 and 3
+//     of the row index, which makes the 8 probabilities a lane holds per
+//     k-step 8 consecutive keys; V is pre-transposed per block in HBM (a cheap
+//     bandwidth-bound pass) so those 8 keys are one 16-byte LDS read.
+//   * K and V^T tiles move HBM -> LDS with global_load_lds_dwordx4 (no
+//     register staging), double-buffered: tile t+1 is in flight while tile t
+//     is computed.  Tiles use an XOR swizzle of their 16-byte chunks so that
+//     the row-strided operand reads are bank-conflict free.
+//   * online softmax in the log2 domain with lazy rescaling: the running
+//     maximum only moves (and O, l are only rescaled) when a tile raises it by
+//     more than 2^8.
 //   * blockIdx -> row remap keeps consecutive query blocks of a head on one
 //     XCD (workgroups are dealt round-robin to the 8 XCDs), so the K/V blocks
 //     they share are served from that XCD's L2.
@@ -30,9 +40,12 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) const void gbl_void_t;
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kLazy = 8.0f;      // log2 headroom before the running max moves
 
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
     uint32_t u = __float_as_uint(f);
@@ -50,153 +63,61 @@ __device__ __forceinline__ int swap23(int r) {
 struct FwdArgs {
     const uint16_t* Q;
     const uint16_t* K;
-    const uint16_t* V;
+    const uint16_t* Vt;      // [BH][nb][D][BLK] transposed V blocks (zero-padded keys)
     const int32_t* row_ptr;
     const int32_t* col_idx;
-    const uint16_t* kbar;    // [BH][nb][D] bf16 centroid keys (compensation) or null
-    const uint16_t* vbar;    // [BH][nb][D] bf16 centroid values
+    const uint16_t* kbar;    // [BH][nb][D] centroid keys (compensation) or null
+    const uint16_t* vbart;   // [BH][ntc][D][BLK] transposed centroid values
     uint16_t* O;
     float* lse;
-    int32_t N, nb;
+    int32_t N, nb, ntc;
     int64_t rows;
     float c;                 // scale * log2(e)
 };
 
 template <int D, int BLK>
-struct Lds {
-    static constexpr int KST = D + 8;        // bf16 per K row (+16 B: bank shift)
-    static constexpr int VST = BLK + 8;      // bf16 per V^T row
-    static constexpr int K_BYTES = BLK * KST * 2;
-    static constexpr int V_BYTES = D * VST * 2;
-    static constexpr int BIAS_BYTES = BLK * 4;
-    static constexpr int BASE = K_BYTES + V_BYTES + BIAS_BYTES;
+struct Cfg {
+    static constexpr int NWQ = BLK / 64;            // query groups of 64
+    static constexpr int NW = NWQ * 2;              // x 2 key halves
+    static constexpr int NT = NW * 64;
+    static constexpr int KH = BLK / 2;              // keys per half
+    static constexpr int KTW = KH / 32;             // 32-key MFMA tiles per wave
+    static constexpr int KRB = D * 2;               // bytes per K row
+    static constexpr int VRB = BLK * 2;             // bytes per V^T row
+    static constexpr int KCH = KRB / 16;            // 16-byte chunks per K row
+    static constexpr int VCH = VRB / 16;
+    static constexpr int K_BYTES = BLK * KRB;
+    static constexpr int V_BYTES = D * VRB;
+    static constexpr int STAGE = K_BYTES + V_BYTES + BLK * 4;   // + bias
+    static constexpr int MERGE = NWQ * (2 * (D / 32) * 64 * 16 * 4 + 2 * 2 * 32 * 4);
+    static constexpr int BASE = 2 * STAGE > MERGE ? 2 * STAGE : MERGE;
 };
 
-// Stage BLK key rows and the matching value rows (transposed) into LDS.
-// Rows r >= nvalid are zero.  src_row(r) gives the global row of tile row r.
-template <int D, int BLK, int NT, typename RowFn>
-__device__ __forceinline__ void stage_tile(const uint16_t* __restrict__ Kg,
-                                           const uint16_t* __restrict__ Vg, int nvalid,
-                                           RowFn src_row, uint16_t* Ks, uint16_t* Vt) {
-    using L = Lds<D, BLK>;
-    constexpr int CH = D / 8;
-    const int tid = threadIdx.x;
-    // K: row-major, 16-byte chunks
+// Copy ROWS rows of RB bytes (row r at row_addr(r)) into an LDS tile whose
+// 16-byte chunks are XOR-swizzled by the row index.  Every wave instruction
+// moves 1 KB: lane L lands at byte offset L*16 of the wave's slice.
+template <int ROWS, int RB, int NW, typename RowAddr>
+__device__ __forceinline__ void dma_tile(unsigned char* tile, int wave, int lane,
+                                         RowAddr row_addr) {
+    constexpr int CH = RB / 16;
+    constexpr int INSTR = ROWS * RB / (1024 * NW);
+    static_assert(INSTR * 1024 * NW == ROWS * RB, "tile must be a whole number of wave slices");
 #pragma unroll
-    for (int c = tid; c < BLK * CH; c += NT) {
-        const int r = c / CH, ch = c % CH;
-        uint4 v = make_uint4(0, 0, 0, 0);
-        if (r < nvalid) v = *reinterpret_cast<const uint4*>(Kg + src_row(r) * D + ch * 8);
-        *reinterpret_cast<uint4*>(Ks + r * L::KST + ch * 8) = v;
+    for (int n = 0; n < INSTR; ++n) {
+        const int off = (n * NW + wave) * 1024;
+        const int lin = off + lane * 16;
+        const int row = lin / RB;
+        const int chunk = ((lin % RB) / 16) ^ (row & (CH - 1));
+        const unsigned char* g = row_addr(row) + chunk * 16;
+        __builtin_amdgcn_global_load_lds((gbl_void_t*)g, (lds_void_t*)(tile + off), 16, 0, 0);
     }
-    // V: 8 keys x 8 channels per thread, transposed in registers
-#pragma unroll
-    for (int g = tid; g < (BLK / 8) * CH; g += NT) {
-        const int dg = g % CH, kg = g / CH;
-        uint32_t w[8][4];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            uint4 v = make_uint4(0, 0, 0, 0);
-            const int r = kg * 8 + e;
-            if (r < nvalid) v = *reinterpret_cast<const uint4*>(Vg + src_row(r) * D + dg * 8);
-            w[e][0] = v.x; w[e][1] = v.y; w[e][2] = v.z; w[e][3] = v.w;
-        }
-#pragma unroll
-        for (int c = 0; c < 8; ++c) {
-            uint32_t o[4];
-#pragma unroll
-            for (int p = 0; p < 4; ++p) {
-                const uint32_t x = w[2 * p][c >> 1], y = w[2 * p + 1][c >> 1];
-                o[p] = (c & 1) ? ((x >> 16) | (y & 0xFFFF0000u)) : ((x & 0xFFFFu) | (y << 16));
-            }
-            *reinterpret_cast<uint4*>(Vt + (dg * 8 + c) * L::VST + kg * 8) =
-                make_uint4(o[0], o[1], o[2], o[3]);
-        }
-    }
-}
-
-// One KV tile of the online softmax for the 32 queries of this wave.
-template <int D, int BLK>
-__device__ __forceinline__ void attend_tile(const uint16_t* Ks, const uint16_t* Vt,
-                                            const float* bias, bool use_bias,
-                                            const bf16x8 (&qf)[D / 16], f32x16 (&oacc)[D / 32],
-                                            float& m_run, float& l_run, float c) {
-    using L = Lds<D, BLK>;
-    constexpr int KT = BLK / 32;
-    const int lane = threadIdx.x & 63;
-    const int r32 = lane & 31, h = lane >> 5;
-    const int krow = swap23(r32);
-
-    f32x16 s[KT];
-#pragma unroll
-    for (int kt = 0; kt < KT; ++kt) {
-        f32x16 acc = {};
-#pragma unroll
-        for (int st = 0; st < D / 16; ++st) {
-            const bf16x8 a = as_bf16x8(
-                *reinterpret_cast<const uint4*>(Ks + (kt * 32 + krow) * L::KST + st * 16 + h * 8));
-            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[st], acc, 0, 0, 0);
-        }
-        s[kt] = acc;
-    }
-
-    // logits in the log2 domain and the tile maximum of this query
-    float mx = -INFINITY;
-#pragma unroll
-    for (int kt = 0; kt < KT; ++kt)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            float t = s[kt][i] * c;
-            if (use_bias) t += bias[kt * 32 + swap23(8 * (i >> 2) + 4 * h + (i & 3))];
-            s[kt][i] = t;
-            mx = fmaxf(mx, t);
-        }
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float m_new = fmaxf(m_run, mx);
-    const float base = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f(m_run - base);
-    float sum = 0.f;
-#pragma unroll
-    for (int kt = 0; kt < KT; ++kt)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const float p = __builtin_amdgcn_exp2f(s[kt][i] - base);
-            s[kt][i] = p;
-            sum += p;
-        }
-    l_run = l_run * alpha + sum;
-    m_run = m_new;
-#pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt) oacc[dt] *= alpha;
-
-    // O^T += V^T P^T
-#pragma unroll
-    for (int kt = 0; kt < KT; ++kt)
-#pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) {
-            bf16x8 pb;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) pb[e] = (__bf16)s[kt][8 * s2 + e];
-#pragma unroll
-            for (int dt = 0; dt < D / 32; ++dt) {
-                const bf16x8 a = as_bf16x8(*reinterpret_cast<const uint4*>(
-                    Vt + (dt * 32 + r32) * L::VST + kt * 32 + 16 * s2 + 8 * h));
-                oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, oacc[dt], 0, 0, 0);
-            }
-        }
 }
 
 template <int D, int BLK, bool COMP>
 __global__ __launch_bounds__(BLK * 2) void k_bsattn_fwd(FwdArgs a) {
-    using L = Lds<D, BLK>;
-    constexpr int NT = BLK * 2;
+    using C = Cfg<D, BLK>;
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-    uint16_t* Ks = reinterpret_cast<uint16_t*>(smem);
-    uint16_t* Vt = reinterpret_cast<uint16_t*>(smem + L::K_BYTES);
-    float* bias = reinterpret_cast<float*>(smem + L::K_BYTES + L::V_BYTES);
-    int16_t* skip = reinterpret_cast<int16_t*>(smem + L::BASE);   // COMP: [nb]
-    unsigned char* kept = smem + L::BASE + 2 * (size_t)a.nb;        // COMP: [nb]
-    __shared__ int s_nskip;
+    unsigned char* kept = smem + C::BASE;            // COMP: [nb] flags
 
     // XCD-aware remap: the workgroups dealt to one XCD take consecutive rows
     const int64_t G = a.rows;
@@ -206,146 +127,356 @@ __global__ __launch_bounds__(BLK * 2) void k_bsattn_fwd(FwdArgs a) {
 
     const int i = (int)(row % a.nb);
     const int64_t bh = row / a.nb;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int qg = wave >> 1, kh = wave & 1;
     const int r32 = lane & 31, h = lane >> 5;
     const int64_t head_off = bh * (int64_t)a.N * D;
-    const uint16_t* Kh = a.K + head_off;
-    const uint16_t* Vh = a.V + head_off;
+    const unsigned char* Kh = reinterpret_cast<const unsigned char*>(a.K + head_off);
+    const unsigned char* Vth =
+        reinterpret_cast<const unsigned char*>(a.Vt + bh * (int64_t)a.nb * D * BLK);
+    const int last_n = a.N - (a.nb - 1) * BLK;
 
-    // this lane's query and its Q^T fragments (B operand)
-    const int q_local = wave * 32 + r32;
-    const int qn = i * BLK + q_local;
-    bf16x8 qf[D / 16];
+    // Q^T fragments (B operand) of this wave's 64 queries
+    bf16x8 qf[2][D / 16];
 #pragma unroll
-    for (int st = 0; st < D / 16; ++st) {
-        uint4 v = make_uint4(0, 0, 0, 0);
-        if (qn < a.N) v = *reinterpret_cast<const uint4*>(a.Q + head_off + (int64_t)qn * D + st * 16 + h * 8);
-        qf[st] = as_bf16x8(v);
+    for (int nt = 0; nt < 2; ++nt) {
+        const int qn = i * BLK + qg * 64 + nt * 32 + r32;
+#pragma unroll
+        for (int st = 0; st < D / 16; ++st) {
+            uint4 v = make_uint4(0, 0, 0, 0);
+            if (qn < a.N)
+                v = *reinterpret_cast<const uint4*>(a.Q + head_off + (int64_t)qn * D + st * 16 + h * 8);
+            qf[nt][st] = as_bf16x8(v);
+        }
     }
-
-    f32x16 oacc[D / 32];
-#pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt) oacc[dt] = f32x16{};
-    float m_run = -INFINITY, l_run = 0.f;
 
     const int beg = a.row_ptr[row], end = a.row_ptr[row + 1];
-    const int last_n = a.N - (a.nb - 1) * BLK;
-    for (int e = beg; e < end; ++e) {
-        const int j = a.col_idx[e];
-        if ((unsigned)j >= (unsigned)a.nb) continue;
-        const int nvalid = j == a.nb - 1 ? last_n : BLK;
-        __syncthreads();
-        stage_tile<D, BLK, NT>(Kh, Vh, nvalid, [&](int r) { return (int64_t)j * BLK + r; }, Ks, Vt);
-        const bool partial = nvalid < BLK;
-        if (partial)
-            for (int r = tid; r < BLK; r += NT) bias[r] = r < nvalid ? 0.f : -INFINITY;
-        __syncthreads();
-        attend_tile<D, BLK>(Ks, Vt, bias, partial, qf, oacc, m_run, l_run, a.c);
-    }
-
+    const int nk = end - beg;
+    const int T = nk + (COMP ? a.ntc : 0);
     if constexpr (COMP) {
-        // complement of the kept list, ascending (one wave, ballot compaction)
+        for (int j = tid; j < a.nb; j += C::NT) kept[j] = 0;
         __syncthreads();
-        for (int j = tid; j < a.nb; j += NT) kept[j] = 0;
-        __syncthreads();
-        for (int e = beg + tid; e < end; e += NT) {
+        for (int e = beg + tid; e < end; e += C::NT) {
             const int j = a.col_idx[e];
             if ((unsigned)j < (unsigned)a.nb) kept[j] = 1;
         }
         __syncthreads();
-        if (wave == 0) {
-            int cnt = 0;
-            for (int j0 = 0; j0 < a.nb; j0 += 64) {
-                const int j = j0 + lane;
-                const bool sk = j < a.nb && !kept[j];
-                const unsigned long long m = __ballot(sk);
-                const int pos = __popcll(m & ((1ull << lane) - 1ull));
-                if (sk) skip[cnt + pos] = (int16_t)j;
-                cnt += __popcll(m);
+    }
+
+    // Issues the HBM -> LDS copies of tile t into stage buffer b and writes its
+    // key bias (0 / -inf for a short last block; log2 n_j / -inf for centroids).
+    auto issue = [&](int t, int b) {
+        unsigned char* st = smem + b * C::STAGE;
+        float* bias = reinterpret_cast<float*>(st + C::K_BYTES + C::V_BYTES);
+        if (!COMP || t < nk) {
+            int j = a.col_idx[beg + t];
+            j = j < 0 ? 0 : (j >= a.nb ? a.nb - 1 : j);
+            const int nval = j == a.nb - 1 ? last_n : BLK;
+            const unsigned char* kb = Kh + (int64_t)j * BLK * C::KRB;
+            dma_tile<BLK, C::KRB, C::NW>(st, wave, lane, [&](int r) {
+                return kb + (int64_t)(r < nval ? r : nval - 1) * C::KRB;
+            });
+            const unsigned char* vb = Vth + (int64_t)j * D * C::VRB;
+            dma_tile<D, C::VRB, C::NW>(st + C::K_BYTES, wave, lane,
+                                       [&](int r) { return vb + (int64_t)r * C::VRB; });
+            if (nval < BLK)
+                for (int r = tid; r < BLK; r += C::NT) bias[r] = r < nval ? 0.f : -INFINITY;
+        } else {
+            const int tc = t - nk;
+            const int j0 = tc * BLK;
+            const int nval = a.nb - j0 < BLK ? a.nb - j0 : BLK;
+            const unsigned char* kb =
+                reinterpret_cast<const unsigned char*>(a.kbar + (bh * a.nb + j0) * (int64_t)D);
+            dma_tile<BLK, C::KRB, C::NW>(st, wave, lane, [&](int r) {
+                return kb + (int64_t)(r < nval ? r : nval - 1) * C::KRB;
+            });
+            const unsigned char* vb = reinterpret_cast<const unsigned char*>(
+                a.vbart + (bh * a.ntc + tc) * (int64_t)D * BLK);
+            dma_tile<D, C::VRB, C::NW>(st + C::K_BYTES, wave, lane,
+                                       [&](int r) { return vb + (int64_t)r * C::VRB; });
+            for (int r = tid; r < BLK; r += C::NT) {
+                const int j = j0 + r;
+                float bv = -INFINITY;
+                if (j < a.nb && !kept[j]) bv = __log2f((float)(j == a.nb - 1 ? last_n : BLK));
+                bias[r] = bv;
             }
-            if (lane == 0) s_nskip = cnt;
         }
+    };
+    auto biased = [&](int t) {
+        if (COMP && t >= nk) return true;
+        int j = a.col_idx[beg + t];
+        return j >= a.nb - 1 && last_n < BLK;
+    };
+
+    f32x16 oacc[D / 32][2];
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) oacc[dt][nt] = f32x16{};
+    float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
+
+    if (T > 0) issue(0, 0);
+    for (int t = 0; t < T; ++t) {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
-        const int nskip = s_nskip;
-        const uint16_t* kb = a.kbar + bh * (int64_t)a.nb * D;
-        const uint16_t* vb = a.vbar + bh * (int64_t)a.nb * D;
-        for (int t0 = 0; t0 < nskip; t0 += BLK) {
-            const int nvalid = min(BLK, nskip - t0);
-            __syncthreads();
-            stage_tile<D, BLK, NT>(kb, vb, nvalid, [&](int r) { return (int64_t)skip[t0 + r]; },
-                                   Ks, Vt);
-            for (int r = tid; r < BLK; r += NT) {
-                float b = -INFINITY;
-                if (r < nvalid) {
-                    const int j = skip[t0 + r];
-                    b = __log2f((float)(j == a.nb - 1 ? last_n : BLK));
-                }
-                bias[r] = b;
+        if (t + 1 < T) issue(t + 1, (t + 1) & 1);
+        const unsigned char* Ks = smem + (t & 1) * C::STAGE;
+        const unsigned char* Vs = Ks + C::K_BYTES;
+        const float* bias = reinterpret_cast<const float*>(Vs + C::V_BYTES);
+        const bool use_bias = biased(t);
+
+        // S^T = K Q^T for this wave's key half
+        f32x16 s[C::KTW][2];
+#pragma unroll
+        for (int kt = 0; kt < C::KTW; ++kt)
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt) s[kt][nt] = f32x16{};
+#pragma unroll
+        for (int st = 0; st < D / 16; ++st) {
+#pragma unroll
+            for (int kt = 0; kt < C::KTW; ++kt) {
+                const int krow = kh * C::KH + kt * 32 + swap23(r32);
+                const int pos = (st * 2 + h) ^ (krow & (C::KCH - 1));
+                const bf16x8 av =
+                    as_bf16x8(*reinterpret_cast<const uint4*>(Ks + krow * C::KRB + pos * 16));
+#pragma unroll
+                for (int nt = 0; nt < 2; ++nt)
+                    s[kt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qf[nt][st], s[kt][nt], 0, 0, 0);
             }
-            __syncthreads();
-            attend_tile<D, BLK>(Ks, Vt, bias, true, qf, oacc, m_run, l_run, a.c);
+        }
+
+        // online softmax (log2 domain), P in bf16
+        bf16x8 pb[C::KTW][2][2];
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) {
+            float mx = -INFINITY;
+            if (use_bias) {
+#pragma unroll
+                for (int kt = 0; kt < C::KTW; ++kt)
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) {
+                        const int key = kh * C::KH + kt * 32 + swap23(8 * (e >> 2) + 4 * h + (e & 3));
+                        const float v = __builtin_fmaf(s[kt][nt][e], a.c, bias[key]);
+                        s[kt][nt][e] = v;
+                        mx = fmaxf(mx, v);
+                    }
+            } else {
+#pragma unroll
+                for (int kt = 0; kt < C::KTW; ++kt)
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[kt][nt][e]);
+                mx *= a.c;
+            }
+            mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+            if (mx > m_run[nt] + kLazy) {
+                const float alpha = __builtin_amdgcn_exp2f(m_run[nt] - mx);
+                l_run[nt] *= alpha;
+#pragma unroll
+                for (int dt = 0; dt < D / 32; ++dt) oacc[dt][nt] *= alpha;
+                m_run[nt] = mx;
+            }
+            const float base = m_run[nt] == -INFINITY ? 0.f : m_run[nt];
+            float sum = 0.f;
+#pragma unroll
+            for (int kt = 0; kt < C::KTW; ++kt)
+#pragma unroll
+                for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const float v = s[kt][nt][8 * s2 + e];
+                        const float p = use_bias ? __builtin_amdgcn_exp2f(v - base)
+                                                 : __builtin_amdgcn_exp2f(__builtin_fmaf(v, a.c, -base));
+                        sum += p;
+                        pb[kt][s2][nt][e] = (__bf16)p;
+                    }
+            l_run[nt] += sum;
+        }
+
+        // O^T += V^T P^T
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt) {
+            const int d = dt * 32 + r32;
+#pragma unroll
+            for (int kt = 0; kt < C::KTW; ++kt)
+#pragma unroll
+                for (int s2 = 0; s2 < 2; ++s2) {
+                    const int chunk = (kh * C::KH + kt * 32 + 16 * s2 + 8 * h) / 8;
+                    const int pos = chunk ^ (d & (C::VCH - 1));
+                    const bf16x8 av =
+                        as_bf16x8(*reinterpret_cast<const uint4*>(Vs + d * C::VRB + pos * 16));
+#pragma unroll
+                    for (int nt = 0; nt < 2; ++nt)
+                        oacc[dt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb[kt][s2][nt], oacc[dt][nt], 0, 0, 0);
+                }
         }
     }
 
-    // epilogue: O = O^T / l, lse = (m + log2 l) * ln 2
-    const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    if (qn < a.N) {
-        uint16_t* orow = a.O + head_off + (int64_t)qn * D;
+    // merge the two key halves of every query group, then write O and lse
+    float l_tot[2];
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) l_tot[nt] = l_run[nt] + __shfl_xor(l_run[nt], 32, 64);
+    __syncthreads();                                   // stage buffers are free
+    float4* mo = reinterpret_cast<float4*>(smem + qg * (C::MERGE / C::NWQ));
+    float* ml = reinterpret_cast<float*>(smem + qg * (C::MERGE / C::NWQ) + 2 * (D / 32) * 64 * 16 * 4);
+    if (kh == 1) {
 #pragma unroll
         for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int d0 = dt * 32 + 8 * g + 4 * h;
-                const uint32_t lo = f32_to_bf16_rne(oacc[dt][4 * g + 0] * inv) |
-                                    ((uint32_t)f32_to_bf16_rne(oacc[dt][4 * g + 1] * inv) << 16);
-                const uint32_t hi = f32_to_bf16_rne(oacc[dt][4 * g + 2] * inv) |
-                                    ((uint32_t)f32_to_bf16_rne(oacc[dt][4 * g + 3] * inv) << 16);
-                *reinterpret_cast<uint2*>(orow + d0) = make_uint2(lo, hi);
+            for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+                for (int g = 0; g < 4; ++g)
+                    mo[((dt * 2 + nt) * 4 + g) * 64 + lane] =
+                        make_float4(oacc[dt][nt][4 * g], oacc[dt][nt][4 * g + 1],
+                                    oacc[dt][nt][4 * g + 2], oacc[dt][nt][4 * g + 3]);
+        if (h == 0)
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt) {
+                ml[nt * 32 + r32] = m_run[nt];
+                ml[64 + nt * 32 + r32] = l_tot[nt];
             }
-        if (a.lse && h == 0)
-            a.lse[bh * (int64_t)a.N + qn] = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
+    }
+    __syncthreads();
+    if (kh == 0) {
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) {
+            const float m1 = ml[nt * 32 + r32], l1 = ml[64 + nt * 32 + r32];
+            const float m0 = m_run[nt];
+            const float m = fmaxf(m0, m1);
+            const float mb = m == -INFINITY ? 0.f : m;
+            const float a0 = __builtin_amdgcn_exp2f(m0 - mb), a1 = __builtin_amdgcn_exp2f(m1 - mb);
+            const float l = l_tot[nt] * a0 + l1 * a1;
+            const float inv = l > 0.f ? 1.f / l : 0.f;
+            const int qn = i * BLK + qg * 64 + nt * 32 + r32;
+            if (qn < a.N) {
+                uint16_t* orow = a.O + head_off + (int64_t)qn * D;
+#pragma unroll
+                for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+                    for (int g = 0; g < 4; ++g) {
+                        const float4 o1 = mo[((dt * 2 + nt) * 4 + g) * 64 + lane];
+                        const float v0 = (oacc[dt][nt][4 * g + 0] * a0 + o1.x * a1) * inv;
+                        const float v1 = (oacc[dt][nt][4 * g + 1] * a0 + o1.y * a1) * inv;
+                        const float v2 = (oacc[dt][nt][4 * g + 2] * a0 + o1.z * a1) * inv;
+                        const float v3 = (oacc[dt][nt][4 * g + 3] * a0 + o1.w * a1) * inv;
+                        const uint32_t lo = f32_to_bf16_rne(v0) | ((uint32_t)f32_to_bf16_rne(v1) << 16);
+                        const uint32_t hi = f32_to_bf16_rne(v2) | ((uint32_t)f32_to_bf16_rne(v3) << 16);
+                        *reinterpret_cast<uint2*>(orow + dt * 32 + 8 * g + 4 * h) = make_uint2(lo, hi);
+                    }
+                if (a.lse && h == 0)
+                    a.lse[bh * (int64_t)a.N + qn] = l > 0.f ? (m + __log2f(l)) * kLn2 : -INFINITY;
+            }
+        }
     }
 }
 
-// Centroid pseudo-tokens for compensation, rounded to bf16 for the matrix cores:
-// kbar = k_mean, vbar = v_sum / n_j.
-__global__ void k_comp_prep(const float* __restrict__ k_mean, const float* __restrict__ v_sum,
-                            uint16_t* __restrict__ kbar, uint16_t* __restrict__ vbar,
-                            int64_t total, int D, int nb, int block, int last_n) {
-    for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < total;
-         e += (int64_t)gridDim.x * blockDim.x) {
-        const int j = (int)((e / D) % nb);
-        const float n = (float)(j == nb - 1 ? last_n : block);
-        kbar[e] = f32_to_bf16_rne(k_mean[e]);
-        vbar[e] = f32_to_bf16_rne(v_sum[e] / n);
+// V blocks transposed to [D][BLK] (keys past the end of the sequence are 0).
+template <int D, int BLK>
+__global__ __launch_bounds__(256) void k_vt_prep(const uint16_t* __restrict__ V,
+                                                 uint16_t* __restrict__ Vt, int N, int nb) {
+    __shared__ uint16_t tile[BLK][D + 8];
+    const int j = blockIdx.x;
+    const int64_t bh = blockIdx.y;
+    const int n = min(BLK, N - j * BLK);
+    const uint16_t* src = V + (bh * N + (int64_t)j * BLK) * D;
+    for (int c = threadIdx.x; c < BLK * (D / 8); c += 256) {
+        const int r = c / (D / 8), ch = c % (D / 8);
+        uint4 v = make_uint4(0, 0, 0, 0);
+        if (r < n) v = *reinterpret_cast<const uint4*>(src + (int64_t)r * D + ch * 8);
+        *reinterpret_cast<uint4*>(&tile[r][ch * 8]) = v;
     }
+    __syncthreads();
+    uint16_t* dst = Vt + (bh * nb + j) * (int64_t)D * BLK;
+    for (int p = threadIdx.x; p < D * (BLK / 8); p += 256) {
+        const int d = p / (BLK / 8), kc = p % (BLK / 8);
+        uint32_t w[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            w[e] = (uint32_t)tile[kc * 8 + 2 * e][d] | ((uint32_t)tile[kc * 8 + 2 * e + 1][d] << 16);
+        *reinterpret_cast<uint4*>(dst + (int64_t)d * BLK + kc * 8) = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+}
+
+// Centroid pseudo-tokens for compensation, rounded to bf16 for the matrix
+// cores: kbar = k_mean [nb][D]; vbar = v_sum / n_j, stored transposed in
+// tiles of BLK blocks [ntc][D][BLK] (blocks past nb are 0).
+template <int D, int BLK>
+__global__ __launch_bounds__(256) void k_comp_prep(const float* __restrict__ k_mean,
+                                                   const float* __restrict__ v_sum,
+                                                   uint16_t* __restrict__ kbar,
+                                                   uint16_t* __restrict__ vbart, int nb, int ntc,
+                                                   int last_n) {
+    const int tc = blockIdx.x;
+    const int64_t bh = blockIdx.y;
+    for (int p = threadIdx.x; p < BLK * D; p += 256) {
+        const int r = p / D, d = p % D;
+        const int j = tc * BLK + r;
+        if (j < nb) {
+            const int64_t e = (bh * nb + j) * (int64_t)D + d;
+            kbar[e] = f32_to_bf16_rne(k_mean[e]);
+        }
+    }
+    for (int p = threadIdx.x; p < BLK * D; p += 256) {
+        const int d = p / BLK, r = p % BLK;
+        const int j = tc * BLK + r;
+        uint16_t v = 0;
+        if (j < nb) {
+            const float n = (float)(j == nb - 1 ? last_n : BLK);
+            v = f32_to_bf16_rne(v_sum[(bh * nb + j) * (int64_t)D + d] / n);
+        }
+        vbart[((bh * ntc + tc) * (int64_t)D + d) * BLK + r] = v;
+    }
+}
+
+struct WsLayout {
+    size_t vt, kbar, vbart, total;
+};
+
+WsLayout ws_layout(const Geometry& g, bool comp) {
+    WsLayout L{};
+    const int64_t ntc = ceil_div(g.nb, g.block);
+    size_t off = 0;
+    L.vt = off; off = align_up(off + (size_t)g.BH() * g.nb * g.d * g.block * 2, 256);
+    if (comp) {
+        L.kbar = off; off = align_up(off + (size_t)g.BH() * g.nb * g.d * 2, 256);
+        L.vbart = off; off = align_up(off + (size_t)g.BH() * ntc * g.d * g.block * 2, 256);
+    }
+    L.total = off;
+    return L;
 }
 
 template <int D, int BLK, bool COMP>
-sa_status launch_t(const FwdArgs& a, int nb, hipStream_t stream) {
-    using L = Lds<D, BLK>;
-    const size_t lds = L::BASE + (COMP ? (size_t)nb * 3 + 16 : 0);
+sa_status launch_t(const FwdArgs& a, const Geometry& g, const uint16_t* V, uint16_t* vt,
+                   const float* k_mean, const float* v_sum, uint16_t* kbar, uint16_t* vbart,
+                   hipStream_t stream) {
+    using C = Cfg<D, BLK>;
+    hipLaunchKernelGGL((k_vt_prep<D, BLK>), dim3(g.nb, (unsigned)g.BH()), dim3(256), 0, stream, V,
+                       vt, g.N, g.nb);
+    sa_status st = hip_check(hipGetLastError(), "k_vt_prep launch");
+    if (st != SA_OK) return st;
+    if (COMP) {
+        hipLaunchKernelGGL((k_comp_prep<D, BLK>), dim3(a.ntc, (unsigned)g.BH()), dim3(256), 0, stream,
+                           k_mean, v_sum, kbar, vbart, g.nb, a.ntc, g.N - (g.nb - 1) * BLK);
+        if ((st = hip_check(hipGetLastError(), "k_comp_prep launch")) != SA_OK) return st;
+    }
+    const size_t lds = C::BASE + (COMP ? (size_t)g.nb + 16 : 0);
     static bool configured = false;
     if (!configured) {
-        const int most = L::BASE + (COMP ? 4096 * 3 + 16 : 0);
-        sa_status st = hip_check(hipFuncSetAttribute((const void*)k_bsattn_fwd<D, BLK, COMP>,
-                                                     hipFuncAttributeMaxDynamicSharedMemorySize,
-                                                     most),
-                                 "k_bsattn_fwd shared memory");
+        const int most = C::BASE + (COMP ? 4096 + 16 : 0);
+        st = hip_check(hipFuncSetAttribute((const void*)k_bsattn_fwd<D, BLK, COMP>,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, most),
+                       "k_bsattn_fwd shared memory");
         if (st != SA_OK) return st;
         configured = true;
     }
-    hipLaunchKernelGGL((k_bsattn_fwd<D, BLK, COMP>), dim3((unsigned)a.rows), dim3(BLK * 2), lds,
-                       stream, a);
+    if (a.rows == 0) return SA_OK;
+    hipLaunchKernelGGL((k_bsattn_fwd<D, BLK, COMP>), dim3((unsigned)a.rows), dim3(C::NT), lds, stream, a);
     return hip_check(hipGetLastError(), "k_bsattn_fwd launch");
 }
 
 }  // namespace
 
-size_t fwd_workspace_bytes(const Geometry& g) {
-    return align_up((size_t)g.BH() * g.nb * g.d * 2, 256) * 2;
-}
+size_t fwd_workspace_bytes(const Geometry& g, bool comp) { return ws_layout(g, comp).total; }
 
 sa_status launch_fwd(const Geometry& g, const uint16_t* Q, const uint16_t* K, const uint16_t* V,
                      const int32_t* row_ptr, const int32_t* col_idx, const float* k_mean,
@@ -353,31 +484,26 @@ sa_status launch_fwd(const Geometry& g, const uint16_t* Q, const uint16_t* K, co
     const bool comp = k_mean != nullptr;
     if (comp && g.nb > 4096)
         return fail(SA_ERR_UNSUPPORTED, "compensation supports nb <= 4096 (got %d)", g.nb);
+    const WsLayout L = ws_layout(g, comp);
     FwdArgs a{};
-    a.Q = Q; a.K = K; a.V = V; a.row_ptr = row_ptr; a.col_idx = col_idx;
+    a.Q = Q; a.K = K; a.row_ptr = row_ptr; a.col_idx = col_idx;
     a.O = O; a.lse = lse; a.N = g.N; a.nb = g.nb; a.rows = g.rows();
+    a.ntc = (int32_t)ceil_div(g.nb, g.block);
     a.c = g.scale * kLog2e;
-    if (comp) {
-        const size_t half = align_up((size_t)g.BH() * g.nb * g.d * 2, 256);
-        uint16_t* kbar = reinterpret_cast<uint16_t*>(ws);
-        uint16_t* vbar = reinterpret_cast<uint16_t*>(ws + half);
-        const int64_t total = g.BH() * g.nb * g.d;
-        const int64_t blocks = ceil_div(total, 256);
-        hipLaunchKernelGGL(k_comp_prep, dim3((unsigned)(blocks < 8192 ? blocks : 8192)), dim3(256), 0,
-                           stream, k_mean, v_sum, kbar, vbar, total, g.d, g.nb, g.block,
-                           g.N - (g.nb - 1) * g.block);
-        sa_status st = hip_check(hipGetLastError(), "k_comp_prep launch");
-        if (st != SA_OK) return st;
-        a.kbar = kbar; a.vbar = vbar;
-    }
+    uint16_t* vt = reinterpret_cast<uint16_t*>(ws + L.vt);
+    uint16_t* kbar = comp ? reinterpret_cast<uint16_t*>(ws + L.kbar) : nullptr;
+    uint16_t* vbart = comp ? reinterpret_cast<uint16_t*>(ws + L.vbart) : nullptr;
+    a.Vt = vt; a.kbar = kbar; a.vbart = vbart;
+#define SA_LAUNCH(D_, B_)                                                                      \
+    return comp ? launch_t<D_, B_, true>(a, g, V, vt, k_mean, v_sum, kbar, vbart, stream)      \
+                : launch_t<D_, B_, false>(a, g, V, vt, k_mean, v_sum, kbar, vbart, stream)
     if (g.d == 128) {
-        if (g.block == 128)
-            return comp ? launch_t<128, 128, true>(a, g.nb, stream) : launch_t<128, 128, false>(a, g.nb, stream);
-        return comp ? launch_t<128, 64, true>(a, g.nb, stream) : launch_t<128, 64, false>(a, g.nb, stream);
+        if (g.block == 128) SA_LAUNCH(128, 128);
+        SA_LAUNCH(128, 64);
     }
-    if (g.block == 128)
-        return comp ? launch_t<64, 128, true>(a, g.nb, stream) : launch_t<64, 128, false>(a, g.nb, stream);
-    return comp ? launch_t<64, 64, true>(a, g.nb, stream) : launch_t<64, 64, false>(a, g.nb, stream);
+    if (g.block == 128) SA_LAUNCH(64, 128);
+    SA_LAUNCH(64, 64);
+#undef SA_LAUNCH
 }
 
 }  // namespace sa

@@ -181,9 +181,12 @@ __global__ __launch_bounds__(kThreads) void k_score(const float* __restrict__ qm
 // ----------------------------------------------------------------------------
 // k_select
 // ----------------------------------------------------------------------------
+constexpr int kInlineHeads = 64;
+
 struct SelectArgs {
     const float* S;           // [rows][nb] scores (scored rules)
-    const int32_t* k_head;    // [H] blocks kept per head (TOPK)
+    const int32_t* k_head;    // [H] blocks kept per head (TOPK), when H > kInlineHeads
+    int32_t k_inline[kInlineHeads];   // blocks kept per head, when H <= kInlineHeads
     uint32_t* bits;           // [rows][words]
     int32_t* counts;          // [rows]
     int32_t H, N, nb, nb_pad, words, block, HgW;
@@ -243,7 +246,7 @@ __global__ __launch_bounds__(kThreads) void k_select(SelectArgs a) {
 
         int m;
         if (a.rule == SA_RULE_TOPK) {
-            m = a.k_head[h];
+            m = a.H <= kInlineHeads ? a.k_inline[h] : a.k_head[h];
         } else {
             // p_r = exp(S_r - S_max) in fp64, summed sequentially in rank order
             const double smax = (double)S[ord[0]];
@@ -382,6 +385,16 @@ __global__ __launch_bounds__(kThreads) void k_expand(const uint32_t* __restrict_
     }
 }
 
+// Writes up to kInlineHeads per-head budgets, passed by value, to device memory
+// (stream-ordered; no host buffer has to outlive the call).
+struct HeadChunk {
+    int32_t k[kInlineHeads];
+};
+
+__global__ void k_set_heads(int32_t* __restrict__ dst, HeadChunk c, int n) {
+    if ((int)threadIdx.x < n) dst[threadIdx.x] = c.k[threadIdx.x];
+}
+
 template <int D, int BLK>
 void launch_pool_t(const PoolArgs& a, int nroles, int64_t BH, int nb, hipStream_t s) {
     hipLaunchKernelGGL((k_pool<D, BLK>), dim3(nb, (unsigned)BH, nroles), dim3(kThreads), 0, s, a);
@@ -498,12 +511,21 @@ sa_status launch_select(const Geometry& g, const SelectPlan& p, const int32_t* k
     }
 
     // 3. selection
-    if (p.rule == SA_RULE_TOPK) {
-        st = hip_check(hipMemcpyAsync(k_dev, k_host, (size_t)g.H * sizeof(int32_t),
-                                      hipMemcpyHostToDevice, stream), "copy k per head");
-        if (st != SA_OK) return st;
-    }
     SelectArgs sa{};
+    if (p.rule == SA_RULE_TOPK) {
+        if (g.H <= kInlineHeads) {
+            for (int h = 0; h < g.H; ++h) sa.k_inline[h] = k_host[h];
+        } else {
+            for (int h0 = 0; h0 < g.H; h0 += kInlineHeads) {
+                HeadChunk c{};
+                const int n = g.H - h0 < kInlineHeads ? g.H - h0 : kInlineHeads;
+                for (int t = 0; t < n; ++t) c.k[t] = k_host[h0 + t];
+                hipLaunchKernelGGL(k_set_heads, dim3(1), dim3(kInlineHeads), 0, stream,
+                                   k_dev + h0, c, n);
+                if ((st = hip_check(hipGetLastError(), "k_set_heads launch")) != SA_OK) return st;
+            }
+        }
+    }
     sa.S = S; sa.k_head = k_dev; sa.bits = bits; sa.counts = counts;
     sa.H = g.H; sa.N = g.N; sa.nb = g.nb; sa.nb_pad = p.nb_pad; sa.words = p.words;
     sa.block = g.block; sa.HgW = g.Hg * g.W; sa.rule = p.rule; sa.mass = p.mass;

@@ -120,7 +120,7 @@ SA_API sa_status sparse_attn_workspace_size(const sa_problem* prob,
         if ((st = check_spec(g, spec)) != SA_OK) return st;
         *bytes = make_select_plan(g, *spec).total;
     } else {
-        *bytes = fwd_workspace_bytes(g);
+        *bytes = fwd_workspace_bytes(g, true);
     }
     return SA_OK;
 }
@@ -233,14 +233,12 @@ SA_API sa_status sparse_attn_fwd(const sa_problem* prob, const void* Q, const vo
     if (!row_ptr || !col_idx) return fail(SA_ERR_INVALID_ARG, "row_ptr and col_idx are required");
     if ((k_mean == nullptr) != (v_sum == nullptr))
         return fail(SA_ERR_INVALID_ARG, "k_mean and v_sum must be given together");
-    if (k_mean) {
-        const size_t need = fwd_workspace_bytes(g);
-        if (!workspace) return fail(SA_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", need);
-        if (((uintptr_t)workspace & 255u) != 0)
-            return fail(SA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
-        if (ws_bytes < need)
-            return fail(SA_ERR_WORKSPACE, "workspace too small: %zu < %zu bytes", ws_bytes, need);
-    }
+    const size_t need = fwd_workspace_bytes(g, k_mean != nullptr);
+    if (!workspace) return fail(SA_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", need);
+    if (((uintptr_t)workspace & 255u) != 0)
+        return fail(SA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+    if (ws_bytes < need)
+        return fail(SA_ERR_WORKSPACE, "workspace too small: %zu < %zu bytes", ws_bytes, need);
     return launch_fwd(g, (const uint16_t*)Q, (const uint16_t*)K, (const uint16_t*)V, row_ptr,
                       col_idx, k_mean, v_sum, (uint16_t*)O, lse, (char*)workspace,
                       (hipStream_t)stream);

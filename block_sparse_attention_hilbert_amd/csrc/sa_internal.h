@@ -58,7 +58,8 @@ sa_status launch_select(const Geometry& g, const SelectPlan& p,
 // ----------------------------------------------------------------------------
 // attention (k_attn.hip)
 // ----------------------------------------------------------------------------
-size_t fwd_workspace_bytes(const Geometry& g);
+// Workspace of the attention call: V transposed per block (+ centroid tiles).
+size_t fwd_workspace_bytes(const Geometry& g, bool comp);
 
 sa_status launch_fwd(const Geometry& g, const uint16_t* Q, const uint16_t* K,
                      const uint16_t* V, const int32_t* row_ptr,

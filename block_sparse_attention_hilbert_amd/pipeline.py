@@ -34,8 +34,7 @@ class BlockSparseAttention:
                                           device=self.device)
             self.sel.v_sum = torch.empty_like(self.sel.k_mean)
         self.ws_select = alloc_workspace(workspace_size(prob, spec), self.device)
-        self.ws_fwd = alloc_workspace(workspace_size(prob, None), self.device) \
-            if spec.want_comp else None
+        self.ws_fwd = alloc_workspace(workspace_size(prob, None), self.device)
         self.O = torch.empty(shape, dtype=torch.bfloat16, device=self.device)
         self.lse = torch.empty(prob.B, prob.H, prob.N, dtype=torch.float32,
                                device=self.device) if want_lse else None

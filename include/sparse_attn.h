@@ -104,8 +104,10 @@ typedef struct {
 
 /*
  * Workspace bytes needed by sparse_attn_select (spec != NULL) or by
- * sparse_attn_fwd with compensation (spec == NULL).  The same buffer may be
- * reused by consecutive calls on one stream.
+ * sparse_attn_fwd (spec == NULL; the size covers calls with and without
+ * compensation: 2*B*H*nb*d*block bytes for V re-laid out block by block, plus
+ * the bf16 centroid tiles).  The same buffer may be reused by consecutive
+ * calls on one stream.
  */
 sa_status sparse_attn_workspace_size(const sa_problem* prob,
                                      const sa_select_spec* spec, size_t* bytes);
@@ -179,8 +181,10 @@ sa_status sparse_attn_select(const sa_problem* prob, const sa_select_spec* spec,
  *   checked).  O: device bf16 [B,H,N,d].  lse: optional device fp32 [B,H,N],
  *   natural-log log-sum-exp of the logits (including compensation terms).
  * A row with no kept block and no compensation gives O = 0, lse = -inf.
- * workspace: needed only with compensation (size from
- *   sparse_attn_workspace_size(prob, NULL)); may be NULL otherwise.
+ * Column indices outside [0, nb) are clamped into range (no fault; results
+ * for such input are unspecified).
+ * workspace: device, 256-byte aligned, >= sparse_attn_workspace_size(prob,
+ *   NULL); it receives V transposed block by block (and the centroid tiles).
  * Precision: QK^T and PV on bf16 matrix cores with fp32 accumulation, softmax
  *   in fp32, output rounded to bf16.
  */

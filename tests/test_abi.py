@@ -91,8 +91,10 @@ def test_workspace_sizes_are_consistent():
     b = sa.workspace_size(p, sa.SelectSpec(rule="mass", sub_block=16))
     c = sa.workspace_size(p, sa.SelectSpec(rule="none", window_frames=1))
     assert 0 < c < a < b
-    # compensation: bf16 centroid keys and values, [B*H*nb*d] each
-    assert sa.workspace_size(p) == 2 * (1 * 2 * 4 * 128 * 2)
+    # V re-laid out per block [B*H*nb*d*block] bf16 + centroid keys [B*H*nb*d]
+    # + centroid values in tiles of `block` blocks [B*H*ceil(nb/block)*d*block]
+    BH, nb, d, blk = 2, 4, 128, 128
+    assert sa.workspace_size(p) == 2 * (BH * nb * d * blk + BH * nb * d + BH * 1 * d * blk)
 
 
 def test_select_and_fwd_reject_before_any_launch():
@@ -124,6 +126,9 @@ def test_select_and_fwd_reject_before_any_launch():
     assert st == sa.SA_ERR_INVALID_ARG                     # k_mean without v_sum
     st = sa.lib.sparse_attn_fwd(ctypes.byref(p), fake, fake, fake, fake, fake, fake, fake,
                                 fake, None, None, 0, None)
+    assert st == sa.SA_ERR_WORKSPACE
+    st = sa.lib.sparse_attn_fwd(ctypes.byref(p), fake, fake, fake, fake, fake, None, None,
+                                fake, None, fake, 1024, None)
     assert st == sa.SA_ERR_WORKSPACE
     st = sa.lib.sparse_attn_fwd(ctypes.byref(p), fake, fake, fake, None, fake, None, None,
                                 fake, None, None, 0, None)

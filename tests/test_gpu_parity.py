@@ -50,6 +50,9 @@ SMALL = {
     "mass_sub32_d64_b128": W.CONFIGS[2].replace(T=3, Hg=10, W=13, H=2, d=64, sub_block=32),
     "mass_comp_d64_b128": W.CONFIGS[2].replace(T=5, Hg=7, W=11, H=2, d=64, comp=True, mass=0.5),
     "topk_d128_b64_wide": W.CONFIGS[3].replace(T=5, Hg=9, W=29, H=2, block=64, density=0.3),
+    # more heads than the per-head budgets passed inline with the launch
+    "topk_70heads_d64_b64": W.CONFIGS[5].replace(T=2, Hg=8, W=9, H=70, d=64, hilbert=False,
+                                                 comp=False, sub_block=0),
 }
 
 
