@@ -70,6 +70,7 @@ struct FwdArgs {
     const uint16_t* vbart;   // [BH][ntc][D][BLK] transposed centroid values
     uint16_t* O;
     float* lse;
+    int32_t* sched;          // [3][8] per-XCD row range start, end and pull counter
     int32_t N, nb, ntc;
     int64_t rows;
     float c;                 // scale * log2(e)
@@ -91,39 +92,40 @@ struct Cfg {
     static constexpr int STAGE = K_BYTES + V_BYTES + BLK * 4;   // + bias
     static constexpr int MERGE = NWQ * (2 * (D / 32) * 64 * 16 * 4 + 2 * 2 * 32 * 4);
     static constexpr int BASE = 2 * STAGE > MERGE ? 2 * STAGE : MERGE;
+    static constexpr int MAX_NB = 4096;                 // list / flag capacity
 };
 
-// Copy ROWS rows of RB bytes (row r at row_addr(r)) into an LDS tile whose
-// 16-byte chunks are XOR-swizzled by the row index.  Every wave instruction
-// moves 1 KB: lane L lands at byte offset L*16 of the wave's slice.
-template <int ROWS, int RB, int NW, typename RowAddr>
-__device__ __forceinline__ void dma_tile(unsigned char* tile, int wave, int lane,
-                                         RowAddr row_addr) {
+// Byte offset, inside a tile of ROWS rows of RB bytes, of the 16-byte chunk that
+// lane `lane` of wave `wave` fetches with DMA instruction n.  The tile's 16-byte
+// chunks are XOR-swizzled by the row index; every wave instruction fills 1 KB
+// of LDS, lane L landing at byte L*16 of the wave's slice.
+template <int RB, int NW>
+__device__ __forceinline__ uint32_t dma_src_offset(int n, int wave, int lane, int max_row) {
     constexpr int CH = RB / 16;
+    const int lin = (n * NW + wave) * 1024 + lane * 16;
+    const int row = lin / RB;
+    const int chunk = ((lin % RB) / 16) ^ (row & (CH - 1));
+    return (uint32_t)((row < max_row ? row : max_row) * RB + chunk * 16);
+}
+
+template <int ROWS, int RB, int NW>
+__device__ __forceinline__ void dma_tile(unsigned char* tile, const unsigned char* base,
+                                         const uint32_t (&off)[ROWS * RB / (1024 * NW)], int wave) {
     constexpr int INSTR = ROWS * RB / (1024 * NW);
     static_assert(INSTR * 1024 * NW == ROWS * RB, "tile must be a whole number of wave slices");
 #pragma unroll
-    for (int n = 0; n < INSTR; ++n) {
-        const int off = (n * NW + wave) * 1024;
-        const int lin = off + lane * 16;
-        const int row = lin / RB;
-        const int chunk = ((lin % RB) / 16) ^ (row & (CH - 1));
-        const unsigned char* g = row_addr(row) + chunk * 16;
-        __builtin_amdgcn_global_load_lds((gbl_void_t*)g, (lds_void_t*)(tile + off), 16, 0, 0);
-    }
+    for (int n = 0; n < INSTR; ++n)
+        __builtin_amdgcn_global_load_lds((gbl_void_t*)(base + off[n]),
+                                         (lds_void_t*)(tile + (n * NW + wave) * 1024), 16, 0, 0);
 }
 
+// One row = one (batch, head, query block): all its kept tiles, then (with
+// compensation) the centroid tiles, then the merge of the two key halves.
 template <int D, int BLK, bool COMP>
-__global__ __launch_bounds__(BLK * 2) void k_bsattn_fwd(FwdArgs a) {
+__device__ __forceinline__ void process_row(const FwdArgs& a, int64_t row, unsigned char* smem) {
     using C = Cfg<D, BLK>;
-    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-    unsigned char* kept = smem + C::BASE;            // COMP: [nb] flags
-
-    // XCD-aware remap: the workgroups dealt to one XCD take consecutive rows
-    const int64_t G = a.rows;
-    const int64_t w = blockIdx.x;
-    const int64_t q8 = G / 8, rem = G % 8, x = w % 8;
-    const int64_t row = x * q8 + (x < rem ? x : rem) + w / 8;
+    unsigned char* kept = smem + C::BASE;                              // COMP: [nb] flags
+    int16_t* list = reinterpret_cast<int16_t*>(smem + C::BASE + C::MAX_NB);  // kept blocks
 
     const int i = (int)(row % a.nb);
     const int64_t bh = row / a.nb;
@@ -154,15 +156,27 @@ __global__ __launch_bounds__(BLK * 2) void k_bsattn_fwd(FwdArgs a) {
     const int beg = a.row_ptr[row], end = a.row_ptr[row + 1];
     const int nk = end - beg;
     const int T = nk + (COMP ? a.ntc : 0);
-    if constexpr (COMP) {
+    // the row's kept blocks (clamped into range) and, for compensation, flags
+    if constexpr (COMP)
         for (int j = tid; j < a.nb; j += C::NT) kept[j] = 0;
-        __syncthreads();
-        for (int e = beg + tid; e < end; e += C::NT) {
-            const int j = a.col_idx[e];
-            if ((unsigned)j < (unsigned)a.nb) kept[j] = 1;
-        }
+    for (int e = tid; e < nk; e += C::NT) {
+        int j = a.col_idx[beg + e];
+        j = j < 0 ? 0 : (j >= a.nb ? a.nb - 1 : j);
+        list[e] = (int16_t)j;
+    }
+    __syncthreads();
+    if constexpr (COMP) {
+        for (int e = tid; e < nk; e += C::NT) kept[list[e]] = 1;
         __syncthreads();
     }
+
+    // per-lane DMA source offsets (full tiles; the clamped set for a short block)
+    constexpr int KI = C::K_BYTES / (1024 * C::NW), VI = C::V_BYTES / (1024 * C::NW);
+    uint32_t koff[KI], voff[VI];
+#pragma unroll
+    for (int n = 0; n < KI; ++n) koff[n] = dma_src_offset<C::KRB, C::NW>(n, wave, lane, BLK - 1);
+#pragma unroll
+    for (int n = 0; n < VI; ++n) voff[n] = dma_src_offset<C::VRB, C::NW>(n, wave, lane, D - 1);
 
     // Issues the HBM -> LDS copies of tile t into stage buffer b and writes its
     // key bias (0 / -inf for a short last block; log2 n_j / -inf for centroids).
@@ -170,31 +184,33 @@ __global__ __launch_bounds__(BLK * 2) void k_bsattn_fwd(FwdArgs a) {
         unsigned char* st = smem + b * C::STAGE;
         float* bias = reinterpret_cast<float*>(st + C::K_BYTES + C::V_BYTES);
         if (!COMP || t < nk) {
-            int j = a.col_idx[beg + t];
-            j = j < 0 ? 0 : (j >= a.nb ? a.nb - 1 : j);
-            const int nval = j == a.nb - 1 ? last_n : BLK;
+            const int j = __builtin_amdgcn_readfirstlane(list[t]);
             const unsigned char* kb = Kh + (int64_t)j * BLK * C::KRB;
-            dma_tile<BLK, C::KRB, C::NW>(st, wave, lane, [&](int r) {
-                return kb + (int64_t)(r < nval ? r : nval - 1) * C::KRB;
-            });
             const unsigned char* vb = Vth + (int64_t)j * D * C::VRB;
-            dma_tile<D, C::VRB, C::NW>(st + C::K_BYTES, wave, lane,
-                                       [&](int r) { return vb + (int64_t)r * C::VRB; });
-            if (nval < BLK)
+            const int nval = j == a.nb - 1 ? last_n : BLK;
+            if (nval == BLK) {
+                dma_tile<BLK, C::KRB, C::NW>(st, kb, koff, wave);
+            } else {
+                uint32_t ko[KI];
+#pragma unroll
+                for (int n = 0; n < KI; ++n) ko[n] = dma_src_offset<C::KRB, C::NW>(n, wave, lane, nval - 1);
+                dma_tile<BLK, C::KRB, C::NW>(st, kb, ko, wave);
                 for (int r = tid; r < BLK; r += C::NT) bias[r] = r < nval ? 0.f : -INFINITY;
+            }
+            dma_tile<D, C::VRB, C::NW>(st + C::K_BYTES, vb, voff, wave);
         } else {
             const int tc = t - nk;
             const int j0 = tc * BLK;
             const int nval = a.nb - j0 < BLK ? a.nb - j0 : BLK;
             const unsigned char* kb =
                 reinterpret_cast<const unsigned char*>(a.kbar + (bh * a.nb + j0) * (int64_t)D);
-            dma_tile<BLK, C::KRB, C::NW>(st, wave, lane, [&](int r) {
-                return kb + (int64_t)(r < nval ? r : nval - 1) * C::KRB;
-            });
+            uint32_t ko[KI];
+#pragma unroll
+            for (int n = 0; n < KI; ++n) ko[n] = dma_src_offset<C::KRB, C::NW>(n, wave, lane, nval - 1);
+            dma_tile<BLK, C::KRB, C::NW>(st, kb, ko, wave);
             const unsigned char* vb = reinterpret_cast<const unsigned char*>(
                 a.vbart + (bh * a.ntc + tc) * (int64_t)D * BLK);
-            dma_tile<D, C::VRB, C::NW>(st + C::K_BYTES, wave, lane,
-                                       [&](int r) { return vb + (int64_t)r * C::VRB; });
+            dma_tile<D, C::VRB, C::NW>(st + C::K_BYTES, vb, voff, wave);
             for (int r = tid; r < BLK; r += C::NT) {
                 const int j = j0 + r;
                 float bv = -INFINITY;
@@ -203,10 +219,10 @@ __global__ __launch_bounds__(BLK * 2) void k_bsattn_fwd(FwdArgs a) {
             }
         }
     };
+    // whether tile t carries a key bias (a short last block or a centroid tile)
     auto biased = [&](int t) {
         if (COMP && t >= nk) return true;
-        int j = a.col_idx[beg + t];
-        return j >= a.nb - 1 && last_n < BLK;
+        return last_n < BLK && __builtin_amdgcn_readfirstlane(list[t]) == a.nb - 1;
     };
 
     f32x16 oacc[D / 32][2];
@@ -226,24 +242,42 @@ __global__ __launch_bounds__(BLK * 2) void k_bsattn_fwd(FwdArgs a) {
         const float* bias = reinterpret_cast<const float*>(Vs + C::V_BYTES);
         const bool use_bias = biased(t);
 
-        // S^T = K Q^T for this wave's key half
+        // S^T = K Q^T for this wave's key half (all K operands read up front)
+        bf16x8 kop[D / 16][C::KTW];
+#pragma unroll
+        for (int st = 0; st < D / 16; ++st)
+#pragma unroll
+            for (int kt = 0; kt < C::KTW; ++kt) {
+                const int krow = kh * C::KH + kt * 32 + swap23(r32);
+                const int pos = (st * 2 + h) ^ (krow & (C::KCH - 1));
+                kop[st][kt] = as_bf16x8(*reinterpret_cast<const uint4*>(Ks + krow * C::KRB + pos * 16));
+            }
         f32x16 s[C::KTW][2];
 #pragma unroll
         for (int kt = 0; kt < C::KTW; ++kt)
 #pragma unroll
             for (int nt = 0; nt < 2; ++nt) s[kt][nt] = f32x16{};
 #pragma unroll
-        for (int st = 0; st < D / 16; ++st) {
+        for (int st = 0; st < D / 16; ++st)
 #pragma unroll
-            for (int kt = 0; kt < C::KTW; ++kt) {
-                const int krow = kh * C::KH + kt * 32 + swap23(r32);
-                const int pos = (st * 2 + h) ^ (krow & (C::KCH - 1));
-                const bf16x8 av =
-                    as_bf16x8(*reinterpret_cast<const uint4*>(Ks + krow * C::KRB + pos * 16));
+            for (int kt = 0; kt < C::KTW; ++kt)
 #pragma unroll
                 for (int nt = 0; nt < 2; ++nt)
-                    s[kt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qf[nt][st], s[kt][nt], 0, 0, 0);
-            }
+                    s[kt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[st][kt], qf[nt][st], s[kt][nt], 0, 0, 0);
+
+        // V^T operands for the PV product, read while the softmax runs
+        bf16x8 vop[D / 32][C::KTW][2];
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt) {
+            const int d = dt * 32 + r32;
+#pragma unroll
+            for (int kt = 0; kt < C::KTW; ++kt)
+#pragma unroll
+                for (int s2 = 0; s2 < 2; ++s2) {
+                    const int chunk = (kh * C::KH + kt * 32 + 16 * s2 + 8 * h) / 8;
+                    const int pos = chunk ^ (d & (C::VCH - 1));
+                    vop[dt][kt][s2] = as_bf16x8(*reinterpret_cast<const uint4*>(Vs + d * C::VRB + pos * 16));
+                }
         }
 
         // online softmax (log2 domain), P in bf16
@@ -295,21 +329,14 @@ __global__ __launch_bounds__(BLK * 2) void k_bsattn_fwd(FwdArgs a) {
 
         // O^T += V^T P^T
 #pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt) {
-            const int d = dt * 32 + r32;
+        for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
             for (int kt = 0; kt < C::KTW; ++kt)
 #pragma unroll
-                for (int s2 = 0; s2 < 2; ++s2) {
-                    const int chunk = (kh * C::KH + kt * 32 + 16 * s2 + 8 * h) / 8;
-                    const int pos = chunk ^ (d & (C::VCH - 1));
-                    const bf16x8 av =
-                        as_bf16x8(*reinterpret_cast<const uint4*>(Vs + d * C::VRB + pos * 16));
+                for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
                     for (int nt = 0; nt < 2; ++nt)
-                        oacc[dt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb[kt][s2][nt], oacc[dt][nt], 0, 0, 0);
-                }
-        }
+                        oacc[dt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[dt][kt][s2], pb[kt][s2][nt], oacc[dt][nt], 0, 0, 0);
     }
 
     // merge the two key halves of every query group, then write O and lse
@@ -368,6 +395,101 @@ __global__ __launch_bounds__(BLK * 2) void k_bsattn_fwd(FwdArgs a) {
             }
         }
     }
+}
+
+// Persistent grid.  The rows are split into 8 contiguous ranges of equal work
+// (k_sched); workgroup w pulls rows of range w % 8 -- the XCD it is dealt to --
+// in order, so concurrently running rows of one XCD are neighbouring query
+// blocks that share K/V blocks in that XCD's L2.  A workgroup whose range is
+// exhausted takes rows from the other ranges.
+template <int D, int BLK, bool COMP>
+__global__ __launch_bounds__(BLK * 2) void k_bsattn_fwd(FwdArgs a) {
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+    __shared__ int s_row;
+    const int x0 = blockIdx.x % 8;
+    for (int k = 0; k < 8; ++k) {
+        const int x = (x0 + k) % 8;
+        const int start = a.sched[x], stop = a.sched[8 + x];
+        for (;;) {
+            if (threadIdx.x == 0) {
+                const int idx = start < stop ? atomicAdd(&a.sched[16 + x], 1) : 0;
+                s_row = start + idx < stop ? start + idx : -1;
+            }
+            __syncthreads();
+            const int row = s_row;
+            __syncthreads();
+            if (row < 0) break;
+            process_row<D, BLK, COMP>(a, row, smem);
+        }
+    }
+}
+
+// Splits the R rows into 8 contiguous ranges of (nearly) equal work, where a
+// row costs its number of tiles plus a fixed overhead; resets the pull counters.
+constexpr int kSchedThreads = 1024;
+constexpr int kSchedItems = 8;
+
+__global__ __launch_bounds__(kSchedThreads) void k_sched(const int32_t* __restrict__ row_ptr,
+                                                         int32_t* __restrict__ sched, int64_t R,
+                                                         int extra) {
+    __shared__ long long wsum[kSchedThreads / 64];
+    __shared__ long long s_total, s_carry;
+    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    auto cost = [&](int64_t r) -> long long {
+        return (long long)(row_ptr[r + 1] - row_ptr[r]) + extra;
+    };
+    // total work
+    long long part = 0;
+    for (int64_t r = tid; r < R; r += kSchedThreads) part += cost(r);
+    for (int off = 32; off > 0; off >>= 1) part += __shfl_xor(part, off, 64);
+    if (lane == 0) wsum[wid] = part;
+    if (tid < 8) { sched[tid] = (int32_t)R; sched[8 + tid] = (int32_t)R; sched[16 + tid] = 0; }
+    __syncthreads();
+    if (tid == 0) {
+        long long t = 0;
+        for (int k = 0; k < kSchedThreads / 64; ++k) t += wsum[k];
+        s_total = t;
+        s_carry = 0;
+        sched[0] = 0;
+    }
+    __syncthreads();
+    const long long total = s_total;
+    // exclusive prefix of the costs; range x starts at the row whose work
+    // interval [prefix, prefix + cost) contains x/8 of the total
+    for (int64_t base = 0; base < R; base += (int64_t)kSchedThreads * kSchedItems) {
+        long long c[kSchedItems], sum = 0;
+        const int64_t my = base + (int64_t)tid * kSchedItems;
+#pragma unroll
+        for (int k = 0; k < kSchedItems; ++k) {
+            c[k] = my + k < R ? cost(my + k) : 0;
+            sum += c[k];
+        }
+        long long xs = sum;
+        for (int off = 1; off < 64; off <<= 1) {
+            const long long y = __shfl_up(xs, off, 64);
+            if (lane >= off) xs += y;
+        }
+        __syncthreads();
+        if (lane == 63) wsum[wid] = xs;
+        __syncthreads();
+        long long run = s_carry + xs - sum;
+        for (int k = 0; k < wid; ++k) run += wsum[k];
+#pragma unroll
+        for (int k = 0; k < kSchedItems; ++k) {
+            if (my + k < R) {
+                for (int x = 1; x < 8; ++x) {
+                    const long long tgt = (long long)x * total;      // 8 * (x/8 of the total)
+                    if (run * 8 <= tgt && tgt < (run + c[k]) * 8) sched[x] = (int32_t)(my + k);
+                }
+            }
+            run += c[k];
+        }
+        __syncthreads();
+        if (tid == kSchedThreads - 1) s_carry = run;
+        __syncthreads();
+    }
+    __syncthreads();
+    if (tid < 8) sched[8 + tid] = tid < 7 ? sched[tid + 1] : (int32_t)R;
 }
 
 // V blocks transposed to [D][BLK] (keys past the end of the sequence are 0).
@@ -429,13 +551,14 @@ __global__ __launch_bounds__(256) void k_comp_prep(const float* __restrict__ k_m
 }
 
 struct WsLayout {
-    size_t vt, kbar, vbart, total;
+    size_t sched, vt, kbar, vbart, total;
 };
 
 WsLayout ws_layout(const Geometry& g, bool comp) {
     WsLayout L{};
     const int64_t ntc = ceil_div(g.nb, g.block);
     size_t off = 0;
+    L.sched = off; off = align_up(off + 24 * sizeof(int32_t), 256);
     L.vt = off; off = align_up(off + (size_t)g.BH() * g.nb * g.d * g.block * 2, 256);
     if (comp) {
         L.kbar = off; off = align_up(off + (size_t)g.BH() * g.nb * g.d * 2, 256);
@@ -459,10 +582,10 @@ sa_status launch_t(const FwdArgs& a, const Geometry& g, const uint16_t* V, uint1
                            k_mean, v_sum, kbar, vbart, g.nb, a.ntc, g.N - (g.nb - 1) * BLK);
         if ((st = hip_check(hipGetLastError(), "k_comp_prep launch")) != SA_OK) return st;
     }
-    const size_t lds = C::BASE + (COMP ? (size_t)g.nb + 16 : 0);
+    const size_t lds = C::BASE + C::MAX_NB + 2 * (size_t)g.nb;
     static bool configured = false;
     if (!configured) {
-        const int most = C::BASE + (COMP ? 4096 + 16 : 0);
+        const int most = C::BASE + C::MAX_NB + 2 * C::MAX_NB;
         st = hip_check(hipFuncSetAttribute((const void*)k_bsattn_fwd<D, BLK, COMP>,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, most),
                        "k_bsattn_fwd shared memory");
@@ -470,7 +593,26 @@ sa_status launch_t(const FwdArgs& a, const Geometry& g, const uint16_t* V, uint1
         configured = true;
     }
     if (a.rows == 0) return SA_OK;
-    hipLaunchKernelGGL((k_bsattn_fwd<D, BLK, COMP>), dim3((unsigned)a.rows), dim3(C::NT), lds, stream, a);
+    hipLaunchKernelGGL(k_sched, dim3(1), dim3(kSchedThreads), 0, stream, a.row_ptr, a.sched,
+                       a.rows, (COMP ? a.ntc : 0) + 2);
+    if ((st = hip_check(hipGetLastError(), "k_sched launch")) != SA_OK) return st;
+    // persistent grid: as many workgroups as the chip holds at once
+    static int resident = 0;
+    if (resident == 0) {
+        int dev = 0, cus = 0, per_cu = 0;
+        if ((st = hip_check(hipGetDevice(&dev), "hipGetDevice")) != SA_OK) return st;
+        st = hip_check(hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev),
+                       "multiprocessor count");
+        if (st != SA_OK) return st;
+        st = hip_check(hipOccupancyMaxActiveBlocksPerMultiprocessor(
+                           &per_cu, (const void*)k_bsattn_fwd<D, BLK, COMP>, C::NT,
+                           C::BASE + C::MAX_NB + 2 * C::MAX_NB),
+                       "occupancy query");
+        if (st != SA_OK) return st;
+        resident = cus * (per_cu > 0 ? per_cu : 1);
+    }
+    const int64_t grid = a.rows < resident ? a.rows : resident;
+    hipLaunchKernelGGL((k_bsattn_fwd<D, BLK, COMP>), dim3((unsigned)grid), dim3(C::NT), lds, stream, a);
     return hip_check(hipGetLastError(), "k_bsattn_fwd launch");
 }
 
@@ -482,8 +624,7 @@ sa_status launch_fwd(const Geometry& g, const uint16_t* Q, const uint16_t* K, co
                      const int32_t* row_ptr, const int32_t* col_idx, const float* k_mean,
                      const float* v_sum, uint16_t* O, float* lse, char* ws, hipStream_t stream) {
     const bool comp = k_mean != nullptr;
-    if (comp && g.nb > 4096)
-        return fail(SA_ERR_UNSUPPORTED, "compensation supports nb <= 4096 (got %d)", g.nb);
+    if (g.nb > 4096) return fail(SA_ERR_UNSUPPORTED, "attention supports nb <= 4096 (got %d)", g.nb);
     const WsLayout L = ws_layout(g, comp);
     FwdArgs a{};
     a.Q = Q; a.K = K; a.row_ptr = row_ptr; a.col_idx = col_idx;
@@ -494,6 +635,7 @@ sa_status launch_fwd(const Geometry& g, const uint16_t* Q, const uint16_t* K, co
     uint16_t* kbar = comp ? reinterpret_cast<uint16_t*>(ws + L.kbar) : nullptr;
     uint16_t* vbart = comp ? reinterpret_cast<uint16_t*>(ws + L.vbart) : nullptr;
     a.Vt = vt; a.kbar = kbar; a.vbart = vbart;
+    a.sched = reinterpret_cast<int32_t*>(ws + L.sched);
 #define SA_LAUNCH(D_, B_)                                                                      \
     return comp ? launch_t<D_, B_, true>(a, g, V, vt, k_mean, v_sum, kbar, vbart, stream)      \
                 : launch_t<D_, B_, false>(a, g, V, vt, k_mean, v_sum, kbar, vbart, stream)

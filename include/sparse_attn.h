@@ -187,6 +187,7 @@ sa_status sparse_attn_select(const sa_problem* prob, const sa_select_spec* spec,
  *   NULL); it receives V transposed block by block (and the centroid tiles).
  * Precision: QK^T and PV on bf16 matrix cores with fp32 accumulation, softmax
  *   in fp32, output rounded to bf16.
+ * Limits: nb <= 4096 (SA_ERR_UNSUPPORTED above).
  */
 sa_status sparse_attn_fwd(const sa_problem* prob, const void* Q, const void* K,
                           const void* V, const int32_t* row_ptr,

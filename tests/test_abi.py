@@ -94,7 +94,8 @@ def test_workspace_sizes_are_consistent():
     # V re-laid out per block [B*H*nb*d*block] bf16 + centroid keys [B*H*nb*d]
     # + centroid values in tiles of `block` blocks [B*H*ceil(nb/block)*d*block]
     BH, nb, d, blk = 2, 4, 128, 128
-    assert sa.workspace_size(p) == 2 * (BH * nb * d * blk + BH * nb * d + BH * 1 * d * blk)
+    # (plus 256 bytes of row-schedule counters)
+    assert sa.workspace_size(p) == 256 + 2 * (BH * nb * d * blk + BH * nb * d + BH * 1 * d * blk)
 
 
 def test_select_and_fwd_reject_before_any_launch():
