@@ -108,15 +108,35 @@ __device__ __forceinline__ uint32_t dma_src_offset(int n, int wave, int lane, in
     return (uint32_t)((row < max_row ? row : max_row) * RB + chunk * 16);
 }
 
+// HBM -> LDS copy of one tile: global_load_lds_dwordx4 per wave instruction,
+// source = base (uniform, SGPRs) + this lane's offset, destination = the wave's
+// 1 KB slice.  Issued through inline assembly so that the compiler does not
+// treat every later LDS read as dependent on these copies (it cannot tell the
+// two stages apart and would wait for all of them, which removes the overlap
+// of the copy of tile t+1 with the compute of tile t); completion is ordered
+// explicitly by the s_waitcnt vmcnt(0) + barrier at the top of every tile.  The
+// instruction has no register results; M0 carries the LDS address and is
+// restored afterwards.
 template <int ROWS, int RB, int NW>
 __device__ __forceinline__ void dma_tile(unsigned char* tile, const unsigned char* base,
                                          const uint32_t (&off)[ROWS * RB / (1024 * NW)], int wave) {
     constexpr int INSTR = ROWS * RB / (1024 * NW);
     static_assert(INSTR * 1024 * NW == ROWS * RB, "tile must be a whole number of wave slices");
+    const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_void_t*)tile;
 #pragma unroll
-    for (int n = 0; n < INSTR; ++n)
-        __builtin_amdgcn_global_load_lds((gbl_void_t*)(base + off[n]),
-                                         (lds_void_t*)(tile + (n * NW + wave) * 1024), 16, 0, 0);
+    for (int n = 0; n < INSTR; ++n) {
+        const uint32_t dst = __builtin_amdgcn_readfirstlane(lds0 + (n * NW + wave) * 1024);
+        uint32_t saved;
+        asm volatile(
+            "s_mov_b32 %0, m0\n\t"
+            "s_mov_b32 m0, %1\n\t"
+            "s_nop 0\n\t"
+            "global_load_lds_dwordx4 %2, %3\n\t"
+            "s_mov_b32 m0, %0"
+            : "=&s"(saved)
+            : "s"(dst), "v"(off[n]), "s"(base)
+            : "memory");
+    }
 }
 
 // One row = one (batch, head, query block): all its kept tiles, then (with
