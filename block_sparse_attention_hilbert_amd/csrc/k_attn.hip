@@ -33,6 +33,8 @@
 //     they share are served from that XCD's L2.
 #include <math.h>
 
+#include <type_traits>
+
 #include "sa_internal.h"
 
 namespace sa {
@@ -76,9 +78,19 @@ struct FwdArgs {
     float c;                 // scale * log2(e)
 };
 
+// Query tiles (of 32 queries) per wave.  Two halve the LDS operand traffic per
+// flop but need ~360 registers (one wave per SIMD); one keeps a wave under 256
+// registers so that two waves share every SIMD and the hardware overlaps one
+// wave's matrix-core work with the other's softmax.
+#ifndef SA_NQT
+#define SA_NQT 1
+#endif
+constexpr int NQT = SA_NQT;
+
 template <int D, int BLK>
 struct Cfg {
-    static constexpr int NWQ = BLK / 64;            // query groups of 64
+    static constexpr int QW = 32 * NQT;             // queries per wave
+    static constexpr int NWQ = BLK / QW;            // query groups
     static constexpr int NW = NWQ * 2;              // x 2 key halves
     static constexpr int NT = NW * 64;
     static constexpr int KH = BLK / 2;              // keys per half
@@ -90,7 +102,7 @@ struct Cfg {
     static constexpr int K_BYTES = BLK * KRB;
     static constexpr int V_BYTES = D * VRB;
     static constexpr int STAGE = K_BYTES + V_BYTES + BLK * 4;   // + bias
-    static constexpr int MERGE = NWQ * (2 * (D / 32) * 64 * 16 * 4 + 2 * 2 * 32 * 4);
+    static constexpr int MERGE = NWQ * (NQT * (D / 32) * 64 * 16 * 4 + 2 * NQT * 32 * 4);
     static constexpr int BASE = 2 * STAGE > MERGE ? 2 * STAGE : MERGE;
     static constexpr int MAX_NB = 4096;                 // list / flag capacity
 };
@@ -160,10 +172,10 @@ __device__ __forceinline__ void process_row(const FwdArgs& a, int64_t row, unsig
     const int last_n = a.N - (a.nb - 1) * BLK;
 
     // Q^T fragments (B operand) of this wave's 64 queries
-    bf16x8 qf[2][D / 16];
+    bf16x8 qf[NQT][D / 16];
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-        const int qn = i * BLK + qg * 64 + nt * 32 + r32;
+    for (int nt = 0; nt < NQT; ++nt) {
+        const int qn = i * BLK + qg * C::QW + nt * 32 + r32;
 #pragma unroll
         for (int st = 0; st < D / 16; ++st) {
             uint4 v = make_uint4(0, 0, 0, 0);
@@ -210,6 +222,7 @@ __device__ __forceinline__ void process_row(const FwdArgs& a, int64_t row, unsig
             const int nval = j == a.nb - 1 ? last_n : BLK;
             if (nval == BLK) {
                 dma_tile<BLK, C::KRB, C::NW>(st, kb, koff, wave);
+                for (int r = tid; r < BLK; r += C::NT) bias[r] = 0.f;
             } else {
                 uint32_t ko[KI];
 #pragma unroll
@@ -239,54 +252,80 @@ __device__ __forceinline__ void process_row(const FwdArgs& a, int64_t row, unsig
             }
         }
     };
-    // whether tile t carries a key bias (a short last block or a centroid tile)
-    auto biased = [&](int t) {
-        if (COMP && t >= nk) return true;
-        return last_n < BLK && __builtin_amdgcn_readfirstlane(list[t]) == a.nb - 1;
-    };
 
-    f32x16 oacc[D / 32][2];
+    f32x16 oacc[D / 32][NQT];
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt) oacc[dt][nt] = f32x16{};
-    float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
+        for (int nt = 0; nt < NQT; ++nt) oacc[dt][nt] = f32x16{};
+    float m_run[NQT], l_run[NQT];
+#pragma unroll
+    for (int nt = 0; nt < NQT; ++nt) { m_run[nt] = -INFINITY; l_run[nt] = 0.f; }
 
-    if (T > 0) issue(0, 0);
-    for (int t = 0; t < T; ++t) {
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
-        if (t + 1 < T) issue(t + 1, (t + 1) & 1);
-        const unsigned char* Ks = smem + (t & 1) * C::STAGE;
-        const unsigned char* Vs = Ks + C::K_BYTES;
-        const float* bias = reinterpret_cast<const float*>(Vs + C::V_BYTES);
-        const bool use_bias = biased(t);
-
-        // S^T = K Q^T for this wave's key half (all K operands read up front)
-        bf16x8 kop[D / 16][C::KTW];
+    // One KV tile for this wave: S^T = K Q^T over its key half, online softmax
+    // (log2 domain, lazy rescale), O^T += V^T P^T.  Operands are streamed from
+    // LDS.  Every tile carries a key bias (0 for a full block; -inf past the
+    // end of a short last block; log2 n_j / -inf for centroid tiles), so the
+    // code has a single path.
+    auto attend = [&](const unsigned char* Ks, const unsigned char* Vs, const float* bias) {
+        f32x16 s[C::KTW][NQT];
+#pragma unroll
+        for (int kt = 0; kt < C::KTW; ++kt)
+#pragma unroll
+            for (int nt = 0; nt < NQT; ++nt) s[kt][nt] = f32x16{};
 #pragma unroll
         for (int st = 0; st < D / 16; ++st)
 #pragma unroll
             for (int kt = 0; kt < C::KTW; ++kt) {
                 const int krow = kh * C::KH + kt * 32 + swap23(r32);
                 const int pos = (st * 2 + h) ^ (krow & (C::KCH - 1));
-                kop[st][kt] = as_bf16x8(*reinterpret_cast<const uint4*>(Ks + krow * C::KRB + pos * 16));
+                const bf16x8 kop = as_bf16x8(*reinterpret_cast<const uint4*>(Ks + krow * C::KRB + pos * 16));
+#pragma unroll
+                for (int nt = 0; nt < NQT; ++nt)
+                    s[kt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qf[nt][st], s[kt][nt], 0, 0, 0);
             }
-        f32x16 s[C::KTW][2];
+
+        bf16x8 pb[C::KTW][2][NQT];
 #pragma unroll
-        for (int kt = 0; kt < C::KTW; ++kt)
-#pragma unroll
-            for (int nt = 0; nt < 2; ++nt) s[kt][nt] = f32x16{};
-#pragma unroll
-        for (int st = 0; st < D / 16; ++st)
+        for (int nt = 0; nt < NQT; ++nt) {
+            float mx = -INFINITY;
 #pragma unroll
             for (int kt = 0; kt < C::KTW; ++kt)
 #pragma unroll
-                for (int nt = 0; nt < 2; ++nt)
-                    s[kt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[st][kt], qf[nt][st], s[kt][nt], 0, 0, 0);
+                for (int g = 0; g < 4; ++g) {
+                    const int key = kh * C::KH + kt * 32 + 16 * (g >> 1) + 8 * h + 4 * (g & 1);
+                    const float4 bv = *reinterpret_cast<const float4*>(bias + key);
+                    const float b4[4] = {bv.x, bv.y, bv.z, bv.w};
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const float v = __builtin_fmaf(s[kt][nt][4 * g + e], a.c, b4[e]);
+                        s[kt][nt][4 * g + e] = v;
+                        mx = fmaxf(mx, v);
+                    }
+                }
+            mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+            if (mx > m_run[nt] + kLazy) {
+                const float alpha = __builtin_amdgcn_exp2f(m_run[nt] - mx);
+                l_run[nt] *= alpha;
+#pragma unroll
+                for (int dt = 0; dt < D / 32; ++dt) oacc[dt][nt] *= alpha;
+                m_run[nt] = mx;
+            }
+            const float nbase = m_run[nt] == -INFINITY ? 0.f : -m_run[nt];
+            float sum = 0.f;
+#pragma unroll
+            for (int kt = 0; kt < C::KTW; ++kt)
+#pragma unroll
+                for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const float p = __builtin_amdgcn_exp2f(s[kt][nt][8 * s2 + e] + nbase);
+                        sum += p;
+                        pb[kt][s2][nt][e] = (__bf16)p;
+                    }
+            l_run[nt] += sum;
+        }
 
-        // V^T operands for the PV product, read while the softmax runs
-        bf16x8 vop[D / 32][C::KTW][2];
 #pragma unroll
         for (int dt = 0; dt < D / 32; ++dt) {
             const int d = dt * 32 + r32;
@@ -296,112 +335,69 @@ __device__ __forceinline__ void process_row(const FwdArgs& a, int64_t row, unsig
                 for (int s2 = 0; s2 < 2; ++s2) {
                     const int chunk = (kh * C::KH + kt * 32 + 16 * s2 + 8 * h) / 8;
                     const int pos = chunk ^ (d & (C::VCH - 1));
-                    vop[dt][kt][s2] = as_bf16x8(*reinterpret_cast<const uint4*>(Vs + d * C::VRB + pos * 16));
+                    const bf16x8 vop = as_bf16x8(*reinterpret_cast<const uint4*>(Vs + d * C::VRB + pos * 16));
+#pragma unroll
+                    for (int nt = 0; nt < NQT; ++nt)
+                        oacc[dt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pb[kt][s2][nt], oacc[dt][nt], 0, 0, 0);
                 }
         }
+    };
 
-        // online softmax (log2 domain), P in bf16
-        bf16x8 pb[C::KTW][2][2];
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt) {
-            float mx = -INFINITY;
-            if (use_bias) {
-#pragma unroll
-                for (int kt = 0; kt < C::KTW; ++kt)
-#pragma unroll
-                    for (int e = 0; e < 16; ++e) {
-                        const int key = kh * C::KH + kt * 32 + swap23(8 * (e >> 2) + 4 * h + (e & 3));
-                        const float v = __builtin_fmaf(s[kt][nt][e], a.c, bias[key]);
-                        s[kt][nt][e] = v;
-                        mx = fmaxf(mx, v);
-                    }
-            } else {
-#pragma unroll
-                for (int kt = 0; kt < C::KTW; ++kt)
-#pragma unroll
-                    for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[kt][nt][e]);
-                mx *= a.c;
-            }
-            mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-            if (mx > m_run[nt] + kLazy) {
-                const float alpha = __builtin_amdgcn_exp2f(m_run[nt] - mx);
-                l_run[nt] *= alpha;
-#pragma unroll
-                for (int dt = 0; dt < D / 32; ++dt) oacc[dt][nt] *= alpha;
-                m_run[nt] = mx;
-            }
-            const float base = m_run[nt] == -INFINITY ? 0.f : m_run[nt];
-            float sum = 0.f;
-#pragma unroll
-            for (int kt = 0; kt < C::KTW; ++kt)
-#pragma unroll
-                for (int s2 = 0; s2 < 2; ++s2)
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        const float v = s[kt][nt][8 * s2 + e];
-                        const float p = use_bias ? __builtin_amdgcn_exp2f(v - base)
-                                                 : __builtin_amdgcn_exp2f(__builtin_fmaf(v, a.c, -base));
-                        sum += p;
-                        pb[kt][s2][nt][e] = (__bf16)p;
-                    }
-            l_run[nt] += sum;
-        }
+    if (T > 0) issue(0, 0);
+    for (int t = 0; t < T; ++t) {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        if (t + 1 < T) issue(t + 1, (t + 1) & 1);
+        const unsigned char* Ks = smem + (t & 1) * C::STAGE;
+        const unsigned char* Vs = Ks + C::K_BYTES;
+        const float* bias = reinterpret_cast<const float*>(Vs + C::V_BYTES);
 
-        // O^T += V^T P^T
-#pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-            for (int kt = 0; kt < C::KTW; ++kt)
-#pragma unroll
-                for (int s2 = 0; s2 < 2; ++s2)
-#pragma unroll
-                    for (int nt = 0; nt < 2; ++nt)
-                        oacc[dt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[dt][kt][s2], pb[kt][s2][nt], oacc[dt][nt], 0, 0, 0);
+        attend(Ks, Vs, bias);
     }
 
     // merge the two key halves of every query group, then write O and lse
-    float l_tot[2];
+    float l_tot[NQT];
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) l_tot[nt] = l_run[nt] + __shfl_xor(l_run[nt], 32, 64);
+    for (int nt = 0; nt < NQT; ++nt) l_tot[nt] = l_run[nt] + __shfl_xor(l_run[nt], 32, 64);
     __syncthreads();                                   // stage buffers are free
     float4* mo = reinterpret_cast<float4*>(smem + qg * (C::MERGE / C::NWQ));
-    float* ml = reinterpret_cast<float*>(smem + qg * (C::MERGE / C::NWQ) + 2 * (D / 32) * 64 * 16 * 4);
+    float* ml = reinterpret_cast<float*>(smem + qg * (C::MERGE / C::NWQ) + NQT * (D / 32) * 64 * 16 * 4);
     if (kh == 1) {
 #pragma unroll
         for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
-            for (int nt = 0; nt < 2; ++nt)
+            for (int nt = 0; nt < NQT; ++nt)
 #pragma unroll
                 for (int g = 0; g < 4; ++g)
-                    mo[((dt * 2 + nt) * 4 + g) * 64 + lane] =
+                    mo[((dt * NQT + nt) * 4 + g) * 64 + lane] =
                         make_float4(oacc[dt][nt][4 * g], oacc[dt][nt][4 * g + 1],
                                     oacc[dt][nt][4 * g + 2], oacc[dt][nt][4 * g + 3]);
         if (h == 0)
 #pragma unroll
-            for (int nt = 0; nt < 2; ++nt) {
+            for (int nt = 0; nt < NQT; ++nt) {
                 ml[nt * 32 + r32] = m_run[nt];
-                ml[64 + nt * 32 + r32] = l_tot[nt];
+                ml[NQT * 32 + nt * 32 + r32] = l_tot[nt];
             }
     }
     __syncthreads();
     if (kh == 0) {
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt) {
-            const float m1 = ml[nt * 32 + r32], l1 = ml[64 + nt * 32 + r32];
+        for (int nt = 0; nt < NQT; ++nt) {
+            const float m1 = ml[nt * 32 + r32], l1 = ml[NQT * 32 + nt * 32 + r32];
             const float m0 = m_run[nt];
             const float m = fmaxf(m0, m1);
             const float mb = m == -INFINITY ? 0.f : m;
             const float a0 = __builtin_amdgcn_exp2f(m0 - mb), a1 = __builtin_amdgcn_exp2f(m1 - mb);
             const float l = l_tot[nt] * a0 + l1 * a1;
             const float inv = l > 0.f ? 1.f / l : 0.f;
-            const int qn = i * BLK + qg * 64 + nt * 32 + r32;
+            const int qn = i * BLK + qg * C::QW + nt * 32 + r32;
             if (qn < a.N) {
                 uint16_t* orow = a.O + head_off + (int64_t)qn * D;
 #pragma unroll
                 for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
                     for (int g = 0; g < 4; ++g) {
-                        const float4 o1 = mo[((dt * 2 + nt) * 4 + g) * 64 + lane];
+                        const float4 o1 = mo[((dt * NQT + nt) * 4 + g) * 64 + lane];
                         const float v0 = (oacc[dt][nt][4 * g + 0] * a0 + o1.x * a1) * inv;
                         const float v1 = (oacc[dt][nt][4 * g + 1] * a0 + o1.y * a1) * inv;
                         const float v2 = (oacc[dt][nt][4 * g + 2] * a0 + o1.z * a1) * inv;
@@ -423,7 +419,8 @@ __device__ __forceinline__ void process_row(const FwdArgs& a, int64_t row, unsig
 // blocks that share K/V blocks in that XCD's L2.  A workgroup whose range is
 // exhausted takes rows from the other ranges.
 template <int D, int BLK, bool COMP>
-__global__ __launch_bounds__(BLK * 2) void k_bsattn_fwd(FwdArgs a) {
+__global__ __launch_bounds__(BLK * 4 / NQT) __attribute__((amdgpu_waves_per_eu(NQT == 1 ? 2 : 1)))
+void k_bsattn_fwd(FwdArgs a) {
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     __shared__ int s_row;
     const int x0 = blockIdx.x % 8;
