@@ -41,6 +41,7 @@ namespace sa {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) const void gbl_void_t;
@@ -60,6 +61,17 @@ __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast
 // Row order of K inside a 32-row tile: bits 2 and 3 of the row index swapped.
 __device__ __forceinline__ int swap23(int r) {
     return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1);
+}
+
+// x[lane] op x[lane ^ 32] through the VALU half-wave swap (no LDS round trip):
+// the two results of v_permlane32_swap hold x of this lane and of its partner.
+__device__ __forceinline__ float xmax32(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xsum32(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 struct FwdArgs {
@@ -212,6 +224,7 @@ __device__ __forceinline__ void process_row(const FwdArgs& a, int64_t row, unsig
 
     // Issues the HBM -> LDS copies of tile t into stage buffer b and writes its
     // key bias (0 / -inf for a short last block; log2 n_j / -inf for centroids).
+    const float inv_c = 1.f / a.c;
     auto issue = [&](int t, int b) {
         unsigned char* st = smem + b * C::STAGE;
         float* bias = reinterpret_cast<float*>(st + C::K_BYTES + C::V_BYTES);
@@ -222,7 +235,6 @@ __device__ __forceinline__ void process_row(const FwdArgs& a, int64_t row, unsig
             const int nval = j == a.nb - 1 ? last_n : BLK;
             if (nval == BLK) {
                 dma_tile<BLK, C::KRB, C::NW>(st, kb, koff, wave);
-                for (int r = tid; r < BLK; r += C::NT) bias[r] = 0.f;
             } else {
                 uint32_t ko[KI];
 #pragma unroll
@@ -247,7 +259,7 @@ __device__ __forceinline__ void process_row(const FwdArgs& a, int64_t row, unsig
             for (int r = tid; r < BLK; r += C::NT) {
                 const int j = j0 + r;
                 float bv = -INFINITY;
-                if (j < a.nb && !kept[j]) bv = __log2f((float)(j == a.nb - 1 ? last_n : BLK));
+                if (j < a.nb && !kept[j]) bv = __log2f((float)(j == a.nb - 1 ? last_n : BLK)) * inv_c;
                 bias[r] = bv;
             }
         }
@@ -264,10 +276,13 @@ __device__ __forceinline__ void process_row(const FwdArgs& a, int64_t row, unsig
 
     // One KV tile for this wave: S^T = K Q^T over its key half, online softmax
     // (log2 domain, lazy rescale), O^T += V^T P^T.  Operands are streamed from
-    // LDS.  Every tile carries a key bias (0 for a full block; -inf past the
-    // end of a short last block; log2 n_j / -inf for centroid tiles), so the
-    // code has a single path.
-    auto attend = [&](const unsigned char* Ks, const unsigned char* Vs, const float* bias) {
+    // LDS.  A tile with masked or weighted keys (short last block: -inf past its
+    // end; centroid tiles: log2 n_j, -inf for kept blocks) adds its key bias,
+    // stored divided by the log2-domain scale c, to the raw scores; the max is
+    // taken on raw scores (c > 0), and c s - m is one FMA.
+    const bf16x2 kOnes2 = {(__bf16)1.f, (__bf16)1.f};
+    auto attend = [&](const unsigned char* Ks, const unsigned char* Vs, const float* bias,
+                      bool biased) {
         f32x16 s[C::KTW][NQT];
 #pragma unroll
         for (int kt = 0; kt < C::KTW; ++kt)
@@ -284,11 +299,7 @@ __device__ __forceinline__ void process_row(const FwdArgs& a, int64_t row, unsig
                 for (int nt = 0; nt < NQT; ++nt)
                     s[kt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qf[nt][st], s[kt][nt], 0, 0, 0);
             }
-
-        bf16x8 pb[C::KTW][2][NQT];
-#pragma unroll
-        for (int nt = 0; nt < NQT; ++nt) {
-            float mx = -INFINITY;
+        if (biased) {
 #pragma unroll
             for (int kt = 0; kt < C::KTW; ++kt)
 #pragma unroll
@@ -297,13 +308,21 @@ __device__ __forceinline__ void process_row(const FwdArgs& a, int64_t row, unsig
                     const float4 bv = *reinterpret_cast<const float4*>(bias + key);
                     const float b4[4] = {bv.x, bv.y, bv.z, bv.w};
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const float v = __builtin_fmaf(s[kt][nt][4 * g + e], a.c, b4[e]);
-                        s[kt][nt][4 * g + e] = v;
-                        mx = fmaxf(mx, v);
-                    }
+                    for (int nt = 0; nt < NQT; ++nt)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) s[kt][nt][4 * g + e] += b4[e];
                 }
-            mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        }
+
+        bf16x8 pb[C::KTW][2][NQT];
+#pragma unroll
+        for (int nt = 0; nt < NQT; ++nt) {
+            float mx = -INFINITY;
+#pragma unroll
+            for (int kt = 0; kt < C::KTW; ++kt)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[kt][nt][e]);
+            mx = xmax32(mx) * a.c;
             if (mx > m_run[nt] + kLazy) {
                 const float alpha = __builtin_amdgcn_exp2f(m_run[nt] - mx);
                 l_run[nt] *= alpha;
@@ -312,18 +331,23 @@ __device__ __forceinline__ void process_row(const FwdArgs& a, int64_t row, unsig
                 m_run[nt] = mx;
             }
             const float nbase = m_run[nt] == -INFINITY ? 0.f : -m_run[nt];
-            float sum = 0.f;
+            // the row sum adds the bf16 weights that enter P V
+            float sum = l_run[nt];
 #pragma unroll
             for (int kt = 0; kt < C::KTW; ++kt)
 #pragma unroll
-                for (int s2 = 0; s2 < 2; ++s2)
+                for (int s2 = 0; s2 < 2; ++s2) {
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        const float p = __builtin_amdgcn_exp2f(s[kt][nt][8 * s2 + e] + nbase);
-                        sum += p;
-                        pb[kt][s2][nt][e] = (__bf16)p;
-                    }
-            l_run[nt] += sum;
+                    for (int e = 0; e < 8; ++e)
+                        pb[kt][s2][nt][e] =
+                            (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(s[kt][nt][8 * s2 + e], a.c, nbase));
+                    const bf16x8 w = pb[kt][s2][nt];
+                    sum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(w, w, 0, 1), kOnes2, sum, false);
+                    sum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(w, w, 2, 3), kOnes2, sum, false);
+                    sum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(w, w, 4, 5), kOnes2, sum, false);
+                    sum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(w, w, 6, 7), kOnes2, sum, false);
+                }
+            l_run[nt] = sum;
         }
 
 #pragma unroll
@@ -351,14 +375,15 @@ __device__ __forceinline__ void process_row(const FwdArgs& a, int64_t row, unsig
         const unsigned char* Ks = smem + (t & 1) * C::STAGE;
         const unsigned char* Vs = Ks + C::K_BYTES;
         const float* bias = reinterpret_cast<const float*>(Vs + C::V_BYTES);
-
-        attend(Ks, Vs, bias);
+        bool biased = COMP && t >= nk;
+        if (!biased) biased = last_n < BLK && __builtin_amdgcn_readfirstlane(list[t]) == a.nb - 1;
+        attend(Ks, Vs, bias, biased);
     }
 
     // merge the two key halves of every query group, then write O and lse
     float l_tot[NQT];
 #pragma unroll
-    for (int nt = 0; nt < NQT; ++nt) l_tot[nt] = l_run[nt] + __shfl_xor(l_run[nt], 32, 64);
+    for (int nt = 0; nt < NQT; ++nt) l_tot[nt] = xsum32(l_run[nt]);
     __syncthreads();                                   // stage buffers are free
     float4* mo = reinterpret_cast<float4*>(smem + qg * (C::MERGE / C::NWQ));
     float* ml = reinterpret_cast<float*>(smem + qg * (C::MERGE / C::NWQ) + NQT * (D / 32) * 64 * 16 * 4);
