@@ -9,6 +9,7 @@ stream.  The functions mirror the C ABI in ``include/sparse_attn.h``:
 * :func:`hilbert_permute`, :func:`hilbert_unpermute` -- token reordering
 * :func:`select` -- ``sparse_attn_select``: keep lists as CSR
 * :func:`fwd` -- ``sparse_attn_fwd``: block-sparse attention (+ compensation)
+* :func:`fwd_prepare`, :func:`fwd_run` -- its two halves
 * :func:`workspace_size`
 
 If the shared library is missing the import fails loudly; there is no
@@ -34,7 +35,7 @@ RULES = {"none": SA_RULE_NONE, "topk": SA_RULE_TOPK, "mass": SA_RULE_MASS}
 
 EXPORTS = ("sparse_attn_workspace_size", "hilbert_perm_build", "hilbert_permute",
            "hilbert_unpermute", "sparse_attn_select", "sparse_attn_fwd",
-           "sparse_attn_last_error")
+           "sparse_attn_fwd_prepare", "sparse_attn_fwd_run", "sparse_attn_last_error")
 
 
 class SaProblem(ctypes.Structure):
@@ -72,6 +73,9 @@ def _load():
     lib.sparse_attn_select.argtypes = [P(SaProblem), P(SaSelectSpec), vp, vp, vp, vp, vp, vp,
                                        vp, vp, vp, sz, vp]
     lib.sparse_attn_fwd.argtypes = [P(SaProblem), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.sparse_attn_fwd_prepare.argtypes = [P(SaProblem), vp, vp, vp, vp, vp, sz, vp]
+    lib.sparse_attn_fwd_run.argtypes = [P(SaProblem), vp, vp, vp, vp, ctypes.c_int32, vp, vp, vp,
+                                        sz, vp]
     for name in EXPORTS[:-1]:
         getattr(lib, name).restype = ctypes.c_int
     lib.sparse_attn_last_error.argtypes = []
@@ -246,6 +250,26 @@ def fwd(prob: Problem, Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor,
                                _ptr(col_idx), _ptr(k_mean), _ptr(v_sum), _ptr(O), _ptr(lse),
                                _ptr(workspace), ws_bytes, _stream(stream)))
     return (O, lse) if lse is not None else O
+
+
+def fwd_prepare(prob: Problem, V: torch.Tensor, row_ptr: torch.Tensor,
+                k_mean: Optional[torch.Tensor] = None, v_sum: Optional[torch.Tensor] = None, *,
+                workspace: torch.Tensor, stream=None) -> None:
+    """sparse_attn_fwd_prepare: V (and the centroids) laid out in ``workspace``."""
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(lib.sparse_attn_fwd_prepare(ctypes.byref(prob.c()), _ptr(V), _ptr(row_ptr),
+                                       _ptr(k_mean), _ptr(v_sum), _ptr(workspace), ws_bytes,
+                                       _stream(stream)))
+
+
+def fwd_run(prob: Problem, Q: torch.Tensor, K: torch.Tensor, row_ptr: torch.Tensor,
+            col_idx: torch.Tensor, with_comp: bool, *, O: torch.Tensor,
+            lse: Optional[torch.Tensor] = None, workspace: torch.Tensor, stream=None) -> None:
+    """sparse_attn_fwd_run: the attention kernel on a prepared workspace."""
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(lib.sparse_attn_fwd_run(ctypes.byref(prob.c()), _ptr(Q), _ptr(K), _ptr(row_ptr),
+                                   _ptr(col_idx), int(bool(with_comp)), _ptr(O), _ptr(lse),
+                                   _ptr(workspace), ws_bytes, _stream(stream)))
 
 
 def problem_for(wl, scale: float = 0.0) -> Problem:

@@ -6,31 +6,35 @@
 // weight = the block's token count (a logit bias of log n_j).
 //
 // Mapping onto CDNA4
-//   * one workgroup = one (batch, head, query block).  Wave (qg, kh) owns 64
+//   * one workgroup = one (batch, head, query block).  Wave (qg, kh) owns 32
 //     queries (query group qg) and one half of the keys of every KV tile (kh);
-//     the two key halves are merged once at the end, like two KV splits.
-//     64 queries per wave means every K / V operand read from LDS feeds two
-//     matrix-core instructions, halving LDS traffic per flop.
+//     the two key halves are merged once at the end, like two KV splits.  A
+//     wave stays under 256 registers, so two waves share every SIMD.
 //   * S^T = K Q^T on v_mfma_f32_32x32x16_bf16: Q^T (B operand) stays in
 //     registers for the whole row, K (A operand) is read from LDS.  In the
 //     32x32 accumulator layout a lane holds one query column, so the softmax
 //     statistics are lane-local; the two lane halves sharing a query exchange
-//     their maximum once per tile (xor 32).
+//     their maximum once per tile (v_permlane32_swap).
 //   * O^T = V^T P^T on the same instruction: P goes from the S^T accumulators
 //     into the B operand.  K rows are read in an order that swaps bits 2 and 3
 //     of the row index, which makes the 8 probabilities a lane holds per
 //     k-step 8 consecutive keys; V is pre-transposed per block in HBM (a cheap
 //     bandwidth-bound pass) so those 8 keys are one 16-byte LDS read.
+//   * software pipeline of two phases per tile: a matrix phase (P_t V_t and
+//     S_{t+1} = K_{t+1} Q^T, interleaved) and a vector phase (softmax of
+//     S_{t+1}).  With 8 waves, waves w and w + 4 share a SIMD; the second four
+//     run one phase behind the first four (one extra barrier at the start), so
+//     on every SIMD one wave's matrix phase overlaps the other's vector phase
+//     and the barriers keep the two in alternation.
 //   * K and V^T tiles move HBM -> LDS with global_load_lds_dwordx4 (no
-//     register staging), double-buffered: tile t+1 is in flight while tile t
-//     is computed.  Tiles use an XOR swizzle of their 16-byte chunks so that
-//     the row-strided operand reads are bank-conflict free.
+//     register staging) into two K slots and two V slots: the copies of K_{t+2}
+//     and V_{t+1} are in flight while P_t V_t and S_{t+1} are computed.  Tiles
+//     use an XOR swizzle of their 16-byte chunks so that the row-strided
+//     operand reads are bank-conflict free.
 //   * online softmax in the log2 domain with lazy rescaling: the running
 //     maximum only moves (and O, l are only rescaled) when a tile raises it by
 //     more than 2^8.
-//   * blockIdx -> row remap keeps consecutive query blocks of a head on one
-//     XCD (workgroups are dealt round-robin to the 8 XCDs), so the K/V blocks
-//     they share are served from that XCD's L2.
+//   * persistent grid with per-XCD row ranges (see k_bsattn_fwd).
 #include <math.h>
 
 #include <type_traits>
@@ -44,11 +48,16 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) void lds_void_t;
-typedef __attribute__((address_space(1))) const void gbl_void_t;
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kLazy = 8.0f;      // log2 headroom before the running max moves
+#ifndef SA_PF
+#define SA_PF 4                    // LDS operand reads in flight in the matrix phase
+#endif
+#ifndef SA_SGB
+#define SA_SGB 1
+#endif
 
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
     uint32_t u = __float_as_uint(f);
@@ -74,6 +83,14 @@ __device__ __forceinline__ float xsum32(float x) {
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// Workgroup barrier without a memory fence: LDS operands are consumed (waited
+// for) inside the phase that reads them, and the tile copies are completed
+// with explicit vmcnt waits, so the fence's waits would only stall the copies
+// in flight.  The memory clobber keeps the compiler from moving LDS accesses
+// across it.
+__device__ __forceinline__ void wg_barrier() { asm volatile("s_barrier" ::: "memory"); }
+__device__ __forceinline__ void copies_done() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
 struct FwdArgs {
     const uint16_t* Q;
     const uint16_t* K;
@@ -90,21 +107,16 @@ struct FwdArgs {
     float c;                 // scale * log2(e)
 };
 
-// Query tiles (of 32 queries) per wave.  Two halve the LDS operand traffic per
-// flop but need ~360 registers (one wave per SIMD); one keeps a wave under 256
-// registers so that two waves share every SIMD and the hardware overlaps one
-// wave's matrix-core work with the other's softmax.
-#ifndef SA_NQT
-#define SA_NQT 1
-#endif
-constexpr int NQT = SA_NQT;
-
 template <int D, int BLK>
 struct Cfg {
-    static constexpr int QW = 32 * NQT;             // queries per wave
-    static constexpr int NWQ = BLK / QW;            // query groups
+    static constexpr int NWQ = BLK / 32;            // query groups of 32 queries
     static constexpr int NW = NWQ * 2;              // x 2 key halves
     static constexpr int NT = NW * 64;
+    // 8 waves: two phase groups of 4 (one wave of each per SIMD); the first
+    // group issues all tile copies.  4 waves (64-token blocks): one group, and
+    // two workgroups share a CU.
+    static constexpr bool PING = NW == 8;
+    static constexpr int NWI = PING ? NW / 2 : NW;  // waves issuing copies
     static constexpr int KH = BLK / 2;              // keys per half
     static constexpr int KTW = KH / 32;             // 32-key MFMA tiles per wave
     static constexpr int KRB = D * 2;               // bytes per K row
@@ -113,20 +125,26 @@ struct Cfg {
     static constexpr int VCH = VRB / 16;
     static constexpr int K_BYTES = BLK * KRB;
     static constexpr int V_BYTES = D * VRB;
-    static constexpr int STAGE = K_BYTES + V_BYTES + BLK * 4;   // + bias
-    static constexpr int MERGE = NWQ * (NQT * (D / 32) * 64 * 16 * 4 + 2 * NQT * 32 * 4);
-    static constexpr int BASE = 2 * STAGE > MERGE ? 2 * STAGE : MERGE;
+    static constexpr int KI = K_BYTES / (1024 * NWI);   // copy instructions per issuing wave
+    static constexpr int VI = V_BYTES / (1024 * NWI);
+    static constexpr int NSTEP = KTW * D / 16;      // MFMAs of each product per tile
+    static constexpr int SLOTS = 2 * K_BYTES + 2 * V_BYTES;
+    static constexpr int MERGE = NWQ * ((D / 32) * 64 * 16 * 4 + 2 * 32 * 4);
+    static constexpr int BASE = SLOTS > MERGE ? SLOTS : MERGE;
     static constexpr int MAX_NB = 4096;                 // list / flag capacity
+    static_assert(KI * 1024 * NWI == K_BYTES && VI * 1024 * NWI == V_BYTES, "whole wave slices");
+    static_assert(NSTEP == (D / 32) * KTW * 2, "both products take the same number of steps");
 };
 
-// Byte offset, inside a tile of ROWS rows of RB bytes, of the 16-byte chunk that
-// lane `lane` of wave `wave` fetches with DMA instruction n.  The tile's 16-byte
-// chunks are XOR-swizzled by the row index; every wave instruction fills 1 KB
-// of LDS, lane L landing at byte L*16 of the wave's slice.
-template <int RB, int NW>
-__device__ __forceinline__ uint32_t dma_src_offset(int n, int wave, int lane, int max_row) {
+// Byte offset, inside a tile of rows of RB bytes, of the 16-byte chunk that lane
+// `lane` of issuing wave `wi` fetches with copy instruction n.  The tile's
+// 16-byte chunks are XOR-swizzled by the row index; every wave instruction
+// fills 1 KB of LDS, lane L landing at byte L*16 of the wave's slice.  Rows
+// above max_row are clamped to it.
+template <int RB, int NWI>
+__device__ __forceinline__ uint32_t dma_src_offset(int n, int wi, int lane, int max_row) {
     constexpr int CH = RB / 16;
-    const int lin = (n * NW + wave) * 1024 + lane * 16;
+    const int lin = (n * NWI + wi) * 1024 + lane * 16;
     const int row = lin / RB;
     const int chunk = ((lin % RB) / 16) ^ (row & (CH - 1));
     return (uint32_t)((row < max_row ? row : max_row) * RB + chunk * 16);
@@ -136,20 +154,21 @@ __device__ __forceinline__ uint32_t dma_src_offset(int n, int wave, int lane, in
 // source = base (uniform, SGPRs) + this lane's offset, destination = the wave's
 // 1 KB slice.  Issued through inline assembly so that the compiler does not
 // treat every later LDS read as dependent on these copies (it cannot tell the
-// two stages apart and would wait for all of them, which removes the overlap
-// of the copy of tile t+1 with the compute of tile t); completion is ordered
-// explicitly by the s_waitcnt vmcnt(0) + barrier at the top of every tile.  The
-// instruction has no register results; M0 carries the LDS address and is
-// restored afterwards.
-template <int ROWS, int RB, int NW>
-__device__ __forceinline__ void dma_tile(unsigned char* tile, const unsigned char* base,
-                                         const uint32_t (&off)[ROWS * RB / (1024 * NW)], int wave) {
-    constexpr int INSTR = ROWS * RB / (1024 * NW);
-    static_assert(INSTR * 1024 * NW == ROWS * RB, "tile must be a whole number of wave slices");
+// slots apart and would wait for all of them); completion is ordered
+// explicitly by copies_done() + a barrier.  The instruction has no register
+// results; M0 carries the LDS address and is restored afterwards.
+template <int RB, int INSTR, int NWI>
+__device__ __forceinline__ void dma_tile(unsigned char* tile, const unsigned char* base, int max_row,
+                                         int wi, int lane) {
     const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_void_t*)tile;
+    // the base is wave-uniform by construction; say so, so that it sits in SGPRs
+    const uint64_t b = (uint64_t)(uintptr_t)base;
+    const uint64_t ub = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32)) << 32) |
+                        (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b);
+    const unsigned char* sbase = reinterpret_cast<const unsigned char*>((uintptr_t)ub);
 #pragma unroll
     for (int n = 0; n < INSTR; ++n) {
-        const uint32_t dst = __builtin_amdgcn_readfirstlane(lds0 + (n * NW + wave) * 1024);
+        const uint32_t dst = __builtin_amdgcn_readfirstlane(lds0 + (n * NWI + wi) * 1024);
         uint32_t saved;
         asm volatile(
             "s_mov_b32 %0, m0\n\t"
@@ -158,7 +177,7 @@ __device__ __forceinline__ void dma_tile(unsigned char* tile, const unsigned cha
             "global_load_lds_dwordx4 %2, %3\n\t"
             "s_mov_b32 m0, %0"
             : "=&s"(saved)
-            : "s"(dst), "v"(off[n]), "s"(base)
+            : "s"(dst), "v"(dma_src_offset<RB, NWI>(n, wi, lane, max_row)), "s"(sbase)
             : "memory");
     }
 }
@@ -168,6 +187,10 @@ __device__ __forceinline__ void dma_tile(unsigned char* tile, const unsigned cha
 template <int D, int BLK, bool COMP>
 __device__ __forceinline__ void process_row(const FwdArgs& a, int64_t row, unsigned char* smem) {
     using C = Cfg<D, BLK>;
+    using yes = std::true_type;
+    using no = std::false_type;
+    unsigned char* kslot = smem;                                       // 2 K tiles
+    unsigned char* vslot = smem + 2 * C::K_BYTES;                      // 2 V^T tiles
     unsigned char* kept = smem + C::BASE;                              // COMP: [nb] flags
     int16_t* list = reinterpret_cast<int16_t*>(smem + C::BASE + C::MAX_NB);  // kept blocks
 
@@ -176,6 +199,8 @@ __device__ __forceinline__ void process_row(const FwdArgs& a, int64_t row, unsig
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int qg = wave >> 1, kh = wave & 1;
+    const bool issuer = wave < C::NWI;
+    const bool lagging = C::PING && wave >= C::NWI;
     const int r32 = lane & 31, h = lane >> 5;
     const int64_t head_off = bh * (int64_t)a.N * D;
     const unsigned char* Kh = reinterpret_cast<const unsigned char*>(a.K + head_off);
@@ -183,22 +208,18 @@ __device__ __forceinline__ void process_row(const FwdArgs& a, int64_t row, unsig
         reinterpret_cast<const unsigned char*>(a.Vt + bh * (int64_t)a.nb * D * BLK);
     const int last_n = a.N - (a.nb - 1) * BLK;
 
-    // Q^T fragments (B operand) of this wave's 64 queries
-    bf16x8 qf[NQT][D / 16];
+    // Q^T fragments (B operand) of this wave's 32 queries
+    bf16x8 qf[D / 16];
+    const int qn = i * BLK + qg * 32 + r32;
 #pragma unroll
-    for (int nt = 0; nt < NQT; ++nt) {
-        const int qn = i * BLK + qg * C::QW + nt * 32 + r32;
-#pragma unroll
-        for (int st = 0; st < D / 16; ++st) {
-            uint4 v = make_uint4(0, 0, 0, 0);
-            if (qn < a.N)
-                v = *reinterpret_cast<const uint4*>(a.Q + head_off + (int64_t)qn * D + st * 16 + h * 8);
-            qf[nt][st] = as_bf16x8(v);
-        }
+    for (int st = 0; st < D / 16; ++st) {
+        uint4 v = make_uint4(0, 0, 0, 0);
+        if (qn < a.N) v = *reinterpret_cast<const uint4*>(a.Q + head_off + (int64_t)qn * D + st * 16 + h * 8);
+        qf[st] = as_bf16x8(v);
     }
 
-    const int beg = a.row_ptr[row], end = a.row_ptr[row + 1];
-    const int nk = end - beg;
+    const int beg = __builtin_amdgcn_readfirstlane(a.row_ptr[row]);
+    const int nk = __builtin_amdgcn_readfirstlane(a.row_ptr[row + 1]) - beg;
     const int T = nk + (COMP ? a.ntc : 0);
     // the row's kept blocks (clamped into range) and, for compensation, flags
     if constexpr (COMP)
@@ -214,226 +235,237 @@ __device__ __forceinline__ void process_row(const FwdArgs& a, int64_t row, unsig
         __syncthreads();
     }
 
-    // per-lane DMA source offsets (full tiles; the clamped set for a short block)
-    constexpr int KI = C::K_BYTES / (1024 * C::NW), VI = C::V_BYTES / (1024 * C::NW);
-    uint32_t koff[KI], voff[VI];
-#pragma unroll
-    for (int n = 0; n < KI; ++n) koff[n] = dma_src_offset<C::KRB, C::NW>(n, wave, lane, BLK - 1);
-#pragma unroll
-    for (int n = 0; n < VI; ++n) voff[n] = dma_src_offset<C::VRB, C::NW>(n, wave, lane, D - 1);
-
-    // Issues the HBM -> LDS copies of tile t into stage buffer b and writes its
-    // key bias (0 / -inf for a short last block; log2 n_j / -inf for centroids).
-    const float inv_c = 1.f / a.c;
-    auto issue = [&](int t, int b) {
-        unsigned char* st = smem + b * C::STAGE;
-        float* bias = reinterpret_cast<float*>(st + C::K_BYTES + C::V_BYTES);
-        if (!COMP || t < nk) {
-            const int j = __builtin_amdgcn_readfirstlane(list[t]);
-            const unsigned char* kb = Kh + (int64_t)j * BLK * C::KRB;
-            const unsigned char* vb = Vth + (int64_t)j * D * C::VRB;
-            const int nval = j == a.nb - 1 ? last_n : BLK;
-            if (nval == BLK) {
-                dma_tile<BLK, C::KRB, C::NW>(st, kb, koff, wave);
-            } else {
-                uint32_t ko[KI];
-#pragma unroll
-                for (int n = 0; n < KI; ++n) ko[n] = dma_src_offset<C::KRB, C::NW>(n, wave, lane, nval - 1);
-                dma_tile<BLK, C::KRB, C::NW>(st, kb, ko, wave);
-                for (int r = tid; r < BLK; r += C::NT) bias[r] = r < nval ? 0.f : -INFINITY;
-            }
-            dma_tile<D, C::VRB, C::NW>(st + C::K_BYTES, vb, voff, wave);
+    // copies of tile u (kept block list[u], or centroid tile u - nk) into slot b
+    auto issue_k = [&](int u, int b) {
+        unsigned char* dst = kslot + b * C::K_BYTES;
+        if (!COMP || u < nk) {
+            const int j = __builtin_amdgcn_readfirstlane(list[u]);
+            const unsigned char* src = Kh + (int64_t)j * BLK * C::KRB;
+            // a short last block has its rows clamped (finite, masked by the bias)
+            dma_tile<C::KRB, C::KI, C::NWI>(dst, src, j == a.nb - 1 ? last_n - 1 : BLK - 1, wave, lane);
         } else {
-            const int tc = t - nk;
-            const int j0 = tc * BLK;
+            const int j0 = (u - nk) * BLK;
             const int nval = a.nb - j0 < BLK ? a.nb - j0 : BLK;
-            const unsigned char* kb =
-                reinterpret_cast<const unsigned char*>(a.kbar + (bh * a.nb + j0) * (int64_t)D);
-            uint32_t ko[KI];
-#pragma unroll
-            for (int n = 0; n < KI; ++n) ko[n] = dma_src_offset<C::KRB, C::NW>(n, wave, lane, nval - 1);
-            dma_tile<BLK, C::KRB, C::NW>(st, kb, ko, wave);
-            const unsigned char* vb = reinterpret_cast<const unsigned char*>(
-                a.vbart + (bh * a.ntc + tc) * (int64_t)D * BLK);
-            dma_tile<D, C::VRB, C::NW>(st + C::K_BYTES, vb, voff, wave);
-            for (int r = tid; r < BLK; r += C::NT) {
-                const int j = j0 + r;
-                float bv = -INFINITY;
-                if (j < a.nb && !kept[j]) bv = __log2f((float)(j == a.nb - 1 ? last_n : BLK)) * inv_c;
-                bias[r] = bv;
-            }
+            dma_tile<C::KRB, C::KI, C::NWI>(dst, reinterpret_cast<const unsigned char*>(
+                                                     a.kbar + (bh * a.nb + j0) * (int64_t)D),
+                                            nval - 1, wave, lane);
         }
     };
+    auto issue_v = [&](int u, int b) {
+        unsigned char* dst = vslot + b * C::V_BYTES;
+        const unsigned char* src;
+        if (!COMP || u < nk)
+            src = Vth + (int64_t)__builtin_amdgcn_readfirstlane(list[u]) * D * C::VRB;
+        else
+            src = reinterpret_cast<const unsigned char*>(a.vbart + (bh * a.ntc + (u - nk)) * (int64_t)D * BLK);
+        dma_tile<C::VRB, C::VI, C::NWI>(dst, src, D - 1, wave, lane);
+    };
 
-    f32x16 oacc[D / 32][NQT];
+    f32x16 oacc[D / 32];
 #pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-        for (int nt = 0; nt < NQT; ++nt) oacc[dt][nt] = f32x16{};
-    float m_run[NQT], l_run[NQT];
-#pragma unroll
-    for (int nt = 0; nt < NQT; ++nt) { m_run[nt] = -INFINITY; l_run[nt] = 0.f; }
-
-    // One KV tile for this wave: S^T = K Q^T over its key half, online softmax
-    // (log2 domain, lazy rescale), O^T += V^T P^T.  Operands are streamed from
-    // LDS.  A tile with masked or weighted keys (short last block: -inf past its
-    // end; centroid tiles: log2 n_j, -inf for kept blocks) adds its key bias,
-    // stored divided by the log2-domain scale c, to the raw scores; the max is
-    // taken on raw scores (c > 0), and c s - m is one FMA.
+    for (int dt = 0; dt < D / 32; ++dt) oacc[dt] = f32x16{};
+    float m_run = -INFINITY, l_run = 0.f;
+    f32x16 s[C::KTW];            // S^T of the next tile (matrix phase -> vector phase)
+    bf16x8 pb[C::KTW][2];        // P^T of the current tile (vector phase -> matrix phase)
     const bf16x2 kOnes2 = {(__bf16)1.f, (__bf16)1.f};
-    auto attend = [&](const unsigned char* Ks, const unsigned char* Vs, const float* bias,
-                      bool biased) {
-        f32x16 s[C::KTW][NQT];
+    const float inv_c = 1.f / a.c;
+    const float lb_full = __log2f((float)BLK) * inv_c, lb_last = __log2f((float)last_n) * inv_c;
+
+    // Matrix phase of step t: O^T += V_t^T P_t^T (PV) and S^T = K_{t+1} Q^T (S),
+    // interleaved so that the accumulator chains alternate.  Operand reads run
+    // PF instructions ahead of the matrix-core instructions that consume them.
+    auto matrix_phase = [&](auto do_pv, auto do_s, int t) {
+        constexpr bool DS = decltype(do_s)::value, DP = decltype(do_pv)::value;
+        constexpr int NOP = (DS ? C::NSTEP : 0) + (DP ? C::NSTEP : 0);
+        constexpr int PF = SA_PF;
+        const unsigned char* Ks = kslot + ((t + 1) & 1) * C::K_BYTES;
+        const unsigned char* Vs = vslot + (t & 1) * C::V_BYTES;
+        // op k: S step k/2 (even) and PV step k/2 (odd) when both run
+        auto is_s = [&](int k) { return DS && (!DP || (k & 1) == 0); };
+        auto step = [&](int k) { return DS && DP ? k >> 1 : k; };
+        auto load = [&](int k) -> bf16x8 {
+            const int u = step(k);
+            if (is_s(k)) {
+                const int kt = u % C::KTW, st = u / C::KTW;
+                const int krow = kh * C::KH + kt * 32 + swap23(r32);
+                const int pos = (st * 2 + h) ^ (krow & (C::KCH - 1));
+                return as_bf16x8(*reinterpret_cast<const uint4*>(Ks + krow * C::KRB + pos * 16));
+            }
+            const int dt = u % (D / 32), q = u / (D / 32);
+            const int kt = q >> 1, s2 = q & 1;
+            const int d = dt * 32 + r32;
+            const int chunk = (kh * C::KH + kt * 32 + 16 * s2 + 8 * h) / 8;
+            const int pos = chunk ^ (d & (C::VCH - 1));
+            return as_bf16x8(*reinterpret_cast<const uint4*>(Vs + d * C::VRB + pos * 16));
+        };
+        bf16x8 ring[PF];
+#pragma unroll
+        for (int k = 0; k < PF && k < NOP; ++k) ring[k] = load(k);
+#pragma unroll
+        for (int k = 0; k < NOP; ++k) {
+            const bf16x8 op = ring[k % PF];
+            if (k + PF < NOP) ring[k % PF] = load(k + PF);
+            const int u = step(k);
+            if (is_s(k)) {
+                const int kt = u % C::KTW, st = u / C::KTW;
+                s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op, qf[st], st == 0 ? f32x16{} : s[kt], 0, 0, 0);
+            } else {
+                const int dt = u % (D / 32), q = u / (D / 32);
+                oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op, pb[q >> 1][q & 1], oacc[dt], 0, 0, 0);
+            }
+        }
+#if SA_SGB
+        // keep the order: PF reads, then (1 read, 1 MFMA) pairs, then the tail
+#pragma unroll
+        for (int k = 0; k < PF && k < NOP; ++k) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+#pragma unroll
+        for (int k = 0; k < NOP; ++k) {
+            if (k + PF < NOP) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        }
+#endif
+    };
+
+    // Vector phase: online softmax of S^T of tile u into P^T.  A tile with
+    // masked or weighted keys (short last block: -inf past its end; centroid
+    // tile: log2 n_j, -inf for kept blocks and past nb) adds that key bias,
+    // divided by the log2-domain scale c, to the raw scores; the max is taken on
+    // raw scores (c > 0), and c s - m is one FMA.
+    auto vector_phase = [&](int u) {
+        const bool cent = COMP && u >= nk;
+        int nval = BLK;
+        if (!cent && last_n < BLK && __builtin_amdgcn_readfirstlane(list[u]) == a.nb - 1) nval = last_n;
+        if (cent || nval < BLK) {
+            const int j0 = (u - nk) * BLK;
+#pragma unroll
+            for (int kt = 0; kt < C::KTW; ++kt)
+#pragma unroll
+                for (int g = 0; g < 4; ++g)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int key = kh * C::KH + kt * 32 + 16 * (g >> 1) + 8 * h + 4 * (g & 1) + e;
+                        float b;
+                        if (cent) {
+                            const int j = j0 + key;
+                            b = (j < a.nb && !kept[j]) ? (j == a.nb - 1 ? lb_last : lb_full) : -INFINITY;
+                        } else {
+                            b = key < nval ? 0.f : -INFINITY;
+                        }
+                        s[kt][4 * g + e] += b;
+                    }
+        }
+        float mx = -INFINITY;
 #pragma unroll
         for (int kt = 0; kt < C::KTW; ++kt)
 #pragma unroll
-            for (int nt = 0; nt < NQT; ++nt) s[kt][nt] = f32x16{};
+            for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[kt][e]);
+        mx = xmax32(mx) * a.c;
+        if (mx > m_run + kLazy) {
+            const float alpha = __builtin_amdgcn_exp2f(m_run - mx);
+            l_run *= alpha;
 #pragma unroll
-        for (int st = 0; st < D / 16; ++st)
+            for (int dt = 0; dt < D / 32; ++dt) oacc[dt] *= alpha;
+            m_run = mx;
+        }
+        const float nbase = m_run == -INFINITY ? 0.f : -m_run;
+        // the row sum adds the bf16 weights that enter P V
+        float sum = l_run;
 #pragma unroll
-            for (int kt = 0; kt < C::KTW; ++kt) {
-                const int krow = kh * C::KH + kt * 32 + swap23(r32);
-                const int pos = (st * 2 + h) ^ (krow & (C::KCH - 1));
-                const bf16x8 kop = as_bf16x8(*reinterpret_cast<const uint4*>(Ks + krow * C::KRB + pos * 16));
+        for (int kt = 0; kt < C::KTW; ++kt)
 #pragma unroll
-                for (int nt = 0; nt < NQT; ++nt)
-                    s[kt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qf[nt][st], s[kt][nt], 0, 0, 0);
+            for (int s2 = 0; s2 < 2; ++s2) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    pb[kt][s2][e] = (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(s[kt][8 * s2 + e], a.c, nbase));
+                const bf16x8 w = pb[kt][s2];
+                sum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(w, w, 0, 1), kOnes2, sum, false);
+                sum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(w, w, 2, 3), kOnes2, sum, false);
+                sum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(w, w, 4, 5), kOnes2, sum, false);
+                sum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(w, w, 6, 7), kOnes2, sum, false);
             }
-        if (biased) {
-#pragma unroll
-            for (int kt = 0; kt < C::KTW; ++kt)
-#pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const int key = kh * C::KH + kt * 32 + 16 * (g >> 1) + 8 * h + 4 * (g & 1);
-                    const float4 bv = *reinterpret_cast<const float4*>(bias + key);
-                    const float b4[4] = {bv.x, bv.y, bv.z, bv.w};
-#pragma unroll
-                    for (int nt = 0; nt < NQT; ++nt)
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) s[kt][nt][4 * g + e] += b4[e];
-                }
-        }
-
-        bf16x8 pb[C::KTW][2][NQT];
-#pragma unroll
-        for (int nt = 0; nt < NQT; ++nt) {
-            float mx = -INFINITY;
-#pragma unroll
-            for (int kt = 0; kt < C::KTW; ++kt)
-#pragma unroll
-                for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[kt][nt][e]);
-            mx = xmax32(mx) * a.c;
-            if (mx > m_run[nt] + kLazy) {
-                const float alpha = __builtin_amdgcn_exp2f(m_run[nt] - mx);
-                l_run[nt] *= alpha;
-#pragma unroll
-                for (int dt = 0; dt < D / 32; ++dt) oacc[dt][nt] *= alpha;
-                m_run[nt] = mx;
-            }
-            const float nbase = m_run[nt] == -INFINITY ? 0.f : -m_run[nt];
-            // the row sum adds the bf16 weights that enter P V
-            float sum = l_run[nt];
-#pragma unroll
-            for (int kt = 0; kt < C::KTW; ++kt)
-#pragma unroll
-                for (int s2 = 0; s2 < 2; ++s2) {
-#pragma unroll
-                    for (int e = 0; e < 8; ++e)
-                        pb[kt][s2][nt][e] =
-                            (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(s[kt][nt][8 * s2 + e], a.c, nbase));
-                    const bf16x8 w = pb[kt][s2][nt];
-                    sum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(w, w, 0, 1), kOnes2, sum, false);
-                    sum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(w, w, 2, 3), kOnes2, sum, false);
-                    sum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(w, w, 4, 5), kOnes2, sum, false);
-                    sum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(w, w, 6, 7), kOnes2, sum, false);
-                }
-            l_run[nt] = sum;
-        }
-
-#pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt) {
-            const int d = dt * 32 + r32;
-#pragma unroll
-            for (int kt = 0; kt < C::KTW; ++kt)
-#pragma unroll
-                for (int s2 = 0; s2 < 2; ++s2) {
-                    const int chunk = (kh * C::KH + kt * 32 + 16 * s2 + 8 * h) / 8;
-                    const int pos = chunk ^ (d & (C::VCH - 1));
-                    const bf16x8 vop = as_bf16x8(*reinterpret_cast<const uint4*>(Vs + d * C::VRB + pos * 16));
-#pragma unroll
-                    for (int nt = 0; nt < NQT; ++nt)
-                        oacc[dt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pb[kt][s2][nt], oacc[dt][nt], 0, 0, 0);
-                }
-        }
+        l_run = sum;
     };
 
-    if (T > 0) issue(0, 0);
-    for (int t = 0; t < T; ++t) {
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
-        if (t + 1 < T) issue(t + 1, (t + 1) & 1);
-        const unsigned char* Ks = smem + (t & 1) * C::STAGE;
-        const unsigned char* Vs = Ks + C::K_BYTES;
-        const float* bias = reinterpret_cast<const float*>(Vs + C::V_BYTES);
-        bool biased = COMP && t >= nk;
-        if (!biased) biased = last_n < BLK && __builtin_amdgcn_readfirstlane(list[t]) == a.nb - 1;
-        attend(Ks, Vs, bias, biased);
+    // Pipeline over the T tiles.  Step t (t = -1 .. T-1) = matrix phase (P_t V_t,
+    // S_{t+1}; the issuing waves start the copies of K_{t+2} and V_{t+1}), then
+    // vector phase (softmax of S_{t+1}).  A barrier precedes each phase; the
+    // lagging group passes one extra barrier first, the leading one after the
+    // last step, so both pass the same number.
+    if (T > 0) {
+        if (issuer) issue_k(0, 0);
+        copies_done();
+        wg_barrier();
+        if (lagging) wg_barrier();
+        // step -1: S_0
+        wg_barrier();
+        if (issuer) {
+            if (T > 1) issue_k(1, 1);
+            issue_v(0, 0);
+        }
+        matrix_phase(no{}, yes{}, -1);
+        if (C::PING) wg_barrier();
+        vector_phase(0);
+        copies_done();
+        for (int t = 0; t + 1 < T; ++t) {
+            wg_barrier();
+            if (issuer) {
+                if (t + 2 < T) issue_k(t + 2, t & 1);
+                issue_v(t + 1, (t + 1) & 1);
+            }
+            matrix_phase(yes{}, yes{}, t);
+            if (C::PING) wg_barrier();
+            vector_phase(t + 1);
+            copies_done();
+        }
+        // step T-1: P_{T-1} V_{T-1}
+        wg_barrier();
+        matrix_phase(yes{}, no{}, T - 1);
+        if (C::PING) wg_barrier();
+        if (C::PING && !lagging) wg_barrier();
     }
 
     // merge the two key halves of every query group, then write O and lse
-    float l_tot[NQT];
-#pragma unroll
-    for (int nt = 0; nt < NQT; ++nt) l_tot[nt] = xsum32(l_run[nt]);
-    __syncthreads();                                   // stage buffers are free
+    const float l_tot = xsum32(l_run);
+    __syncthreads();                                   // tile slots are free
     float4* mo = reinterpret_cast<float4*>(smem + qg * (C::MERGE / C::NWQ));
-    float* ml = reinterpret_cast<float*>(smem + qg * (C::MERGE / C::NWQ) + NQT * (D / 32) * 64 * 16 * 4);
+    float* ml = reinterpret_cast<float*>(smem + qg * (C::MERGE / C::NWQ) + (D / 32) * 64 * 16 * 4);
     if (kh == 1) {
 #pragma unroll
         for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
-            for (int nt = 0; nt < NQT; ++nt)
-#pragma unroll
-                for (int g = 0; g < 4; ++g)
-                    mo[((dt * NQT + nt) * 4 + g) * 64 + lane] =
-                        make_float4(oacc[dt][nt][4 * g], oacc[dt][nt][4 * g + 1],
-                                    oacc[dt][nt][4 * g + 2], oacc[dt][nt][4 * g + 3]);
-        if (h == 0)
-#pragma unroll
-            for (int nt = 0; nt < NQT; ++nt) {
-                ml[nt * 32 + r32] = m_run[nt];
-                ml[NQT * 32 + nt * 32 + r32] = l_tot[nt];
-            }
+            for (int g = 0; g < 4; ++g)
+                mo[(dt * 4 + g) * 64 + lane] = make_float4(oacc[dt][4 * g], oacc[dt][4 * g + 1],
+                                                           oacc[dt][4 * g + 2], oacc[dt][4 * g + 3]);
+        if (h == 0) {
+            ml[r32] = m_run;
+            ml[32 + r32] = l_tot;
+        }
     }
     __syncthreads();
     if (kh == 0) {
+        const float m1 = ml[r32], l1 = ml[32 + r32];
+        const float m = fmaxf(m_run, m1);
+        const float mb = m == -INFINITY ? 0.f : m;
+        const float a0 = __builtin_amdgcn_exp2f(m_run - mb), a1 = __builtin_amdgcn_exp2f(m1 - mb);
+        const float l = l_tot * a0 + l1 * a1;
+        const float inv = l > 0.f ? 1.f / l : 0.f;
+        if (qn < a.N) {
+            uint16_t* orow = a.O + head_off + (int64_t)qn * D;
 #pragma unroll
-        for (int nt = 0; nt < NQT; ++nt) {
-            const float m1 = ml[nt * 32 + r32], l1 = ml[NQT * 32 + nt * 32 + r32];
-            const float m0 = m_run[nt];
-            const float m = fmaxf(m0, m1);
-            const float mb = m == -INFINITY ? 0.f : m;
-            const float a0 = __builtin_amdgcn_exp2f(m0 - mb), a1 = __builtin_amdgcn_exp2f(m1 - mb);
-            const float l = l_tot[nt] * a0 + l1 * a1;
-            const float inv = l > 0.f ? 1.f / l : 0.f;
-            const int qn = i * BLK + qg * C::QW + nt * 32 + r32;
-            if (qn < a.N) {
-                uint16_t* orow = a.O + head_off + (int64_t)qn * D;
+            for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
-                for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-                    for (int g = 0; g < 4; ++g) {
-                        const float4 o1 = mo[((dt * NQT + nt) * 4 + g) * 64 + lane];
-                        const float v0 = (oacc[dt][nt][4 * g + 0] * a0 + o1.x * a1) * inv;
-                        const float v1 = (oacc[dt][nt][4 * g + 1] * a0 + o1.y * a1) * inv;
-                        const float v2 = (oacc[dt][nt][4 * g + 2] * a0 + o1.z * a1) * inv;
-                        const float v3 = (oacc[dt][nt][4 * g + 3] * a0 + o1.w * a1) * inv;
-                        const uint32_t lo = f32_to_bf16_rne(v0) | ((uint32_t)f32_to_bf16_rne(v1) << 16);
-                        const uint32_t hi = f32_to_bf16_rne(v2) | ((uint32_t)f32_to_bf16_rne(v3) << 16);
-                        *reinterpret_cast<uint2*>(orow + dt * 32 + 8 * g + 4 * h) = make_uint2(lo, hi);
-                    }
-                if (a.lse && h == 0)
-                    a.lse[bh * (int64_t)a.N + qn] = l > 0.f ? (m + __log2f(l)) * kLn2 : -INFINITY;
-            }
+                for (int g = 0; g < 4; ++g) {
+                    const float4 o1 = mo[(dt * 4 + g) * 64 + lane];
+                    const float v0 = (oacc[dt][4 * g + 0] * a0 + o1.x * a1) * inv;
+                    const float v1 = (oacc[dt][4 * g + 1] * a0 + o1.y * a1) * inv;
+                    const float v2 = (oacc[dt][4 * g + 2] * a0 + o1.z * a1) * inv;
+                    const float v3 = (oacc[dt][4 * g + 3] * a0 + o1.w * a1) * inv;
+                    const uint32_t lo = f32_to_bf16_rne(v0) | ((uint32_t)f32_to_bf16_rne(v1) << 16);
+                    const uint32_t hi = f32_to_bf16_rne(v2) | ((uint32_t)f32_to_bf16_rne(v3) << 16);
+                    *reinterpret_cast<uint2*>(orow + dt * 32 + 8 * g + 4 * h) = make_uint2(lo, hi);
+                }
+            if (a.lse && h == 0)
+                a.lse[bh * (int64_t)a.N + qn] = l > 0.f ? (m + __log2f(l)) * kLn2 : -INFINITY;
         }
     }
 }
@@ -444,7 +476,7 @@ __device__ __forceinline__ void process_row(const FwdArgs& a, int64_t row, unsig
 // blocks that share K/V blocks in that XCD's L2.  A workgroup whose range is
 // exhausted takes rows from the other ranges.
 template <int D, int BLK, bool COMP>
-__global__ __launch_bounds__(BLK * 4 / NQT) __attribute__((amdgpu_waves_per_eu(NQT == 1 ? 2 : 1)))
+__global__ __launch_bounds__(BLK * 4) __attribute__((amdgpu_waves_per_eu(2)))
 void k_bsattn_fwd(FwdArgs a) {
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     __shared__ int s_row;
@@ -464,6 +496,12 @@ void k_bsattn_fwd(FwdArgs a) {
             process_row<D, BLK, COMP>(a, row, smem);
         }
     }
+}
+
+// Zeroes the 8 per-XCD pull counters before an attention launch (a kernel,
+// not a memset, so that the sequence can be captured in a graph).
+__global__ void k_reset_pull(int32_t* __restrict__ sched) {
+    if (threadIdx.x < 8) sched[16 + threadIdx.x] = 0;
 }
 
 // Splits the R rows into 8 contiguous ranges of (nearly) equal work, where a
@@ -610,11 +648,12 @@ WsLayout ws_layout(const Geometry& g, bool comp) {
     return L;
 }
 
+// Preparation: V re-laid out block by block, the centroid tiles with
+// compensation, and the per-XCD row ranges.
 template <int D, int BLK, bool COMP>
-sa_status launch_t(const FwdArgs& a, const Geometry& g, const uint16_t* V, uint16_t* vt,
-                   const float* k_mean, const float* v_sum, uint16_t* kbar, uint16_t* vbart,
-                   hipStream_t stream) {
-    using C = Cfg<D, BLK>;
+sa_status prepare_t(const FwdArgs& a, const Geometry& g, const uint16_t* V, uint16_t* vt,
+                    const float* k_mean, const float* v_sum, uint16_t* kbar, uint16_t* vbart,
+                    hipStream_t stream) {
     hipLaunchKernelGGL((k_vt_prep<D, BLK>), dim3(g.nb, (unsigned)g.BH()), dim3(256), 0, stream, V,
                        vt, g.N, g.nb);
     sa_status st = hip_check(hipGetLastError(), "k_vt_prep launch");
@@ -624,6 +663,17 @@ sa_status launch_t(const FwdArgs& a, const Geometry& g, const uint16_t* V, uint1
                            k_mean, v_sum, kbar, vbart, g.nb, a.ntc, g.N - (g.nb - 1) * BLK);
         if ((st = hip_check(hipGetLastError(), "k_comp_prep launch")) != SA_OK) return st;
     }
+    if (a.rows == 0) return SA_OK;
+    hipLaunchKernelGGL(k_sched, dim3(1), dim3(kSchedThreads), 0, stream, a.row_ptr, a.sched,
+                       a.rows, (COMP ? a.ntc : 0) + 2);
+    return hip_check(hipGetLastError(), "k_sched launch");
+}
+
+// The attention kernel on a persistent grid.
+template <int D, int BLK, bool COMP>
+sa_status run_t(const FwdArgs& a, const Geometry& g, hipStream_t stream) {
+    using C = Cfg<D, BLK>;
+    sa_status st = SA_OK;
     const size_t lds = C::BASE + C::MAX_NB + 2 * (size_t)g.nb;
     static bool configured = false;
     if (!configured) {
@@ -635,59 +685,87 @@ sa_status launch_t(const FwdArgs& a, const Geometry& g, const uint16_t* V, uint1
         configured = true;
     }
     if (a.rows == 0) return SA_OK;
-    hipLaunchKernelGGL(k_sched, dim3(1), dim3(kSchedThreads), 0, stream, a.row_ptr, a.sched,
-                       a.rows, (COMP ? a.ntc : 0) + 2);
-    if ((st = hip_check(hipGetLastError(), "k_sched launch")) != SA_OK) return st;
-    // persistent grid: as many workgroups as the chip holds at once
+    // as many workgroups as the chip holds at once (LDS per workgroup depends
+    // on nb, so the answer is cached per size)
     static int resident = 0;
-    if (resident == 0) {
+    static size_t resident_lds = 0;
+    if (resident == 0 || resident_lds != lds) {
         int dev = 0, cus = 0, per_cu = 0;
         if ((st = hip_check(hipGetDevice(&dev), "hipGetDevice")) != SA_OK) return st;
         st = hip_check(hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev),
                        "multiprocessor count");
         if (st != SA_OK) return st;
         st = hip_check(hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                           &per_cu, (const void*)k_bsattn_fwd<D, BLK, COMP>, C::NT,
-                           C::BASE + C::MAX_NB + 2 * C::MAX_NB),
+                           &per_cu, (const void*)k_bsattn_fwd<D, BLK, COMP>, C::NT, lds),
                        "occupancy query");
         if (st != SA_OK) return st;
         resident = cus * (per_cu > 0 ? per_cu : 1);
+        resident_lds = lds;
     }
     const int64_t grid = a.rows < resident ? a.rows : resident;
+    hipLaunchKernelGGL(k_reset_pull, dim3(1), dim3(64), 0, stream, a.sched);
+    if ((st = hip_check(hipGetLastError(), "k_reset_pull launch")) != SA_OK) return st;
     hipLaunchKernelGGL((k_bsattn_fwd<D, BLK, COMP>), dim3((unsigned)grid), dim3(C::NT), lds, stream, a);
     return hip_check(hipGetLastError(), "k_bsattn_fwd launch");
 }
 
-}  // namespace
-
-size_t fwd_workspace_bytes(const Geometry& g, bool comp) { return ws_layout(g, comp).total; }
-
-sa_status launch_fwd(const Geometry& g, const uint16_t* Q, const uint16_t* K, const uint16_t* V,
-                     const int32_t* row_ptr, const int32_t* col_idx, const float* k_mean,
-                     const float* v_sum, uint16_t* O, float* lse, char* ws, hipStream_t stream) {
-    const bool comp = k_mean != nullptr;
-    if (g.nb > 4096) return fail(SA_ERR_UNSUPPORTED, "attention supports nb <= 4096 (got %d)", g.nb);
+FwdArgs make_args(const Geometry& g, bool comp, const uint16_t* Q, const uint16_t* K,
+                  const int32_t* row_ptr, const int32_t* col_idx, uint16_t* O, float* lse, char* ws) {
     const WsLayout L = ws_layout(g, comp);
     FwdArgs a{};
     a.Q = Q; a.K = K; a.row_ptr = row_ptr; a.col_idx = col_idx;
     a.O = O; a.lse = lse; a.N = g.N; a.nb = g.nb; a.rows = g.rows();
     a.ntc = (int32_t)ceil_div(g.nb, g.block);
     a.c = g.scale * kLog2e;
-    uint16_t* vt = reinterpret_cast<uint16_t*>(ws + L.vt);
-    uint16_t* kbar = comp ? reinterpret_cast<uint16_t*>(ws + L.kbar) : nullptr;
-    uint16_t* vbart = comp ? reinterpret_cast<uint16_t*>(ws + L.vbart) : nullptr;
-    a.Vt = vt; a.kbar = kbar; a.vbart = vbart;
+    a.Vt = reinterpret_cast<uint16_t*>(ws + L.vt);
+    a.kbar = comp ? reinterpret_cast<uint16_t*>(ws + L.kbar) : nullptr;
+    a.vbart = comp ? reinterpret_cast<uint16_t*>(ws + L.vbart) : nullptr;
     a.sched = reinterpret_cast<int32_t*>(ws + L.sched);
-#define SA_LAUNCH(D_, B_)                                                                      \
-    return comp ? launch_t<D_, B_, true>(a, g, V, vt, k_mean, v_sum, kbar, vbart, stream)      \
-                : launch_t<D_, B_, false>(a, g, V, vt, k_mean, v_sum, kbar, vbart, stream)
-    if (g.d == 128) {
-        if (g.block == 128) SA_LAUNCH(128, 128);
-        SA_LAUNCH(128, 64);
-    }
-    if (g.block == 128) SA_LAUNCH(64, 128);
-    SA_LAUNCH(64, 64);
-#undef SA_LAUNCH
+    return a;
 }
+
+}  // namespace
+
+size_t fwd_workspace_bytes(const Geometry& g, bool comp) { return ws_layout(g, comp).total; }
+
+#define SA_DISPATCH(CALL)                                   \
+    if (g.d == 128) {                                       \
+        if (g.block == 128) {                               \
+            if (comp) return CALL(128, 128, true);          \
+            return CALL(128, 128, false);                   \
+        }                                                   \
+        if (comp) return CALL(128, 64, true);               \
+        return CALL(128, 64, false);                        \
+    }                                                       \
+    if (g.block == 128) {                                   \
+        if (comp) return CALL(64, 128, true);               \
+        return CALL(64, 128, false);                        \
+    }                                                       \
+    if (comp) return CALL(64, 64, true);                    \
+    return CALL(64, 64, false);
+
+sa_status launch_fwd_prepare(const Geometry& g, const uint16_t* V, const int32_t* row_ptr,
+                             const float* k_mean, const float* v_sum, char* ws, hipStream_t stream) {
+    const bool comp = k_mean != nullptr;
+    if (g.nb > 4096) return fail(SA_ERR_UNSUPPORTED, "attention supports nb <= 4096 (got %d)", g.nb);
+    const FwdArgs a = make_args(g, comp, nullptr, nullptr, row_ptr, nullptr, nullptr, nullptr, ws);
+    uint16_t* vt = const_cast<uint16_t*>(a.Vt);
+    uint16_t* kbar = const_cast<uint16_t*>(a.kbar);
+    uint16_t* vbart = const_cast<uint16_t*>(a.vbart);
+#define SA_PREP(D_, B_, C_) prepare_t<D_, B_, C_>(a, g, V, vt, k_mean, v_sum, kbar, vbart, stream)
+    SA_DISPATCH(SA_PREP)
+#undef SA_PREP
+}
+
+sa_status launch_fwd_run(const Geometry& g, bool comp, const uint16_t* Q, const uint16_t* K,
+                         const int32_t* row_ptr, const int32_t* col_idx, uint16_t* O, float* lse,
+                         char* ws, hipStream_t stream) {
+    if (g.nb > 4096) return fail(SA_ERR_UNSUPPORTED, "attention supports nb <= 4096 (got %d)", g.nb);
+    const FwdArgs a = make_args(g, comp, Q, K, row_ptr, col_idx, O, lse, ws);
+#define SA_RUN(D_, B_, C_) run_t<D_, B_, C_>(a, g, stream)
+    SA_DISPATCH(SA_RUN)
+#undef SA_RUN
+}
+#undef SA_DISPATCH
 
 }  // namespace sa

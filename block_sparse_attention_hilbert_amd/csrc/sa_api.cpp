@@ -218,6 +218,53 @@ SA_API sa_status sparse_attn_select(const sa_problem* prob, const sa_select_spec
                          (char*)workspace, (hipStream_t)stream);
 }
 
+static sa_status check_fwd_workspace(const Geometry& g, bool comp, const void* workspace,
+                                     size_t ws_bytes) {
+    const size_t need = fwd_workspace_bytes(g, comp);
+    if (!workspace) return fail(SA_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", need);
+    if (((uintptr_t)workspace & 255u) != 0)
+        return fail(SA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+    if (ws_bytes < need)
+        return fail(SA_ERR_WORKSPACE, "workspace too small: %zu < %zu bytes", ws_bytes, need);
+    return SA_OK;
+}
+
+SA_API sa_status sparse_attn_fwd_prepare(const sa_problem* prob, const void* V,
+                                         const int32_t* row_ptr, const float* k_mean,
+                                         const float* v_sum, void* workspace, size_t ws_bytes,
+                                         void* stream) {
+    clear_error();
+    Geometry g;
+    sa_status st = check_problem(prob, &g);
+    if (st != SA_OK) return st;
+    if (!V) return fail(SA_ERR_INVALID_ARG, "V is required");
+    if (!aligned16(V)) return fail(SA_ERR_INVALID_ARG, "V must be 16-byte aligned");
+    if (!row_ptr) return fail(SA_ERR_INVALID_ARG, "row_ptr is required");
+    if ((k_mean == nullptr) != (v_sum == nullptr))
+        return fail(SA_ERR_INVALID_ARG, "k_mean and v_sum must be given together");
+    if ((st = check_fwd_workspace(g, k_mean != nullptr, workspace, ws_bytes)) != SA_OK) return st;
+    return launch_fwd_prepare(g, (const uint16_t*)V, row_ptr, k_mean, v_sum, (char*)workspace,
+                              (hipStream_t)stream);
+}
+
+SA_API sa_status sparse_attn_fwd_run(const sa_problem* prob, const void* Q, const void* K,
+                                     const int32_t* row_ptr, const int32_t* col_idx,
+                                     int32_t with_comp, void* O, float* lse, void* workspace,
+                                     size_t ws_bytes, void* stream) {
+    clear_error();
+    Geometry g;
+    sa_status st = check_problem(prob, &g);
+    if (st != SA_OK) return st;
+    if (!Q || !K || !O) return fail(SA_ERR_INVALID_ARG, "Q, K and O are required");
+    if (!aligned16(Q) || !aligned16(K) || !aligned16(O))
+        return fail(SA_ERR_INVALID_ARG, "Q, K, O must be 16-byte aligned");
+    if (!row_ptr || !col_idx) return fail(SA_ERR_INVALID_ARG, "row_ptr and col_idx are required");
+    if (with_comp != 0 && with_comp != 1) return fail(SA_ERR_INVALID_ARG, "with_comp must be 0 or 1");
+    if ((st = check_fwd_workspace(g, with_comp != 0, workspace, ws_bytes)) != SA_OK) return st;
+    return launch_fwd_run(g, with_comp != 0, (const uint16_t*)Q, (const uint16_t*)K, row_ptr,
+                          col_idx, (uint16_t*)O, lse, (char*)workspace, (hipStream_t)stream);
+}
+
 SA_API sa_status sparse_attn_fwd(const sa_problem* prob, const void* Q, const void* K,
                                  const void* V, const int32_t* row_ptr,
                                  const int32_t* col_idx, const float* k_mean,
@@ -233,15 +280,13 @@ SA_API sa_status sparse_attn_fwd(const sa_problem* prob, const void* Q, const vo
     if (!row_ptr || !col_idx) return fail(SA_ERR_INVALID_ARG, "row_ptr and col_idx are required");
     if ((k_mean == nullptr) != (v_sum == nullptr))
         return fail(SA_ERR_INVALID_ARG, "k_mean and v_sum must be given together");
-    const size_t need = fwd_workspace_bytes(g, k_mean != nullptr);
-    if (!workspace) return fail(SA_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", need);
-    if (((uintptr_t)workspace & 255u) != 0)
-        return fail(SA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
-    if (ws_bytes < need)
-        return fail(SA_ERR_WORKSPACE, "workspace too small: %zu < %zu bytes", ws_bytes, need);
-    return launch_fwd(g, (const uint16_t*)Q, (const uint16_t*)K, (const uint16_t*)V, row_ptr,
-                      col_idx, k_mean, v_sum, (uint16_t*)O, lse, (char*)workspace,
-                      (hipStream_t)stream);
+    const bool comp = k_mean != nullptr;
+    if ((st = check_fwd_workspace(g, comp, workspace, ws_bytes)) != SA_OK) return st;
+    st = launch_fwd_prepare(g, (const uint16_t*)V, row_ptr, k_mean, v_sum, (char*)workspace,
+                            (hipStream_t)stream);
+    if (st != SA_OK) return st;
+    return launch_fwd_run(g, comp, (const uint16_t*)Q, (const uint16_t*)K, row_ptr, col_idx,
+                          (uint16_t*)O, lse, (char*)workspace, (hipStream_t)stream);
 }
 
 SA_API const char* sparse_attn_last_error(void) { return g_last_error.c_str(); }

@@ -61,11 +61,11 @@ sa_status launch_select(const Geometry& g, const SelectPlan& p,
 // Workspace of the attention call: V transposed per block (+ centroid tiles).
 size_t fwd_workspace_bytes(const Geometry& g, bool comp);
 
-sa_status launch_fwd(const Geometry& g, const uint16_t* Q, const uint16_t* K,
-                     const uint16_t* V, const int32_t* row_ptr,
-                     const int32_t* col_idx, const float* k_mean,
-                     const float* v_sum, uint16_t* O, float* lse, char* ws,
-                     hipStream_t stream);
+sa_status launch_fwd_prepare(const Geometry& g, const uint16_t* V, const int32_t* row_ptr,
+                             const float* k_mean, const float* v_sum, char* ws, hipStream_t stream);
+sa_status launch_fwd_run(const Geometry& g, bool comp, const uint16_t* Q, const uint16_t* K,
+                         const int32_t* row_ptr, const int32_t* col_idx, uint16_t* O, float* lse,
+                         char* ws, hipStream_t stream);
 
 // ----------------------------------------------------------------------------
 // token reordering (k_permute.hip)

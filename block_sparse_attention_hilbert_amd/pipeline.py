@@ -14,8 +14,8 @@ from typing import Optional
 import numpy as np
 import torch
 
-from . import (Problem, Selection, SelectSpec, alloc_workspace, fwd, hilbert_perm_build,
-               hilbert_permute, hilbert_unpermute, select, workspace_size)
+from . import (Problem, Selection, SelectSpec, alloc_workspace, fwd, fwd_prepare, fwd_run,
+               hilbert_perm_build, hilbert_permute, hilbert_unpermute, select, workspace_size)
 
 
 class BlockSparseAttention:
@@ -69,6 +69,20 @@ class BlockSparseAttention:
         out = self.Op if self.hilbert else self.O
         fwd(self.prob, Q, K, V, rp, ci, self.sel.k_mean, self.sel.v_sum, O=out, lse=self.lse,
             workspace=self.ws_fwd)
+        return out
+
+    def run_fwd_prepare(self, V, row_ptr=None):
+        """First half of run_fwd: V (and the centroids) laid out in the workspace."""
+        rp = self.sel.row_ptr if row_ptr is None else row_ptr
+        fwd_prepare(self.prob, V, rp, self.sel.k_mean, self.sel.v_sum, workspace=self.ws_fwd)
+
+    def run_fwd_attention(self, Q, K, row_ptr=None, col_idx=None):
+        """Second half of run_fwd: the attention kernel alone."""
+        rp = self.sel.row_ptr if row_ptr is None else row_ptr
+        ci = self.sel.col_idx if col_idx is None else col_idx
+        out = self.Op if self.hilbert else self.O
+        fwd_run(self.prob, Q, K, rp, ci, self.spec.want_comp, O=out, lse=self.lse,
+                workspace=self.ws_fwd)
         return out
 
     def unpermute_output(self):

@@ -195,6 +195,32 @@ sa_status sparse_attn_fwd(const sa_problem* prob, const void* Q, const void* K,
                           const float* v_sum, void* O, float* lse,
                           void* workspace, size_t ws_bytes, void* stream);
 
+/*
+ * sparse_attn_fwd in two halves, for callers that reuse the prepared V or time
+ * the attention kernel alone.  sparse_attn_fwd(...) is exactly
+ * sparse_attn_fwd_prepare(...) followed by sparse_attn_fwd_run(...) on the
+ * same stream, workspace and problem.
+ *
+ * sparse_attn_fwd_prepare: writes into the workspace V re-laid out block by
+ *   block ([B,H,nb,d,block] bf16, keys past N zero), with compensation
+ *   (k_mean, v_sum both non-NULL) the bf16 centroid keys and values, and the
+ *   split of the rows into per-XCD work ranges (reads row_ptr).
+ * sparse_attn_fwd_run: the attention kernel.  Reads the workspace written by
+ *   the last sparse_attn_fwd_prepare on this stream, which must have had the
+ *   same prob, the same row_ptr contents and with_comp = (k_mean != NULL);
+ *   this is not checked.  It may be called several times per preparation
+ *   (with other Q, K, O or col_idx of the same row structure).
+ * Arguments, errors and limits as for sparse_attn_fwd.
+ */
+sa_status sparse_attn_fwd_prepare(const sa_problem* prob, const void* V,
+                                  const int32_t* row_ptr, const float* k_mean,
+                                  const float* v_sum, void* workspace,
+                                  size_t ws_bytes, void* stream);
+sa_status sparse_attn_fwd_run(const sa_problem* prob, const void* Q, const void* K,
+                              const int32_t* row_ptr, const int32_t* col_idx,
+                              int32_t with_comp, void* O, float* lse,
+                              void* workspace, size_t ws_bytes, void* stream);
+
 /* Text of the last failure on the calling thread ("" after success). */
 const char* sparse_attn_last_error(void);
 

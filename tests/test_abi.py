@@ -139,3 +139,26 @@ def test_select_and_fwd_reject_before_any_launch():
     assert st == sa.SA_ERR_INVALID_ARG
     assert sa.lib.hilbert_perm_build(0, 1, 1, None, None) == sa.SA_ERR_INVALID_ARG
     assert sa.lib.hilbert_perm_build(300, 1, 1, None, None) == sa.SA_ERR_UNSUPPORTED
+
+
+def test_fwd_halves_reject_before_any_launch():
+    p = _prob().c()
+    vp = ctypes.c_void_p
+    fake = vp(1 << 20)
+    odd = vp((1 << 20) + 8)
+    prep, run = sa.lib.sparse_attn_fwd_prepare, sa.lib.sparse_attn_fwd_run
+    assert prep(ctypes.byref(p), None, fake, None, None, fake, 1 << 30, None) == sa.SA_ERR_INVALID_ARG
+    assert prep(ctypes.byref(p), odd, fake, None, None, fake, 1 << 30, None) == sa.SA_ERR_INVALID_ARG
+    assert prep(ctypes.byref(p), fake, None, None, None, fake, 1 << 30, None) == sa.SA_ERR_INVALID_ARG
+    assert prep(ctypes.byref(p), fake, fake, fake, None, fake, 1 << 30, None) == sa.SA_ERR_INVALID_ARG
+    assert prep(ctypes.byref(p), fake, fake, None, None, fake, 16, None) == sa.SA_ERR_WORKSPACE
+    assert run(ctypes.byref(p), fake, fake, fake, fake, 2, fake, None, fake, 1 << 30,
+               None) == sa.SA_ERR_INVALID_ARG
+    assert run(ctypes.byref(p), None, fake, fake, fake, 0, fake, None, fake, 1 << 30,
+               None) == sa.SA_ERR_INVALID_ARG
+    assert run(ctypes.byref(p), fake, fake, fake, None, 0, fake, None, fake, 1 << 30,
+               None) == sa.SA_ERR_INVALID_ARG
+    # the compensation workspace is larger than the plain one
+    need = sa.workspace_size(_prob())
+    assert run(ctypes.byref(p), fake, fake, fake, fake, 1, fake, None, fake, need - 256,
+               None) == sa.SA_ERR_WORKSPACE
