@@ -45,7 +45,6 @@ namespace sa {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) void lds_void_t;
 
@@ -267,7 +266,6 @@ __device__ __forceinline__ void process_row(const FwdArgs& a, int64_t row, unsig
     float m_run = -INFINITY, l_run = 0.f;
     f32x16 s[C::KTW];            // S^T of the next tile (matrix phase -> vector phase)
     bf16x8 pb[C::KTW][2];        // P^T of the current tile (vector phase -> matrix phase)
-    const bf16x2 kOnes2 = {(__bf16)1.f, (__bf16)1.f};
     const float inv_c = 1.f / a.c;
     const float lb_full = __log2f((float)BLK) * inv_c, lb_last = __log2f((float)last_n) * inv_c;
 
@@ -368,22 +366,22 @@ __device__ __forceinline__ void process_row(const FwdArgs& a, int64_t row, unsig
             m_run = mx;
         }
         const float nbase = m_run == -INFINITY ? 0.f : -m_run;
-        // the row sum adds the bf16 weights that enter P V
-        float sum = l_run;
+        // fp32 row sum in four independent chains (plain adds: the dot-product
+        // instructions share the matrix core's issue and stall behind the
+        // other wave's matrix instructions)
+        float sum4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kt = 0; kt < C::KTW; ++kt)
 #pragma unroll
             for (int s2 = 0; s2 < 2; ++s2) {
 #pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    pb[kt][s2][e] = (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(s[kt][8 * s2 + e], a.c, nbase));
-                const bf16x8 w = pb[kt][s2];
-                sum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(w, w, 0, 1), kOnes2, sum, false);
-                sum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(w, w, 2, 3), kOnes2, sum, false);
-                sum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(w, w, 4, 5), kOnes2, sum, false);
-                sum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(w, w, 6, 7), kOnes2, sum, false);
+                for (int e = 0; e < 8; ++e) {
+                    const float x = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kt][8 * s2 + e], a.c, nbase));
+                    pb[kt][s2][e] = (__bf16)x;
+                    sum4[e & 3] += x;
+                }
             }
-        l_run = sum;
+        l_run += (sum4[0] + sum4[1]) + (sum4[2] + sum4[3]);
     };
 
     // Pipeline over the T tiles.  Step t (t = -1 .. T-1) = matrix phase (P_t V_t,
