@@ -15,6 +15,10 @@ Sources (titles of the pages the method is taken from):
   values of a cluster replaces the skipped ones), section 1 / 2B (selection
   on attention scores under a fixed density budget), section 4 (top-p
   selection), section 2B (streaming update, no materialised logits).
+* "SVG-EAR" again -- section 2B (error-aware routing: the compensation
+  error of every block, probed with the query-cluster centroids standing in
+  for the individual queries, ranks the blocks by error per unit cost under
+  the density budget).
 * "SVOO: Training-Free Sparse Attention ... Bidirectional Co-Clustering" --
   section 2A (density that covers a share of the cumulative attention mass).
 * "LVSA: Training-Free Sparse Attention for Long Video Diffusion" -- abstract
@@ -359,15 +363,62 @@ def anchor_blocks(nb: int, A: int, offset: int) -> np.ndarray:
     return (int(offset) + np.arange(A, dtype=np.int64) * (nb // A)) % nb
 
 
+# ---------------------------------------------------------------------------
+# O4b. error-aware routing (SVG-EAR 2B)
+# ---------------------------------------------------------------------------
+
+def error_keys(Qh: np.ndarray, Kh: np.ndarray, Vh: np.ndarray, block: int,
+               sigma: float) -> np.ndarray:
+    """Routing key of every (query block i, KV block j) of one head, float64 [nb, nb].
+
+    The query block's mean qbar_i stands in for its queries (the page's query
+    centroids; cost O(C_q N_k d) instead of O(N_q N_k d)).  With the logits
+    l_t = sigma * qbar_i . k_t of the tokens t of block j and m = max_t l_t:
+
+      exact contribution     A = sum_t exp(l_t - m) v_t
+      centroid replacement   Ahat = n_j exp(S_ij - m) vbar_j
+
+    where S_ij is the pooled score fl32(sigma * qbar_i . kbar_j) of the
+    score-based rules (the centroid's logit) and vbar_j = fl32(sum_t v_t) / n_j
+    (the block sum the compensation uses).  The key is the log of the
+    compensation error per unit of cost, on one scale for the whole row:
+
+      key = ln ||A - Ahat||_2 + m - ln n_j          (-inf when A == Ahat)
+
+    qbar, kbar are the fp32 block means of the score-based rules; every other
+    step is float64.
+    """
+    b = block_bounds(Qh.shape[0], block)
+    nb = b.size - 1
+    n = np.diff(b).astype(np.float64)
+    qm = block_means(Qh, block).astype(np.float64)
+    S = block_scores(block_means(Qh, block), block_means(Kh, block), sigma).astype(np.float64)
+    vbar = block_sums_f32(Vh, block).astype(np.float64) / n[:, None]
+    keys = np.empty((nb, nb), dtype=np.float64)
+    for j in range(nb):
+        Kj = np.asarray(Kh[b[j]:b[j + 1]], dtype=np.float64)
+        Vj = np.asarray(Vh[b[j]:b[j + 1]], dtype=np.float64)
+        L = sigma * (qm @ Kj.T)                         # [nb, n_j]
+        m = L.max(axis=1)
+        A = np.exp(L - m[:, None]) @ Vj                 # [nb, d]
+        Ahat = (n[j] * np.exp(S[:, j] - m))[:, None] * vbar[j][None, :]
+        err = np.sqrt(((A - Ahat) ** 2).sum(axis=1))
+        with np.errstate(divide="ignore"):
+            keys[:, j] = np.log(err) + m - np.log(n[j])
+    return keys
+
+
 def select_head(Qh: Optional[np.ndarray], Kh: Optional[np.ndarray], *, N: int,
                 block: int, HgW: int, sigma: float, rule: str, k: int = 0,
                 tau: float = 1.0, sub_block: int = 0, diag: bool = False,
                 window_frames: int = -1, n_anchors: int = 0,
-                anchor_offset: int = 0):
+                anchor_offset: int = 0, Vh: Optional[np.ndarray] = None):
     """Keep mask [nb, nb] of one (batch, head) and the scores it was decided on.
 
-    Qh, Kh: exact token values [N, d] (already in the order blocks are formed
-    in).  Returns (keep bool [nb, nb], scores float32 [nb, nb] or None).
+    Qh, Kh (and Vh for the error rule): exact token values [N, d] (already in
+    the order blocks are formed in).  Returns (keep bool [nb, nb], ranking
+    keys [nb, nb] or None): float32 pooled scores for "topk" / "mass", the
+    float64 error keys for "err" (top-k by error per block size, SVG-EAR 2B).
     """
     nb = -(-N // block)
     keep = np.zeros((nb, nb), dtype=bool)
@@ -378,6 +429,11 @@ def select_head(Qh: Optional[np.ndarray], Kh: Optional[np.ndarray], *, N: int,
         else:
             S = block_scores(block_means(Qh, block), block_means(Kh, block), sigma)
         keep |= topk_keep(S, k) if rule == "topk" else mass_keep(S, tau)
+    elif rule == "err":
+        if sub_block:
+            raise ValueError("the error rule works on whole blocks")
+        S = error_keys(Qh, Kh, Vh, block, sigma)
+        keep |= topk_keep(S, k)
     elif rule != "none":
         raise ValueError(rule)
     if diag:
@@ -501,27 +557,30 @@ def head_k(wl, h: int) -> int:
     return 0
 
 
-def select_workload(wl, Q, K, heads=None, anchor_offset: int = 0, perm=None):
-    """Keep masks [B, len(heads), nb, nb] and scores for bf16-bit inputs Q, K.
+def select_workload(wl, Q, K, heads=None, anchor_offset: int = 0, perm=None, V=None):
+    """Keep masks [B, len(heads), nb, nb] and ranking keys for bf16-bit inputs.
 
-    Q, K: uint16 [B, nh, N, d] in raster order; ``perm`` (Hilbert order) is
-    applied first when given.
+    Q, K (and V for the error rule): uint16 [B, nh, N, d] in raster order;
+    ``perm`` (Hilbert order) is applied first when given.
     """
     heads = list(range(wl.H)) if heads is None else list(heads)
     B, nh = Q.shape[0], Q.shape[1]
     keep = np.zeros((B, nh, wl.nb, wl.nb), dtype=bool)
-    scores = np.zeros((B, nh, wl.nb, wl.nb), dtype=np.float32)
+    scores = np.zeros((B, nh, wl.nb, wl.nb), dtype=np.float64 if wl.rule == "err" else np.float32)
     for bi in range(B):
         for hi, h in enumerate(heads):
             q = bf16_to_f64(Q[bi, hi]) if wl.rule != "none" else None
             k = bf16_to_f64(K[bi, hi]) if wl.rule != "none" else None
+            v = bf16_to_f64(V[bi, hi]) if wl.rule == "err" else None
             if perm is not None and q is not None:
                 q, k = permute_tokens(q, perm), permute_tokens(k, perm)
+                if v is not None:
+                    v = permute_tokens(v, perm)
             kk, S = select_head(q, k, N=wl.N, block=wl.block, HgW=wl.Hg * wl.W,
                                 sigma=wl.scale, rule=wl.rule, k=head_k(wl, h),
                                 tau=wl.mass, sub_block=wl.sub_block, diag=wl.diag,
                                 window_frames=wl.window_frames,
-                                n_anchors=wl.n_anchors, anchor_offset=anchor_offset)
+                                n_anchors=wl.n_anchors, anchor_offset=anchor_offset, Vh=v)
             keep[bi, hi] = kk
             if S is not None:
                 scores[bi, hi] = S
