@@ -82,7 +82,8 @@ def cpu_baseline(wl, Q, K, V, budget_s: float = 15.0):
     heads = blocks = 0
     for h in range(wl.H):
         keep, _ = oracle.select_workload(wl, Q[:, h:h + 1], K[:, h:h + 1], heads=[h],
-                                         anchor_offset=off, perm=perm)
+                                         anchor_offset=off, perm=perm,
+                                         V=V[:, h:h + 1] if wl.rule == "err" else None)
         q, k, v = (oracle.bf16_to_f64(x[0, h]) for x in (Q, K, V))
         if perm is not None:
             q, k, v = (oracle.permute_tokens(x, perm) for x in (q, k, v))
@@ -110,6 +111,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", type=int, default=2, help="workload number 1..5")
+    ap.add_argument("--workload", default=None,
+                    help="workload by name (overrides --config), e.g. wan13b_err")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calib-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (counter calibration)")
@@ -136,7 +139,7 @@ def main():
         print(json.dumps({"calib_copy_bytes": n, "launches": 5}))
         return
 
-    wl = W.CONFIGS[args.config]
+    wl = W.by_name(args.workload) if args.workload else W.CONFIGS[args.config]
     log(f"[bench] workload {wl.name}: generating inputs")
     Q, K, V = W.make_qkv(wl)
 

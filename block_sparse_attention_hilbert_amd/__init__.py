@@ -30,8 +30,8 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libsparse_attn.so")
 
 SA_OK, SA_ERR_INVALID_ARG, SA_ERR_UNSUPPORTED, SA_ERR_WORKSPACE, SA_ERR_HIP = range(5)
-SA_RULE_NONE, SA_RULE_TOPK, SA_RULE_MASS = range(3)
-RULES = {"none": SA_RULE_NONE, "topk": SA_RULE_TOPK, "mass": SA_RULE_MASS}
+SA_RULE_NONE, SA_RULE_TOPK, SA_RULE_MASS, SA_RULE_ERR = range(4)
+RULES = {"none": SA_RULE_NONE, "topk": SA_RULE_TOPK, "mass": SA_RULE_MASS, "err": SA_RULE_ERR}
 
 EXPORTS = ("sparse_attn_workspace_size", "hilbert_perm_build", "hilbert_permute",
            "hilbert_unpermute", "sparse_attn_select", "sparse_attn_fwd",

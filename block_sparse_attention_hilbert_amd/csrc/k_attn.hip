@@ -742,6 +742,18 @@ size_t fwd_workspace_bytes(const Geometry& g, bool comp) { return ws_layout(g, c
     if (comp) return CALL(64, 64, true);                    \
     return CALL(64, 64, false);
 
+sa_status launch_vt_layout(const Geometry& g, const uint16_t* V, uint16_t* Vt, hipStream_t stream) {
+    const dim3 grid(g.nb, (unsigned)g.BH());
+    if (g.d == 128) {
+        if (g.block == 128) hipLaunchKernelGGL((k_vt_prep<128, 128>), grid, dim3(256), 0, stream, V, Vt, g.N, g.nb);
+        else hipLaunchKernelGGL((k_vt_prep<128, 64>), grid, dim3(256), 0, stream, V, Vt, g.N, g.nb);
+    } else {
+        if (g.block == 128) hipLaunchKernelGGL((k_vt_prep<64, 128>), grid, dim3(256), 0, stream, V, Vt, g.N, g.nb);
+        else hipLaunchKernelGGL((k_vt_prep<64, 64>), grid, dim3(256), 0, stream, V, Vt, g.N, g.nb);
+    }
+    return hip_check(hipGetLastError(), "k_vt_prep launch");
+}
+
 sa_status launch_fwd_prepare(const Geometry& g, const uint16_t* V, const int32_t* row_ptr,
                              const float* k_mean, const float* v_sum, char* ws, hipStream_t stream) {
     const bool comp = k_mean != nullptr;

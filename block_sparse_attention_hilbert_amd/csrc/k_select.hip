@@ -456,6 +456,11 @@ SelectPlan make_select_plan(const Geometry& g, const sa_select_spec& s) {
     p.off_bits = off; off = align_up(off + (size_t)g.rows() * p.words * sizeof(uint32_t), 256);
     p.off_counts = off; off = align_up(off + (size_t)g.rows() * sizeof(int32_t), 256);
     p.off_k = off; off = align_up(off + (size_t)g.H * sizeof(int32_t), 256);
+    const bool err = s.rule == SA_RULE_ERR;
+    p.off_vt = off;
+    off = align_up(off + (err ? (size_t)g.BH() * g.nb * g.d * g.block * 2 : 0), 256);
+    p.off_keys = off;
+    off = align_up(off + (err ? (size_t)g.rows() * g.nb * sizeof(float) : 0), 256);
     p.total = off;
     return p;
 }
@@ -465,9 +470,13 @@ sa_status launch_select(const Geometry& g, const SelectPlan& p, const int32_t* k
                         int32_t* row_ptr, int32_t* col_idx, float* scores, float* k_mean,
                         float* v_sum, char* ws, hipStream_t stream) {
     const bool scored = p.rule != SA_RULE_NONE;
+    const bool err = p.rule == SA_RULE_ERR;
     float* qm = reinterpret_cast<float*>(ws + p.off_qm);
     float* km = reinterpret_cast<float*>(ws + p.off_km);
-    float* S = scores ? scores : reinterpret_cast<float*>(ws + p.off_scores);
+    // pooled scores; with the error rule they only feed the routing keys,
+    // which take their place as the ranking key (and as the scores output)
+    float* S = (scores && !err) ? scores : reinterpret_cast<float*>(ws + p.off_scores);
+    float* keys = err ? (scores ? scores : reinterpret_cast<float*>(ws + p.off_keys)) : nullptr;
     uint32_t* bits = reinterpret_cast<uint32_t*>(ws + p.off_bits);
     int32_t* counts = reinterpret_cast<int32_t*>(ws + p.off_counts);
     int32_t* k_dev = reinterpret_cast<int32_t*>(ws + p.off_k);
@@ -510,9 +519,16 @@ sa_status launch_select(const Geometry& g, const SelectPlan& p, const int32_t* k
         if (st != SA_OK) return st;
     }
 
+    // 2b. error-aware routing keys
+    if (err) {
+        uint16_t* vt = reinterpret_cast<uint16_t*>(ws + p.off_vt);
+        if ((st = launch_vt_layout(g, V, vt, stream)) != SA_OK) return st;
+        if ((st = launch_route_keys(g, qm, K, vt, v_sum, S, keys, stream)) != SA_OK) return st;
+    }
+
     // 3. selection
     SelectArgs sa{};
-    if (p.rule == SA_RULE_TOPK) {
+    if (p.rule == SA_RULE_TOPK || err) {
         if (g.H <= kInlineHeads) {
             for (int h = 0; h < g.H; ++h) sa.k_inline[h] = k_host[h];
         } else {
@@ -526,9 +542,9 @@ sa_status launch_select(const Geometry& g, const SelectPlan& p, const int32_t* k
             }
         }
     }
-    sa.S = S; sa.k_head = k_dev; sa.bits = bits; sa.counts = counts;
+    sa.S = err ? keys : S; sa.k_head = k_dev; sa.bits = bits; sa.counts = counts;
     sa.H = g.H; sa.N = g.N; sa.nb = g.nb; sa.nb_pad = p.nb_pad; sa.words = p.words;
-    sa.block = g.block; sa.HgW = g.Hg * g.W; sa.rule = p.rule; sa.mass = p.mass;
+    sa.block = g.block; sa.HgW = g.Hg * g.W; sa.rule = err ? SA_RULE_TOPK : p.rule; sa.mass = p.mass;
     sa.diag = p.diag; sa.window_frames = p.window_frames; sa.n_anchors = p.n_anchors;
     sa.anchor_offset = p.anchor_offset;
     const size_t lds = scored ? (size_t)p.nb_pad * 12 + (size_t)p.words * 32

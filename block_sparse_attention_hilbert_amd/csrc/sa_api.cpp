@@ -63,8 +63,15 @@ static sa_status check_problem(const sa_problem* p, Geometry* g) {
 
 static sa_status check_spec(const Geometry& g, const sa_select_spec* s) {
     if (!s) return fail(SA_ERR_INVALID_ARG, "spec is NULL");
-    if (s->rule != SA_RULE_NONE && s->rule != SA_RULE_TOPK && s->rule != SA_RULE_MASS)
+    if (s->rule != SA_RULE_NONE && s->rule != SA_RULE_TOPK && s->rule != SA_RULE_MASS &&
+        s->rule != SA_RULE_ERR)
         return fail(SA_ERR_INVALID_ARG, "unknown rule %d", s->rule);
+    if (s->rule == SA_RULE_ERR) {
+        if (s->want_comp != 1)
+            return fail(SA_ERR_INVALID_ARG, "SA_RULE_ERR needs want_comp = 1");
+        if (s->sub_block != 0)
+            return fail(SA_ERR_INVALID_ARG, "SA_RULE_ERR works on whole blocks (sub_block = 0)");
+    }
     if (s->rule != SA_RULE_NONE && g.nb > 4096)
         return fail(SA_ERR_UNSUPPORTED, "scored rules support nb <= 4096 (got %d)", g.nb);
     if (g.rows() * (int64_t)g.nb > (int64_t)INT32_MAX)
@@ -76,7 +83,7 @@ static sa_status check_spec(const Geometry& g, const sa_select_spec* s) {
                         "sub_block = %d must be 0 or a power of two >= 16 dividing block = %d",
                         sb, g.block);
     }
-    if (s->rule == SA_RULE_TOPK) {
+    if (s->rule == SA_RULE_TOPK || s->rule == SA_RULE_ERR) {
         if (s->topk) {
             for (int h = 0; h < g.H; ++h)
                 if (s->topk[h] < 1)
@@ -87,7 +94,7 @@ static sa_status check_spec(const Geometry& g, const sa_select_spec* s) {
                     return fail(SA_ERR_INVALID_ARG, "density[%d] = %g must be in (0, 1]", h,
                                 (double)s->density[h]);
         } else {
-            return fail(SA_ERR_INVALID_ARG, "SA_RULE_TOPK needs topk or density");
+            return fail(SA_ERR_INVALID_ARG, "SA_RULE_TOPK and SA_RULE_ERR need topk or density");
         }
     }
     if (s->rule == SA_RULE_MASS && !(s->mass > 0.f && s->mass <= 1.f))
@@ -202,7 +209,7 @@ SA_API sa_status sparse_attn_select(const sa_problem* prob, const sa_select_spec
     }
     for (int h = 0; h < g.H; ++h) {
         int64_t k = 0;
-        if (spec->rule == SA_RULE_TOPK) {
+        if (spec->rule == SA_RULE_TOPK || spec->rule == SA_RULE_ERR) {
             if (spec->topk) {
                 k = spec->topk[h];
             } else {

@@ -43,8 +43,9 @@ struct SelectPlan {
     int32_t diag, window_frames, n_anchors;
     int64_t anchor_offset;
     int32_t want_comp;
-    // workspace carve-up (byte offsets)
-    size_t off_qm, off_km, off_scores, off_bits, off_counts, off_k, total;
+    // workspace carve-up (byte offsets); the error rule adds V re-laid out
+    // per block and its routing keys
+    size_t off_qm, off_km, off_scores, off_bits, off_counts, off_k, off_vt, off_keys, total;
 };
 
 SelectPlan make_select_plan(const Geometry& g, const sa_select_spec& s);
@@ -56,8 +57,22 @@ sa_status launch_select(const Geometry& g, const SelectPlan& p,
                         float* v_sum, char* ws, hipStream_t stream);
 
 // ----------------------------------------------------------------------------
+// error-aware routing keys (k_route.hip)
+// ----------------------------------------------------------------------------
+// keys[(bh*nb + i)*nb + j] for every query block i and KV block j from the
+// query block means qm [BH,nb,d], K [BH,N,d], V re-laid out per block
+// Vt [BH,nb,d,block], the block sums v_sum [BH,nb,d] and the pooled scores
+// S [BH*nb, nb].
+sa_status launch_route_keys(const Geometry& g, const float* qm, const uint16_t* K,
+                            const uint16_t* Vt, const float* v_sum, const float* S, float* keys,
+                            hipStream_t stream);
+
+// ----------------------------------------------------------------------------
 // attention (k_attn.hip)
 // ----------------------------------------------------------------------------
+// V re-laid out block by block, [BH, nb, d, block] (keys past N are zero).
+sa_status launch_vt_layout(const Geometry& g, const uint16_t* V, uint16_t* Vt, hipStream_t stream);
+
 // Workspace of the attention call: V transposed per block (+ centroid tiles).
 size_t fwd_workspace_bytes(const Geometry& g, bool comp);
 

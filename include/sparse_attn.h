@@ -78,8 +78,10 @@ typedef struct {
 enum {
     SA_RULE_NONE = 0,     /* structural blocks only (window, anchors, diagonal) */
     SA_RULE_TOPK = 1,     /* k highest pooled scores per query block  [EAR 2B] */
-    SA_RULE_MASS = 2      /* shortest score-ranked prefix reaching `mass` of the
+    SA_RULE_MASS = 2,     /* shortest score-ranked prefix reaching `mass` of the
                              softmax mass of the pooled scores  [EAR 4, SVOO 2A] */
+    SA_RULE_ERR = 3       /* k largest compensation errors per block size  [EAR 2B
+                             error-aware routing]; needs want_comp, whole blocks */
 };
 
 /* Selection rule.  Host-side struct; `topk` and `density` are host arrays. */
@@ -150,13 +152,25 @@ sa_status hilbert_unpermute(const sa_problem* prob, const void* src, void* dst,
  * fused-multiply-add chain over the d channels; with sub_block, qbar/kbar are
  * sub-block means and S[i,j] is the max over the sub-block pairs of (i, j).
  *
+ * SA_RULE_ERR [EAR 2B] ranks the blocks of row i by the compensation error of
+ * block j probed with the query block's mean qbar_i (the query centroid):
+ *   m = max_t scale*qbar_i.k_t over the tokens t of block j,
+ *   A = sum_t exp(scale*qbar_i.k_t - m) v_t,  Ahat = n_j exp(S[i,j] - m) vbar_j,
+ *   key[i,j] = ln ||A - Ahat||_2 + m - ln n_j   (-inf when A == Ahat),
+ * with vbar_j = fl32(sum_t v_t) / n_j, and keeps the k largest keys (k from
+ * topk / density as for SA_RULE_TOPK; ties by lower j).  It requires
+ * want_comp = 1 (the error is that of the compensation) and sub_block = 0.
+ * The probe is computed on the matrix cores with bf16 hi/lo splits of qbar
+ * and of the exponentials (about 16 significant bits), fp32 accumulation.
+ *
  * Q, K: device bf16 [B,H,N,d] (ignored for SA_RULE_NONE).  V: device bf16, used
- *   only when want_comp (else may be NULL).
+ *   when want_comp (else may be NULL).
  * row_ptr: device int32 [B*H*nb + 1]; col_idx: device int32, capacity
  *   B*H*nb*nb.  Row r = (b*H + h)*nb + i lists its kept KV blocks in
  *   col_idx[row_ptr[r] .. row_ptr[r+1]), strictly ascending.
- * scores: optional device fp32 [B*H*nb*nb] receiving S (NULL: not written;
- *   never written for SA_RULE_NONE).
+ * scores: optional device fp32 [B*H*nb*nb] receiving the ranking key: S for
+ *   TOPK / MASS, key for ERR (NULL: not written; never written for
+ *   SA_RULE_NONE).
  * k_mean, v_sum: device fp32 [B,H,nb,d] when want_comp (block means of K;
  *   fp32 block sums of V), else NULL.
  * workspace: device, 256-byte aligned, >= sparse_attn_workspace_size(prob, spec).

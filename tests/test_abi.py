@@ -77,7 +77,10 @@ def test_spec_validation():
            sa.SelectSpec(rule="mass", sub_block=256),
            sa.SelectSpec(rule="none", window_frames=-2),
            sa.SelectSpec(rule="none", n_anchors=5),               # nb = 4
-           sa.SelectSpec(rule="none", n_anchors=1, anchor_offset=-1)]
+           sa.SelectSpec(rule="none", n_anchors=1, anchor_offset=-1),
+           sa.SelectSpec(rule="err", density=[0.5, 0.5]),                 # no compensation
+           sa.SelectSpec(rule="err", want_comp=True),                     # no k, no density
+           sa.SelectSpec(rule="err", density=[0.5, 0.5], want_comp=True, sub_block=16)]
     for s in bad:
         assert _err(sa.workspace_size, p, s) == sa.SA_ERR_INVALID_ARG, s
     big = sa.Problem(1, 1, 4097 * 64, 64, 4097, 1, 64, 64)
@@ -91,6 +94,10 @@ def test_workspace_sizes_are_consistent():
     b = sa.workspace_size(p, sa.SelectSpec(rule="mass", sub_block=16))
     c = sa.workspace_size(p, sa.SelectSpec(rule="none", window_frames=1))
     assert 0 < c < a < b
+    # the error rule adds V re-laid out per block and its keys to the topk layout
+    t = sa.workspace_size(p, sa.SelectSpec(rule="topk", topk=[1, 1], want_comp=True))
+    e = sa.workspace_size(p, sa.SelectSpec(rule="err", topk=[1, 1], want_comp=True))
+    assert e == t + 2 * 4 * 128 * 128 * 2 + 256           # keys: 128 bytes rounded up to 256
     # V re-laid out per block [B*H*nb*d*block] bf16 + centroid keys [B*H*nb*d]
     # + centroid values in tiles of `block` blocks [B*H*ceil(nb/block)*d*block]
     BH, nb, d, blk = 2, 4, 128, 128

@@ -12,8 +12,8 @@ import pytest
 
 import oracle
 import workloads as W
-from parity_util import (ATOL_MAX, ATOL_MEAN, LSE_ATOL, OracleCase, compare_attention,
-                         from_dev, log, mask_report, to_dev)
+from parity_util import (ATOL_MAX, ATOL_MEAN, ERR_KEY_ATOL, LSE_ATOL, OracleCase,
+                         compare_attention, compare_keys, from_dev, log, mask_report, to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -53,6 +53,15 @@ SMALL = {
     # more heads than the per-head budgets passed inline with the launch
     "topk_70heads_d64_b64": W.CONFIGS[5].replace(T=2, Hg=8, W=9, H=70, d=64, hilbert=False,
                                                  comp=False, sub_block=0),
+    # error-aware routing (keys ranked top-k, compensation on)
+    "err_d128_b128": W.CONFIGS[2].replace(T=3, Hg=10, W=13, H=3, rule="err", density=0.2,
+                                          comp=True),
+    "err_hilbert_d128_b64": W.CONFIGS[5].replace(T=3, Hg=10, W=13, H=3, rule="err",
+                                                 sub_block=0),
+    "err_d64_b64_wide": W.CONFIGS[3].replace(T=5, Hg=9, W=29, H=2, d=64, block=64, rule="err",
+                                             density=0.3, comp=True),
+    "err_d64_b128_diag": W.CONFIGS[1].replace(T=3, Hg=10, W=13, H=2, block=128, rule="err",
+                                              comp=True, diag=True),
 }
 
 
@@ -67,7 +76,12 @@ def test_small_workload_parity(name):
     O = pipe(to_dev(Q), to_dev(K), to_dev(V), anchor_offset=off)
     torch.cuda.synchronize()
 
-    if wl.rule != "none":
+    if wl.rule == "err":
+        S = pipe.sel.scores.view(wl.B, wl.H, wl.nb, wl.nb).cpu().numpy()
+        kerr = compare_keys(S, case)
+        log(f"[parity] {name}: routing keys max |err| = {kerr:.2e}")
+        assert kerr <= ERR_KEY_ATOL
+    elif wl.rule != "none":
         S = pipe.sel.scores.view(wl.B, wl.H, wl.nb, wl.nb).cpu().numpy()
         assert np.array_equal(S, case.S), "pooled scores differ"
     if wl.comp:
@@ -79,6 +93,19 @@ def test_small_workload_parity(name):
                 assert np.array_equal(km[b, h], oracle.block_means(k, wl.block))
                 assert np.array_equal(vs[b, h], oracle.block_sums_f32(v, wl.block))
     keep = pipe.keep_mask()
+    if wl.rule == "err":
+        # the selection on the kernel's own keys is exact: top-k by key,
+        # then the structured blocks
+        for b in range(wl.B):
+            for h in range(wl.H):
+                want = oracle.topk_keep(S[b, h].astype(np.float64), oracle.head_k(wl, h))
+                if wl.diag:
+                    want |= np.eye(wl.nb, dtype=bool)
+                if wl.window_frames >= 0:
+                    want |= oracle.window_keep(wl.N, wl.block, wl.Hg * wl.W, wl.window_frames)
+                if wl.n_anchors > 0:
+                    want[:, oracle.anchor_blocks(wl.nb, wl.n_anchors, off)] = True
+                assert np.array_equal(keep[b, h], want), (b, h)
     bad, excused, failures = mask_report(keep, case)
     log(f"[parity] {name}: density={keep.mean():.3f} mismatched rows={bad} near-ties={excused}")
     assert not failures, failures[:5]

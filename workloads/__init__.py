@@ -65,7 +65,7 @@ class Workload:
     Hg: int
     W: int
     block: int
-    rule: str = "topk"             # "topk" | "mass" | "none"
+    rule: str = "topk"             # "topk" | "mass" | "err" | "none"
     topk: Optional[int] = None     # same k for every head
     density: Optional[float] = None  # same density for every head
     head_density: bool = False     # per-head density profile
@@ -123,6 +123,25 @@ CONFIGS = {
                 head_density=True, sub_block=16, comp=True, hilbert=True,
                 seed=5),
 }
+
+
+# Workloads of the extensions beyond the five above, by name: error-aware
+# routing (SVG-EAR page, section 2B) on the 1.3B-sized layer at a fixed 20 %
+# budget with compensation, and the score-based top-k rule at the same budget
+# for comparison.
+EXTRA = {
+    "wan13b_err": CONFIGS[2].replace(name="wan13b_err", rule="err", density=0.2, comp=True),
+    "wan13b_topk_comp": CONFIGS[2].replace(name="wan13b_topk_comp", rule="topk", density=0.2,
+                                           comp=True),
+}
+
+
+def by_name(name: str) -> Workload:
+    """Workload of the table above or of EXTRA by its name."""
+    for wl in list(CONFIGS.values()) + list(EXTRA.values()):
+        if wl.name == name:
+            return wl
+    raise KeyError(name)
 
 
 def head_density_profile(H: int, seed: int) -> np.ndarray:
