@@ -599,32 +599,36 @@ __global__ __launch_bounds__(256) void k_vt_prep(const uint16_t* __restrict__ V,
 
 // Centroid pseudo-tokens for compensation, rounded to bf16 for the matrix
 // cores: kbar = k_mean [nb][D]; vbar = v_sum / n_j, stored transposed in
-// tiles of BLK blocks [ntc][D][BLK] (blocks past nb are 0).
+// tiles of BLK blocks [ntc][D][BLK] (blocks past nb are 0).  One workgroup per
+// run of kCompRun blocks, so that the launch fills the chip.
+constexpr int kCompRun = 16;
+
 template <int D, int BLK>
 __global__ __launch_bounds__(256) void k_comp_prep(const float* __restrict__ k_mean,
                                                    const float* __restrict__ v_sum,
                                                    uint16_t* __restrict__ kbar,
                                                    uint16_t* __restrict__ vbart, int nb, int ntc,
                                                    int last_n) {
-    const int tc = blockIdx.x;
+    static_assert(BLK % kCompRun == 0, "runs do not straddle centroid tiles");
+    const int j0 = blockIdx.x * kCompRun;          // first block of the run
     const int64_t bh = blockIdx.y;
-    for (int p = threadIdx.x; p < BLK * D; p += 256) {
-        const int r = p / D, d = p % D;
-        const int j = tc * BLK + r;
+    for (int p = threadIdx.x; p < kCompRun * D; p += 256) {
+        const int j = j0 + p / D, d = p % D;
         if (j < nb) {
             const int64_t e = (bh * nb + j) * (int64_t)D + d;
             kbar[e] = f32_to_bf16_rne(k_mean[e]);
         }
     }
-    for (int p = threadIdx.x; p < BLK * D; p += 256) {
-        const int d = p / BLK, r = p % BLK;
-        const int j = tc * BLK + r;
+    const int tc = j0 / BLK, r0 = j0 % BLK;
+    for (int p = threadIdx.x; p < kCompRun * D; p += 256) {
+        const int d = p / kCompRun, r = p % kCompRun;
+        const int j = j0 + r;
         uint16_t v = 0;
         if (j < nb) {
             const float n = (float)(j == nb - 1 ? last_n : BLK);
             v = f32_to_bf16_rne(v_sum[(bh * nb + j) * (int64_t)D + d] / n);
         }
-        vbart[((bh * ntc + tc) * (int64_t)D + d) * BLK + r] = v;
+        vbart[((bh * ntc + tc) * (int64_t)D + d) * BLK + r0 + r] = v;
     }
 }
 
@@ -657,7 +661,8 @@ sa_status prepare_t(const FwdArgs& a, const Geometry& g, const uint16_t* V, uint
     sa_status st = hip_check(hipGetLastError(), "k_vt_prep launch");
     if (st != SA_OK) return st;
     if (COMP) {
-        hipLaunchKernelGGL((k_comp_prep<D, BLK>), dim3(a.ntc, (unsigned)g.BH()), dim3(256), 0, stream,
+        hipLaunchKernelGGL((k_comp_prep<D, BLK>), dim3(a.ntc * (BLK / kCompRun), (unsigned)g.BH()),
+                           dim3(256), 0, stream,
                            k_mean, v_sum, kbar, vbart, g.nb, a.ntc, g.N - (g.nb - 1) * BLK);
         if ((st = hip_check(hipGetLastError(), "k_comp_prep launch")) != SA_OK) return st;
     }
