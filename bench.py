@@ -2,6 +2,7 @@
 """Benchmark of one block-sparse attention call on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2]
+                    [--workload NAME] [--refresh-every R]
 
 A step is one full call of the hot path on the workload's synthetic inputs
 (already resident in HBM): Hilbert reordering when the workload uses it,
@@ -16,6 +17,9 @@ divided by the whole step time; ``ms_per_step`` is that step time.
 ``roofline`` reports the attention kernel alone against the bf16 matrix-core
 peak, timed with HIP events on the stream it is launched on.
 ``cpu_baseline`` times the CPU oracle on a bounded sample of the same workload.
+With ``--refresh-every R`` (mask reuse across calls) only every R-th call
+selects; the others keep its mask and recompute only the compensation
+centroids; the default R = 1 selects on every call.
 """
 from __future__ import annotations
 
@@ -113,6 +117,9 @@ def main():
     ap.add_argument("--config", type=int, default=2, help="workload number 1..5")
     ap.add_argument("--workload", default=None,
                     help="workload by name (overrides --config), e.g. wan13b_err")
+    ap.add_argument("--refresh-every", type=int, default=1,
+                    help="mask reuse: select on every r-th call only, the calls in between "
+                         "keep the mask (compensation centroids still from their own K, V)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calib-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (counter calibration)")
@@ -147,20 +154,28 @@ def main():
         return torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).cuda()
 
     Qd, Kd, Vd = dev(Q), dev(K), dev(V)
-    pipe = BlockSparseAttention(sa.problem_for(wl), sa.spec_for(wl), hilbert=wl.hilbert)
+    pipe = BlockSparseAttention(sa.problem_for(wl), sa.spec_for(wl), hilbert=wl.hilbert,
+                                refresh_every=args.refresh_every)
     stream = torch.cuda.current_stream()
+    selected = []
 
     def step(call_idx, ev):
         off = W.anchor_offset(wl.seed, call_idx, wl.nb) if wl.n_anchors else None
+        reuse = pipe.reuses_next()
+        selected.append(not reuse)
         Qp, Kp, Vp = pipe.permute_inputs(Qd, Kd, Vd)
         ev[0].record(stream)
-        pipe.run_select(Qp, Kp, Vp, off)
+        if reuse:
+            pipe.run_centroids(Kp, Vp)
+        else:
+            pipe.run_select(Qp, Kp, Vp, off)
         ev[1].record(stream)
         pipe.run_fwd_prepare(Vp)
         ev[2].record(stream)
         pipe.run_fwd_attention(Qp, Kp)
         ev[3].record(stream)
         pipe.unpermute_output()
+        pipe.calls += 1
 
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)]
               for _ in range(max(args.steps, 1))]
@@ -209,8 +224,10 @@ def main():
                    "mass": wl.mass if wl.rule == "mass" else None,
                    "density_kept": round(float(keep.mean()), 4),
                    "hilbert": wl.hilbert, "compensation": wl.comp,
+                   "mask_refresh_every": args.refresh_every,
                    "parallelism": "single GPU"},
         "ms_select": round(sel_s * 1e3, 4),
+        "selections_timed": int(sum(selected[args.warmup:])),
         "ms_attention": round(fwd_s * 1e3, 4),
         "ms_attention_prepare": round(float(np.mean(prep_ms)), 4),
         "select_over_attention": round(sel_s / fwd_s, 4),

@@ -35,7 +35,8 @@ RULES = {"none": SA_RULE_NONE, "topk": SA_RULE_TOPK, "mass": SA_RULE_MASS, "err"
 
 EXPORTS = ("sparse_attn_workspace_size", "hilbert_perm_build", "hilbert_permute",
            "hilbert_unpermute", "sparse_attn_select", "sparse_attn_fwd",
-           "sparse_attn_fwd_prepare", "sparse_attn_fwd_run", "sparse_attn_last_error")
+           "sparse_attn_fwd_prepare", "sparse_attn_fwd_run", "sparse_attn_centroids",
+           "sparse_attn_last_error")
 
 
 class SaProblem(ctypes.Structure):
@@ -62,8 +63,12 @@ class SparseAttnError(RuntimeError):
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is not built; run "
-                          "`python -m block_sparse_attention_hilbert_amd.build`")
+                          "`python block_sparse_attention_hilbert_amd/build.py`")
     lib = ctypes.CDLL(LIB_PATH)
+    missing = [name for name in EXPORTS if not hasattr(lib, name)]
+    if missing:
+        raise ImportError(f"{LIB_PATH} is out of date (no {', '.join(missing)}); rebuild it "
+                          "with `python block_sparse_attention_hilbert_amd/build.py`")
     vp, sz = ctypes.c_void_p, ctypes.c_size_t
     P = ctypes.POINTER
     lib.sparse_attn_workspace_size.argtypes = [P(SaProblem), P(SaSelectSpec), P(sz)]
@@ -74,6 +79,7 @@ def _load():
                                        vp, vp, vp, sz, vp]
     lib.sparse_attn_fwd.argtypes = [P(SaProblem), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.sparse_attn_fwd_prepare.argtypes = [P(SaProblem), vp, vp, vp, vp, vp, sz, vp]
+    lib.sparse_attn_centroids.argtypes = [P(SaProblem), vp, vp, vp, vp, vp]
     lib.sparse_attn_fwd_run.argtypes = [P(SaProblem), vp, vp, vp, vp, ctypes.c_int32, vp, vp, vp,
                                         sz, vp]
     for name in EXPORTS[:-1]:
@@ -232,6 +238,13 @@ def select(prob: Problem, spec: SelectSpec, Q: torch.Tensor, K: torch.Tensor,
                                   _ptr(out.scores), _ptr(out.k_mean), _ptr(out.v_sum),
                                   _ptr(workspace), ws_bytes, _stream(stream)))
     return out
+
+
+def centroids(prob: Problem, K: torch.Tensor, V: torch.Tensor, k_mean: torch.Tensor,
+              v_sum: torch.Tensor, stream=None) -> None:
+    """sparse_attn_centroids: block means of K and block sums of V (no selection)."""
+    _check(lib.sparse_attn_centroids(ctypes.byref(prob.c()), _ptr(K), _ptr(V), _ptr(k_mean),
+                                     _ptr(v_sum), _stream(stream)))
 
 
 def fwd(prob: Problem, Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor,

@@ -1,6 +1,8 @@
 """Builds libsparse_attn.so (gfx950) in-tree with hipcc.
 
-    python -m block_sparse_attention_hilbert_amd.build
+    python block_sparse_attention_hilbert_amd/build.py
+
+(run by path: importing the package loads the library this script builds)
 """
 from __future__ import annotations
 

@@ -465,6 +465,23 @@ SelectPlan make_select_plan(const Geometry& g, const sa_select_spec& s) {
     return p;
 }
 
+sa_status launch_centroids(const Geometry& g, const uint16_t* K, const uint16_t* V, float* k_mean,
+                           float* v_sum, hipStream_t stream) {
+    PoolArgs pa{};
+    pa.src[1] = K; pa.src[2] = V;
+    pa.block_out[1] = k_mean; pa.block_out[2] = v_sum;
+    pa.roles[0] = 1; pa.roles[1] = 2;
+    pa.N = g.N; pa.nb = g.nb; pa.unit = g.block; pa.n_units = g.nb;
+    if (g.d == 128) {
+        if (g.block == 128) launch_pool_t<128, 128>(pa, 2, g.BH(), g.nb, stream);
+        else launch_pool_t<128, 64>(pa, 2, g.BH(), g.nb, stream);
+    } else {
+        if (g.block == 128) launch_pool_t<64, 128>(pa, 2, g.BH(), g.nb, stream);
+        else launch_pool_t<64, 64>(pa, 2, g.BH(), g.nb, stream);
+    }
+    return hip_check(hipGetLastError(), "k_pool launch");
+}
+
 sa_status launch_select(const Geometry& g, const SelectPlan& p, const int32_t* k_host,
                         const uint16_t* Q, const uint16_t* K, const uint16_t* V,
                         int32_t* row_ptr, int32_t* col_idx, float* scores, float* k_mean,

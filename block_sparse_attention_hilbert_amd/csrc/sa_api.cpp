@@ -225,6 +225,20 @@ SA_API sa_status sparse_attn_select(const sa_problem* prob, const sa_select_spec
                          (char*)workspace, (hipStream_t)stream);
 }
 
+SA_API sa_status sparse_attn_centroids(const sa_problem* prob, const void* K, const void* V,
+                                       float* k_mean, float* v_sum, void* stream) {
+    clear_error();
+    Geometry g;
+    sa_status st = check_problem(prob, &g);
+    if (st != SA_OK) return st;
+    if (!K || !V || !k_mean || !v_sum)
+        return fail(SA_ERR_INVALID_ARG, "K, V, k_mean and v_sum are required");
+    if (!aligned16(K) || !aligned16(V) || !aligned16(k_mean) || !aligned16(v_sum))
+        return fail(SA_ERR_INVALID_ARG, "K, V, k_mean, v_sum must be 16-byte aligned");
+    return launch_centroids(g, (const uint16_t*)K, (const uint16_t*)V, k_mean, v_sum,
+                            (hipStream_t)stream);
+}
+
 static sa_status check_fwd_workspace(const Geometry& g, bool comp, const void* workspace,
                                      size_t ws_bytes) {
     const size_t need = fwd_workspace_bytes(g, comp);

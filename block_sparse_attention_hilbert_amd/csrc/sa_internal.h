@@ -56,6 +56,10 @@ sa_status launch_select(const Geometry& g, const SelectPlan& p,
                         int32_t* col_idx, float* scores, float* k_mean,
                         float* v_sum, char* ws, hipStream_t stream);
 
+// Block means of K and block sums of V (the compensation statistics) alone.
+sa_status launch_centroids(const Geometry& g, const uint16_t* K, const uint16_t* V, float* k_mean,
+                           float* v_sum, hipStream_t stream);
+
 // ----------------------------------------------------------------------------
 // error-aware routing keys (k_route.hip)
 // ----------------------------------------------------------------------------

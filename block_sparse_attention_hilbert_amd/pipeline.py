@@ -6,6 +6,13 @@ block-sparse attention with optional centroid compensation (SVG-EAR page,
 section 2A), and the inverse reordering of O.  Every step is one or more HIP
 kernels of libsparse_attn.so enqueued on the current stream; this class only
 owns the buffers so that repeated calls allocate nothing.
+
+Mask reuse (DFSAttn page, trick 3: the previous step's mask is cached; SVOO
+page, section 2B: the clustering is refreshed only every few diffusion steps):
+with ``refresh_every = r`` the selection runs on calls 0, r, 2r, ... and the
+calls in between keep its CSR.  A reusing call still reorders its own inputs
+and, with compensation, recomputes the centroids of the skipped blocks from
+its own K and V (sparse_attn_centroids); only the keep decision is reused.
 """
 from __future__ import annotations
 
@@ -14,14 +21,21 @@ from typing import Optional
 import numpy as np
 import torch
 
-from . import (Problem, Selection, SelectSpec, alloc_workspace, fwd, fwd_prepare, fwd_run,
-               hilbert_perm_build, hilbert_permute, hilbert_unpermute, select, workspace_size)
+from . import (Problem, Selection, SelectSpec, alloc_workspace, centroids, fwd, fwd_prepare,
+               fwd_run, hilbert_perm_build, hilbert_permute, hilbert_unpermute, select,
+               workspace_size)
 
 
 class BlockSparseAttention:
     def __init__(self, prob: Problem, spec: SelectSpec, hilbert: bool = False,
-                 device="cuda", want_scores: bool = False, want_lse: bool = False):
+                 device="cuda", want_scores: bool = False, want_lse: bool = False,
+                 refresh_every: int = 1):
+        if refresh_every < 1:
+            raise ValueError("refresh_every must be >= 1")
         self.prob, self.spec, self.hilbert = prob, spec, hilbert
+        self.refresh_every = int(refresh_every)
+        self.calls = 0              # calls made so far (the reuse policy counts them)
+        self.have_mask = False
         self.device = torch.device(device)
         nb, rows = prob.nb, prob.rows
         shape = (prob.B, prob.H, prob.N, prob.d)
@@ -60,8 +74,19 @@ class BlockSparseAttention:
         spec = self.spec
         if anchor_offset is not None:
             spec = SelectSpec(**{**spec.__dict__, "anchor_offset": int(anchor_offset)})
-        return select(self.prob, spec, Q, K, V if spec.want_comp else None,
-                      out=self.sel, workspace=self.ws_select)
+        sel = select(self.prob, spec, Q, K, V if spec.want_comp else None,
+                     out=self.sel, workspace=self.ws_select)
+        self.have_mask = True
+        return sel
+
+    def run_centroids(self, K, V):
+        """Compensation statistics of the current K, V for a reused mask."""
+        if self.spec.want_comp:
+            centroids(self.prob, K, V, self.sel.k_mean, self.sel.v_sum)
+
+    def reuses_next(self) -> bool:
+        """Whether the next call keeps the current mask under the refresh policy."""
+        return self.have_mask and self.calls % self.refresh_every != 0
 
     def run_fwd(self, Q, K, V, row_ptr=None, col_idx=None):
         rp = self.sel.row_ptr if row_ptr is None else row_ptr
@@ -90,10 +115,21 @@ class BlockSparseAttention:
             hilbert_unpermute(self.prob, self.Op, self.perm_dev, self.O)
         return self.O
 
-    def __call__(self, Q, K, V, anchor_offset: Optional[int] = None) -> torch.Tensor:
+    def __call__(self, Q, K, V, anchor_offset: Optional[int] = None,
+                 reuse_mask: Optional[bool] = None) -> torch.Tensor:
+        """One call.  ``reuse_mask``: keep the last selection (True), select
+        anew (False) or follow the refresh policy (None)."""
+        if reuse_mask is None:
+            reuse_mask = self.reuses_next()
+        if reuse_mask and not self.have_mask:
+            raise RuntimeError("no mask to reuse: the first call must select")
         Qp, Kp, Vp = self.permute_inputs(Q, K, V)
-        self.run_select(Qp, Kp, Vp, anchor_offset)
+        if reuse_mask:
+            self.run_centroids(Kp, Vp)
+        else:
+            self.run_select(Qp, Kp, Vp, anchor_offset)
         self.run_fwd(Qp, Kp, Vp)
+        self.calls += 1
         return self.unpermute_output()
 
     def keep_mask(self) -> np.ndarray:

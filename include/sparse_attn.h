@@ -183,6 +183,22 @@ sa_status sparse_attn_select(const sa_problem* prob, const sa_select_spec* spec,
                              void* workspace, size_t ws_bytes, void* stream);
 
 /*
+ * Compensation statistics of the current K and V without a selection
+ * [EAR 2A; mask reuse across steps: DFS trick 3, SVOO 2B].  A caller that keeps
+ * the CSR of an earlier sparse_attn_select (the mask of a previous call or
+ * diffusion step) and skips the selection still needs the centroids of the
+ * blocks it now skips, taken from the current K and V:
+ *   k_mean[b,h,j,:] = mean of K over the tokens of block j (fp32 rounding of
+ *                     the exact mean, as sparse_attn_select writes it),
+ *   v_sum[b,h,j,:]  = fp32 rounding of the exact sum of V over block j.
+ * K, V: device bf16 [B,H,N,d], 16-byte aligned.  k_mean, v_sum: device fp32
+ * [B,H,nb,d].  No workspace.  Errors: SA_ERR_INVALID_ARG for a NULL or
+ * misaligned pointer, problem errors as for every call.
+ */
+sa_status sparse_attn_centroids(const sa_problem* prob, const void* K, const void* V,
+                                float* k_mean, float* v_sum, void* stream);
+
+/*
  * Block-sparse attention forward [EAR 2B streaming update; SPADE part 3].
  * For a query token n of block i:
  *   O[n] = sum_t exp(l_t - m) v_t / sum_t exp(l_t - m),  l_t = scale * q_n.k_t,

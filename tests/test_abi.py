@@ -169,3 +169,27 @@ def test_fwd_halves_reject_before_any_launch():
     need = sa.workspace_size(_prob())
     assert run(ctypes.byref(p), fake, fake, fake, fake, 1, fake, None, fake, need - 256,
                None) == sa.SA_ERR_WORKSPACE
+
+
+def test_centroids_reject_before_any_launch():
+    p = _prob().c()
+    vp = ctypes.c_void_p
+    fake, odd = vp(1 << 20), vp((1 << 20) + 8)
+    assert sa.lib.sparse_attn_centroids(ctypes.byref(p), None, fake, fake, fake, None) == \
+        sa.SA_ERR_INVALID_ARG
+    assert b"required" in sa.lib.sparse_attn_last_error()
+    assert sa.lib.sparse_attn_centroids(ctypes.byref(p), fake, fake, fake, None, None) == \
+        sa.SA_ERR_INVALID_ARG
+    assert sa.lib.sparse_attn_centroids(ctypes.byref(p), fake, odd, fake, fake, None) == \
+        sa.SA_ERR_INVALID_ARG
+    assert b"aligned" in sa.lib.sparse_attn_last_error()
+    bad = _prob(N=391).c()
+    assert sa.lib.sparse_attn_centroids(ctypes.byref(bad), fake, fake, fake, fake, None) == \
+        sa.SA_ERR_INVALID_ARG
+
+
+def test_reuse_policy_needs_a_first_selection():
+    from block_sparse_attention_hilbert_amd.pipeline import BlockSparseAttention
+    with pytest.raises(ValueError):
+        BlockSparseAttention(_prob(), sa.SelectSpec(rule="mass"), device="cpu", refresh_every=0)
+

@@ -237,3 +237,51 @@ def test_fwd_halves_match_fwd(name):
     for o, lse in outs:
         assert torch.equal(o.view(torch.int16), ref.view(torch.int16))
         assert torch.equal(lse, ref_lse)
+
+
+@pytest.mark.parametrize("name", ["hilbert_comp_d128_b64", "mass_d128_b128", "err_d128_b128"])
+def test_mask_reuse_across_steps(name):
+    """Mask reuse (DFSAttn trick 3, SVOO 2B): step 0 selects, steps 1 and 2 keep
+    its CSR.  Every step's output must equal the oracle's attention over step
+    0's mask with that step's own inputs (and, with compensation, the
+    centroids of that step's K and V)."""
+    wl = SMALL[name]
+    log(f"[reuse] {name}: N={wl.N} nb={wl.nb} H={wl.H}")
+    steps = W.make_step_qkv(wl, 3, drift=0.2)
+    pipe = _pipeline(wl)
+    pipe.refresh_every = 3
+    keep0 = None
+    changed_total = 0
+    for s, (Q, K, V) in enumerate(steps):
+        case = OracleCase(wl, Q, K, V, anchor_offset=0)
+        assert pipe.reuses_next() == (s > 0)
+        O = pipe(to_dev(Q), to_dev(K), to_dev(V), anchor_offset=0)
+        torch.cuda.synchronize()
+        keep = pipe.keep_mask()
+        if s == 0:
+            keep0 = keep.copy()
+            bad, excused, failures = mask_report(keep, case)
+            assert not failures, failures[:5]
+            case.keep = keep0
+        else:
+            assert np.array_equal(keep, keep0), "reused mask changed"
+            changed = int((case.keep != keep0).any(axis=-1).sum())
+            changed_total += changed
+            log(f"[reuse] {name}: step {s}: rows whose fresh mask would differ: {changed}")
+            case.keep = keep0
+            if wl.comp:
+                km = pipe.sel.k_mean.cpu().numpy()
+                vs = pipe.sel.v_sum.cpu().numpy()
+                for b in range(wl.B):
+                    for h in range(wl.H):
+                        q, k, v = case.head_inputs(b, h)
+                        assert np.array_equal(km[b, h], oracle.block_means(k, wl.block))
+                        assert np.array_equal(vs[b, h], oracle.block_sums_f32(v, wl.block))
+        lse = pipe.lse.cpu().numpy()
+        if wl.hilbert:
+            lse = lse[..., np.argsort(pipe.perm)]
+        emax, emean, lmax, n = compare_attention(from_dev(O), case, None, lse_gpu=lse)
+        log(f"[reuse] {name}: step {s}: attention max={emax:.2e} mean={emean:.2e} lse={lmax:.2e}")
+        assert emax <= ATOL_MAX and emean <= ATOL_MEAN and lmax <= LSE_ATOL
+    # the drift is large enough that a fresh selection would have differed
+    assert changed_total > 0

@@ -76,3 +76,14 @@ def test_head_density_profile_range():
     rho = W.head_density_profile(12, 5)
     assert rho.dtype == np.float32 and np.all(rho >= 0.05) and np.all(rho <= 0.5)
     assert np.array_equal(rho, W.CONFIGS[5].densities())
+
+
+def test_step_inputs_start_at_the_workload_and_drift():
+    wl = W.CONFIGS[1]
+    steps = W.make_step_qkv(wl, 3, drift=0.1)
+    Q, K, V = W.make_qkv(wl)
+    assert all(np.array_equal(a, b) for a, b in zip(steps[0], (Q, K, V)))
+    # each later step moves further from step 0, and stays bf16 of a blend
+    d1 = np.abs(W.bf16_bits_to_f32(steps[1][0]) - W.bf16_bits_to_f32(Q)).mean()
+    d2 = np.abs(W.bf16_bits_to_f32(steps[2][0]) - W.bf16_bits_to_f32(Q)).mean()
+    assert 0 < d1 < d2

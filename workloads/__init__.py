@@ -308,3 +308,26 @@ def make_qkv(wl: Workload, heads=None, alpha: float = None, workers: int = 8,
         with concurrent.futures.ThreadPoolExecutor(min(workers, len(jobs))) as ex:
             list(ex.map(one, jobs))
     return Q, K, V
+
+
+def make_step_qkv(wl: Workload, steps: int, drift: float = 0.05, workers: int = 8):
+    """Inputs of ``steps`` consecutive calls whose activations drift slowly, as
+    across neighbouring diffusion steps (the setting of mask reuse).
+
+    Step s blends two independent draws of the workload (seeds ``wl.seed`` and
+    ``wl.seed + 7919``) in float32: X_s = (1 - a_s) X_a + a_s X_b with
+    a_s = drift * s, rounded once to bfloat16.  Step 0 equals make_qkv(wl).
+    Returns a list of (Q, K, V) bf16-bit arrays.
+    """
+    A = make_qkv(wl, workers=workers)
+    Bq = make_qkv(wl.replace(seed=wl.seed + 7919), workers=workers)
+    out = [A]
+    for s in range(1, steps):
+        a = np.float32(drift * s)
+        step = []
+        for xa, xb in zip(A, Bq):
+            x = (np.float32(1) - a) * bf16_bits_to_f32(xa) + a * bf16_bits_to_f32(xb)
+            step.append(f32_to_bf16_bits(x.astype(np.float32)))
+        out.append(tuple(step))
+    return out
+
