@@ -10,6 +10,11 @@ stream.  The functions mirror the C ABI in ``include/sparse_attn.h``:
 * :func:`select` -- ``sparse_attn_select``: keep lists as CSR
 * :func:`fwd` -- ``sparse_attn_fwd``: block-sparse attention (+ compensation)
 * :func:`fwd_prepare`, :func:`fwd_run` -- its two halves
+  (:func:`fwd_prepare_counts`: with a token count per KV block)
+* :func:`centroids` -- compensation statistics alone (mask reuse)
+* :func:`cluster_size`, :func:`cluster`, :func:`cluster_gather`,
+  :func:`cluster_scatter`, :func:`cluster_select` -- data-dependent block
+  formation (co-clustering / k-means) and selection over clusters
 * :func:`workspace_size`
 
 If the shared library is missing the import fails loudly; there is no
@@ -32,11 +37,15 @@ LIB_PATH = os.path.join(_PKG, "libsparse_attn.so")
 SA_OK, SA_ERR_INVALID_ARG, SA_ERR_UNSUPPORTED, SA_ERR_WORKSPACE, SA_ERR_HIP = range(5)
 SA_RULE_NONE, SA_RULE_TOPK, SA_RULE_MASS, SA_RULE_ERR = range(4)
 RULES = {"none": SA_RULE_NONE, "topk": SA_RULE_TOPK, "mass": SA_RULE_MASS, "err": SA_RULE_ERR}
+SA_CLUSTER_COCLUSTER, SA_CLUSTER_KMEANS = 1, 2
+CLUSTER_MODES = {"cocluster": SA_CLUSTER_COCLUSTER, "kmeans": SA_CLUSTER_KMEANS}
 
 EXPORTS = ("sparse_attn_workspace_size", "hilbert_perm_build", "hilbert_permute",
            "hilbert_unpermute", "sparse_attn_select", "sparse_attn_fwd",
            "sparse_attn_fwd_prepare", "sparse_attn_fwd_run", "sparse_attn_centroids",
-           "sparse_attn_last_error")
+           "sparse_attn_fwd_prepare_counts", "sparse_attn_cluster_size", "sparse_attn_cluster",
+           "sparse_attn_cluster_gather", "sparse_attn_cluster_scatter",
+           "sparse_attn_cluster_select", "sparse_attn_last_error")
 
 
 class SaProblem(ctypes.Structure):
@@ -52,6 +61,11 @@ class SaSelectSpec(ctypes.Structure):
                 ("mass", ctypes.c_float), ("diag", ctypes.c_int32),
                 ("window_frames", ctypes.c_int32), ("n_anchors", ctypes.c_int32),
                 ("anchor_offset", ctypes.c_int64), ("want_comp", ctypes.c_int32)]
+
+
+class SaClusterSpec(ctypes.Structure):
+    _fields_ = [("mode", ctypes.c_int32), ("n_clusters", ctypes.c_int32),
+                ("iters", ctypes.c_int32)]
 
 
 class SparseAttnError(RuntimeError):
@@ -82,6 +96,13 @@ def _load():
     lib.sparse_attn_centroids.argtypes = [P(SaProblem), vp, vp, vp, vp, vp]
     lib.sparse_attn_fwd_run.argtypes = [P(SaProblem), vp, vp, vp, vp, ctypes.c_int32, vp, vp, vp,
                                         sz, vp]
+    lib.sparse_attn_fwd_prepare_counts.argtypes = [P(SaProblem), vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.sparse_attn_cluster_size.argtypes = [P(SaProblem), P(SaClusterSpec), vp, vp, vp]
+    lib.sparse_attn_cluster.argtypes = [P(SaProblem), P(SaClusterSpec)] + [vp] * 15 + [sz, vp]
+    lib.sparse_attn_cluster_gather.argtypes = [P(SaProblem), P(SaClusterSpec), vp, vp, vp, vp]
+    lib.sparse_attn_cluster_scatter.argtypes = [P(SaProblem), P(SaClusterSpec)] + [vp] * 6
+    lib.sparse_attn_cluster_select.argtypes = ([P(SaProblem), P(SaClusterSpec), P(SaSelectSpec)]
+                                               + [vp] * 13 + [sz, vp])
     for name in EXPORTS[:-1]:
         getattr(lib, name).restype = ctypes.c_int
     lib.sparse_attn_last_error.argtypes = []
@@ -300,3 +321,147 @@ def spec_for(wl, anchor_offset: int = 0) -> SelectSpec:
                       mass=wl.mass, diag=wl.diag, window_frames=wl.window_frames,
                       n_anchors=wl.n_anchors, anchor_offset=anchor_offset,
                       want_comp=wl.comp)
+
+
+def fwd_prepare_counts(prob: Problem, V: torch.Tensor, row_ptr: torch.Tensor,
+                       kv_count: torch.Tensor, k_mean: Optional[torch.Tensor] = None,
+                       v_sum: Optional[torch.Tensor] = None, *, workspace: torch.Tensor,
+                       stream=None) -> None:
+    """sparse_attn_fwd_prepare_counts: as fwd_prepare, with int32 [B*H, nb] token
+    counts per KV block (keys past a block's count take no part)."""
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(lib.sparse_attn_fwd_prepare_counts(ctypes.byref(prob.c()), _ptr(V), _ptr(row_ptr),
+                                              _ptr(k_mean), _ptr(v_sum), _ptr(kv_count),
+                                              _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+# ---------------------------------------------------------------------------
+# data-dependent block formation
+# ---------------------------------------------------------------------------
+
+@dataclass
+class ClusterSpec:
+    mode: str = "kmeans"          # "cocluster" | "kmeans"
+    n_clusters: int = 64
+    iters: int = 3
+
+    def c(self) -> SaClusterSpec:
+        return SaClusterSpec(CLUSTER_MODES[self.mode], self.n_clusters, self.iters)
+
+
+def cluster_size(prob: Problem, cspec: ClusterSpec):
+    """(nbp, ws_cluster, ws_select): blocks of the padded clustered layout and
+    the workspace bytes of cluster() and cluster_select()."""
+    nbp = ctypes.c_int32(0)
+    w1, w2 = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    _check(lib.sparse_attn_cluster_size(ctypes.byref(prob.c()), ctypes.byref(cspec.c()),
+                                        ctypes.byref(nbp), ctypes.byref(w1), ctypes.byref(w2)))
+    return int(nbp.value), int(w1.value), int(w2.value)
+
+
+def padded_problem(prob: Problem, nbp: int) -> Problem:
+    """The attention problem on the padded clustered layout (one flat frame)."""
+    Np = nbp * prob.block
+    return Problem(prob.B, prob.H, Np, prob.d, 1, 1, Np, prob.block, prob.scale)
+
+
+@dataclass
+class Clusters:
+    """Output of cluster(): layouts (int32) and centroids (fp32) of both sides."""
+    q_order: torch.Tensor     # [B*H, Np] token at each padded slot, -1 = padding
+    k_order: torch.Tensor
+    q_blk: torch.Tensor       # [B*H, nbp] cluster of each padded block, -1 = none
+    k_blk: torch.Tensor
+    q_cnt: torch.Tensor       # [B*H, nbp] tokens in each padded block
+    k_cnt: torch.Tensor
+    q_cent: torch.Tensor      # [B*H, C, d]
+    k_cent: torch.Tensor
+    q_count: torch.Tensor     # [B*H, C] cluster sizes
+    k_count: torch.Tensor
+    v_cent: Optional[torch.Tensor] = None
+
+    @staticmethod
+    def empty(prob: Problem, cspec: ClusterSpec, nbp: int, with_v: bool, device) -> "Clusters":
+        BH, C, Np = prob.B * prob.H, cspec.n_clusters, nbp * prob.block
+        i32 = dict(dtype=torch.int32, device=device)
+        f32 = dict(dtype=torch.float32, device=device)
+        return Clusters(torch.empty(BH, Np, **i32), torch.empty(BH, Np, **i32),
+                        torch.empty(BH, nbp, **i32), torch.empty(BH, nbp, **i32),
+                        torch.empty(BH, nbp, **i32), torch.empty(BH, nbp, **i32),
+                        torch.empty(BH, C, prob.d, **f32), torch.empty(BH, C, prob.d, **f32),
+                        torch.empty(BH, C, **i32), torch.empty(BH, C, **i32),
+                        torch.empty(BH, C, prob.d, **f32) if with_v else None)
+
+
+def cluster(prob: Problem, cspec: ClusterSpec, Q: torch.Tensor, K: torch.Tensor,
+            V: Optional[torch.Tensor] = None, *, out: Optional[Clusters] = None,
+            workspace: Optional[torch.Tensor] = None, stream=None) -> Clusters:
+    """sparse_attn_cluster: clusters of Q and K per (b, h) and their padded
+    layouts; with V also the value means of the key clusters."""
+    nbp, ws_c, _ = cluster_size(prob, cspec)
+    if out is None:
+        out = Clusters.empty(prob, cspec, nbp, V is not None, Q.device)
+    if workspace is None:
+        workspace = alloc_workspace(ws_c, Q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.sparse_attn_cluster(ctypes.byref(prob.c()), ctypes.byref(cspec.c()), _ptr(Q),
+                                   _ptr(K), _ptr(V), _ptr(out.q_order), _ptr(out.k_order),
+                                   _ptr(out.q_blk), _ptr(out.k_blk), _ptr(out.q_cnt),
+                                   _ptr(out.k_cnt), _ptr(out.q_cent), _ptr(out.k_cent),
+                                   _ptr(out.v_cent if V is not None else None),
+                                   _ptr(out.q_count), _ptr(out.k_count), _ptr(workspace),
+                                   ws_bytes, _stream(stream)))
+    return out
+
+
+def cluster_gather(prob: Problem, cspec: ClusterSpec, order: torch.Tensor, src: torch.Tensor,
+                   dst: torch.Tensor, stream=None) -> torch.Tensor:
+    """sparse_attn_cluster_gather: rows of src [B,H,N,d] into the padded layout dst
+    [B,H,Np,d] (zero rows for padding)."""
+    _check(lib.sparse_attn_cluster_gather(ctypes.byref(prob.c()), ctypes.byref(cspec.c()),
+                                          _ptr(order), _ptr(src), _ptr(dst), _stream(stream)))
+    return dst
+
+
+def cluster_scatter(prob: Problem, cspec: ClusterSpec, order: torch.Tensor, src: torch.Tensor,
+                    dst: torch.Tensor, lse_src: Optional[torch.Tensor] = None,
+                    lse_dst: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """sparse_attn_cluster_scatter: rows of the padded layout back to token order."""
+    _check(lib.sparse_attn_cluster_scatter(ctypes.byref(prob.c()), ctypes.byref(cspec.c()),
+                                           _ptr(order), _ptr(src), _ptr(dst), _ptr(lse_src),
+                                           _ptr(lse_dst), _stream(stream)))
+    return dst
+
+
+def cluster_select(prob: Problem, cspec: ClusterSpec, spec: SelectSpec, cl: Clusters, *,
+                   out: Optional[Selection] = None, want_scores: bool = False,
+                   workspace: Optional[torch.Tensor] = None, stream=None) -> Selection:
+    """sparse_attn_cluster_select: keep decision over clusters as CSR over the
+    padded blocks (+ per-block compensation statistics with want_comp)."""
+    nbp, _, ws_s = cluster_size(prob, cspec)
+    dev = cl.q_cent.device
+    BH, C = prob.B * prob.H, cspec.n_clusters
+    rows = BH * nbp
+    if out is None:
+        out = Selection(torch.empty(rows + 1, dtype=torch.int32, device=dev),
+                        torch.empty(rows * nbp, dtype=torch.int32, device=dev))
+        if want_scores:
+            out.scores = torch.empty(BH, C, C, dtype=torch.float32, device=dev)
+        if spec.want_comp:
+            out.k_mean = torch.empty(prob.B, prob.H, nbp, prob.d, dtype=torch.float32, device=dev)
+            out.v_sum = torch.empty_like(out.k_mean)
+    if workspace is None:
+        workspace = alloc_workspace(ws_s, dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    cs, keep = spec.c()
+    _check(lib.sparse_attn_cluster_select(
+        ctypes.byref(prob.c()), ctypes.byref(cspec.c()), ctypes.byref(cs), _ptr(cl.q_cent),
+        _ptr(cl.k_cent), _ptr(cl.v_cent), _ptr(cl.k_count), _ptr(cl.q_blk), _ptr(cl.k_blk),
+        _ptr(cl.k_cnt), _ptr(out.row_ptr), _ptr(out.col_idx), _ptr(out.scores),
+        _ptr(out.k_mean), _ptr(out.v_sum), _ptr(workspace), ws_bytes, _stream(stream)))
+    return out
+
+
+def cluster_spec_for(wl) -> ClusterSpec:
+    """Cluster spec of a workload description (cluster, n_clusters, cluster_iters)."""
+    return ClusterSpec(wl.cluster, wl.n_clusters, wl.cluster_iters)

@@ -98,9 +98,11 @@ struct FwdArgs {
     const int32_t* col_idx;
     const uint16_t* kbar;    // [BH][nb][D] centroid keys (compensation) or null
     const uint16_t* vbart;   // [BH][ntc][D][BLK] transposed centroid values
+    const int16_t* cnt;      // [BH][nb] tokens of each KV block
     uint16_t* O;
     float* lse;
-    int32_t* sched;          // [3][8] per-XCD row range start, end and pull counter
+    int32_t* sched;          // [3][8] per-XCD row range start, end and pull counter;
+                             // [24] = 1 when the block counts come from the caller
     int32_t N, nb, ntc;
     int64_t rows;
     float c;                 // scale * log2(e)
@@ -190,8 +192,11 @@ __device__ __forceinline__ void process_row(const FwdArgs& a, int64_t row, unsig
     using no = std::false_type;
     unsigned char* kslot = smem;                                       // 2 K tiles
     unsigned char* vslot = smem + 2 * C::K_BYTES;                      // 2 V^T tiles
-    unsigned char* kept = smem + C::BASE;                              // COMP: [nb] flags
+    // COMP: [nb] centroid weight of each block: its token count when skipped,
+    // 0 when kept or empty
+    unsigned char* cw = smem + C::BASE;
     int16_t* list = reinterpret_cast<int16_t*>(smem + C::BASE + C::MAX_NB);  // kept blocks
+    int16_t* lcnt = list + a.nb;                                       // their token counts
 
     const int i = (int)(row % a.nb);
     const int64_t bh = row / a.nb;
@@ -220,19 +225,24 @@ __device__ __forceinline__ void process_row(const FwdArgs& a, int64_t row, unsig
     const int beg = __builtin_amdgcn_readfirstlane(a.row_ptr[row]);
     const int nk = __builtin_amdgcn_readfirstlane(a.row_ptr[row + 1]) - beg;
     const int T = nk + (COMP ? a.ntc : 0);
-    // the row's kept blocks (clamped into range) and, for compensation, flags
+    const int16_t* cnt_h = a.cnt + bh * a.nb;
+    // the row's kept blocks (clamped into range) with their token counts and,
+    // for compensation, the centroid weights
     if constexpr (COMP)
-        for (int j = tid; j < a.nb; j += C::NT) kept[j] = 0;
+        for (int j = tid; j < a.nb; j += C::NT) cw[j] = (unsigned char)cnt_h[j];
     for (int e = tid; e < nk; e += C::NT) {
         int j = a.col_idx[beg + e];
         j = j < 0 ? 0 : (j >= a.nb ? a.nb - 1 : j);
         list[e] = (int16_t)j;
+        lcnt[e] = cnt_h[j];
     }
     __syncthreads();
     if constexpr (COMP) {
-        for (int e = tid; e < nk; e += C::NT) kept[list[e]] = 1;
+        for (int e = tid; e < nk; e += C::NT) cw[list[e]] = 0;
         __syncthreads();
     }
+    // block counts from the caller: centroid weights other than BLK and last_n
+    const bool var_cnt = COMP && __builtin_amdgcn_readfirstlane(a.sched[24]) != 0;
 
     // copies of tile u (kept block list[u], or centroid tile u - nk) into slot b
     auto issue_k = [&](int u, int b) {
@@ -325,14 +335,13 @@ __device__ __forceinline__ void process_row(const FwdArgs& a, int64_t row, unsig
     };
 
     // Vector phase: online softmax of S^T of tile u into P^T.  A tile with
-    // masked or weighted keys (short last block: -inf past its end; centroid
-    // tile: log2 n_j, -inf for kept blocks and past nb) adds that key bias,
+    // masked or weighted keys (short block: -inf past its token count; centroid
+    // tile: log2 n_j, -inf for kept or empty blocks and past nb) adds that key bias,
     // divided by the log2-domain scale c, to the raw scores; the max is taken on
     // raw scores (c > 0), and c s - m is one FMA.
     auto vector_phase = [&](int u) {
         const bool cent = COMP && u >= nk;
-        int nval = BLK;
-        if (!cent && last_n < BLK && __builtin_amdgcn_readfirstlane(list[u]) == a.nb - 1) nval = last_n;
+        const int nval = cent ? BLK : __builtin_amdgcn_readfirstlane((int)lcnt[u]);
         if (cent || nval < BLK) {
             const int j0 = (u - nk) * BLK;
 #pragma unroll
@@ -345,7 +354,11 @@ __device__ __forceinline__ void process_row(const FwdArgs& a, int64_t row, unsig
                         float b;
                         if (cent) {
                             const int j = j0 + key;
-                            b = (j < a.nb && !kept[j]) ? (j == a.nb - 1 ? lb_last : lb_full) : -INFINITY;
+                            const int n = j < a.nb ? cw[j] : 0;
+                            if (var_cnt)
+                                b = n ? __log2f((float)n) * inv_c : -INFINITY;
+                            else
+                                b = n == 0 ? -INFINITY : (n == BLK ? lb_full : lb_last);
                         } else {
                             b = key < nval ? 0.f : -INFINITY;
                         }
@@ -597,8 +610,26 @@ __global__ __launch_bounds__(256) void k_vt_prep(const uint16_t* __restrict__ V,
     }
 }
 
+// Token count of every KV block: the caller's counts (clamped to the block's
+// extent) or, without them, BLK and N - (nb - 1) BLK for the last block.
+// Records in sched[24] which of the two it was.
+__global__ void k_fill_counts(const int32_t* __restrict__ kv_count, int16_t* __restrict__ cnt,
+                              int32_t* __restrict__ sched, int N, int nb, int blk, int64_t total) {
+    const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (e == 0) sched[24] = kv_count != nullptr;
+    if (e >= total) return;
+    const int j = (int)(e % nb);
+    const int lim = N - j * blk < blk ? N - j * blk : blk;
+    int n = lim;
+    if (kv_count) {
+        n = kv_count[e];
+        n = n < 0 ? 0 : (n > lim ? lim : n);
+    }
+    cnt[e] = (int16_t)n;
+}
+
 // Centroid pseudo-tokens for compensation, rounded to bf16 for the matrix
-// cores: kbar = k_mean [nb][D]; vbar = v_sum / n_j, stored transposed in
+// cores: kbar = k_mean [nb][D]; vbar = v_sum / n_j (0 for an empty block), stored transposed in
 // tiles of BLK blocks [ntc][D][BLK] (blocks past nb are 0).  One workgroup per
 // run of kCompRun blocks, so that the launch fills the chip.
 constexpr int kCompRun = 16;
@@ -606,9 +637,9 @@ constexpr int kCompRun = 16;
 template <int D, int BLK>
 __global__ __launch_bounds__(256) void k_comp_prep(const float* __restrict__ k_mean,
                                                    const float* __restrict__ v_sum,
+                                                   const int16_t* __restrict__ cnt,
                                                    uint16_t* __restrict__ kbar,
-                                                   uint16_t* __restrict__ vbart, int nb, int ntc,
-                                                   int last_n) {
+                                                   uint16_t* __restrict__ vbart, int nb, int ntc) {
     static_assert(BLK % kCompRun == 0, "runs do not straddle centroid tiles");
     const int j0 = blockIdx.x * kCompRun;          // first block of the run
     const int64_t bh = blockIdx.y;
@@ -625,22 +656,23 @@ __global__ __launch_bounds__(256) void k_comp_prep(const float* __restrict__ k_m
         const int j = j0 + r;
         uint16_t v = 0;
         if (j < nb) {
-            const float n = (float)(j == nb - 1 ? last_n : BLK);
-            v = f32_to_bf16_rne(v_sum[(bh * nb + j) * (int64_t)D + d] / n);
+            const int n = cnt[bh * nb + j];
+            if (n > 0) v = f32_to_bf16_rne(v_sum[(bh * nb + j) * (int64_t)D + d] / (float)n);
         }
         vbart[((bh * ntc + tc) * (int64_t)D + d) * BLK + r0 + r] = v;
     }
 }
 
 struct WsLayout {
-    size_t sched, vt, kbar, vbart, total;
+    size_t sched, cnt, vt, kbar, vbart, total;
 };
 
 WsLayout ws_layout(const Geometry& g, bool comp) {
     WsLayout L{};
     const int64_t ntc = ceil_div(g.nb, g.block);
     size_t off = 0;
-    L.sched = off; off = align_up(off + 24 * sizeof(int32_t), 256);
+    L.sched = off; off = align_up(off + 32 * sizeof(int32_t), 256);
+    L.cnt = off; off = align_up(off + (size_t)g.BH() * g.nb * sizeof(int16_t), 256);
     L.vt = off; off = align_up(off + (size_t)g.BH() * g.nb * g.d * g.block * 2, 256);
     if (comp) {
         L.kbar = off; off = align_up(off + (size_t)g.BH() * g.nb * g.d * 2, 256);
@@ -650,20 +682,24 @@ WsLayout ws_layout(const Geometry& g, bool comp) {
     return L;
 }
 
-// Preparation: V re-laid out block by block, the centroid tiles with
-// compensation, and the per-XCD row ranges.
+// Preparation: the block token counts, V re-laid out block by block, the
+// centroid tiles with compensation, and the per-XCD row ranges.
 template <int D, int BLK, bool COMP>
 sa_status prepare_t(const FwdArgs& a, const Geometry& g, const uint16_t* V, uint16_t* vt,
-                    const float* k_mean, const float* v_sum, uint16_t* kbar, uint16_t* vbart,
-                    hipStream_t stream) {
+                    const float* k_mean, const float* v_sum, const int32_t* kv_count,
+                    uint16_t* kbar, uint16_t* vbart, hipStream_t stream) {
+    int16_t* cnt = const_cast<int16_t*>(a.cnt);
+    const int64_t ncnt = g.BH() * g.nb;
+    hipLaunchKernelGGL(k_fill_counts, dim3((unsigned)ceil_div(ncnt, 256)), dim3(256), 0, stream,
+                       kv_count, cnt, a.sched, g.N, g.nb, BLK, ncnt);
+    sa_status st = hip_check(hipGetLastError(), "k_fill_counts launch");
+    if (st != SA_OK) return st;
     hipLaunchKernelGGL((k_vt_prep<D, BLK>), dim3(g.nb, (unsigned)g.BH()), dim3(256), 0, stream, V,
                        vt, g.N, g.nb);
-    sa_status st = hip_check(hipGetLastError(), "k_vt_prep launch");
-    if (st != SA_OK) return st;
+    if ((st = hip_check(hipGetLastError(), "k_vt_prep launch")) != SA_OK) return st;
     if (COMP) {
         hipLaunchKernelGGL((k_comp_prep<D, BLK>), dim3(a.ntc * (BLK / kCompRun), (unsigned)g.BH()),
-                           dim3(256), 0, stream,
-                           k_mean, v_sum, kbar, vbart, g.nb, a.ntc, g.N - (g.nb - 1) * BLK);
+                           dim3(256), 0, stream, k_mean, v_sum, a.cnt, kbar, vbart, g.nb, a.ntc);
         if ((st = hip_check(hipGetLastError(), "k_comp_prep launch")) != SA_OK) return st;
     }
     if (a.rows == 0) return SA_OK;
@@ -677,10 +713,10 @@ template <int D, int BLK, bool COMP>
 sa_status run_t(const FwdArgs& a, const Geometry& g, hipStream_t stream) {
     using C = Cfg<D, BLK>;
     sa_status st = SA_OK;
-    const size_t lds = C::BASE + C::MAX_NB + 2 * (size_t)g.nb;
+    const size_t lds = C::BASE + C::MAX_NB + 4 * (size_t)g.nb;
     static bool configured = false;
     if (!configured) {
-        const int most = C::BASE + C::MAX_NB + 2 * C::MAX_NB;
+        const int most = C::BASE + C::MAX_NB + 4 * C::MAX_NB;
         st = hip_check(hipFuncSetAttribute((const void*)k_bsattn_fwd<D, BLK, COMP>,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, most),
                        "k_bsattn_fwd shared memory");
@@ -724,6 +760,7 @@ FwdArgs make_args(const Geometry& g, bool comp, const uint16_t* Q, const uint16_
     a.kbar = comp ? reinterpret_cast<uint16_t*>(ws + L.kbar) : nullptr;
     a.vbart = comp ? reinterpret_cast<uint16_t*>(ws + L.vbart) : nullptr;
     a.sched = reinterpret_cast<int32_t*>(ws + L.sched);
+    a.cnt = reinterpret_cast<int16_t*>(ws + L.cnt);
     return a;
 }
 
@@ -760,14 +797,15 @@ sa_status launch_vt_layout(const Geometry& g, const uint16_t* V, uint16_t* Vt, h
 }
 
 sa_status launch_fwd_prepare(const Geometry& g, const uint16_t* V, const int32_t* row_ptr,
-                             const float* k_mean, const float* v_sum, char* ws, hipStream_t stream) {
+                             const float* k_mean, const float* v_sum, const int32_t* kv_count,
+                             char* ws, hipStream_t stream) {
     const bool comp = k_mean != nullptr;
     if (g.nb > 4096) return fail(SA_ERR_UNSUPPORTED, "attention supports nb <= 4096 (got %d)", g.nb);
     const FwdArgs a = make_args(g, comp, nullptr, nullptr, row_ptr, nullptr, nullptr, nullptr, ws);
     uint16_t* vt = const_cast<uint16_t*>(a.Vt);
     uint16_t* kbar = const_cast<uint16_t*>(a.kbar);
     uint16_t* vbart = const_cast<uint16_t*>(a.vbart);
-#define SA_PREP(D_, B_, C_) prepare_t<D_, B_, C_>(a, g, V, vt, k_mean, v_sum, kbar, vbart, stream)
+#define SA_PREP(D_, B_, C_) prepare_t<D_, B_, C_>(a, g, V, vt, k_mean, v_sum, kv_count, kbar, vbart, stream)
     SA_DISPATCH(SA_PREP)
 #undef SA_PREP
 }

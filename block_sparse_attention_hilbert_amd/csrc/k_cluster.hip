@@ -1,0 +1,722 @@
+// Data-dependent block formation for gfx950 (SVOO page, section 2B: online
+// bidirectional co-clustering; SVG-EAR page, section 2A: k-means and a
+// permutation that makes every cluster contiguous).
+//
+// Per (batch, head) and per side (queries, keys):
+//   k_chunk_assign  initial partition: C equal chunks of the token order
+//   k_assign        every token to its best centroid: the largest
+//                   x.c (co-clustering affinity) or x.c - |c|^2/2 (k-means),
+//                   each dot product a sequential fp32 FMA chain over the
+//                   channels, ties to the lower index -- the integer decision
+//                   is taken in one fixed arithmetic
+//   k_hist, k_hist_scan, k_sort_scatter
+//                   stable counting sort of the tokens by cluster (tiles of
+//                   1024 tokens; LDS bitonic sort inside a tile)
+//   k_segmean       cluster means from exact fp64 sums (an empty cluster keeps
+//                   its previous centroid)
+//   k_layout        the padded layout: each cluster takes whole blocks
+//                   (its tokens in ascending order, then padding); per-block
+//                   cluster and token count
+//   k_gather_rows, k_scatter_rows
+//                   tensors into / out of the padded layout
+//   k_cselect, k_crow_count, k_crow_fill, k_block_comp
+//                   cluster-level selection, its block-level CSR and the
+//                   per-block compensation statistics
+#include <math.h>
+
+#include "sa_internal.h"
+
+namespace sa {
+namespace {
+
+constexpr int kTok = 1024;          // tokens per sort tile (and threads of the sort kernels)
+constexpr int kCmax = 1024;         // largest number of clusters
+
+// ----------------------------------------------------------------------------
+// initial partition
+// ----------------------------------------------------------------------------
+__global__ void k_chunk_assign(int32_t* __restrict__ assign, int N, int C) {
+    const int64_t bh = blockIdx.y;
+    const int t = blockIdx.x * blockDim.x + threadIdx.x;
+    if (t >= N) return;
+    // chunk c holds tokens [floor(cN/C), floor((c+1)N/C))
+    assign[bh * N + t] = (int32_t)((((int64_t)t + 1) * C + N - 1) / N - 1);
+}
+
+// ----------------------------------------------------------------------------
+// assignment
+// ----------------------------------------------------------------------------
+constexpr int kAsgThreads = 256;
+constexpr int kAsgChunk = 32;       // centroids staged in LDS at a time
+
+template <int D>
+__global__ __launch_bounds__(kAsgThreads) void k_assign(const uint16_t* __restrict__ X,
+                                                        const float* __restrict__ cent,
+                                                        int32_t* __restrict__ assign, int N, int C,
+                                                        int kmeans) {
+    __shared__ float cs[kAsgChunk][D];
+    __shared__ float bias[kAsgChunk];
+    const int64_t bh = blockIdx.y;
+    const int tid = threadIdx.x;
+    const int t = blockIdx.x * kAsgThreads + tid;
+    float x[D];
+    {
+        const int tt = t < N ? t : N - 1;
+        const uint4* row = reinterpret_cast<const uint4*>(X + (bh * N + tt) * (int64_t)D);
+#pragma unroll
+        for (int q = 0; q < D / 8; ++q) {
+            const uint4 v = row[q];
+            const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                x[q * 8 + 2 * e] = __uint_as_float(w[e] << 16);
+                x[q * 8 + 2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
+            }
+        }
+    }
+    float best = -INFINITY;
+    int arg = 0;
+    const float* cb = cent + bh * (int64_t)C * D;
+    for (int c0 = 0; c0 < C; c0 += kAsgChunk) {
+        const int nc = C - c0 < kAsgChunk ? C - c0 : kAsgChunk;
+        __syncthreads();
+        for (int p = tid; p < nc * D; p += kAsgThreads) cs[p / D][p % D] = cb[(int64_t)(c0 + p / D) * D + p % D];
+        __syncthreads();
+        if (tid < nc) {
+            float b = 0.f;
+            if (kmeans) {
+                float acc = 0.f;
+                for (int d = 0; d < D; ++d) acc = __builtin_fmaf(cs[tid][d], cs[tid][d], acc);
+                b = -0.5f * acc;
+            }
+            bias[tid] = b;
+        }
+        __syncthreads();
+        for (int j = 0; j < nc; ++j) {
+            float acc = 0.f;
+#pragma unroll
+            for (int d = 0; d < D; ++d) acc = __builtin_fmaf(x[d], cs[j][d], acc);
+            const float s = acc + bias[j];
+            if (s > best) {
+                best = s;
+                arg = c0 + j;
+            }
+        }
+    }
+    if (t < N) assign[bh * N + t] = arg;
+}
+
+// ----------------------------------------------------------------------------
+// stable counting sort by cluster
+// ----------------------------------------------------------------------------
+__global__ __launch_bounds__(kTok) void k_hist(const int32_t* __restrict__ assign,
+                                               int32_t* __restrict__ tile_hist, int N, int C,
+                                               int ntiles) {
+    __shared__ int32_t h[kCmax];
+    const int64_t bh = blockIdx.y;
+    const int tile = blockIdx.x, tid = threadIdx.x;
+    for (int c = tid; c < C; c += kTok) h[c] = 0;
+    __syncthreads();
+    const int t = tile * kTok + tid;
+    if (t < N) atomicAdd(&h[assign[bh * N + t]], 1);
+    __syncthreads();
+    for (int c = tid; c < C; c += kTok) tile_hist[(bh * ntiles + tile) * C + c] = h[c];
+}
+
+// Per cluster: total count and start in the sorted order; per (tile, cluster):
+// where the tile's tokens of that cluster go.
+__global__ __launch_bounds__(kTok) void k_hist_scan(const int32_t* __restrict__ tile_hist,
+                                                    int32_t* __restrict__ tile_off,
+                                                    int32_t* __restrict__ count,
+                                                    int32_t* __restrict__ cstart, int C,
+                                                    int ntiles) {
+    __shared__ int32_t wsum[kTok / 64];
+    const int64_t bh = blockIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    const int32_t* th = tile_hist + bh * ntiles * (int64_t)C;
+    int32_t total = 0;
+    if (tid < C)
+        for (int t = 0; t < ntiles; ++t) total += th[(int64_t)t * C + tid];
+    // exclusive scan of the totals over the clusters
+    int32_t x = total;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int32_t y = __shfl_up(x, off, 64);
+        if (lane >= off) x += y;
+    }
+    if (lane == 63) wsum[wid] = x;
+    __syncthreads();
+    int32_t before = 0;
+    for (int w = 0; w < wid; ++w) before += wsum[w];
+    const int32_t start = before + x - total;
+    if (tid < C) {
+        count[bh * C + tid] = total;
+        cstart[bh * C + tid] = start;
+        int32_t run = start;
+        for (int t = 0; t < ntiles; ++t) {
+            tile_off[(bh * ntiles + t) * (int64_t)C + tid] = run;
+            run += th[(int64_t)t * C + tid];
+        }
+    }
+}
+
+__global__ __launch_bounds__(kTok) void k_sort_scatter(const int32_t* __restrict__ assign,
+                                                       const int32_t* __restrict__ tile_off,
+                                                       int32_t* __restrict__ sorted, int N, int C,
+                                                       int ntiles) {
+    __shared__ uint32_t key[kTok];
+    const int64_t bh = blockIdx.y;
+    const int tile = blockIdx.x, tid = threadIdx.x;
+    const int t = tile * kTok + tid;
+    key[tid] = t < N ? ((uint32_t)assign[bh * N + t] << 10) | (uint32_t)tid : 0xffffffffu;
+    __syncthreads();
+    for (int size = 2; size <= kTok; size <<= 1) {
+        for (int stride = size >> 1; stride > 0; stride >>= 1) {
+            if (tid < kTok / 2) {
+                const int lo = 2 * tid - (tid & (stride - 1));
+                const int hi = lo + stride;
+                const bool up = (lo & size) == 0;
+                const uint32_t a = key[lo], b = key[hi];
+                if ((a > b) == up) { key[lo] = b; key[hi] = a; }
+            }
+            __syncthreads();
+        }
+    }
+    const uint32_t k = key[tid];
+    if (k == 0xffffffffu) return;
+    const uint32_t c = k >> 10;
+    // first sorted position of cluster c in this tile (lower bound of c << 10)
+    int lo = 0, hi = tid;
+    while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (key[mid] < (c << 10)) lo = mid + 1;
+        else hi = mid;
+    }
+    const int rank = tid - lo;
+    const int dst = tile_off[(bh * ntiles + tile) * (int64_t)C + c] + rank;
+    sorted[bh * N + dst] = tile * kTok + (int)(k & 1023u);
+}
+
+// ----------------------------------------------------------------------------
+// cluster means (exact fp64 sums, one fp32 rounding); empty clusters untouched
+// ----------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void k_segmean(const uint16_t* __restrict__ X,
+                                                 const int32_t* __restrict__ sorted,
+                                                 const int32_t* __restrict__ count,
+                                                 const int32_t* __restrict__ cstart,
+                                                 float* __restrict__ cent, int N, int C) {
+    constexpr int CH = D / 8;                 // 16-byte chunks per row
+    constexpr int ST = 256 / CH;              // token streams
+    __shared__ double red[ST][D];
+    const int c = blockIdx.x;
+    const int64_t bh = blockIdx.y;
+    const int tid = threadIdx.x;
+    const int n = count[bh * C + c];
+    if (n == 0) return;
+    const int s0 = cstart[bh * C + c];
+    const int ch = tid % CH, st = tid / CH;
+    double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    for (int r = st; r < n; r += ST) {
+        const int tok = sorted[bh * N + s0 + r];
+        const uint4 v = *reinterpret_cast<const uint4*>(X + (bh * N + tok) * (int64_t)D + ch * 8);
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            acc[2 * e] += (double)__uint_as_float(w[e] << 16);
+            acc[2 * e + 1] += (double)__uint_as_float(w[e] & 0xffff0000u);
+        }
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) red[st][ch * 8 + e] = acc[e];
+    __syncthreads();
+    if (tid < D) {
+        double s = 0.0;
+        for (int k = 0; k < ST; ++k) s += red[k][tid];
+        cent[(bh * C + c) * (int64_t)D + tid] = (float)(s / (double)n);
+    }
+}
+
+// ----------------------------------------------------------------------------
+// padded layout of one side
+// ----------------------------------------------------------------------------
+__global__ __launch_bounds__(kTok) void k_layout(const int32_t* __restrict__ sorted,
+                                                 const int32_t* __restrict__ count,
+                                                 const int32_t* __restrict__ cstart,
+                                                 int32_t* __restrict__ order,
+                                                 int32_t* __restrict__ blk_cluster,
+                                                 int32_t* __restrict__ blk_count, int N, int C,
+                                                 int block, int nbp) {
+    __shared__ int32_t bstart[kCmax];
+    __shared__ int32_t cst[kCmax];
+    __shared__ int32_t wsum[kTok / 64];
+    const int64_t bh = blockIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    const int64_t np = (int64_t)nbp * block;
+    for (int64_t p = tid; p < np; p += kTok) order[bh * np + p] = -1;
+    for (int j = tid; j < nbp; j += kTok) {
+        blk_cluster[bh * nbp + j] = -1;
+        blk_count[bh * nbp + j] = 0;
+    }
+    const int n = tid < C ? count[bh * C + tid] : 0;
+    const int nblk = (n + block - 1) / block;
+    int32_t x = nblk;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int32_t y = __shfl_up(x, off, 64);
+        if (lane >= off) x += y;
+    }
+    if (lane == 63) wsum[wid] = x;
+    __syncthreads();                       // also orders the fills above before the writes below
+    int32_t before = 0;
+    for (int w = 0; w < wid; ++w) before += wsum[w];
+    if (tid < C) {
+        bstart[tid] = before + x - nblk;
+        cst[tid] = cstart[bh * C + tid];
+    }
+    __syncthreads();
+    if (tid < C) {
+        for (int k = 0; k < nblk; ++k) {
+            blk_cluster[bh * nbp + bstart[tid] + k] = tid;
+            blk_count[bh * nbp + bstart[tid] + k] = n - k * block < block ? n - k * block : block;
+        }
+    }
+    for (int r = tid; r < N; r += kTok) {
+        // the cluster of sorted position r: the last c with cst[c] <= r
+        int lo = 0, hi = C - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (cst[mid] <= r) lo = mid;
+            else hi = mid - 1;
+        }
+        const int64_t p = (int64_t)bstart[lo] * block + (r - cst[lo]);
+        order[bh * np + p] = sorted[bh * N + r];
+    }
+}
+
+// ----------------------------------------------------------------------------
+// into / out of the padded layout (16-byte pieces of rows)
+// ----------------------------------------------------------------------------
+template <int D>
+__global__ void k_gather_rows(const uint16_t* __restrict__ src, const int32_t* __restrict__ order,
+                              uint16_t* __restrict__ dst, int N, int64_t np) {
+    constexpr int CH = D / 8;
+    const int64_t bh = blockIdx.y;
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= np * CH) return;
+    const int64_t p = i / CH;
+    const int ch = (int)(i % CH);
+    const int tok = order[bh * np + p];
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (tok >= 0) v = *reinterpret_cast<const uint4*>(src + (bh * N + tok) * (int64_t)D + ch * 8);
+    *reinterpret_cast<uint4*>(dst + (bh * np + p) * D + ch * 8) = v;
+}
+
+template <int D>
+__global__ void k_scatter_rows(const uint16_t* __restrict__ src, const int32_t* __restrict__ order,
+                               uint16_t* __restrict__ dst, const float* __restrict__ lse_src,
+                               float* __restrict__ lse_dst, int N, int64_t np) {
+    constexpr int CH = D / 8;
+    const int64_t bh = blockIdx.y;
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= np * CH) return;
+    const int64_t p = i / CH;
+    const int ch = (int)(i % CH);
+    const int tok = order[bh * np + p];
+    if (tok < 0) return;
+    *reinterpret_cast<uint4*>(dst + (bh * N + tok) * (int64_t)D + ch * 8) =
+        *reinterpret_cast<const uint4*>(src + (bh * np + p) * D + ch * 8);
+    if (lse_src && ch == 0) lse_dst[bh * N + tok] = lse_src[bh * np + p];
+}
+
+// ----------------------------------------------------------------------------
+// cluster-level selection
+// ----------------------------------------------------------------------------
+constexpr int kSelThreads = 256;
+
+__device__ __forceinline__ uint32_t ordered_f32(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u << 1) == 0) u = 0;                     // -0 -> +0
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+struct CSelArgs {
+    const float* S;             // [BH][C][C]
+    const int32_t* nk;          // [BH][C] key-cluster sizes
+    const int64_t* budget;      // [H] token budget (TOPK)
+    uint8_t* keep;              // [BH][C][C]
+    int32_t C, Cpad, H, rule, diag;
+    float mass;
+};
+
+__global__ __launch_bounds__(kSelThreads) void k_cselect(CSelArgs a) {
+    extern __shared__ unsigned char smem[];
+    unsigned long long* key = reinterpret_cast<unsigned long long*>(smem);   // [Cpad]
+    double* cum = reinterpret_cast<double*>(smem);                           // aliases key
+    int32_t* ord = reinterpret_cast<int32_t*>(smem + (size_t)a.Cpad * 8);    // [Cpad]
+    __shared__ int32_t s_live, s_cut;
+    const int64_t row = blockIdx.x;                // bh * C + cq
+    const int cq = (int)(row % a.C);
+    const int64_t bh = row / a.C;
+    const int h = (int)(bh % a.H);
+    const int tid = threadIdx.x;
+    const float* S = a.S + row * a.C;
+    const int32_t* nk = a.nk + bh * a.C;
+    if (tid == 0) { s_live = 0; s_cut = 0; }
+    __syncthreads();
+    int live_local = 0;
+    for (int j = tid; j < a.Cpad; j += kSelThreads) {
+        const bool live = j < a.C && nk[j] > 0;
+        live_local += live;
+        key[j] = live ? ((unsigned long long)(~ordered_f32(S[j])) << 32) | (uint32_t)j : ~0ull;
+    }
+    if (live_local) atomicAdd(&s_live, live_local);
+    __syncthreads();
+    for (int size = 2; size <= a.Cpad; size <<= 1) {
+        for (int stride = size >> 1; stride > 0; stride >>= 1) {
+            for (int t = tid; t < a.Cpad / 2; t += kSelThreads) {
+                const int lo = 2 * t - (t & (stride - 1));
+                const int hi = lo + stride;
+                const bool up = (lo & size) == 0;
+                const unsigned long long x = key[lo], y = key[hi];
+                if ((x > y) == up) { key[lo] = y; key[hi] = x; }
+            }
+            __syncthreads();
+        }
+    }
+    const int live = s_live;
+    for (int r = tid; r < live; r += kSelThreads) ord[r] = (int32_t)(key[r] & 0xffffffffu);
+    __syncthreads();
+    if (a.rule == SA_RULE_TOPK) {
+        if (tid == 0) {
+            const int64_t budget = a.budget[h];
+            int64_t run = 0;
+            int m = 0;
+            while (m < live) {
+                run += nk[ord[m]];
+                ++m;
+                if (run >= budget) break;
+            }
+            s_cut = m;
+        }
+    } else {
+        // weight n_b exp(S_b - S_max) in fp64, summed sequentially in rank order
+        const double smax = live > 0 ? (double)S[ord[0]] : 0.0;
+        for (int r = tid; r < live; r += kSelThreads)
+            cum[r] = (double)nk[ord[r]] * exp((double)S[ord[r]] - smax);
+        __syncthreads();
+        if (tid == 0 && live > 0) {
+            double run = 0.0;
+            for (int r = 0; r < live; ++r) { run += cum[r]; cum[r] = run; }
+            const double thr = (double)a.mass * cum[live - 1];
+            int m = live;
+            for (int r = 0; r < live; ++r)
+                if (cum[r] >= thr) { m = r + 1; break; }
+            s_cut = m;
+        }
+    }
+    __syncthreads();
+    const int m = s_cut;
+    uint8_t* out = a.keep + row * a.C;
+    for (int j = tid; j < a.C; j += kSelThreads) out[j] = 0;
+    __syncthreads();
+    for (int r = tid; r < m; r += kSelThreads) out[ord[r]] = 1;
+    if (tid == 0 && a.diag && nk[cq] > 0) out[cq] = 1;
+}
+
+// token budgets of a chunk of heads, passed by value
+constexpr int kBudgetChunk = 64;
+struct BudgetChunk {
+    int64_t v[kBudgetChunk];
+};
+__global__ void k_set_budget(int64_t* __restrict__ dst, BudgetChunk c, int n) {
+    if ((int)threadIdx.x < n) dst[threadIdx.x] = c.v[threadIdx.x];
+}
+
+// blocks kept by every row of the padded layout
+__global__ void k_crow_count(const uint8_t* __restrict__ keep, const int32_t* __restrict__ nk,
+                             const int32_t* __restrict__ q_blk, int32_t* __restrict__ counts,
+                             int64_t rows, int nbp, int C, int block) {
+    const int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (r >= rows) return;
+    const int64_t bh = r / nbp;
+    const int cq = q_blk[r];
+    int32_t n = 0;
+    if (cq >= 0) {
+        const uint8_t* kr = keep + (bh * C + cq) * C;
+        for (int c = 0; c < C; ++c)
+            if (kr[c]) n += (nk[bh * C + c] + block - 1) / block;
+    }
+    counts[r] = n;
+}
+
+// one wave per row: the blocks of the kept key clusters, ascending
+__global__ __launch_bounds__(256) void k_crow_fill(const uint8_t* __restrict__ keep,
+                                                   const int32_t* __restrict__ nk,
+                                                   const int32_t* __restrict__ q_blk,
+                                                   const int32_t* __restrict__ row_ptr,
+                                                   int32_t* __restrict__ col_idx, int64_t rows,
+                                                   int nbp, int C, int block) {
+    const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (r >= rows) return;
+    const int64_t bh = r / nbp;
+    const int cq = q_blk[r];
+    if (cq < 0) return;
+    const uint8_t* kr = keep + (bh * C + cq) * C;
+    int32_t bbase = 0;                 // first block of cluster c0 + lane (all clusters)
+    int32_t obase = row_ptr[r];        // next output slot
+    for (int c0 = 0; c0 < C; c0 += 64) {
+        const int c = c0 + lane;
+        const int nb_c = c < C ? (nk[bh * C + c] + block - 1) / block : 0;
+        const int kept = (c < C && kr[c]) ? nb_c : 0;
+        int32_t xb = nb_c, xk = kept;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const int32_t yb = __shfl_up(xb, off, 64), yk = __shfl_up(xk, off, 64);
+            if (lane >= off) { xb += yb; xk += yk; }
+        }
+        const int32_t first = bbase + xb - nb_c;
+        const int32_t out = obase + xk - kept;
+        for (int k = 0; k < kept; ++k) col_idx[out + k] = first + k;
+        bbase += __shfl(xb, 63, 64);
+        obase += __shfl(xk, 63, 64);
+    }
+}
+
+// compensation statistics per block: the cluster's centroid key and its value
+// mean times the block's token count
+template <int D>
+__global__ void k_block_comp(const float* __restrict__ k_cent, const float* __restrict__ v_cent,
+                             const int32_t* __restrict__ k_blk, const int32_t* __restrict__ k_cnt,
+                             float* __restrict__ k_mean, float* __restrict__ v_sum, int nbp, int C) {
+    const int j = blockIdx.x;
+    const int64_t bh = blockIdx.y;
+    const int d = threadIdx.x;
+    const int c = k_blk[bh * nbp + j];
+    const int n = k_cnt[bh * nbp + j];
+    float km = 0.f, vs = 0.f;
+    if (c >= 0 && n > 0) {
+        km = k_cent[(bh * C + c) * (int64_t)D + d];
+        vs = (float)n * v_cent[(bh * C + c) * (int64_t)D + d];
+    }
+    k_mean[(bh * nbp + j) * (int64_t)D + d] = km;
+    v_sum[(bh * nbp + j) * (int64_t)D + d] = vs;
+}
+
+// ----------------------------------------------------------------------------
+// host side
+// ----------------------------------------------------------------------------
+struct ClusterWs {
+    size_t assign[2], sorted[2], hist, off, cstart[2], total;
+};
+
+ClusterWs cluster_ws(const Geometry& g, int C) {
+    ClusterWs w{};
+    const int64_t ntiles = ceil_div(g.N, kTok);
+    size_t o = 0;
+    for (int s = 0; s < 2; ++s) {
+        w.assign[s] = o; o = align_up(o + (size_t)g.BH() * g.N * 4, 256);
+        w.sorted[s] = o; o = align_up(o + (size_t)g.BH() * g.N * 4, 256);
+        w.cstart[s] = o; o = align_up(o + (size_t)g.BH() * C * 4, 256);
+    }
+    w.hist = o; o = align_up(o + (size_t)g.BH() * ntiles * C * 4, 256);
+    w.off = o; o = align_up(o + (size_t)g.BH() * ntiles * C * 4, 256);
+    w.total = o;
+    return w;
+}
+
+template <int D>
+sa_status segmean(const Geometry& g, int C, const uint16_t* X, const int32_t* sorted,
+                  const int32_t* count, const int32_t* cstart, float* cent, hipStream_t st) {
+    hipLaunchKernelGGL((k_segmean<D>), dim3(C, (unsigned)g.BH()), dim3(256), 0, st, X, sorted,
+                       count, cstart, cent, g.N, C);
+    return hip_check(hipGetLastError(), "k_segmean launch");
+}
+
+// sorts side s by its assignment and refreshes its centroids
+template <int D>
+sa_status sort_and_mean(const Geometry& g, int C, char* ws, const ClusterWs& w, int s,
+                        const uint16_t* X, int32_t* count, float* cent, hipStream_t st) {
+    const int ntiles = (int)ceil_div(g.N, kTok);
+    const int32_t* assign = reinterpret_cast<const int32_t*>(ws + w.assign[s]);
+    int32_t* sorted = reinterpret_cast<int32_t*>(ws + w.sorted[s]);
+    int32_t* hist = reinterpret_cast<int32_t*>(ws + w.hist);
+    int32_t* off = reinterpret_cast<int32_t*>(ws + w.off);
+    int32_t* cstart = reinterpret_cast<int32_t*>(ws + w.cstart[s]);
+    hipLaunchKernelGGL(k_hist, dim3(ntiles, (unsigned)g.BH()), dim3(kTok), 0, st, assign, hist, g.N,
+                       C, ntiles);
+    sa_status e = hip_check(hipGetLastError(), "k_hist launch");
+    if (e != SA_OK) return e;
+    hipLaunchKernelGGL(k_hist_scan, dim3((unsigned)g.BH()), dim3(kTok), 0, st, hist, off, count,
+                       cstart, C, ntiles);
+    if ((e = hip_check(hipGetLastError(), "k_hist_scan launch")) != SA_OK) return e;
+    hipLaunchKernelGGL(k_sort_scatter, dim3(ntiles, (unsigned)g.BH()), dim3(kTok), 0, st, assign,
+                       off, sorted, g.N, C, ntiles);
+    if ((e = hip_check(hipGetLastError(), "k_sort_scatter launch")) != SA_OK) return e;
+    return segmean<D>(g, C, X, sorted, count, cstart, cent, st);
+}
+
+template <int D>
+sa_status assign_side(const Geometry& g, int C, char* ws, const ClusterWs& w, int s,
+                      const uint16_t* X, const float* cent, int kmeans, hipStream_t st) {
+    int32_t* assign = reinterpret_cast<int32_t*>(ws + w.assign[s]);
+    hipLaunchKernelGGL((k_assign<D>), dim3((unsigned)ceil_div(g.N, kAsgThreads), (unsigned)g.BH()),
+                       dim3(kAsgThreads), 0, st, X, cent, assign, g.N, C, kmeans);
+    return hip_check(hipGetLastError(), "k_assign launch");
+}
+
+template <int D>
+sa_status cluster_t(const Geometry& g, const sa_cluster_spec& cs, const uint16_t* Q,
+                    const uint16_t* K, const uint16_t* V, ClusterOut o, char* ws, hipStream_t st) {
+    const int C = cs.n_clusters;
+    const ClusterWs w = cluster_ws(g, C);
+    sa_status e;
+    // initial partition of both sides and its centroids
+    for (int s = 0; s < 2; ++s) {
+        hipLaunchKernelGGL(k_chunk_assign, dim3((unsigned)ceil_div(g.N, 256), (unsigned)g.BH()),
+                           dim3(256), 0, st, reinterpret_cast<int32_t*>(ws + w.assign[s]), g.N, C);
+        if ((e = hip_check(hipGetLastError(), "k_chunk_assign launch")) != SA_OK) return e;
+        if ((e = sort_and_mean<D>(g, C, ws, w, s, s ? K : Q, s ? o.k_count : o.q_count,
+                                  s ? o.k_cent : o.q_cent, st)) != SA_OK)
+            return e;
+    }
+    for (int it = 0; it < cs.iters; ++it) {
+        if (cs.mode == SA_CLUSTER_COCLUSTER) {
+            // keys by affinity to the query centroids, then queries by affinity
+            // to the refreshed key centroids
+            if ((e = assign_side<D>(g, C, ws, w, 1, K, o.q_cent, 0, st)) != SA_OK) return e;
+            if ((e = sort_and_mean<D>(g, C, ws, w, 1, K, o.k_count, o.k_cent, st)) != SA_OK) return e;
+            if ((e = assign_side<D>(g, C, ws, w, 0, Q, o.k_cent, 0, st)) != SA_OK) return e;
+            if ((e = sort_and_mean<D>(g, C, ws, w, 0, Q, o.q_count, o.q_cent, st)) != SA_OK) return e;
+        } else {
+            for (int s = 0; s < 2; ++s) {
+                const uint16_t* X = s ? K : Q;
+                float* cent = s ? o.k_cent : o.q_cent;
+                if ((e = assign_side<D>(g, C, ws, w, s, X, cent, 1, st)) != SA_OK) return e;
+                if ((e = sort_and_mean<D>(g, C, ws, w, s, X, s ? o.k_count : o.q_count, cent, st)) != SA_OK)
+                    return e;
+            }
+        }
+    }
+    if (o.v_cent) {
+        if ((e = segmean<D>(g, C, V, reinterpret_cast<const int32_t*>(ws + w.sorted[1]), o.k_count,
+                            reinterpret_cast<const int32_t*>(ws + w.cstart[1]), o.v_cent, st)) != SA_OK)
+            return e;
+    }
+    const int nbp = padded_block_count(g, C);
+    for (int s = 0; s < 2; ++s) {
+        hipLaunchKernelGGL(k_layout, dim3((unsigned)g.BH()), dim3(kTok), 0, st,
+                           reinterpret_cast<const int32_t*>(ws + w.sorted[s]),
+                           s ? o.k_count : o.q_count,
+                           reinterpret_cast<const int32_t*>(ws + w.cstart[s]),
+                           s ? o.k_order : o.q_order, s ? o.k_blk : o.q_blk,
+                           s ? o.k_cnt : o.q_cnt, g.N, C, g.block, nbp);
+        if ((e = hip_check(hipGetLastError(), "k_layout launch")) != SA_OK) return e;
+    }
+    return SA_OK;
+}
+
+}  // namespace
+
+int padded_block_count(const Geometry& g, int C) { return (int)ceil_div(g.N, g.block) + C; }
+
+size_t cluster_workspace_bytes(const Geometry& g, int C) { return cluster_ws(g, C).total; }
+
+sa_status launch_cluster(const Geometry& g, const sa_cluster_spec& cs, const uint16_t* Q,
+                         const uint16_t* K, const uint16_t* V, const ClusterOut& o, char* ws,
+                         hipStream_t st) {
+    return g.d == 128 ? cluster_t<128>(g, cs, Q, K, V, o, ws, st)
+                      : cluster_t<64>(g, cs, Q, K, V, o, ws, st);
+}
+
+sa_status launch_cluster_gather(const Geometry& g, int C, const int32_t* order, const uint16_t* src,
+                                uint16_t* dst, hipStream_t st) {
+    const int64_t np = (int64_t)padded_block_count(g, C) * g.block;
+    const unsigned nblk = (unsigned)ceil_div(np * (g.d / 8), 256);
+    if (g.d == 128)
+        hipLaunchKernelGGL((k_gather_rows<128>), dim3(nblk, (unsigned)g.BH()), dim3(256), 0, st, src,
+                           order, dst, g.N, np);
+    else
+        hipLaunchKernelGGL((k_gather_rows<64>), dim3(nblk, (unsigned)g.BH()), dim3(256), 0, st, src,
+                           order, dst, g.N, np);
+    return hip_check(hipGetLastError(), "k_gather_rows launch");
+}
+
+sa_status launch_cluster_scatter(const Geometry& g, int C, const int32_t* order,
+                                 const uint16_t* src, uint16_t* dst, const float* lse_src,
+                                 float* lse_dst, hipStream_t st) {
+    const int64_t np = (int64_t)padded_block_count(g, C) * g.block;
+    const unsigned nblk = (unsigned)ceil_div(np * (g.d / 8), 256);
+    if (g.d == 128)
+        hipLaunchKernelGGL((k_scatter_rows<128>), dim3(nblk, (unsigned)g.BH()), dim3(256), 0, st, src,
+                           order, dst, lse_src, lse_dst, g.N, np);
+    else
+        hipLaunchKernelGGL((k_scatter_rows<64>), dim3(nblk, (unsigned)g.BH()), dim3(256), 0, st, src,
+                           order, dst, lse_src, lse_dst, g.N, np);
+    return hip_check(hipGetLastError(), "k_scatter_rows launch");
+}
+
+size_t cluster_select_workspace_bytes(const Geometry& g, int C) {
+    const int nbp = padded_block_count(g, C);
+    size_t o = 0;
+    o = align_up(o + (size_t)g.BH() * C * C * 4, 256);      // scores
+    o = align_up(o + (size_t)g.BH() * C * C, 256);          // keep flags
+    o = align_up(o + (size_t)g.BH() * nbp * 4, 256);        // row counts
+    o = align_up(o + (size_t)g.H * 8, 256);                 // token budgets
+    return o;
+}
+
+sa_status launch_cluster_select(const Geometry& g, const sa_cluster_spec& cs, const ClusterSel& a,
+                                const int64_t* budget_host, char* ws, hipStream_t st) {
+    const int C = cs.n_clusters;
+    const int nbp = padded_block_count(g, C);
+    size_t o = 0;
+    float* S = reinterpret_cast<float*>(ws + o);
+    o = align_up(o + (size_t)g.BH() * C * C * 4, 256);
+    uint8_t* keep = reinterpret_cast<uint8_t*>(ws + o);
+    o = align_up(o + (size_t)g.BH() * C * C, 256);
+    int32_t* counts = reinterpret_cast<int32_t*>(ws + o);
+    o = align_up(o + (size_t)g.BH() * nbp * 4, 256);
+    int64_t* budget = reinterpret_cast<int64_t*>(ws + o);
+    if (a.scores) S = a.scores;
+    sa_status e;
+    if ((e = launch_pooled_scores(g.d, a.q_cent, a.k_cent, S, C, g.scale, g.BH(), st)) != SA_OK) return e;
+    if (a.rule == SA_RULE_TOPK) {
+        for (int h0 = 0; h0 < g.H; h0 += kBudgetChunk) {
+            BudgetChunk c{};
+            const int n = g.H - h0 < kBudgetChunk ? g.H - h0 : kBudgetChunk;
+            for (int t = 0; t < n; ++t) c.v[t] = budget_host[h0 + t];
+            hipLaunchKernelGGL(k_set_budget, dim3(1), dim3(kBudgetChunk), 0, st, budget + h0, c, n);
+            if ((e = hip_check(hipGetLastError(), "k_set_budget launch")) != SA_OK) return e;
+        }
+    }
+    CSelArgs ca{};
+    ca.S = S; ca.nk = a.k_count; ca.budget = budget; ca.keep = keep;
+    ca.C = C; ca.H = g.H; ca.rule = a.rule; ca.diag = a.diag; ca.mass = a.mass;
+    int cpad = 2;
+    while (cpad < C) cpad <<= 1;
+    ca.Cpad = cpad;
+    hipLaunchKernelGGL(k_cselect, dim3((unsigned)(g.BH() * C)), dim3(kSelThreads), (size_t)cpad * 12, st, ca);
+    if ((e = hip_check(hipGetLastError(), "k_cselect launch")) != SA_OK) return e;
+    const int64_t rows = g.BH() * nbp;
+    hipLaunchKernelGGL(k_crow_count, dim3((unsigned)ceil_div(rows, 256)), dim3(256), 0, st, keep,
+                       a.k_count, a.q_blk, counts, rows, nbp, C, g.block);
+    if ((e = hip_check(hipGetLastError(), "k_crow_count launch")) != SA_OK) return e;
+    if ((e = launch_row_scan(counts, a.row_ptr, rows, st)) != SA_OK) return e;
+    hipLaunchKernelGGL(k_crow_fill, dim3((unsigned)ceil_div(rows, 4)), dim3(256), 0, st, keep,
+                       a.k_count, a.q_blk, a.row_ptr, a.col_idx, rows, nbp, C, g.block);
+    if ((e = hip_check(hipGetLastError(), "k_crow_fill launch")) != SA_OK) return e;
+    if (a.k_mean) {
+        if (g.d == 128)
+            hipLaunchKernelGGL((k_block_comp<128>), dim3(nbp, (unsigned)g.BH()), dim3(128), 0, st,
+                               a.k_cent, a.v_cent, a.k_blk, a.k_cnt, a.k_mean, a.v_sum, nbp, C);
+        else
+            hipLaunchKernelGGL((k_block_comp<64>), dim3(nbp, (unsigned)g.BH()), dim3(64), 0, st,
+                               a.k_cent, a.v_cent, a.k_blk, a.k_cnt, a.k_mean, a.v_sum, nbp, C);
+        if ((e = hip_check(hipGetLastError(), "k_block_comp launch")) != SA_OK) return e;
+    }
+    return SA_OK;
+}
+
+}  // namespace sa

@@ -465,6 +465,17 @@ SelectPlan make_select_plan(const Geometry& g, const sa_select_spec& s) {
     return p;
 }
 
+sa_status launch_pooled_scores(int d, const float* qm, const float* km, float* S, int n,
+                               float scale, int64_t BH, hipStream_t stream) {
+    return d == 128 ? launch_score_d<128>(1, qm, km, S, n, n, scale, BH, stream)
+                    : launch_score_d<64>(1, qm, km, S, n, n, scale, BH, stream);
+}
+
+sa_status launch_row_scan(const int32_t* counts, int32_t* row_ptr, int64_t R, hipStream_t stream) {
+    hipLaunchKernelGGL(k_scan, dim3(1), dim3(kScanThreads), 0, stream, counts, row_ptr, R);
+    return hip_check(hipGetLastError(), "k_scan launch");
+}
+
 sa_status launch_centroids(const Geometry& g, const uint16_t* K, const uint16_t* V, float* k_mean,
                            float* v_sum, hipStream_t stream) {
     PoolArgs pa{};

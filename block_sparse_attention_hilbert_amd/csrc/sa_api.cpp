@@ -264,8 +264,8 @@ SA_API sa_status sparse_attn_fwd_prepare(const sa_problem* prob, const void* V,
     if ((k_mean == nullptr) != (v_sum == nullptr))
         return fail(SA_ERR_INVALID_ARG, "k_mean and v_sum must be given together");
     if ((st = check_fwd_workspace(g, k_mean != nullptr, workspace, ws_bytes)) != SA_OK) return st;
-    return launch_fwd_prepare(g, (const uint16_t*)V, row_ptr, k_mean, v_sum, (char*)workspace,
-                              (hipStream_t)stream);
+    return launch_fwd_prepare(g, (const uint16_t*)V, row_ptr, k_mean, v_sum, nullptr,
+                              (char*)workspace, (hipStream_t)stream);
 }
 
 SA_API sa_status sparse_attn_fwd_run(const sa_problem* prob, const void* Q, const void* K,
@@ -303,11 +303,206 @@ SA_API sa_status sparse_attn_fwd(const sa_problem* prob, const void* Q, const vo
         return fail(SA_ERR_INVALID_ARG, "k_mean and v_sum must be given together");
     const bool comp = k_mean != nullptr;
     if ((st = check_fwd_workspace(g, comp, workspace, ws_bytes)) != SA_OK) return st;
-    st = launch_fwd_prepare(g, (const uint16_t*)V, row_ptr, k_mean, v_sum, (char*)workspace,
-                            (hipStream_t)stream);
+    st = launch_fwd_prepare(g, (const uint16_t*)V, row_ptr, k_mean, v_sum, nullptr,
+                            (char*)workspace, (hipStream_t)stream);
     if (st != SA_OK) return st;
     return launch_fwd_run(g, comp, (const uint16_t*)Q, (const uint16_t*)K, row_ptr, col_idx,
                           (uint16_t*)O, lse, (char*)workspace, (hipStream_t)stream);
+}
+
+SA_API sa_status sparse_attn_fwd_prepare_counts(const sa_problem* prob, const void* V,
+                                                const int32_t* row_ptr, const float* k_mean,
+                                                const float* v_sum, const int32_t* kv_count,
+                                                void* workspace, size_t ws_bytes, void* stream) {
+    clear_error();
+    Geometry g;
+    sa_status st = check_problem(prob, &g);
+    if (st != SA_OK) return st;
+    if (!V) return fail(SA_ERR_INVALID_ARG, "V is required");
+    if (!aligned16(V)) return fail(SA_ERR_INVALID_ARG, "V must be 16-byte aligned");
+    if (!row_ptr) return fail(SA_ERR_INVALID_ARG, "row_ptr is required");
+    if (!kv_count) return fail(SA_ERR_INVALID_ARG, "kv_count is required");
+    if ((k_mean == nullptr) != (v_sum == nullptr))
+        return fail(SA_ERR_INVALID_ARG, "k_mean and v_sum must be given together");
+    if ((st = check_fwd_workspace(g, k_mean != nullptr, workspace, ws_bytes)) != SA_OK) return st;
+    return launch_fwd_prepare(g, (const uint16_t*)V, row_ptr, k_mean, v_sum, kv_count,
+                              (char*)workspace, (hipStream_t)stream);
+}
+
+// ---------------------------------------------------------------------------
+// data-dependent block formation
+// ---------------------------------------------------------------------------
+static sa_status check_cluster(const Geometry& g, const sa_cluster_spec* cs) {
+    if (!cs) return fail(SA_ERR_INVALID_ARG, "cspec is NULL");
+    if (cs->mode != SA_CLUSTER_COCLUSTER && cs->mode != SA_CLUSTER_KMEANS)
+        return fail(SA_ERR_INVALID_ARG, "unknown cluster mode %d", cs->mode);
+    const int cmax = g.N < 1024 ? g.N : 1024;
+    if (cs->n_clusters < 1 || cs->n_clusters > cmax)
+        return fail(SA_ERR_INVALID_ARG, "n_clusters = %d must be in [1, %d]", cs->n_clusters, cmax);
+    if (cs->iters < 1 || cs->iters > 64)
+        return fail(SA_ERR_INVALID_ARG, "iters = %d must be in [1, 64]", cs->iters);
+    const int64_t nbp = padded_block_count(g, cs->n_clusters);
+    if (nbp > 4096)
+        return fail(SA_ERR_UNSUPPORTED, "padded layout of %lld blocks (attention supports <= 4096)",
+                    (long long)nbp);
+    if (g.BH() * nbp * nbp > (int64_t)INT32_MAX)
+        return fail(SA_ERR_UNSUPPORTED, "B*H*nbp*nbp exceeds the int32 range of row_ptr");
+    return SA_OK;
+}
+
+static sa_status check_ws(size_t need, const void* workspace, size_t ws_bytes) {
+    if (need == 0) return SA_OK;
+    if (!workspace) return fail(SA_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", need);
+    if (((uintptr_t)workspace & 255u) != 0)
+        return fail(SA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+    if (ws_bytes < need)
+        return fail(SA_ERR_WORKSPACE, "workspace too small: %zu < %zu bytes", ws_bytes, need);
+    return SA_OK;
+}
+
+SA_API sa_status sparse_attn_cluster_size(const sa_problem* prob, const sa_cluster_spec* cspec,
+                                          int32_t* nb_padded, size_t* ws_cluster,
+                                          size_t* ws_select) {
+    clear_error();
+    Geometry g;
+    sa_status st = check_problem(prob, &g);
+    if (st != SA_OK) return st;
+    if ((st = check_cluster(g, cspec)) != SA_OK) return st;
+    if (nb_padded) *nb_padded = padded_block_count(g, cspec->n_clusters);
+    if (ws_cluster) *ws_cluster = cluster_workspace_bytes(g, cspec->n_clusters);
+    if (ws_select) *ws_select = cluster_select_workspace_bytes(g, cspec->n_clusters);
+    return SA_OK;
+}
+
+SA_API sa_status sparse_attn_cluster(const sa_problem* prob, const sa_cluster_spec* cspec,
+                                     const void* Q, const void* K, const void* V,
+                                     int32_t* q_order, int32_t* k_order, int32_t* q_blk,
+                                     int32_t* k_blk, int32_t* q_cnt, int32_t* k_cnt,
+                                     float* q_cent, float* k_cent, float* v_cent,
+                                     int32_t* q_count, int32_t* k_count, void* workspace,
+                                     size_t ws_bytes, void* stream) {
+    clear_error();
+    Geometry g;
+    sa_status st = check_problem(prob, &g);
+    if (st != SA_OK) return st;
+    if ((st = check_cluster(g, cspec)) != SA_OK) return st;
+    if (!Q || !K) return fail(SA_ERR_INVALID_ARG, "Q and K are required");
+    if (!aligned16(Q) || !aligned16(K) || (V && !aligned16(V)))
+        return fail(SA_ERR_INVALID_ARG, "Q, K, V must be 16-byte aligned");
+    if ((V == nullptr) != (v_cent == nullptr))
+        return fail(SA_ERR_INVALID_ARG, "V and v_cent must be given together");
+    if (!q_order || !k_order || !q_blk || !k_blk || !q_cnt || !k_cnt || !q_cent || !k_cent ||
+        !q_count || !k_count)
+        return fail(SA_ERR_INVALID_ARG, "every output except v_cent is required");
+    if ((st = check_ws(cluster_workspace_bytes(g, cspec->n_clusters), workspace, ws_bytes)) != SA_OK)
+        return st;
+    ClusterOut o{q_order, k_order, q_blk, k_blk, q_cnt, k_cnt, q_cent, k_cent, v_cent,
+                 q_count, k_count};
+    return launch_cluster(g, *cspec, (const uint16_t*)Q, (const uint16_t*)K, (const uint16_t*)V,
+                          o, (char*)workspace, (hipStream_t)stream);
+}
+
+static sa_status check_rows(const Geometry& g, const void* src, void* dst, int64_t src_rows,
+                            int64_t dst_rows) {
+    if (!src || !dst) return fail(SA_ERR_INVALID_ARG, "src and dst are required");
+    if (!aligned16(src) || !aligned16(dst))
+        return fail(SA_ERR_INVALID_ARG, "src and dst must be 16-byte aligned");
+    const char* s = (const char*)src;
+    const char* d = (const char*)dst;
+    const size_t sb = (size_t)g.BH() * src_rows * g.d * 2, db = (size_t)g.BH() * dst_rows * g.d * 2;
+    if (s < d + db && d < s + sb) return fail(SA_ERR_INVALID_ARG, "src and dst overlap");
+    return SA_OK;
+}
+
+SA_API sa_status sparse_attn_cluster_gather(const sa_problem* prob, const sa_cluster_spec* cspec,
+                                            const int32_t* order, const void* src, void* dst,
+                                            void* stream) {
+    clear_error();
+    Geometry g;
+    sa_status st = check_problem(prob, &g);
+    if (st != SA_OK) return st;
+    if ((st = check_cluster(g, cspec)) != SA_OK) return st;
+    if (!order) return fail(SA_ERR_INVALID_ARG, "order is required");
+    const int64_t np = (int64_t)padded_block_count(g, cspec->n_clusters) * g.block;
+    if ((st = check_rows(g, src, dst, g.N, np)) != SA_OK) return st;
+    return launch_cluster_gather(g, cspec->n_clusters, order, (const uint16_t*)src,
+                                 (uint16_t*)dst, (hipStream_t)stream);
+}
+
+SA_API sa_status sparse_attn_cluster_scatter(const sa_problem* prob, const sa_cluster_spec* cspec,
+                                             const int32_t* order, const void* src, void* dst,
+                                             const float* lse_src, float* lse_dst, void* stream) {
+    clear_error();
+    Geometry g;
+    sa_status st = check_problem(prob, &g);
+    if (st != SA_OK) return st;
+    if ((st = check_cluster(g, cspec)) != SA_OK) return st;
+    if (!order) return fail(SA_ERR_INVALID_ARG, "order is required");
+    if ((lse_src == nullptr) != (lse_dst == nullptr))
+        return fail(SA_ERR_INVALID_ARG, "lse_src and lse_dst must be given together");
+    const int64_t np = (int64_t)padded_block_count(g, cspec->n_clusters) * g.block;
+    if ((st = check_rows(g, src, dst, np, g.N)) != SA_OK) return st;
+    return launch_cluster_scatter(g, cspec->n_clusters, order, (const uint16_t*)src,
+                                  (uint16_t*)dst, lse_src, lse_dst, (hipStream_t)stream);
+}
+
+SA_API sa_status sparse_attn_cluster_select(const sa_problem* prob, const sa_cluster_spec* cspec,
+                                            const sa_select_spec* spec, const float* q_cent,
+                                            const float* k_cent, const float* v_cent,
+                                            const int32_t* k_count, const int32_t* q_blk,
+                                            const int32_t* k_blk, const int32_t* k_cnt,
+                                            int32_t* row_ptr, int32_t* col_idx, float* scores,
+                                            float* k_mean, float* v_sum, void* workspace,
+                                            size_t ws_bytes, void* stream) {
+    clear_error();
+    Geometry g;
+    sa_status st = check_problem(prob, &g);
+    if (st != SA_OK) return st;
+    if ((st = check_cluster(g, cspec)) != SA_OK) return st;
+    if (!spec) return fail(SA_ERR_INVALID_ARG, "spec is NULL");
+    if (spec->rule != SA_RULE_TOPK && spec->rule != SA_RULE_MASS)
+        return fail(SA_ERR_UNSUPPORTED, "cluster selection supports SA_RULE_TOPK and SA_RULE_MASS");
+    if (spec->sub_block != 0 || spec->window_frames != -1 || spec->n_anchors != 0)
+        return fail(SA_ERR_UNSUPPORTED,
+                    "cluster selection has no sub-blocks, windows or anchors (sub_block = 0, "
+                    "window_frames = -1, n_anchors = 0)");
+    if (spec->diag != 0 && spec->diag != 1) return fail(SA_ERR_INVALID_ARG, "diag must be 0 or 1");
+    if (spec->want_comp != 0 && spec->want_comp != 1)
+        return fail(SA_ERR_INVALID_ARG, "want_comp must be 0 or 1");
+    if (spec->rule == SA_RULE_TOPK) {
+        if (spec->topk) return fail(SA_ERR_UNSUPPORTED, "cluster top-k takes density, not topk");
+        if (!spec->density) return fail(SA_ERR_INVALID_ARG, "SA_RULE_TOPK needs density");
+        for (int h = 0; h < g.H; ++h)
+            if (!(spec->density[h] > 0.f && spec->density[h] <= 1.f))
+                return fail(SA_ERR_INVALID_ARG, "density[%d] = %g must be in (0, 1]", h,
+                            (double)spec->density[h]);
+    } else if (!(spec->mass > 0.f && spec->mass <= 1.f)) {
+        return fail(SA_ERR_INVALID_ARG, "mass = %g must be in (0, 1]", (double)spec->mass);
+    }
+    if (!q_cent || !k_cent || !k_count || !q_blk || !k_blk || !k_cnt || !row_ptr || !col_idx)
+        return fail(SA_ERR_INVALID_ARG, "q_cent, k_cent, k_count, q_blk, k_blk, k_cnt, row_ptr "
+                                        "and col_idx are required");
+    if (spec->want_comp && (!v_cent || !k_mean || !v_sum))
+        return fail(SA_ERR_INVALID_ARG, "want_comp needs v_cent, k_mean and v_sum");
+    const int C = cspec->n_clusters;
+    if ((st = check_ws(cluster_select_workspace_bytes(g, C), workspace, ws_bytes)) != SA_OK)
+        return st;
+    std::string bbuf((size_t)g.H * sizeof(int64_t), '\0');
+    int64_t* budget = (int64_t*)&bbuf[0];
+    for (int h = 0; h < g.H; ++h) {
+        int64_t b = 0;
+        if (spec->rule == SA_RULE_TOPK)
+            b = (int64_t)ceil((double)spec->density[h] * (double)g.N * (1.0 - 1e-6));
+        budget[h] = b < 1 ? 1 : b;
+    }
+    ClusterSel a{};
+    a.q_cent = q_cent; a.k_cent = k_cent; a.v_cent = v_cent;
+    a.k_count = k_count; a.q_blk = q_blk; a.k_blk = k_blk; a.k_cnt = k_cnt;
+    a.row_ptr = row_ptr; a.col_idx = col_idx; a.scores = scores;
+    a.k_mean = spec->want_comp ? k_mean : nullptr;
+    a.v_sum = spec->want_comp ? v_sum : nullptr;
+    a.rule = spec->rule; a.diag = spec->diag; a.mass = spec->mass;
+    return launch_cluster_select(g, *cspec, a, budget, (char*)workspace, (hipStream_t)stream);
 }
 
 SA_API const char* sparse_attn_last_error(void) { return g_last_error.c_str(); }

@@ -60,6 +60,48 @@ sa_status launch_select(const Geometry& g, const SelectPlan& p,
 sa_status launch_centroids(const Geometry& g, const uint16_t* K, const uint16_t* V, float* k_mean,
                            float* v_sum, hipStream_t stream);
 
+// Pooled scores S[bh][i][j] = fl32(scale * seqfma(qm_i, km_j)) of n x n rows.
+sa_status launch_pooled_scores(int d, const float* qm, const float* km, float* S, int n,
+                               float scale, int64_t BH, hipStream_t stream);
+
+// Exclusive scan counts[R] -> row_ptr[R+1].
+sa_status launch_row_scan(const int32_t* counts, int32_t* row_ptr, int64_t R, hipStream_t stream);
+
+// ----------------------------------------------------------------------------
+// data-dependent block formation (k_cluster.hip)
+// ----------------------------------------------------------------------------
+struct ClusterOut {
+    int32_t *q_order, *k_order;       // [BH][nbp*block] token per padded slot, -1 = padding
+    int32_t *q_blk, *k_blk;           // [BH][nbp] cluster of each padded block, -1 = none
+    int32_t *q_cnt, *k_cnt;           // [BH][nbp] tokens of each padded block
+    float *q_cent, *k_cent, *v_cent;  // [BH][C][d] (v_cent optional)
+    int32_t *q_count, *k_count;       // [BH][C]
+};
+
+struct ClusterSel {
+    const float *q_cent, *k_cent, *v_cent;
+    const int32_t *k_count, *q_blk, *k_blk, *k_cnt;
+    int32_t *row_ptr, *col_idx;
+    float *scores, *k_mean, *v_sum;   // scores [BH][C][C] optional; k_mean/v_sum [BH][nbp][d] optional
+    int32_t rule, diag;
+    float mass;
+};
+
+// ceil(N / block) + C: blocks of the padded clustered layout
+int padded_block_count(const Geometry& g, int C);
+size_t cluster_workspace_bytes(const Geometry& g, int C);
+size_t cluster_select_workspace_bytes(const Geometry& g, int C);
+sa_status launch_cluster(const Geometry& g, const sa_cluster_spec& cs, const uint16_t* Q,
+                         const uint16_t* K, const uint16_t* V, const ClusterOut& o, char* ws,
+                         hipStream_t stream);
+sa_status launch_cluster_gather(const Geometry& g, int C, const int32_t* order, const uint16_t* src,
+                                uint16_t* dst, hipStream_t stream);
+sa_status launch_cluster_scatter(const Geometry& g, int C, const int32_t* order,
+                                 const uint16_t* src, uint16_t* dst, const float* lse_src,
+                                 float* lse_dst, hipStream_t stream);
+sa_status launch_cluster_select(const Geometry& g, const sa_cluster_spec& cs, const ClusterSel& a,
+                                const int64_t* budget_host, char* ws, hipStream_t stream);
+
 // ----------------------------------------------------------------------------
 // error-aware routing keys (k_route.hip)
 // ----------------------------------------------------------------------------
@@ -77,11 +119,15 @@ sa_status launch_route_keys(const Geometry& g, const float* qm, const uint16_t* 
 // V re-laid out block by block, [BH, nb, d, block] (keys past N are zero).
 sa_status launch_vt_layout(const Geometry& g, const uint16_t* V, uint16_t* Vt, hipStream_t stream);
 
-// Workspace of the attention call: V transposed per block (+ centroid tiles).
+// Workspace of the attention call: block token counts, V transposed per block
+// (+ centroid tiles).
 size_t fwd_workspace_bytes(const Geometry& g, bool comp);
 
+// kv_count: device int32 [BH, nb] token counts per KV block, or null for the
+// fixed layout (block, the last one N - (nb - 1) block).
 sa_status launch_fwd_prepare(const Geometry& g, const uint16_t* V, const int32_t* row_ptr,
-                             const float* k_mean, const float* v_sum, char* ws, hipStream_t stream);
+                             const float* k_mean, const float* v_sum, const int32_t* kv_count,
+                             char* ws, hipStream_t stream);
 sa_status launch_fwd_run(const Geometry& g, bool comp, const uint16_t* Q, const uint16_t* K,
                          const int32_t* row_ptr, const int32_t* col_idx, uint16_t* O, float* lse,
                          char* ws, hipStream_t stream);

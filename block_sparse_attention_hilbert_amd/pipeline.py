@@ -13,6 +13,12 @@ with ``refresh_every = r`` the selection runs on calls 0, r, 2r, ... and the
 calls in between keep its CSR.  A reusing call still reorders its own inputs
 and, with compensation, recomputes the centroids of the skipped blocks from
 its own K and V (sparse_attn_centroids); only the keep decision is reused.
+
+:class:`ClusteredAttention` is the same call with data-dependent blocks
+(SVOO page, section 2B: bidirectional Q/K co-clustering; SVG-EAR page,
+section 2A: k-means clusters made contiguous by a permutation): cluster Q and
+K, gather them (and V) into the padded clustered layout, select over
+clusters, attend with per-block token counts, scatter O back to token order.
 """
 from __future__ import annotations
 
@@ -21,8 +27,10 @@ from typing import Optional
 import numpy as np
 import torch
 
-from . import (Problem, Selection, SelectSpec, alloc_workspace, centroids, fwd, fwd_prepare,
-               fwd_run, hilbert_perm_build, hilbert_permute, hilbert_unpermute, select,
+from . import (Clusters, ClusterSpec, Problem, Selection, SelectSpec, alloc_workspace,
+               centroids, cluster, cluster_gather, cluster_scatter, cluster_select,
+               cluster_size, fwd, fwd_prepare, fwd_prepare_counts, fwd_run,
+               hilbert_perm_build, hilbert_permute, hilbert_unpermute, padded_problem, select,
                workspace_size)
 
 
@@ -141,3 +149,95 @@ class BlockSparseAttention:
         rows = np.repeat(np.arange(p.rows), np.diff(rp))
         keep[rows, ci] = True
         return keep.reshape(p.B, p.H, p.nb, p.nb)
+
+
+class ClusteredAttention:
+    """One attention call over data-dependent blocks, preallocated buffers.
+
+    prob: the problem in token order; cspec: clustering; spec: selection over
+    clusters (SA_RULE_TOPK with density, or SA_RULE_MASS; diag; want_comp).
+    """
+
+    def __init__(self, prob: Problem, cspec: ClusterSpec, spec: SelectSpec, device="cuda",
+                 want_scores: bool = False, want_lse: bool = False):
+        self.prob, self.cspec, self.spec = prob, cspec, spec
+        self.device = torch.device(device)
+        self.nbp, ws_c, ws_s = cluster_size(prob, cspec)
+        self.pprob = padded_problem(prob, self.nbp)
+        pp = self.pprob
+        self.cl = Clusters.empty(prob, cspec, self.nbp, spec.want_comp, self.device)
+        rows = pp.rows
+        self.sel = Selection(torch.empty(rows + 1, dtype=torch.int32, device=self.device),
+                             torch.empty(rows * self.nbp, dtype=torch.int32, device=self.device))
+        if want_scores:
+            self.sel.scores = torch.empty(prob.B * prob.H, cspec.n_clusters, cspec.n_clusters,
+                                          dtype=torch.float32, device=self.device)
+        if spec.want_comp:
+            self.sel.k_mean = torch.empty(pp.B, pp.H, self.nbp, pp.d, dtype=torch.float32,
+                                          device=self.device)
+            self.sel.v_sum = torch.empty_like(self.sel.k_mean)
+        self.ws_cluster = alloc_workspace(ws_c, self.device)
+        self.ws_select = alloc_workspace(ws_s, self.device)
+        self.ws_fwd = alloc_workspace(workspace_size(pp, None), self.device)
+        pshape = (pp.B, pp.H, pp.N, pp.d)
+        self.Qp = torch.empty(pshape, dtype=torch.bfloat16, device=self.device)
+        self.Kp = torch.empty_like(self.Qp)
+        self.Vp = torch.empty_like(self.Qp)
+        self.Op = torch.empty_like(self.Qp)
+        self.O = torch.empty(prob.B, prob.H, prob.N, prob.d, dtype=torch.bfloat16,
+                             device=self.device)
+        self.lsep = self.lse = None
+        if want_lse:
+            self.lsep = torch.empty(pp.B, pp.H, pp.N, dtype=torch.float32, device=self.device)
+            self.lse = torch.empty(prob.B, prob.H, prob.N, dtype=torch.float32,
+                                   device=self.device)
+
+    def run_cluster(self, Q, K, V):
+        cluster(self.prob, self.cspec, Q, K, V if self.spec.want_comp else None, out=self.cl,
+                workspace=self.ws_cluster)
+        return self.cl
+
+    def run_gather(self, Q, K, V):
+        cluster_gather(self.prob, self.cspec, self.cl.q_order, Q, self.Qp)
+        cluster_gather(self.prob, self.cspec, self.cl.k_order, K, self.Kp)
+        cluster_gather(self.prob, self.cspec, self.cl.k_order, V, self.Vp)
+
+    def run_select(self) -> Selection:
+        return cluster_select(self.prob, self.cspec, self.spec, self.cl, out=self.sel,
+                              workspace=self.ws_select)
+
+    def run_fwd_prepare(self):
+        fwd_prepare_counts(self.pprob, self.Vp, self.sel.row_ptr, self.cl.k_cnt,
+                           self.sel.k_mean, self.sel.v_sum, workspace=self.ws_fwd)
+
+    def run_fwd_attention(self):
+        fwd_run(self.pprob, self.Qp, self.Kp, self.sel.row_ptr, self.sel.col_idx,
+                self.spec.want_comp, O=self.Op, lse=self.lsep, workspace=self.ws_fwd)
+        return self.Op
+
+    def run_scatter(self):
+        cluster_scatter(self.prob, self.cspec, self.cl.q_order, self.Op, self.O, self.lsep,
+                        self.lse)
+        return self.O
+
+    def __call__(self, Q, K, V) -> torch.Tensor:
+        self.run_cluster(Q, K, V)
+        self.run_gather(Q, K, V)
+        self.run_select()
+        self.run_fwd_prepare()
+        self.run_fwd_attention()
+        return self.run_scatter()
+
+    def kept_tokens(self) -> torch.Tensor:
+        """Key tokens each query block attends to exactly, [B*H*nbp] (device)."""
+        pp = self.pprob
+        rp = self.sel.row_ptr.long()
+        ci = self.sel.col_idx[: int(rp[-1])].long()
+        cnt = self.cl.k_cnt.reshape(-1).long()
+        bh = torch.repeat_interleave(torch.arange(pp.rows, device=rp.device) // self.nbp,
+                                     rp[1:] - rp[:-1])
+        per = cnt[bh * self.nbp + ci]
+        out = torch.zeros(pp.rows, dtype=torch.long, device=rp.device)
+        rows = torch.repeat_interleave(torch.arange(pp.rows, device=rp.device), rp[1:] - rp[:-1])
+        out.index_add_(0, rows, per)
+        return out

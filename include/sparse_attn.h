@@ -84,6 +84,21 @@ enum {
                              error-aware routing]; needs want_comp, whole blocks */
 };
 
+/* Data-dependent block formation [SVOO 2B co-clustering, EAR 2A k-means]. */
+enum {
+    SA_CLUSTER_COCLUSTER = 1, /* keys by affinity (dot product) to the query
+                                 centroids, then queries by affinity to the key
+                                 centroids, alternately  [SVOO 2B]            */
+    SA_CLUSTER_KMEANS = 2     /* k-means (squared Euclidean distance) on Q and on
+                                 K separately  [EAR 2A]                       */
+};
+
+typedef struct {
+    int32_t mode;         /* SA_CLUSTER_*                                        */
+    int32_t n_clusters;   /* C in [1, min(N, 1024)], the same for Q and K        */
+    int32_t iters;        /* rounds in [1, 64] (one round assigns both sides)    */
+} sa_cluster_spec;
+
 /* Selection rule.  Host-side struct; `topk` and `density` are host arrays. */
 typedef struct {
     int32_t rule;            /* SA_RULE_*                                         */
@@ -250,6 +265,118 @@ sa_status sparse_attn_fwd_run(const sa_problem* prob, const void* Q, const void*
                               const int32_t* row_ptr, const int32_t* col_idx,
                               int32_t with_comp, void* O, float* lse,
                               void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * ---------------------------------------------------------------------------
+ * Data-dependent block formation [SVOO 2B; EAR 2A].  Instead of fixed runs of
+ * `block` tokens, the blocks are clusters of tokens with similar content,
+ * found per (batch, head) and separately for queries and keys:
+ *   start:  C equal chunks of the token order; their means are the centroids;
+ *   round:  COCLUSTER -- every key goes to the query centroid c maximising
+ *           k.c, key centroids = means; every query goes to the key centroid
+ *           maximising q.c, query centroids = means (key cluster c is the
+ *           partner of query cluster c);
+ *           KMEANS -- every query (key) goes to the query (key) centroid
+ *           maximising x.c - |c|^2/2 (nearest in Euclidean distance), then
+ *           centroids = means.
+ * Arithmetic of the decision: x.c is a sequential fp32 fused-multiply-add
+ * chain over the channels (channel order), |c|^2/2 = fl32(0.5 * that chain of
+ * c with itself), one fp32 add; ties go to the lower cluster index.  Means
+ * are fp32 roundings of exact sums (fp64) divided by the count; an empty
+ * cluster keeps its previous centroid.
+ *
+ * Padded layout: a cluster takes whole blocks of the layout -- its tokens in
+ * ascending token order, then zero padding to a multiple of `block`; clusters
+ * follow each other in index order.  The layout has nbp = ceil(N/block) + C
+ * blocks (an upper bound for every head), Np = nbp * block slots; blocks past
+ * the last cluster are empty.  Attention on the layout is a plain sa_problem
+ * with N = Np (T = Hg = 1, W = Np) whose KV blocks carry token counts
+ * (sparse_attn_fwd_prepare_counts).
+ * ---------------------------------------------------------------------------
+ *
+ * sparse_attn_cluster_size: nbp and the workspace bytes of sparse_attn_cluster
+ *   (ws_cluster) and of sparse_attn_cluster_select (ws_select).
+ */
+sa_status sparse_attn_cluster_size(const sa_problem* prob, const sa_cluster_spec* cspec,
+                                   int32_t* nb_padded, size_t* ws_cluster, size_t* ws_select);
+
+/*
+ * sparse_attn_cluster: clusters Q and K of every (b, h) and lays them out.
+ * Q, K: device bf16 [B,H,N,d].  V: optional device bf16 [B,H,N,d]: with V,
+ *   v_cent receives the means of V over the key clusters (compensation).
+ * Outputs (device): q_order, k_order int32 [B*H, Np] (token at each padded
+ *   slot, -1 for padding); q_blk, k_blk int32 [B*H, nbp] (cluster of each
+ *   padded block, -1 for none); q_cnt, k_cnt int32 [B*H, nbp] (tokens in each
+ *   padded block); q_cent, k_cent fp32 [B*H, C, d]; q_count, k_count int32
+ *   [B*H, C] (cluster sizes).  v_cent may be NULL.
+ * workspace: device, 256-byte aligned, >= ws_cluster bytes.
+ */
+sa_status sparse_attn_cluster(const sa_problem* prob, const sa_cluster_spec* cspec,
+                              const void* Q, const void* K, const void* V,
+                              int32_t* q_order, int32_t* k_order, int32_t* q_blk,
+                              int32_t* k_blk, int32_t* q_cnt, int32_t* k_cnt,
+                              float* q_cent, float* k_cent, float* v_cent,
+                              int32_t* q_count, int32_t* k_count,
+                              void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * Rows into / out of the padded layout.  gather: dst[b,h,p,:] =
+ * src[b,h,order[b,h,p],:] (zeros where order = -1); src [B,H,N,d], dst
+ * [B,H,Np,d].  scatter: dst[b,h,order[b,h,p],:] = src[b,h,p,:] for every slot
+ * with order >= 0 (other rows of dst untouched); with lse_src/lse_dst
+ * (fp32 [B,H,Np] / [B,H,N], both or neither) the same for the log-sum-exp.
+ * bf16 rows, 16-byte aligned; src and dst must not overlap.
+ */
+sa_status sparse_attn_cluster_gather(const sa_problem* prob, const sa_cluster_spec* cspec,
+                                     const int32_t* order, const void* src, void* dst,
+                                     void* stream);
+sa_status sparse_attn_cluster_scatter(const sa_problem* prob, const sa_cluster_spec* cspec,
+                                      const int32_t* order, const void* src, void* dst,
+                                      const float* lse_src, float* lse_dst, void* stream);
+
+/*
+ * sparse_attn_cluster_select: the keep decision over clusters, as CSR over
+ * the padded blocks.  S[a,b] = fl32(scale * seqfma(q_cent[a], k_cent[b])).
+ * Empty key clusters are never kept; the others are ranked by S (descending,
+ * lower index on ties) and query cluster a keeps
+ *   SA_RULE_TOPK: the shortest prefix whose key tokens reach
+ *                 max(1, ceil(density[h] * N * (1 - 1e-6)));
+ *   SA_RULE_MASS: the shortest prefix whose sum of n_b exp(S_b - S_max)
+ *                 (fp64, rank order) reaches mass * (the total);
+ * plus b = a when diag and key cluster a is not empty.  Every padded block of
+ * query cluster a then keeps every padded block of its kept key clusters;
+ * blocks of no cluster keep nothing.  spec: rule TOPK (density only) or MASS,
+ *   diag, want_comp; sub_block, windows and anchors are not supported.
+ * Inputs as written by sparse_attn_cluster (v_cent needed with want_comp).
+ * row_ptr int32 [B*H*nbp + 1], col_idx int32 capacity B*H*nbp*nbp (ascending
+ *   rows).  scores: optional fp32 [B*H, C, C].  k_mean, v_sum: fp32
+ *   [B*H, nbp, d] with want_comp: the key centroid of the block's cluster and
+ *   (block token count) x (value mean of the cluster), so that the
+ *   compensation of the attention call adds, for every skipped key cluster,
+ *   its centroid with the cluster's token count as weight.
+ * workspace: device, 256-byte aligned, >= ws_select bytes.
+ */
+sa_status sparse_attn_cluster_select(const sa_problem* prob, const sa_cluster_spec* cspec,
+                                     const sa_select_spec* spec, const float* q_cent,
+                                     const float* k_cent, const float* v_cent,
+                                     const int32_t* k_count, const int32_t* q_blk,
+                                     const int32_t* k_blk, const int32_t* k_cnt,
+                                     int32_t* row_ptr, int32_t* col_idx, float* scores,
+                                     float* k_mean, float* v_sum,
+                                     void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * sparse_attn_fwd_prepare with token counts per KV block: kv_count device
+ * int32 [B*H, nb] in [0, block]; keys past the count of a block take no part
+ * (masked in kept blocks; weight n_j = the count for compensation, a block
+ * with count 0 contributes nothing).  sparse_attn_fwd_prepare is this call
+ * with the counts of the fixed layout (block, the last one N - (nb-1)*block).
+ * Follow it with sparse_attn_fwd_run as usual.
+ */
+sa_status sparse_attn_fwd_prepare_counts(const sa_problem* prob, const void* V,
+                                         const int32_t* row_ptr, const float* k_mean,
+                                         const float* v_sum, const int32_t* kv_count,
+                                         void* workspace, size_t ws_bytes, void* stream);
 
 /* Text of the last failure on the calling thread ("" after success). */
 const char* sparse_attn_last_error(void);

@@ -101,8 +101,9 @@ def test_workspace_sizes_are_consistent():
     # V re-laid out per block [B*H*nb*d*block] bf16 + centroid keys [B*H*nb*d]
     # + centroid values in tiles of `block` blocks [B*H*ceil(nb/block)*d*block]
     BH, nb, d, blk = 2, 4, 128, 128
-    # (plus 256 bytes of row-schedule counters)
-    assert sa.workspace_size(p) == 256 + 2 * (BH * nb * d * blk + BH * nb * d + BH * 1 * d * blk)
+    # (plus 256 bytes of row-schedule counters and 256 bytes of block token
+    # counts, int16 [B*H*nb] rounded up)
+    assert sa.workspace_size(p) == 512 + 2 * (BH * nb * d * blk + BH * nb * d + BH * 1 * d * blk)
 
 
 def test_select_and_fwd_reject_before_any_launch():
@@ -193,3 +194,78 @@ def test_reuse_policy_needs_a_first_selection():
     with pytest.raises(ValueError):
         BlockSparseAttention(_prob(), sa.SelectSpec(rule="mass"), device="cpu", refresh_every=0)
 
+
+
+def test_cluster_sizes_and_validation():
+    """Data-dependent block formation: sizes of the padded layout and the
+    workspaces, and every malformed call rejected on the host."""
+    p = sa.Problem(1, 12, 32760, 128, 21, 30, 52, 128)
+    nbp, wc, ws = sa.cluster_size(p, sa.ClusterSpec("kmeans", 64, 3))
+    assert nbp == 256 + 64
+    # assignment + sorted order of both sides (int32 [BH, N]) dominate the workspace
+    assert wc >= 4 * 12 * 32760 * 4
+    assert ws >= 12 * 64 * 64 * 5
+    small = _prob()
+    for cs, code in [(sa.ClusterSpec("kmeans", 0, 1), sa.SA_ERR_INVALID_ARG),
+                     (sa.ClusterSpec("kmeans", 391, 1), sa.SA_ERR_INVALID_ARG),   # > N
+                     (sa.ClusterSpec("kmeans", 4, 0), sa.SA_ERR_INVALID_ARG),
+                     (sa.ClusterSpec("kmeans", 4, 65), sa.SA_ERR_INVALID_ARG)]:
+        assert _err(sa.cluster_size, small, cs) == code, cs
+    bad_mode = sa.SaClusterSpec(7, 4, 1)
+    assert sa.lib.sparse_attn_cluster_size(ctypes.byref(small.c()), ctypes.byref(bad_mode),
+                                           None, None, None) == sa.SA_ERR_INVALID_ARG
+    big = sa.Problem(1, 1, 4090 * 64, 64, 4090, 1, 64, 64)
+    assert _err(sa.cluster_size, big, sa.ClusterSpec("kmeans", 16, 1)) == sa.SA_ERR_UNSUPPORTED
+
+
+def test_cluster_calls_reject_before_any_launch():
+    p = _prob().c()
+    cs = sa.ClusterSpec("cocluster", 4, 2).c()
+    vp = ctypes.c_void_p
+    fake, odd = vp(1 << 20), vp((1 << 20) + 8)
+    outs = [fake] * 10
+    cl = sa.lib.sparse_attn_cluster
+    assert cl(ctypes.byref(p), ctypes.byref(cs), None, fake, None, *outs[:8], None, *outs[:2],
+              fake, 1 << 30, None) == sa.SA_ERR_INVALID_ARG            # no Q
+    assert cl(ctypes.byref(p), ctypes.byref(cs), odd, fake, None, *outs[:8], None, *outs[:2],
+              fake, 1 << 30, None) == sa.SA_ERR_INVALID_ARG            # misaligned
+    assert cl(ctypes.byref(p), ctypes.byref(cs), fake, fake, fake, *outs[:8], None, *outs[:2],
+              fake, 1 << 30, None) == sa.SA_ERR_INVALID_ARG            # V without v_cent
+    assert cl(ctypes.byref(p), ctypes.byref(cs), fake, fake, None, *outs[:8], None, *outs[:2],
+              fake, 64, None) == sa.SA_ERR_WORKSPACE
+    assert cl(ctypes.byref(p), ctypes.byref(cs), fake, fake, None, *outs[:8], None, *outs[:2],
+              vp((1 << 20) + 64), 1 << 30, None) == sa.SA_ERR_WORKSPACE
+    # gather / scatter: overlap, missing order, lse pairs
+    g, s = sa.lib.sparse_attn_cluster_gather, sa.lib.sparse_attn_cluster_scatter
+    assert g(ctypes.byref(p), ctypes.byref(cs), None, fake, vp(1 << 30), None) == \
+        sa.SA_ERR_INVALID_ARG
+    assert g(ctypes.byref(p), ctypes.byref(cs), fake, fake, vp((1 << 20) + 4096), None) == \
+        sa.SA_ERR_INVALID_ARG
+    assert b"overlap" in sa.lib.sparse_attn_last_error()
+    assert s(ctypes.byref(p), ctypes.byref(cs), fake, fake, vp(1 << 30), fake, None, None) == \
+        sa.SA_ERR_INVALID_ARG
+    # selection over clusters: supported rules and structure only
+    sel = sa.lib.sparse_attn_cluster_select
+    ptrs = [fake] * 7 + [fake, fake]
+    for spec, code in [(sa.SelectSpec(rule="none"), sa.SA_ERR_UNSUPPORTED),
+                       (sa.SelectSpec(rule="err", density=[0.2, 0.2], want_comp=True),
+                        sa.SA_ERR_UNSUPPORTED),
+                       (sa.SelectSpec(rule="topk", topk=[1, 1]), sa.SA_ERR_UNSUPPORTED),
+                       (sa.SelectSpec(rule="topk"), sa.SA_ERR_INVALID_ARG),
+                       (sa.SelectSpec(rule="mass", sub_block=16), sa.SA_ERR_UNSUPPORTED),
+                       (sa.SelectSpec(rule="mass", window_frames=1), sa.SA_ERR_UNSUPPORTED),
+                       (sa.SelectSpec(rule="mass", n_anchors=1), sa.SA_ERR_UNSUPPORTED),
+                       (sa.SelectSpec(rule="mass", mass=0.0), sa.SA_ERR_INVALID_ARG),
+                       (sa.SelectSpec(rule="mass", want_comp=True), sa.SA_ERR_INVALID_ARG)]:
+        c, keep = spec.c()
+        st = sel(ctypes.byref(p), ctypes.byref(cs), ctypes.byref(c), *ptrs, None, None, None,
+                 fake, 1 << 30, None)
+        assert st == code, spec
+    c, keep = sa.SelectSpec(rule="mass").c()
+    assert sel(ctypes.byref(p), ctypes.byref(cs), ctypes.byref(c), *ptrs, None, None, None,
+               fake, 8, None) == sa.SA_ERR_WORKSPACE
+    # prepare with counts needs the counts
+    prep = sa.lib.sparse_attn_fwd_prepare_counts
+    assert prep(ctypes.byref(p), fake, fake, None, None, None, fake, 1 << 30, None) == \
+        sa.SA_ERR_INVALID_ARG
+    assert b"kv_count" in sa.lib.sparse_attn_last_error()

@@ -1,0 +1,227 @@
+"""GPU parity of data-dependent block formation (SVOO section 2B co-clustering,
+SVG-EAR section 2A k-means), through the C ABI, against the oracle.
+
+Bar:
+* cluster sizes, centroids (query, key, value means), the padded layouts
+  (slot order, block cluster, block token count), the cluster scores and the
+  per-block compensation statistics: bit-exact -- the assignment is a decision
+  taken in the same fp32 arithmetic on both sides, means are fp32 roundings of
+  exact sums;
+* the block-level keep (CSR): bit-exact up to rows excused as near ties
+  (cluster scores within 1e-6 of the row's largest |score|, or the cumulative
+  weight at the cut within 1e-6 of mass x total), counted and reported;
+* attention output in token order, given the oracle's clusters and keep:
+  max |err| <= 2e-2, mean |err| <= 2e-3 against the float64 oracle; lse within
+  2e-2.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from oracle import clusters as OC
+import workloads as W
+from parity_util import ATOL_MAX, ATOL_MEAN, LSE_ATOL, TIE_REL, from_dev, log, to_dev
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import block_sparse_attention_hilbert_amd as sa  # noqa: F401  (fails loudly if unbuilt)
+    yield
+
+
+def _pipe(wl, want_lse=True):
+    import block_sparse_attention_hilbert_amd as sa
+    from block_sparse_attention_hilbert_amd.pipeline import ClusteredAttention
+    spec = sa.spec_for(wl)
+    if spec.topk is not None:
+        raise ValueError("cluster selection takes a density")
+    return ClusteredAttention(sa.problem_for(wl), sa.cluster_spec_for(wl), spec,
+                              want_scores=True, want_lse=want_lse)
+
+
+# several clusters, ragged cluster sizes, both head dims and block sizes
+BASE = W.CONFIGS[2].replace(T=3, Hg=10, W=13, H=2)          # N = 390
+SMALL = {
+    "cocluster_mass_d128_b128": BASE.replace(cluster="cocluster", n_clusters=3, cluster_iters=2),
+    "kmeans_topk_comp_d128_b64": BASE.replace(block=64, cluster="kmeans", n_clusters=6,
+                                              cluster_iters=3, rule="topk", density=0.3,
+                                              comp=True),
+    "cocluster_topk_comp_diag_d64_b64": BASE.replace(d=64, block=64, H=3, cluster="cocluster",
+                                                     n_clusters=8, cluster_iters=4, rule="topk",
+                                                     density=0.25, comp=True, diag=True),
+    "kmeans_mass_d64_b128_wide": W.CONFIGS[2].replace(T=5, Hg=9, W=29, H=2, d=64,
+                                                      cluster="kmeans", n_clusters=10,
+                                                      cluster_iters=2, mass=0.7),
+    "kmeans_one_cluster": BASE.replace(block=64, cluster="kmeans", n_clusters=1,
+                                       cluster_iters=1, rule="topk", density=0.5, comp=True),
+    "cocluster_iid_many": W.CONFIGS[1].replace(T=3, Hg=10, W=13, H=2, cluster="cocluster",
+                                               n_clusters=40, cluster_iters=2, rule="mass",
+                                               mass=0.8, diag=False, comp=True, topk=None),
+}
+
+
+def _keep_from_csr(rp, ci, rows, nbp):
+    keep = np.zeros((rows, nbp), dtype=bool)
+    r = np.repeat(np.arange(rows), np.diff(rp))
+    keep[r, ci[: rp[-1]]] = True
+    return keep
+
+
+def _excused(S_row, nk, wl, gk, ok):
+    """A differing cluster-level row is excused by a near tie of the oracle's
+    scores among the swapped clusters or a cumulative weight at the cut within
+    1e-6 of the threshold."""
+    only_g, only_o = np.nonzero(gk & ~ok)[0], np.nonzero(ok & ~gk)[0]
+    s = S_row.astype(np.float64)
+    live = np.nonzero(nk > 0)[0]
+    tol = TIE_REL * np.max(np.abs(s[live]))
+    if only_g.size and only_o.size and all(abs(s[x] - s[y]) <= tol for x in only_g for y in only_o):
+        return True
+    if wl.rule == "mass":
+        order = live[np.argsort(-s[live], kind="stable")]
+        w = nk[order] * np.exp(s[order] - s[order[0]])
+        cum = np.cumsum(w)
+        thr = float(np.float32(wl.mass)) * cum[-1]
+        return bool(np.min(np.abs(cum - thr)) <= TIE_REL * cum[-1])
+    return False
+
+
+def check_case(wl, Q, K, V, heads, q_clusters_per_head=None, seed=0):
+    """Runs the clustered call on the GPU and checks the heads `heads` (indices
+    into b * H + h) against the oracle.  Returns the attention errors."""
+    pipe = _pipe(wl)
+    O = pipe(to_dev(Q), to_dev(K), to_dev(V))
+    torch.cuda.synchronize()
+    C, nbp, blk = wl.n_clusters, pipe.nbp, wl.block
+    cl, sel = pipe.cl, pipe.sel
+    g = {k: getattr(cl, k).cpu().numpy() for k in
+         ("q_order", "k_order", "q_blk", "k_blk", "q_cnt", "k_cnt", "q_cent", "k_cent",
+          "q_count", "k_count")}
+    v_cent = cl.v_cent.cpu().numpy() if cl.v_cent is not None else None
+    S_gpu = sel.scores.cpu().numpy()
+    rp = sel.row_ptr.cpu().numpy().astype(np.int64)
+    ci = sel.col_idx.cpu().numpy()
+    keep_gpu = _keep_from_csr(rp, ci, wl.B * wl.H * nbp, nbp).reshape(wl.B * wl.H, nbp, nbp)
+    for r in range(keep_gpu.shape[0] * nbp):
+        cols = ci[rp[r]: rp[r + 1]]
+        assert np.all(np.diff(cols) > 0), "CSR rows must be ascending"
+    Og = from_dev(O)
+    lse_g = pipe.lse.cpu().numpy()
+    km = sel.k_mean.cpu().numpy() if sel.k_mean is not None else None
+    vs = sel.v_sum.cpu().numpy() if sel.v_sum is not None else None
+    rng = np.random.default_rng(seed)
+    errs, lse_errs, excused = [], [], 0
+    for bh in heads:
+        b, h = divmod(bh, wl.H)
+        q = oracle.bf16_to_f64(Q[b, h])
+        k = oracle.bf16_to_f64(K[b, h])
+        v = oracle.bf16_to_f64(V[b, h])
+        ref = OC.cluster_workload_head(wl, q, k)
+        tag = f"{wl.name} bh={bh}"
+        assert np.array_equal(g["q_count"][bh], ref["nq"]), tag
+        assert np.array_equal(g["k_count"][bh], ref["nk"]), tag
+        assert np.array_equal(g["q_cent"][bh].view(np.uint32), ref["cq"].view(np.uint32)), tag
+        assert np.array_equal(g["k_cent"][bh].view(np.uint32), ref["ck"].view(np.uint32)), tag
+        for side in ("q", "k"):
+            assert np.array_equal(g[f"{side}_order"][bh], ref[f"{side}_order"]), (tag, side)
+            assert np.array_equal(g[f"{side}_blk"][bh], ref[f"{side}_blk"]), (tag, side)
+            assert np.array_equal(g[f"{side}_cnt"][bh], ref[f"{side}_cnt"]), (tag, side)
+        assert np.array_equal(S_gpu[bh].view(np.uint32), ref["S"].view(np.uint32)), tag
+        if wl.comp:
+            vref = OC.cluster_means(v, ref["ak"], C)
+            live = ref["nk"] > 0
+            assert np.array_equal(v_cent[bh][live].view(np.uint32), vref[live].view(np.uint32)), tag
+            kb, kc = ref["k_blk"], ref["k_cnt"]
+            for j in range(nbp):
+                if kb[j] >= 0:
+                    assert np.array_equal(km[b, h, j].view(np.uint32),
+                                          ref["ck"][kb[j]].view(np.uint32)), (tag, j)
+                    want = (np.float32(kc[j]) * vref[kb[j]]).astype(np.float32)
+                    assert np.array_equal(vs[b, h, j].view(np.uint32), want.view(np.uint32)), (tag, j)
+                else:
+                    assert not km[b, h, j].any() and not vs[b, h, j].any(), (tag, j)
+        # cluster-level keep read back from the block-level CSR
+        keepC_gpu = np.zeros((C, C), dtype=bool)
+        qb = ref["q_blk"]
+        for i in range(nbp):
+            if qb[i] >= 0:
+                kept_blocks = np.nonzero(keep_gpu[bh, i])[0]
+                keepC_gpu[qb[i], np.unique(ref["k_blk"][kept_blocks])] = True
+        assert np.array_equal(keep_gpu[bh], OC.cluster_block_keep(keepC_gpu, qb, ref["k_blk"])), tag
+        for a in np.nonzero(np.any(keepC_gpu != ref["keepC"], axis=1))[0]:
+            if ref["nq"][a] == 0:
+                continue
+            assert _excused(ref["S"][a], ref["nk"], wl, keepC_gpu[a], ref["keepC"][a]), (tag, a)
+            excused += 1
+        # attention in token order, given the oracle's partition and keep
+        qcs = list(range(C))
+        if q_clusters_per_head is not None and q_clusters_per_head < C:
+            qcs = sorted(rng.choice(C, q_clusters_per_head, replace=False).tolist())
+        Oref, lref = OC.cluster_attention_head(q, k, v, ref["aq"], ref["ak"], ref["keepC"],
+                                               wl.scale, comp=wl.comp, q_clusters=qcs)
+        sel_tok = np.isin(ref["aq"], qcs)
+        og = oracle.bf16_to_f64(Og[b, h])
+        errs.append(np.abs(og[sel_tok] - Oref[sel_tok]).ravel())
+        lg, lr = lse_g[b, h][sel_tok].astype(np.float64), lref[sel_tok]
+        fin = np.isfinite(lr)
+        assert np.array_equal(fin, np.isfinite(lg)), tag
+        if fin.any():
+            lse_errs.append(np.abs(lg[fin] - lr[fin]))
+    e = np.concatenate(errs)
+    le = np.concatenate(lse_errs) if lse_errs else np.zeros(1)
+    return float(e.max()), float(e.mean()), float(le.max()), excused
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_small_cluster_parity(name):
+    wl = SMALL[name].replace(name=name)
+    log(f"[cluster] {name}: N={wl.N} H={wl.H} d={wl.d} block={wl.block} C={wl.n_clusters} "
+        f"mode={wl.cluster} rule={wl.rule} comp={wl.comp}")
+    Q, K, V = W.make_qkv(wl)
+    emax, emean, lmax, exc = check_case(wl, Q, K, V, heads=range(wl.B * wl.H))
+    log(f"[cluster] {name}: max {emax:.2e} mean {emean:.2e} lse {lmax:.2e} excused rows {exc}")
+    assert emax <= ATOL_MAX and emean <= ATOL_MEAN and lmax <= LSE_ATOL
+
+
+@pytest.mark.parametrize("name", ["wan13b_cocluster", "wan13b_kmeans_comp"])
+def test_full_size_cluster_parity(name):
+    """The full 1.3B-sized layer (12 heads, N = 32,760): the whole call on the
+    GPU; layouts, centroids, scores and keep of two heads checked exactly and
+    the output of 6 sampled query clusters per checked head."""
+    wl = W.by_name(name)
+    log(f"[cluster-full] {name}: N={wl.N} H={wl.H} C={wl.n_clusters}")
+    Q, K, V = W.make_qkv(wl)
+    emax, emean, lmax, exc = check_case(wl, Q, K, V, heads=[0, wl.H - 1],
+                                        q_clusters_per_head=6, seed=1)
+    log(f"[cluster-full] {name}: max {emax:.2e} mean {emean:.2e} lse {lmax:.2e} excused {exc}")
+    assert emax <= ATOL_MAX and emean <= ATOL_MEAN and lmax <= LSE_ATOL
+
+
+def test_counts_prepare_matches_fixed_layout():
+    """fwd_prepare_counts with the fixed layout's own counts gives the same bits
+    as fwd_prepare (with compensation), and counts below a block's extent mask
+    exactly the keys past them (equal to attention on the shortened sequence)."""
+    import block_sparse_attention_hilbert_amd as sa
+    wl = W.CONFIGS[2].replace(T=3, Hg=10, W=13, H=2, rule="topk", density=0.5, comp=True)
+    prob = sa.problem_for(wl)
+    Q, K, V = (to_dev(x) for x in W.make_qkv(wl))
+    sel = sa.select(prob, sa.spec_for(wl), Q, K, V)
+    ws = sa.alloc_workspace(sa.workspace_size(prob, None), Q.device)
+    O1 = torch.empty_like(Q)
+    O2 = torch.empty_like(Q)
+    sa.fwd_prepare(prob, V, sel.row_ptr, sel.k_mean, sel.v_sum, workspace=ws)
+    sa.fwd_run(prob, Q, K, sel.row_ptr, sel.col_idx, True, O=O1, workspace=ws)
+    nb = prob.nb
+    cnt = np.full((wl.B * wl.H, nb), wl.block, np.int32)
+    cnt[:, -1] = wl.N - (nb - 1) * wl.block
+    sa.fwd_prepare_counts(prob, V, sel.row_ptr, torch.from_numpy(cnt).cuda(), sel.k_mean,
+                          sel.v_sum, workspace=ws)
+    sa.fwd_run(prob, Q, K, sel.row_ptr, sel.col_idx, True, O=O2, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(O1.view(torch.int16), O2.view(torch.int16))

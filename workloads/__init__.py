@@ -79,6 +79,9 @@ class Workload:
     gen: str = "smooth"            # "iid" | "smooth"
     head_freq: bool = False        # head-dependent wave-number range
     seed: int = 0
+    cluster: str = ""              # "" (fixed blocks) | "cocluster" | "kmeans"
+    n_clusters: int = 0
+    cluster_iters: int = 0
 
     @property
     def N(self) -> int:
@@ -129,10 +132,22 @@ CONFIGS = {
 # routing (SVG-EAR page, section 2B) on the 1.3B-sized layer at a fixed 20 %
 # budget with compensation, and the score-based top-k rule at the same budget
 # for comparison.
+#
+# Data-dependent block formation on the same layer: SVOO's bidirectional
+# Q/K co-clustering (section 2B) with the cumulative-mass rule it selects by
+# (section 2A), and SVG-EAR's k-means clusters (section 2A) with a 20 % token
+# budget and centroid compensation.  64 clusters of ~512 tokens each (4
+# blocks of 128 when full) keep the padding of the clustered layout small;
+# 3 refinement rounds.
 EXTRA = {
     "wan13b_err": CONFIGS[2].replace(name="wan13b_err", rule="err", density=0.2, comp=True),
     "wan13b_topk_comp": CONFIGS[2].replace(name="wan13b_topk_comp", rule="topk", density=0.2,
                                            comp=True),
+    "wan13b_cocluster": CONFIGS[2].replace(name="wan13b_cocluster", cluster="cocluster",
+                                           n_clusters=64, cluster_iters=3),
+    "wan13b_kmeans_comp": CONFIGS[2].replace(name="wan13b_kmeans_comp", cluster="kmeans",
+                                             n_clusters=64, cluster_iters=3, rule="topk",
+                                             density=0.2, comp=True),
 }
 
 
