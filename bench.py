@@ -20,6 +20,13 @@ peak, timed with HIP events on the stream it is launched on.
 With ``--refresh-every R`` (mask reuse across calls) only every R-th call
 selects; the others keep its mask and recompute only the compensation
 centroids; the default R = 1 selects on every call.
+
+Workloads with data-dependent blocks (``--workload wan13b_cocluster`` or
+``wan13b_kmeans_comp``) time the clustered call instead: clustering of Q and
+K, gathering Q, K, V into the padded clustered layout and the selection over
+clusters (reported as ``ms_select``), the attention on that layout with token
+counts per block, and the scatter of O back to token order.  Their kept work
+counts true tokens only (padding excluded).
 """
 from __future__ import annotations
 
@@ -109,6 +116,41 @@ def cpu_baseline(wl, Q, K, V, budget_s: float = 15.0):
                       f"{blocks} query blocks ({dt:.1f} s wall)"}
 
 
+def cpu_baseline_clusters(wl, Q, K, V, budget_s: float = 15.0):
+    """The clustered path's oracle on a bounded sample: heads in turn, each one's
+    clustering and selection, then float64 attention of its query clusters one
+    by one until the budget is spent.  Kept-token TFLOP/s of the sample."""
+    import oracle
+    from oracle import clusters as OC
+    from threadpoolctl import threadpool_info
+
+    t0 = time.perf_counter()
+    flops = 0.0
+    heads = done = 0
+    for h in range(wl.H):
+        q, k, v = (oracle.bf16_to_f64(x[0, h]) for x in (Q, K, V))
+        ref = OC.cluster_workload_head(wl, q, k)
+        kept_tok = ref["keepC"].astype(np.float64) @ ref["nk"].astype(np.float64)
+        for a in range(wl.n_clusters):
+            if ref["nq"][a] == 0:
+                continue
+            OC.cluster_attention_head(q, k, v, ref["aq"], ref["ak"], ref["keepC"], wl.scale,
+                                      comp=wl.comp, q_clusters=[a])
+            flops += 4.0 * wl.d * float(ref["nq"][a]) * float(kept_tok[a])
+            done += 1
+            if time.perf_counter() - t0 > budget_s:
+                break
+        heads += 1
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{heads} of {wl.H} heads of batch 0: clustering + selection + float64 "
+                      f"attention of {done} query clusters ({dt:.1f} s wall)"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -154,6 +196,11 @@ def main():
         return torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).cuda()
 
     Qd, Kd, Vd = dev(Q), dev(K), dev(V)
+    if wl.cluster:
+        if args.refresh_every != 1:
+            log("[bench] --refresh-every applies to fixed blocks only")
+            sys.exit(2)
+        return bench_clusters(args, wl, Q, K, V, Qd, Kd, Vd)
     pipe = BlockSparseAttention(sa.problem_for(wl), sa.spec_for(wl), hilbert=wl.hilbert,
                                 refresh_every=args.refresh_every)
     stream = torch.cuda.current_stream()
@@ -240,6 +287,93 @@ def main():
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (oracle, bounded sample)")
         out["cpu_baseline"] = cpu_baseline(wl, Q, K, V)
+    print(json.dumps(out), flush=True)
+
+
+def bench_clusters(args, wl, Q, K, V, Qd, Kd, Vd):
+    import torch
+    import block_sparse_attention_hilbert_amd as sa
+    from block_sparse_attention_hilbert_amd.pipeline import ClusteredAttention
+
+    pipe = ClusteredAttention(sa.problem_for(wl), sa.cluster_spec_for(wl), sa.spec_for(wl))
+    stream = torch.cuda.current_stream()
+
+    def step(ev):
+        ev[0].record(stream)
+        pipe.run_cluster(Qd, Kd, Vd)
+        ev[1].record(stream)
+        pipe.run_gather(Qd, Kd, Vd)
+        pipe.run_select()
+        ev[2].record(stream)
+        pipe.run_fwd_prepare()
+        ev[3].record(stream)
+        pipe.run_fwd_attention()
+        ev[4].record(stream)
+        pipe.run_scatter()
+
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)]
+              for _ in range(max(args.steps, 1))]
+    log(f"[bench] warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step(events[0])
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    step_s = (time.perf_counter() - t0) / args.steps
+    ev = events[: args.steps]
+    cl_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    gs_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
+    prep_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in ev]))
+    fwd_ms = float(np.mean([e[3].elapsed_time(e[4]) for e in ev]))
+    log(f"[bench] {args.steps} steps: {step_s * 1e3:.3f} ms/step")
+    # kept work in true tokens: q tokens of each padded query block times the
+    # key tokens of the blocks it keeps
+    kept = pipe.kept_tokens().cpu().numpy().astype(np.float64)
+    qcnt = pipe.cl.q_cnt.reshape(-1).cpu().numpy().astype(np.float64)
+    F_kept = 4.0 * wl.d * float((qcnt * kept).sum())
+    slots = float(pipe.pprob.N) * wl.B * wl.H
+    fwd_s = fwd_ms / 1e3
+    achieved = F_kept / fwd_s / 1e12
+    sel_s = (cl_ms + gs_ms) / 1e3
+    out = {
+        "metric": "ms/attn call + effective TFLOP/s (kept blocks) at N=32760, H=12, d=128, 1 GPU",
+        "value": round(F_kept / step_s / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_s * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded smooth-field video-latent Q/K, N(0,1) V)",
+        "config": {"workload": wl.name, "B": wl.B, "H": wl.H, "N": wl.N, "d": wl.d,
+                   "latent_grid": [wl.T, wl.Hg, wl.W], "block": wl.block, "rule": wl.rule,
+                   "mass": wl.mass if wl.rule == "mass" else None,
+                   "cluster": wl.cluster, "n_clusters": wl.n_clusters,
+                   "cluster_iters": wl.cluster_iters, "padded_blocks": pipe.nbp,
+                   "token_density_kept": round(float((qcnt * kept).sum()) /
+                                               (wl.B * wl.H * float(wl.N) ** 2), 4),
+                   "padding_fraction": round(1.0 - wl.B * wl.H * wl.N / slots, 4),
+                   "compensation": wl.comp, "parallelism": "single GPU"},
+        "ms_cluster": round(cl_ms, 4),
+        "ms_gather_select": round(gs_ms, 4),
+        "ms_select": round(sel_s * 1e3, 4),
+        "ms_attention": round(fwd_ms, 4),
+        "ms_attention_prepare": round(prep_ms, 4),
+        "select_over_attention": round(sel_s / fwd_s, 4),
+        "kept_tflop_per_call": round(F_kept / 1e12, 4),
+        "roofline": {"bound": "mfma", "kernel": ATTN_KERNEL, "achieved": round(achieved, 2),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": read_traffic(wl.name)},
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] cpu baseline (oracle, bounded sample)")
+        out["cpu_baseline"] = cpu_baseline_clusters(wl, Q, K, V)
     print(json.dumps(out), flush=True)
 
 

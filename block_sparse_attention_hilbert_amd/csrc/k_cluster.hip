@@ -4,7 +4,8 @@
 //
 // Per (batch, head) and per side (queries, keys):
 //   k_chunk_assign  initial partition: C equal chunks of the token order
-//   k_assign        every token to its best centroid: the largest
+//   k_cent_prep, k_assign
+//                   every token to its best centroid: the largest
 //                   x.c (co-clustering affinity) or x.c - |c|^2/2 (k-means),
 //                   each dot product a sequential fp32 FMA chain over the
 //                   channels, ties to the lower index -- the integer decision
@@ -47,59 +48,82 @@ __global__ void k_chunk_assign(int32_t* __restrict__ assign, int N, int C) {
 // assignment
 // ----------------------------------------------------------------------------
 constexpr int kAsgThreads = 256;
-constexpr int kAsgChunk = 32;       // centroids staged in LDS at a time
+constexpr int kAsgIlp = 8;          // centroid chains a thread runs side by side
 
+// Centroids of every head transposed to [D][Cp] (Cp = C rounded up to 8, the
+// padding 0) and their decision bias: -|c|^2/2 = fl32(-0.5 * seqfma(c, c))
+// for k-means, 0 for co-clustering, -inf for the padding (never chosen).
+template <int D>
+__global__ void k_cent_prep(const float* __restrict__ cent, float* __restrict__ centT,
+                            float* __restrict__ bias, int C, int Cp, int kmeans) {
+    const int64_t bh = blockIdx.y;
+    const int e = blockIdx.x * blockDim.x + threadIdx.x;      // (d, c) of centT
+    if (e < D * Cp) {
+        const int d = e / Cp, c = e % Cp;
+        centT[bh * (int64_t)D * Cp + e] = c < C ? cent[(bh * C + c) * (int64_t)D + d] : 0.f;
+    }
+    if (e < Cp) {
+        float b = e < C ? 0.f : -INFINITY;
+        if (kmeans && e < C) {
+            const float* ce = cent + (bh * C + e) * (int64_t)D;
+            float acc = 0.f;
+            for (int d = 0; d < D; ++d) acc = __builtin_fmaf(ce[d], ce[d], acc);
+            b = -0.5f * acc;
+        }
+        bias[bh * Cp + e] = b;
+    }
+}
+
+// One thread per token, its row in registers as packed bf16 pairs.  The
+// centroid values are the same for every lane, so they come through the
+// scalar data path (wave-uniform loads of 8 consecutive floats of the
+// transposed centroids) and enter each FMA as its scalar operand.  Each of the
+// 8 interleaved chains is the sequential FMA over the channels in channel
+// order; the score is the chain plus the bias, one fp32 add; strict > keeps
+// the lowest index on ties.
 template <int D>
 __global__ __launch_bounds__(kAsgThreads) void k_assign(const uint16_t* __restrict__ X,
-                                                        const float* __restrict__ cent,
-                                                        int32_t* __restrict__ assign, int N, int C,
-                                                        int kmeans) {
-    __shared__ float cs[kAsgChunk][D];
-    __shared__ float bias[kAsgChunk];
+                                                        const float* __restrict__ centT,
+                                                        const float* __restrict__ bias,
+                                                        int32_t* __restrict__ assign, int N,
+                                                        int Cp) {
     const int64_t bh = blockIdx.y;
-    const int tid = threadIdx.x;
-    const int t = blockIdx.x * kAsgThreads + tid;
-    float x[D];
+    const int t = blockIdx.x * kAsgThreads + threadIdx.x;
+    uint32_t xw[D / 2];
     {
         const int tt = t < N ? t : N - 1;
         const uint4* row = reinterpret_cast<const uint4*>(X + (bh * N + tt) * (int64_t)D);
 #pragma unroll
         for (int q = 0; q < D / 8; ++q) {
             const uint4 v = row[q];
-            const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                x[q * 8 + 2 * e] = __uint_as_float(w[e] << 16);
-                x[q * 8 + 2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
-            }
+            xw[4 * q] = v.x;
+            xw[4 * q + 1] = v.y;
+            xw[4 * q + 2] = v.z;
+            xw[4 * q + 3] = v.w;
         }
     }
+    const float* ct = centT + bh * (int64_t)D * Cp;
+    const float* bs = bias + bh * Cp;
     float best = -INFINITY;
     int arg = 0;
-    const float* cb = cent + bh * (int64_t)C * D;
-    for (int c0 = 0; c0 < C; c0 += kAsgChunk) {
-        const int nc = C - c0 < kAsgChunk ? C - c0 : kAsgChunk;
-        __syncthreads();
-        for (int p = tid; p < nc * D; p += kAsgThreads) cs[p / D][p % D] = cb[(int64_t)(c0 + p / D) * D + p % D];
-        __syncthreads();
-        if (tid < nc) {
-            float b = 0.f;
-            if (kmeans) {
-                float acc = 0.f;
-                for (int d = 0; d < D; ++d) acc = __builtin_fmaf(cs[tid][d], cs[tid][d], acc);
-                b = -0.5f * acc;
-            }
-            bias[tid] = b;
-        }
-        __syncthreads();
-        for (int j = 0; j < nc; ++j) {
-            float acc = 0.f;
+#pragma unroll 1
+    for (int j = 0; j < Cp; j += kAsgIlp) {
+        float acc[kAsgIlp];
 #pragma unroll
-            for (int d = 0; d < D; ++d) acc = __builtin_fmaf(x[d], cs[j][d], acc);
-            const float s = acc + bias[j];
+        for (int k = 0; k < kAsgIlp; ++k) acc[k] = 0.f;
+#pragma unroll
+        for (int d = 0; d < D; ++d) {
+            const float xd = __uint_as_float((d & 1) ? (xw[d / 2] & 0xffff0000u) : (xw[d / 2] << 16));
+            const float* c = ct + (int64_t)d * Cp + j;
+#pragma unroll
+            for (int k = 0; k < kAsgIlp; ++k) acc[k] = __builtin_fmaf(xd, c[k], acc[k]);
+        }
+#pragma unroll
+        for (int k = 0; k < kAsgIlp; ++k) {
+            const float s = acc[k] + bs[j + k];
             if (s > best) {
                 best = s;
-                arg = c0 + j;
+                arg = j + k;
             }
         }
     }
@@ -216,17 +240,32 @@ __global__ __launch_bounds__(256) void k_segmean(const uint16_t* __restrict__ X,
     if (n == 0) return;
     const int s0 = cstart[bh * C + c];
     const int ch = tid % CH, st = tid / CH;
+    const int32_t* srt = sorted + bh * N + s0;
+    const uint16_t* Xh = X + bh * N * (int64_t)D + ch * 8;
     double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    for (int r = st; r < n; r += ST) {
-        const int tok = sorted[bh * N + s0 + r];
-        const uint4 v = *reinterpret_cast<const uint4*>(X + (bh * N + tok) * (int64_t)D + ch * 8);
+    auto add = [&](uint4 v) {
         const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             acc[2 * e] += (double)__uint_as_float(w[e] << 16);
             acc[2 * e + 1] += (double)__uint_as_float(w[e] & 0xffff0000u);
         }
+    };
+    // the sums are exact, so the order of the additions is free: four rows in
+    // flight per thread hide the index -> row load latency
+    constexpr int U = 4;
+    int r = st;
+    for (; r + (U - 1) * ST < n; r += U * ST) {
+        int tok[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) tok[u] = srt[r + u * ST];
+        uint4 v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) v[u] = *reinterpret_cast<const uint4*>(Xh + (int64_t)tok[u] * D);
+#pragma unroll
+        for (int u = 0; u < U; ++u) add(v[u]);
     }
+    for (; r < n; r += ST) add(*reinterpret_cast<const uint4*>(Xh + (int64_t)srt[r] * D));
 #pragma unroll
     for (int e = 0; e < 8; ++e) red[st][ch * 8 + e] = acc[e];
     __syncthreads();
@@ -240,6 +279,9 @@ __global__ __launch_bounds__(256) void k_segmean(const uint16_t* __restrict__ X,
 // ----------------------------------------------------------------------------
 // padded layout of one side
 // ----------------------------------------------------------------------------
+// One thread per padded slot (grid: slot tiles x heads); every slot and block
+// entry is written exactly once.  Each workgroup first scans the clusters'
+// block counts (C <= 1024, one per thread) for the first block of each.
 __global__ __launch_bounds__(kTok) void k_layout(const int32_t* __restrict__ sorted,
                                                  const int32_t* __restrict__ count,
                                                  const int32_t* __restrict__ cstart,
@@ -247,17 +289,10 @@ __global__ __launch_bounds__(kTok) void k_layout(const int32_t* __restrict__ sor
                                                  int32_t* __restrict__ blk_cluster,
                                                  int32_t* __restrict__ blk_count, int N, int C,
                                                  int block, int nbp) {
-    __shared__ int32_t bstart[kCmax];
-    __shared__ int32_t cst[kCmax];
+    __shared__ int32_t bstart[kCmax], nblk_s[kCmax], cst[kCmax], cnt[kCmax];
     __shared__ int32_t wsum[kTok / 64];
-    const int64_t bh = blockIdx.x;
+    const int64_t bh = blockIdx.y;
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-    const int64_t np = (int64_t)nbp * block;
-    for (int64_t p = tid; p < np; p += kTok) order[bh * np + p] = -1;
-    for (int j = tid; j < nbp; j += kTok) {
-        blk_cluster[bh * nbp + j] = -1;
-        blk_count[bh * nbp + j] = 0;
-    }
     const int n = tid < C ? count[bh * C + tid] : 0;
     const int nblk = (n + block - 1) / block;
     int32_t x = nblk;
@@ -267,30 +302,40 @@ __global__ __launch_bounds__(kTok) void k_layout(const int32_t* __restrict__ sor
         if (lane >= off) x += y;
     }
     if (lane == 63) wsum[wid] = x;
-    __syncthreads();                       // also orders the fills above before the writes below
+    __syncthreads();
     int32_t before = 0;
     for (int w = 0; w < wid; ++w) before += wsum[w];
     if (tid < C) {
         bstart[tid] = before + x - nblk;
+        nblk_s[tid] = nblk;
         cst[tid] = cstart[bh * C + tid];
+        cnt[tid] = n;
     }
     __syncthreads();
-    if (tid < C) {
-        for (int k = 0; k < nblk; ++k) {
-            blk_cluster[bh * nbp + bstart[tid] + k] = tid;
-            blk_count[bh * nbp + bstart[tid] + k] = n - k * block < block ? n - k * block : block;
-        }
+    const int64_t np = (int64_t)nbp * block;
+    const int64_t p = (int64_t)blockIdx.x * kTok + tid;
+    if (p >= np) return;
+    const int j = (int)(p / block);
+    // the cluster owning block j: the last c with bstart[c] <= j (an empty
+    // cluster shares its start with the next one, which comes later)
+    int lo = 0, hi = C - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (bstart[mid] <= j) lo = mid;
+        else hi = mid - 1;
     }
-    for (int r = tid; r < N; r += kTok) {
-        // the cluster of sorted position r: the last c with cst[c] <= r
-        int lo = 0, hi = C - 1;
-        while (lo < hi) {
-            const int mid = (lo + hi + 1) >> 1;
-            if (cst[mid] <= r) lo = mid;
-            else hi = mid - 1;
-        }
-        const int64_t p = (int64_t)bstart[lo] * block + (r - cst[lo]);
-        order[bh * np + p] = sorted[bh * N + r];
+    int tok = -1, bc = -1, bn = 0;
+    if (j < bstart[lo] + nblk_s[lo]) {
+        const int off = (int)(p - (int64_t)bstart[lo] * block);
+        if (off < cnt[lo]) tok = sorted[bh * N + cst[lo] + off];
+        bc = lo;
+        const int rest = cnt[lo] - (j - bstart[lo]) * block;
+        bn = rest < block ? rest : block;
+    }
+    order[bh * np + p] = tok;
+    if (p % block == 0) {
+        blk_cluster[bh * nbp + j] = bc;
+        blk_count[bh * nbp + j] = bn;
     }
 }
 
@@ -508,8 +553,10 @@ __global__ void k_block_comp(const float* __restrict__ k_cent, const float* __re
 // host side
 // ----------------------------------------------------------------------------
 struct ClusterWs {
-    size_t assign[2], sorted[2], hist, off, cstart[2], total;
+    size_t assign[2], sorted[2], hist, off, cstart[2], centT, bias, total;
 };
+
+inline int padded_c(int C) { return (C + kAsgIlp - 1) / kAsgIlp * kAsgIlp; }
 
 ClusterWs cluster_ws(const Geometry& g, int C) {
     ClusterWs w{};
@@ -522,6 +569,8 @@ ClusterWs cluster_ws(const Geometry& g, int C) {
     }
     w.hist = o; o = align_up(o + (size_t)g.BH() * ntiles * C * 4, 256);
     w.off = o; o = align_up(o + (size_t)g.BH() * ntiles * C * 4, 256);
+    w.centT = o; o = align_up(o + (size_t)g.BH() * g.d * padded_c(C) * 4, 256);
+    w.bias = o; o = align_up(o + (size_t)g.BH() * padded_c(C) * 4, 256);
     w.total = o;
     return w;
 }
@@ -561,8 +610,15 @@ template <int D>
 sa_status assign_side(const Geometry& g, int C, char* ws, const ClusterWs& w, int s,
                       const uint16_t* X, const float* cent, int kmeans, hipStream_t st) {
     int32_t* assign = reinterpret_cast<int32_t*>(ws + w.assign[s]);
+    float* centT = reinterpret_cast<float*>(ws + w.centT);
+    float* bias = reinterpret_cast<float*>(ws + w.bias);
+    const int Cp = padded_c(C);
+    hipLaunchKernelGGL((k_cent_prep<D>), dim3((unsigned)ceil_div((int64_t)D * Cp, 256), (unsigned)g.BH()),
+                       dim3(256), 0, st, cent, centT, bias, C, Cp, kmeans);
+    sa_status e = hip_check(hipGetLastError(), "k_cent_prep launch");
+    if (e != SA_OK) return e;
     hipLaunchKernelGGL((k_assign<D>), dim3((unsigned)ceil_div(g.N, kAsgThreads), (unsigned)g.BH()),
-                       dim3(kAsgThreads), 0, st, X, cent, assign, g.N, C, kmeans);
+                       dim3(kAsgThreads), 0, st, X, centT, bias, assign, g.N, Cp);
     return hip_check(hipGetLastError(), "k_assign launch");
 }
 
@@ -606,7 +662,8 @@ sa_status cluster_t(const Geometry& g, const sa_cluster_spec& cs, const uint16_t
     }
     const int nbp = padded_block_count(g, C);
     for (int s = 0; s < 2; ++s) {
-        hipLaunchKernelGGL(k_layout, dim3((unsigned)g.BH()), dim3(kTok), 0, st,
+        const unsigned tiles = (unsigned)ceil_div((int64_t)nbp * g.block, kTok);
+        hipLaunchKernelGGL(k_layout, dim3(tiles, (unsigned)g.BH()), dim3(kTok), 0, st,
                            reinterpret_cast<const int32_t*>(ws + w.sorted[s]),
                            s ? o.k_count : o.q_count,
                            reinterpret_cast<const int32_t*>(ws + w.cstart[s]),
