@@ -186,7 +186,8 @@ __device__ __forceinline__ void dma_tile(unsigned char* tile, const unsigned cha
 // One row = one (batch, head, query block): all its kept tiles, then (with
 // compensation) the centroid tiles, then the merge of the two key halves.
 template <int D, int BLK, bool COMP>
-__device__ __forceinline__ void process_row(const FwdArgs& a, int64_t row, unsigned char* smem) {
+__device__ __forceinline__ void process_row(const FwdArgs& a, int64_t row, unsigned char* smem,
+                                            bool var_cnt) {
     using C = Cfg<D, BLK>;
     using yes = std::true_type;
     using no = std::false_type;
@@ -197,6 +198,8 @@ __device__ __forceinline__ void process_row(const FwdArgs& a, int64_t row, unsig
     unsigned char* cw = smem + C::BASE;
     int16_t* list = reinterpret_cast<int16_t*>(smem + C::BASE + C::MAX_NB);  // kept blocks
     int16_t* lcnt = list + a.nb;                                       // their token counts
+    // COMP: key bias of a centroid of n tokens, log2(n) / c (-inf for n = 0)
+    const float* lut = reinterpret_cast<const float*>(lcnt + a.nb);
 
     const int i = (int)(row % a.nb);
     const int64_t bh = row / a.nb;
@@ -226,23 +229,25 @@ __device__ __forceinline__ void process_row(const FwdArgs& a, int64_t row, unsig
     const int nk = __builtin_amdgcn_readfirstlane(a.row_ptr[row + 1]) - beg;
     const int T = nk + (COMP ? a.ntc : 0);
     const int16_t* cnt_h = a.cnt + bh * a.nb;
+    // token count of block j: the caller's (var_cnt) or the fixed layout's
+    auto count_of = [&](int j) -> int {
+        return var_cnt ? (int)cnt_h[j] : (j == a.nb - 1 ? last_n : BLK);
+    };
     // the row's kept blocks (clamped into range) with their token counts and,
     // for compensation, the centroid weights
     if constexpr (COMP)
-        for (int j = tid; j < a.nb; j += C::NT) cw[j] = (unsigned char)cnt_h[j];
+        for (int j = tid; j < a.nb; j += C::NT) cw[j] = (unsigned char)count_of(j);
     for (int e = tid; e < nk; e += C::NT) {
         int j = a.col_idx[beg + e];
         j = j < 0 ? 0 : (j >= a.nb ? a.nb - 1 : j);
         list[e] = (int16_t)j;
-        lcnt[e] = cnt_h[j];
+        if (var_cnt) lcnt[e] = cnt_h[j];
     }
     __syncthreads();
     if constexpr (COMP) {
         for (int e = tid; e < nk; e += C::NT) cw[list[e]] = 0;
         __syncthreads();
     }
-    // block counts from the caller: centroid weights other than BLK and last_n
-    const bool var_cnt = COMP && __builtin_amdgcn_readfirstlane(a.sched[24]) != 0;
 
     // copies of tile u (kept block list[u], or centroid tile u - nk) into slot b
     auto issue_k = [&](int u, int b) {
@@ -276,8 +281,6 @@ __device__ __forceinline__ void process_row(const FwdArgs& a, int64_t row, unsig
     float m_run = -INFINITY, l_run = 0.f;
     f32x16 s[C::KTW];            // S^T of the next tile (matrix phase -> vector phase)
     bf16x8 pb[C::KTW][2];        // P^T of the current tile (vector phase -> matrix phase)
-    const float inv_c = 1.f / a.c;
-    const float lb_full = __log2f((float)BLK) * inv_c, lb_last = __log2f((float)last_n) * inv_c;
 
     // Matrix phase of step t: O^T += V_t^T P_t^T (PV) and S^T = K_{t+1} Q^T (S),
     // interleaved so that the accumulator chains alternate.  Operand reads run
@@ -341,7 +344,13 @@ __device__ __forceinline__ void process_row(const FwdArgs& a, int64_t row, unsig
     // raw scores (c > 0), and c s - m is one FMA.
     auto vector_phase = [&](int u) {
         const bool cent = COMP && u >= nk;
-        const int nval = cent ? BLK : __builtin_amdgcn_readfirstlane((int)lcnt[u]);
+        int nval = BLK;
+        if (!cent) {
+            if (var_cnt)
+                nval = __builtin_amdgcn_readfirstlane((int)lcnt[u]);
+            else if (last_n < BLK && __builtin_amdgcn_readfirstlane(list[u]) == a.nb - 1)
+                nval = last_n;
+        }
         if (cent || nval < BLK) {
             const int j0 = (u - nk) * BLK;
 #pragma unroll
@@ -354,11 +363,7 @@ __device__ __forceinline__ void process_row(const FwdArgs& a, int64_t row, unsig
                         float b;
                         if (cent) {
                             const int j = j0 + key;
-                            const int n = j < a.nb ? cw[j] : 0;
-                            if (var_cnt)
-                                b = n ? __log2f((float)n) * inv_c : -INFINITY;
-                            else
-                                b = n == 0 ? -INFINITY : (n == BLK ? lb_full : lb_last);
+                            b = lut[j < a.nb ? cw[j] : 0];
                         } else {
                             b = key < nval ? 0.f : -INFINITY;
                         }
@@ -491,6 +496,16 @@ __global__ __launch_bounds__(BLK * 4) __attribute__((amdgpu_waves_per_eu(2)))
 void k_bsattn_fwd(FwdArgs a) {
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     __shared__ int s_row;
+    // block token counts from the caller (else the fixed layout's)
+    const bool var_cnt = __builtin_amdgcn_readfirstlane(a.sched[24]) != 0;
+    if constexpr (COMP) {
+        // key bias of a centroid by its token count (log2 domain, divided by c)
+        using C = Cfg<D, BLK>;
+        float* lut = reinterpret_cast<float*>(smem + C::BASE + C::MAX_NB + 4 * a.nb);
+        const float inv_c = 1.f / a.c;
+        for (int n = threadIdx.x; n <= BLK; n += C::NT) lut[n] = n ? __log2f((float)n) * inv_c : -INFINITY;
+        __syncthreads();
+    }
     const int x0 = blockIdx.x % 8;
     for (int k = 0; k < 8; ++k) {
         const int x = (x0 + k) % 8;
@@ -504,7 +519,7 @@ void k_bsattn_fwd(FwdArgs a) {
             const int row = s_row;
             __syncthreads();
             if (row < 0) break;
-            process_row<D, BLK, COMP>(a, row, smem);
+            process_row<D, BLK, COMP>(a, row, smem, var_cnt);
         }
     }
 }
@@ -713,10 +728,10 @@ template <int D, int BLK, bool COMP>
 sa_status run_t(const FwdArgs& a, const Geometry& g, hipStream_t stream) {
     using C = Cfg<D, BLK>;
     sa_status st = SA_OK;
-    const size_t lds = C::BASE + C::MAX_NB + 4 * (size_t)g.nb;
+    const size_t lds = C::BASE + C::MAX_NB + 4 * (size_t)g.nb + (COMP ? 4 * (BLK + 1) : 0);
     static bool configured = false;
     if (!configured) {
-        const int most = C::BASE + C::MAX_NB + 4 * C::MAX_NB;
+        const int most = C::BASE + C::MAX_NB + 4 * C::MAX_NB + 4 * (BLK + 1);
         st = hip_check(hipFuncSetAttribute((const void*)k_bsattn_fwd<D, BLK, COMP>,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, most),
                        "k_bsattn_fwd shared memory");
