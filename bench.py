@@ -197,9 +197,6 @@ def main():
 
     Qd, Kd, Vd = dev(Q), dev(K), dev(V)
     if wl.cluster:
-        if args.refresh_every != 1:
-            log("[bench] --refresh-every applies to fixed blocks only")
-            sys.exit(2)
         return bench_clusters(args, wl, Q, K, V, Qd, Kd, Vd)
     pipe = BlockSparseAttention(sa.problem_for(wl), sa.spec_for(wl), hilbert=wl.hilbert,
                                 refresh_every=args.refresh_every)
@@ -295,21 +292,30 @@ def bench_clusters(args, wl, Q, K, V, Qd, Kd, Vd):
     import block_sparse_attention_hilbert_amd as sa
     from block_sparse_attention_hilbert_amd.pipeline import ClusteredAttention
 
-    pipe = ClusteredAttention(sa.problem_for(wl), sa.cluster_spec_for(wl), sa.spec_for(wl))
+    pipe = ClusteredAttention(sa.problem_for(wl), sa.cluster_spec_for(wl), sa.spec_for(wl),
+                              refresh_every=args.refresh_every)
     stream = torch.cuda.current_stream()
+    selected = []
 
     def step(ev):
+        reuse = pipe.reuses_next()
+        selected.append(not reuse)
         ev[0].record(stream)
-        pipe.run_cluster(Qd, Kd, Vd)
+        if not reuse:
+            pipe.run_cluster(Qd, Kd, Vd)
         ev[1].record(stream)
         pipe.run_gather(Qd, Kd, Vd)
-        pipe.run_select()
+        if reuse:
+            pipe.run_centroids()
+        else:
+            pipe.run_select()
         ev[2].record(stream)
         pipe.run_fwd_prepare()
         ev[3].record(stream)
         pipe.run_fwd_attention()
         ev[4].record(stream)
         pipe.run_scatter()
+        pipe.calls += 1
 
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)]
               for _ in range(max(args.steps, 1))]
@@ -358,7 +364,9 @@ def bench_clusters(args, wl, Q, K, V, Qd, Kd, Vd):
                    "token_density_kept": round(float((qcnt * kept).sum()) /
                                                (wl.B * wl.H * float(wl.N) ** 2), 4),
                    "padding_fraction": round(1.0 - wl.B * wl.H * wl.N / slots, 4),
-                   "compensation": wl.comp, "parallelism": "single GPU"},
+                   "compensation": wl.comp, "partition_refresh_every": args.refresh_every,
+                   "parallelism": "single GPU"},
+        "clusterings_timed": int(sum(selected[args.warmup:])),
         "ms_cluster": round(cl_ms, 4),
         "ms_gather_select": round(gs_ms, 4),
         "ms_select": round(sel_s * 1e3, 4),

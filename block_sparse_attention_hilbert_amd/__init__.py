@@ -45,7 +45,8 @@ EXPORTS = ("sparse_attn_workspace_size", "hilbert_perm_build", "hilbert_permute"
            "sparse_attn_fwd_prepare", "sparse_attn_fwd_run", "sparse_attn_centroids",
            "sparse_attn_fwd_prepare_counts", "sparse_attn_cluster_size", "sparse_attn_cluster",
            "sparse_attn_cluster_gather", "sparse_attn_cluster_scatter",
-           "sparse_attn_cluster_select", "sparse_attn_last_error")
+           "sparse_attn_cluster_select", "sparse_attn_cluster_centroids",
+           "sparse_attn_last_error")
 
 
 class SaProblem(ctypes.Structure):
@@ -103,6 +104,7 @@ def _load():
     lib.sparse_attn_cluster_scatter.argtypes = [P(SaProblem), P(SaClusterSpec)] + [vp] * 6
     lib.sparse_attn_cluster_select.argtypes = ([P(SaProblem), P(SaClusterSpec), P(SaSelectSpec)]
                                                + [vp] * 13 + [sz, vp])
+    lib.sparse_attn_cluster_centroids.argtypes = [P(SaProblem), P(SaClusterSpec)] + [vp] * 10
     for name in EXPORTS[:-1]:
         getattr(lib, name).restype = ctypes.c_int
     lib.sparse_attn_last_error.argtypes = []
@@ -460,6 +462,18 @@ def cluster_select(prob: Problem, cspec: ClusterSpec, spec: SelectSpec, cl: Clus
         _ptr(cl.k_cnt), _ptr(out.row_ptr), _ptr(out.col_idx), _ptr(out.scores),
         _ptr(out.k_mean), _ptr(out.v_sum), _ptr(workspace), ws_bytes, _stream(stream)))
     return out
+
+
+def cluster_centroids(prob: Problem, cspec: ClusterSpec, Kp: torch.Tensor, Vp: torch.Tensor,
+                      cl: Clusters, k_mean: torch.Tensor, v_sum: torch.Tensor,
+                      stream=None) -> None:
+    """sparse_attn_cluster_centroids: key / value means of the kept partition
+    from this call's K, V in the padded layout (into cl.k_cent, cl.v_cent) and
+    the per-block compensation statistics."""
+    _check(lib.sparse_attn_cluster_centroids(ctypes.byref(prob.c()), ctypes.byref(cspec.c()),
+                                             _ptr(Kp), _ptr(Vp), _ptr(cl.k_count), _ptr(cl.k_blk),
+                                             _ptr(cl.k_cnt), _ptr(cl.k_cent), _ptr(cl.v_cent),
+                                             _ptr(k_mean), _ptr(v_sum), _stream(stream)))
 
 
 def cluster_spec_for(wl) -> ClusterSpec:

@@ -277,6 +277,54 @@ __global__ __launch_bounds__(256) void k_segmean(const uint16_t* __restrict__ X,
 }
 
 // ----------------------------------------------------------------------------
+// cluster means from tensors already in the padded layout (a call that reuses
+// the partition): cluster c's tokens are the first count[c] rows of its
+// blocks, which start after the blocks of the clusters before it
+// ----------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void k_cmean_padded(const uint16_t* __restrict__ Xp,
+                                                      const int32_t* __restrict__ count,
+                                                      float* __restrict__ cent, int64_t np, int C,
+                                                      int block) {
+    constexpr int CH = D / 8;
+    constexpr int ST = 256 / CH;
+    __shared__ double red[ST][D];
+    __shared__ int32_t wpart[4];
+    const int c = blockIdx.x;
+    const int64_t bh = blockIdx.y;
+    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    const int32_t* cnt = count + bh * C;
+    int32_t part = 0;
+    for (int k = tid; k < c; k += 256) part += (cnt[k] + block - 1) / block;
+    for (int off = 32; off > 0; off >>= 1) part += __shfl_xor(part, off, 64);
+    if (lane == 0) wpart[wid] = part;
+    __syncthreads();
+    const int64_t first = (int64_t)(wpart[0] + wpart[1] + wpart[2] + wpart[3]) * block;
+    const int n = cnt[c];
+    if (n == 0) return;
+    const int ch = tid % CH, st = tid / CH;
+    const uint16_t* src = Xp + (bh * np + first) * D + ch * 8;
+    double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    for (int r = st; r < n; r += ST) {
+        const uint4 v = *reinterpret_cast<const uint4*>(src + (int64_t)r * D);
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            acc[2 * e] += (double)__uint_as_float(w[e] << 16);
+            acc[2 * e + 1] += (double)__uint_as_float(w[e] & 0xffff0000u);
+        }
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) red[st][ch * 8 + e] = acc[e];
+    __syncthreads();
+    if (tid < D) {
+        double s = 0.0;
+        for (int k = 0; k < ST; ++k) s += red[k][tid];
+        cent[(bh * C + c) * (int64_t)D + tid] = (float)(s / (double)n);
+    }
+}
+
+// ----------------------------------------------------------------------------
 // padded layout of one side
 // ----------------------------------------------------------------------------
 // One thread per padded slot (grid: slot tiles x heads); every slot and block
@@ -774,6 +822,32 @@ sa_status launch_cluster_select(const Geometry& g, const sa_cluster_spec& cs, co
         if ((e = hip_check(hipGetLastError(), "k_block_comp launch")) != SA_OK) return e;
     }
     return SA_OK;
+}
+
+sa_status launch_cluster_centroids(const Geometry& g, int C, const uint16_t* Kp,
+                                   const uint16_t* Vp, const int32_t* k_count,
+                                   const int32_t* k_blk, const int32_t* k_cnt, float* k_cent,
+                                   float* v_cent, float* k_mean, float* v_sum, hipStream_t st) {
+    const int nbp = padded_block_count(g, C);
+    const int64_t np = (int64_t)nbp * g.block;
+    const dim3 grid((unsigned)C, (unsigned)g.BH());
+    sa_status e;
+    for (int s = 0; s < 2; ++s) {
+        const uint16_t* X = s ? Vp : Kp;
+        float* out = s ? v_cent : k_cent;
+        if (g.d == 128)
+            hipLaunchKernelGGL((k_cmean_padded<128>), grid, dim3(256), 0, st, X, k_count, out, np, C, g.block);
+        else
+            hipLaunchKernelGGL((k_cmean_padded<64>), grid, dim3(256), 0, st, X, k_count, out, np, C, g.block);
+        if ((e = hip_check(hipGetLastError(), "k_cmean_padded launch")) != SA_OK) return e;
+    }
+    if (g.d == 128)
+        hipLaunchKernelGGL((k_block_comp<128>), dim3(nbp, (unsigned)g.BH()), dim3(128), 0, st,
+                           k_cent, v_cent, k_blk, k_cnt, k_mean, v_sum, nbp, C);
+    else
+        hipLaunchKernelGGL((k_block_comp<64>), dim3(nbp, (unsigned)g.BH()), dim3(64), 0, st,
+                           k_cent, v_cent, k_blk, k_cnt, k_mean, v_sum, nbp, C);
+    return hip_check(hipGetLastError(), "k_block_comp launch");
 }
 
 }  // namespace sa

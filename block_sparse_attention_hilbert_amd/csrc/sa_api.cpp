@@ -505,4 +505,23 @@ SA_API sa_status sparse_attn_cluster_select(const sa_problem* prob, const sa_clu
     return launch_cluster_select(g, *cspec, a, budget, (char*)workspace, (hipStream_t)stream);
 }
 
+SA_API sa_status sparse_attn_cluster_centroids(const sa_problem* prob, const sa_cluster_spec* cspec,
+                                               const void* Kp, const void* Vp,
+                                               const int32_t* k_count, const int32_t* k_blk,
+                                               const int32_t* k_cnt, float* k_cent, float* v_cent,
+                                               float* k_mean, float* v_sum, void* stream) {
+    clear_error();
+    Geometry g;
+    sa_status st = check_problem(prob, &g);
+    if (st != SA_OK) return st;
+    if ((st = check_cluster(g, cspec)) != SA_OK) return st;
+    if (!Kp || !Vp || !k_count || !k_blk || !k_cnt || !k_cent || !v_cent || !k_mean || !v_sum)
+        return fail(SA_ERR_INVALID_ARG, "every argument is required");
+    if (!aligned16(Kp) || !aligned16(Vp))
+        return fail(SA_ERR_INVALID_ARG, "Kp and Vp must be 16-byte aligned");
+    return launch_cluster_centroids(g, cspec->n_clusters, (const uint16_t*)Kp, (const uint16_t*)Vp,
+                                    k_count, k_blk, k_cnt, k_cent, v_cent, k_mean, v_sum,
+                                    (hipStream_t)stream);
+}
+
 SA_API const char* sparse_attn_last_error(void) { return g_last_error.c_str(); }

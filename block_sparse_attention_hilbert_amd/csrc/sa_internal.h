@@ -101,6 +101,12 @@ sa_status launch_cluster_scatter(const Geometry& g, int C, const int32_t* order,
                                  float* lse_dst, hipStream_t stream);
 sa_status launch_cluster_select(const Geometry& g, const sa_cluster_spec& cs, const ClusterSel& a,
                                 const int64_t* budget_host, char* ws, hipStream_t stream);
+// Key and value means of the clusters from K, V in the padded layout, and the
+// per-block compensation statistics (a call that reuses the partition).
+sa_status launch_cluster_centroids(const Geometry& g, int C, const uint16_t* Kp,
+                                   const uint16_t* Vp, const int32_t* k_count,
+                                   const int32_t* k_blk, const int32_t* k_cnt, float* k_cent,
+                                   float* v_cent, float* k_mean, float* v_sum, hipStream_t stream);
 
 // ----------------------------------------------------------------------------
 // error-aware routing keys (k_route.hip)

@@ -19,6 +19,10 @@ its own K and V (sparse_attn_centroids); only the keep decision is reused.
 section 2A: k-means clusters made contiguous by a permutation): cluster Q and
 K, gather them (and V) into the padded clustered layout, select over
 clusters, attend with per-block token counts, scatter O back to token order.
+With ``refresh_every = r`` it clusters and selects on calls 0, r, 2r, ...
+(SVOO keeps its partition for ~20 diffusion steps); the calls in between keep
+the partition and the keep lists, gather their own Q, K, V into the layout and,
+with compensation, take the cluster centroids from their own K and V.
 """
 from __future__ import annotations
 
@@ -28,7 +32,8 @@ import numpy as np
 import torch
 
 from . import (Clusters, ClusterSpec, Problem, Selection, SelectSpec, alloc_workspace,
-               centroids, cluster, cluster_gather, cluster_scatter, cluster_select,
+               centroids, cluster, cluster_centroids, cluster_gather, cluster_scatter,
+               cluster_select,
                cluster_size, fwd, fwd_prepare, fwd_prepare_counts, fwd_run,
                hilbert_perm_build, hilbert_permute, hilbert_unpermute, padded_problem, select,
                workspace_size)
@@ -159,8 +164,13 @@ class ClusteredAttention:
     """
 
     def __init__(self, prob: Problem, cspec: ClusterSpec, spec: SelectSpec, device="cuda",
-                 want_scores: bool = False, want_lse: bool = False):
+                 want_scores: bool = False, want_lse: bool = False, refresh_every: int = 1):
+        if refresh_every < 1:
+            raise ValueError("refresh_every must be >= 1")
         self.prob, self.cspec, self.spec = prob, cspec, spec
+        self.refresh_every = int(refresh_every)
+        self.calls = 0
+        self.have_partition = False
         self.device = torch.device(device)
         self.nbp, ws_c, ws_s = cluster_size(prob, cspec)
         self.pprob = padded_problem(prob, self.nbp)
@@ -195,7 +205,18 @@ class ClusteredAttention:
     def run_cluster(self, Q, K, V):
         cluster(self.prob, self.cspec, Q, K, V if self.spec.want_comp else None, out=self.cl,
                 workspace=self.ws_cluster)
+        self.have_partition = True
         return self.cl
+
+    def reuses_next(self) -> bool:
+        """Whether the next call keeps the current partition and selection."""
+        return self.have_partition and self.calls % self.refresh_every != 0
+
+    def run_centroids(self):
+        """Compensation statistics of this call's (gathered) K, V for a kept partition."""
+        if self.spec.want_comp:
+            cluster_centroids(self.prob, self.cspec, self.Kp, self.Vp, self.cl, self.sel.k_mean,
+                              self.sel.v_sum)
 
     def run_gather(self, Q, K, V):
         cluster_gather(self.prob, self.cspec, self.cl.q_order, Q, self.Qp)
@@ -220,12 +241,23 @@ class ClusteredAttention:
                         self.lse)
         return self.O
 
-    def __call__(self, Q, K, V) -> torch.Tensor:
-        self.run_cluster(Q, K, V)
+    def __call__(self, Q, K, V, reuse: Optional[bool] = None) -> torch.Tensor:
+        """One call.  ``reuse``: keep the partition and selection (True), form
+        them anew (False) or follow the refresh policy (None)."""
+        if reuse is None:
+            reuse = self.reuses_next()
+        if reuse and not self.have_partition:
+            raise RuntimeError("no partition to reuse: the first call must cluster")
+        if not reuse:
+            self.run_cluster(Q, K, V)
         self.run_gather(Q, K, V)
-        self.run_select()
+        if reuse:
+            self.run_centroids()
+        else:
+            self.run_select()
         self.run_fwd_prepare()
         self.run_fwd_attention()
+        self.calls += 1
         return self.run_scatter()
 
     def kept_tokens(self) -> torch.Tensor:

@@ -366,6 +366,24 @@ sa_status sparse_attn_cluster_select(const sa_problem* prob, const sa_cluster_sp
                                      void* workspace, size_t ws_bytes, void* stream);
 
 /*
+ * sparse_attn_cluster_centroids: for a call that reuses a partition (and its
+ * selection) made on an earlier call [SVOO 2B: the clustering is kept for
+ * several diffusion steps]: the key and value means of every key cluster from
+ * this call's K and V, already gathered into the padded layout (Kp, Vp: device
+ * bf16 [B,H,Np,d], padding rows zero, e.g. by sparse_attn_cluster_gather with
+ * k_order), written to k_cent, v_cent (fp32 [B*H, C, d]; clusters with no
+ * token are left untouched), and the per-block compensation statistics k_mean,
+ * v_sum (fp32 [B*H, nbp, d]) as sparse_attn_cluster_select writes them.
+ * k_count, k_blk, k_cnt: as written by sparse_attn_cluster.  Means are fp32
+ * roundings of exact sums, so unchanged inputs reproduce sparse_attn_cluster's
+ * centroids bit for bit.
+ */
+sa_status sparse_attn_cluster_centroids(const sa_problem* prob, const sa_cluster_spec* cspec,
+                                        const void* Kp, const void* Vp, const int32_t* k_count,
+                                        const int32_t* k_blk, const int32_t* k_cnt, float* k_cent,
+                                        float* v_cent, float* k_mean, float* v_sum, void* stream);
+
+/*
  * sparse_attn_fwd_prepare with token counts per KV block: kv_count device
  * int32 [B*H, nb] in [0, block]; keys past the count of a block take no part
  * (masked in kept blocks; weight n_j = the count for compensation, a block

@@ -269,3 +269,19 @@ def test_cluster_calls_reject_before_any_launch():
     assert prep(ctypes.byref(p), fake, fake, None, None, None, fake, 1 << 30, None) == \
         sa.SA_ERR_INVALID_ARG
     assert b"kv_count" in sa.lib.sparse_attn_last_error()
+
+
+def test_cluster_centroids_reject_before_any_launch():
+    p = _prob().c()
+    cs = sa.ClusterSpec("kmeans", 4, 2).c()
+    vp = ctypes.c_void_p
+    fake, odd = vp(1 << 20), vp((1 << 20) + 8)
+    f = sa.lib.sparse_attn_cluster_centroids
+    assert f(ctypes.byref(p), ctypes.byref(cs), fake, fake, fake, fake, fake, fake, fake, fake,
+             None, None) == sa.SA_ERR_INVALID_ARG
+    assert f(ctypes.byref(p), ctypes.byref(cs), odd, fake, fake, fake, fake, fake, fake, fake,
+             fake, None) == sa.SA_ERR_INVALID_ARG
+    assert b"aligned" in sa.lib.sparse_attn_last_error()
+    bad = sa.ClusterSpec("kmeans", 0, 2).c()
+    assert f(ctypes.byref(p), ctypes.byref(bad), fake, fake, fake, fake, fake, fake, fake, fake,
+             fake, None) == sa.SA_ERR_INVALID_ARG

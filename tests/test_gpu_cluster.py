@@ -225,3 +225,57 @@ def test_counts_prepare_matches_fixed_layout():
     sa.fwd_run(prob, Q, K, sel.row_ptr, sel.col_idx, True, O=O2, workspace=ws)
     torch.cuda.synchronize()
     assert torch.equal(O1.view(torch.int16), O2.view(torch.int16))
+
+
+@pytest.mark.parametrize("name", ["kmeans_topk_comp_d128_b64", "cocluster_mass_d128_b128"])
+def test_partition_reuse_across_steps(name):
+    """Reuse of the clustering (SVOO 2B: kept for several diffusion steps): step
+    0 clusters and selects, steps 1 and 2 keep its partition and keep lists.
+    Every step must equal the oracle's cluster attention over step 0's
+    partition and keep with that step's own Q, K, V (with compensation: the
+    centroids of that step's K and V), and the recomputed centroids must be
+    the exact means of the step's keys and values per kept cluster."""
+    wl = SMALL[name].replace(name=name)
+    log(f"[cluster-reuse] {name}")
+    steps = W.make_step_qkv(wl, 3, drift=0.2)
+    pipe = _pipe(wl)
+    pipe.refresh_every = 3
+    ref0 = []
+    moved = 0
+    for s, (Q, K, V) in enumerate(steps):
+        assert pipe.reuses_next() == (s > 0)
+        O = pipe(to_dev(Q), to_dev(K), to_dev(V))
+        torch.cuda.synchronize()
+        Og = from_dev(O)
+        lse_g = pipe.lse.cpu().numpy()
+        errs, lerrs = [], []
+        for bh in range(wl.B * wl.H):
+            b, h = divmod(bh, wl.H)
+            q, k, v = (oracle.bf16_to_f64(x[b, h]) for x in (Q, K, V))
+            if s == 0:
+                ref0.append(OC.cluster_workload_head(wl, q, k))
+            r = ref0[bh]
+            assert np.array_equal(pipe.cl.k_order[bh].cpu().numpy(), r["k_order"])
+            assert np.array_equal(pipe.cl.q_order[bh].cpu().numpy(), r["q_order"])
+            if s > 0:
+                fresh = OC.cluster_workload_head(wl, q, k)
+                moved += int(np.sum(fresh["ak"] != r["ak"]) + np.sum(fresh["aq"] != r["aq"]))
+            if wl.comp:
+                live = r["nk"] > 0
+                kc = OC.cluster_means(k, r["ak"], wl.n_clusters)
+                vc = OC.cluster_means(v, r["ak"], wl.n_clusters)
+                assert np.array_equal(pipe.cl.k_cent[bh].cpu().numpy()[live].view(np.uint32),
+                                      kc[live].view(np.uint32))
+                assert np.array_equal(pipe.cl.v_cent[bh].cpu().numpy()[live].view(np.uint32),
+                                      vc[live].view(np.uint32))
+            Oref, lref = OC.cluster_attention_head(q, k, v, r["aq"], r["ak"], r["keepC"],
+                                                   wl.scale, comp=wl.comp)
+            errs.append(np.abs(oracle.bf16_to_f64(Og[b, h]) - Oref).ravel())
+            lerrs.append(np.abs(lse_g[b, h].astype(np.float64) - lref))
+        e = np.concatenate(errs)
+        le = np.concatenate(lerrs)
+        log(f"[cluster-reuse] {name}: step {s}: max {e.max():.2e} mean {e.mean():.2e} "
+            f"lse {le.max():.2e}")
+        assert e.max() <= ATOL_MAX and e.mean() <= ATOL_MEAN and le.max() <= LSE_ATOL
+    log(f"[cluster-reuse] {name}: tokens a fresh clustering would move: {moved}")
+    assert moved > 0
