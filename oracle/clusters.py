@@ -132,15 +132,18 @@ def padded_blocks(N: int, block: int, C: int) -> int:
     return -(-N // block) + C
 
 
-def cluster_layout(assign: np.ndarray, C: int, block: int):
+def cluster_layout(assign: np.ndarray, C: int, block: int, nbp: int = None):
     """Padded layout of one side of one head.
 
     Returns (order, blk_cluster, blk_count): order[p] = token at slot p or -1
     (padding), for nbp * block slots; blk_cluster[j] = cluster of block j or -1;
-    blk_count[j] = tokens (not padding) in block j.
+    blk_count[j] = tokens (not padding) in block j.  ``nbp`` defaults to the
+    bound ceil(N / block) + C; clusters of at most ``block`` tokens each fit in
+    nbp = C blocks.
     """
     N = assign.size
-    nbp = padded_blocks(N, block, C)
+    if nbp is None:
+        nbp = padded_blocks(N, block, C)
     n = np.bincount(assign, minlength=C)
     nblk = -(-n // block)
     order = np.full(nbp * block, -1, dtype=np.int64)
