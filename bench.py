@@ -122,6 +122,7 @@ def cpu_baseline_clusters(wl, Q, K, V, budget_s: float = 15.0):
     by one until the budget is spent.  Kept-token TFLOP/s of the sample."""
     import oracle
     from oracle import clusters as OC
+    from oracle import tiles as OT
     from threadpoolctl import threadpool_info
 
     t0 = time.perf_counter()
@@ -129,7 +130,10 @@ def cpu_baseline_clusters(wl, Q, K, V, budget_s: float = 15.0):
     heads = done = 0
     for h in range(wl.H):
         q, k, v = (oracle.bf16_to_f64(x[0, h]) for x in (Q, K, V))
-        ref = OC.cluster_workload_head(wl, q, k)
+        if wl.cluster == "tiles":
+            ref = OT.tiles_workload_head(wl, q, k)
+        else:
+            ref = OC.cluster_workload_head(wl, q, k)
         kept_tok = ref["keepC"].astype(np.float64) @ ref["nk"].astype(np.float64)
         for a in range(wl.n_clusters):
             if ref["nq"][a] == 0:
@@ -147,7 +151,7 @@ def cpu_baseline_clusters(wl, Q, K, V, budget_s: float = 15.0):
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
             "kind": "oracle",
-            "sample": f"{heads} of {wl.H} heads of batch 0: clustering + selection + float64 "
+            "sample": f"{heads} of {wl.H} heads of batch 0: block formation + selection + float64 "
                       f"attention of {done} query clusters ({dt:.1f} s wall)"}
 
 
@@ -366,6 +370,8 @@ def bench_clusters(args, wl, Q, K, V, Qd, Kd, Vd):
                    "padding_fraction": round(1.0 - wl.B * wl.H * wl.N / slots, 4),
                    "compensation": wl.comp, "partition_refresh_every": args.refresh_every,
                    "parallelism": "single GPU"},
+        "tile_shape_per_head": (None if pipe.shape_idx is None else
+                                [list(wl.tile_shapes[i]) for i in pipe.shape_idx.cpu().tolist()]),
         "clusterings_timed": int(sum(selected[args.warmup:])),
         "ms_cluster": round(cl_ms, 4),
         "ms_gather_select": round(gs_ms, 4),

@@ -13,8 +13,10 @@ stream.  The functions mirror the C ABI in ``include/sparse_attn.h``:
   (:func:`fwd_prepare_counts`: with a token count per KV block)
 * :func:`centroids` -- compensation statistics alone (mask reuse)
 * :func:`cluster_size`, :func:`cluster`, :func:`cluster_gather`,
-  :func:`cluster_scatter`, :func:`cluster_select` -- data-dependent block
-  formation (co-clustering / k-means) and selection over clusters
+  :func:`cluster_scatter`, :func:`cluster_select`, :func:`cluster_centroids` --
+  data-dependent block formation (co-clustering / k-means / tiles) and
+  selection over clusters
+* :func:`sics` -- per-head choice of a tile shape (SICS scheme generation)
 * :func:`workspace_size`
 
 If the shared library is missing the import fails loudly; there is no
@@ -37,15 +39,16 @@ LIB_PATH = os.path.join(_PKG, "libsparse_attn.so")
 SA_OK, SA_ERR_INVALID_ARG, SA_ERR_UNSUPPORTED, SA_ERR_WORKSPACE, SA_ERR_HIP = range(5)
 SA_RULE_NONE, SA_RULE_TOPK, SA_RULE_MASS, SA_RULE_ERR = range(4)
 RULES = {"none": SA_RULE_NONE, "topk": SA_RULE_TOPK, "mass": SA_RULE_MASS, "err": SA_RULE_ERR}
-SA_CLUSTER_COCLUSTER, SA_CLUSTER_KMEANS = 1, 2
-CLUSTER_MODES = {"cocluster": SA_CLUSTER_COCLUSTER, "kmeans": SA_CLUSTER_KMEANS}
+SA_CLUSTER_COCLUSTER, SA_CLUSTER_KMEANS, SA_CLUSTER_TILES = 1, 2, 3
+CLUSTER_MODES = {"cocluster": SA_CLUSTER_COCLUSTER, "kmeans": SA_CLUSTER_KMEANS,
+                 "tiles": SA_CLUSTER_TILES}
 
 EXPORTS = ("sparse_attn_workspace_size", "hilbert_perm_build", "hilbert_permute",
            "hilbert_unpermute", "sparse_attn_select", "sparse_attn_fwd",
            "sparse_attn_fwd_prepare", "sparse_attn_fwd_run", "sparse_attn_centroids",
            "sparse_attn_fwd_prepare_counts", "sparse_attn_cluster_size", "sparse_attn_cluster",
            "sparse_attn_cluster_gather", "sparse_attn_cluster_scatter",
-           "sparse_attn_cluster_select", "sparse_attn_cluster_centroids",
+           "sparse_attn_cluster_select", "sparse_attn_cluster_centroids", "sparse_attn_sics",
            "sparse_attn_last_error")
 
 
@@ -64,9 +67,14 @@ class SaSelectSpec(ctypes.Structure):
                 ("anchor_offset", ctypes.c_int64), ("want_comp", ctypes.c_int32)]
 
 
+class SaTileShape(ctypes.Structure):
+    _fields_ = [("t", ctypes.c_int32), ("y", ctypes.c_int32), ("x", ctypes.c_int32)]
+
+
 class SaClusterSpec(ctypes.Structure):
     _fields_ = [("mode", ctypes.c_int32), ("n_clusters", ctypes.c_int32),
-                ("iters", ctypes.c_int32)]
+                ("iters", ctypes.c_int32), ("n_shapes", ctypes.c_int32),
+                ("shapes", ctypes.POINTER(SaTileShape)), ("shape_idx", ctypes.c_void_p)]
 
 
 class SparseAttnError(RuntimeError):
@@ -105,6 +113,7 @@ def _load():
     lib.sparse_attn_cluster_select.argtypes = ([P(SaProblem), P(SaClusterSpec), P(SaSelectSpec)]
                                                + [vp] * 13 + [sz, vp])
     lib.sparse_attn_cluster_centroids.argtypes = [P(SaProblem), P(SaClusterSpec)] + [vp] * 10
+    lib.sparse_attn_sics.argtypes = [P(SaProblem), P(SaClusterSpec), vp, vp, vp, vp, vp, sz, vp]
     for name in EXPORTS[:-1]:
         getattr(lib, name).restype = ctypes.c_int
     lib.sparse_attn_last_error.argtypes = []
@@ -343,12 +352,21 @@ def fwd_prepare_counts(prob: Problem, V: torch.Tensor, row_ptr: torch.Tensor,
 
 @dataclass
 class ClusterSpec:
-    mode: str = "kmeans"          # "cocluster" | "kmeans"
-    n_clusters: int = 64
+    mode: str = "kmeans"          # "cocluster" | "kmeans" | "tiles"
+    n_clusters: int = 64          # tiles: the menu's largest tile count
     iters: int = 3
+    shapes: Optional[Sequence] = None          # tiles: menu of (t, y, x)
+    shape_idx: Optional[torch.Tensor] = None   # tiles: device int32 [B*H]
 
     def c(self) -> SaClusterSpec:
-        return SaClusterSpec(CLUSTER_MODES[self.mode], self.n_clusters, self.iters)
+        n, sp = 0, None
+        if self.shapes:
+            arr = (SaTileShape * len(self.shapes))(*[SaTileShape(*map(int, s)) for s in self.shapes])
+            self._shape_arr = arr                  # lives as long as the spec
+            sp = ctypes.cast(arr, ctypes.POINTER(SaTileShape))
+            n = len(self.shapes)
+        return SaClusterSpec(CLUSTER_MODES[self.mode], self.n_clusters, self.iters, n, sp,
+                             None if self.shape_idx is None else self.shape_idx.data_ptr())
 
 
 def cluster_size(prob: Problem, cspec: ClusterSpec):
@@ -476,6 +494,24 @@ def cluster_centroids(prob: Problem, cspec: ClusterSpec, Kp: torch.Tensor, Vp: t
                                              _ptr(k_mean), _ptr(v_sum), _stream(stream)))
 
 
+def sics(prob: Problem, cspec: ClusterSpec, Q: torch.Tensor, K: torch.Tensor,
+         shape_idx: torch.Tensor, scores: Optional[torch.Tensor] = None, *,
+         workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """sparse_attn_sics: per (b, h) the tile shape of the menu with the most
+    coherent tiles (mean intra-tile cosine of Q and K) into shape_idx (device
+    int32 [B*H]); scores (device fp64 [B*H, n_shapes]) if given."""
+    if workspace is None:
+        workspace = alloc_workspace(cluster_size(prob, cspec)[1], Q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.sparse_attn_sics(ctypes.byref(prob.c()), ctypes.byref(cspec.c()), _ptr(Q), _ptr(K),
+                                _ptr(scores), _ptr(shape_idx), _ptr(workspace), ws_bytes,
+                                _stream(stream)))
+    return shape_idx
+
+
 def cluster_spec_for(wl) -> ClusterSpec:
-    """Cluster spec of a workload description (cluster, n_clusters, cluster_iters)."""
+    """Cluster spec of a workload description (cluster, n_clusters, cluster_iters,
+    tile_shapes)."""
+    if wl.cluster == "tiles":
+        return ClusterSpec("tiles", wl.n_clusters, 0, shapes=[tuple(s) for s in wl.tile_shapes])
     return ClusterSpec(wl.cluster, wl.n_clusters, wl.cluster_iters)

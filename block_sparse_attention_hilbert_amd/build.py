@@ -18,7 +18,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libsparse_attn.so")
 SOURCES = ["sa_api.cpp", "hilbert.cpp", "k_select.hip", "k_attn.hip", "k_permute.hip", "k_route.hip",
-           "k_cluster.hip"]
+           "k_cluster.hip", "k_tiles.hip"]
 ARCH = "gfx950"
 
 

@@ -229,7 +229,8 @@ __global__ __launch_bounds__(256) void k_segmean(const uint16_t* __restrict__ X,
                                                  const int32_t* __restrict__ sorted,
                                                  const int32_t* __restrict__ count,
                                                  const int32_t* __restrict__ cstart,
-                                                 float* __restrict__ cent, int N, int C) {
+                                                 float* __restrict__ cent, int N, int C,
+                                                 int zero_empty) {
     constexpr int CH = D / 8;                 // 16-byte chunks per row
     constexpr int ST = 256 / CH;              // token streams
     __shared__ double red[ST][D];
@@ -237,7 +238,12 @@ __global__ __launch_bounds__(256) void k_segmean(const uint16_t* __restrict__ X,
     const int64_t bh = blockIdx.y;
     const int tid = threadIdx.x;
     const int n = count[bh * C + c];
-    if (n == 0) return;
+    if (n == 0) {
+        // an empty cluster keeps its previous centroid, or (no previous one:
+        // an empty tile) gets zeros
+        if (zero_empty && tid < D) cent[(bh * C + c) * (int64_t)D + tid] = 0.f;
+        return;
+    }
     const int s0 = cstart[bh * C + c];
     const int ch = tid % CH, st = tid / CH;
     const int32_t* srt = sorted + bh * N + s0;
@@ -526,21 +532,25 @@ __global__ void k_set_budget(int64_t* __restrict__ dst, BudgetChunk c, int n) {
     if ((int)threadIdx.x < n) dst[threadIdx.x] = c.v[threadIdx.x];
 }
 
-// blocks kept by every row of the padded layout
-__global__ void k_crow_count(const uint8_t* __restrict__ keep, const int32_t* __restrict__ nk,
-                             const int32_t* __restrict__ q_blk, int32_t* __restrict__ counts,
-                             int64_t rows, int nbp, int C, int block) {
-    const int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+// blocks kept by every row of the padded layout (one wave per row)
+__global__ __launch_bounds__(256) void k_crow_count(const uint8_t* __restrict__ keep,
+                                                    const int32_t* __restrict__ nk,
+                                                    const int32_t* __restrict__ q_blk,
+                                                    int32_t* __restrict__ counts, int64_t rows,
+                                                    int nbp, int C, int block) {
+    const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
     if (r >= rows) return;
     const int64_t bh = r / nbp;
     const int cq = q_blk[r];
     int32_t n = 0;
     if (cq >= 0) {
         const uint8_t* kr = keep + (bh * C + cq) * C;
-        for (int c = 0; c < C; ++c)
+        for (int c = lane; c < C; c += 64)
             if (kr[c]) n += (nk[bh * C + c] + block - 1) / block;
     }
-    counts[r] = n;
+    for (int off = 32; off > 0; off >>= 1) n += __shfl_xor(n, off, 64);
+    if (lane == 0) counts[r] = n;
 }
 
 // one wave per row: the blocks of the kept key clusters, ascending
@@ -625,16 +635,18 @@ ClusterWs cluster_ws(const Geometry& g, int C) {
 
 template <int D>
 sa_status segmean(const Geometry& g, int C, const uint16_t* X, const int32_t* sorted,
-                  const int32_t* count, const int32_t* cstart, float* cent, hipStream_t st) {
+                  const int32_t* count, const int32_t* cstart, float* cent, hipStream_t st,
+                  int zero_empty = 0) {
     hipLaunchKernelGGL((k_segmean<D>), dim3(C, (unsigned)g.BH()), dim3(256), 0, st, X, sorted,
-                       count, cstart, cent, g.N, C);
+                       count, cstart, cent, g.N, C, zero_empty);
     return hip_check(hipGetLastError(), "k_segmean launch");
 }
 
 // sorts side s by its assignment and refreshes its centroids
 template <int D>
 sa_status sort_and_mean(const Geometry& g, int C, char* ws, const ClusterWs& w, int s,
-                        const uint16_t* X, int32_t* count, float* cent, hipStream_t st) {
+                        const uint16_t* X, int32_t* count, float* cent, hipStream_t st,
+                        int zero_empty = 0) {
     const int ntiles = (int)ceil_div(g.N, kTok);
     const int32_t* assign = reinterpret_cast<const int32_t*>(ws + w.assign[s]);
     int32_t* sorted = reinterpret_cast<int32_t*>(ws + w.sorted[s]);
@@ -651,7 +663,7 @@ sa_status sort_and_mean(const Geometry& g, int C, char* ws, const ClusterWs& w, 
     hipLaunchKernelGGL(k_sort_scatter, dim3(ntiles, (unsigned)g.BH()), dim3(kTok), 0, st, assign,
                        off, sorted, g.N, C, ntiles);
     if ((e = hip_check(hipGetLastError(), "k_sort_scatter launch")) != SA_OK) return e;
-    return segmean<D>(g, C, X, sorted, count, cstart, cent, st);
+    return segmean<D>(g, C, X, sorted, count, cstart, cent, st, zero_empty);
 }
 
 template <int D>
@@ -676,8 +688,19 @@ sa_status cluster_t(const Geometry& g, const sa_cluster_spec& cs, const uint16_t
     const int C = cs.n_clusters;
     const ClusterWs w = cluster_ws(g, C);
     sa_status e;
+    if (cs.mode == SA_CLUSTER_TILES) {
+        // the partition is geometric: the tiles of each head's chosen shape,
+        // the same for queries and keys
+        for (int s = 0; s < 2; ++s) {
+            if ((e = launch_tile_assign(g, cs, reinterpret_cast<int32_t*>(ws + w.assign[s]), st)) != SA_OK)
+                return e;
+            if ((e = sort_and_mean<D>(g, C, ws, w, s, s ? K : Q, s ? o.k_count : o.q_count,
+                                      s ? o.k_cent : o.q_cent, st, 1)) != SA_OK)
+                return e;
+        }
+    }
     // initial partition of both sides and its centroids
-    for (int s = 0; s < 2; ++s) {
+    for (int s = 0; s < 2 && cs.mode != SA_CLUSTER_TILES; ++s) {
         hipLaunchKernelGGL(k_chunk_assign, dim3((unsigned)ceil_div(g.N, 256), (unsigned)g.BH()),
                            dim3(256), 0, st, reinterpret_cast<int32_t*>(ws + w.assign[s]), g.N, C);
         if ((e = hip_check(hipGetLastError(), "k_chunk_assign launch")) != SA_OK) return e;
@@ -685,7 +708,7 @@ sa_status cluster_t(const Geometry& g, const sa_cluster_spec& cs, const uint16_t
                                   s ? o.k_cent : o.q_cent, st)) != SA_OK)
             return e;
     }
-    for (int it = 0; it < cs.iters; ++it) {
+    for (int it = 0; it < (cs.mode == SA_CLUSTER_TILES ? 0 : cs.iters); ++it) {
         if (cs.mode == SA_CLUSTER_COCLUSTER) {
             // keys by affinity to the query centroids, then queries by affinity
             // to the refreshed key centroids
@@ -705,10 +728,11 @@ sa_status cluster_t(const Geometry& g, const sa_cluster_spec& cs, const uint16_t
     }
     if (o.v_cent) {
         if ((e = segmean<D>(g, C, V, reinterpret_cast<const int32_t*>(ws + w.sorted[1]), o.k_count,
-                            reinterpret_cast<const int32_t*>(ws + w.cstart[1]), o.v_cent, st)) != SA_OK)
+                            reinterpret_cast<const int32_t*>(ws + w.cstart[1]), o.v_cent, st,
+                            cs.mode == SA_CLUSTER_TILES)) != SA_OK)
             return e;
     }
-    const int nbp = padded_block_count(g, C);
+    const int nbp = padded_block_count(g, cs);
     for (int s = 0; s < 2; ++s) {
         const unsigned tiles = (unsigned)ceil_div((int64_t)nbp * g.block, kTok);
         hipLaunchKernelGGL(k_layout, dim3(tiles, (unsigned)g.BH()), dim3(kTok), 0, st,
@@ -724,9 +748,17 @@ sa_status cluster_t(const Geometry& g, const sa_cluster_spec& cs, const uint16_t
 
 }  // namespace
 
-int padded_block_count(const Geometry& g, int C) { return (int)ceil_div(g.N, g.block) + C; }
+int padded_block_count(const Geometry& g, const sa_cluster_spec& cs) {
+    return cs.mode == SA_CLUSTER_TILES ? cs.n_clusters
+                                       : (int)ceil_div(g.N, g.block) + cs.n_clusters;
+}
 
-size_t cluster_workspace_bytes(const Geometry& g, int C) { return cluster_ws(g, C).total; }
+size_t cluster_workspace_bytes(const Geometry& g, const sa_cluster_spec& cs) {
+    const size_t a = cluster_ws(g, cs.n_clusters).total;
+    if (cs.mode != SA_CLUSTER_TILES) return a;
+    const size_t b = sics_workspace_bytes(g, cs);     // sparse_attn_sics shares the buffer
+    return a > b ? a : b;
+}
 
 sa_status launch_cluster(const Geometry& g, const sa_cluster_spec& cs, const uint16_t* Q,
                          const uint16_t* K, const uint16_t* V, const ClusterOut& o, char* ws,
@@ -735,9 +767,9 @@ sa_status launch_cluster(const Geometry& g, const sa_cluster_spec& cs, const uin
                       : cluster_t<64>(g, cs, Q, K, V, o, ws, st);
 }
 
-sa_status launch_cluster_gather(const Geometry& g, int C, const int32_t* order, const uint16_t* src,
-                                uint16_t* dst, hipStream_t st) {
-    const int64_t np = (int64_t)padded_block_count(g, C) * g.block;
+sa_status launch_cluster_gather(const Geometry& g, const sa_cluster_spec& cs, const int32_t* order,
+                                const uint16_t* src, uint16_t* dst, hipStream_t st) {
+    const int64_t np = (int64_t)padded_block_count(g, cs) * g.block;
     const unsigned nblk = (unsigned)ceil_div(np * (g.d / 8), 256);
     if (g.d == 128)
         hipLaunchKernelGGL((k_gather_rows<128>), dim3(nblk, (unsigned)g.BH()), dim3(256), 0, st, src,
@@ -748,10 +780,10 @@ sa_status launch_cluster_gather(const Geometry& g, int C, const int32_t* order, 
     return hip_check(hipGetLastError(), "k_gather_rows launch");
 }
 
-sa_status launch_cluster_scatter(const Geometry& g, int C, const int32_t* order,
+sa_status launch_cluster_scatter(const Geometry& g, const sa_cluster_spec& cs, const int32_t* order,
                                  const uint16_t* src, uint16_t* dst, const float* lse_src,
                                  float* lse_dst, hipStream_t st) {
-    const int64_t np = (int64_t)padded_block_count(g, C) * g.block;
+    const int64_t np = (int64_t)padded_block_count(g, cs) * g.block;
     const unsigned nblk = (unsigned)ceil_div(np * (g.d / 8), 256);
     if (g.d == 128)
         hipLaunchKernelGGL((k_scatter_rows<128>), dim3(nblk, (unsigned)g.BH()), dim3(256), 0, st, src,
@@ -762,8 +794,9 @@ sa_status launch_cluster_scatter(const Geometry& g, int C, const int32_t* order,
     return hip_check(hipGetLastError(), "k_scatter_rows launch");
 }
 
-size_t cluster_select_workspace_bytes(const Geometry& g, int C) {
-    const int nbp = padded_block_count(g, C);
+size_t cluster_select_workspace_bytes(const Geometry& g, const sa_cluster_spec& cs) {
+    const int C = cs.n_clusters;
+    const int nbp = padded_block_count(g, cs);
     size_t o = 0;
     o = align_up(o + (size_t)g.BH() * C * C * 4, 256);      // scores
     o = align_up(o + (size_t)g.BH() * C * C, 256);          // keep flags
@@ -775,7 +808,7 @@ size_t cluster_select_workspace_bytes(const Geometry& g, int C) {
 sa_status launch_cluster_select(const Geometry& g, const sa_cluster_spec& cs, const ClusterSel& a,
                                 const int64_t* budget_host, char* ws, hipStream_t st) {
     const int C = cs.n_clusters;
-    const int nbp = padded_block_count(g, C);
+    const int nbp = padded_block_count(g, cs);
     size_t o = 0;
     float* S = reinterpret_cast<float*>(ws + o);
     o = align_up(o + (size_t)g.BH() * C * C * 4, 256);
@@ -805,7 +838,7 @@ sa_status launch_cluster_select(const Geometry& g, const sa_cluster_spec& cs, co
     hipLaunchKernelGGL(k_cselect, dim3((unsigned)(g.BH() * C)), dim3(kSelThreads), (size_t)cpad * 12, st, ca);
     if ((e = hip_check(hipGetLastError(), "k_cselect launch")) != SA_OK) return e;
     const int64_t rows = g.BH() * nbp;
-    hipLaunchKernelGGL(k_crow_count, dim3((unsigned)ceil_div(rows, 256)), dim3(256), 0, st, keep,
+    hipLaunchKernelGGL(k_crow_count, dim3((unsigned)ceil_div(rows, 4)), dim3(256), 0, st, keep,
                        a.k_count, a.q_blk, counts, rows, nbp, C, g.block);
     if ((e = hip_check(hipGetLastError(), "k_crow_count launch")) != SA_OK) return e;
     if ((e = launch_row_scan(counts, a.row_ptr, rows, st)) != SA_OK) return e;
@@ -824,11 +857,12 @@ sa_status launch_cluster_select(const Geometry& g, const sa_cluster_spec& cs, co
     return SA_OK;
 }
 
-sa_status launch_cluster_centroids(const Geometry& g, int C, const uint16_t* Kp,
+sa_status launch_cluster_centroids(const Geometry& g, const sa_cluster_spec& cs, const uint16_t* Kp,
                                    const uint16_t* Vp, const int32_t* k_count,
                                    const int32_t* k_blk, const int32_t* k_cnt, float* k_cent,
                                    float* v_cent, float* k_mean, float* v_sum, hipStream_t st) {
-    const int nbp = padded_block_count(g, C);
+    const int C = cs.n_clusters;
+    const int nbp = padded_block_count(g, cs);
     const int64_t np = (int64_t)nbp * g.block;
     const dim3 grid((unsigned)C, (unsigned)g.BH());
     sa_status e;

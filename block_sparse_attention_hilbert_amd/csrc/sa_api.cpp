@@ -334,14 +334,35 @@ SA_API sa_status sparse_attn_fwd_prepare_counts(const sa_problem* prob, const vo
 // ---------------------------------------------------------------------------
 static sa_status check_cluster(const Geometry& g, const sa_cluster_spec* cs) {
     if (!cs) return fail(SA_ERR_INVALID_ARG, "cspec is NULL");
-    if (cs->mode != SA_CLUSTER_COCLUSTER && cs->mode != SA_CLUSTER_KMEANS)
+    if (cs->mode != SA_CLUSTER_COCLUSTER && cs->mode != SA_CLUSTER_KMEANS &&
+        cs->mode != SA_CLUSTER_TILES)
         return fail(SA_ERR_INVALID_ARG, "unknown cluster mode %d", cs->mode);
-    const int cmax = g.N < 1024 ? g.N : 1024;
-    if (cs->n_clusters < 1 || cs->n_clusters > cmax)
-        return fail(SA_ERR_INVALID_ARG, "n_clusters = %d must be in [1, %d]", cs->n_clusters, cmax);
-    if (cs->iters < 1 || cs->iters > 64)
-        return fail(SA_ERR_INVALID_ARG, "iters = %d must be in [1, 64]", cs->iters);
-    const int64_t nbp = padded_block_count(g, cs->n_clusters);
+    if (cs->mode == SA_CLUSTER_TILES) {
+        if (cs->n_shapes < 1 || cs->n_shapes > 16 || !cs->shapes)
+            return fail(SA_ERR_INVALID_ARG, "a menu of 1 to 16 tile shapes is required (got %d)",
+                        cs->n_shapes);
+        for (int s = 0; s < cs->n_shapes; ++s) {
+            const sa_tile_shape sh = cs->shapes[s];
+            if (sh.t < 1 || sh.y < 1 || sh.x < 1)
+                return fail(SA_ERR_INVALID_ARG, "tile shape %d has a side < 1", s);
+            if ((int64_t)sh.t * sh.y * sh.x > g.block)
+                return fail(SA_ERR_INVALID_ARG, "tile shape %d holds %lld tokens > block = %d", s,
+                            (long long)sh.t * sh.y * sh.x, g.block);
+        }
+        const int mt = menu_max_tiles(g, *cs);
+        if (mt > 1024)
+            return fail(SA_ERR_UNSUPPORTED, "the menu cuts the grid into %d tiles (at most 1024)", mt);
+        if (cs->n_clusters != mt)
+            return fail(SA_ERR_INVALID_ARG, "n_clusters = %d must be the menu's largest tile count %d",
+                        cs->n_clusters, mt);
+    } else {
+        const int cmax = g.N < 1024 ? g.N : 1024;
+        if (cs->n_clusters < 1 || cs->n_clusters > cmax)
+            return fail(SA_ERR_INVALID_ARG, "n_clusters = %d must be in [1, %d]", cs->n_clusters, cmax);
+        if (cs->iters < 1 || cs->iters > 64)
+            return fail(SA_ERR_INVALID_ARG, "iters = %d must be in [1, 64]", cs->iters);
+    }
+    const int64_t nbp = padded_block_count(g, *cs);
     if (nbp > 4096)
         return fail(SA_ERR_UNSUPPORTED, "padded layout of %lld blocks (attention supports <= 4096)",
                     (long long)nbp);
@@ -368,9 +389,9 @@ SA_API sa_status sparse_attn_cluster_size(const sa_problem* prob, const sa_clust
     sa_status st = check_problem(prob, &g);
     if (st != SA_OK) return st;
     if ((st = check_cluster(g, cspec)) != SA_OK) return st;
-    if (nb_padded) *nb_padded = padded_block_count(g, cspec->n_clusters);
-    if (ws_cluster) *ws_cluster = cluster_workspace_bytes(g, cspec->n_clusters);
-    if (ws_select) *ws_select = cluster_select_workspace_bytes(g, cspec->n_clusters);
+    if (nb_padded) *nb_padded = padded_block_count(g, *cspec);
+    if (ws_cluster) *ws_cluster = cluster_workspace_bytes(g, *cspec);
+    if (ws_select) *ws_select = cluster_select_workspace_bytes(g, *cspec);
     return SA_OK;
 }
 
@@ -394,12 +415,32 @@ SA_API sa_status sparse_attn_cluster(const sa_problem* prob, const sa_cluster_sp
     if (!q_order || !k_order || !q_blk || !k_blk || !q_cnt || !k_cnt || !q_cent || !k_cent ||
         !q_count || !k_count)
         return fail(SA_ERR_INVALID_ARG, "every output except v_cent is required");
-    if ((st = check_ws(cluster_workspace_bytes(g, cspec->n_clusters), workspace, ws_bytes)) != SA_OK)
+    if (cspec->mode == SA_CLUSTER_TILES && !cspec->shape_idx)
+        return fail(SA_ERR_INVALID_ARG, "SA_CLUSTER_TILES needs shape_idx");
+    if ((st = check_ws(cluster_workspace_bytes(g, *cspec), workspace, ws_bytes)) != SA_OK)
         return st;
     ClusterOut o{q_order, k_order, q_blk, k_blk, q_cnt, k_cnt, q_cent, k_cent, v_cent,
                  q_count, k_count};
     return launch_cluster(g, *cspec, (const uint16_t*)Q, (const uint16_t*)K, (const uint16_t*)V,
                           o, (char*)workspace, (hipStream_t)stream);
+}
+
+SA_API sa_status sparse_attn_sics(const sa_problem* prob, const sa_cluster_spec* cspec,
+                                  const void* Q, const void* K, double* scores,
+                                  int32_t* shape_idx, void* workspace, size_t ws_bytes,
+                                  void* stream) {
+    clear_error();
+    Geometry g;
+    sa_status st = check_problem(prob, &g);
+    if (st != SA_OK) return st;
+    if ((st = check_cluster(g, cspec)) != SA_OK) return st;
+    if (cspec->mode != SA_CLUSTER_TILES)
+        return fail(SA_ERR_INVALID_ARG, "sparse_attn_sics needs mode SA_CLUSTER_TILES");
+    if (!Q || !K || !shape_idx) return fail(SA_ERR_INVALID_ARG, "Q, K and shape_idx are required");
+    if (!aligned16(Q) || !aligned16(K)) return fail(SA_ERR_INVALID_ARG, "Q, K must be 16-byte aligned");
+    if ((st = check_ws(sics_workspace_bytes(g, *cspec), workspace, ws_bytes)) != SA_OK) return st;
+    return launch_sics(g, *cspec, (const uint16_t*)Q, (const uint16_t*)K, scores, shape_idx,
+                       (char*)workspace, (hipStream_t)stream);
 }
 
 static sa_status check_rows(const Geometry& g, const void* src, void* dst, int64_t src_rows,
@@ -423,9 +464,9 @@ SA_API sa_status sparse_attn_cluster_gather(const sa_problem* prob, const sa_clu
     if (st != SA_OK) return st;
     if ((st = check_cluster(g, cspec)) != SA_OK) return st;
     if (!order) return fail(SA_ERR_INVALID_ARG, "order is required");
-    const int64_t np = (int64_t)padded_block_count(g, cspec->n_clusters) * g.block;
+    const int64_t np = (int64_t)padded_block_count(g, *cspec) * g.block;
     if ((st = check_rows(g, src, dst, g.N, np)) != SA_OK) return st;
-    return launch_cluster_gather(g, cspec->n_clusters, order, (const uint16_t*)src,
+    return launch_cluster_gather(g, *cspec, order, (const uint16_t*)src,
                                  (uint16_t*)dst, (hipStream_t)stream);
 }
 
@@ -440,9 +481,9 @@ SA_API sa_status sparse_attn_cluster_scatter(const sa_problem* prob, const sa_cl
     if (!order) return fail(SA_ERR_INVALID_ARG, "order is required");
     if ((lse_src == nullptr) != (lse_dst == nullptr))
         return fail(SA_ERR_INVALID_ARG, "lse_src and lse_dst must be given together");
-    const int64_t np = (int64_t)padded_block_count(g, cspec->n_clusters) * g.block;
+    const int64_t np = (int64_t)padded_block_count(g, *cspec) * g.block;
     if ((st = check_rows(g, src, dst, np, g.N)) != SA_OK) return st;
-    return launch_cluster_scatter(g, cspec->n_clusters, order, (const uint16_t*)src,
+    return launch_cluster_scatter(g, *cspec, order, (const uint16_t*)src,
                                   (uint16_t*)dst, lse_src, lse_dst, (hipStream_t)stream);
 }
 
@@ -485,7 +526,7 @@ SA_API sa_status sparse_attn_cluster_select(const sa_problem* prob, const sa_clu
     if (spec->want_comp && (!v_cent || !k_mean || !v_sum))
         return fail(SA_ERR_INVALID_ARG, "want_comp needs v_cent, k_mean and v_sum");
     const int C = cspec->n_clusters;
-    if ((st = check_ws(cluster_select_workspace_bytes(g, C), workspace, ws_bytes)) != SA_OK)
+    if ((st = check_ws(cluster_select_workspace_bytes(g, *cspec), workspace, ws_bytes)) != SA_OK)
         return st;
     std::string bbuf((size_t)g.H * sizeof(int64_t), '\0');
     int64_t* budget = (int64_t*)&bbuf[0];
@@ -519,7 +560,7 @@ SA_API sa_status sparse_attn_cluster_centroids(const sa_problem* prob, const sa_
         return fail(SA_ERR_INVALID_ARG, "every argument is required");
     if (!aligned16(Kp) || !aligned16(Vp))
         return fail(SA_ERR_INVALID_ARG, "Kp and Vp must be 16-byte aligned");
-    return launch_cluster_centroids(g, cspec->n_clusters, (const uint16_t*)Kp, (const uint16_t*)Vp,
+    return launch_cluster_centroids(g, *cspec, (const uint16_t*)Kp, (const uint16_t*)Vp,
                                     k_count, k_blk, k_cnt, k_cent, v_cent, k_mean, v_sum,
                                     (hipStream_t)stream);
 }

@@ -87,26 +87,41 @@ struct ClusterSel {
     float mass;
 };
 
-// ceil(N / block) + C: blocks of the padded clustered layout
-int padded_block_count(const Geometry& g, int C);
-size_t cluster_workspace_bytes(const Geometry& g, int C);
-size_t cluster_select_workspace_bytes(const Geometry& g, int C);
+// Blocks of the padded clustered layout: ceil(N / block) + C, or C for tiles
+// (one block per tile).
+int padded_block_count(const Geometry& g, const sa_cluster_spec& cs);
+size_t cluster_workspace_bytes(const Geometry& g, const sa_cluster_spec& cs);
+size_t cluster_select_workspace_bytes(const Geometry& g, const sa_cluster_spec& cs);
 sa_status launch_cluster(const Geometry& g, const sa_cluster_spec& cs, const uint16_t* Q,
                          const uint16_t* K, const uint16_t* V, const ClusterOut& o, char* ws,
                          hipStream_t stream);
-sa_status launch_cluster_gather(const Geometry& g, int C, const int32_t* order, const uint16_t* src,
-                                uint16_t* dst, hipStream_t stream);
-sa_status launch_cluster_scatter(const Geometry& g, int C, const int32_t* order,
+sa_status launch_cluster_gather(const Geometry& g, const sa_cluster_spec& cs, const int32_t* order,
+                                const uint16_t* src, uint16_t* dst, hipStream_t stream);
+sa_status launch_cluster_scatter(const Geometry& g, const sa_cluster_spec& cs, const int32_t* order,
                                  const uint16_t* src, uint16_t* dst, const float* lse_src,
                                  float* lse_dst, hipStream_t stream);
 sa_status launch_cluster_select(const Geometry& g, const sa_cluster_spec& cs, const ClusterSel& a,
                                 const int64_t* budget_host, char* ws, hipStream_t stream);
 // Key and value means of the clusters from K, V in the padded layout, and the
 // per-block compensation statistics (a call that reuses the partition).
-sa_status launch_cluster_centroids(const Geometry& g, int C, const uint16_t* Kp,
+sa_status launch_cluster_centroids(const Geometry& g, const sa_cluster_spec& cs, const uint16_t* Kp,
                                    const uint16_t* Vp, const int32_t* k_count,
                                    const int32_t* k_blk, const int32_t* k_cnt, float* k_cent,
                                    float* v_cent, float* k_mean, float* v_sum, hipStream_t stream);
+
+// ----------------------------------------------------------------------------
+// SICS scheme generation over shaped tiles (k_tiles.hip)
+// ----------------------------------------------------------------------------
+// Largest tile count of the menu on the grid.
+int menu_max_tiles(const Geometry& g, const sa_cluster_spec& cs);
+size_t sics_workspace_bytes(const Geometry& g, const sa_cluster_spec& cs);
+// Shape scores (fp64 [BH, n_shapes], optional) and the chosen shape per (b, h).
+sa_status launch_sics(const Geometry& g, const sa_cluster_spec& cs, const uint16_t* Q,
+                      const uint16_t* K, double* scores, int32_t* shape_idx, char* ws,
+                      hipStream_t stream);
+// assign[bh][n] = tile of token n under shape cs.shape_idx[bh].
+sa_status launch_tile_assign(const Geometry& g, const sa_cluster_spec& cs, int32_t* assign,
+                             hipStream_t stream);
 
 // ----------------------------------------------------------------------------
 // error-aware routing keys (k_route.hip)

@@ -23,6 +23,8 @@ With ``refresh_every = r`` it clusters and selects on calls 0, r, 2r, ...
 (SVOO keeps its partition for ~20 diffusion steps); the calls in between keep
 the partition and the keep lists, gather their own Q, K, V into the layout and,
 with compensation, take the cluster centroids from their own K and V.
+With a ``tiles`` cluster spec (SPADE parts 1-2) the partition of every head is
+the tile grid of the menu shape that SICS picks for it on the refreshing call.
 """
 from __future__ import annotations
 
@@ -33,7 +35,7 @@ import torch
 
 from . import (Clusters, ClusterSpec, Problem, Selection, SelectSpec, alloc_workspace,
                centroids, cluster, cluster_centroids, cluster_gather, cluster_scatter,
-               cluster_select,
+               cluster_select, sics,
                cluster_size, fwd, fwd_prepare, fwd_prepare_counts, fwd_run,
                hilbert_perm_build, hilbert_permute, hilbert_unpermute, padded_problem, select,
                workspace_size)
@@ -167,11 +169,20 @@ class ClusteredAttention:
                  want_scores: bool = False, want_lse: bool = False, refresh_every: int = 1):
         if refresh_every < 1:
             raise ValueError("refresh_every must be >= 1")
-        self.prob, self.cspec, self.spec = prob, cspec, spec
+        self.prob, self.spec = prob, spec
+        self.device = torch.device(device)
+        self.shape_idx = self.shape_scores = None
+        if cspec.mode == "tiles":
+            BH = prob.B * prob.H
+            self.shape_idx = torch.zeros(BH, dtype=torch.int32, device=self.device)
+            self.shape_scores = torch.zeros(BH, len(cspec.shapes), dtype=torch.float64,
+                                            device=self.device)
+            cspec = ClusterSpec(cspec.mode, cspec.n_clusters, cspec.iters, list(cspec.shapes),
+                                self.shape_idx)
+        self.cspec = cspec
         self.refresh_every = int(refresh_every)
         self.calls = 0
         self.have_partition = False
-        self.device = torch.device(device)
         self.nbp, ws_c, ws_s = cluster_size(prob, cspec)
         self.pprob = padded_problem(prob, self.nbp)
         pp = self.pprob
@@ -203,6 +214,9 @@ class ClusteredAttention:
                                    device=self.device)
 
     def run_cluster(self, Q, K, V):
+        if self.cspec.mode == "tiles":
+            sics(self.prob, self.cspec, Q, K, self.shape_idx, self.shape_scores,
+                 workspace=self.ws_cluster)
         cluster(self.prob, self.cspec, Q, K, V if self.spec.want_comp else None, out=self.cl,
                 workspace=self.ws_cluster)
         self.have_partition = True

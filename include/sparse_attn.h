@@ -89,14 +89,30 @@ enum {
     SA_CLUSTER_COCLUSTER = 1, /* keys by affinity (dot product) to the query
                                  centroids, then queries by affinity to the key
                                  centroids, alternately  [SVOO 2B]            */
-    SA_CLUSTER_KMEANS = 2     /* k-means (squared Euclidean distance) on Q and on
+    SA_CLUSTER_KMEANS = 2,    /* k-means (squared Euclidean distance) on Q and on
                                  K separately  [EAR 2A]                       */
+    SA_CLUSTER_TILES = 3      /* the tiles of one shape of a menu per (b, h),
+                                 chosen by sparse_attn_sics  [SPADE parts 1-2] */
 };
+
+/* A 3D tile shape (latent frames, rows, columns) [SPADE part 1]. */
+typedef struct {
+    int32_t t, y, x;
+} sa_tile_shape;
 
 typedef struct {
     int32_t mode;         /* SA_CLUSTER_*                                        */
-    int32_t n_clusters;   /* C in [1, min(N, 1024)], the same for Q and K        */
-    int32_t iters;        /* rounds in [1, 64] (one round assigns both sides)    */
+    int32_t n_clusters;   /* COCLUSTER, KMEANS: C in [1, min(N, 1024)], the same
+                             for Q and K.  TILES: the largest tile count of the
+                             menu (must be <= 1024)                              */
+    int32_t iters;        /* COCLUSTER, KMEANS: rounds in [1, 64] (one round
+                             assigns both sides); ignored by TILES               */
+    int32_t n_shapes;     /* TILES: menu size in [1, 16]                         */
+    const sa_tile_shape* shapes;  /* TILES: host [n_shapes]; every shape's volume
+                                     t*y*x <= block, so a tile is one block      */
+    const int32_t* shape_idx;     /* TILES: device int32 [B*H], the menu entry of
+                                     each (b, h) (sparse_attn_sics writes it);
+                                     needed by sparse_attn_cluster only          */
 } sa_cluster_spec;
 
 /* Selection rule.  Host-side struct; `topk` and `density` are host arrays. */
@@ -285,11 +301,15 @@ sa_status sparse_attn_fwd_run(const sa_problem* prob, const void* Q, const void*
  * are fp32 roundings of exact sums (fp64) divided by the count; an empty
  * cluster keeps its previous centroid.
  *
+ * TILES -- no iteration: the clusters of (b, h) are the tiles of menu shape
+ *           shape_idx[b*H+h], the same partition for Q and K; clusters past
+ *           that shape's tile count are empty and their centroids are 0.
+ *
  * Padded layout: a cluster takes whole blocks of the layout -- its tokens in
  * ascending token order, then zero padding to a multiple of `block`; clusters
  * follow each other in index order.  The layout has nbp = ceil(N/block) + C
- * blocks (an upper bound for every head), Np = nbp * block slots; blocks past
- * the last cluster are empty.  Attention on the layout is a plain sa_problem
+ * blocks (an upper bound for every head; TILES: nbp = C, one block per tile),
+ * Np = nbp * block slots; blocks past the last cluster are empty.  Attention on the layout is a plain sa_problem
  * with N = Np (T = Hg = 1, W = Np) whose KV blocks carry token counts
  * (sparse_attn_fwd_prepare_counts).
  * ---------------------------------------------------------------------------
@@ -299,6 +319,29 @@ sa_status sparse_attn_fwd_run(const sa_problem* prob, const void* Q, const void*
  */
 sa_status sparse_attn_cluster_size(const sa_problem* prob, const sa_cluster_spec* cspec,
                                    int32_t* nb_padded, size_t* ws_cluster, size_t* ws_select);
+
+/*
+ * SICS scheme generation [SPADE part 2: per head and step, the sum of
+ * intra-block cosine similarities decides the scheme; part 1: a menu of 3D
+ * tile shapes].  cspec: mode SA_CLUSTER_TILES with the menu.  For every
+ * (b, h) and menu shape s: tiles of s cut the (T, Hg, W) grid ([tt*t,
+ * (tt+1)*t) x ... clipped at the grid's end, numbered in raster order of the
+ * tile coordinates); the score is the mean cosine similarity of the ordered
+ * pairs of distinct tokens inside a tile, over queries and keys:
+ *     (sum_tiles |sum_a q_a/|q_a||^2 - nq + |sum_a k_a/|k_a||^2 - nk)
+ *       / (2 sum_tiles n (n - 1))
+ * (nq, nk: tokens with a non-zero vector; a zero vector has cosine 0), in
+ * fp64; shape_idx[b*H+h] = the shape with the largest score, the first of the
+ * menu on ties.  Q, K: device bf16 [B,H,N,d].  scores: optional device fp64
+ * [B*H, n_shapes].  shape_idx: device int32 [B*H].  workspace: device,
+ * 256-byte aligned, >= the ws_cluster of sparse_attn_cluster_size.  The
+ * partition itself is then sparse_attn_cluster with the same cspec and
+ * shape_idx set: every tile is one block (nbp = n_clusters), tokens in raster
+ * order inside it.
+ */
+sa_status sparse_attn_sics(const sa_problem* prob, const sa_cluster_spec* cspec, const void* Q,
+                           const void* K, double* scores, int32_t* shape_idx, void* workspace,
+                           size_t ws_bytes, void* stream);
 
 /*
  * sparse_attn_cluster: clusters Q and K of every (b, h) and lays them out.

@@ -19,6 +19,7 @@ import pytest
 
 import oracle
 from oracle import clusters as OC
+from oracle import tiles as OT
 import workloads as W
 from parity_util import ATOL_MAX, ATOL_MEAN, LSE_ATOL, TIE_REL, from_dev, log, to_dev
 
@@ -63,6 +64,15 @@ SMALL = {
     "cocluster_iid_many": W.CONFIGS[1].replace(T=3, Hg=10, W=13, H=2, cluster="cocluster",
                                                n_clusters=40, cluster_iters=2, rule="mass",
                                                mass=0.8, diag=False, comp=True, topk=None),
+    # SICS scheme generation over shaped tiles (SPADE parts 1-2), heads of
+    # different anisotropy so that they pick different shapes
+    "tiles_topk_d128_b64": BASE.replace(H=4, block=64, cluster="tiles", aniso=True,
+                                        tile_shapes=((1, 4, 16), (1, 8, 8), (2, 4, 8), (3, 2, 8)),
+                                        n_clusters=12, rule="topk", density=0.3),
+    "tiles_mass_comp_diag_d64_b128": W.CONFIGS[2].replace(
+        T=5, Hg=9, W=29, H=4, d=64, cluster="tiles", aniso=True,
+        tile_shapes=((1, 4, 32), (1, 8, 16), (2, 4, 16), (5, 3, 8)), n_clusters=20,
+        mass=0.8, comp=True, diag=True),
 }
 
 
@@ -104,6 +114,10 @@ def check_case(wl, Q, K, V, heads, q_clusters_per_head=None, seed=0):
          ("q_order", "k_order", "q_blk", "k_blk", "q_cnt", "k_cnt", "q_cent", "k_cent",
           "q_count", "k_count")}
     v_cent = cl.v_cent.cpu().numpy() if cl.v_cent is not None else None
+    tiles = wl.cluster == "tiles"
+    if tiles:
+        pick_gpu = pipe.shape_idx.cpu().numpy()
+        sc_gpu = pipe.shape_scores.cpu().numpy()
     S_gpu = sel.scores.cpu().numpy()
     rp = sel.row_ptr.cpu().numpy().astype(np.int64)
     ci = sel.col_idx.cpu().numpy()
@@ -117,13 +131,25 @@ def check_case(wl, Q, K, V, heads, q_clusters_per_head=None, seed=0):
     vs = sel.v_sum.cpu().numpy() if sel.v_sum is not None else None
     rng = np.random.default_rng(seed)
     errs, lse_errs, excused = [], [], 0
+    picks = []
     for bh in heads:
         b, h = divmod(bh, wl.H)
         q = oracle.bf16_to_f64(Q[b, h])
         k = oracle.bf16_to_f64(K[b, h])
         v = oracle.bf16_to_f64(V[b, h])
-        ref = OC.cluster_workload_head(wl, q, k)
         tag = f"{wl.name} bh={bh}"
+        if tiles:
+            ref = OT.tiles_workload_head(wl, q, k)
+            assert np.allclose(sc_gpu[bh], ref["scores"], rtol=1e-9, atol=1e-12), tag
+            if pick_gpu[bh] != ref["pick"]:
+                # a near tie of the two shapes' scores; follow the GPU's pick
+                top = ref["scores"]
+                assert abs(top[pick_gpu[bh]] - top[ref["pick"]]) <= 1e-9 * np.abs(top).max(), tag
+                excused += 1
+                ref = OT.tiles_workload_head(wl, q, k, shape_idx=pick_gpu[bh])
+            picks.append(int(ref["pick"]))
+        else:
+            ref = OC.cluster_workload_head(wl, q, k)
         assert np.array_equal(g["q_count"][bh], ref["nq"]), tag
         assert np.array_equal(g["k_count"][bh], ref["nk"]), tag
         assert np.array_equal(g["q_cent"][bh].view(np.uint32), ref["cq"].view(np.uint32)), tag
@@ -175,6 +201,8 @@ def check_case(wl, Q, K, V, heads, q_clusters_per_head=None, seed=0):
             lse_errs.append(np.abs(lg[fin] - lr[fin]))
     e = np.concatenate(errs)
     le = np.concatenate(lse_errs) if lse_errs else np.zeros(1)
+    if tiles:
+        log(f"[cluster] {wl.name}: shapes picked per checked head {picks}")
     return float(e.max()), float(e.mean()), float(le.max()), excused
 
 
@@ -189,7 +217,7 @@ def test_small_cluster_parity(name):
     assert emax <= ATOL_MAX and emean <= ATOL_MEAN and lmax <= LSE_ATOL
 
 
-@pytest.mark.parametrize("name", ["wan13b_cocluster", "wan13b_kmeans_comp"])
+@pytest.mark.parametrize("name", ["wan13b_cocluster", "wan13b_kmeans_comp", "wan13b_sics"])
 def test_full_size_cluster_parity(name):
     """The full 1.3B-sized layer (12 heads, N = 32,760): the whole call on the
     GPU; layouts, centroids, scores and keep of two heads checked exactly and

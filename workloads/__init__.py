@@ -51,6 +51,10 @@ import numpy as np
 # the wan13b workload keeps roughly 15-30 % of the KV blocks (the measured
 # density is always reported next to any result).
 SMOOTH_ALPHA = 2.25
+# Head-dependent anisotropy (a field smoother along one axis than the others,
+# which axis depending on the head): largest wave numbers (t, y, x), head h
+# takes entry h mod 4.
+ANISO_FMAX = ((0, 3, 3), (3, 0, 3), (3, 3, 0), (3, 3, 3))
 NOISE_STD = 0.3
 N_MODES = 8
 
@@ -79,9 +83,11 @@ class Workload:
     gen: str = "smooth"            # "iid" | "smooth"
     head_freq: bool = False        # head-dependent wave-number range
     seed: int = 0
-    cluster: str = ""              # "" (fixed blocks) | "cocluster" | "kmeans"
+    cluster: str = ""              # "" (fixed blocks) | "cocluster" | "kmeans" | "tiles"
     n_clusters: int = 0
     cluster_iters: int = 0
+    tile_shapes: tuple = ()        # "tiles": the menu of (t, y, x) tile shapes
+    aniso: bool = False            # head-dependent anisotropy of the smooth field
 
     @property
     def N(self) -> int:
@@ -139,6 +145,13 @@ CONFIGS = {
 # budget and centroid compensation.  64 clusters of ~512 tokens each (4
 # blocks of 128 when full) keep the padding of the clustered layout small;
 # 3 refinement rounds.
+#
+# SPADE's scheme generation (parts 1-2): per head, the tile shape of SICS_MENU
+# whose tiles are the most coherent (SICS), each tile one block; a 15 % token
+# budget (the page's ~85 % sparsity).  Every menu shape holds 128 tokens; on
+# the 21x30x52 grid the largest entry has 352 tiles (n_clusters).
+SICS_MENU = ((1, 4, 32), (1, 8, 16), (2, 4, 16), (2, 8, 8), (4, 4, 8), (8, 4, 4))
+
 EXTRA = {
     "wan13b_err": CONFIGS[2].replace(name="wan13b_err", rule="err", density=0.2, comp=True),
     "wan13b_topk_comp": CONFIGS[2].replace(name="wan13b_topk_comp", rule="topk", density=0.2,
@@ -148,6 +161,9 @@ EXTRA = {
     "wan13b_kmeans_comp": CONFIGS[2].replace(name="wan13b_kmeans_comp", cluster="kmeans",
                                              n_clusters=64, cluster_iters=3, rule="topk",
                                              density=0.2, comp=True),
+    "wan13b_sics": CONFIGS[2].replace(name="wan13b_sics", cluster="tiles",
+                                      tile_shapes=SICS_MENU, n_clusters=352, rule="topk",
+                                      density=0.15, aniso=True),
 }
 
 
@@ -224,29 +240,34 @@ def _scratch(name: str, shape, dtype) -> np.ndarray:
 
 
 def _smooth_field(rng: np.random.Generator, T: int, Hg: int, W: int, d: int,
-                  fmax: int, alpha: float) -> np.ndarray:
+                  fmax, alpha: float) -> np.ndarray:
     """Sum of N_MODES random low-frequency 3D cosines per channel -> [N, d] float32.
 
     F_c(t,y,x) = sum_m a_m cos(2 pi (f_t t/T + f_y y/Hg + f_x x/W) + phi_m),
     evaluated separably as the real part of a product of 1D complex
     exponentials (one complex coefficient per channel and wave-number triple).
+    ``fmax``: the largest wave number, one for all axes or a (t, y, x) triple.
     """
-    freqs = rng.integers(0, fmax + 1, size=(d, N_MODES, 3))
+    if isinstance(fmax, (tuple, list)):
+        nfs = tuple(int(f) + 1 for f in fmax)
+        freqs = rng.integers(0, np.array(nfs), size=(d, N_MODES, 3))
+    else:
+        nfs = (fmax + 1,) * 3
+        freqs = rng.integers(0, fmax + 1, size=(d, N_MODES, 3))
     phase = rng.uniform(0.0, 2.0 * math.pi, size=(d, N_MODES))
     amp = alpha * rng.standard_normal((d, N_MODES)) / math.sqrt(N_MODES)
-    nf = fmax + 1
-    coef = np.zeros((d, nf, nf, nf), dtype=np.complex128)
+    nft, nfy, nfx = nfs
+    coef = np.zeros((d, nft, nfy, nfx), dtype=np.complex128)
     cc = np.repeat(np.arange(d), N_MODES)
     np.add.at(coef, (cc, freqs[..., 0].ravel(), freqs[..., 1].ravel(),
                      freqs[..., 2].ravel()),
               (amp * np.exp(1j * phase)).ravel())
-    f = np.arange(nf)
-    et = np.exp(2j * math.pi * np.outer(np.arange(T), f) / T)    # [T, nf]
-    ey = np.exp(2j * math.pi * np.outer(np.arange(Hg), f) / Hg)  # [Hg, nf]
-    ex = np.exp(2j * math.pi * np.outer(np.arange(W), f) / W)    # [W, nf]
+    et = np.exp(2j * math.pi * np.outer(np.arange(T), np.arange(nft)) / T)    # [T, nft]
+    ey = np.exp(2j * math.pi * np.outer(np.arange(Hg), np.arange(nfy)) / Hg)  # [Hg, nfy]
+    ex = np.exp(2j * math.pi * np.outer(np.arange(W), np.arange(nfx)) / W)    # [W, nfx]
     g1 = coef @ ex.T                                    # [d, ft, fy, W]
     g2 = np.einsum("cabx,yb->caxy", g1, ey)             # [d, ft, W, Hg]
-    g2 = g2.transpose(1, 3, 2, 0).reshape(nf, Hg * W * d)  # [ft, (y, x, c)]
+    g2 = g2.transpose(1, 3, 2, 0).reshape(nft, Hg * W * d)  # [ft, (y, x, c)]
     # Re(et @ g2) = et.re @ g2.re - et.im @ g2.im, a few frames at a time
     g2r = np.ascontiguousarray(g2.real)
     g2i = np.ascontiguousarray(g2.imag)
@@ -281,6 +302,8 @@ def make_head(wl: Workload, b: int, h: int, alpha: float = None, out=None):
             f32_to_bf16_bits(buf, o, tmp)
     elif wl.gen == "smooth":
         fmax = 1 + (h % 4) if wl.head_freq else 3
+        if wl.aniso:
+            fmax = ANISO_FMAX[h % len(ANISO_FMAX)]
         a = SMOOTH_ALPHA if alpha is None else alpha
         field = _smooth_field(rng, wl.T, wl.Hg, wl.W, d, fmax, a)
         for o in out[:2]:
