@@ -204,19 +204,26 @@ __global__ __launch_bounds__(D) void k_sics_tiles(const double* __restrict__ U,
     }
 }
 
-// Score of every (shape, b*h): the tiles' sums in tile order.
-__global__ void k_sics_shapes(const double* __restrict__ tile_sics,
-                              const double* __restrict__ tile_pairs, double* __restrict__ scores,
-                              Menu m, int64_t BH, int cmax) {
-    const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;     // bh * n + s
+// Score of every (shape, b*h), one wave each: lane L sums tiles L, L+64, ...
+// in order, then a fixed tree over the lanes.
+__global__ __launch_bounds__(256) void k_sics_shapes(const double* __restrict__ tile_sics,
+                                                     const double* __restrict__ tile_pairs,
+                                                     double* __restrict__ scores, Menu m,
+                                                     int64_t BH, int cmax) {
+    const int64_t e = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);     // bh * n + s
     if (e >= BH * m.n) return;
+    const int lane = threadIdx.x & 63;
     const int s = (int)(e % m.n);
     double total = 0.0, pairs = 0.0;
-    for (int t = 0; t < m.ntiles[s]; ++t) {
+    for (int t = lane; t < m.ntiles[s]; t += 64) {
         total += tile_sics[e * cmax + t];
         pairs += tile_pairs[e * cmax + t];
     }
-    scores[e] = pairs > 0.0 ? total / (2.0 * pairs) : 0.0;
+    for (int off = 32; off > 0; off >>= 1) {
+        total += __shfl_down(total, off, 64);
+        pairs += __shfl_down(pairs, off, 64);
+    }
+    if (lane == 0) scores[e] = pairs > 0.0 ? total / (2.0 * pairs) : 0.0;
 }
 
 __global__ void k_sics_pick(const double* __restrict__ scores, int32_t* __restrict__ shape_idx,
@@ -290,7 +297,7 @@ sa_status launch_sics(const Geometry& g, const sa_cluster_spec& cs, const uint16
         hipLaunchKernelGGL((k_sics_tiles<64>), gt, dim3(64), 0, st, U, NZ, tsics, tpairs, m, g.T,
                            g.Hg, g.W, na, cmax);
     if ((e = hip_check(hipGetLastError(), "k_sics_tiles launch")) != SA_OK) return e;
-    hipLaunchKernelGGL(k_sics_shapes, dim3((unsigned)ceil_div(g.BH() * m.n, 64)), dim3(64), 0, st,
+    hipLaunchKernelGGL(k_sics_shapes, dim3((unsigned)ceil_div(g.BH() * m.n, 4)), dim3(256), 0, st,
                        tsics, tpairs, sc, m, g.BH(), cmax);
     if ((e = hip_check(hipGetLastError(), "k_sics_shapes launch")) != SA_OK) return e;
     hipLaunchKernelGGL(k_sics_pick, dim3((unsigned)ceil_div(g.BH(), 256)), dim3(256), 0, st, sc,

@@ -285,3 +285,32 @@ def test_cluster_centroids_reject_before_any_launch():
     bad = sa.ClusterSpec("kmeans", 0, 2).c()
     assert f(ctypes.byref(p), ctypes.byref(bad), fake, fake, fake, fake, fake, fake, fake, fake,
              fake, None) == sa.SA_ERR_INVALID_ARG
+
+
+def test_sics_and_tile_mode_reject_before_any_launch():
+    p = sa.Problem(1, 2, 390, 128, 3, 10, 13, 64)
+    menu = [(1, 4, 16), (1, 8, 8), (2, 4, 8)]
+    good = sa.ClusterSpec("tiles", 12, 0, shapes=menu)
+    nbp, wc, ws = sa.cluster_size(p, good)
+    assert nbp == 12                                   # one block per tile
+    vp = ctypes.c_void_p
+    fake = vp(1 << 20)
+    f = sa.lib.sparse_attn_sics
+    for cs, code in [(sa.ClusterSpec("kmeans", 4, 2), sa.SA_ERR_INVALID_ARG),      # not tiles
+                     (sa.ClusterSpec("tiles", 11, 0, shapes=menu), sa.SA_ERR_INVALID_ARG),
+                     (sa.ClusterSpec("tiles", 12, 0, shapes=menu + [(2, 8, 8)]),
+                      sa.SA_ERR_INVALID_ARG),           # 128 tokens > block 64
+                     (sa.ClusterSpec("tiles", 12, 0, shapes=[(0, 4, 16)]), sa.SA_ERR_INVALID_ARG),
+                     (sa.ClusterSpec("tiles", 12, 0, shapes=[]), sa.SA_ERR_INVALID_ARG)]:
+        st = f(ctypes.byref(p.c()), ctypes.byref(cs.c()), fake, fake, None, fake, fake, 1 << 30, None)
+        assert st == code, cs
+    st = f(ctypes.byref(p.c()), ctypes.byref(good.c()), fake, fake, None, None, fake, 1 << 30, None)
+    assert st == sa.SA_ERR_INVALID_ARG                 # no shape_idx output
+    st = f(ctypes.byref(p.c()), ctypes.byref(good.c()), fake, fake, None, fake, fake, 64, None)
+    assert st == sa.SA_ERR_WORKSPACE
+    # the partition call needs the per-head shapes
+    outs = [fake] * 10
+    st = sa.lib.sparse_attn_cluster(ctypes.byref(p.c()), ctypes.byref(good.c()), fake, fake, None,
+                                    *outs[:8], None, *outs[:2], fake, 1 << 30, None)
+    assert st == sa.SA_ERR_INVALID_ARG
+    assert b"shape_idx" in sa.lib.sparse_attn_last_error()
