@@ -73,6 +73,12 @@ SMALL = {
         T=5, Hg=9, W=29, H=4, d=64, cluster="tiles", aniso=True,
         tile_shapes=((1, 4, 32), (1, 8, 16), (2, 4, 16), (5, 3, 8)), n_clusters=20,
         mass=0.8, comp=True, diag=True),
+    # batches of two
+    "kmeans_comp_batch2": BASE.replace(B=2, block=64, cluster="kmeans", n_clusters=6,
+                                       cluster_iters=2, rule="topk", density=0.3, comp=True),
+    "tiles_topk_batch2": BASE.replace(B=2, H=3, block=64, cluster="tiles", aniso=True,
+                                      tile_shapes=((1, 4, 16), (1, 8, 8), (2, 4, 8)),
+                                      n_clusters=12, rule="topk", density=0.3),
 }
 
 

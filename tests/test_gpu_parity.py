@@ -62,6 +62,12 @@ SMALL = {
                                              density=0.3, comp=True),
     "err_d64_b128_diag": W.CONFIGS[1].replace(T=3, Hg=10, W=13, H=2, block=128, rule="err",
                                               comp=True, diag=True),
+    # batches of two: every kernel indexes (batch, head) pairs
+    "mass_batch2": W.CONFIGS[2].replace(B=2, T=3, Hg=10, W=13, H=2),
+    "hilbert_comp_batch2": W.CONFIGS[5].replace(B=2, T=3, Hg=10, W=13, H=3),
+    "window_anchor_batch2": W.CONFIGS[4].replace(B=2, T=6, Hg=10, W=13, H=2),
+    "err_batch2": W.CONFIGS[2].replace(B=2, T=3, Hg=10, W=13, H=2, rule="err", density=0.3,
+                                       comp=True),
 }
 
 
