@@ -599,29 +599,42 @@ __global__ __launch_bounds__(kSchedThreads) void k_sched(const int32_t* __restri
 }
 
 // V blocks transposed to [D][BLK] (keys past the end of the sequence are 0).
+// Each thread moves one 8 x 8 sub-tile (8 keys x 8 channels) through its
+// registers: 8 16-byte row loads, a transpose of the bf16 pairs, 8 16-byte
+// stores of 8 consecutive keys of one channel.  Consecutive lanes take
+// consecutive key groups, so 16 (8) lanes write one whole 256-byte (128-byte)
+// row of the transposed block.
 template <int D, int BLK>
 __global__ __launch_bounds__(256) void k_vt_prep(const uint16_t* __restrict__ V,
                                                  uint16_t* __restrict__ Vt, int N, int nb) {
-    __shared__ uint16_t tile[BLK][D + 8];
+    constexpr int KC = BLK / 8, DC = D / 8;
     const int j = blockIdx.x;
     const int64_t bh = blockIdx.y;
     const int n = min(BLK, N - j * BLK);
     const uint16_t* src = V + (bh * N + (int64_t)j * BLK) * D;
-    for (int c = threadIdx.x; c < BLK * (D / 8); c += 256) {
-        const int r = c / (D / 8), ch = c % (D / 8);
-        uint4 v = make_uint4(0, 0, 0, 0);
-        if (r < n) v = *reinterpret_cast<const uint4*>(src + (int64_t)r * D + ch * 8);
-        *reinterpret_cast<uint4*>(&tile[r][ch * 8]) = v;
-    }
-    __syncthreads();
     uint16_t* dst = Vt + (bh * nb + j) * (int64_t)D * BLK;
-    for (int p = threadIdx.x; p < D * (BLK / 8); p += 256) {
-        const int d = p / (BLK / 8), kc = p % (BLK / 8);
-        uint32_t w[4];
+    for (int p = threadIdx.x; p < KC * DC; p += 256) {
+        const int kc = p % KC, dc = p / KC;
+        uint32_t w[8][4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-            w[e] = (uint32_t)tile[kc * 8 + 2 * e][d] | ((uint32_t)tile[kc * 8 + 2 * e + 1][d] << 16);
-        *reinterpret_cast<uint4*>(dst + (int64_t)d * BLK + kc * 8) = make_uint4(w[0], w[1], w[2], w[3]);
+        for (int r = 0; r < 8; ++r) {
+            const int key = kc * 8 + r;
+            uint4 v = make_uint4(0, 0, 0, 0);
+            if (key < n) v = *reinterpret_cast<const uint4*>(src + (int64_t)key * D + dc * 8);
+            w[r][0] = v.x; w[r][1] = v.y; w[r][2] = v.z; w[r][3] = v.w;
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            // channel dc*8 + i of keys kc*8 .. kc*8 + 7
+            uint32_t o[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const uint32_t a = w[2 * q][i / 2], b = w[2 * q + 1][i / 2];
+                o[q] = (i & 1) ? ((a >> 16) | (b & 0xffff0000u)) : ((a & 0xffffu) | (b << 16));
+            }
+            *reinterpret_cast<uint4*>(dst + (int64_t)(dc * 8 + i) * BLK + kc * 8) =
+                make_uint4(o[0], o[1], o[2], o[3]);
+        }
     }
 }
 

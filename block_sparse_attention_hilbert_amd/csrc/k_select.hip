@@ -44,13 +44,18 @@ struct PoolArgs {
     int32_t N, nb, unit, n_units;
 };
 
+// One workgroup per (block, b*h, role).  Thread (s, ch) sums rows
+// [s*SEGR, (s+1)*SEGR) of channels [8 ch, 8 ch + 8) straight from HBM (SEGR
+// 16-byte loads in flight per thread, no LDS staging); the 16 segment sums
+// then combine into unit and block sums.  Sums of bf16 values are exact in
+// fp64, so the grouping does not change the result.
 template <int D, int BLK>
 __global__ __launch_bounds__(kThreads) void k_pool(PoolArgs a) {
     constexpr int CH = D / 8;             // 16-byte chunks per row
-    constexpr int SEG = 16;               // rows per partial sum
-    constexpr int NSEG = BLK / SEG;
-    __shared__ uint4 tile[BLK * CH];      // BLK x D bf16
-    __shared__ double seg[NSEG][D];
+    constexpr int NS = kThreads / CH;     // row segments (16 for d = 128, 32 for d = 64)
+    constexpr int SEGR = BLK / NS;        // rows per segment
+    static_assert(SEGR >= 1 && NS * SEGR == BLK, "segments tile the block");
+    __shared__ double seg[NS][D];
 
     const int blk = blockIdx.x;
     const int64_t bh = blockIdx.y;
@@ -58,45 +63,52 @@ __global__ __launch_bounds__(kThreads) void k_pool(PoolArgs a) {
     const int tid = threadIdx.x;
     const int row0 = blk * BLK;
     const int n = min(BLK, a.N - row0);
-    const uint4* src = reinterpret_cast<const uint4*>(a.src[role] + (bh * a.N + row0) * D);
+    const int sgi = tid / CH, ch = tid % CH;
+    const uint4* src = reinterpret_cast<const uint4*>(a.src[role] + (bh * a.N + row0) * D) + ch;
 
-    for (int c = tid; c < n * CH; c += kThreads) tile[c] = src[c];
-    __syncthreads();
-
-    // partial sums over 16-row segments (exact in fp64)
-    const uint16_t* t16 = reinterpret_cast<const uint16_t*>(tile);
-    const int nseg = (n + SEG - 1) / SEG;
-    for (int p = tid; p < nseg * D; p += kThreads) {
-        const int s = p / D, c = p % D;
-        const int r1 = min(n, (s + 1) * SEG);
-        double acc = 0.0;
-        for (int r = s * SEG; r < r1; ++r) acc += (double)bf16_to_f32(t16[r * D + c]);
-        seg[s][c] = acc;
+    uint4 v[SEGR];
+#pragma unroll
+    for (int r = 0; r < SEGR; ++r) {
+        const int row = sgi * SEGR + r;
+        v[r] = row < n ? src[row * CH] : make_uint4(0, 0, 0, 0);
     }
+    double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+    for (int r = 0; r < SEGR; ++r) {
+        const uint32_t w[4] = {v[r].x, v[r].y, v[r].z, v[r].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            acc[2 * e] += (double)__uint_as_float(w[e] << 16);
+            acc[2 * e + 1] += (double)__uint_as_float(w[e] & 0xffff0000u);
+        }
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) seg[sgi][ch * 8 + e] = acc[e];
     __syncthreads();
 
+    const int nseg = (n + SEGR - 1) / SEGR;
     float* uo = a.unit_out[role];
     if (uo) {
         const int spb = BLK / a.unit;
-        const int segs_per_unit = a.unit / SEG;
+        const int segs_per_unit = a.unit / SEGR;
         const int nunit = (n + a.unit - 1) / a.unit;
         for (int p = tid; p < nunit * D; p += kThreads) {
             const int u = p / D, c = p % D;
-            double acc = 0.0;
-            for (int s = u * segs_per_unit; s < min(nseg, (u + 1) * segs_per_unit); ++s)
-                acc += seg[s][c];
+            double t = 0.0;
+            for (int s2 = u * segs_per_unit; s2 < min(nseg, (u + 1) * segs_per_unit); ++s2)
+                t += seg[s2][c];
             const int cnt = min(a.unit, n - u * a.unit);
             uo[((int64_t)bh * a.n_units + (int64_t)blk * spb + u) * D + c] =
-                (float)(acc / (double)cnt);
+                (float)(t / (double)cnt);
         }
     }
     float* bo = a.block_out[role];
     if (bo) {
         for (int c = tid; c < D; c += kThreads) {
-            double acc = 0.0;
-            for (int s = 0; s < nseg; ++s) acc += seg[s][c];
-            const float v = role == 2 ? (float)acc : (float)(acc / (double)n);
-            bo[((int64_t)bh * a.nb + blk) * D + c] = v;
+            double t = 0.0;
+            for (int s2 = 0; s2 < nseg; ++s2) t += seg[s2][c];
+            const float val = role == 2 ? (float)t : (float)(t / (double)n);
+            bo[((int64_t)bh * a.nb + blk) * D + c] = val;
         }
     }
 }
