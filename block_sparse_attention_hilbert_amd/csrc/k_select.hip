@@ -265,8 +265,21 @@ __global__ __launch_bounds__(kThreads) void k_select(SelectArgs a) {
             for (int r = tid; r < nb; r += kThreads) cum[r] = exp((double)S[ord[r]] - smax);
             __syncthreads();
             if (tid == 0) {
+                // the same sequential sum, 32 values at a time through registers
+                // so that the LDS loads are not serialised behind the adds
+                constexpr int CK = 32;
                 double run = 0.0;
-                for (int r = 0; r < nb; ++r) { run += cum[r]; cum[r] = run; }
+                int r = 0;
+                for (; r + CK <= nb; r += CK) {
+                    double v[CK];
+#pragma unroll
+                    for (int k = 0; k < CK; ++k) v[k] = cum[r + k];
+#pragma unroll
+                    for (int k = 0; k < CK; ++k) { run += v[k]; v[k] = run; }
+#pragma unroll
+                    for (int k = 0; k < CK; ++k) cum[r + k] = v[k];
+                }
+                for (; r < nb; ++r) { run += cum[r]; cum[r] = run; }
             }
             __syncthreads();
             const double thr = (double)a.mass * cum[nb - 1];
