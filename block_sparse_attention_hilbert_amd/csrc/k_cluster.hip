@@ -4,7 +4,7 @@
 //
 // Per (batch, head) and per side (queries, keys):
 //   k_chunk_assign  initial partition: C equal chunks of the token order
-//   k_cent_prep, k_assign
+//   k_cent_bias + k_assign_mx (C <= 64), k_cent_prep + k_assign (larger C)
 //                   every token to its best centroid: the largest
 //                   x.c (co-clustering affinity) or x.c - |c|^2/2 (k-means),
 //                   each dot product a sequential fp32 FMA chain over the
@@ -128,6 +128,212 @@ __global__ __launch_bounds__(kAsgThreads) void k_assign(const uint16_t* __restri
         }
     }
     if (t < N) assign[bh * N + t] = arg;
+}
+
+// ----------------------------------------------------------------------------
+// assignment on the matrix cores with a certified filter (C <= 64)
+//
+// s~[c, t] = x_t . c on v_mfma_f32_32x32x16_bf16: x is bf16 (exact operand),
+// the fp32 centroid is split into bf16 hi + lo; |s~ - seqfma| <= 2^-14.7
+// sum_d |x_d c_d| (split remainder 2^-16, fp32 accumulation of 256 terms, the
+// chain's own 128 roundings).  With B = 2^-12 (|x| |c| + |bias_c|), a
+// centroid can win only if s~ + bias + B >= the token's best s~ + bias - B;
+// those candidates (about one per token) get the exact decision arithmetic
+// of k_assign, and the exact winner among them is the winner among all.
+// One wave = 32 tokens (two lanes per token); the workgroup's centroids sit in
+// LDS (fp32; the hi / lo operands are split from them).  Each token's
+// candidates are evaluated by its own two lanes in ascending index order.
+// ----------------------------------------------------------------------------
+typedef __bf16 amx_bf16x8 __attribute__((ext_vector_type(8)));
+typedef float amx_f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kAmxC = 64;                  // centroid slots (C <= 64)
+constexpr float kAmxEps = 1.0f / 4096.0f;  // bound factor 2^-12
+
+__device__ __forceinline__ uint16_t amx_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+__device__ __forceinline__ uint32_t amx_ordered(float f) {
+    const uint32_t u = __float_as_uint(f);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// The centroids' decision bias (as k_cent_prep: fl32(-0.5 seqfma(c, c)) for
+// k-means, 0 for co-clustering, -inf for unused slots) and an upper bound of
+// their norm.  One thread per (slot, b*h).
+__global__ void k_cent_bias(const float* __restrict__ cent, float* __restrict__ bias,
+                            float* __restrict__ cnorm, int C, int D, int kmeans, int64_t BH) {
+    const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (e >= BH * kAmxC) return;
+    const int c = (int)(e % kAmxC);
+    const int64_t bh = e / kAmxC;
+    float acc = 0.f;
+    if (c < C) {
+        const float* row = cent + (bh * C + c) * (int64_t)D;
+        for (int k = 0; k < D; ++k) acc = __builtin_fmaf(row[k], row[k], acc);
+    }
+    bias[e] = c < C ? (kmeans ? -0.5f * acc : 0.f) : -INFINITY;
+    cnorm[e] = sqrtf(acc) * (1.0f + 1.0f / 1024.0f);
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void k_assign_mx(const uint16_t* __restrict__ X,
+                                                   const float* __restrict__ cent,
+                                                   const float* __restrict__ bias,
+                                                   const float* __restrict__ cnorm,
+                                                   int32_t* __restrict__ assign, int N, int C) {
+    constexpr int ROW = D + 4;                     // floats per centroid row in LDS
+    __shared__ float cs[kAmxC * ROW];              // the head's centroids (fp32)
+    __shared__ float sb[kAmxC], sn[kAmxC];         // bias and norm bound
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int r32 = lane & 31, hf = lane >> 5;
+    const int64_t bh = blockIdx.y;
+    const int tok0 = blockIdx.x * 128 + wave * 32;
+    const int nct = (C + 31) / 32;                 // centroid tiles
+    const uint16_t* Xh = X + bh * (int64_t)N * D;
+    {
+        const float* ch = cent + bh * (int64_t)C * D;
+        for (int p = threadIdx.x; p < kAmxC * (D / 4); p += 256) {
+            const int c = p / (D / 4), o = p % (D / 4);
+            float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (c < C) v = reinterpret_cast<const float4*>(ch + (int64_t)c * D)[o];
+            *reinterpret_cast<float4*>(cs + c * ROW + 4 * o) = v;
+        }
+        if (threadIdx.x < kAmxC) {
+            sb[threadIdx.x] = bias[bh * kAmxC + threadIdx.x];
+            sn[threadIdx.x] = cnorm[bh * kAmxC + threadIdx.x];
+        }
+    }
+
+    // B operand (x^T) of the wave's 32 tokens: lane (r32, hf) holds channels
+    // 16 st + 8 hf .. + 7 of token r32, for st = 0 .. D/16 - 1
+    amx_bf16x8 xf[D / 16];
+    float nx;
+    {
+        const int t = min(tok0 + r32, N - 1);
+        const uint4* row = reinterpret_cast<const uint4*>(Xh + (int64_t)t * D);
+        float ss = 0.f;
+#pragma unroll
+        for (int st = 0; st < D / 16; ++st) {
+            const uint4 v = row[2 * st + hf];
+            xf[st] = __builtin_bit_cast(amx_bf16x8, v);
+            const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float a = __uint_as_float(w[e] << 16), b = __uint_as_float(w[e] & 0xffff0000u);
+                ss = __builtin_fmaf(a, a, ss);
+                ss = __builtin_fmaf(b, b, ss);
+            }
+        }
+        ss += __shfl_xor(ss, 32, 64);
+        nx = sqrtf(ss) * (1.0f + 1.0f / 1024.0f);
+    }
+    __syncthreads();
+
+    amx_f32x16 acc[2] = {amx_f32x16{}, amx_f32x16{}};
+#pragma unroll
+    for (int st = 0; st < D / 16; ++st) {
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) {
+            if (ct >= nct) break;
+            const float* cr = cs + (ct * 32 + r32) * ROW + 16 * st + 8 * hf;
+            float v[8];
+            *reinterpret_cast<float4*>(v) = *reinterpret_cast<const float4*>(cr);
+            *reinterpret_cast<float4*>(v + 4) = *reinterpret_cast<const float4*>(cr + 4);
+            uint32_t h[4], l[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const uint16_t h0 = amx_bf16(v[2 * e]), h1 = amx_bf16(v[2 * e + 1]);
+                const uint16_t l0 = amx_bf16(v[2 * e] - __uint_as_float((uint32_t)h0 << 16));
+                const uint16_t l1 = amx_bf16(v[2 * e + 1] - __uint_as_float((uint32_t)h1 << 16));
+                h[e] = h0 | ((uint32_t)h1 << 16);
+                l[e] = l0 | ((uint32_t)l1 << 16);
+            }
+            const amx_bf16x8 ah = __builtin_bit_cast(amx_bf16x8, make_uint4(h[0], h[1], h[2], h[3]));
+            const amx_bf16x8 al = __builtin_bit_cast(amx_bf16x8, make_uint4(l[0], l[1], l[2], l[3]));
+            acc[ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, xf[st], acc[ct], 0, 0, 0);
+            acc[ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, xf[st], acc[ct], 0, 0, 0);
+        }
+    }
+
+    // element r of tile ct: centroid ct*32 + 8 (r / 4) + 4 hf + r % 4, token r32.
+    // The token's best lower bound, then the mask of its candidates.
+    float thr = -INFINITY;
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct) {
+        if (ct >= nct) break;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int c = ct * 32 + 8 * (r / 4) + 4 * hf + (r % 4);
+            const float b = sb[c];
+            thr = fmaxf(thr, (acc[ct][r] + b) - kAmxEps * (nx * sn[c] + fabsf(b)));
+        }
+    }
+    thr = fmaxf(thr, __shfl_xor(thr, 32, 64));
+    uint64_t cand = 0;
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct) {
+        if (ct >= nct) break;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int c = ct * 32 + 8 * (r / 4) + 4 * hf + (r % 4);
+            const float b = sb[c];
+            const float hi = (acc[ct][r] + b) + kAmxEps * (nx * sn[c] + fabsf(b));
+            if (c < C && hi >= thr) cand |= 1ull << c;
+        }
+    }
+    cand |= __shfl_xor(cand, 32, 64);
+
+    // Exact decision arithmetic for the candidates, in ascending centroid
+    // order: the token's two lanes run the chain over the channels in order,
+    // 8 channels at a time, handing the partial sum across (lane hf = 0 holds
+    // channel groups 0, 2, 4, ...; hf = 1 groups 1, 3, 5, ...).
+    float best = -INFINITY;
+    int arg = 0;
+    for (;;) {
+        const uint64_t any = __ballot(cand != 0);
+        if (any == 0) break;
+        const bool act = cand != 0;
+        const int c = act ? __ffsll((long long)cand) - 1 : 0;
+        if (act) cand &= cand - 1;
+        const float* cr = cs + c * ROW + 8 * hf;
+        float a = 0.f;
+#pragma unroll
+        for (int st = 0; st < D / 16; ++st) {
+            const uint4 xv = __builtin_bit_cast(uint4, xf[st]);
+            const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
+            const float4 c0 = *reinterpret_cast<const float4*>(cr + 16 * st);
+            const float4 c1 = *reinterpret_cast<const float4*>(cr + 16 * st + 4);
+            const float cc[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+            // group 2 st (lane hf = 0), then group 2 st + 1 (lane hf = 1)
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+                float t = a;
+                if (hf == half) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        t = __builtin_fmaf(__uint_as_float(xw[e] << 16), cc[2 * e], t);
+                        t = __builtin_fmaf(__uint_as_float(xw[e] & 0xffff0000u), cc[2 * e + 1], t);
+                    }
+                }
+                // both lanes take the sum of the lane that just worked
+                const float o = __shfl_xor(t, 32, 64);
+                a = hf == half ? t : o;
+            }
+        }
+        if (act) {
+            const float sc = a + sb[c];
+            if (sc > best) {
+                best = sc;
+                arg = c;
+            }
+        }
+    }
+    const int t = tok0 + r32;
+    if (hf == 0 && t < N) assign[bh * N + t] = arg;
 }
 
 // ----------------------------------------------------------------------------
@@ -611,7 +817,7 @@ __global__ void k_block_comp(const float* __restrict__ k_cent, const float* __re
 // host side
 // ----------------------------------------------------------------------------
 struct ClusterWs {
-    size_t assign[2], sorted[2], hist, off, cstart[2], centT, bias, total;
+    size_t assign[2], sorted[2], hist, off, cstart[2], centT, bias, abias, cnorm, total;
 };
 
 inline int padded_c(int C) { return (C + kAsgIlp - 1) / kAsgIlp * kAsgIlp; }
@@ -629,6 +835,10 @@ ClusterWs cluster_ws(const Geometry& g, int C) {
     w.off = o; o = align_up(o + (size_t)g.BH() * ntiles * C * 4, 256);
     w.centT = o; o = align_up(o + (size_t)g.BH() * g.d * padded_c(C) * 4, 256);
     w.bias = o; o = align_up(o + (size_t)g.BH() * padded_c(C) * 4, 256);
+    if (C <= kAmxC) {
+        w.abias = o; o = align_up(o + (size_t)g.BH() * kAmxC * 4, 256);
+        w.cnorm = o; o = align_up(o + (size_t)g.BH() * kAmxC * 4, 256);
+    }
     w.total = o;
     return w;
 }
@@ -670,6 +880,17 @@ template <int D>
 sa_status assign_side(const Geometry& g, int C, char* ws, const ClusterWs& w, int s,
                       const uint16_t* X, const float* cent, int kmeans, hipStream_t st) {
     int32_t* assign = reinterpret_cast<int32_t*>(ws + w.assign[s]);
+    if (C <= kAmxC) {
+        float* ab = reinterpret_cast<float*>(ws + w.abias);
+        float* cn = reinterpret_cast<float*>(ws + w.cnorm);
+        hipLaunchKernelGGL(k_cent_bias, dim3((unsigned)ceil_div(g.BH() * kAmxC, 64)), dim3(64), 0,
+                           st, cent, ab, cn, C, D, kmeans, g.BH());
+        sa_status e = hip_check(hipGetLastError(), "k_cent_bias launch");
+        if (e != SA_OK) return e;
+        hipLaunchKernelGGL((k_assign_mx<D>), dim3((unsigned)ceil_div(g.N, 128), (unsigned)g.BH()),
+                           dim3(256), 0, st, X, cent, ab, cn, assign, g.N, C);
+        return hip_check(hipGetLastError(), "k_assign_mx launch");
+    }
     float* centT = reinterpret_cast<float*>(ws + w.centT);
     float* bias = reinterpret_cast<float*>(ws + w.bias);
     const int Cp = padded_c(C);

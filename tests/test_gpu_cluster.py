@@ -73,6 +73,9 @@ SMALL = {
         T=5, Hg=9, W=29, H=4, d=64, cluster="tiles", aniso=True,
         tile_shapes=((1, 4, 32), (1, 8, 16), (2, 4, 16), (5, 3, 8)), n_clusters=20,
         mass=0.8, comp=True, diag=True),
+    # more than 64 clusters: the assignment's vector-unit path
+    "kmeans_c100_mass_comp": BASE.replace(block=64, cluster="kmeans", n_clusters=100,
+                                          cluster_iters=2, mass=0.9, comp=True),
     # batches of two
     "kmeans_comp_batch2": BASE.replace(B=2, block=64, cluster="kmeans", n_clusters=6,
                                        cluster_iters=2, rule="topk", density=0.3, comp=True),
