@@ -4,7 +4,7 @@
 //
 // Per (batch, head) and per side (queries, keys):
 //   k_chunk_assign  initial partition: C equal chunks of the token order
-//   k_cent_bias + k_assign_mx (C <= 64), k_cent_prep + k_assign (larger C)
+//   k_assign_mx (C <= 64), k_cent_prep + k_assign (larger C)
 //                   every token to its best centroid: the largest
 //                   x.c (co-clustering affinity) or x.c - |c|^2/2 (k-means),
 //                   each dot product a sequential fp32 FMA chain over the
@@ -161,30 +161,11 @@ __device__ __forceinline__ uint32_t amx_ordered(float f) {
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// The centroids' decision bias (as k_cent_prep: fl32(-0.5 seqfma(c, c)) for
-// k-means, 0 for co-clustering, -inf for unused slots) and an upper bound of
-// their norm.  One thread per (slot, b*h).
-__global__ void k_cent_bias(const float* __restrict__ cent, float* __restrict__ bias,
-                            float* __restrict__ cnorm, int C, int D, int kmeans, int64_t BH) {
-    const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (e >= BH * kAmxC) return;
-    const int c = (int)(e % kAmxC);
-    const int64_t bh = e / kAmxC;
-    float acc = 0.f;
-    if (c < C) {
-        const float* row = cent + (bh * C + c) * (int64_t)D;
-        for (int k = 0; k < D; ++k) acc = __builtin_fmaf(row[k], row[k], acc);
-    }
-    bias[e] = c < C ? (kmeans ? -0.5f * acc : 0.f) : -INFINITY;
-    cnorm[e] = sqrtf(acc) * (1.0f + 1.0f / 1024.0f);
-}
-
 template <int D>
 __global__ __launch_bounds__(256) void k_assign_mx(const uint16_t* __restrict__ X,
                                                    const float* __restrict__ cent,
-                                                   const float* __restrict__ bias,
-                                                   const float* __restrict__ cnorm,
-                                                   int32_t* __restrict__ assign, int N, int C) {
+                                                   int32_t* __restrict__ assign, int N, int C,
+                                                   int kmeans) {
     constexpr int ROW = D + 4;                     // floats per centroid row in LDS
     __shared__ float cs[kAmxC * ROW];              // the head's centroids (fp32)
     __shared__ float sb[kAmxC], sn[kAmxC];         // bias and norm bound
@@ -202,10 +183,16 @@ __global__ __launch_bounds__(256) void k_assign_mx(const uint16_t* __restrict__ 
             if (c < C) v = reinterpret_cast<const float4*>(ch + (int64_t)c * D)[o];
             *reinterpret_cast<float4*>(cs + c * ROW + 4 * o) = v;
         }
-        if (threadIdx.x < kAmxC) {
-            sb[threadIdx.x] = bias[bh * kAmxC + threadIdx.x];
-            sn[threadIdx.x] = cnorm[bh * kAmxC + threadIdx.x];
-        }
+    }
+    __syncthreads();
+    if (threadIdx.x < kAmxC) {
+        // decision bias, as k_cent_prep: fl32(-0.5 seqfma(c, c)) for k-means,
+        // 0 for co-clustering, -inf for unused slots; a norm upper bound
+        const int c = threadIdx.x;
+        float acc = 0.f;
+        for (int k = 0; k < D; ++k) acc = __builtin_fmaf(cs[c * ROW + k], cs[c * ROW + k], acc);
+        sb[c] = c < C ? (kmeans ? -0.5f * acc : 0.f) : -INFINITY;
+        sn[c] = sqrtf(acc) * (1.0f + 1.0f / 1024.0f);
     }
 
     // B operand (x^T) of the wave's 32 tokens: lane (r32, hf) holds channels
@@ -817,7 +804,7 @@ __global__ void k_block_comp(const float* __restrict__ k_cent, const float* __re
 // host side
 // ----------------------------------------------------------------------------
 struct ClusterWs {
-    size_t assign[2], sorted[2], hist, off, cstart[2], centT, bias, abias, cnorm, total;
+    size_t assign[2], sorted[2], hist, off, cstart[2], centT, bias, total;
 };
 
 inline int padded_c(int C) { return (C + kAsgIlp - 1) / kAsgIlp * kAsgIlp; }
@@ -835,10 +822,6 @@ ClusterWs cluster_ws(const Geometry& g, int C) {
     w.off = o; o = align_up(o + (size_t)g.BH() * ntiles * C * 4, 256);
     w.centT = o; o = align_up(o + (size_t)g.BH() * g.d * padded_c(C) * 4, 256);
     w.bias = o; o = align_up(o + (size_t)g.BH() * padded_c(C) * 4, 256);
-    if (C <= kAmxC) {
-        w.abias = o; o = align_up(o + (size_t)g.BH() * kAmxC * 4, 256);
-        w.cnorm = o; o = align_up(o + (size_t)g.BH() * kAmxC * 4, 256);
-    }
     w.total = o;
     return w;
 }
@@ -881,14 +864,8 @@ sa_status assign_side(const Geometry& g, int C, char* ws, const ClusterWs& w, in
                       const uint16_t* X, const float* cent, int kmeans, hipStream_t st) {
     int32_t* assign = reinterpret_cast<int32_t*>(ws + w.assign[s]);
     if (C <= kAmxC) {
-        float* ab = reinterpret_cast<float*>(ws + w.abias);
-        float* cn = reinterpret_cast<float*>(ws + w.cnorm);
-        hipLaunchKernelGGL(k_cent_bias, dim3((unsigned)ceil_div(g.BH() * kAmxC, 64)), dim3(64), 0,
-                           st, cent, ab, cn, C, D, kmeans, g.BH());
-        sa_status e = hip_check(hipGetLastError(), "k_cent_bias launch");
-        if (e != SA_OK) return e;
         hipLaunchKernelGGL((k_assign_mx<D>), dim3((unsigned)ceil_div(g.N, 128), (unsigned)g.BH()),
-                           dim3(256), 0, st, X, cent, ab, cn, assign, g.N, C);
+                           dim3(256), 0, st, X, cent, assign, g.N, C, kmeans);
         return hip_check(hipGetLastError(), "k_assign_mx launch");
     }
     float* centT = reinterpret_cast<float*>(ws + w.centT);
