@@ -294,20 +294,37 @@ __device__ __forceinline__ void process_row(const FwdArgs& a, int64_t row, unsig
         // op k: S step k/2 (even) and PV step k/2 (odd) when both run
         auto is_s = [&](int k) { return DS && (!DP || (k & 1) == 0); };
         auto step = [&](int k) { return DS && DP ? k >> 1 : k; };
+        // Operand addresses by XOR.  The slots start 256-byte aligned, so a K
+        // row starts KRB-aligned; its 16-byte chunk c sits at position
+        // c ^ (row & (KCH - 1)), and the row's low bits are those of
+        // swap23(r32) (kh KH + 32 kt is a multiple of KCH).  Chunk 2 st + h of
+        // row kh KH + 32 kt + swap23(r32) is therefore at kbase ^ (32 st) +
+        // 32 kt KRB, where kbase holds the lane's row and 16 (h ^ (row &
+        // (KCH - 1))); the XOR only touches bits below KRB.  V^T row
+        // d = 32 dt + r32, key chunk 2 m + h: vbase ^ (32 m) + 32 dt VRB.  One
+        // XOR per read and two base registers per phase.
+        const uint32_t ks32 = (uint32_t)(uintptr_t)(const lds_void_t*)Ks;
+        const uint32_t vs32 = (uint32_t)(uintptr_t)(const lds_void_t*)Vs;
+        uint32_t kbase = ks32 + (uint32_t)((kh * C::KH + swap23(r32)) * C::KRB) +
+                               16u * (uint32_t)(h ^ (swap23(r32) & (C::KCH - 1)));
+        uint32_t vbase = vs32 + (uint32_t)(r32 * C::VRB) + 16u * (uint32_t)(h ^ (r32 & (C::VCH - 1)));
+        // opaque to the optimiser: the per-read XORs are formed here, each
+        // phase, instead of being hoisted out of the tile loop into registers
+        asm volatile("" : "+v"(kbase), "+v"(vbase));
+        auto lds16 = [](uint32_t addr) -> bf16x8 {
+            typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+            return __builtin_bit_cast(bf16x8, *reinterpret_cast<const __attribute__((address_space(3))) u32x4_t*>((uintptr_t)addr));
+        };
         auto load = [&](int k) -> bf16x8 {
             const int u = step(k);
             if (is_s(k)) {
                 const int kt = u % C::KTW, st = u / C::KTW;
-                const int krow = kh * C::KH + kt * 32 + swap23(r32);
-                const int pos = (st * 2 + h) ^ (krow & (C::KCH - 1));
-                return as_bf16x8(*reinterpret_cast<const uint4*>(Ks + krow * C::KRB + pos * 16));
+                return lds16((kbase ^ (32u * st)) + (uint32_t)(kt * 32 * C::KRB));
             }
             const int dt = u % (D / 32), q = u / (D / 32);
             const int kt = q >> 1, s2 = q & 1;
-            const int d = dt * 32 + r32;
-            const int chunk = (kh * C::KH + kt * 32 + 16 * s2 + 8 * h) / 8;
-            const int pos = chunk ^ (d & (C::VCH - 1));
-            return as_bf16x8(*reinterpret_cast<const uint4*>(Vs + d * C::VRB + pos * 16));
+            const int m = (kh * C::KH + kt * 32 + 16 * s2) / 16;      // chunk pair of the 16 keys
+            return lds16((vbase ^ (32u * m)) + (uint32_t)(dt * 32 * C::VRB));
         };
         bf16x8 ring[PF];
 #pragma unroll
@@ -494,7 +511,9 @@ __device__ __forceinline__ void process_row(const FwdArgs& a, int64_t row, unsig
 template <int D, int BLK, bool COMP>
 __global__ __launch_bounds__(BLK * 4) __attribute__((amdgpu_waves_per_eu(2)))
 void k_bsattn_fwd(FwdArgs a) {
-    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
+    // the tile slots start 256-byte aligned: operand addresses are formed by XOR
+    unsigned char* smem = smem_raw + ((256u - ((uint32_t)(uintptr_t)(lds_void_t*)smem_raw & 255u)) & 255u);
     __shared__ int s_row;
     // block token counts from the caller (else the fixed layout's)
     const bool var_cnt = __builtin_amdgcn_readfirstlane(a.sched[24]) != 0;
@@ -741,10 +760,10 @@ template <int D, int BLK, bool COMP>
 sa_status run_t(const FwdArgs& a, const Geometry& g, hipStream_t stream) {
     using C = Cfg<D, BLK>;
     sa_status st = SA_OK;
-    const size_t lds = C::BASE + C::MAX_NB + 4 * (size_t)g.nb + (COMP ? 4 * (BLK + 1) : 0);
+    const size_t lds = 256 + C::BASE + C::MAX_NB + 4 * (size_t)g.nb + (COMP ? 4 * (BLK + 1) : 0);
     static bool configured = false;
     if (!configured) {
-        const int most = C::BASE + C::MAX_NB + 4 * C::MAX_NB + 4 * (BLK + 1);
+        const int most = 256 + C::BASE + C::MAX_NB + 4 * C::MAX_NB + 4 * (BLK + 1);
         st = hip_check(hipFuncSetAttribute((const void*)k_bsattn_fwd<D, BLK, COMP>,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, most),
                        "k_bsattn_fwd shared memory");
