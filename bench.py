@@ -167,6 +167,9 @@ def main():
                     help="mask reuse: select on every r-th call only, the calls in between "
                          "keep the mask (compensation centroids still from their own K, V)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--graph", action="store_true",
+                    help="data-dependent blocks: time the calls as HIP graph replays "
+                         "(stage times still come from eager calls)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
@@ -338,6 +341,19 @@ def bench_clusters(args, wl, Q, K, V, Qd, Kd, Vd):
     prep_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in ev]))
     fwd_ms = float(np.mean([e[3].elapsed_time(e[4]) for e in ev]))
     log(f"[bench] {args.steps} steps: {step_s * 1e3:.3f} ms/step")
+    eager_s = step_s
+    if args.graph:
+        from block_sparse_attention_hilbert_amd.pipeline import GraphedCall
+        graphed = GraphedCall(pipe, Qd, Kd, Vd)
+        for _ in range(args.warmup):
+            graphed()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            graphed()
+        torch.cuda.synchronize()
+        step_s = (time.perf_counter() - t0) / args.steps
+        log(f"[bench] {args.steps} graph replays: {step_s * 1e3:.3f} ms/step")
     # kept work in true tokens: q tokens of each padded query block times the
     # key tokens of the blocks it keeps
     kept = pipe.kept_tokens().cpu().numpy().astype(np.float64)
@@ -369,10 +385,12 @@ def bench_clusters(args, wl, Q, K, V, Qd, Kd, Vd):
                                                (wl.B * wl.H * float(wl.N) ** 2), 4),
                    "padding_fraction": round(1.0 - wl.B * wl.H * wl.N / slots, 4),
                    "compensation": wl.comp, "partition_refresh_every": args.refresh_every,
+                   "launch": "hip graph replay" if args.graph else "eager",
                    "parallelism": "single GPU"},
         "tile_shape_per_head": (None if pipe.shape_idx is None else
                                 [list(wl.tile_shapes[i]) for i in pipe.shape_idx.cpu().tolist()]),
         "clusterings_timed": int(sum(selected[args.warmup:])),
+        "ms_per_step_eager": round(eager_s * 1e3, 4),
         "ms_cluster": round(cl_ms, 4),
         "ms_gather_select": round(gs_ms, 4),
         "ms_select": round(sel_s * 1e3, 4),

@@ -287,3 +287,49 @@ class ClusteredAttention:
         rows = torch.repeat_interleave(torch.arange(pp.rows, device=rp.device), rp[1:] - rp[:-1])
         out.index_add_(0, rows, per)
         return out
+
+
+class GraphedCall:
+    """A pipeline's call captured as HIP graphs and replayed.
+
+    One graph per variant of the call: forming the selection (or partition)
+    anew and keeping it.  A replay enqueues every kernel of the call with one
+    host launch instead of one per kernel.  It reads the input tensors given
+    here (the caller copies each step's data into them) and writes the
+    pipeline's own output buffers (``pipe.O``, ``pipe.lse``).  Each variant is
+    first run once eagerly on a side stream, so the library's one-time set-up
+    (kernel attributes, occupancy queries) happens outside the capture; the
+    library enqueues no memset, copy, allocation or host synchronisation, so
+    the whole call is capturable.  Calls through the graphs and eager calls of
+    the same pipeline can be mixed: both follow ``pipe.calls``.
+    """
+
+    def __init__(self, pipe, Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor):
+        self.pipe = pipe
+        self.inputs = (Q, K, V)
+        kw = "reuse" if isinstance(pipe, ClusteredAttention) else "reuse_mask"
+        self._run = lambda keep: pipe(Q, K, V, **{kw: keep})
+        calls = pipe.calls
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for keep in (False, True):        # forming first: keeping needs a selection
+                self._run(keep)
+        torch.cuda.current_stream().wait_stream(side)
+        self.graphs = {}
+        for keep in (False, True):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                self._run(keep)
+            self.graphs[keep] = g
+        pipe.calls = calls
+
+    def __call__(self, keep: Optional[bool] = None) -> torch.Tensor:
+        """One call: ``keep`` the last selection / partition (True), form it
+        anew (False) or follow the pipeline's refresh policy (None)."""
+        p = self.pipe
+        if keep is None:
+            keep = p.reuses_next()
+        self.graphs[bool(keep)].replay()
+        p.calls += 1
+        return p.O
