@@ -14,7 +14,10 @@
 //             index asc), top-k or cumulative-mass cut (SVG-EAR page, sections
 //             2B and 4; SVOO page, section 2A), union with the diagonal, the
 //             temporal window and the rotating anchors (LVSA abstract); writes
-//             a kept-block bitmap and count.
+//             a kept-block bitmap and count.  k_select_w takes the same
+//             decision with one wave per query block (rows of up to 2048
+//             blocks): radix select for top-k, a register sort for the mass
+//             rule.
 //   k_scan    exclusive scan of the counts -> CSR row pointers.
 //   k_expand  bitmap -> ascending column indices.
 #include <math.h>
@@ -206,6 +209,7 @@ struct SelectArgs {
     float mass;
     int32_t diag, window_frames, n_anchors;
     int64_t anchor_offset;
+    int64_t rows;
 };
 
 // Monotone map of fp32 to uint32 (ascending), with -0 and +0 equal.
@@ -321,6 +325,251 @@ __global__ __launch_bounds__(kThreads) void k_select(SelectArgs a) {
     if (local) atomicAdd(&s_count, local);
     __syncthreads();
     if (tid == 0) a.counts[row] = s_count;
+}
+
+// ----------------------------------------------------------------------------
+// k_select_w: the same decision, one wave per query block (nb <= 2048)
+// ----------------------------------------------------------------------------
+// The row's sort keys (score descending, index ascending, as one ascending
+// uint64) sit in registers, E per lane: element e is lane e / E, register
+// e % E.  Top-k needs only the set of the k smallest keys: a radix select over
+// the key's bytes (LDS histogram per wave), stopping once the k-th key's
+// bucket holds exactly the keys still wanted.  The mass rule needs the rank
+// order: a bitonic sort over the registers (lane shuffles for strides of E or
+// more), then p_r = exp(S_r - S_max) in fp64 per element and the cumulative
+// sum taken strictly in rank order by one scalar chain (total first, then the
+// cut), exactly as the workgroup kernel does.  No workgroup barriers.
+constexpr int kSelWaves = kThreads / 64;   // rows per workgroup
+constexpr int kSelMaxWords = 64;           // bitmap words per row
+
+__device__ __forceinline__ float ordered_to_float(uint32_t o) {
+    return __uint_as_float((o & 0x80000000u) ? (o & 0x7fffffffu) : ~o);
+}
+
+// x of lane ^ M: DPP quad permutes for M = 1, 2 (no LDS round trip), the
+// LDS crossbar's swizzle (bit-mask mode) for M = 4 .. 16, the half-wave swap
+// for M = 32
+template <int M>
+__device__ __forceinline__ uint32_t xor_lane(uint32_t x) {
+    if constexpr (M == 1)
+        return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0xB1, 0xF, 0xF, false);   // [1,0,3,2]
+    else if constexpr (M == 2)
+        return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x4E, 0xF, 0xF, false);   // [2,3,0,1]
+    else if constexpr (M < 32)
+        return (uint32_t)__builtin_amdgcn_ds_swizzle((int)x, (M << 10) | 0x1F);
+    else {
+        const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+        return r[0] == x ? r[1] : r[0];
+    }
+}
+
+template <int M>
+__device__ __forceinline__ uint64_t xor_lane_u64(uint64_t v) {
+    const uint32_t lo = xor_lane<M>((uint32_t)v);
+    const uint32_t hi = xor_lane<M>((uint32_t)(v >> 32));
+    return ((uint64_t)hi << 32) | lo;
+}
+
+// one compare-exchange stage across lanes (partner lane ^ M)
+template <int E, int M>
+__device__ __forceinline__ void cross_stage(uint64_t (&k)[E], int lane, int size, int stride) {
+#pragma unroll
+    for (int r = 0; r < E; ++r) {
+        const int e = lane * E + r;
+        const uint64_t o = xor_lane_u64<M>(k[r]);
+        const bool take_min = ((e & stride) == 0) == ((e & size) == 0);
+        const uint64_t mn = o < k[r] ? o : k[r], mx = o < k[r] ? k[r] : o;
+        k[r] = take_min ? mn : mx;
+    }
+}
+
+// ascending bitonic sort of the wave's 64 E keys
+template <int E>
+__device__ __forceinline__ void wave_sort(uint64_t (&k)[E], int lane) {
+    constexpr int P = 64 * E;
+#pragma unroll
+    for (int size = 2; size <= P; size <<= 1) {
+#pragma unroll
+        for (int stride = size >> 1; stride > 0; stride >>= 1) {
+            if (stride >= E) {
+                switch (stride / E) {
+                case 1: cross_stage<E, 1>(k, lane, size, stride); break;
+                case 2: cross_stage<E, 2>(k, lane, size, stride); break;
+                case 4: cross_stage<E, 4>(k, lane, size, stride); break;
+                case 8: cross_stage<E, 8>(k, lane, size, stride); break;
+                case 16: cross_stage<E, 16>(k, lane, size, stride); break;
+                default: cross_stage<E, 32>(k, lane, size, stride); break;
+                }
+            } else {
+#pragma unroll
+                for (int r = 0; r < E; ++r) {
+                    if (r & stride) continue;
+                    const bool up = ((lane * E + r) & size) == 0;
+                    const uint64_t x = k[r], y = k[r + stride];
+                    const bool sw = (x > y) == up;
+                    k[r] = sw ? y : x;
+                    k[r + stride] = sw ? x : y;
+                }
+            }
+        }
+    }
+}
+
+template <int E>
+__global__ __launch_bounds__(kThreads) void k_select_w(SelectArgs a) {
+    __shared__ uint32_t s_bits[kSelWaves][kSelMaxWords];
+    __shared__ uint32_t s_hist[kSelWaves][256];
+    extern __shared__ double s_cum[];                  // mass rule: [kSelWaves][64 E]
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int64_t row = (int64_t)blockIdx.x * kSelWaves + wv;
+    if (row >= a.rows) return;
+    const int nb = a.nb;
+    const int i = (int)(row % nb);
+    const int h = (int)((row / nb) % a.H);
+    uint32_t* bits = s_bits[wv];
+    for (int w = lane; w < kSelMaxWords; w += 64) bits[w] = 0;
+    auto mark = [&](int j) {
+        if ((uint32_t)j < (uint32_t)nb) atomicOr(&bits[j >> 5], 1u << (j & 31));
+    };
+
+    if (a.rule != SA_RULE_NONE) {
+        const float* S = a.S + row * (int64_t)nb;
+        uint64_t k[E];
+#pragma unroll
+        for (int r = 0; r < E; ++r) {
+            const int j = lane * E + r;
+            k[r] = j < nb ? ((uint64_t)(~ordered_bits(S[j])) << 32) | (uint32_t)j : ~0ull;
+        }
+        if (a.rule == SA_RULE_TOPK) {
+            int m = a.H <= kInlineHeads ? a.k_inline[h] : a.k_head[h];
+            m = m < 0 ? 0 : (m > nb ? nb : m);
+            if (m > 0) {
+                uint32_t* hist = s_hist[wv];
+                uint64_t prefix = 0, mask = 0;
+                uint32_t krem = (uint32_t)m;
+                for (int pass = 0; pass < 8; ++pass) {
+                    const int sh = 56 - 8 * pass;
+                    for (int b = lane; b < 256; b += 64) hist[b] = 0;
+#pragma unroll
+                    for (int r = 0; r < E; ++r)
+                        if ((k[r] & mask) == prefix) atomicAdd(&hist[(uint32_t)(k[r] >> sh) & 255u], 1u);
+                    uint32_t c[4];
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) c[q] = hist[lane * 4 + q];
+                    const uint32_t lsum = c[0] + c[1] + c[2] + c[3];
+                    uint32_t incl = lsum;
+#pragma unroll
+                    for (int off = 1; off < 64; off <<= 1) {
+                        const uint32_t y = (uint32_t)__shfl_up((int)incl, off, 64);
+                        if (lane >= off) incl += y;
+                    }
+                    // the lane holding the bucket of the krem-th candidate
+                    const int L = __ffsll((unsigned long long)__ballot(incl >= krem)) - 1;
+                    uint32_t below = (uint32_t)__builtin_amdgcn_readlane((int)(incl - lsum), L);
+                    int b = 0;
+                    uint32_t cb = 0;
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const uint32_t cq = (uint32_t)__builtin_amdgcn_readlane((int)c[q], L);
+                        if (cb == 0 && below + cq >= krem) {
+                            b = L * 4 + q;
+                            cb = cq;
+                        } else if (cb == 0) {
+                            below += cq;
+                        }
+                    }
+                    krem -= below;
+                    prefix |= (uint64_t)b << sh;
+                    mask |= (uint64_t)255 << sh;
+                    if (cb == krem) break;   // the whole bucket is kept
+                }
+#pragma unroll
+                for (int r = 0; r < E; ++r)
+                    if ((k[r] & mask) <= prefix) mark((int)(uint32_t)k[r]);
+            }
+        } else {
+            wave_sort<E>(k, lane);
+            // p_r = exp(S_r - S_max) in fp64, rank r = lane E + reg
+            const double smax =
+                (double)ordered_to_float(~(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(k[0] >> 32)));
+            double* cum = s_cum + wv * 64 * E;
+#pragma unroll
+            for (int r = 0; r < E; ++r)
+                cum[lane * E + r] =
+                    lane * E + r < nb ? exp((double)ordered_to_float(~(uint32_t)(k[r] >> 32)) - smax) : 0.0;
+            // the running sum strictly in rank order, by one lane, 8 values
+            // per LDS round trip; the ranks past nb add +0.0, which leaves a
+            // non-negative sum unchanged
+            if (lane == 0) {
+                double run = 0.0;
+                for (int c = 0; c < nb; c += 8) {
+                    double v[8];
+#pragma unroll
+                    for (int q = 0; q < 8; ++q) v[q] = cum[c + q];
+#pragma unroll
+                    for (int q = 0; q < 8; ++q) {
+                        run += v[q];
+                        v[q] = run;
+                    }
+#pragma unroll
+                    for (int q = 0; q < 8; ++q) cum[c + q] = v[q];
+                }
+            }
+            // the cut: the first rank whose running sum reaches mass x total
+            const double thr = (double)a.mass * cum[nb - 1];
+            int first = E;
+#pragma unroll
+            for (int r = E - 1; r >= 0; --r)
+                if (lane * E + r < nb && cum[lane * E + r] >= thr) first = r;
+            const uint64_t hit = __ballot(first < E);
+            int m = nb;
+            if (hit) {
+                const int L = __ffsll((unsigned long long)hit) - 1;
+                m = L * E + __builtin_amdgcn_readlane(first, L) + 1;
+            }
+#pragma unroll
+            for (int r = 0; r < E; ++r)
+                if (lane * E + r < m) mark((int)(uint32_t)k[r]);
+        }
+    }
+
+    if (a.diag && lane == 0) mark(i);
+    if (a.window_frames >= 0) {
+        // the blocks whose frames meet [lo_i - r, hi_i + r]: a block's first
+        // and last frame grow with its index, so they form one range [jb, ja]
+        const int r = a.window_frames;
+        const int lo_i = (i * a.block) / a.HgW;
+        const int hi_i = (min(a.N, (i + 1) * a.block) - 1) / a.HgW;
+        const int A = hi_i + r, B = lo_i - r;
+        int ja = -1, jb = 0;
+        if (A >= 0) ja = min(nb - 1, (int)(((int64_t)(A + 1) * a.HgW - 1) / a.block));
+        if (B > 0) {
+            const int64_t t = (int64_t)B * a.HgW + 1;
+            jb = t > a.N ? nb : (int)((t + a.block - 1) / a.block) - 1;
+        }
+        for (int w = lane; w < a.words; w += 64) {
+            const int b0 = max(jb, 32 * w), b1 = min(ja, 32 * w + 31);
+            if (b0 <= b1) {
+                const int n = b1 - b0 + 1;
+                const uint32_t m = (n == 32 ? ~0u : ((1u << n) - 1u)) << (b0 - 32 * w);
+                atomicOr(&bits[w], m);
+            }
+        }
+    }
+    if (a.n_anchors > 0) {
+        const int64_t step = nb / a.n_anchors;
+        for (int m = lane; m < a.n_anchors; m += 64) mark((int)((a.anchor_offset + m * step) % nb));
+    }
+    uint32_t* out = a.bits + row * (int64_t)a.words;
+    int local = 0;
+    for (int w = lane; w < a.words; w += 64) {
+        const uint32_t word = bits[w];
+        out[w] = word;
+        local += __popc(word);
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) local += __shfl_xor(local, off, 64);
+    if (lane == 0) a.counts[row] = local;
 }
 
 // ----------------------------------------------------------------------------
@@ -600,9 +849,38 @@ sa_status launch_select(const Geometry& g, const SelectPlan& p, const int32_t* k
     sa.block = g.block; sa.HgW = g.Hg * g.W; sa.rule = err ? SA_RULE_TOPK : p.rule; sa.mass = p.mass;
     sa.diag = p.diag; sa.window_frames = p.window_frames; sa.n_anchors = p.n_anchors;
     sa.anchor_offset = p.anchor_offset;
-    const size_t lds = scored ? (size_t)p.nb_pad * 12 + (size_t)p.words * 32
-                              : (size_t)p.words * 32 + 16;
-    hipLaunchKernelGGL(k_select, dim3((unsigned)g.rows()), dim3(kThreads), lds, stream, sa);
+    sa.rows = g.rows();
+    if (p.nb_pad <= 64 * 32) {
+        // one wave per row, E = nb_pad / 64 keys per lane
+        const dim3 grid((unsigned)ceil_div(g.rows(), kSelWaves));
+        // without scores no keys are held: the one-key build
+        const int E = !scored || p.nb_pad <= 64 ? 1 : p.nb_pad / 64;
+        // mass rule: the running sums of each wave's row in LDS
+        const size_t lds = p.rule == SA_RULE_MASS ? (size_t)kSelWaves * 64 * E * sizeof(double) : 0;
+        if (E == 32 && lds > 0) {
+            static bool configured = false;
+            if (!configured) {
+                st = hip_check(hipFuncSetAttribute((const void*)k_select_w<32>,
+                                                   hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                   (int)lds),
+                               "k_select shared memory");
+                if (st != SA_OK) return st;
+                configured = true;
+            }
+        }
+        switch (E) {
+        case 1: hipLaunchKernelGGL(k_select_w<1>, grid, dim3(kThreads), lds, stream, sa); break;
+        case 2: hipLaunchKernelGGL(k_select_w<2>, grid, dim3(kThreads), lds, stream, sa); break;
+        case 4: hipLaunchKernelGGL(k_select_w<4>, grid, dim3(kThreads), lds, stream, sa); break;
+        case 8: hipLaunchKernelGGL(k_select_w<8>, grid, dim3(kThreads), lds, stream, sa); break;
+        case 16: hipLaunchKernelGGL(k_select_w<16>, grid, dim3(kThreads), lds, stream, sa); break;
+        default: hipLaunchKernelGGL(k_select_w<32>, grid, dim3(kThreads), lds, stream, sa); break;
+        }
+    } else {
+        const size_t lds = scored ? (size_t)p.nb_pad * 12 + (size_t)p.words * 32
+                                  : (size_t)p.words * 32 + 16;
+        hipLaunchKernelGGL(k_select, dim3((unsigned)g.rows()), dim3(kThreads), lds, stream, sa);
+    }
     if ((st = hip_check(hipGetLastError(), "k_select launch")) != SA_OK) return st;
 
     // 4. CSR
