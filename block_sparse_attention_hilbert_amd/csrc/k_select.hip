@@ -119,27 +119,35 @@ __global__ __launch_bounds__(kThreads) void k_pool(PoolArgs a) {
 // ----------------------------------------------------------------------------
 // k_score
 // ----------------------------------------------------------------------------
-constexpr int kTile = 16;   // 16 x 16 block pairs per workgroup
+constexpr int kTile = 16;   // 16 x 16 threads per workgroup
 
-template <int D, int SPB>
+// Thread (ti, tj) of a workgroup takes the MT x MT block pairs (ti + 16 a,
+// tj + 16 b) of its 16 MT x 16 MT tile; the unit means of the tile's query
+// and key blocks are staged in LDS (rows padded by 4 floats, so the 16 key
+// rows a wave reads at once fall in distinct banks).  Each pair's dot
+// product stays one sequential fp32 FMA chain over the channels; the channel
+// loop is unrolled so that the operand reads of the next step are issued
+// under the FMAs of the current one.
+template <int D, int SPB, int MT>
 __global__ __launch_bounds__(kThreads) void k_score(const float* __restrict__ qm,
                                                     const float* __restrict__ km,
                                                     float* __restrict__ S, int nb,
                                                     int n_units, float scale) {
     constexpr int ROW = SPB * D + 4;      // floats per block row in LDS (+4: bank shift)
+    constexpr int TB = kTile * MT;        // blocks per tile side
     extern __shared__ float lds[];
-    float* qs = lds;                      // [kTile][ROW]
-    float* ks = lds + kTile * ROW;        // [kTile][ROW]
+    float* qs = lds;                      // [TB][ROW]
+    float* ks = lds + TB * ROW;           // [TB][ROW]
 
     const int64_t bh = blockIdx.z;
-    const int i0 = blockIdx.y * kTile, j0 = blockIdx.x * kTile;
+    const int i0 = blockIdx.y * TB, j0 = blockIdx.x * TB;
     const int tid = threadIdx.x;
     const float* qb = qm + bh * (int64_t)n_units * D;
     const float* kb = km + bh * (int64_t)n_units * D;
 
-    // stage the unit means of 16 query blocks and 16 key blocks (float4)
+    // stage the unit means of TB query blocks and TB key blocks (float4)
     constexpr int V4 = SPB * D / 4;
-    for (int p = tid; p < kTile * V4; p += kThreads) {
+    for (int p = tid; p < TB * V4; p += kThreads) {
         const int b = p / V4, o = p % V4;
         const int u = o / (D / 4);                      // unit within the block
         float4 qv = make_float4(0.f, 0.f, 0.f, 0.f), kv = qv;
@@ -153,44 +161,59 @@ __global__ __launch_bounds__(kThreads) void k_score(const float* __restrict__ qm
     __syncthreads();
 
     const int ti = tid / kTile, tj = tid % kTile;
-    const int i = i0 + ti, j = j0 + tj;
-    if (i >= nb || j >= nb) return;
-    const int nu_i = min(SPB, n_units - i * SPB);       // units that exist
-    const int nu_j = min(SPB, n_units - j * SPB);
-    const float* q = qs + ti * ROW;
-    const float* k = ks + tj * ROW;
-
-    float acc[SPB][SPB];
+    float acc[MT][MT][SPB][SPB];
 #pragma unroll
-    for (int x = 0; x < SPB; ++x)
+    for (int a = 0; a < MT; ++a)
 #pragma unroll
-        for (int y = 0; y < SPB; ++y) acc[x][y] = 0.f;
+        for (int b = 0; b < MT; ++b)
+#pragma unroll
+            for (int x = 0; x < SPB; ++x)
+#pragma unroll
+                for (int y = 0; y < SPB; ++y) acc[a][b][x][y] = 0.f;
+    // with many pairs per thread a full unroll would hoist every operand read
+    constexpr int UNR = MT == 1 ? D / 4 : 4;
+#pragma unroll(UNR)
     for (int c = 0; c < D; c += 4) {
-        float4 qv[SPB], kv[SPB];
+        float4 qv[MT][SPB], kv[MT][SPB];
 #pragma unroll
-        for (int x = 0; x < SPB; ++x) {
-            qv[x] = *reinterpret_cast<const float4*>(q + x * D + c);
-            kv[x] = *reinterpret_cast<const float4*>(k + x * D + c);
-        }
+        for (int a = 0; a < MT; ++a)
 #pragma unroll
-        for (int x = 0; x < SPB; ++x)
-#pragma unroll
-            for (int y = 0; y < SPB; ++y) {
-                float s = acc[x][y];
-                s = __builtin_fmaf(qv[x].x, kv[y].x, s);
-                s = __builtin_fmaf(qv[x].y, kv[y].y, s);
-                s = __builtin_fmaf(qv[x].z, kv[y].z, s);
-                s = __builtin_fmaf(qv[x].w, kv[y].w, s);
-                acc[x][y] = s;
+            for (int x = 0; x < SPB; ++x) {
+                qv[a][x] = *reinterpret_cast<const float4*>(qs + (ti + kTile * a) * ROW + x * D + c);
+                kv[a][x] = *reinterpret_cast<const float4*>(ks + (tj + kTile * a) * ROW + x * D + c);
             }
+#pragma unroll
+        for (int a = 0; a < MT; ++a)
+#pragma unroll
+            for (int b = 0; b < MT; ++b)
+#pragma unroll
+                for (int x = 0; x < SPB; ++x)
+#pragma unroll
+                    for (int y = 0; y < SPB; ++y) {
+                        float s = acc[a][b][x][y];
+                        s = __builtin_fmaf(qv[a][x].x, kv[b][y].x, s);
+                        s = __builtin_fmaf(qv[a][x].y, kv[b][y].y, s);
+                        s = __builtin_fmaf(qv[a][x].z, kv[b][y].z, s);
+                        s = __builtin_fmaf(qv[a][x].w, kv[b][y].w, s);
+                        acc[a][b][x][y] = s;
+                    }
     }
-    float best = -INFINITY;
 #pragma unroll
-    for (int x = 0; x < SPB; ++x)
+    for (int a = 0; a < MT; ++a)
 #pragma unroll
-        for (int y = 0; y < SPB; ++y)
-            if (x < nu_i && y < nu_j) best = fmaxf(best, scale * acc[x][y]);
-    S[(bh * nb + i) * (int64_t)nb + j] = best;
+        for (int b = 0; b < MT; ++b) {
+            const int i = i0 + ti + kTile * a, j = j0 + tj + kTile * b;
+            if (i >= nb || j >= nb) continue;
+            const int nu_i = min(SPB, n_units - i * SPB);       // units that exist
+            const int nu_j = min(SPB, n_units - j * SPB);
+            float best = -INFINITY;
+#pragma unroll
+            for (int x = 0; x < SPB; ++x)
+#pragma unroll
+                for (int y = 0; y < SPB; ++y)
+                    if (x < nu_i && y < nu_j) best = fmaxf(best, scale * acc[a][b][x][y]);
+            S[(bh * nb + i) * (int64_t)nb + j] = best;
+        }
 }
 
 // ----------------------------------------------------------------------------
@@ -677,16 +700,19 @@ void launch_pool_t(const PoolArgs& a, int nroles, int64_t BH, int nb, hipStream_
 template <int D, int SPB>
 sa_status launch_score_t(const float* qm, const float* km, float* S, int nb, int n_units,
                          float scale, int64_t BH, hipStream_t s) {
-    const dim3 grid((nb + kTile - 1) / kTile, (nb + kTile - 1) / kTile, (unsigned)BH);
-    const size_t lds = 2 * kTile * (SPB * D + 4) * sizeof(float);
+    // two by two block pairs per thread when a block has one or two units
+    constexpr int MT = SPB <= 2 ? 2 : 1;
+    constexpr int TB = kTile * MT;
+    const dim3 grid((nb + TB - 1) / TB, (nb + TB - 1) / TB, (unsigned)BH);
+    const size_t lds = 2 * TB * (SPB * D + 4) * sizeof(float);
     if (lds > 65536) {
-        sa_status st = hip_check(hipFuncSetAttribute((const void*)k_score<D, SPB>,
+        sa_status st = hip_check(hipFuncSetAttribute((const void*)k_score<D, SPB, MT>,
                                                      hipFuncAttributeMaxDynamicSharedMemorySize,
                                                      (int)lds),
                                  "k_score shared memory");
         if (st != SA_OK) return st;
     }
-    hipLaunchKernelGGL((k_score<D, SPB>), grid, dim3(kThreads), lds, s, qm, km, S, nb, n_units,
+    hipLaunchKernelGGL((k_score<D, SPB, MT>), grid, dim3(kThreads), lds, s, qm, km, S, nb, n_units,
                        scale);
     return hip_check(hipGetLastError(), "k_score launch");
 }
