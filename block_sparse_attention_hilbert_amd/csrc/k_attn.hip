@@ -130,7 +130,7 @@ struct Cfg {
     static constexpr int VI = V_BYTES / (1024 * NWI);
     static constexpr int NSTEP = KTW * D / 16;      // MFMAs of each product per tile
     static constexpr int SLOTS = 2 * K_BYTES + 2 * V_BYTES;
-    static constexpr int MERGE = NWQ * ((D / 32) * 64 * 16 * 4 + 2 * 32 * 4);
+    static constexpr int MERGE = NWQ * ((D / 32) * 64 * 16 * 4 + 2 * 64 * 4);
     static constexpr int BASE = SLOTS > MERGE ? SLOTS : MERGE;
     static constexpr int MAX_NB = 4096;                 // list / flag capacity
     static_assert(KI * 1024 * NWI == K_BYTES && VI * 1024 * NWI == V_BYTES, "whole wave slices");
@@ -457,49 +457,92 @@ __device__ __forceinline__ void process_row(const FwdArgs& a, int64_t row, unsig
         if (C::PING && !lagging) wg_barrier();
     }
 
-    // merge the two key halves of every query group, then write O and lse
+    // Merge the two key halves of every query group.  Wave kh finalises the
+    // output channel tiles dt in [kh HD, kh HD + HD) and takes the partner's
+    // partial sums of those tiles from LDS (the sum of the two scaled halves
+    // is the same either way round).  The two lanes of a query (h = 0, 1)
+    // then swap halves across the half-wave, so that each lane writes whole
+    // 8-channel groups: lane h = 0 the groups 0 and 2 of a tile, h = 1 the
+    // groups 1 and 3, one 16-byte store each.
+    constexpr int HD = D / 64;
     const float l_tot = xsum32(l_run);
     __syncthreads();                                   // tile slots are free
-    float4* mo = reinterpret_cast<float4*>(smem + qg * (C::MERGE / C::NWQ));
-    float* ml = reinterpret_cast<float*>(smem + qg * (C::MERGE / C::NWQ) + (D / 32) * 64 * 16 * 4);
-    if (kh == 1) {
+    unsigned char* mbase = smem + qg * (C::MERGE / C::NWQ);
+    float4* mo = reinterpret_cast<float4*>(mbase);     // [wave kh][HD tiles][4 groups][64 lanes]
+    float* ml = reinterpret_cast<float*>(mbase + (D / 32) * 64 * 16 * 4);   // [wave kh][m, l][32]
+    // (kh is uniform but not a constant: each half is its own code path, so
+    // that the accumulator tiles keep constant register indices)
+    auto send = [&](auto KHC) {
+        constexpr int K = decltype(KHC)::value;
 #pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt)
+        for (int t = 0; t < HD; ++t)
 #pragma unroll
             for (int g = 0; g < 4; ++g)
-                mo[(dt * 4 + g) * 64 + lane] = make_float4(oacc[dt][4 * g], oacc[dt][4 * g + 1],
-                                                           oacc[dt][4 * g + 2], oacc[dt][4 * g + 3]);
-        if (h == 0) {
-            ml[r32] = m_run;
-            ml[32 + r32] = l_tot;
-        }
+                mo[((K * HD + t) * 4 + g) * 64 + lane] =
+                    make_float4(oacc[(1 - K) * HD + t][4 * g], oacc[(1 - K) * HD + t][4 * g + 1],
+                                oacc[(1 - K) * HD + t][4 * g + 2], oacc[(1 - K) * HD + t][4 * g + 3]);
+    };
+    if (kh == 0)
+        send(std::integral_constant<int, 0>{});
+    else
+        send(std::integral_constant<int, 1>{});
+    if (h == 0) {
+        ml[kh * 64 + r32] = m_run;
+        ml[kh * 64 + 32 + r32] = l_tot;
     }
     __syncthreads();
-    if (kh == 0) {
-        const float m1 = ml[r32], l1 = ml[32 + r32];
-        const float m = fmaxf(m_run, m1);
-        const float mb = m == -INFINITY ? 0.f : m;
-        const float a0 = __builtin_amdgcn_exp2f(m_run - mb), a1 = __builtin_amdgcn_exp2f(m1 - mb);
-        const float l = l_tot * a0 + l1 * a1;
-        const float inv = l > 0.f ? 1.f / l : 0.f;
-        if (qn < a.N) {
-            uint16_t* orow = a.O + head_off + (int64_t)qn * D;
+    const int ok = 1 - kh;
+    const float m1 = ml[ok * 64 + r32], l1 = ml[ok * 64 + 32 + r32];
+    const float m = fmaxf(m_run, m1);
+    const float mb = m == -INFINITY ? 0.f : m;
+    const float a0 = __builtin_amdgcn_exp2f(m_run - mb), a1 = __builtin_amdgcn_exp2f(m1 - mb);
+    const float l = kh == 0 ? l_tot * a0 + l1 * a1 : l1 * a1 + l_tot * a0;
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    auto finish = [&](auto KHC) {
+        constexpr int K = decltype(KHC)::value;
+        uint16_t* orow = a.O + head_off + (int64_t)qn * D;
 #pragma unroll
-            for (int dt = 0; dt < D / 32; ++dt)
+        for (int t = 0; t < HD; ++t) {
+            constexpr int OK = 1 - K;
+            const int dt = K * HD + t;
+            uint32_t pk[4][2];
 #pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const float4 o1 = mo[(dt * 4 + g) * 64 + lane];
-                    const float v0 = (oacc[dt][4 * g + 0] * a0 + o1.x * a1) * inv;
-                    const float v1 = (oacc[dt][4 * g + 1] * a0 + o1.y * a1) * inv;
-                    const float v2 = (oacc[dt][4 * g + 2] * a0 + o1.z * a1) * inv;
-                    const float v3 = (oacc[dt][4 * g + 3] * a0 + o1.w * a1) * inv;
-                    const uint32_t lo = f32_to_bf16_rne(v0) | ((uint32_t)f32_to_bf16_rne(v1) << 16);
-                    const uint32_t hi = f32_to_bf16_rne(v2) | ((uint32_t)f32_to_bf16_rne(v3) << 16);
-                    *reinterpret_cast<uint2*>(orow + dt * 32 + 8 * g + 4 * h) = make_uint2(lo, hi);
+            for (int g = 0; g < 4; ++g) {
+                const float4 o1 = mo[((OK * HD + t) * 4 + g) * 64 + lane];
+                const float v0 = (oacc[dt][4 * g + 0] * a0 + o1.x * a1) * inv;
+                const float v1 = (oacc[dt][4 * g + 1] * a0 + o1.y * a1) * inv;
+                const float v2 = (oacc[dt][4 * g + 2] * a0 + o1.z * a1) * inv;
+                const float v3 = (oacc[dt][4 * g + 3] * a0 + o1.w * a1) * inv;
+                pk[g][0] = f32_to_bf16_rne(v0) | ((uint32_t)f32_to_bf16_rne(v1) << 16);
+                pk[g][1] = f32_to_bf16_rne(v2) | ((uint32_t)f32_to_bf16_rne(v3) << 16);
+            }
+#pragma unroll
+            for (int g0 = 0; g0 < 4; g0 += 2) {
+                // lanes 0-31 keep group g0 and receive the partner's part of
+                // it; lanes 32-63 keep group g0 + 1 likewise
+                uint32_t w[4];
+#pragma unroll
+                for (int e = 0; e < 2; ++e) {
+                    const auto r = __builtin_amdgcn_permlane32_swap(pk[g0][e], pk[g0 + 1][e], false, false);
+                    if (h == 0) {
+                        w[e] = pk[g0][e];           // channels 8 g0 + 0..3 (own)
+                        w[2 + e] = r[1];            // channels 8 g0 + 4..7 (partner's)
+                    } else {
+                        w[e] = r[0];                // channels 8 (g0+1) + 0..3 (partner's)
+                        w[2 + e] = pk[g0 + 1][e];   // channels 8 (g0+1) + 4..7 (own)
+                    }
                 }
-            if (a.lse && h == 0)
-                a.lse[bh * (int64_t)a.N + qn] = l > 0.f ? (m + __log2f(l)) * kLn2 : -INFINITY;
+                *reinterpret_cast<uint4*>(orow + dt * 32 + 8 * (g0 + h)) = make_uint4(w[0], w[1], w[2], w[3]);
+            }
         }
+    };
+    if (qn < a.N) {
+        if (kh == 0)
+            finish(std::integral_constant<int, 0>{});
+        else
+            finish(std::integral_constant<int, 1>{});
+        if (a.lse && kh == 0 && h == 0)
+            a.lse[bh * (int64_t)a.N + qn] = l > 0.f ? (m + __log2f(l)) * kLn2 : -INFINITY;
     }
 }
 
