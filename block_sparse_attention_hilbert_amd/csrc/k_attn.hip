@@ -52,7 +52,7 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kLazy = 8.0f;      // log2 headroom before the running max moves
 #ifndef SA_PF
-#define SA_PF 4                    // LDS operand reads in flight in the matrix phase
+#define SA_PF 5                    // LDS operand reads in flight in the matrix phase
 #endif
 #ifndef SA_SGB
 #define SA_SGB 1
