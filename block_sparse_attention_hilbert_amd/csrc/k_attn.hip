@@ -102,7 +102,8 @@ struct FwdArgs {
     uint16_t* O;
     float* lse;
     int32_t* sched;          // [3][8] per-XCD row range start, end and pull counter;
-                             // [24] = 1 when the block counts come from the caller
+                             // [24] = 1 when the block counts come from the caller;
+                             // [25] workgroups of the launch that are done
     int32_t N, nb, ntc;
     int64_t rows;
     float c;                 // scale * log2(e)
@@ -584,12 +585,16 @@ void k_bsattn_fwd(FwdArgs a) {
             process_row<D, BLK, COMP>(a, row, smem, var_cnt);
         }
     }
-}
-
-// Zeroes the 8 per-XCD pull counters before an attention launch (a kernel,
-// not a memset, so that the sequence can be captured in a graph).
-__global__ void k_reset_pull(int32_t* __restrict__ sched) {
-    if (threadIdx.x < 8) sched[16 + threadIdx.x] = 0;
+    // The last workgroup to finish re-arms the pull counters for the next
+    // launch: every other workgroup has made its last pull before counting
+    // itself done.
+    if (threadIdx.x == 0) {
+        __threadfence();
+        if (atomicAdd(&a.sched[25], 1) == (int)gridDim.x - 1) {
+            for (int x = 0; x < 8; ++x) a.sched[16 + x] = 0;
+            a.sched[25] = 0;
+        }
+    }
 }
 
 // Splits the R rows into 8 contiguous ranges of (nearly) equal work, where a
@@ -599,7 +604,7 @@ constexpr int kSchedItems = 8;
 
 __global__ __launch_bounds__(kSchedThreads) void k_sched(const int32_t* __restrict__ row_ptr,
                                                          int32_t* __restrict__ sched, int64_t R,
-                                                         int extra) {
+                                                         int extra, int cnt_flag) {
     __shared__ long long wsum[kSchedThreads / 64];
     __shared__ long long s_total, s_carry;
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
@@ -612,6 +617,7 @@ __global__ __launch_bounds__(kSchedThreads) void k_sched(const int32_t* __restri
     for (int off = 32; off > 0; off >>= 1) part += __shfl_xor(part, off, 64);
     if (lane == 0) wsum[wid] = part;
     if (tid < 8) { sched[tid] = (int32_t)R; sched[8 + tid] = (int32_t)R; sched[16 + tid] = 0; }
+    if (tid == 0) { sched[24] = cnt_flag; sched[25] = 0; }
     __syncthreads();
     if (tid == 0) {
         long long t = 0;
@@ -702,11 +708,9 @@ __global__ __launch_bounds__(256) void k_vt_prep(const uint16_t* __restrict__ V,
 
 // Token count of every KV block: the caller's counts (clamped to the block's
 // extent) or, without them, BLK and N - (nb - 1) BLK for the last block.
-// Records in sched[24] which of the two it was.
 __global__ void k_fill_counts(const int32_t* __restrict__ kv_count, int16_t* __restrict__ cnt,
-                              int32_t* __restrict__ sched, int N, int nb, int blk, int64_t total) {
+                              int N, int nb, int blk, int64_t total) {
     const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (e == 0) sched[24] = kv_count != nullptr;
     if (e >= total) return;
     const int j = (int)(e % nb);
     const int lim = N - j * blk < blk ? N - j * blk : blk;
@@ -778,12 +782,15 @@ template <int D, int BLK, bool COMP>
 sa_status prepare_t(const FwdArgs& a, const Geometry& g, const uint16_t* V, uint16_t* vt,
                     const float* k_mean, const float* v_sum, const int32_t* kv_count,
                     uint16_t* kbar, uint16_t* vbart, hipStream_t stream) {
-    int16_t* cnt = const_cast<int16_t*>(a.cnt);
-    const int64_t ncnt = g.BH() * g.nb;
-    hipLaunchKernelGGL(k_fill_counts, dim3((unsigned)ceil_div(ncnt, 256)), dim3(256), 0, stream,
-                       kv_count, cnt, a.sched, g.N, g.nb, BLK, ncnt);
-    sa_status st = hip_check(hipGetLastError(), "k_fill_counts launch");
-    if (st != SA_OK) return st;
+    // the block counts are read only with the caller's counts or compensation
+    sa_status st = SA_OK;
+    if (COMP || kv_count) {
+        int16_t* cnt = const_cast<int16_t*>(a.cnt);
+        const int64_t ncnt = g.BH() * g.nb;
+        hipLaunchKernelGGL(k_fill_counts, dim3((unsigned)ceil_div(ncnt, 256)), dim3(256), 0, stream,
+                           kv_count, cnt, g.N, g.nb, BLK, ncnt);
+        if ((st = hip_check(hipGetLastError(), "k_fill_counts launch")) != SA_OK) return st;
+    }
     hipLaunchKernelGGL((k_vt_prep<D, BLK>), dim3(g.nb, (unsigned)g.BH()), dim3(256), 0, stream, V,
                        vt, g.N, g.nb);
     if ((st = hip_check(hipGetLastError(), "k_vt_prep launch")) != SA_OK) return st;
@@ -794,7 +801,7 @@ sa_status prepare_t(const FwdArgs& a, const Geometry& g, const uint16_t* V, uint
     }
     if (a.rows == 0) return SA_OK;
     hipLaunchKernelGGL(k_sched, dim3(1), dim3(kSchedThreads), 0, stream, a.row_ptr, a.sched,
-                       a.rows, (COMP ? a.ntc : 0) + 2);
+                       a.rows, (COMP ? a.ntc : 0) + 2, kv_count != nullptr ? 1 : 0);
     return hip_check(hipGetLastError(), "k_sched launch");
 }
 
@@ -832,8 +839,6 @@ sa_status run_t(const FwdArgs& a, const Geometry& g, hipStream_t stream) {
         resident_lds = lds;
     }
     const int64_t grid = a.rows < resident ? a.rows : resident;
-    hipLaunchKernelGGL(k_reset_pull, dim3(1), dim3(64), 0, stream, a.sched);
-    if ((st = hip_check(hipGetLastError(), "k_reset_pull launch")) != SA_OK) return st;
     hipLaunchKernelGGL((k_bsattn_fwd<D, BLK, COMP>), dim3((unsigned)grid), dim3(C::NT), lds, stream, a);
     return hip_check(hipGetLastError(), "k_bsattn_fwd launch");
 }
