@@ -42,7 +42,11 @@
  *     library allocates nothing, keeps no state between calls and never
  *     synchronises the stream.
  *   - Ordering: device work is enqueued on `stream` (a hipStream_t; NULL is
- *     the default stream) and is asynchronous.
+ *     the default stream) and is asynchronous.  A workspace carries one
+ *     call's intermediate state on the device (pooled means, scores, the
+ *     re-laid-out V, the attention kernel's row counters): calls that share
+ *     a workspace must be ordered (one stream, or synchronised streams);
+ *     two such calls in flight at once race.
  *   - Errors: arguments are validated on the host before any launch; a
  *     failed check returns SA_ERR_INVALID_ARG, SA_ERR_UNSUPPORTED or
  *     SA_ERR_WORKSPACE and enqueues nothing.  A failed launch returns
