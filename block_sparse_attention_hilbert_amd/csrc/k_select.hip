@@ -120,20 +120,23 @@ __global__ __launch_bounds__(kThreads) void k_pool(PoolArgs a) {
 // k_score
 // ----------------------------------------------------------------------------
 constexpr int kTile = 16;   // 16 x 16 threads per workgroup
+constexpr int kScoreChunk = 32;   // channels of the unit means staged in LDS at a time
 
 // Thread (ti, tj) of a workgroup takes the MT x MT block pairs (ti + 16 a,
 // tj + 16 b) of its 16 MT x 16 MT tile; the unit means of the tile's query
-// and key blocks are staged in LDS (rows padded by 4 floats, so the 16 key
-// rows a wave reads at once fall in distinct banks).  Each pair's dot
-// product stays one sequential fp32 FMA chain over the channels; the channel
-// loop is unrolled so that the operand reads of the next step are issued
-// under the FMAs of the current one.
+// and key blocks are staged in LDS 32 channels at a time (rows padded by 4
+// floats, so the 16 key rows a wave reads at once fall in distinct banks;
+// ~17 KB per workgroup, so that several share a CU).  Each pair's dot
+// product stays one sequential fp32 FMA chain over the channels, continued
+// from chunk to chunk; the channel loop is unrolled so that the operand reads
+// of the next step are issued under the FMAs of the current one.
 template <int D, int SPB, int MT>
 __global__ __launch_bounds__(kThreads) void k_score(const float* __restrict__ qm,
                                                     const float* __restrict__ km,
                                                     float* __restrict__ S, int nb,
                                                     int n_units, float scale) {
-    constexpr int ROW = SPB * D + 4;      // floats per block row in LDS (+4: bank shift)
+    constexpr int DC = kScoreChunk;       // channels staged at a time
+    constexpr int ROW = SPB * DC + 4;     // floats per block row in LDS (+4: bank shift)
     constexpr int TB = kTile * MT;        // blocks per tile side
     extern __shared__ float lds[];
     float* qs = lds;                      // [TB][ROW]
@@ -145,21 +148,6 @@ __global__ __launch_bounds__(kThreads) void k_score(const float* __restrict__ qm
     const float* qb = qm + bh * (int64_t)n_units * D;
     const float* kb = km + bh * (int64_t)n_units * D;
 
-    // stage the unit means of TB query blocks and TB key blocks (float4)
-    constexpr int V4 = SPB * D / 4;
-    for (int p = tid; p < TB * V4; p += kThreads) {
-        const int b = p / V4, o = p % V4;
-        const int u = o / (D / 4);                      // unit within the block
-        float4 qv = make_float4(0.f, 0.f, 0.f, 0.f), kv = qv;
-        if (i0 + b < nb && (i0 + b) * SPB + u < n_units)
-            qv = reinterpret_cast<const float4*>(qb + (int64_t)(i0 + b) * SPB * D)[o];
-        if (j0 + b < nb && (j0 + b) * SPB + u < n_units)
-            kv = reinterpret_cast<const float4*>(kb + (int64_t)(j0 + b) * SPB * D)[o];
-        *reinterpret_cast<float4*>(qs + b * ROW + o * 4) = qv;
-        *reinterpret_cast<float4*>(ks + b * ROW + o * 4) = kv;
-    }
-    __syncthreads();
-
     const int ti = tid / kTile, tj = tid % kTile;
     float acc[MT][MT][SPB][SPB];
 #pragma unroll
@@ -170,33 +158,51 @@ __global__ __launch_bounds__(kThreads) void k_score(const float* __restrict__ qm
             for (int x = 0; x < SPB; ++x)
 #pragma unroll
                 for (int y = 0; y < SPB; ++y) acc[a][b][x][y] = 0.f;
-    // with many pairs per thread a full unroll would hoist every operand read
-    constexpr int UNR = MT == 1 ? D / 4 : 4;
+    // channels DC at a time: stage the chunk of the unit means of TB query
+    // and TB key blocks (float4), then continue every chain over it
+    constexpr int V4 = SPB * DC / 4;
+    for (int ch = 0; ch < D; ch += DC) {
+        if (ch > 0) __syncthreads();                        // the last chunk is consumed
+        for (int p = tid; p < TB * V4; p += kThreads) {
+            const int b = p / V4, o = p % V4;
+            const int u = o / (DC / 4), w = o % (DC / 4);   // unit within the block, float4 in the chunk
+            float4 qv = make_float4(0.f, 0.f, 0.f, 0.f), kv = qv;
+            if (i0 + b < nb && (i0 + b) * SPB + u < n_units)
+                qv = *reinterpret_cast<const float4*>(qb + ((int64_t)(i0 + b) * SPB + u) * D + ch + 4 * w);
+            if (j0 + b < nb && (j0 + b) * SPB + u < n_units)
+                kv = *reinterpret_cast<const float4*>(kb + ((int64_t)(j0 + b) * SPB + u) * D + ch + 4 * w);
+            *reinterpret_cast<float4*>(qs + b * ROW + o * 4) = qv;
+            *reinterpret_cast<float4*>(ks + b * ROW + o * 4) = kv;
+        }
+        __syncthreads();
+        // with many pairs per thread a full unroll would hoist every operand read
+        constexpr int UNR = MT == 1 ? DC / 4 : 4;
 #pragma unroll(UNR)
-    for (int c = 0; c < D; c += 4) {
-        float4 qv[MT][SPB], kv[MT][SPB];
+        for (int c = 0; c < DC; c += 4) {
+            float4 qv[MT][SPB], kv[MT][SPB];
 #pragma unroll
-        for (int a = 0; a < MT; ++a)
+            for (int a = 0; a < MT; ++a)
 #pragma unroll
-            for (int x = 0; x < SPB; ++x) {
-                qv[a][x] = *reinterpret_cast<const float4*>(qs + (ti + kTile * a) * ROW + x * D + c);
-                kv[a][x] = *reinterpret_cast<const float4*>(ks + (tj + kTile * a) * ROW + x * D + c);
-            }
+                for (int x = 0; x < SPB; ++x) {
+                    qv[a][x] = *reinterpret_cast<const float4*>(qs + (ti + kTile * a) * ROW + x * DC + c);
+                    kv[a][x] = *reinterpret_cast<const float4*>(ks + (tj + kTile * a) * ROW + x * DC + c);
+                }
 #pragma unroll
-        for (int a = 0; a < MT; ++a)
+            for (int a = 0; a < MT; ++a)
 #pragma unroll
-            for (int b = 0; b < MT; ++b)
+                for (int b = 0; b < MT; ++b)
 #pragma unroll
-                for (int x = 0; x < SPB; ++x)
+                    for (int x = 0; x < SPB; ++x)
 #pragma unroll
-                    for (int y = 0; y < SPB; ++y) {
-                        float s = acc[a][b][x][y];
-                        s = __builtin_fmaf(qv[a][x].x, kv[b][y].x, s);
-                        s = __builtin_fmaf(qv[a][x].y, kv[b][y].y, s);
-                        s = __builtin_fmaf(qv[a][x].z, kv[b][y].z, s);
-                        s = __builtin_fmaf(qv[a][x].w, kv[b][y].w, s);
-                        acc[a][b][x][y] = s;
-                    }
+                        for (int y = 0; y < SPB; ++y) {
+                            float s = acc[a][b][x][y];
+                            s = __builtin_fmaf(qv[a][x].x, kv[b][y].x, s);
+                            s = __builtin_fmaf(qv[a][x].y, kv[b][y].y, s);
+                            s = __builtin_fmaf(qv[a][x].z, kv[b][y].z, s);
+                            s = __builtin_fmaf(qv[a][x].w, kv[b][y].w, s);
+                            acc[a][b][x][y] = s;
+                        }
+        }
     }
 #pragma unroll
     for (int a = 0; a < MT; ++a)
@@ -704,7 +710,7 @@ sa_status launch_score_t(const float* qm, const float* km, float* S, int nb, int
     constexpr int MT = SPB <= 2 ? 2 : 1;
     constexpr int TB = kTile * MT;
     const dim3 grid((nb + TB - 1) / TB, (nb + TB - 1) / TB, (unsigned)BH);
-    const size_t lds = 2 * TB * (SPB * D + 4) * sizeof(float);
+    const size_t lds = 2 * TB * (SPB * kScoreChunk + 4) * sizeof(float);
     if (lds > 65536) {
         sa_status st = hip_check(hipFuncSetAttribute((const void*)k_score<D, SPB, MT>,
                                                      hipFuncAttributeMaxDynamicSharedMemorySize,
