@@ -185,13 +185,72 @@ class SelectSpec:
         return s, keep
 
 
-def _ptr(t: Optional[torch.Tensor]):
-    return None if t is None else ctypes.c_void_p(t.data_ptr())
+_BF16, _I32, _F32, _U8 = torch.bfloat16, torch.int32, torch.float32, torch.uint8
 
 
-def _stream(stream=None):
-    s = torch.cuda.current_stream() if stream is None else stream
-    return ctypes.c_void_p(s.cuda_stream)
+class _Args:
+    """Checked device pointers of one call's tensor arguments.  The C library
+    sees only addresses and sizes, so everything it cannot check is checked
+    here, before the call: each tensor's dtype, exact shape or minimum element
+    count and contiguity (the kernels index dense row-major buffers) as it is
+    marshalled, then that all of them live on one GPU."""
+
+    def __init__(self):
+        self.seen = []
+
+    def __call__(self, t: Optional[torch.Tensor], name: str, dtype: torch.dtype, *, shape=None,
+                 numel: Optional[int] = None, optional: bool = False):
+        if t is None:
+            if optional:
+                return None
+            raise ValueError(f"{name} is required")
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{name} must be a torch.Tensor (got {type(t).__name__})")
+        if t.dtype != dtype:
+            raise TypeError(f"{name} must be {dtype} (got {t.dtype})")
+        if shape is not None and tuple(t.shape) != tuple(shape):
+            raise ValueError(f"{name} must have shape {tuple(shape)} (got {tuple(t.shape)})")
+        if numel is not None and t.numel() < numel:
+            raise ValueError(f"{name} holds {t.numel()} elements; at least {numel} are needed")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+        self.seen.append((name, t))
+        return ctypes.c_void_p(t.data_ptr())
+
+    def call(self, fn, *args):
+        """fn(*args) once every tensor seen is on the same GPU."""
+        dev = None
+        for name, t in self.seen:
+            if t.device.type != "cuda":
+                raise ValueError(f"{name} must be a GPU tensor (got device {t.device})")
+            if dev is None:
+                dev = t.device
+            elif t.device != dev:
+                raise ValueError(f"{name} is on {t.device}, the call's other tensors on {dev}")
+        return fn(*[a.handle() if isinstance(a, _Stream) else a for a in args])
+
+
+def _ws(A: _Args, workspace: Optional[torch.Tensor]):
+    """(pointer, bytes) of a workspace buffer (uint8, contiguous, same GPU)."""
+    if workspace is None:
+        return None, 0
+    return A(workspace, "workspace", _U8), workspace.numel()
+
+
+def _tokens(prob: "Problem", N: Optional[int] = None):
+    return (prob.B, prob.H, prob.N if N is None else N, prob.d)
+
+
+class _Stream:
+    """The HIP stream of a call (the current one unless given), looked up
+    when the call is made, after its arguments are checked."""
+
+    def __init__(self, stream=None):
+        self.stream = stream
+
+    def handle(self):
+        s = torch.cuda.current_stream() if self.stream is None else self.stream
+        return ctypes.c_void_p(s.cuda_stream)
 
 
 def workspace_size(prob: Problem, spec: Optional[SelectSpec] = None) -> int:
@@ -221,19 +280,29 @@ def hilbert_perm_build(T: int, Hg: int, W: int):
     return perm, inv
 
 
+def _permute_args(A: "_Args", prob: Problem, src, perm_dev, dst):
+    ps = A(src, "src", _BF16, shape=_tokens(prob))
+    dev = src.device
+    if dst is None:
+        dst = torch.empty(_tokens(prob), dtype=_BF16, device=dev)
+    pd = A(dst, "dst", _BF16, shape=_tokens(prob))
+    pp = A(perm_dev, "perm_dev", _I32, shape=(prob.N,))
+    return ps, pd, pp, dst
+
+
 def hilbert_permute(prob: Problem, src: torch.Tensor, perm_dev: torch.Tensor,
                     dst: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
-    dst = torch.empty_like(src) if dst is None else dst
-    _check(lib.hilbert_permute(ctypes.byref(prob.c()), _ptr(src), _ptr(dst), _ptr(perm_dev),
-                               _stream(stream)))
+    A = _Args()
+    ps, pd, pp, dst = _permute_args(A, prob, src, perm_dev, dst)
+    _check(A.call(lib.hilbert_permute, ctypes.byref(prob.c()), ps, pd, pp, _Stream(stream)))
     return dst
 
 
 def hilbert_unpermute(prob: Problem, src: torch.Tensor, perm_dev: torch.Tensor,
                       dst: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
-    dst = torch.empty_like(src) if dst is None else dst
-    _check(lib.hilbert_unpermute(ctypes.byref(prob.c()), _ptr(src), _ptr(dst), _ptr(perm_dev),
-                                 _stream(stream)))
+    A = _Args()
+    ps, pd, pp, dst = _permute_args(A, prob, src, perm_dev, dst)
+    _check(A.call(lib.hilbert_unpermute, ctypes.byref(prob.c()), ps, pd, pp, _Stream(stream)))
     return dst
 
 
@@ -251,6 +320,7 @@ def select(prob: Problem, spec: SelectSpec, Q: torch.Tensor, K: torch.Tensor,
            out: Optional[Selection] = None, workspace: Optional[torch.Tensor] = None,
            stream=None) -> Selection:
     """sparse_attn_select.  Output buffers are allocated unless ``out`` is given."""
+    A = _Args()
     dev = (Q if Q is not None else K).device
     nb, rows = prob.nb, prob.rows
     if out is None:
@@ -264,19 +334,37 @@ def select(prob: Problem, spec: SelectSpec, Q: torch.Tensor, K: torch.Tensor,
     if workspace is None:
         workspace = alloc_workspace(workspace_size(prob, spec), dev)
     cs, keep = spec.c()
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check(lib.sparse_attn_select(ctypes.byref(prob.c()), ctypes.byref(cs), _ptr(Q), _ptr(K),
-                                  _ptr(V), _ptr(out.row_ptr), _ptr(out.col_idx),
-                                  _ptr(out.scores), _ptr(out.k_mean), _ptr(out.v_sum),
-                                  _ptr(workspace), ws_bytes, _stream(stream)))
+    tok, stat = _tokens(prob), (prob.B, prob.H, nb, prob.d)
+    args = [A(Q, "Q", _BF16, shape=tok, optional=True),
+            A(K, "K", _BF16, shape=tok, optional=True),
+            A(V, "V", _BF16, shape=tok, optional=True),
+            A(out.row_ptr, "row_ptr", _I32, numel=rows + 1),
+            A(out.col_idx, "col_idx", _I32, numel=rows * nb),
+            A(out.scores, "scores", _F32, numel=rows * nb, optional=True),
+            A(out.k_mean, "k_mean", _F32, shape=stat, optional=True),
+            A(out.v_sum, "v_sum", _F32, shape=stat, optional=True)]
+    wp, ws_bytes = _ws(A, workspace)
+    _check(A.call(lib.sparse_attn_select, ctypes.byref(prob.c()), ctypes.byref(cs), *args, wp, ws_bytes,
+                                  _Stream(stream)))
     return out
 
 
 def centroids(prob: Problem, K: torch.Tensor, V: torch.Tensor, k_mean: torch.Tensor,
               v_sum: torch.Tensor, stream=None) -> None:
     """sparse_attn_centroids: block means of K and block sums of V (no selection)."""
-    _check(lib.sparse_attn_centroids(ctypes.byref(prob.c()), _ptr(K), _ptr(V), _ptr(k_mean),
-                                     _ptr(v_sum), _stream(stream)))
+    A = _Args()
+    dev, tok, stat = K.device, _tokens(prob), (prob.B, prob.H, prob.nb, prob.d)
+    _check(A.call(lib.sparse_attn_centroids, ctypes.byref(prob.c()), A(K, "K", _BF16, shape=tok),
+                                     A(V, "V", _BF16, shape=tok),
+                                     A(k_mean, "k_mean", _F32, shape=stat),
+                                     A(v_sum, "v_sum", _F32, shape=stat),
+                                     _Stream(stream)))
+
+
+def _comp_args(A: "_Args", prob: Problem, k_mean, v_sum):
+    stat = (prob.B, prob.H, prob.nb, prob.d)
+    return (A(k_mean, "k_mean", _F32, shape=stat, optional=True),
+            A(v_sum, "v_sum", _F32, shape=stat, optional=True))
 
 
 def fwd(prob: Problem, Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor,
@@ -285,15 +373,24 @@ def fwd(prob: Problem, Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor,
         lse: Optional[torch.Tensor] = None, want_lse: bool = False,
         workspace: Optional[torch.Tensor] = None, stream=None):
     """sparse_attn_fwd.  Returns O (and lse when requested or given)."""
-    O = torch.empty_like(Q) if O is None else O
+    A = _Args()
+    tok = _tokens(prob)
+    pq = A(Q, "Q", _BF16, shape=tok)
+    dev = Q.device
+    O = torch.empty(tok, dtype=_BF16, device=dev) if O is None else O
     if want_lse and lse is None:
-        lse = torch.empty(prob.B, prob.H, prob.N, dtype=torch.float32, device=Q.device)
+        lse = torch.empty(prob.B, prob.H, prob.N, dtype=torch.float32, device=dev)
     if workspace is None:
-        workspace = alloc_workspace(workspace_size(prob, None), Q.device)
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check(lib.sparse_attn_fwd(ctypes.byref(prob.c()), _ptr(Q), _ptr(K), _ptr(V), _ptr(row_ptr),
-                               _ptr(col_idx), _ptr(k_mean), _ptr(v_sum), _ptr(O), _ptr(lse),
-                               _ptr(workspace), ws_bytes, _stream(stream)))
+        workspace = alloc_workspace(workspace_size(prob, None), dev)
+    wp, ws_bytes = _ws(A, workspace)
+    _check(A.call(lib.sparse_attn_fwd, ctypes.byref(prob.c()), pq, A(K, "K", _BF16, shape=tok),
+                               A(V, "V", _BF16, shape=tok),
+                               A(row_ptr, "row_ptr", _I32, numel=prob.rows + 1),
+                               A(col_idx, "col_idx", _I32),
+                               *_comp_args(A, prob, k_mean, v_sum),
+                               A(O, "O", _BF16, shape=tok),
+                               A(lse, "lse", _F32, shape=tok[:3], optional=True),
+                               wp, ws_bytes, _Stream(stream)))
     return (O, lse) if lse is not None else O
 
 
@@ -301,20 +398,31 @@ def fwd_prepare(prob: Problem, V: torch.Tensor, row_ptr: torch.Tensor,
                 k_mean: Optional[torch.Tensor] = None, v_sum: Optional[torch.Tensor] = None, *,
                 workspace: torch.Tensor, stream=None) -> None:
     """sparse_attn_fwd_prepare: V (and the centroids) laid out in ``workspace``."""
-    ws_bytes = workspace.numel() * workspace.element_size()
-    _check(lib.sparse_attn_fwd_prepare(ctypes.byref(prob.c()), _ptr(V), _ptr(row_ptr),
-                                       _ptr(k_mean), _ptr(v_sum), _ptr(workspace), ws_bytes,
-                                       _stream(stream)))
+    A = _Args()
+    pv = A(V, "V", _BF16, shape=_tokens(prob))
+    dev = V.device
+    wp, ws_bytes = _ws(A, workspace)
+    _check(A.call(lib.sparse_attn_fwd_prepare, ctypes.byref(prob.c()), pv,
+                                       A(row_ptr, "row_ptr", _I32, numel=prob.rows + 1),
+                                       *_comp_args(A, prob, k_mean, v_sum), wp, ws_bytes,
+                                       _Stream(stream)))
 
 
 def fwd_run(prob: Problem, Q: torch.Tensor, K: torch.Tensor, row_ptr: torch.Tensor,
             col_idx: torch.Tensor, with_comp: bool, *, O: torch.Tensor,
             lse: Optional[torch.Tensor] = None, workspace: torch.Tensor, stream=None) -> None:
     """sparse_attn_fwd_run: the attention kernel on a prepared workspace."""
-    ws_bytes = workspace.numel() * workspace.element_size()
-    _check(lib.sparse_attn_fwd_run(ctypes.byref(prob.c()), _ptr(Q), _ptr(K), _ptr(row_ptr),
-                                   _ptr(col_idx), int(bool(with_comp)), _ptr(O), _ptr(lse),
-                                   _ptr(workspace), ws_bytes, _stream(stream)))
+    A = _Args()
+    tok = _tokens(prob)
+    pq = A(Q, "Q", _BF16, shape=tok)
+    dev = Q.device
+    wp, ws_bytes = _ws(A, workspace)
+    _check(A.call(lib.sparse_attn_fwd_run, ctypes.byref(prob.c()), pq, A(K, "K", _BF16, shape=tok),
+                                   A(row_ptr, "row_ptr", _I32, numel=prob.rows + 1),
+                                   A(col_idx, "col_idx", _I32), int(bool(with_comp)),
+                                   A(O, "O", _BF16, shape=tok),
+                                   A(lse, "lse", _F32, shape=tok[:3], optional=True),
+                                   wp, ws_bytes, _Stream(stream)))
 
 
 def problem_for(wl, scale: float = 0.0) -> Problem:
@@ -340,10 +448,14 @@ def fwd_prepare_counts(prob: Problem, V: torch.Tensor, row_ptr: torch.Tensor,
                        stream=None) -> None:
     """sparse_attn_fwd_prepare_counts: as fwd_prepare, with int32 [B*H, nb] token
     counts per KV block (keys past a block's count take no part)."""
-    ws_bytes = workspace.numel() * workspace.element_size()
-    _check(lib.sparse_attn_fwd_prepare_counts(ctypes.byref(prob.c()), _ptr(V), _ptr(row_ptr),
-                                              _ptr(k_mean), _ptr(v_sum), _ptr(kv_count),
-                                              _ptr(workspace), ws_bytes, _stream(stream)))
+    A = _Args()
+    pv = A(V, "V", _BF16, shape=_tokens(prob))
+    dev = V.device
+    wp, ws_bytes = _ws(A, workspace)
+    _check(A.call(lib.sparse_attn_fwd_prepare_counts, ctypes.byref(prob.c()), pv, A(row_ptr, "row_ptr", _I32, numel=prob.rows + 1),
+        *_comp_args(A, prob, k_mean, v_sum),
+        A(kv_count, "kv_count", _I32, numel=prob.B * prob.H * prob.nb),
+        wp, ws_bytes, _Stream(stream)))
 
 
 # ---------------------------------------------------------------------------
@@ -359,6 +471,8 @@ class ClusterSpec:
     shape_idx: Optional[torch.Tensor] = None   # tiles: device int32 [B*H]
 
     def c(self) -> SaClusterSpec:
+        if self.shape_idx is not None:
+            _Args()(self.shape_idx, "shape_idx", _I32)
         n, sp = 0, None
         if self.shapes:
             arr = (SaTileShape * len(self.shapes))(*[SaTileShape(*map(int, s)) for s in self.shapes])
@@ -418,28 +532,44 @@ def cluster(prob: Problem, cspec: ClusterSpec, Q: torch.Tensor, K: torch.Tensor,
             workspace: Optional[torch.Tensor] = None, stream=None) -> Clusters:
     """sparse_attn_cluster: clusters of Q and K per (b, h) and their padded
     layouts; with V also the value means of the key clusters."""
+    A = _Args()
     nbp, ws_c, _ = cluster_size(prob, cspec)
     if out is None:
         out = Clusters.empty(prob, cspec, nbp, V is not None, Q.device)
     if workspace is None:
         workspace = alloc_workspace(ws_c, Q.device)
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check(lib.sparse_attn_cluster(ctypes.byref(prob.c()), ctypes.byref(cspec.c()), _ptr(Q),
-                                   _ptr(K), _ptr(V), _ptr(out.q_order), _ptr(out.k_order),
-                                   _ptr(out.q_blk), _ptr(out.k_blk), _ptr(out.q_cnt),
-                                   _ptr(out.k_cnt), _ptr(out.q_cent), _ptr(out.k_cent),
-                                   _ptr(out.v_cent if V is not None else None),
-                                   _ptr(out.q_count), _ptr(out.k_count), _ptr(workspace),
-                                   ws_bytes, _stream(stream)))
+    dev, tok = Q.device, _tokens(prob)
+    BH, C, Np = prob.B * prob.H, cspec.n_clusters, nbp * prob.block
+    if cspec.shape_idx is not None:
+        A(cspec.shape_idx, "shape_idx", _I32, shape=(BH,))
+    args = [A(Q, "Q", _BF16, shape=tok), A(K, "K", _BF16, shape=tok),
+            A(V, "V", _BF16, shape=tok, optional=True)]
+    args += [A(getattr(out, f), f, _I32, shape=(BH, Np)) for f in ("q_order", "k_order")]
+    args += [A(getattr(out, f), f, _I32, shape=(BH, nbp))
+             for f in ("q_blk", "k_blk", "q_cnt", "k_cnt")]
+    args += [A(getattr(out, f), f, _F32, shape=(BH, C, prob.d)) for f in ("q_cent", "k_cent")]
+    args += [A(out.v_cent if V is not None else None, "v_cent", _F32, shape=(BH, C, prob.d), optional=V is None)]
+    args += [A(getattr(out, f), f, _I32, shape=(BH, C)) for f in ("q_count", "k_count")]
+    wp, ws_bytes = _ws(A, workspace)
+    _check(A.call(lib.sparse_attn_cluster, ctypes.byref(prob.c()), ctypes.byref(cspec.c()), *args, wp,
+                                   ws_bytes, _Stream(stream)))
     return out
+
+
+def _padded_rows(prob: Problem, cspec: ClusterSpec) -> int:
+    return cluster_size(prob, cspec)[0] * prob.block
 
 
 def cluster_gather(prob: Problem, cspec: ClusterSpec, order: torch.Tensor, src: torch.Tensor,
                    dst: torch.Tensor, stream=None) -> torch.Tensor:
     """sparse_attn_cluster_gather: rows of src [B,H,N,d] into the padded layout dst
     [B,H,Np,d] (zero rows for padding)."""
-    _check(lib.sparse_attn_cluster_gather(ctypes.byref(prob.c()), ctypes.byref(cspec.c()),
-                                          _ptr(order), _ptr(src), _ptr(dst), _stream(stream)))
+    A = _Args()
+    Np, dev = _padded_rows(prob, cspec), src.device
+    _check(A.call(lib.sparse_attn_cluster_gather, ctypes.byref(prob.c()), ctypes.byref(cspec.c()),
+        A(order, "order", _I32, shape=(prob.B * prob.H, Np)),
+        A(src, "src", _BF16, shape=_tokens(prob)),
+        A(dst, "dst", _BF16, shape=_tokens(prob, Np)), _Stream(stream)))
     return dst
 
 
@@ -447,9 +577,15 @@ def cluster_scatter(prob: Problem, cspec: ClusterSpec, order: torch.Tensor, src:
                     dst: torch.Tensor, lse_src: Optional[torch.Tensor] = None,
                     lse_dst: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     """sparse_attn_cluster_scatter: rows of the padded layout back to token order."""
-    _check(lib.sparse_attn_cluster_scatter(ctypes.byref(prob.c()), ctypes.byref(cspec.c()),
-                                           _ptr(order), _ptr(src), _ptr(dst), _ptr(lse_src),
-                                           _ptr(lse_dst), _stream(stream)))
+    A = _Args()
+    Np, dev = _padded_rows(prob, cspec), src.device
+    _check(A.call(lib.sparse_attn_cluster_scatter, ctypes.byref(prob.c()), ctypes.byref(cspec.c()),
+        A(order, "order", _I32, shape=(prob.B * prob.H, Np)),
+        A(src, "src", _BF16, shape=_tokens(prob, Np)),
+        A(dst, "dst", _BF16, shape=_tokens(prob)),
+        A(lse_src, "lse_src", _F32, shape=(prob.B, prob.H, Np), optional=True),
+        A(lse_dst, "lse_dst", _F32, shape=(prob.B, prob.H, prob.N), optional=True),
+        _Stream(stream)))
     return dst
 
 
@@ -458,6 +594,7 @@ def cluster_select(prob: Problem, cspec: ClusterSpec, spec: SelectSpec, cl: Clus
                    workspace: Optional[torch.Tensor] = None, stream=None) -> Selection:
     """sparse_attn_cluster_select: keep decision over clusters as CSR over the
     padded blocks (+ per-block compensation statistics with want_comp)."""
+    A = _Args()
     nbp, _, ws_s = cluster_size(prob, cspec)
     dev = cl.q_cent.device
     BH, C = prob.B * prob.H, cspec.n_clusters
@@ -472,13 +609,23 @@ def cluster_select(prob: Problem, cspec: ClusterSpec, spec: SelectSpec, cl: Clus
             out.v_sum = torch.empty_like(out.k_mean)
     if workspace is None:
         workspace = alloc_workspace(ws_s, dev)
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    wp, ws_bytes = _ws(A, workspace)
     cs, keep = spec.c()
-    _check(lib.sparse_attn_cluster_select(
-        ctypes.byref(prob.c()), ctypes.byref(cspec.c()), ctypes.byref(cs), _ptr(cl.q_cent),
-        _ptr(cl.k_cent), _ptr(cl.v_cent), _ptr(cl.k_count), _ptr(cl.q_blk), _ptr(cl.k_blk),
-        _ptr(cl.k_cnt), _ptr(out.row_ptr), _ptr(out.col_idx), _ptr(out.scores),
-        _ptr(out.k_mean), _ptr(out.v_sum), _ptr(workspace), ws_bytes, _stream(stream)))
+    cen, stat = (BH, C, prob.d), (prob.B, prob.H, nbp, prob.d)
+    _check(A.call(lib.sparse_attn_cluster_select, ctypes.byref(prob.c()), ctypes.byref(cspec.c()), ctypes.byref(cs),
+        A(cl.q_cent, "q_cent", _F32, shape=cen),
+        A(cl.k_cent, "k_cent", _F32, shape=cen),
+        A(cl.v_cent, "v_cent", _F32, shape=cen, optional=True),
+        A(cl.k_count, "k_count", _I32, shape=(BH, C)),
+        A(cl.q_blk, "q_blk", _I32, shape=(BH, nbp)),
+        A(cl.k_blk, "k_blk", _I32, shape=(BH, nbp)),
+        A(cl.k_cnt, "k_cnt", _I32, shape=(BH, nbp)),
+        A(out.row_ptr, "row_ptr", _I32, numel=rows + 1),
+        A(out.col_idx, "col_idx", _I32, numel=rows * nbp),
+        A(out.scores, "scores", _F32, numel=BH * C * C, optional=True),
+        A(out.k_mean, "k_mean", _F32, shape=stat, optional=True),
+        A(out.v_sum, "v_sum", _F32, shape=stat, optional=True),
+        wp, ws_bytes, _Stream(stream)))
     return out
 
 
@@ -488,10 +635,19 @@ def cluster_centroids(prob: Problem, cspec: ClusterSpec, Kp: torch.Tensor, Vp: t
     """sparse_attn_cluster_centroids: key / value means of the kept partition
     from this call's K, V in the padded layout (into cl.k_cent, cl.v_cent) and
     the per-block compensation statistics."""
-    _check(lib.sparse_attn_cluster_centroids(ctypes.byref(prob.c()), ctypes.byref(cspec.c()),
-                                             _ptr(Kp), _ptr(Vp), _ptr(cl.k_count), _ptr(cl.k_blk),
-                                             _ptr(cl.k_cnt), _ptr(cl.k_cent), _ptr(cl.v_cent),
-                                             _ptr(k_mean), _ptr(v_sum), _stream(stream)))
+    A = _Args()
+    nbp = cluster_size(prob, cspec)[0]
+    BH, C, dev = prob.B * prob.H, cspec.n_clusters, Kp.device
+    ptok, cen, stat = _tokens(prob, nbp * prob.block), (BH, C, prob.d), (prob.B, prob.H, nbp, prob.d)
+    _check(A.call(lib.sparse_attn_cluster_centroids, ctypes.byref(prob.c()), ctypes.byref(cspec.c()), A(Kp, "Kp", _BF16, shape=ptok),
+        A(Vp, "Vp", _BF16, shape=ptok),
+        A(cl.k_count, "k_count", _I32, shape=(BH, C)),
+        A(cl.k_blk, "k_blk", _I32, shape=(BH, nbp)),
+        A(cl.k_cnt, "k_cnt", _I32, shape=(BH, nbp)),
+        A(cl.k_cent, "k_cent", _F32, shape=cen),
+        A(cl.v_cent, "v_cent", _F32, shape=cen),
+        A(k_mean, "k_mean", _F32, shape=stat),
+        A(v_sum, "v_sum", _F32, shape=stat), _Stream(stream)))
 
 
 def sics(prob: Problem, cspec: ClusterSpec, Q: torch.Tensor, K: torch.Tensor,
@@ -500,12 +656,17 @@ def sics(prob: Problem, cspec: ClusterSpec, Q: torch.Tensor, K: torch.Tensor,
     """sparse_attn_sics: per (b, h) the tile shape of the menu with the most
     coherent tiles (mean intra-tile cosine of Q and K) into shape_idx (device
     int32 [B*H]); scores (device fp64 [B*H, n_shapes]) if given."""
+    A = _Args()
     if workspace is None:
         workspace = alloc_workspace(cluster_size(prob, cspec)[1], Q.device)
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check(lib.sparse_attn_sics(ctypes.byref(prob.c()), ctypes.byref(cspec.c()), _ptr(Q), _ptr(K),
-                                _ptr(scores), _ptr(shape_idx), _ptr(workspace), ws_bytes,
-                                _stream(stream)))
+    dev, tok, BH = Q.device, _tokens(prob), prob.B * prob.H
+    wp, ws_bytes = _ws(A, workspace)
+    _check(A.call(lib.sparse_attn_sics, ctypes.byref(prob.c()), ctypes.byref(cspec.c()), A(Q, "Q", _BF16, shape=tok),
+        A(K, "K", _BF16, shape=tok),
+        A(scores, "scores", torch.float64, shape=(BH, len(cspec.shapes or ())),
+             optional=True),
+        A(shape_idx, "shape_idx", _I32, shape=(BH,)), wp, ws_bytes,
+        _Stream(stream)))
     return shape_idx
 
 

@@ -226,8 +226,10 @@ __device__ __forceinline__ void process_row(const FwdArgs& a, int64_t row, unsig
         qf[st] = as_bf16x8(v);
     }
 
+    // a row longer than nb (a malformed CSR) is cut to its first nb entries and
+    // a negative length taken as empty: the LDS lists below hold nb entries
     const int beg = __builtin_amdgcn_readfirstlane(a.row_ptr[row]);
-    const int nk = __builtin_amdgcn_readfirstlane(a.row_ptr[row + 1]) - beg;
+    const int nk = min(max(__builtin_amdgcn_readfirstlane(a.row_ptr[row + 1]) - beg, 0), a.nb);
     const int T = nk + (COMP ? a.ntc : 0);
     const int16_t* cnt_h = a.cnt + bh * a.nb;
     // token count of block j: the caller's (var_cnt) or the fixed layout's
@@ -604,12 +606,14 @@ constexpr int kSchedItems = 8;
 
 __global__ __launch_bounds__(kSchedThreads) void k_sched(const int32_t* __restrict__ row_ptr,
                                                          int32_t* __restrict__ sched, int64_t R,
-                                                         int extra, int cnt_flag) {
+                                                         int nb, int extra, int cnt_flag) {
     __shared__ long long wsum[kSchedThreads / 64];
     __shared__ long long s_total, s_carry;
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    // a row's tiles as the attention kernel counts them (length clamped to [0, nb])
     auto cost = [&](int64_t r) -> long long {
-        return (long long)(row_ptr[r + 1] - row_ptr[r]) + extra;
+        const int n = row_ptr[r + 1] - row_ptr[r];
+        return (long long)(n < 0 ? 0 : (n > nb ? nb : n)) + extra;
     };
     // total work
     long long part = 0;
@@ -801,7 +805,7 @@ sa_status prepare_t(const FwdArgs& a, const Geometry& g, const uint16_t* V, uint
     }
     if (a.rows == 0) return SA_OK;
     hipLaunchKernelGGL(k_sched, dim3(1), dim3(kSchedThreads), 0, stream, a.row_ptr, a.sched,
-                       a.rows, (COMP ? a.ntc : 0) + 2, kv_count != nullptr ? 1 : 0);
+                       a.rows, g.nb, (COMP ? a.ntc : 0) + 2, kv_count != nullptr ? 1 : 0);
     return hip_check(hipGetLastError(), "k_sched launch");
 }
 
@@ -811,33 +815,14 @@ sa_status run_t(const FwdArgs& a, const Geometry& g, hipStream_t stream) {
     using C = Cfg<D, BLK>;
     sa_status st = SA_OK;
     const size_t lds = 256 + C::BASE + C::MAX_NB + 4 * (size_t)g.nb + (COMP ? 4 * (BLK + 1) : 0);
-    static bool configured = false;
-    if (!configured) {
-        const int most = 256 + C::BASE + C::MAX_NB + 4 * C::MAX_NB + 4 * (BLK + 1);
-        st = hip_check(hipFuncSetAttribute((const void*)k_bsattn_fwd<D, BLK, COMP>,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, most),
-                       "k_bsattn_fwd shared memory");
-        if (st != SA_OK) return st;
-        configured = true;
-    }
+    const int most = 256 + C::BASE + C::MAX_NB + 4 * C::MAX_NB + 4 * (BLK + 1);
+    st = ensure_max_lds((const void*)k_bsattn_fwd<D, BLK, COMP>, most, "k_bsattn_fwd shared memory");
+    if (st != SA_OK) return st;
     if (a.rows == 0) return SA_OK;
-    // as many workgroups as the chip holds at once (LDS per workgroup depends
-    // on nb, so the answer is cached per size)
-    static int resident = 0;
-    static size_t resident_lds = 0;
-    if (resident == 0 || resident_lds != lds) {
-        int dev = 0, cus = 0, per_cu = 0;
-        if ((st = hip_check(hipGetDevice(&dev), "hipGetDevice")) != SA_OK) return st;
-        st = hip_check(hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev),
-                       "multiprocessor count");
-        if (st != SA_OK) return st;
-        st = hip_check(hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                           &per_cu, (const void*)k_bsattn_fwd<D, BLK, COMP>, C::NT, lds),
-                       "occupancy query");
-        if (st != SA_OK) return st;
-        resident = cus * (per_cu > 0 ? per_cu : 1);
-        resident_lds = lds;
-    }
+    // as many workgroups as the chip holds at once (LDS per workgroup depends on nb)
+    int resident = 0;
+    st = resident_workgroups((const void*)k_bsattn_fwd<D, BLK, COMP>, C::NT, lds, &resident);
+    if (st != SA_OK) return st;
     const int64_t grid = a.rows < resident ? a.rows : resident;
     hipLaunchKernelGGL((k_bsattn_fwd<D, BLK, COMP>), dim3((unsigned)grid), dim3(C::NT), lds, stream, a);
     return hip_check(hipGetLastError(), "k_bsattn_fwd launch");

@@ -399,6 +399,14 @@ __device__ __forceinline__ uint64_t xor_lane_u64(uint64_t v) {
     return ((uint64_t)hi << 32) | lo;
 }
 
+// Hand-off between lanes of one wave through LDS: every LDS access the wave
+// issued before it has completed (its writes and atomics are visible to every
+// lane) before any access after it.
+__device__ __forceinline__ void wave_lds_sync() {
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_wave_barrier();
+}
+
 // one compare-exchange stage across lanes (partner lane ^ M)
 template <int E, int M>
 __device__ __forceinline__ void cross_stage(uint64_t (&k)[E], int lane, int size, int stride) {
@@ -457,6 +465,7 @@ __global__ __launch_bounds__(kThreads) void k_select_w(SelectArgs a) {
     const int h = (int)((row / nb) % a.H);
     uint32_t* bits = s_bits[wv];
     for (int w = lane; w < kSelMaxWords; w += 64) bits[w] = 0;
+    wave_lds_sync();
     auto mark = [&](int j) {
         if ((uint32_t)j < (uint32_t)nb) atomicOr(&bits[j >> 5], 1u << (j & 31));
     };
@@ -478,10 +487,13 @@ __global__ __launch_bounds__(kThreads) void k_select_w(SelectArgs a) {
                 uint32_t krem = (uint32_t)m;
                 for (int pass = 0; pass < 8; ++pass) {
                     const int sh = 56 - 8 * pass;
+                    wave_lds_sync();          // the last pass's reads are done
                     for (int b = lane; b < 256; b += 64) hist[b] = 0;
+                    wave_lds_sync();
 #pragma unroll
                     for (int r = 0; r < E; ++r)
                         if ((k[r] & mask) == prefix) atomicAdd(&hist[(uint32_t)(k[r] >> sh) & 255u], 1u);
+                    wave_lds_sync();
                     uint32_t c[4];
 #pragma unroll
                     for (int q = 0; q < 4; ++q) c[q] = hist[lane * 4 + q];
@@ -529,6 +541,7 @@ __global__ __launch_bounds__(kThreads) void k_select_w(SelectArgs a) {
             // the running sum strictly in rank order, by one lane, 8 values
             // per LDS round trip; the ranks past nb add +0.0, which leaves a
             // non-negative sum unchanged
+            wave_lds_sync();
             if (lane == 0) {
                 double run = 0.0;
                 for (int c = 0; c < nb; c += 8) {
@@ -544,6 +557,7 @@ __global__ __launch_bounds__(kThreads) void k_select_w(SelectArgs a) {
                     for (int q = 0; q < 8; ++q) cum[c + q] = v[q];
                 }
             }
+            wave_lds_sync();
             // the cut: the first rank whose running sum reaches mass x total
             const double thr = (double)a.mass * cum[nb - 1];
             int first = E;
@@ -589,6 +603,7 @@ __global__ __launch_bounds__(kThreads) void k_select_w(SelectArgs a) {
         const int64_t step = nb / a.n_anchors;
         for (int m = lane; m < a.n_anchors; m += 64) mark((int)((a.anchor_offset + m * step) % nb));
     }
+    wave_lds_sync();
     uint32_t* out = a.bits + row * (int64_t)a.words;
     int local = 0;
     for (int w = lane; w < a.words; w += 64) {
@@ -712,10 +727,8 @@ sa_status launch_score_t(const float* qm, const float* km, float* S, int nb, int
     const dim3 grid((nb + TB - 1) / TB, (nb + TB - 1) / TB, (unsigned)BH);
     const size_t lds = 2 * TB * (SPB * kScoreChunk + 4) * sizeof(float);
     if (lds > 65536) {
-        sa_status st = hip_check(hipFuncSetAttribute((const void*)k_score<D, SPB, MT>,
-                                                     hipFuncAttributeMaxDynamicSharedMemorySize,
-                                                     (int)lds),
-                                 "k_score shared memory");
+        sa_status st = ensure_max_lds((const void*)k_score<D, SPB, MT>, (int)lds,
+                                      "k_score shared memory");
         if (st != SA_OK) return st;
     }
     hipLaunchKernelGGL((k_score<D, SPB, MT>), grid, dim3(kThreads), lds, s, qm, km, S, nb, n_units,
@@ -890,15 +903,8 @@ sa_status launch_select(const Geometry& g, const SelectPlan& p, const int32_t* k
         // mass rule: the running sums of each wave's row in LDS
         const size_t lds = p.rule == SA_RULE_MASS ? (size_t)kSelWaves * 64 * E * sizeof(double) : 0;
         if (E == 32 && lds > 0) {
-            static bool configured = false;
-            if (!configured) {
-                st = hip_check(hipFuncSetAttribute((const void*)k_select_w<32>,
-                                                   hipFuncAttributeMaxDynamicSharedMemorySize,
-                                                   (int)lds),
-                               "k_select shared memory");
-                if (st != SA_OK) return st;
-                configured = true;
-            }
+            st = ensure_max_lds((const void*)k_select_w<32>, (int)lds, "k_select shared memory");
+            if (st != SA_OK) return st;
         }
         switch (E) {
         case 1: hipLaunchKernelGGL(k_select_w<1>, grid, dim3(kThreads), lds, stream, sa); break;

@@ -6,6 +6,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <map>
+#include <mutex>
 #include <string>
 
 #include "sa_internal.h"
@@ -32,6 +34,60 @@ sa_status hip_check(hipError_t e, const char* what) {
 }
 
 static void clear_error() { g_last_error.clear(); }
+
+// Per-device launch set-up memo (see sa_internal.h).
+namespace {
+struct LaunchKey {
+    int dev;
+    const void* fn;
+    int threads;
+    size_t lds;
+    bool operator<(const LaunchKey& o) const {
+        if (dev != o.dev) return dev < o.dev;
+        if (fn != o.fn) return fn < o.fn;
+        if (threads != o.threads) return threads < o.threads;
+        return lds < o.lds;
+    }
+};
+std::mutex g_launch_mu;
+std::map<LaunchKey, int> g_max_lds;      // (dev, fn) -> dynamic LDS limit set
+std::map<LaunchKey, int> g_resident;     // (dev, fn, threads, lds) -> workgroups
+}  // namespace
+
+sa_status ensure_max_lds(const void* fn, int bytes, const char* what) {
+    int dev = 0;
+    sa_status st = hip_check(hipGetDevice(&dev), "hipGetDevice");
+    if (st != SA_OK) return st;
+    std::lock_guard<std::mutex> lock(g_launch_mu);
+    const LaunchKey key{dev, fn, 0, 0};
+    auto it = g_max_lds.find(key);
+    if (it != g_max_lds.end() && it->second >= bytes) return SA_OK;
+    st = hip_check(hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, bytes), what);
+    if (st == SA_OK) g_max_lds[key] = bytes;
+    return st;
+}
+
+sa_status resident_workgroups(const void* fn, int threads, size_t lds, int* out) {
+    int dev = 0;
+    sa_status st = hip_check(hipGetDevice(&dev), "hipGetDevice");
+    if (st != SA_OK) return st;
+    std::lock_guard<std::mutex> lock(g_launch_mu);
+    const LaunchKey key{dev, fn, threads, lds};
+    auto it = g_resident.find(key);
+    if (it != g_resident.end()) {
+        *out = it->second;
+        return SA_OK;
+    }
+    int cus = 0, per_cu = 0;
+    st = hip_check(hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev),
+                   "multiprocessor count");
+    if (st != SA_OK) return st;
+    st = hip_check(hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, threads, lds),
+                   "occupancy query");
+    if (st != SA_OK) return st;
+    *out = g_resident[key] = cus * (per_cu > 0 ? per_cu : 1);
+    return SA_OK;
+}
 
 static bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 

@@ -18,6 +18,15 @@ sa_status hip_check(hipError_t e, const char* what);
 
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// Launch set-up kept per device, safe to call from several host threads:
+// raises a kernel's dynamic-LDS limit to at least `bytes` on the current
+// device (one HIP call per kernel and device, repeated only for a larger
+// size), and the number of workgroups of `threads` threads and `lds` bytes
+// the current device holds at once (one occupancy query per kernel, device
+// and size).  These are the library's only host-side state.
+sa_status ensure_max_lds(const void* fn, int bytes, const char* what);
+sa_status resident_workgroups(const void* fn, int threads, size_t lds, int* out);
+
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 // Geometry derived from a validated sa_problem.

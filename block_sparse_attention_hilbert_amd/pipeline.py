@@ -47,6 +47,10 @@ class BlockSparseAttention:
                  refresh_every: int = 1):
         if refresh_every < 1:
             raise ValueError("refresh_every must be >= 1")
+        if hilbert and spec.window_frames >= 0:
+            # the window is a range of latent frames over raster-ordered blocks;
+            # blocks of Hilbert-ordered tokens span frames in no such order
+            raise ValueError("a latent-frame window needs raster token order (hilbert=False)")
         self.prob, self.spec, self.hilbert = prob, spec, hilbert
         self.refresh_every = int(refresh_every)
         self.calls = 0              # calls made so far (the reuse policy counts them)
@@ -305,6 +309,12 @@ class GraphedCall:
     """
 
     def __init__(self, pipe, Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor):
+        if getattr(pipe.spec, "n_anchors", 0) > 0:
+            # the selection takes the anchor offset by value at launch, so a
+            # replay would repeat the captured call's anchors instead of
+            # rotating them
+            raise ValueError("rotating anchors change on every call; run them eagerly, "
+                             "not as graph replays")
         self.pipe = pipe
         self.inputs = (Q, K, V)
         kw = "reuse" if isinstance(pipe, ClusteredAttention) else "reuse_mask"

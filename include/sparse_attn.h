@@ -39,8 +39,11 @@
  *     N - (nb-1)*block tokens.
  *   - Ownership: the caller allocates and frees every buffer (device memory
  *     for tensors, masks and workspace; host memory for host arrays).  The
- *     library allocates nothing, keeps no state between calls and never
- *     synchronises the stream.
+ *     library allocates no memory and never synchronises the stream.  Its
+ *     only state between calls is host-side launch set-up, kept per device
+ *     behind a mutex (safe from several host threads): a kernel's LDS limit
+ *     raised once per device and the number of workgroups a device holds
+ *     at once, queried once per kernel, device and size.
  *   - Ordering: device work is enqueued on `stream` (a hipStream_t; NULL is
  *     the default stream) and is asynchronous.  A workspace carries one
  *     call's intermediate state on the device (pooled means, scores, the
@@ -246,8 +249,12 @@ sa_status sparse_attn_centroids(const sa_problem* prob, const void* K, const voi
  *   checked).  O: device bf16 [B,H,N,d].  lse: optional device fp32 [B,H,N],
  *   natural-log log-sum-exp of the logits (including compensation terms).
  * A row with no kept block and no compensation gives O = 0, lse = -inf.
- * Column indices outside [0, nb) are clamped into range (no fault; results
- * for such input are unspecified).
+ * A malformed CSR cannot make the kernel read or write outside its buffers:
+ * column indices outside [0, nb) are clamped into range, a row longer than
+ * nb entries is cut to its first nb, and a row with row_ptr[r+1] < row_ptr[r]
+ * is taken as empty (results for such input are unspecified, but the call
+ * ends normally).  row_ptr itself must hold B*H*nb + 1 entries whose values
+ * index col_idx's capacity.
  * workspace: device, 256-byte aligned, >= sparse_attn_workspace_size(prob,
  *   NULL); it receives V transposed block by block (and the centroid tiles).
  * Precision: QK^T and PV on bf16 matrix cores with fp32 accumulation, softmax

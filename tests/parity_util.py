@@ -16,9 +16,10 @@ TIE_REL = 1e-6       # near-tie band, relative to the row's largest |score|
 # Error-aware routing keys (natural-log units).  The kernel's two contractions
 # carry 16 significant bits per operand (hi/lo bf16 pairs) with fp32
 # accumulation; a float32 emulation of that arithmetic stays within 2e-5 of the
-# float64 keys on the test workloads, so 1e-3 leaves a wide margin.  Two blocks
+# float64 keys on the test workloads and the kernel's measured worst case on
+# the full 1.3B-sized layer is 2.7e-5, so 2e-4 leaves a 7x margin.  Two blocks
 # whose oracle keys are within twice that are a near tie.
-ERR_KEY_ATOL = 1e-3
+ERR_KEY_ATOL = 2e-4
 
 
 def log(*a):
@@ -79,9 +80,13 @@ def mask_report(keep_gpu, case: OracleCase):
         only_g, only_o = np.nonzero(g & ~o)[0], np.nonzero(o & ~g)[0]
         ok = False
         if wl.rule != "none" and only_g.size + only_o.size > 0:
-            # (a) every swapped pair of blocks is a near tie of the oracle scores
+            # (a) every swapped pair of blocks is a near tie of the oracle
+            # scores.  Scored rules see bit-identical scores on both sides, so
+            # equal scores are decided by the index tie-break and a swap of
+            # two equal scores is an error, not a near tie.  Routing keys are
+            # not bit-identical: there the band alone decides.
             if only_g.size and only_o.size:
-                ok = all(s[x] == s[y] or abs(s[x] - s[y]) <= tol
+                ok = all(abs(s[x] - s[y]) <= tol and (wl.rule == "err" or s[x] != s[y])
                          for x in only_g for y in only_o)
             if wl.rule == "mass" and not ok:
                 # (b) the cumulative mass at the cutoff sits within 1e-6 Z of tau Z

@@ -314,3 +314,67 @@ def test_sics_and_tile_mode_reject_before_any_launch():
                                     *outs[:8], None, *outs[:2], fake, 1 << 30, None)
     assert st == sa.SA_ERR_INVALID_ARG
     assert b"shape_idx" in sa.lib.sparse_attn_last_error()
+
+
+def test_binding_checks_tensor_arguments():
+    """The binding checks what the C library cannot see behind a pointer: the
+    dtype, shape, contiguity and device of every tensor, before any call."""
+    import torch
+    p = _prob()
+    tok = (p.B, p.H, p.N, p.d)
+    bf = torch.zeros(tok, dtype=torch.bfloat16)
+    rp = torch.zeros(p.rows + 1, dtype=torch.int32)
+    ci = torch.zeros(p.rows * p.nb, dtype=torch.int32)
+    # dtype: an fp16 Q, an int64 row_ptr
+    with pytest.raises(TypeError, match="Q must be torch.bfloat16"):
+        sa.fwd(p, bf.half(), bf, bf, rp, ci, O=bf, workspace=torch.zeros(16, dtype=torch.uint8))
+    with pytest.raises(TypeError, match="row_ptr must be torch.int32"):
+        sa.fwd_run(p, bf, bf, rp.long(), ci, False, O=bf,
+                   workspace=torch.zeros(16, dtype=torch.uint8))
+    # shape: a [B,N,H,d] view, an output of the wrong size, a short lse
+    with pytest.raises(ValueError, match="K must have shape"):
+        sa.fwd_run(p, bf, bf.transpose(1, 2), rp, ci, False, O=bf,
+                   workspace=torch.zeros(16, dtype=torch.uint8))
+    with pytest.raises(ValueError, match="O must have shape"):
+        sa.fwd_run(p, bf, bf, rp, ci, False, O=bf[:, :, :-1],
+                   workspace=torch.zeros(16, dtype=torch.uint8))
+    with pytest.raises(ValueError, match="lse must have shape"):
+        sa.fwd_run(p, bf, bf, rp, ci, False, O=bf, lse=torch.zeros(p.B, p.H, p.N - 1),
+                   workspace=torch.zeros(16, dtype=torch.uint8))
+    # too few elements: row_ptr of rows entries, col_idx of the select output
+    with pytest.raises(ValueError, match="row_ptr holds"):
+        sa.fwd_run(p, bf, bf, rp[:-1], ci, False, O=bf,
+                   workspace=torch.zeros(16, dtype=torch.uint8))
+    out = sa.Selection(rp, ci[:-1])
+    with pytest.raises(ValueError, match="col_idx holds"):
+        sa.select(p, sa.SelectSpec(rule="mass"), bf, bf, out=out,
+                  workspace=torch.zeros(16, dtype=torch.uint8))
+    # contiguity: a permuted copy with the right shape
+    nc = torch.zeros(p.B, p.H, p.d, p.N, dtype=torch.bfloat16).transpose(2, 3)
+    assert tuple(nc.shape) == tok and not nc.is_contiguous()
+    with pytest.raises(ValueError, match="V must be contiguous"):
+        sa.fwd_prepare(p, nc, rp, workspace=torch.zeros(16, dtype=torch.uint8))
+    # device: everything right but on the host
+    with pytest.raises(ValueError, match="Q must be a GPU tensor"):
+        sa.fwd_run(p, bf, bf, rp, ci, False, O=bf, workspace=torch.zeros(16, dtype=torch.uint8))
+    with pytest.raises(ValueError, match="src must be a GPU tensor"):
+        sa.hilbert_permute(p, bf, torch.zeros(p.N, dtype=torch.int32), bf.clone())
+    with pytest.raises(ValueError, match="perm_dev must have shape"):
+        sa.hilbert_permute(p, bf, torch.zeros(p.N - 1, dtype=torch.int32), bf.clone())
+    # the workspace is raw bytes
+    with pytest.raises(TypeError, match="workspace must be torch.uint8"):
+        sa.fwd_prepare(p, bf, rp, workspace=torch.zeros(16, dtype=torch.float32))
+
+
+def test_pipeline_guards():
+    """A latent-frame window needs raster order; graph replays cannot rotate
+    the anchors the selection takes by value."""
+    from types import SimpleNamespace
+
+    from block_sparse_attention_hilbert_amd.pipeline import BlockSparseAttention, GraphedCall
+    with pytest.raises(ValueError, match="raster token order"):
+        BlockSparseAttention(_prob(), sa.SelectSpec(rule="none", window_frames=1), hilbert=True,
+                             device="cpu")
+    fake_pipe = SimpleNamespace(spec=sa.SelectSpec(rule="none", window_frames=1, n_anchors=4))
+    with pytest.raises(ValueError, match="rotating anchors"):
+        GraphedCall(fake_pipe, None, None, None)
