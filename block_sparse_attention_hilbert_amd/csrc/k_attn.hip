@@ -184,6 +184,43 @@ __device__ __forceinline__ void dma_tile(unsigned char* tile, const unsigned cha
     }
 }
 
+// The same copy for a tile whose rows are all in range: lane offsets of copy
+// instruction n are off0 + n NWI 1 KB (the swizzle of a row depends on the row
+// modulo the chunks per row, which a step of NWI KB does not change), and M0
+// advances by NWI KB per instruction.  Two instructions per assembly block;
+// every M0 value is formed outside the assembly (SALU arithmetic inside it
+// would change SCC behind the compiler's back).
+template <int INSTR, int NWI>
+__device__ __forceinline__ void dma_tile_fast(unsigned char* tile, const unsigned char* base,
+                                              uint32_t off0, int wi) {
+    static_assert(INSTR % 2 == 0, "an even number of copy instructions per wave and tile");
+    constexpr uint32_t STRIDE = NWI * 1024;
+    const uint32_t dst = __builtin_amdgcn_readfirstlane(
+        (uint32_t)(uintptr_t)(lds_void_t*)tile + (uint32_t)wi * 1024u);
+    const uint64_t b = (uint64_t)(uintptr_t)base;
+    const uint64_t ub = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32)) << 32) |
+                        (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b);
+    const unsigned char* sbase = reinterpret_cast<const unsigned char*>((uintptr_t)ub);
+#pragma unroll
+    for (int n = 0; n < INSTR; n += 2) {
+        const uint32_t d0 = __builtin_amdgcn_readfirstlane(dst + n * STRIDE);
+        const uint32_t d1 = __builtin_amdgcn_readfirstlane(dst + (n + 1) * STRIDE);
+        uint32_t saved;
+        asm volatile(
+            "s_mov_b32 %0, m0\n\t"
+            "s_mov_b32 m0, %1\n\t"
+            "s_nop 0\n\t"
+            "global_load_lds_dwordx4 %3, %5\n\t"
+            "s_mov_b32 m0, %2\n\t"
+            "s_nop 0\n\t"
+            "global_load_lds_dwordx4 %4, %5\n\t"
+            "s_mov_b32 m0, %0"
+            : "=&s"(saved)
+            : "s"(d0), "s"(d1), "v"(off0 + n * STRIDE), "v"(off0 + (n + 1) * STRIDE), "s"(sbase)
+            : "memory");
+    }
+}
+
 // One row = one (batch, head, query block): all its kept tiles, then (with
 // compensation) the centroid tiles, then the merge of the two key halves.
 template <int D, int BLK, bool COMP>
@@ -253,30 +290,50 @@ __device__ __forceinline__ void process_row(const FwdArgs& a, int64_t row, unsig
     }
 
     // copies of tile u (kept block list[u], or centroid tile u - nk) into slot b
-    auto issue_k = [&](int u, int b) {
+    // Copies of tile u (kept block j = list[u], read by the caller ahead of
+    // time, or centroid tile u - nk) into slot b.  Tiles whose rows are all in
+    // range take the fast path with this lane's precomputed offsets; a short
+    // last block or centroid tile has its rows clamped (finite, masked by the
+    // bias).
+    const uint32_t koff0 = dma_src_offset<C::KRB, C::NWI>(0, wave, lane, BLK - 1);
+    const uint32_t voff0 = dma_src_offset<C::VRB, C::NWI>(0, wave, lane, D - 1);
+    auto issue_k = [&](int u, int b, int j) {
         unsigned char* dst = kslot + b * C::K_BYTES;
         if (!COMP || u < nk) {
-            const int j = __builtin_amdgcn_readfirstlane(list[u]);
             const unsigned char* src = Kh + (int64_t)j * BLK * C::KRB;
-            // a short last block has its rows clamped (finite, masked by the bias)
-            dma_tile<C::KRB, C::KI, C::NWI>(dst, src, j == a.nb - 1 ? last_n - 1 : BLK - 1, wave, lane);
+            if (j == a.nb - 1 && last_n < BLK)
+                dma_tile<C::KRB, C::KI, C::NWI>(dst, src, last_n - 1, wave, lane);
+            else
+                dma_tile_fast<C::KI, C::NWI>(dst, src, koff0, wave);
         } else {
             const int j0 = (u - nk) * BLK;
             const int nval = a.nb - j0 < BLK ? a.nb - j0 : BLK;
-            dma_tile<C::KRB, C::KI, C::NWI>(dst, reinterpret_cast<const unsigned char*>(
-                                                     a.kbar + (bh * a.nb + j0) * (int64_t)D),
-                                            nval - 1, wave, lane);
+            const unsigned char* src =
+                reinterpret_cast<const unsigned char*>(a.kbar + (bh * a.nb + j0) * (int64_t)D);
+            if (nval < BLK)
+                dma_tile<C::KRB, C::KI, C::NWI>(dst, src, nval - 1, wave, lane);
+            else
+                dma_tile_fast<C::KI, C::NWI>(dst, src, koff0, wave);
         }
     };
-    auto issue_v = [&](int u, int b) {
+    auto issue_v = [&](int u, int b, int j) {
         unsigned char* dst = vslot + b * C::V_BYTES;
         const unsigned char* src;
         if (!COMP || u < nk)
-            src = Vth + (int64_t)__builtin_amdgcn_readfirstlane(list[u]) * D * C::VRB;
+            src = Vth + (int64_t)j * D * C::VRB;
         else
             src = reinterpret_cast<const unsigned char*>(a.vbart + (bh * a.ntc + (u - nk)) * (int64_t)D * BLK);
-        dma_tile<C::VRB, C::VI, C::NWI>(dst, src, D - 1, wave, lane);
+        dma_tile_fast<C::VI, C::NWI>(dst, src, voff0, wave);
     };
+    // list entry u, clamped into the list (entries past it are centroid tiles
+    // or past the row: their value is not used)
+    auto list_at = [&](int u) -> int { return (int)list[u < nk ? u : (nk > 0 ? nk - 1 : 0)]; };
+    // the list index of the short last block of the sequence, if the row keeps it
+    const int short_u = !var_cnt && last_n < BLK && nk > 0 &&
+                                __builtin_amdgcn_readfirstlane(list_at(nk - 1)) == a.nb - 1
+                            ? nk - 1
+                            : -1;
+
 
     f32x16 oacc[D / 32];
 #pragma unroll
@@ -368,7 +425,7 @@ __device__ __forceinline__ void process_row(const FwdArgs& a, int64_t row, unsig
         if (!cent) {
             if (var_cnt)
                 nval = __builtin_amdgcn_readfirstlane((int)lcnt[u]);
-            else if (last_n < BLK && __builtin_amdgcn_readfirstlane(list[u]) == a.nb - 1)
+            else if (u == short_u)
                 nval = last_n;
         }
         if (cent || nval < BLK) {
@@ -427,16 +484,20 @@ __device__ __forceinline__ void process_row(const FwdArgs& a, int64_t row, unsig
     // vector phase (softmax of S_{t+1}).  A barrier precedes each phase; the
     // lagging group passes one extra barrier first, the leading one after the
     // last step, so both pass the same number.
+    // block indices of the next step's copies, read from LDS one step ahead
+    int pre_k = 0, pre_v = 0;
     if (T > 0) {
-        if (issuer) issue_k(0, 0);
+        if (issuer) issue_k(0, 0, __builtin_amdgcn_readfirstlane(list_at(0)));
         copies_done();
         wg_barrier();
         if (lagging) wg_barrier();
         // step -1: S_0
         wg_barrier();
         if (issuer) {
-            if (T > 1) issue_k(1, 1);
-            issue_v(0, 0);
+            if (T > 1) issue_k(1, 1, __builtin_amdgcn_readfirstlane(list_at(1)));
+            issue_v(0, 0, __builtin_amdgcn_readfirstlane(list_at(0)));
+            pre_k = list_at(2);
+            pre_v = list_at(1);
         }
         matrix_phase(no{}, yes{}, -1);
         if (C::PING) wg_barrier();
@@ -445,8 +506,11 @@ __device__ __forceinline__ void process_row(const FwdArgs& a, int64_t row, unsig
         for (int t = 0; t + 1 < T; ++t) {
             wg_barrier();
             if (issuer) {
-                if (t + 2 < T) issue_k(t + 2, t & 1);
-                issue_v(t + 1, (t + 1) & 1);
+                const int jk = __builtin_amdgcn_readfirstlane(pre_k), jv = __builtin_amdgcn_readfirstlane(pre_v);
+                if (t + 2 < T) issue_k(t + 2, t & 1, jk);
+                issue_v(t + 1, (t + 1) & 1, jv);
+                pre_k = list_at(t + 3);
+                pre_v = list_at(t + 2);
             }
             matrix_phase(yes{}, yes{}, t);
             if (C::PING) wg_barrier();
