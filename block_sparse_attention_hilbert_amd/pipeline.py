@@ -217,8 +217,11 @@ class ClusteredAttention:
             self.lse = torch.empty(prob.B, prob.H, prob.N, dtype=torch.float32,
                                    device=self.device)
 
-    def run_cluster(self, Q, K, V):
-        if self.cspec.mode == "tiles":
+    def run_cluster(self, Q, K, V, choose_shapes: bool = True):
+        """Form the partition.  In tile mode SICS first picks each head's tile
+        shape, unless ``choose_shapes`` is False: then the shapes already in
+        ``self.shape_idx`` (set by the caller) are used."""
+        if self.cspec.mode == "tiles" and choose_shapes:
             sics(self.prob, self.cspec, Q, K, self.shape_idx, self.shape_scores,
                  workspace=self.ws_cluster)
         cluster(self.prob, self.cspec, Q, K, V if self.spec.want_comp else None, out=self.cl,
@@ -259,15 +262,18 @@ class ClusteredAttention:
                         self.lse)
         return self.O
 
-    def __call__(self, Q, K, V, reuse: Optional[bool] = None) -> torch.Tensor:
+    def __call__(self, Q, K, V, reuse: Optional[bool] = None,
+                 choose_shapes: bool = True) -> torch.Tensor:
         """One call.  ``reuse``: keep the partition and selection (True), form
-        them anew (False) or follow the refresh policy (None)."""
+        them anew (False) or follow the refresh policy (None).
+        ``choose_shapes``: in tile mode, False keeps the caller's per-head
+        shapes in ``self.shape_idx`` instead of running SICS."""
         if reuse is None:
             reuse = self.reuses_next()
         if reuse and not self.have_partition:
             raise RuntimeError("no partition to reuse: the first call must cluster")
         if not reuse:
-            self.run_cluster(Q, K, V)
+            self.run_cluster(Q, K, V, choose_shapes=choose_shapes)
         self.run_gather(Q, K, V)
         if reuse:
             self.run_centroids()

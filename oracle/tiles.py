@@ -104,17 +104,14 @@ def max_tiles(grid, shapes: Sequence[Shape]) -> int:
     return max(n_tiles(*grid, s) for s in shapes)
 
 
-def tiles_workload_head(wl, Qh, Kh, shape_idx=None):
+def tiles_workload_head(wl, Qh, Kh):
     """The tiled path of one head (duck-typed workload: T, Hg, W, block,
-    tile_shapes, scale, rule, density, mass, diag).  ``shape_idx`` overrides
-    the SICS choice (to follow the other side's pick on a near tie).  Returns
-    the same dict as ``clusters.cluster_workload_head`` plus the shape scores
-    and the chosen shape."""
+    tile_shapes, scale, rule, density, mass, diag).  Returns the same dict as
+    ``clusters.cluster_workload_head`` plus the shape scores and the chosen
+    shape."""
     grid = (wl.T, wl.Hg, wl.W)
     shapes = [tuple(s) for s in wl.tile_shapes]
     pick, scores = choose_shape(Qh, Kh, grid, shapes)
-    if shape_idx is not None:
-        pick = int(shape_idx)
     C = max_tiles(grid, shapes)
     a = tile_assign(*grid, shapes[pick])
     N = Qh.shape[0]

@@ -21,7 +21,7 @@ import oracle
 from oracle import clusters as OC
 from oracle import tiles as OT
 import workloads as W
-from parity_util import ATOL_MAX, ATOL_MEAN, LSE_ATOL, TIE_REL, from_dev, log, to_dev
+from parity_util import ATOL_MAX, ATOL_MEAN, LSE_ATOL, TIE_REL, from_dev, log, poison, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -113,20 +113,52 @@ def _excused(S_row, nk, wl, gk, ok):
 
 def check_case(wl, Q, K, V, heads, q_clusters_per_head=None, seed=0):
     """Runs the clustered call on the GPU and checks the heads `heads` (indices
-    into b * H + h) against the oracle.  Returns the attention errors."""
+    into b * H + h) against the oracle.  Returns the attention errors.
+
+    In tile mode the oracle picks each head's shape first.  Where the GPU's
+    pick differs -- allowed only as a near tie of the two shapes' fp64 scores
+    (1e-9 relative) -- the call is run again on the GPU with the oracle's picks
+    forced in, so the partition, selection and attention are checked against
+    the oracle's own choice (the oracle never takes a value from the GPU)."""
     pipe = _pipe(wl)
-    O = pipe(to_dev(Q), to_dev(K), to_dev(V))
+    poison(pipe.O, pipe.Op, pipe.lse, pipe.lsep)
+    Qd, Kd, Vd = to_dev(Q), to_dev(K), to_dev(V)
+    O = pipe(Qd, Kd, Vd)
     torch.cuda.synchronize()
+    tiles = wl.cluster == "tiles"
+    refs = {}
+    excused = 0
+    if tiles:
+        pick_gpu = pipe.shape_idx.cpu().numpy()
+        sc_gpu = pipe.shape_scores.cpu().numpy()
+        forced = pick_gpu.copy()
+        for bh in heads:
+            b, h = divmod(bh, wl.H)
+            q, k = oracle.bf16_to_f64(Q[b, h]), oracle.bf16_to_f64(K[b, h])
+            ref = OT.tiles_workload_head(wl, q, k)
+            tag = f"{wl.name} bh={bh}"
+            assert np.allclose(sc_gpu[bh], ref["scores"], rtol=1e-9, atol=1e-12), tag
+            if pick_gpu[bh] != ref["pick"]:
+                top = ref["scores"]
+                assert abs(top[pick_gpu[bh]] - top[ref["pick"]]) <= 1e-9 * np.abs(top).max(), tag
+                excused += 1
+                forced[bh] = ref["pick"]
+            refs[bh] = ref
+        if excused:
+            log(f"[cluster] {wl.name}: {excused} near-tie shape picks; rerun with the oracle's")
+            pipe.shape_idx.copy_(torch.from_numpy(forced))
+            poison(pipe.O, pipe.Op, pipe.lse, pipe.lsep)
+            O = pipe(Qd, Kd, Vd, reuse=False, choose_shapes=False)
+            torch.cuda.synchronize()
+            assert np.array_equal(pipe.shape_idx.cpu().numpy(), forced)
+    assert not np.any((from_dev(O) & 0x7F80) == 0x7F80), "O holds NaN/Inf: rows not written"
+    assert not np.any(np.isnan(pipe.lse.cpu().numpy())), "lse holds NaN: rows not written"
     C, nbp, blk = wl.n_clusters, pipe.nbp, wl.block
     cl, sel = pipe.cl, pipe.sel
     g = {k: getattr(cl, k).cpu().numpy() for k in
          ("q_order", "k_order", "q_blk", "k_blk", "q_cnt", "k_cnt", "q_cent", "k_cent",
           "q_count", "k_count")}
     v_cent = cl.v_cent.cpu().numpy() if cl.v_cent is not None else None
-    tiles = wl.cluster == "tiles"
-    if tiles:
-        pick_gpu = pipe.shape_idx.cpu().numpy()
-        sc_gpu = pipe.shape_scores.cpu().numpy()
     S_gpu = sel.scores.cpu().numpy()
     rp = sel.row_ptr.cpu().numpy().astype(np.int64)
     ci = sel.col_idx.cpu().numpy()
@@ -139,7 +171,7 @@ def check_case(wl, Q, K, V, heads, q_clusters_per_head=None, seed=0):
     km = sel.k_mean.cpu().numpy() if sel.k_mean is not None else None
     vs = sel.v_sum.cpu().numpy() if sel.v_sum is not None else None
     rng = np.random.default_rng(seed)
-    errs, lse_errs, excused = [], [], 0
+    errs, lse_errs = [], []
     picks = []
     for bh in heads:
         b, h = divmod(bh, wl.H)
@@ -148,14 +180,7 @@ def check_case(wl, Q, K, V, heads, q_clusters_per_head=None, seed=0):
         v = oracle.bf16_to_f64(V[b, h])
         tag = f"{wl.name} bh={bh}"
         if tiles:
-            ref = OT.tiles_workload_head(wl, q, k)
-            assert np.allclose(sc_gpu[bh], ref["scores"], rtol=1e-9, atol=1e-12), tag
-            if pick_gpu[bh] != ref["pick"]:
-                # a near tie of the two shapes' scores; follow the GPU's pick
-                top = ref["scores"]
-                assert abs(top[pick_gpu[bh]] - top[ref["pick"]]) <= 1e-9 * np.abs(top).max(), tag
-                excused += 1
-                ref = OT.tiles_workload_head(wl, q, k, shape_idx=pick_gpu[bh])
+            ref = refs[bh]
             picks.append(int(ref["pick"]))
         else:
             ref = OC.cluster_workload_head(wl, q, k)
@@ -230,12 +255,11 @@ def test_small_cluster_parity(name):
 def test_full_size_cluster_parity(name):
     """The full 1.3B-sized layer (12 heads, N = 32,760): the whole call on the
     GPU; layouts, centroids, scores and keep of two heads checked exactly and
-    the output of 6 sampled query clusters per checked head."""
+    the output of every query cluster of both checked heads."""
     wl = W.by_name(name)
     log(f"[cluster-full] {name}: N={wl.N} H={wl.H} C={wl.n_clusters}")
     Q, K, V = W.make_qkv(wl)
-    emax, emean, lmax, exc = check_case(wl, Q, K, V, heads=[0, wl.H - 1],
-                                        q_clusters_per_head=6, seed=1)
+    emax, emean, lmax, exc = check_case(wl, Q, K, V, heads=[0, wl.H - 1], seed=1)
     log(f"[cluster-full] {name}: max {emax:.2e} mean {emean:.2e} lse {lmax:.2e} excused {exc}")
     assert emax <= ATOL_MAX and emean <= ATOL_MEAN and lmax <= LSE_ATOL
 

@@ -13,7 +13,8 @@ import pytest
 import oracle
 import workloads as W
 from parity_util import (ATOL_MAX, ATOL_MEAN, ERR_KEY_ATOL, LSE_ATOL, OracleCase,
-                         compare_attention, compare_keys, from_dev, log, mask_report, to_dev)
+                         assert_outputs_written, compare_attention, compare_keys, from_dev, log,
+                         mask_report, poison, to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -79,8 +80,10 @@ def test_small_workload_parity(name):
     off = W.anchor_offset(wl.seed, 0, wl.nb)
     case = OracleCase(wl, Q, K, V, anchor_offset=off)
     pipe = _pipeline(wl)
+    poison(pipe.O, pipe.lse, getattr(pipe, "Op", None))
     O = pipe(to_dev(Q), to_dev(K), to_dev(V), anchor_offset=off)
     torch.cuda.synchronize()
+    assert_outputs_written(from_dev(O), pipe.lse.cpu().numpy(), wl, pipe.keep_mask())
 
     if wl.rule == "err":
         S = pipe.sel.scores.view(wl.B, wl.H, wl.nb, wl.nb).cpu().numpy()
@@ -119,8 +122,11 @@ def test_small_workload_parity(name):
     # attention given the oracle's mask
     rp, ci = oracle.keep_to_csr(case.keep.reshape(-1, wl.nb))
     Qp, Kp, Vp = pipe.permute_inputs(to_dev(Q), to_dev(K), to_dev(V))
+    poison(pipe.O, pipe.lse, getattr(pipe, "Op", None))
     pipe.run_fwd(Qp, Kp, Vp, torch.from_numpy(rp).cuda(), torch.from_numpy(ci).cuda())
     O = pipe.unpermute_output()
+    torch.cuda.synchronize()
+    assert_outputs_written(from_dev(O), pipe.lse.cpu().numpy(), wl, case.keep)
     lse = pipe.lse.cpu().numpy()
     if wl.hilbert:
         lse = lse[..., np.argsort(pipe.perm)]            # back to raster order
@@ -291,3 +297,77 @@ def test_mask_reuse_across_steps(name):
         assert emax <= ATOL_MAX and emean <= ATOL_MEAN and lmax <= LSE_ATOL
     # the drift is large enough that a fresh selection would have differed
     assert changed_total > 0
+
+
+def test_largest_attention_window():
+    """The largest attention the interface admits: nb = 4096 blocks of 128
+    tokens at d = 128 (the most LDS a workgroup takes), with a +-0-frame window
+    (LVSA abstract: a temporal window) so that the oracle stays cheap: every
+    row keeps the blocks of its own latent frame(s).  Every output row written;
+    every 8th query block (and the first and last) against the oracle."""
+    wl = W.CONFIGS[4].replace(T=128, Hg=64, W=64, H=1, gen="iid", window_frames=0, n_anchors=0)
+    assert wl.nb == 4096 and wl.d == 128 and wl.block == 128
+    Q, K, V = W.make_qkv(wl)
+    case = OracleCase(wl, Q, K, V)
+    pipe = _pipeline(wl, want_scores=False)
+    poison(pipe.O, pipe.lse)
+    O = pipe(to_dev(Q), to_dev(K), to_dev(V))
+    torch.cuda.synchronize()
+    keep = pipe.keep_mask()
+    assert np.array_equal(keep, case.keep)
+    Og = from_dev(O)
+    assert_outputs_written(Og, pipe.lse.cpu().numpy(), wl, keep)
+    qb = sorted(set([0, wl.nb - 1] + list(range(0, wl.nb, 8))))
+    O_ref, lse_ref = case.attention(0, 0, q_blocks=qb)
+    bounds = oracle.block_bounds(wl.N, wl.block)
+    og = oracle.bf16_to_f64(Og[0, 0])
+    lg = pipe.lse.cpu().numpy()[0, 0].astype(np.float64)
+    e = np.concatenate([np.abs(og[bounds[i]:bounds[i + 1]] - O_ref[bounds[i]:bounds[i + 1]]).ravel()
+                        for i in qb])
+    le = max(float(np.abs(lg[bounds[i]:bounds[i + 1]] - lse_ref[bounds[i]:bounds[i + 1]]).max())
+             for i in qb)
+    log(f"[parity] nb=4096 window: density={keep.mean():.4f} attention on {len(qb)} query blocks "
+        f"max={e.max():.2e} mean={e.mean():.2e} lse={le:.2e}")
+    assert e.max() <= ATOL_MAX and e.mean() <= ATOL_MEAN and le <= LSE_ATOL
+
+
+def test_malformed_csr_is_contained():
+    """A caller's CSR with a row longer than nb entries and a row whose end
+    precedes its start: the kernel cuts the first to nb entries and takes the
+    second as empty, ends normally and writes every other row as usual."""
+    sa = _sa()
+    wl = SMALL["mass_d128_b128"]
+    prob = sa.problem_for(wl)
+    Q, K, V = (to_dev(x) for x in W.make_qkv(wl))
+    nb, rows = prob.nb, prob.rows
+    keep = np.zeros((rows, nb), dtype=bool)
+    keep[:, 0] = True
+    keep[np.arange(rows), np.arange(rows) % nb] = True
+    rp, ci = oracle.keep_to_csr(keep)
+    # row 1: 3 nb entries (every block three times); row 2: end before start
+    long_cols = np.tile(np.arange(nb, dtype=np.int32), 3)
+    lens = np.diff(rp).astype(np.int64)
+    lens[1] = long_cols.size
+    rp2 = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    ci2 = np.concatenate([ci[: rp[1]], long_cols, ci[rp[2]:]]).astype(np.int32)
+    rp2[3] = rp2[2] - 1                       # row 2 ends one entry before it starts
+    ci2 = np.concatenate([ci2, np.zeros(4 * nb, np.int32)])
+    O = torch.empty_like(Q)
+    poison(O)
+    out, lse = sa.fwd(prob, Q, K, V, torch.from_numpy(rp2).cuda(), torch.from_numpy(ci2).cuda(),
+                      O=O, want_lse=True)
+    torch.cuda.synchronize()
+    Og = from_dev(out)
+    assert not np.any((Og & 0x7F80) == 0x7F80), "every row written, no NaN"
+    lse = lse.cpu().numpy()                    # [B, H, N]
+    bounds = oracle.block_bounds(wl.N, wl.block)
+    # row 2 (batch 0, head 0, query block 2) attended to nothing: O = 0, lse = -inf
+    assert np.all(Og[0, 0, bounds[2]:bounds[3]] == 0)
+    assert np.all(np.isneginf(lse[0, 0, bounds[2]:bounds[3]]))
+    assert not np.any(np.isnan(lse))
+    # row 1 attended to the first nb entries of its list: every block once
+    case = OracleCase(wl, *W.make_qkv(wl))
+    case.keep = np.ones((wl.B, wl.H, nb, nb), dtype=bool)
+    O_ref, _ = case.attention(0, 0, q_blocks=[1])
+    e = np.abs(oracle.bf16_to_f64(Og[0, 0, bounds[1]:bounds[2]]) - O_ref[bounds[1]:bounds[2]])
+    assert e.max() <= ATOL_MAX

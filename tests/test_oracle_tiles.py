@@ -140,6 +140,3 @@ def test_tiles_workload_head_layout_is_one_block_per_tile():
         assert np.array_equal(toks[toks >= 0], np.nonzero(a == j)[0])
     # the means are the tiles' exact means
     assert np.array_equal(ref["cq"], OC.cluster_means(Q, a, C))
-    # a near-tie override takes the given shape
-    other = (ref["pick"] + 1) % len(MENU)
-    assert OT.tiles_workload_head(wl, Q, K, shape_idx=other)["pick"] == other
