@@ -8,6 +8,7 @@ stream.  The functions mirror the C ABI in ``include/sparse_attn.h``:
 * :func:`hilbert_perm_build` -- host Hilbert order of a latent grid
 * :func:`hilbert_permute`, :func:`hilbert_unpermute` -- token reordering
 * :func:`select` -- ``sparse_attn_select``: keep lists as CSR
+  (:func:`select_noalloc`: the same with the library's fixed scratch)
 * :func:`fwd` -- ``sparse_attn_fwd``: block-sparse attention (+ compensation)
 * :func:`fwd_prepare`, :func:`fwd_run` -- its two halves
   (:func:`fwd_prepare_counts`: with a token count per KV block)
@@ -49,7 +50,7 @@ EXPORTS = ("sparse_attn_workspace_size", "hilbert_perm_build", "hilbert_permute"
            "sparse_attn_fwd_prepare_counts", "sparse_attn_cluster_size", "sparse_attn_cluster",
            "sparse_attn_cluster_gather", "sparse_attn_cluster_scatter",
            "sparse_attn_cluster_select", "sparse_attn_cluster_centroids", "sparse_attn_sics",
-           "sparse_attn_last_error")
+           "sparse_attn_select_noalloc", "sparse_attn_last_error")
 
 
 class SaProblem(ctypes.Structure):
@@ -100,6 +101,8 @@ def _load():
     lib.hilbert_unpermute.argtypes = [P(SaProblem), vp, vp, vp, vp]
     lib.sparse_attn_select.argtypes = [P(SaProblem), P(SaSelectSpec), vp, vp, vp, vp, vp, vp,
                                        vp, vp, vp, sz, vp]
+    lib.sparse_attn_select_noalloc.argtypes = [P(SaProblem), P(SaSelectSpec), vp, vp, vp, vp, vp,
+                                               vp, vp, vp, vp]
     lib.sparse_attn_fwd.argtypes = [P(SaProblem), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.sparse_attn_fwd_prepare.argtypes = [P(SaProblem), vp, vp, vp, vp, vp, sz, vp]
     lib.sparse_attn_centroids.argtypes = [P(SaProblem), vp, vp, vp, vp, vp]
@@ -346,6 +349,28 @@ def select(prob: Problem, spec: SelectSpec, Q: torch.Tensor, K: torch.Tensor,
     wp, ws_bytes = _ws(A, workspace)
     _check(A.call(lib.sparse_attn_select, ctypes.byref(prob.c()), ctypes.byref(cs), *args, wp, ws_bytes,
                                   _Stream(stream)))
+    return out
+
+
+def select_noalloc(prob: Problem, spec: SelectSpec, Q: torch.Tensor, K: torch.Tensor,
+                   V: Optional[torch.Tensor] = None, *, out: Selection, stream=None) -> Selection:
+    """sparse_attn_select_noalloc: sparse_attn_select with the library's own
+    fixed scratch instead of a workspace (for callers that cannot allocate;
+    the output buffers in ``out`` are the caller's)."""
+    A = _Args()
+    nb, rows = prob.nb, prob.rows
+    cs, keep = spec.c()
+    tok, stat = _tokens(prob), (prob.B, prob.H, nb, prob.d)
+    args = [A(Q, "Q", _BF16, shape=tok, optional=True),
+            A(K, "K", _BF16, shape=tok, optional=True),
+            A(V, "V", _BF16, shape=tok, optional=True),
+            A(out.row_ptr, "row_ptr", _I32, numel=rows + 1),
+            A(out.col_idx, "col_idx", _I32, numel=rows * nb),
+            A(out.scores, "scores", _F32, numel=rows * nb, optional=True),
+            A(out.k_mean, "k_mean", _F32, shape=stat, optional=True),
+            A(out.v_sum, "v_sum", _F32, shape=stat, optional=True)]
+    _check(A.call(lib.sparse_attn_select_noalloc, ctypes.byref(prob.c()), ctypes.byref(cs), *args,
+                  _Stream(stream)))
     return out
 
 

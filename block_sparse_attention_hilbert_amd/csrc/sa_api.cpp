@@ -33,7 +33,7 @@ sa_status hip_check(hipError_t e, const char* what) {
     return fail(SA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
-static void clear_error() { g_last_error.clear(); }
+void clear_error() { g_last_error.clear(); }
 
 // Per-device launch set-up memo (see sa_internal.h).
 namespace {
@@ -92,7 +92,7 @@ sa_status resident_workgroups(const void* fn, int threads, size_t lds, int* out)
 static bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 // Validates the problem statement and fills the derived geometry.
-static sa_status check_problem(const sa_problem* p, Geometry* g) {
+sa_status check_problem(const sa_problem* p, Geometry* g) {
     if (!p) return fail(SA_ERR_INVALID_ARG, "prob is NULL");
     if (p->B < 1 || p->H < 1 || p->N < 1)
         return fail(SA_ERR_INVALID_ARG, "B, H, N must be >= 1 (got %d, %d, %d)", p->B, p->H, p->N);
@@ -117,7 +117,7 @@ static sa_status check_problem(const sa_problem* p, Geometry* g) {
     return SA_OK;
 }
 
-static sa_status check_spec(const Geometry& g, const sa_select_spec* s) {
+sa_status check_spec(const Geometry& g, const sa_select_spec* s) {
     if (!s) return fail(SA_ERR_INVALID_ARG, "spec is NULL");
     if (s->rule != SA_RULE_NONE && s->rule != SA_RULE_TOPK && s->rule != SA_RULE_MASS &&
         s->rule != SA_RULE_ERR)
@@ -228,16 +228,12 @@ SA_API sa_status hilbert_unpermute(const sa_problem* prob, const void* src, void
     return permute_common(prob, src, dst, perm_dev, stream, true);
 }
 
-SA_API sa_status sparse_attn_select(const sa_problem* prob, const sa_select_spec* spec,
-                                    const void* Q, const void* K, const void* V,
-                                    int32_t* row_ptr, int32_t* col_idx, float* scores,
-                                    float* k_mean, float* v_sum, void* workspace,
-                                    size_t ws_bytes, void* stream) {
-    clear_error();
-    Geometry g;
-    sa_status st = check_problem(prob, &g);
-    if (st != SA_OK) return st;
-    if ((st = check_spec(g, spec)) != SA_OK) return st;
+namespace sa {
+
+sa_status check_select_args(const Geometry& g, const sa_select_spec* spec, const void* Q,
+                            const void* K, const void* V, const int32_t* row_ptr,
+                            const int32_t* col_idx, const float* k_mean, const float* v_sum) {
+    (void)g;
     const bool scored = spec->rule != SA_RULE_NONE;
     if (scored && (!Q || !K)) return fail(SA_ERR_INVALID_ARG, "Q and K are required by the rule");
     if ((Q && !aligned16(Q)) || (K && !aligned16(K)) || (V && !aligned16(V)))
@@ -247,14 +243,13 @@ SA_API sa_status sparse_attn_select(const sa_problem* prob, const sa_select_spec
         if (!K || !V) return fail(SA_ERR_INVALID_ARG, "want_comp needs K and V");
         if (!k_mean || !v_sum) return fail(SA_ERR_INVALID_ARG, "want_comp needs k_mean and v_sum");
     }
-    const SelectPlan plan = make_select_plan(g, *spec);
-    if (plan.total > 0) {
-        if (!workspace) return fail(SA_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", plan.total);
-        if (((uintptr_t)workspace & 255u) != 0)
-            return fail(SA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
-        if (ws_bytes < plan.total)
-            return fail(SA_ERR_WORKSPACE, "workspace too small: %zu < %zu bytes", ws_bytes, plan.total);
-    }
+    return SA_OK;
+}
+
+sa_status select_on_workspace(const Geometry& g, const sa_select_spec& spec, const SelectPlan& plan,
+                              const void* Q, const void* K, const void* V, int32_t* row_ptr,
+                              int32_t* col_idx, float* scores, float* k_mean, float* v_sum,
+                              char* ws, hipStream_t stream) {
     // blocks kept per head, resolved on the host
     int32_t k_host[4096];
     int32_t* kh = k_host;
@@ -265,20 +260,45 @@ SA_API sa_status sparse_attn_select(const sa_problem* prob, const sa_select_spec
     }
     for (int h = 0; h < g.H; ++h) {
         int64_t k = 0;
-        if (spec->rule == SA_RULE_TOPK || spec->rule == SA_RULE_ERR) {
-            if (spec->topk) {
-                k = spec->topk[h];
+        if (spec.rule == SA_RULE_TOPK || spec.rule == SA_RULE_ERR) {
+            if (spec.topk) {
+                k = spec.topk[h];
             } else {
-                k = (int64_t)ceil((double)spec->density[h] * (double)g.nb * (1.0 - 1e-6));
+                k = (int64_t)ceil((double)spec.density[h] * (double)g.nb * (1.0 - 1e-6));
             }
             if (k < 1) k = 1;
             if (k > g.nb) k = g.nb;
         }
         kh[h] = (int32_t)k;
     }
-    return launch_select(g, plan, kh, (const uint16_t*)Q, (const uint16_t*)K,
-                         (const uint16_t*)V, row_ptr, col_idx, scores, k_mean, v_sum,
-                         (char*)workspace, (hipStream_t)stream);
+    return launch_select(g, plan, kh, (const uint16_t*)Q, (const uint16_t*)K, (const uint16_t*)V,
+                         row_ptr, col_idx, scores, k_mean, v_sum, ws, stream);
+}
+
+}  // namespace sa
+
+SA_API sa_status sparse_attn_select(const sa_problem* prob, const sa_select_spec* spec,
+                                    const void* Q, const void* K, const void* V,
+                                    int32_t* row_ptr, int32_t* col_idx, float* scores,
+                                    float* k_mean, float* v_sum, void* workspace,
+                                    size_t ws_bytes, void* stream) {
+    clear_error();
+    Geometry g;
+    sa_status st = check_problem(prob, &g);
+    if (st != SA_OK) return st;
+    if ((st = check_spec(g, spec)) != SA_OK) return st;
+    if ((st = check_select_args(g, spec, Q, K, V, row_ptr, col_idx, k_mean, v_sum)) != SA_OK)
+        return st;
+    const SelectPlan plan = make_select_plan(g, *spec);
+    if (plan.total > 0) {
+        if (!workspace) return fail(SA_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", plan.total);
+        if (((uintptr_t)workspace & 255u) != 0)
+            return fail(SA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+        if (ws_bytes < plan.total)
+            return fail(SA_ERR_WORKSPACE, "workspace too small: %zu < %zu bytes", ws_bytes, plan.total);
+    }
+    return select_on_workspace(g, *spec, plan, Q, K, V, row_ptr, col_idx, scores, k_mean, v_sum,
+                               (char*)workspace, (hipStream_t)stream);
 }
 
 SA_API sa_status sparse_attn_centroids(const sa_problem* prob, const void* K, const void* V,

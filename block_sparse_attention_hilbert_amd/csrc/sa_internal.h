@@ -16,6 +16,9 @@ sa_status fail(sa_status st, const char* fmt, ...);
 // Checks a HIP call / the last launch and converts a failure to SA_ERR_HIP.
 sa_status hip_check(hipError_t e, const char* what);
 
+// Clears the calling thread's error message (every entry point starts so).
+void clear_error();
+
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // Launch set-up kept per device, safe to call from several host threads:
@@ -58,6 +61,21 @@ struct SelectPlan {
 };
 
 SelectPlan make_select_plan(const Geometry& g, const sa_select_spec& s);
+
+// Host-side validation shared by the entry points (sa_api.cpp): the problem
+// statement (fills the geometry), the selection spec, and the pointers of a
+// selection call (everything but its workspace).
+sa_status check_problem(const sa_problem* p, Geometry* g);
+sa_status check_spec(const Geometry& g, const sa_select_spec* s);
+sa_status check_select_args(const Geometry& g, const sa_select_spec* spec, const void* Q,
+                            const void* K, const void* V, const int32_t* row_ptr,
+                            const int32_t* col_idx, const float* k_mean, const float* v_sum);
+// A validated selection on a workspace of at least plan.total bytes: the
+// per-head budgets resolved on the host, then the selection kernels.
+sa_status select_on_workspace(const Geometry& g, const sa_select_spec& spec, const SelectPlan& plan,
+                              const void* Q, const void* K, const void* V, int32_t* row_ptr,
+                              int32_t* col_idx, float* scores, float* k_mean, float* v_sum,
+                              char* ws, hipStream_t stream);
 
 sa_status launch_select(const Geometry& g, const SelectPlan& p,
                         const int32_t* k_host, const uint16_t* Q,

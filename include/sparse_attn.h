@@ -221,6 +221,24 @@ sa_status sparse_attn_select(const sa_problem* prob, const sa_select_spec* spec,
                              void* workspace, size_t ws_bytes, void* stream);
 
 /*
+ * sparse_attn_select without a workspace, for callers that cannot allocate
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation).  Arguments, results and errors are those of
+ * sparse_attn_select; the scratch the selection needs (pooled means, scores,
+ * keep bitmap, per-row counts) comes from a fixed 64 MiB device array of the
+ * library, one per GPU, reserved when the library is loaded on that GPU and
+ * held until the process ends.  A selection that needs more scratch (see
+ * sparse_attn_workspace_size) is rejected with SA_ERR_UNSUPPORTED before
+ * anything is enqueued.  The call allocates and frees nothing.  Every call on
+ * one GPU uses that GPU's one array: calls on one GPU must be ordered (one
+ * stream, or synchronised streams); two in flight at once race.
+ */
+sa_status sparse_attn_select_noalloc(const sa_problem* prob, const sa_select_spec* spec,
+                                     const void* Q, const void* K, const void* V,
+                                     int32_t* row_ptr, int32_t* col_idx, float* scores,
+                                     float* k_mean, float* v_sum, void* stream);
+
+/*
  * Compensation statistics of the current K and V without a selection
  * [EAR 2A; mask reuse across steps: DFS trick 3, SVOO 2B].  A caller that keeps
  * the CSR of an earlier sparse_attn_select (the mask of a previous call or

@@ -378,3 +378,26 @@ def test_pipeline_guards():
     fake_pipe = SimpleNamespace(spec=sa.SelectSpec(rule="none", window_frames=1, n_anchors=4))
     with pytest.raises(ValueError, match="rotating anchors"):
         GraphedCall(fake_pipe, None, None, None)
+
+
+def test_noalloc_select_rejects_beyond_its_scratch():
+    """The allocation-free selection holds 64 MiB of scratch per GPU; a
+    selection that needs more (the 40-head 720p layer: ~78 MiB) is refused on
+    the host, before any HIP call, with a message naming both sizes."""
+    import workloads as W
+    wl = W.CONFIGS[3]
+    prob = sa.problem_for(wl)
+    spec = sa.spec_for(wl)
+    need = sa.workspace_size(prob, spec)
+    assert need > 64 << 20
+    cs, keep = spec.c()
+    fake = ctypes.c_void_p(1 << 20)
+    st = sa.lib.sparse_attn_select_noalloc(ctypes.byref(prob.c()), ctypes.byref(cs), fake, fake,
+                                           None, fake, fake, None, None, None, None)
+    assert st == sa.SA_ERR_UNSUPPORTED
+    msg = sa.lib.sparse_attn_last_error().decode()
+    assert str(need) in msg and str(64 << 20) in msg
+    # malformed calls fail the same checks as sparse_attn_select
+    st = sa.lib.sparse_attn_select_noalloc(ctypes.byref(_prob().c()), ctypes.byref(cs), None, None,
+                                           None, fake, fake, None, None, None, None)
+    assert st == sa.SA_ERR_INVALID_ARG
