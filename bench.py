@@ -16,7 +16,14 @@ TFLOP/s over the kept blocks (4*d*sum over kept block pairs of n_i*n_j)
 divided by the whole step time; ``ms_per_step`` is that step time.
 ``roofline`` reports the attention kernel alone against the bf16 matrix-core
 peak, timed with HIP events on the stream it is launched on.
-``cpu_baseline`` times the CPU oracle on a bounded sample of the same workload.
+``cpu_baseline`` times the CPU oracle on the same workload (whole, within a
+time budget), with the tiny workload's oracle on one thread beside it.
+Besides the headline workload the line carries (unless ``--no-extra``):
+``cold_cache`` (the same call with a 512 MB device write before each call, so
+the last-level cache holds none of the inputs), ``bandwidth`` (GB/s of the
+pooling and Hilbert-permutation kernels, HIP events) and ``per_config`` (GPU
+timings of every workload of the table: ms per call, selection and attention,
+kept TFLOP and the attention kernel's fraction of the bf16 peak).
 With ``--refresh-every R`` (mask reuse across calls) only every R-th call
 selects; the others keep its mask and recompute only the compensation
 centroids; the default R = 1 selects on every call.
@@ -75,12 +82,13 @@ def read_traffic(workload: str):
         return None
 
 
-def cpu_baseline(wl, Q, K, V, budget_s: float = 15.0):
-    """The oracle (as it stands) on a bounded sample: heads 0, 1, ... in turn,
+def cpu_baseline(wl, Q, K, V, budget_s: float = 40.0):
+    """The oracle (as it stands) on the workload: heads 0, 1, ... in turn,
     each one's full selection and float64 attention of all its query blocks,
-    until the time budget is spent (the head in progress when it runs out is
-    finished block by block up to the budget).  Reported as kept-block TFLOP/s
-    of the sample."""
+    until done or the time budget is spent (the head in progress when it runs
+    out is finished block by block up to the budget; the 1.3B-sized layer
+    finishes whole in about 20 s on 16 cores).  Reported as kept-block TFLOP/s
+    and wall time; with it, the tiny workload's oracle on one thread."""
     import oracle
     import workloads as W
     from threadpoolctl import threadpool_info
@@ -110,10 +118,34 @@ def cpu_baseline(wl, Q, K, V, budget_s: float = 15.0):
             break
     dt = time.perf_counter() - t0
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
-            "kind": "oracle",
-            "sample": f"{heads} of {wl.H} heads of batch 0: selection + float64 attention of "
-                      f"{blocks} query blocks ({dt:.1f} s wall)"}
+    whole = heads == wl.H and blocks == wl.H * wl.nb
+    out = {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+           "kind": "oracle", "wall_s": round(dt, 2), "whole_workload": whole,
+           "sample": (f"the whole workload: {wl.H} heads, selection + float64 attention of "
+                      f"{blocks} query blocks ({dt:.1f} s wall)" if whole else
+                      f"{heads} of {wl.H} heads of batch 0: selection + float64 attention of "
+                      f"{blocks} query blocks ({dt:.1f} s wall)")}
+    out["tiny_one_thread"] = cpu_tiny_one_thread()
+    return out
+
+
+def cpu_tiny_one_thread():
+    """The oracle on the tiny workload (selection + attention of every head)
+    on one thread: wall time."""
+    import oracle
+    import workloads as W
+    from threadpoolctl import threadpool_limits
+
+    wl = W.CONFIGS[1]
+    Q, K, V = W.make_qkv(wl)
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        keep, _ = oracle.select_workload(wl, Q, K)
+        for h in range(wl.H):
+            oracle.attention_head(oracle.bf16_to_f64(Q[0, h]), oracle.bf16_to_f64(K[0, h]),
+                                  oracle.bf16_to_f64(V[0, h]), keep[0, h], wl.block, wl.scale)
+        dt = time.perf_counter() - t0
+    return {"workload": wl.name, "ms": round(dt * 1e3, 2), "cores": 1}
 
 
 def cpu_baseline_clusters(wl, Q, K, V, budget_s: float = 15.0):
@@ -167,6 +199,11 @@ def main():
                     help="mask reuse: select on every r-th call only, the calls in between "
                          "keep the mask (compensation centroids still from their own K, V)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=40.0,
+                    help="seconds the CPU oracle baseline may take")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="only the headline workload: no cold-cache run, bandwidth legs or "
+                         "per-workload records")
     ap.add_argument("--graph", action="store_true",
                     help="data-dependent blocks: time the calls as HIP graph replays "
                          "(stage times still come from eager calls)")
@@ -180,8 +217,6 @@ def main():
         sys.exit(2)
 
     import torch
-    import block_sparse_attention_hilbert_amd as sa
-    from block_sparse_attention_hilbert_amd.pipeline import BlockSparseAttention
     import workloads as W
 
     if args.calib_copy:
@@ -205,56 +240,9 @@ def main():
     Qd, Kd, Vd = dev(Q), dev(K), dev(V)
     if wl.cluster:
         return bench_clusters(args, wl, Q, K, V, Qd, Kd, Vd)
-    pipe = BlockSparseAttention(sa.problem_for(wl), sa.spec_for(wl), hilbert=wl.hilbert,
-                                refresh_every=args.refresh_every)
-    stream = torch.cuda.current_stream()
-    selected = []
-
-    def step(call_idx, ev):
-        off = W.anchor_offset(wl.seed, call_idx, wl.nb) if wl.n_anchors else None
-        reuse = pipe.reuses_next()
-        selected.append(not reuse)
-        Qp, Kp, Vp = pipe.permute_inputs(Qd, Kd, Vd)
-        ev[0].record(stream)
-        if reuse:
-            pipe.run_centroids(Kp, Vp)
-        else:
-            pipe.run_select(Qp, Kp, Vp, off)
-        ev[1].record(stream)
-        pipe.run_fwd_prepare(Vp)
-        ev[2].record(stream)
-        pipe.run_fwd_attention(Qp, Kp)
-        ev[3].record(stream)
-        pipe.unpermute_output()
-        pipe.calls += 1
-
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)]
-              for _ in range(max(args.steps, 1))]
-    log(f"[bench] warmup {args.warmup}")
-    for i in range(args.warmup):
-        step(i, events[0])
-    torch.cuda.synchronize()
-
-    # timed region: exactly K back-to-back calls, synchronised on both sides;
-    # HIP events on the launch stream bracket selection and attention per call
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(args.warmup + i, events[i])
-    torch.cuda.synchronize()
-    step_s = (time.perf_counter() - t0) / args.steps
-    sel_ms = [e[0].elapsed_time(e[1]) for e in events[: args.steps]]
-    prep_ms = [e[1].elapsed_time(e[2]) for e in events[: args.steps]]
-    fwd_ms = [e[2].elapsed_time(e[3]) for e in events[: args.steps]]
-    log(f"[bench] {args.steps} steps: {step_s * 1e3:.3f} ms/step")
-    # kept work of the last call's mask (only the rotating anchors change it
-    # from call to call)
-    keep = pipe.keep_mask()
-    n = np.diff(np.append(np.arange(wl.nb) * wl.block, wl.N)).astype(np.float64)
-    F_kept = 4.0 * wl.d * float((keep * np.outer(n, n)).sum())
-
-    fwd_s = float(np.mean(fwd_ms)) / 1e3
-    sel_s = float(np.mean(sel_ms)) / 1e3
+    res = time_calls(wl, Qd, Kd, Vd, args.steps, args.warmup, args.refresh_every)
+    step_s, F_kept, keep = res["step_s"], res["F_kept"], res["keep"]
+    fwd_s, sel_s = res["fwd_ms"] / 1e3, res["sel_ms"] / 1e3
     achieved = F_kept / fwd_s / 1e12
     traffic = read_traffic(wl.name)
     out = {
@@ -278,9 +266,9 @@ def main():
                    "mask_refresh_every": args.refresh_every,
                    "parallelism": "single GPU"},
         "ms_select": round(sel_s * 1e3, 4),
-        "selections_timed": int(sum(selected[args.warmup:])),
+        "selections_timed": res["selections"],
         "ms_attention": round(fwd_s * 1e3, 4),
-        "ms_attention_prepare": round(float(np.mean(prep_ms)), 4),
+        "ms_attention_prepare": round(res["prep_ms"], 4),
         "select_over_attention": round(sel_s / fwd_s, 4),
         "kept_tflop_per_call": round(F_kept / 1e12, 4),
         "roofline": {"bound": "mfma", "kernel": ATTN_KERNEL, "achieved": round(achieved, 2),
@@ -288,10 +276,165 @@ def main():
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic},
     }
+    if not args.no_extra:
+        log("[bench] cold calls (a 512 MB write between calls flushes the last-level cache)")
+        cold = time_calls(wl, Qd, Kd, Vd, 10, 2, args.refresh_every, flush_bytes=512 << 20)
+        out["cold_cache"] = {"ms_per_call": round(cold["call_ms"], 4),
+                             "ms_attention": round(cold["fwd_ms"], 4),
+                             "ms_select": round(cold["sel_ms"], 4),
+                             "flush": "512 MB device write before each call, outside the timing"}
+        out["bandwidth"] = bandwidth_legs()
+        out["per_config"] = per_config_records(args, wl, res)
     if not args.no_cpu_baseline:
-        log("[bench] cpu baseline (oracle, bounded sample)")
-        out["cpu_baseline"] = cpu_baseline(wl, Q, K, V)
+        log("[bench] cpu baseline (oracle as it stands, the whole workload)")
+        out["cpu_baseline"] = cpu_baseline(wl, Q, K, V, budget_s=args.cpu_budget)
     print(json.dumps(out), flush=True)
+
+
+def time_calls(wl, Qd, Kd, Vd, steps, warmup, refresh_every=1, flush_bytes=0):
+    """Times `steps` calls of the path on resident inputs after `warmup`
+    untimed ones: the wall time of the back-to-back calls, synchronised on both
+    sides, and HIP events on the launch stream around selection, preparation,
+    attention and the whole call (means).  With ``flush_bytes`` a device
+    buffer of that size is written before every call (outside the events) to
+    flush the last-level cache; the wall time then includes the flushes."""
+    import torch
+    import block_sparse_attention_hilbert_amd as sa
+    from block_sparse_attention_hilbert_amd.pipeline import BlockSparseAttention
+    import workloads as W
+
+    pipe = BlockSparseAttention(sa.problem_for(wl), sa.spec_for(wl), hilbert=wl.hilbert,
+                                refresh_every=refresh_every)
+    stream = torch.cuda.current_stream()
+    flush = torch.empty(flush_bytes, dtype=torch.uint8, device="cuda") if flush_bytes else None
+    selected = []
+
+    def step(call_idx, ev):
+        if flush is not None:
+            flush.fill_(call_idx & 255)
+        off = W.anchor_offset(wl.seed, call_idx, wl.nb) if wl.n_anchors else None
+        reuse = pipe.reuses_next()
+        selected.append(not reuse)
+        ev[0].record(stream)
+        Qp, Kp, Vp = pipe.permute_inputs(Qd, Kd, Vd)
+        ev[1].record(stream)
+        if reuse:
+            pipe.run_centroids(Kp, Vp)
+        else:
+            pipe.run_select(Qp, Kp, Vp, off)
+        ev[2].record(stream)
+        pipe.run_fwd_prepare(Vp)
+        ev[3].record(stream)
+        pipe.run_fwd_attention(Qp, Kp)
+        ev[4].record(stream)
+        pipe.unpermute_output()
+        ev[5].record(stream)
+        pipe.calls += 1
+
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(max(steps, 1))]
+    log(f"[bench] {wl.name}: warmup {warmup}")
+    for i in range(warmup):
+        step(i, events[0])
+    torch.cuda.synchronize()
+    # timed region: exactly `steps` back-to-back calls, synchronised on both sides
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(warmup + i, events[i])
+    torch.cuda.synchronize()
+    step_s = (time.perf_counter() - t0) / steps
+    ev = events[:steps]
+    mean = lambda a, b: float(np.mean([e[a].elapsed_time(e[b]) for e in ev]))
+    log(f"[bench] {wl.name}: {steps} steps: {step_s * 1e3:.3f} ms/step")
+    # kept work of the last call's mask (only the rotating anchors change it
+    # from call to call)
+    keep = pipe.keep_mask()
+    n = np.diff(np.append(np.arange(wl.nb) * wl.block, wl.N)).astype(np.float64)
+    F_kept = 4.0 * wl.d * float((keep * np.outer(n, n)).sum())
+    res = {"step_s": step_s, "F_kept": F_kept, "keep": keep,
+           "sel_ms": mean(1, 2), "prep_ms": mean(2, 3), "fwd_ms": mean(3, 4),
+           "call_ms": mean(0, 5), "selections": int(sum(selected[warmup:]))}
+    del pipe, flush
+    torch.cuda.empty_cache()
+    return res
+
+
+def per_config_records(args, main_wl, main_res):
+    """One record per workload of the table (GPU timings only; inputs made and
+    freed one workload at a time)."""
+    import torch
+    import workloads as W
+
+    recs = []
+    for c in sorted(W.CONFIGS):
+        wl = W.CONFIGS[c]
+        if wl.name == main_wl.name:
+            r = main_res
+        else:
+            Q, K, V = W.make_qkv(wl)
+            dev = lambda x: torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).cuda()
+            Qd, Kd, Vd = dev(Q), dev(K), dev(V)
+            r = time_calls(wl, Qd, Kd, Vd, 10, 2)
+            del Qd, Kd, Vd, Q, K, V
+            torch.cuda.empty_cache()
+        att = r["F_kept"] / (r["fwd_ms"] / 1e3) / 1e12
+        recs.append({"config": c, "workload": wl.name, "B": wl.B, "H": wl.H, "N": wl.N,
+                     "block": wl.block, "rule": wl.rule,
+                     "density_kept": round(float(r["keep"].mean()), 4),
+                     "ms_per_call": round(r["step_s"] * 1e3, 4),
+                     "ms_select": round(r["sel_ms"], 4),
+                     "ms_attention": round(r["fwd_ms"], 4),
+                     "select_over_attention": round(r["sel_ms"] / r["fwd_ms"], 4),
+                     "kept_tflop_per_call": round(r["F_kept"] / 1e12, 4),
+                     "tflops_call": round(r["F_kept"] / r["step_s"] / 1e12, 2),
+                     "tflops_attention": round(att, 2),
+                     "frac": round(att / PEAK_BF16_TFLOPS, 4)})
+    return recs
+
+
+def bandwidth_legs():
+    """Achieved bandwidth of the pooling and reordering kernels on the
+    1.3B-sized layer's shape (one call each, HIP events, mean of 20):
+    pooling = the block means of K and block sums of V (sparse_attn_centroids,
+    the same kernel the selection runs on Q and K: reads two [1,12,32760,128]
+    bf16 tensors, writes fp32 block statistics); reordering = one Hilbert
+    permutation of one tensor (read + write)."""
+    import torch
+    import block_sparse_attention_hilbert_amd as sa
+    import workloads as W
+
+    wl = W.CONFIGS[2]
+    prob = sa.problem_for(wl)
+    dev = lambda x: torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).cuda()
+    Q, K, V = W.make_qkv(wl)
+    Kd, Vd = dev(K), dev(V)
+    km = torch.empty(wl.B, wl.H, wl.nb, wl.d, dtype=torch.float32, device="cuda")
+    vs = torch.empty_like(km)
+    perm = torch.from_numpy(sa.hilbert_perm_build(wl.T, wl.Hg, wl.W)[0]).cuda()
+    dst = torch.empty_like(Kd)
+
+    def timed(fn, reps=20):
+        fn()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for a, b in ev:
+            a.record()
+            fn()
+            b.record()
+        torch.cuda.synchronize()
+        return float(np.mean([a.elapsed_time(b) for a, b in ev]))
+
+    tensor_bytes = wl.B * wl.H * wl.N * wl.d * 2
+    stats_bytes = 2 * wl.B * wl.H * wl.nb * wl.d * 4
+    pool_ms = timed(lambda: sa.centroids(prob, Kd, Vd, km, vs))
+    perm_ms = timed(lambda: sa.hilbert_permute(prob, Kd, perm, dst))
+    pool_b, perm_b = 2 * tensor_bytes + stats_bytes, 2 * tensor_bytes
+    return {"pooling": {"kernel": "k_pool", "ms": round(pool_ms, 4), "bytes": pool_b,
+                        "gbs": round(pool_b / pool_ms / 1e6, 1),
+                        "frac": round(pool_b / pool_ms / 1e6 / PEAK_HBM_GBS, 4)},
+            "permute": {"kernel": "k_permute", "ms": round(perm_ms, 4), "bytes": perm_b,
+                        "gbs": round(perm_b / perm_ms / 1e6, 1),
+                        "frac": round(perm_b / perm_ms / 1e6 / PEAK_HBM_GBS, 4)},
+            "workload": wl.name, "peak_gbs": PEAK_HBM_GBS}
 
 
 def bench_clusters(args, wl, Q, K, V, Qd, Kd, Vd):
