@@ -56,7 +56,8 @@ EXPORTS = ("sparse_attn_workspace_size", "hilbert_perm_build", "hilbert_permute"
 class SaProblem(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int32), ("H", ctypes.c_int32), ("N", ctypes.c_int32),
                 ("d", ctypes.c_int32), ("T", ctypes.c_int32), ("Hg", ctypes.c_int32),
-                ("W", ctypes.c_int32), ("block", ctypes.c_int32), ("scale", ctypes.c_float)]
+                ("W", ctypes.c_int32), ("block", ctypes.c_int32), ("scale", ctypes.c_float),
+                ("token_order", ctypes.c_void_p)]
 
 
 class SaSelectSpec(ctypes.Structure):
@@ -143,6 +144,9 @@ class Problem:
     W: int
     block: int
     scale: float = 0.0
+    # device int32 [N]: blocks are runs of the tokens in this order (Q, K, V,
+    # O and lse stay in the caller's order), or None: as given
+    token_order: Optional[torch.Tensor] = None
 
     @property
     def nb(self) -> int:
@@ -153,8 +157,16 @@ class Problem:
         return self.B * self.H * self.nb
 
     def c(self) -> SaProblem:
+        order = None
+        if self.token_order is not None:
+            t = self.token_order
+            if t.dtype != torch.int32 or tuple(t.shape) != (self.N,) or not t.is_contiguous():
+                raise ValueError(f"token_order must be a contiguous int32 tensor of shape ({self.N},)")
+            if t.device.type != "cuda":
+                raise ValueError("token_order must be a GPU tensor")
+            order = t.data_ptr()
         return SaProblem(self.B, self.H, self.N, self.d, self.T, self.Hg, self.W, self.block,
-                         self.scale)
+                         self.scale, order)
 
 
 @dataclass

@@ -101,6 +101,8 @@ struct FwdArgs {
     const int16_t* cnt;      // [BH][nb] tokens of each KV block
     uint16_t* O;
     float* lse;
+    const int32_t* order;    // token order of the blocks ([N]) or null: Q, O, lse rows go
+                             // through it (K comes already in block order)
     int32_t* sched;          // [3][8] per-XCD row range start, end and pull counter;
                              // [24] = 1 when the block counts come from the caller;
                              // [25] workgroups of the launch that are done
@@ -253,13 +255,15 @@ __device__ __forceinline__ void process_row(const FwdArgs& a, int64_t row, unsig
         reinterpret_cast<const unsigned char*>(a.Vt + bh * (int64_t)a.nb * D * BLK);
     const int last_n = a.N - (a.nb - 1) * BLK;
 
-    // Q^T fragments (B operand) of this wave's 32 queries
+    // Q^T fragments (B operand) of this wave's 32 queries; query qn of the
+    // block order is token qtok of the caller's order
     bf16x8 qf[D / 16];
     const int qn = i * BLK + qg * 32 + r32;
+    const int qtok = qn < a.N ? (a.order ? a.order[qn] : qn) : 0;
 #pragma unroll
     for (int st = 0; st < D / 16; ++st) {
         uint4 v = make_uint4(0, 0, 0, 0);
-        if (qn < a.N) v = *reinterpret_cast<const uint4*>(a.Q + head_off + (int64_t)qn * D + st * 16 + h * 8);
+        if (qn < a.N) v = *reinterpret_cast<const uint4*>(a.Q + head_off + (int64_t)qtok * D + st * 16 + h * 8);
         qf[st] = as_bf16x8(v);
     }
 
@@ -567,7 +571,7 @@ __device__ __forceinline__ void process_row(const FwdArgs& a, int64_t row, unsig
     const float inv = l > 0.f ? 1.f / l : 0.f;
     auto finish = [&](auto KHC) {
         constexpr int K = decltype(KHC)::value;
-        uint16_t* orow = a.O + head_off + (int64_t)qn * D;
+        uint16_t* orow = a.O + head_off + (int64_t)qtok * D;
 #pragma unroll
         for (int t = 0; t < HD; ++t) {
             constexpr int OK = 1 - K;
@@ -609,7 +613,7 @@ __device__ __forceinline__ void process_row(const FwdArgs& a, int64_t row, unsig
         else
             finish(std::integral_constant<int, 1>{});
         if (a.lse && kh == 0 && h == 0)
-            a.lse[bh * (int64_t)a.N + qn] = l > 0.f ? (m + __log2f(l)) * kLn2 : -INFINITY;
+            a.lse[bh * (int64_t)a.N + qtok] = l > 0.f ? (m + __log2f(l)) * kLn2 : -INFINITY;
     }
 }
 
@@ -742,21 +746,29 @@ __global__ __launch_bounds__(kSchedThreads) void k_sched(const int32_t* __restri
 // row of the transposed block.
 template <int D, int BLK>
 __global__ __launch_bounds__(256) void k_vt_prep(const uint16_t* __restrict__ V,
-                                                 uint16_t* __restrict__ Vt, int N, int nb) {
+                                                 uint16_t* __restrict__ Vt, int N, int nb,
+                                                 const int32_t* __restrict__ order) {
     constexpr int KC = BLK / 8, DC = D / 8;
     const int j = blockIdx.x;
     const int64_t bh = blockIdx.y;
     const int n = min(BLK, N - j * BLK);
-    const uint16_t* src = V + (bh * N + (int64_t)j * BLK) * D;
+    const uint16_t* src = V + bh * N * (int64_t)D;
     uint16_t* dst = Vt + (bh * nb + j) * (int64_t)D * BLK;
     for (int p = threadIdx.x; p < KC * DC; p += 256) {
         const int kc = p % KC, dc = p / KC;
-        uint32_t w[8][4];
+        // key kc*8 + r of the block is token j*BLK + kc*8 + r of the block
+        // order (read through the token order when one is given)
+        int tok[8];
 #pragma unroll
         for (int r = 0; r < 8; ++r) {
             const int key = kc * 8 + r;
+            tok[r] = key < n ? (order ? order[j * BLK + key] : j * BLK + key) : -1;
+        }
+        uint32_t w[8][4];
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
             uint4 v = make_uint4(0, 0, 0, 0);
-            if (key < n) v = *reinterpret_cast<const uint4*>(src + (int64_t)key * D + dc * 8);
+            if (tok[r] >= 0) v = *reinterpret_cast<const uint4*>(src + (int64_t)tok[r] * D + dc * 8);
             w[r][0] = v.x; w[r][1] = v.y; w[r][2] = v.z; w[r][3] = v.w;
         }
 #pragma unroll
@@ -826,7 +838,7 @@ __global__ __launch_bounds__(256) void k_comp_prep(const float* __restrict__ k_m
 }
 
 struct WsLayout {
-    size_t sched, cnt, vt, kbar, vbart, total;
+    size_t sched, cnt, vt, kbar, vbart, kord, total;
 };
 
 WsLayout ws_layout(const Geometry& g, bool comp) {
@@ -836,6 +848,9 @@ WsLayout ws_layout(const Geometry& g, bool comp) {
     L.sched = off; off = align_up(off + 32 * sizeof(int32_t), 256);
     L.cnt = off; off = align_up(off + (size_t)g.BH() * g.nb * sizeof(int16_t), 256);
     L.vt = off; off = align_up(off + (size_t)g.BH() * g.nb * g.d * g.block * 2, 256);
+    if (g.order) {   // K in block order, [BH][N][D]
+        L.kord = off; off = align_up(off + (size_t)g.BH() * g.N * g.d * 2, 256);
+    }
     if (comp) {
         L.kbar = off; off = align_up(off + (size_t)g.BH() * g.nb * g.d * 2, 256);
         L.vbart = off; off = align_up(off + (size_t)g.BH() * ntc * g.d * g.block * 2, 256);
@@ -860,7 +875,7 @@ sa_status prepare_t(const FwdArgs& a, const Geometry& g, const uint16_t* V, uint
         if ((st = hip_check(hipGetLastError(), "k_fill_counts launch")) != SA_OK) return st;
     }
     hipLaunchKernelGGL((k_vt_prep<D, BLK>), dim3(g.nb, (unsigned)g.BH()), dim3(256), 0, stream, V,
-                       vt, g.N, g.nb);
+                       vt, g.N, g.nb, g.order);
     if ((st = hip_check(hipGetLastError(), "k_vt_prep launch")) != SA_OK) return st;
     if (COMP) {
         hipLaunchKernelGGL((k_comp_prep<D, BLK>), dim3(a.ntc * (BLK / kCompRun), (unsigned)g.BH()),
@@ -896,7 +911,9 @@ FwdArgs make_args(const Geometry& g, bool comp, const uint16_t* Q, const uint16_
                   const int32_t* row_ptr, const int32_t* col_idx, uint16_t* O, float* lse, char* ws) {
     const WsLayout L = ws_layout(g, comp);
     FwdArgs a{};
-    a.Q = Q; a.K = K; a.row_ptr = row_ptr; a.col_idx = col_idx;
+    a.Q = Q; a.K = g.order ? reinterpret_cast<const uint16_t*>(ws + L.kord) : K;
+    a.order = g.order;
+    a.row_ptr = row_ptr; a.col_idx = col_idx;
     a.O = O; a.lse = lse; a.N = g.N; a.nb = g.nb; a.rows = g.rows();
     a.ntc = (int32_t)ceil_div(g.nb, g.block);
     a.c = g.scale * kLog2e;
@@ -930,12 +947,13 @@ size_t fwd_workspace_bytes(const Geometry& g, bool comp) { return ws_layout(g, c
 
 sa_status launch_vt_layout(const Geometry& g, const uint16_t* V, uint16_t* Vt, hipStream_t stream) {
     const dim3 grid(g.nb, (unsigned)g.BH());
+    const int32_t* o = g.order;
     if (g.d == 128) {
-        if (g.block == 128) hipLaunchKernelGGL((k_vt_prep<128, 128>), grid, dim3(256), 0, stream, V, Vt, g.N, g.nb);
-        else hipLaunchKernelGGL((k_vt_prep<128, 64>), grid, dim3(256), 0, stream, V, Vt, g.N, g.nb);
+        if (g.block == 128) hipLaunchKernelGGL((k_vt_prep<128, 128>), grid, dim3(256), 0, stream, V, Vt, g.N, g.nb, o);
+        else hipLaunchKernelGGL((k_vt_prep<128, 64>), grid, dim3(256), 0, stream, V, Vt, g.N, g.nb, o);
     } else {
-        if (g.block == 128) hipLaunchKernelGGL((k_vt_prep<64, 128>), grid, dim3(256), 0, stream, V, Vt, g.N, g.nb);
-        else hipLaunchKernelGGL((k_vt_prep<64, 64>), grid, dim3(256), 0, stream, V, Vt, g.N, g.nb);
+        if (g.block == 128) hipLaunchKernelGGL((k_vt_prep<64, 128>), grid, dim3(256), 0, stream, V, Vt, g.N, g.nb, o);
+        else hipLaunchKernelGGL((k_vt_prep<64, 64>), grid, dim3(256), 0, stream, V, Vt, g.N, g.nb, o);
     }
     return hip_check(hipGetLastError(), "k_vt_prep launch");
 }
@@ -959,6 +977,11 @@ sa_status launch_fwd_run(const Geometry& g, bool comp, const uint16_t* Q, const 
                          char* ws, hipStream_t stream) {
     if (g.nb > 4096) return fail(SA_ERR_UNSUPPORTED, "attention supports nb <= 4096 (got %d)", g.nb);
     const FwdArgs a = make_args(g, comp, Q, K, row_ptr, col_idx, O, lse, ws);
+    if (g.order) {
+        // the tile copies read whole blocks: K gathered into block order first
+        const sa_status st = launch_permute(g, K, const_cast<uint16_t*>(a.K), g.order, false, stream);
+        if (st != SA_OK) return st;
+    }
 #define SA_RUN(D_, B_, C_) run_t<D_, B_, C_>(a, g, stream)
     SA_DISPATCH(SA_RUN)
 #undef SA_RUN

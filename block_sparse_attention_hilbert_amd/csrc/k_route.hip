@@ -89,7 +89,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_err(const float* __restrict__ q
                                                     const float* __restrict__ v_sum,
                                                     const float* __restrict__ S,
                                                     float* __restrict__ keys, int N, int nb,
-                                                    float scale) {
+                                                    float scale, const int32_t* __restrict__ order) {
     constexpr int KS = D / 16;            // channel steps of L^T
     constexpr int KT = BLK / 32;          // 32-key tiles
     constexpr int DT = D / 32;            // 32-channel tiles of A^T
@@ -132,11 +132,16 @@ __global__ __launch_bounds__(kThreads, 2) void k_err(const float* __restrict__ q
         const int nj = min(BLK, N - j * BLK);
         __syncthreads();   // the previous block's tiles are no longer read
         {
-            const uint16_t* src = K + (bh * N + (int64_t)j * BLK) * D;
+            // key r of block j: token j*BLK + r of the block order (through
+            // the token order when one is given)
+            const uint16_t* src = K + bh * N * (int64_t)D;
             for (int p = tid; p < BLK * (D / 8); p += kThreads) {
                 const int r = p / (D / 8), ch = p % (D / 8);
                 uint4 v = make_uint4(0, 0, 0, 0);
-                if (r < nj) v = *reinterpret_cast<const uint4*>(src + (int64_t)r * D + ch * 8);
+                if (r < nj) {
+                    const int t = order ? order[j * BLK + r] : j * BLK + r;
+                    v = *reinterpret_cast<const uint4*>(src + (int64_t)t * D + ch * 8);
+                }
                 *reinterpret_cast<uint4*>(&ks_lds[r * KROW + ch * 8]) = v;
             }
             const uint16_t* vsrc = Vt + (bh * nb + j) * (int64_t)D * BLK;
@@ -234,7 +239,7 @@ sa_status launch_t(const Geometry& g, const float* qm, const uint16_t* K, const 
     const dim3 grid((unsigned)ceil_div(g.nb, kQPerGroup), (unsigned)ceil_div(g.nb, RJ),
                     (unsigned)g.BH());
     hipLaunchKernelGGL((k_err<D, BLK>), grid, dim3(kThreads), 0, stream, qm, K, Vt, v_sum, S, keys,
-                       g.N, g.nb, g.scale);
+                       g.N, g.nb, g.scale, g.order);
     return hip_check(hipGetLastError(), "k_err launch");
 }
 

@@ -41,6 +41,7 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
 // role 2: V -> block sums v_sum
 struct PoolArgs {
     const uint16_t* src[3];
+    const int32_t* order;    // token order of the blocks ([N]), or null: as given
     float* unit_out[3];      // [BH][n_units][D] or nullptr
     float* block_out[3];     // [BH][nb][D] or nullptr
     int32_t roles[3];
@@ -67,14 +68,21 @@ __global__ __launch_bounds__(kThreads) void k_pool(PoolArgs a) {
     const int row0 = blk * BLK;
     const int n = min(BLK, a.N - row0);
     const int sgi = tid / CH, ch = tid % CH;
-    const uint4* src = reinterpret_cast<const uint4*>(a.src[role] + (bh * a.N + row0) * D) + ch;
+    const uint4* src = reinterpret_cast<const uint4*>(a.src[role] + bh * a.N * D) + ch;
 
-    uint4 v[SEGR];
+    // the block's rows: tokens row0 .. row0+n-1 of the block order (read
+    // through the token order when one is given; all indices first, so the
+    // row loads stay in flight together)
+    int tok[SEGR];
 #pragma unroll
     for (int r = 0; r < SEGR; ++r) {
         const int row = sgi * SEGR + r;
-        v[r] = row < n ? src[row * CH] : make_uint4(0, 0, 0, 0);
+        tok[r] = row < n ? (a.order ? a.order[row0 + row] : row0 + row) : -1;
     }
+    uint4 v[SEGR];
+#pragma unroll
+    for (int r = 0; r < SEGR; ++r)
+        v[r] = tok[r] >= 0 ? src[(int64_t)tok[r] * CH] : make_uint4(0, 0, 0, 0);
     double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
     for (int r = 0; r < SEGR; ++r) {
@@ -798,6 +806,7 @@ sa_status launch_row_scan(const int32_t* counts, int32_t* row_ptr, int64_t R, hi
 sa_status launch_centroids(const Geometry& g, const uint16_t* K, const uint16_t* V, float* k_mean,
                            float* v_sum, hipStream_t stream) {
     PoolArgs pa{};
+    pa.order = g.order;
     pa.src[1] = K; pa.src[2] = V;
     pa.block_out[1] = k_mean; pa.block_out[2] = v_sum;
     pa.roles[0] = 1; pa.roles[1] = 2;
@@ -831,6 +840,7 @@ sa_status launch_select(const Geometry& g, const SelectPlan& p, const int32_t* k
 
     // 1. pooling
     PoolArgs pa{};
+    pa.order = g.order;
     pa.src[0] = Q; pa.src[1] = K; pa.src[2] = V;
     pa.N = g.N; pa.nb = g.nb; pa.unit = p.unit; pa.n_units = p.n_units;
     int nroles = 0;

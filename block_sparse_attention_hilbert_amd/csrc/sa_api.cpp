@@ -114,6 +114,15 @@ sa_status check_problem(const sa_problem* p, Geometry* g) {
     g->T = p->T; g->Hg = p->Hg; g->W = p->W;
     g->nb = (int32_t)ceil_div(p->N, p->block);
     g->scale = p->scale > 0.f ? p->scale : (float)(1.0 / sqrt((double)p->d));
+    g->order = p->token_order;
+    return SA_OK;
+}
+
+// Calls that work on the tokens as given only.
+static sa_status no_token_order(const Geometry& g, const char* call) {
+    if (g.order)
+        return fail(SA_ERR_UNSUPPORTED, "%s takes no token_order (blocks of the tokens as given)",
+                    call);
     return SA_OK;
 }
 
@@ -157,6 +166,9 @@ sa_status check_spec(const Geometry& g, const sa_select_spec* s) {
         return fail(SA_ERR_INVALID_ARG, "mass = %g must be in (0, 1]", (double)s->mass);
     if (s->window_frames < -1)
         return fail(SA_ERR_INVALID_ARG, "window_frames = %d must be >= -1", s->window_frames);
+    if (s->window_frames >= 0 && g.order)
+        return fail(SA_ERR_UNSUPPORTED,
+                    "a latent-frame window needs blocks of raster tokens (no token_order)");
     if (s->n_anchors < 0 || s->n_anchors > g.nb)
         return fail(SA_ERR_INVALID_ARG, "n_anchors = %d must be in [0, nb = %d]", s->n_anchors, g.nb);
     if (s->anchor_offset < 0)
@@ -207,6 +219,7 @@ static sa_status permute_common(const sa_problem* prob, const void* src, void* d
     Geometry g;
     sa_status st = check_problem(prob, &g);
     if (st != SA_OK) return st;
+    if ((st = no_token_order(g, "hilbert_permute and hilbert_unpermute")) != SA_OK) return st;
     if (!src || !dst || !perm) return fail(SA_ERR_INVALID_ARG, "src, dst and perm must be non-NULL");
     if (!aligned16(src) || !aligned16(dst))
         return fail(SA_ERR_INVALID_ARG, "src and dst must be 16-byte aligned");
@@ -394,6 +407,7 @@ SA_API sa_status sparse_attn_fwd_prepare_counts(const sa_problem* prob, const vo
     Geometry g;
     sa_status st = check_problem(prob, &g);
     if (st != SA_OK) return st;
+    if ((st = no_token_order(g, "sparse_attn_fwd_prepare_counts")) != SA_OK) return st;
     if (!V) return fail(SA_ERR_INVALID_ARG, "V is required");
     if (!aligned16(V)) return fail(SA_ERR_INVALID_ARG, "V must be 16-byte aligned");
     if (!row_ptr) return fail(SA_ERR_INVALID_ARG, "row_ptr is required");
@@ -464,6 +478,7 @@ SA_API sa_status sparse_attn_cluster_size(const sa_problem* prob, const sa_clust
     Geometry g;
     sa_status st = check_problem(prob, &g);
     if (st != SA_OK) return st;
+    if ((st = no_token_order(g, "sparse_attn_cluster_size")) != SA_OK) return st;
     if ((st = check_cluster(g, cspec)) != SA_OK) return st;
     if (nb_padded) *nb_padded = padded_block_count(g, *cspec);
     if (ws_cluster) *ws_cluster = cluster_workspace_bytes(g, *cspec);
@@ -482,6 +497,7 @@ SA_API sa_status sparse_attn_cluster(const sa_problem* prob, const sa_cluster_sp
     Geometry g;
     sa_status st = check_problem(prob, &g);
     if (st != SA_OK) return st;
+    if ((st = no_token_order(g, "sparse_attn_cluster")) != SA_OK) return st;
     if ((st = check_cluster(g, cspec)) != SA_OK) return st;
     if (!Q || !K) return fail(SA_ERR_INVALID_ARG, "Q and K are required");
     if (!aligned16(Q) || !aligned16(K) || (V && !aligned16(V)))
@@ -509,6 +525,7 @@ SA_API sa_status sparse_attn_sics(const sa_problem* prob, const sa_cluster_spec*
     Geometry g;
     sa_status st = check_problem(prob, &g);
     if (st != SA_OK) return st;
+    if ((st = no_token_order(g, "sparse_attn_sics")) != SA_OK) return st;
     if ((st = check_cluster(g, cspec)) != SA_OK) return st;
     if (cspec->mode != SA_CLUSTER_TILES)
         return fail(SA_ERR_INVALID_ARG, "sparse_attn_sics needs mode SA_CLUSTER_TILES");
@@ -538,6 +555,7 @@ SA_API sa_status sparse_attn_cluster_gather(const sa_problem* prob, const sa_clu
     Geometry g;
     sa_status st = check_problem(prob, &g);
     if (st != SA_OK) return st;
+    if ((st = no_token_order(g, "sparse_attn_cluster_gather")) != SA_OK) return st;
     if ((st = check_cluster(g, cspec)) != SA_OK) return st;
     if (!order) return fail(SA_ERR_INVALID_ARG, "order is required");
     const int64_t np = (int64_t)padded_block_count(g, *cspec) * g.block;
@@ -553,6 +571,7 @@ SA_API sa_status sparse_attn_cluster_scatter(const sa_problem* prob, const sa_cl
     Geometry g;
     sa_status st = check_problem(prob, &g);
     if (st != SA_OK) return st;
+    if ((st = no_token_order(g, "sparse_attn_cluster_scatter")) != SA_OK) return st;
     if ((st = check_cluster(g, cspec)) != SA_OK) return st;
     if (!order) return fail(SA_ERR_INVALID_ARG, "order is required");
     if ((lse_src == nullptr) != (lse_dst == nullptr))
@@ -575,6 +594,7 @@ SA_API sa_status sparse_attn_cluster_select(const sa_problem* prob, const sa_clu
     Geometry g;
     sa_status st = check_problem(prob, &g);
     if (st != SA_OK) return st;
+    if ((st = no_token_order(g, "sparse_attn_cluster_select")) != SA_OK) return st;
     if ((st = check_cluster(g, cspec)) != SA_OK) return st;
     if (!spec) return fail(SA_ERR_INVALID_ARG, "spec is NULL");
     if (spec->rule != SA_RULE_TOPK && spec->rule != SA_RULE_MASS)
@@ -631,6 +651,7 @@ SA_API sa_status sparse_attn_cluster_centroids(const sa_problem* prob, const sa_
     Geometry g;
     sa_status st = check_problem(prob, &g);
     if (st != SA_OK) return st;
+    if ((st = no_token_order(g, "sparse_attn_cluster_centroids")) != SA_OK) return st;
     if ((st = check_cluster(g, cspec)) != SA_OK) return st;
     if (!Kp || !Vp || !k_count || !k_blk || !k_cnt || !k_cent || !v_cent || !k_mean || !v_sum)
         return fail(SA_ERR_INVALID_ARG, "every argument is required");

@@ -37,6 +37,7 @@ struct Geometry {
     int32_t B, H, N, d, block, nb;
     int32_t T, Hg, W;
     float scale;
+    const int32_t* order;    // device [N] token order of the blocks, or null (as given)
     int64_t BH() const { return (int64_t)B * H; }
     int64_t rows() const { return BH() * nb; }
 };

@@ -1,18 +1,22 @@
 """One block-sparse attention call with preallocated buffers.
 
-The call is the whole hot path: optional Hilbert reordering of Q, K, V
-(DFSAttn page, trick 1), block selection (pooling, scores, keep lists as CSR),
-block-sparse attention with optional centroid compensation (SVG-EAR page,
-section 2A), and the inverse reordering of O.  Every step is one or more HIP
+The call is the whole hot path: block selection (pooling, scores, keep lists
+as CSR) and block-sparse attention with optional centroid compensation
+(SVG-EAR page, section 2A), over blocks of raster tokens or of the 3D Hilbert
+order (DFSAttn page, trick 1).  The Hilbert order is folded into the kernels
+(the problem's token order): pooling and the V re-layout read rows through
+it, the attention kernel reads its queries and writes O and lse through it,
+and only K is gathered into block order once, inside the attention call; Q,
+V and O are never reordered as whole tensors.  Every step is one or more HIP
 kernels of libsparse_attn.so enqueued on the current stream; this class only
 owns the buffers so that repeated calls allocate nothing.
 
 Mask reuse (DFSAttn page, trick 3: the previous step's mask is cached; SVOO
 page, section 2B: the clustering is refreshed only every few diffusion steps):
 with ``refresh_every = r`` the selection runs on calls 0, r, 2r, ... and the
-calls in between keep its CSR.  A reusing call still reorders its own inputs
-and, with compensation, recomputes the centroids of the skipped blocks from
-its own K and V (sparse_attn_centroids); only the keep decision is reused.
+calls in between keep its CSR.  A reusing call still attends over its own
+inputs and, with compensation, recomputes the centroids of the skipped blocks
+from its own K and V (sparse_attn_centroids); only the keep decision is reused.
 
 :class:`ClusteredAttention` is the same call with data-dependent blocks
 (SVOO page, section 2B: bidirectional Q/K co-clustering; SVG-EAR page,
@@ -37,8 +41,7 @@ from . import (Clusters, ClusterSpec, Problem, Selection, SelectSpec, alloc_work
                centroids, cluster, cluster_centroids, cluster_gather, cluster_scatter,
                cluster_select, sics,
                cluster_size, fwd, fwd_prepare, fwd_prepare_counts, fwd_run,
-               hilbert_perm_build, hilbert_permute, hilbert_unpermute, padded_problem, select,
-               workspace_size)
+               hilbert_perm_build, padded_problem, select, workspace_size)
 
 
 class BlockSparseAttention:
@@ -51,11 +54,19 @@ class BlockSparseAttention:
             # the window is a range of latent frames over raster-ordered blocks;
             # blocks of Hilbert-ordered tokens span frames in no such order
             raise ValueError("a latent-frame window needs raster token order (hilbert=False)")
-        self.prob, self.spec, self.hilbert = prob, spec, hilbert
+        self.spec, self.hilbert = spec, hilbert
         self.refresh_every = int(refresh_every)
         self.calls = 0              # calls made so far (the reuse policy counts them)
         self.have_mask = False
         self.device = torch.device(device)
+        self.perm = self.perm_dev = None
+        if hilbert:
+            # blocks of the Hilbert order: the problem's token order
+            perm, _ = hilbert_perm_build(prob.T, prob.Hg, prob.W)
+            self.perm = perm
+            self.perm_dev = torch.from_numpy(perm).to(self.device)
+            prob = Problem(**{**prob.__dict__, "token_order": self.perm_dev})
+        self.prob = prob
         nb, rows = prob.nb, prob.rows
         shape = (prob.B, prob.H, prob.N, prob.d)
         self.sel = Selection(torch.empty(rows + 1, dtype=torch.int32, device=self.device),
@@ -68,26 +79,10 @@ class BlockSparseAttention:
             self.sel.v_sum = torch.empty_like(self.sel.k_mean)
         self.ws_select = alloc_workspace(workspace_size(prob, spec), self.device)
         self.ws_fwd = alloc_workspace(workspace_size(prob, None), self.device)
+        # O and lse in the caller's token order (also with Hilbert blocks)
         self.O = torch.empty(shape, dtype=torch.bfloat16, device=self.device)
         self.lse = torch.empty(prob.B, prob.H, prob.N, dtype=torch.float32,
                                device=self.device) if want_lse else None
-        self.perm_dev = None
-        if hilbert:
-            perm, _ = hilbert_perm_build(prob.T, prob.Hg, prob.W)
-            self.perm = perm
-            self.perm_dev = torch.from_numpy(perm).to(self.device)
-            self.Qp = torch.empty(shape, dtype=torch.bfloat16, device=self.device)
-            self.Kp = torch.empty_like(self.Qp)
-            self.Vp = torch.empty_like(self.Qp)
-            self.Op = torch.empty_like(self.Qp)
-
-    def permute_inputs(self, Q, K, V):
-        if not self.hilbert:
-            return Q, K, V
-        hilbert_permute(self.prob, Q, self.perm_dev, self.Qp)
-        hilbert_permute(self.prob, K, self.perm_dev, self.Kp)
-        hilbert_permute(self.prob, V, self.perm_dev, self.Vp)
-        return self.Qp, self.Kp, self.Vp
 
     def run_select(self, Q, K, V, anchor_offset: Optional[int] = None) -> Selection:
         spec = self.spec
@@ -110,10 +105,9 @@ class BlockSparseAttention:
     def run_fwd(self, Q, K, V, row_ptr=None, col_idx=None):
         rp = self.sel.row_ptr if row_ptr is None else row_ptr
         ci = self.sel.col_idx if col_idx is None else col_idx
-        out = self.Op if self.hilbert else self.O
-        fwd(self.prob, Q, K, V, rp, ci, self.sel.k_mean, self.sel.v_sum, O=out, lse=self.lse,
+        fwd(self.prob, Q, K, V, rp, ci, self.sel.k_mean, self.sel.v_sum, O=self.O, lse=self.lse,
             workspace=self.ws_fwd)
-        return out
+        return self.O
 
     def run_fwd_prepare(self, V, row_ptr=None):
         """First half of run_fwd: V (and the centroids) laid out in the workspace."""
@@ -121,17 +115,12 @@ class BlockSparseAttention:
         fwd_prepare(self.prob, V, rp, self.sel.k_mean, self.sel.v_sum, workspace=self.ws_fwd)
 
     def run_fwd_attention(self, Q, K, row_ptr=None, col_idx=None):
-        """Second half of run_fwd: the attention kernel alone."""
+        """Second half of run_fwd: the attention kernel (with Hilbert blocks,
+        K gathered into block order first)."""
         rp = self.sel.row_ptr if row_ptr is None else row_ptr
         ci = self.sel.col_idx if col_idx is None else col_idx
-        out = self.Op if self.hilbert else self.O
-        fwd_run(self.prob, Q, K, rp, ci, self.spec.want_comp, O=out, lse=self.lse,
+        fwd_run(self.prob, Q, K, rp, ci, self.spec.want_comp, O=self.O, lse=self.lse,
                 workspace=self.ws_fwd)
-        return out
-
-    def unpermute_output(self):
-        if self.hilbert:
-            hilbert_unpermute(self.prob, self.Op, self.perm_dev, self.O)
         return self.O
 
     def __call__(self, Q, K, V, anchor_offset: Optional[int] = None,
@@ -142,14 +131,13 @@ class BlockSparseAttention:
             reuse_mask = self.reuses_next()
         if reuse_mask and not self.have_mask:
             raise RuntimeError("no mask to reuse: the first call must select")
-        Qp, Kp, Vp = self.permute_inputs(Q, K, V)
         if reuse_mask:
-            self.run_centroids(Kp, Vp)
+            self.run_centroids(K, V)
         else:
-            self.run_select(Qp, Kp, Vp, anchor_offset)
-        self.run_fwd(Qp, Kp, Vp)
+            self.run_select(Q, K, V, anchor_offset)
+        self.run_fwd(Q, K, V)
         self.calls += 1
-        return self.unpermute_output()
+        return self.O
 
     def keep_mask(self) -> np.ndarray:
         """Kept-block mask [B, H, nb, nb] of the last selection (host copy)."""

@@ -80,6 +80,23 @@ typedef struct {
     int32_t T, Hg, W;     /* latent grid; T*Hg*W must equal N                   */
     int32_t block;        /* tokens per Q block and per KV block: 64 or 128     */
     float scale;          /* softmax scale; <= 0 selects (float)(1/sqrt(d))     */
+    const int32_t* token_order;
+                          /* NULL: blocks are runs of the tokens as given.
+                             Else device int32 [N], a permutation: blocks are
+                             runs of the sequence token_order[0], token_order[1],
+                             ... (e.g. the Hilbert order of hilbert_perm_build
+                             [DFS trick 1]), while Q, K, V, O and lse stay in
+                             the caller's token order: the kernels read and
+                             write rows through it, so no separate reordering
+                             pass is needed.  Masks, scores and block
+                             statistics are indexed by these blocks.  Taken by
+                             sparse_attn_workspace_size, sparse_attn_select(_noalloc),
+                             sparse_attn_centroids and sparse_attn_fwd(_prepare,
+                             _run) (the forward workspace then also holds K in
+                             block order, gathered by sparse_attn_fwd_run);
+                             the other calls reject it (SA_ERR_UNSUPPORTED), as
+                             does a latent-frame window (frames are runs of
+                             raster blocks).  Not checked to be a permutation. */
 } sa_problem;
 
 enum {

@@ -126,18 +126,24 @@ def poison(*tensors):
             t.fill_(float("nan"))
 
 
-def assert_outputs_written(O_bits, lse, wl, keep):
+def assert_outputs_written(O_bits, lse, wl, keep, perm=None):
     """Every output element finite (written), and lse finite exactly where a
     row attends to something (a kept block or, with compensation, a centroid
     of a skipped block), -inf elsewhere.  O_bits: bf16 bit patterns
-    [B,H,N,d] in the order the rows were computed (lse in the same order);
-    keep: bool [B,H,nb,nb] of the mask the GPU used."""
+    [B,H,N,d] and lse [B,H,N] in the caller's token order; keep: bool
+    [B,H,nb,nb] of the mask the GPU used, over blocks of the token order
+    `perm` (position n of the block order is token perm[n]) or of the tokens
+    as given."""
     assert not np.any((O_bits & 0x7F80) == 0x7F80), "O holds NaN/Inf: rows not written"
     if lse is None:
         return
     bounds = oracle.block_bounds(wl.N, wl.block)
     live = keep.any(axis=-1) | (bool(wl.comp) & (~keep).any(axis=-1))    # [B,H,nb]
-    want = np.repeat(live, np.diff(bounds), axis=-1)                     # [B,H,N]
+    want = np.repeat(live, np.diff(bounds), axis=-1)                     # [B,H,N], block order
+    if perm is not None:
+        raster = np.empty_like(want)
+        raster[..., perm] = want
+        want = raster
     assert not np.any(np.isnan(lse)), "lse holds NaN: rows not written"
     assert np.array_equal(np.isfinite(lse), want), "lse finite where no block is attended"
     assert np.all(np.isneginf(lse[~want])), "lse of an empty row must be -inf"

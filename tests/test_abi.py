@@ -401,3 +401,31 @@ def test_noalloc_select_rejects_beyond_its_scratch():
     st = sa.lib.sparse_attn_select_noalloc(ctypes.byref(_prob().c()), ctypes.byref(cs), None, None,
                                            None, fake, fake, None, None, None, None)
     assert st == sa.SA_ERR_INVALID_ARG
+
+
+def test_token_order_is_refused_where_unsupported():
+    """Only the selection, centroid and forward calls take a token order; the
+    others refuse it before any launch, and so does a latent-frame window
+    (frames are runs of raster blocks)."""
+    p = _prob().c()
+    p.token_order = ctypes.c_void_p(1 << 20)       # never dereferenced on the host
+    vp = ctypes.c_void_p
+    fake = vp(1 << 20)
+    st = sa.lib.hilbert_permute(ctypes.byref(p), fake, vp(1 << 30), fake, None)
+    assert st == sa.SA_ERR_UNSUPPORTED and b"token_order" in sa.lib.sparse_attn_last_error()
+    cs = sa.ClusterSpec("kmeans", 4, 2).c()
+    nbp, w1, w2 = ctypes.c_int32(0), ctypes.c_size_t(0), ctypes.c_size_t(0)
+    st = sa.lib.sparse_attn_cluster_size(ctypes.byref(p), ctypes.byref(cs), ctypes.byref(nbp),
+                                         ctypes.byref(w1), ctypes.byref(w2))
+    assert st == sa.SA_ERR_UNSUPPORTED
+    spec, keep = sa.SelectSpec(rule="none", window_frames=1).c()
+    n = ctypes.c_size_t(0)
+    st = sa.lib.sparse_attn_workspace_size(ctypes.byref(p), ctypes.byref(spec), ctypes.byref(n))
+    assert st == sa.SA_ERR_UNSUPPORTED and b"window" in sa.lib.sparse_attn_last_error()
+    # the forward workspace grows by K in block order
+    q = _prob().c()
+    base = ctypes.c_size_t(0)
+    assert sa.lib.sparse_attn_workspace_size(ctypes.byref(q), None, ctypes.byref(base)) == 0
+    assert sa.lib.sparse_attn_workspace_size(ctypes.byref(p), None, ctypes.byref(n)) == 0
+    g = GOOD
+    assert n.value - base.value >= g["B"] * g["H"] * g["N"] * g["d"] * 2

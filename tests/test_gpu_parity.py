@@ -80,10 +80,10 @@ def test_small_workload_parity(name):
     off = W.anchor_offset(wl.seed, 0, wl.nb)
     case = OracleCase(wl, Q, K, V, anchor_offset=off)
     pipe = _pipeline(wl)
-    poison(pipe.O, pipe.lse, getattr(pipe, "Op", None))
+    poison(pipe.O, pipe.lse)
     O = pipe(to_dev(Q), to_dev(K), to_dev(V), anchor_offset=off)
     torch.cuda.synchronize()
-    assert_outputs_written(from_dev(O), pipe.lse.cpu().numpy(), wl, pipe.keep_mask())
+    assert_outputs_written(from_dev(O), pipe.lse.cpu().numpy(), wl, pipe.keep_mask(), perm=pipe.perm)
 
     if wl.rule == "err":
         S = pipe.sel.scores.view(wl.B, wl.H, wl.nb, wl.nb).cpu().numpy()
@@ -121,16 +121,12 @@ def test_small_workload_parity(name):
 
     # attention given the oracle's mask
     rp, ci = oracle.keep_to_csr(case.keep.reshape(-1, wl.nb))
-    Qp, Kp, Vp = pipe.permute_inputs(to_dev(Q), to_dev(K), to_dev(V))
-    poison(pipe.O, pipe.lse, getattr(pipe, "Op", None))
-    pipe.run_fwd(Qp, Kp, Vp, torch.from_numpy(rp).cuda(), torch.from_numpy(ci).cuda())
-    O = pipe.unpermute_output()
+    poison(pipe.O, pipe.lse)
+    O = pipe.run_fwd(to_dev(Q), to_dev(K), to_dev(V), torch.from_numpy(rp).cuda(),
+                     torch.from_numpy(ci).cuda())
     torch.cuda.synchronize()
-    assert_outputs_written(from_dev(O), pipe.lse.cpu().numpy(), wl, case.keep)
-    lse = pipe.lse.cpu().numpy()
-    if wl.hilbert:
-        lse = lse[..., np.argsort(pipe.perm)]            # back to raster order
-    torch.cuda.synchronize()
+    assert_outputs_written(from_dev(O), pipe.lse.cpu().numpy(), wl, case.keep, perm=pipe.perm)
+    lse = pipe.lse.cpu().numpy()                          # raster order
     emax, emean, lmax, n = compare_attention(from_dev(O), case, None, lse_gpu=lse)
     log(f"[parity] {name}: attention max={emax:.2e} mean={emean:.2e} lse={lmax:.2e}")
     assert emax <= ATOL_MAX and emean <= ATOL_MEAN and lmax <= LSE_ATOL
@@ -234,17 +230,14 @@ def test_fwd_halves_match_fwd(name):
     wl = SMALL[name]
     Q, K, V = (to_dev(x) for x in W.make_qkv(wl))
     pipe = _pipeline(wl)
-    Qp, Kp, Vp = pipe.permute_inputs(Q, K, V)
-    pipe.run_select(Qp, Kp, Vp, 0)
-    ref = pipe.run_fwd(Qp, Kp, Vp).clone()
+    pipe.run_select(Q, K, V, 0)
+    ref = pipe.run_fwd(Q, K, V).clone()
     ref_lse = pipe.lse.clone()
     pipe.O.zero_()
-    if pipe.hilbert:
-        pipe.Op.zero_()
-    pipe.run_fwd_prepare(Vp)
+    pipe.run_fwd_prepare(V)
     outs = []
     for _ in range(2):
-        outs.append((pipe.run_fwd_attention(Qp, Kp).clone(), pipe.lse.clone()))
+        outs.append((pipe.run_fwd_attention(Q, K).clone(), pipe.lse.clone()))
     torch.cuda.synchronize()
     for o, lse in outs:
         assert torch.equal(o.view(torch.int16), ref.view(torch.int16))
@@ -290,8 +283,6 @@ def test_mask_reuse_across_steps(name):
                         assert np.array_equal(km[b, h], oracle.block_means(k, wl.block))
                         assert np.array_equal(vs[b, h], oracle.block_sums_f32(v, wl.block))
         lse = pipe.lse.cpu().numpy()
-        if wl.hilbert:
-            lse = lse[..., np.argsort(pipe.perm)]
         emax, emean, lmax, n = compare_attention(from_dev(O), case, None, lse_gpu=lse)
         log(f"[reuse] {name}: step {s}: attention max={emax:.2e} mean={emean:.2e} lse={lmax:.2e}")
         assert emax <= ATOL_MAX and emean <= ATOL_MEAN and lmax <= LSE_ATOL
