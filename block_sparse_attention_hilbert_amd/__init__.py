@@ -76,7 +76,8 @@ class SaTileShape(ctypes.Structure):
 class SaClusterSpec(ctypes.Structure):
     _fields_ = [("mode", ctypes.c_int32), ("n_clusters", ctypes.c_int32),
                 ("iters", ctypes.c_int32), ("n_shapes", ctypes.c_int32),
-                ("shapes", ctypes.POINTER(SaTileShape)), ("shape_idx", ctypes.c_void_p)]
+                ("shapes", ctypes.POINTER(SaTileShape)), ("shape_idx", ctypes.c_void_p),
+                ("ticket", ctypes.c_float), ("tile_coherence", ctypes.c_void_p)]
 
 
 class SparseAttnError(RuntimeError):
@@ -506,10 +507,16 @@ class ClusterSpec:
     iters: int = 3
     shapes: Optional[Sequence] = None          # tiles: menu of (t, y, x)
     shape_idx: Optional[torch.Tensor] = None   # tiles: device int32 [B*H]
+    ticket: Optional[float] = None             # tiles: SICS ticket in [-1, 1], or none
+    tile_coherence: Optional[torch.Tensor] = None  # tiles + ticket: fp64 [B*H, n_shapes, C]
 
     def c(self) -> SaClusterSpec:
         if self.shape_idx is not None:
             _Args()(self.shape_idx, "shape_idx", _I32)
+        if (self.ticket is None) != (self.tile_coherence is None):
+            raise ValueError("a SICS ticket and tile_coherence go together")
+        if self.tile_coherence is not None:
+            _Args()(self.tile_coherence, "tile_coherence", torch.float64)
         n, sp = 0, None
         if self.shapes:
             arr = (SaTileShape * len(self.shapes))(*[SaTileShape(*map(int, s)) for s in self.shapes])
@@ -517,7 +524,9 @@ class ClusterSpec:
             sp = ctypes.cast(arr, ctypes.POINTER(SaTileShape))
             n = len(self.shapes)
         return SaClusterSpec(CLUSTER_MODES[self.mode], self.n_clusters, self.iters, n, sp,
-                             None if self.shape_idx is None else self.shape_idx.data_ptr())
+                             None if self.shape_idx is None else self.shape_idx.data_ptr(),
+                             0.0 if self.ticket is None else float(self.ticket),
+                             None if self.tile_coherence is None else self.tile_coherence.data_ptr())
 
 
 def cluster_size(prob: Problem, cspec: ClusterSpec):
@@ -711,5 +720,6 @@ def cluster_spec_for(wl) -> ClusterSpec:
     """Cluster spec of a workload description (cluster, n_clusters, cluster_iters,
     tile_shapes)."""
     if wl.cluster == "tiles":
-        return ClusterSpec("tiles", wl.n_clusters, 0, shapes=[tuple(s) for s in wl.tile_shapes])
+        return ClusterSpec("tiles", wl.n_clusters, 0, shapes=[tuple(s) for s in wl.tile_shapes],
+                           ticket=wl.sics_ticket)
     return ClusterSpec(wl.cluster, wl.n_clusters, wl.cluster_iters)

@@ -639,6 +639,12 @@ struct CSelArgs {
     uint8_t* keep;              // [BH][C][C]
     int32_t C, Cpad, H, rule, diag;
     float mass;
+    // tile mode with a SICS ticket: key tile j of head bh may be kept only if
+    // coh[(bh * n_shapes + shape_idx[bh]) * C + j] >= ticket (else coh null)
+    const double* coh;
+    const int32_t* shape_idx;
+    int32_t n_shapes;
+    double ticket;
 };
 
 __global__ __launch_bounds__(kSelThreads) void k_cselect(CSelArgs a) {
@@ -656,9 +662,16 @@ __global__ __launch_bounds__(kSelThreads) void k_cselect(CSelArgs a) {
     const int32_t* nk = a.nk + bh * a.C;
     if (tid == 0) { s_live = 0; s_cut = 0; }
     __syncthreads();
+    const double* coh = nullptr;
+    if (a.coh) {
+        int sh = a.shape_idx[bh];
+        sh = sh < 0 ? 0 : (sh >= a.n_shapes ? a.n_shapes - 1 : sh);
+        coh = a.coh + (bh * a.n_shapes + sh) * a.C;
+    }
     int live_local = 0;
     for (int j = tid; j < a.Cpad; j += kSelThreads) {
-        const bool live = j < a.C && nk[j] > 0;
+        // a live key cluster has tokens and, with a ticket, coherent keys
+        const bool live = j < a.C && nk[j] > 0 && (!coh || coh[j] >= a.ticket);
         live_local += live;
         key[j] = live ? ((unsigned long long)(~ordered_f32(S[j])) << 32) | (uint32_t)j : ~0ull;
     }
@@ -1030,6 +1043,12 @@ sa_status launch_cluster_select(const Geometry& g, const sa_cluster_spec& cs, co
     CSelArgs ca{};
     ca.S = S; ca.nk = a.k_count; ca.budget = budget; ca.keep = keep;
     ca.C = C; ca.H = g.H; ca.rule = a.rule; ca.diag = a.diag; ca.mass = a.mass;
+    if (cs.mode == SA_CLUSTER_TILES && cs.tile_coherence) {
+        ca.coh = cs.tile_coherence;
+        ca.shape_idx = cs.shape_idx;
+        ca.n_shapes = cs.n_shapes;
+        ca.ticket = (double)cs.ticket;
+    }
     int cpad = 2;
     while (cpad < C) cpad <<= 1;
     ca.Cpad = cpad;

@@ -160,14 +160,17 @@ __global__ __launch_bounds__(256) void k_sics_atoms(const uint16_t* __restrict__
 
 // One workgroup of D threads per (tile, shape, b*h); thread c owns channel c.
 // The tile's atoms are summed in raster order and the channels in a fixed
-// tree; writes the tile's SICS (Q and K) and its ordered pair count.
+// tree; writes the tile's SICS (Q and K) and its ordered pair count, and with
+// kcoh the mean cosine of its keys' ordered pairs, SICS_K / (n (n - 1)) (1 for
+// a tile of fewer than two tokens: its mean is its token).
 template <int D>
 __global__ __launch_bounds__(D) void k_sics_tiles(const double* __restrict__ U,
                                                   const int32_t* __restrict__ NZ,
                                                   double* __restrict__ tile_sics,
-                                                  double* __restrict__ tile_pairs, Menu m, int T,
+                                                  double* __restrict__ tile_pairs,
+                                                  double* __restrict__ kcoh, Menu m, int T,
                                                   int Hg, int W, int64_t natoms, int cmax) {
-    __shared__ double wsum[D / 64];
+    __shared__ double wsum[D / 64], wsumk[D / 64];
     const int tile = blockIdx.x, s = blockIdx.y;
     const int64_t bh = blockIdx.z;
     if (tile >= m.ntiles[s]) return;
@@ -181,7 +184,7 @@ __global__ __launch_bounds__(D) void k_sics_tiles(const double* __restrict__ U,
     const int t0 = tt * ts, y0 = ty * ys, x0 = tx * xs;
     const int t1 = min(T, t0 + ts), y1 = min(Hg, y0 + ys), x1 = min(W, x0 + xs);
     double uq = 0.0, uk = 0.0;
-    int nz = 0;
+    int nz = 0, nzk = 0;
     for (int ta = t0 / m.at; ta < (t1 + m.at - 1) / m.at; ++ta)
         for (int ya = y0 / m.ay; ya < (y1 + m.ay - 1) / m.ay; ++ya)
             for (int xa = x0 / m.ax; xa < (x1 + m.ax - 1) / m.ax; ++xa) {
@@ -189,18 +192,29 @@ __global__ __launch_bounds__(D) void k_sics_tiles(const double* __restrict__ U,
                 uq += Uq[a * D + c];
                 uk += Uk[a * D + c];
                 nz += Nq[a] + Nk[a];
+                nzk += Nk[a];
             }
-    double v = uq * uq + uk * uk;
-    for (int off = 32; off > 0; off >>= 1) v += __shfl_down(v, off, 64);
-    if (lane == 0) wsum[wid] = v;
+    double v = uq * uq + uk * uk, vk = uk * uk;
+    for (int off = 32; off > 0; off >>= 1) {
+        v += __shfl_down(v, off, 64);
+        vk += __shfl_down(vk, off, 64);
+    }
+    if (lane == 0) {
+        wsum[wid] = v;
+        wsumk[wid] = vk;
+    }
     __syncthreads();
     if (c == 0) {
-        double tv = 0.0;
-        for (int w = 0; w < D / 64; ++w) tv += wsum[w];
+        double tv = 0.0, tk = 0.0;
+        for (int w = 0; w < D / 64; ++w) {
+            tv += wsum[w];
+            tk += wsumk[w];
+        }
         const double n = (double)(t1 - t0) * (y1 - y0) * (x1 - x0);
         const int64_t o = (bh * m.n + s) * cmax + tile;
         tile_sics[o] = tv - (double)nz;
         tile_pairs[o] = n * (n - 1.0);
+        if (kcoh) kcoh[o] = n < 2.0 ? 1.0 : (tk - (double)nzk) / (n * (n - 1.0));
     }
 }
 
@@ -291,11 +305,11 @@ sa_status launch_sics(const Geometry& g, const sa_cluster_spec& cs, const uint16
     double* tpairs = reinterpret_cast<double*>(ws + w.tpairs);
     const dim3 gt((unsigned)cmax, (unsigned)m.n, (unsigned)g.BH());
     if (g.d == 128)
-        hipLaunchKernelGGL((k_sics_tiles<128>), gt, dim3(128), 0, st, U, NZ, tsics, tpairs, m, g.T,
-                           g.Hg, g.W, na, cmax);
+        hipLaunchKernelGGL((k_sics_tiles<128>), gt, dim3(128), 0, st, U, NZ, tsics, tpairs,
+                           cs.tile_coherence, m, g.T, g.Hg, g.W, na, cmax);
     else
-        hipLaunchKernelGGL((k_sics_tiles<64>), gt, dim3(64), 0, st, U, NZ, tsics, tpairs, m, g.T,
-                           g.Hg, g.W, na, cmax);
+        hipLaunchKernelGGL((k_sics_tiles<64>), gt, dim3(64), 0, st, U, NZ, tsics, tpairs,
+                           cs.tile_coherence, m, g.T, g.Hg, g.W, na, cmax);
     if ((e = hip_check(hipGetLastError(), "k_sics_tiles launch")) != SA_OK) return e;
     hipLaunchKernelGGL(k_sics_shapes, dim3((unsigned)ceil_div(g.BH() * m.n, 4)), dim3(256), 0, st,
                        tsics, tpairs, sc, m, g.BH(), cmax);

@@ -445,6 +445,8 @@ static sa_status check_cluster(const Geometry& g, const sa_cluster_spec* cs) {
         if (cs->n_clusters != mt)
             return fail(SA_ERR_INVALID_ARG, "n_clusters = %d must be the menu's largest tile count %d",
                         cs->n_clusters, mt);
+        if (cs->tile_coherence && !(cs->ticket >= -1.f && cs->ticket <= 1.f))
+            return fail(SA_ERR_INVALID_ARG, "ticket = %g must be in [-1, 1]", (double)cs->ticket);
     } else {
         const int cmax = g.N < 1024 ? g.N : 1024;
         if (cs->n_clusters < 1 || cs->n_clusters > cmax)
@@ -616,6 +618,8 @@ SA_API sa_status sparse_attn_cluster_select(const sa_problem* prob, const sa_clu
     } else if (!(spec->mass > 0.f && spec->mass <= 1.f)) {
         return fail(SA_ERR_INVALID_ARG, "mass = %g must be in (0, 1]", (double)spec->mass);
     }
+    if (cspec->mode == SA_CLUSTER_TILES && cspec->tile_coherence && !cspec->shape_idx)
+        return fail(SA_ERR_INVALID_ARG, "a SICS ticket needs shape_idx (the chosen shapes)");
     if (!q_cent || !k_cent || !k_count || !q_blk || !k_blk || !k_cnt || !row_ptr || !col_idx)
         return fail(SA_ERR_INVALID_ARG, "q_cent, k_cent, k_count, q_blk, k_blk, k_cnt, row_ptr "
                                         "and col_idx are required");

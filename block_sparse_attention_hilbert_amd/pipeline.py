@@ -28,7 +28,9 @@ With ``refresh_every = r`` it clusters and selects on calls 0, r, 2r, ...
 the partition and the keep lists, gather their own Q, K, V into the layout and,
 with compensation, take the cluster centroids from their own K and V.
 With a ``tiles`` cluster spec (SPADE parts 1-2) the partition of every head is
-the tile grid of the menu shape that SICS picks for it on the refreshing call.
+the tile grid of the menu shape that SICS picks for it on the refreshing call;
+with a SICS ticket only the tiles whose keys agree (mean pairwise key cosine
+at least the ticket) may be kept, the others are ignored.
 """
 from __future__ import annotations
 
@@ -164,13 +166,18 @@ class ClusteredAttention:
         self.prob, self.spec = prob, spec
         self.device = torch.device(device)
         self.shape_idx = self.shape_scores = None
+        self.tile_coherence = None
         if cspec.mode == "tiles":
             BH = prob.B * prob.H
             self.shape_idx = torch.zeros(BH, dtype=torch.int32, device=self.device)
             self.shape_scores = torch.zeros(BH, len(cspec.shapes), dtype=torch.float64,
                                             device=self.device)
+            if cspec.ticket is not None:
+                # every tile's key coherence, for the SICS ticket
+                self.tile_coherence = torch.zeros(BH, len(cspec.shapes), cspec.n_clusters,
+                                                  dtype=torch.float64, device=self.device)
             cspec = ClusterSpec(cspec.mode, cspec.n_clusters, cspec.iters, list(cspec.shapes),
-                                self.shape_idx)
+                                self.shape_idx, cspec.ticket, self.tile_coherence)
         self.cspec = cspec
         self.refresh_every = int(refresh_every)
         self.calls = 0

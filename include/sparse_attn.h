@@ -136,7 +136,25 @@ typedef struct {
                                      t*y*x <= block, so a tile is one block      */
     const int32_t* shape_idx;     /* TILES: device int32 [B*H], the menu entry of
                                      each (b, h) (sparse_attn_sics writes it);
-                                     needed by sparse_attn_cluster only          */
+                                     read by sparse_attn_cluster and, with a
+                                     ticket, sparse_attn_cluster_select          */
+    float ticket;                 /* TILES with tile_coherence: the SICS ticket
+                                     [SPADE part 2], finite in [-1, 1].  A key
+                                     tile whose keys agree -- mean cosine of its
+                                     ordered key pairs >= ticket, decided in
+                                     fp64 -- may be kept; the others are ignored
+                                     (never kept; with compensation they enter
+                                     as centroids).  Unused without
+                                     tile_coherence.                             */
+    double* tile_coherence;       /* TILES, optional (null: no ticket, every tile
+                                     may be kept): device fp64 [B*H, n_shapes,
+                                     n_clusters], the mean key cosine of every
+                                     tile of every menu shape (1 for a tile of
+                                     fewer than two tokens; entries past a
+                                     shape's tile count are not written).
+                                     sparse_attn_sics writes it,
+                                     sparse_attn_cluster_select reads it with
+                                     shape_idx and applies the ticket           */
 } sa_cluster_spec;
 
 /* Selection rule.  Host-side struct; `topk` and `density` are host arrays. */

@@ -166,10 +166,12 @@ def cluster_scores(cq: np.ndarray, ck: np.ndarray, sigma: float) -> np.ndarray:
 
 
 def cluster_select(S: np.ndarray, nk: np.ndarray, N: int, rule: str,
-                   density: float = 0.0, tau: float = 1.0, diag: bool = False) -> np.ndarray:
+                   density: float = 0.0, tau: float = 1.0, diag: bool = False,
+                   eligible=None) -> np.ndarray:
     """Kept key clusters of every query cluster, bool [C, C].
 
-    Empty key clusters are never kept.  The others are ranked by S
+    Empty key clusters, and those ``eligible`` (bool [C], optional) rules out,
+    are never kept.  The others are ranked by S
     (descending, lower index on ties); "topk" keeps the shortest prefix whose
     token count reaches B = max(1, ceil(density * N * (1 - 1e-6))) (density a
     float32); "mass" keeps the shortest prefix whose weight sum_{prefix}
@@ -178,10 +180,17 @@ def cluster_select(S: np.ndarray, nk: np.ndarray, N: int, rule: str,
     """
     C = S.shape[0]
     keep = np.zeros((C, C), dtype=bool)
-    live = np.nonzero(nk > 0)[0]
+    ok = nk > 0
+    if eligible is not None:
+        ok = ok & np.asarray(eligible, dtype=bool)
+    live = np.nonzero(ok)[0]
     if rule == "topk":
         budget = max(1, int(np.ceil(float(np.float32(density)) * N * (1.0 - 1e-6))))
     for a in range(C):
+        if diag and nk[a] > 0:
+            keep[a, a] = True
+        if live.size == 0:
+            continue
         s = S[a, live]
         order = live[np.argsort(-s.astype(np.float64), kind="stable")]
         if rule == "topk":
@@ -196,8 +205,6 @@ def cluster_select(S: np.ndarray, nk: np.ndarray, N: int, rule: str,
         else:
             raise ValueError(rule)
         keep[a, order[:min(m, order.size)]] = True
-        if diag and nk[a] > 0:
-            keep[a, a] = True
     return keep
 
 

@@ -22,7 +22,13 @@ where it is used):
 * the blocks of the chosen shape then go through the same selection as
   data-dependent blocks (scores of tile means, token budget or
   count-weighted cumulative mass) -- ``oracle.clusters`` with the tile index
-  as the cluster.
+  as the cluster;
+* the optional SICS ticket theta (part 2's admission test): a key tile may
+  be kept only if the mean cosine of its keys' ordered pairs,
+  SICS_K / (n (n - 1)), is at least theta (a tile of one token counts as 1);
+  the other tiles are ignored by the selection, i.e. treated like empty
+  clusters (the explicit diagonal still adds a query tile's own keys);
+  without a ticket (the default) every tile is admitted, as with theta = -1.
 
 The shape choice is float64 on both sides; the scores of two shapes closer
 than a relative 1e-9 are a near tie.
@@ -100,15 +106,26 @@ def choose_shape(Qh, Kh, grid, shapes: Sequence[Shape]):
     return int(np.argmax(scores)), scores
 
 
+def key_coherence(Kh: np.ndarray, assign: np.ndarray, ntiles: int) -> np.ndarray:
+    """Mean cosine over the ordered pairs of distinct keys of every tile,
+    SICS_K / (n (n - 1)); 1 for a tile of fewer than two tokens."""
+    n = np.bincount(assign, minlength=ntiles).astype(np.float64)
+    out = np.ones(ntiles)
+    many = n >= 2
+    out[many] = sics_per_tile(Kh, assign, ntiles)[many] / (n[many] * (n[many] - 1.0))
+    return out
+
+
 def max_tiles(grid, shapes: Sequence[Shape]) -> int:
     return max(n_tiles(*grid, s) for s in shapes)
 
 
 def tiles_workload_head(wl, Qh, Kh):
     """The tiled path of one head (duck-typed workload: T, Hg, W, block,
-    tile_shapes, scale, rule, density, mass, diag).  Returns the same dict as
-    ``clusters.cluster_workload_head`` plus the shape scores and the chosen
-    shape."""
+    tile_shapes, scale, rule, density, mass, diag, optionally sics_ticket).
+    Returns the same dict as ``clusters.cluster_workload_head`` plus the
+    shape scores, the chosen shape, the key coherence of its tiles and which
+    of them the ticket admits."""
     grid = (wl.T, wl.Hg, wl.W)
     shapes = [tuple(s) for s in wl.tile_shapes]
     pick, scores = choose_shape(Qh, Kh, grid, shapes)
@@ -122,8 +139,17 @@ def tiles_workload_head(wl, Qh, Kh):
     dens = 0.0
     if wl.rule == "topk":
         dens = float(wl.densities()[0])
-    keepC = OC.cluster_select(S, nk, N, wl.rule, density=dens, tau=wl.mass, diag=wl.diag)
+    # the ticket is a float32 compared in float64 with the fp64 coherence
+    ticket = getattr(wl, "sics_ticket", None)
+    coh = key_coherence(Kh, a, C)
+    eligible = np.ones(C, dtype=bool)
+    if ticket is not None:
+        ticket = float(np.float32(ticket))
+        eligible = coh >= ticket
+    keepC = OC.cluster_select(S, nk, N, wl.rule, density=dens, tau=wl.mass, diag=wl.diag,
+                              eligible=eligible)
     order, blk, cnt = OC.cluster_layout(a, C, wl.block, nbp=C)
-    return dict(pick=pick, scores=scores, aq=a, ak=a, cq=cq, ck=ck, S=S, keepC=keepC, nq=nk,
+    return dict(pick=pick, scores=scores, coh=coh, eligible=eligible, ticket=ticket,
+                aq=a, ak=a, cq=cq, ck=ck, S=S, keepC=keepC, nq=nk,
                 nk=nk, q_order=order, q_blk=blk, q_cnt=cnt, k_order=order, k_blk=blk, k_cnt=cnt,
                 keep=OC.cluster_block_keep(keepC, blk, blk))

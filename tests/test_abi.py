@@ -218,6 +218,40 @@ def test_cluster_sizes_and_validation():
     assert _err(sa.cluster_size, big, sa.ClusterSpec("kmeans", 16, 1)) == sa.SA_ERR_UNSUPPORTED
 
 
+def test_sics_ticket_validation():
+    """The SICS ticket is opt-in through tile_coherence: without the buffer
+    the ticket field is never read; with it the ticket must lie in [-1, 1],
+    and the selection needs the chosen shapes."""
+    small = _prob()                                   # grid 3 x 10 x 13
+    menu = [(1, 4, 16), (1, 8, 8)]                    # 3*3*1 and 3*2*2 tiles
+    spec = sa.ClusterSpec("tiles", 12, 0, shapes=menu)
+    sa.cluster_size(small, spec)
+    raw = spec.c()
+    size = sa.lib.sparse_attn_cluster_size
+    for t in (float("nan"), 1.5, -1.25, float("inf")):
+        raw.ticket = t
+        raw.tile_coherence = None                     # no buffer: no ticket, accepted
+        assert size(ctypes.byref(small.c()), ctypes.byref(raw), None, None, None) == sa.SA_OK
+        raw.tile_coherence = 1 << 20
+        assert size(ctypes.byref(small.c()), ctypes.byref(raw), None, None, None) == \
+            sa.SA_ERR_INVALID_ARG, t
+    for t in (-1.0, 0.0, 0.72, 1.0):
+        raw.ticket = t
+        assert size(ctypes.byref(small.c()), ctypes.byref(raw), None, None, None) == sa.SA_OK, t
+    # the selection with a ticket but no shape_idx is refused before any launch
+    raw.ticket, raw.shape_idx = 0.5, None
+    fake = ctypes.c_void_p(1 << 20)
+    sel, _keep = sa.SelectSpec(rule="mass").c()
+    call = sa.lib.sparse_attn_cluster_select
+    args = [*([fake] * 9), None, None, None, fake, 1 << 30, None]
+    assert call(ctypes.byref(small.c()), ctypes.byref(raw), ctypes.byref(sel), *args) == \
+        sa.SA_ERR_INVALID_ARG
+    assert b"shape_idx" in sa.lib.sparse_attn_last_error()
+    # the binding wants both or neither
+    with pytest.raises(ValueError):
+        sa.ClusterSpec("tiles", 12, 0, shapes=menu, ticket=0.5).c()
+
+
 def test_cluster_calls_reject_before_any_launch():
     p = _prob().c()
     cs = sa.ClusterSpec("cocluster", 4, 2).c()

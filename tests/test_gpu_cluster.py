@@ -83,6 +83,11 @@ SMALL = {
                                       tile_shapes=((1, 4, 16), (1, 8, 8), (2, 4, 8)),
                                       n_clusters=12, rule="topk", density=0.3),
 }
+# the SICS ticket: at 0.3 one head admits every tile, two some and one none
+# (its rows keep nothing, or only their own tile with the diagonal)
+SMALL["tiles_ticket_topk_d128_b64"] = SMALL["tiles_topk_d128_b64"].replace(sics_ticket=0.3)
+SMALL["tiles_ticket_mass_comp_diag"] = SMALL["tiles_mass_comp_diag_d64_b128"].replace(
+    sics_ticket=0.3)
 
 
 def _keep_from_csr(rp, ci, rows, nbp):
@@ -143,6 +148,11 @@ def check_case(wl, Q, K, V, heads, q_clusters_per_head=None, seed=0):
                 assert abs(top[pick_gpu[bh]] - top[ref["pick"]]) <= 1e-9 * np.abs(top).max(), tag
                 excused += 1
                 forced[bh] = ref["pick"]
+            if ref["ticket"] is not None:
+                # no tile's coherence may sit on the ticket: then the
+                # admission is exact on both sides
+                nt = int((ref["nk"] > 0).sum())
+                assert np.all(np.abs(ref["coh"][:nt] - ref["ticket"]) > 1e-9), tag
             refs[bh] = ref
         if excused:
             log(f"[cluster] {wl.name}: {excused} near-tie shape picks; rerun with the oracle's")
@@ -151,6 +161,15 @@ def check_case(wl, Q, K, V, heads, q_clusters_per_head=None, seed=0):
             O = pipe(Qd, Kd, Vd, reuse=False, choose_shapes=False)
             torch.cuda.synchronize()
             assert np.array_equal(pipe.shape_idx.cpu().numpy(), forced)
+    if tiles and wl.sics_ticket is not None:
+        coh_gpu = pipe.tile_coherence.cpu().numpy()
+        for bh in heads:
+            ref = refs[bh]
+            nt = int((ref["nk"] > 0).sum())
+            got = coh_gpu[bh, ref["pick"], :nt]
+            assert np.allclose(got, ref["coh"][:nt], rtol=1e-9, atol=1e-12), f"{wl.name} bh={bh}"
+            log(f"[cluster] {wl.name} bh={bh}: {int(ref['eligible'][:nt].sum())} of {nt} "
+                f"tiles admitted by the ticket {ref['ticket']:.3f}")
     assert not np.any((from_dev(O) & 0x7F80) == 0x7F80), "O holds NaN/Inf: rows not written"
     assert not np.any(np.isnan(pipe.lse.cpu().numpy())), "lse holds NaN: rows not written"
     C, nbp, blk = wl.n_clusters, pipe.nbp, wl.block
@@ -217,7 +236,8 @@ def check_case(wl, Q, K, V, heads, q_clusters_per_head=None, seed=0):
         for a in np.nonzero(np.any(keepC_gpu != ref["keepC"], axis=1))[0]:
             if ref["nq"][a] == 0:
                 continue
-            assert _excused(ref["S"][a], ref["nk"], wl, keepC_gpu[a], ref["keepC"][a]), (tag, a)
+            nk_live = ref["nk"] * ref.get("eligible", True)
+            assert _excused(ref["S"][a], nk_live, wl, keepC_gpu[a], ref["keepC"][a]), (tag, a)
             excused += 1
         # attention in token order, given the oracle's partition and keep
         qcs = list(range(C))
@@ -251,7 +271,8 @@ def test_small_cluster_parity(name):
     assert emax <= ATOL_MAX and emean <= ATOL_MEAN and lmax <= LSE_ATOL
 
 
-@pytest.mark.parametrize("name", ["wan13b_cocluster", "wan13b_kmeans_comp", "wan13b_sics"])
+@pytest.mark.parametrize("name", ["wan13b_cocluster", "wan13b_kmeans_comp", "wan13b_sics",
+                                  "wan13b_sics_ticket"])
 def test_full_size_cluster_parity(name):
     """The full 1.3B-sized layer (12 heads, N = 32,760): the whole call on the
     GPU; layouts, centroids, scores and keep of two heads checked exactly and

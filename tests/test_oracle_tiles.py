@@ -140,3 +140,95 @@ def test_tiles_workload_head_layout_is_one_block_per_tile():
         assert np.array_equal(toks[toks >= 0], np.nonzero(a == j)[0])
     # the means are the tiles' exact means
     assert np.array_equal(ref["cq"], OC.cluster_means(Q, a, C))
+
+
+def test_key_coherence_against_pairwise_cosines_and_limits():
+    rng = np.random.default_rng(11)
+    X = rng.normal(size=(40, 8))
+    X[7] = 0.0                                        # a zero key: cosine 0 with everything
+    a = rng.integers(0, 5, size=40)
+    a[3] = 5                                          # tile 5 holds one token
+    coh = OT.key_coherence(X, a, 7)
+    for c in range(5):
+        rows = X[a == c]
+        n = len(rows)
+        assert coh[c] == pytest.approx(_pairwise_cos_sum(rows) / (n * (n - 1)), rel=1e-12,
+                                       abs=1e-12)
+    assert coh[5] == 1.0 and coh[6] == 1.0            # one token, no token
+    # identical keys agree fully; alternating antipodal pairs disagree fully
+    same = np.tile(np.array([[0.5, -1.0, 2.0]]), (6, 1))
+    assert OT.key_coherence(same, np.zeros(6, dtype=np.int64), 1)[0] == pytest.approx(1.0)
+    alt = np.array([[1.0, 2.0], [-1.0, -2.0]])
+    assert OT.key_coherence(alt, np.zeros(2, dtype=np.int64), 1)[0] == pytest.approx(-1.0)
+    # a key and a zero key: the one pair has cosine 0
+    half = np.array([[1.0, 2.0], [0.0, 0.0]])
+    assert OT.key_coherence(half, np.zeros(2, dtype=np.int64), 1)[0] == 0.0
+
+
+def _ticket_field(grid, noisy_tiles, shape, d=16, seed=0):
+    """Keys constant within every tile of `shape` except the tiles listed,
+    whose keys are independent noise; queries random."""
+    T, Hg, W = grid
+    rng = np.random.default_rng(seed)
+    a = OT.tile_assign(T, Hg, W, shape)
+    nt = OT.n_tiles(T, Hg, W, shape)
+    base = rng.normal(size=(nt, d))
+    K = base[a].copy()
+    for t in noisy_tiles:
+        K[a == t] = rng.normal(size=((a == t).sum(), d))
+    return rng.normal(size=(T * Hg * W, d)), K
+
+
+class _TicketWL(_WL):
+    T, Hg, W, block = 2, 8, 16, 64
+    tile_shapes = [(1, 4, 16)]
+    scale = float(np.float32(1 / np.sqrt(16)))
+
+
+@pytest.mark.parametrize("rule,diag", [("topk", False), ("mass", False), ("topk", True)])
+def test_ticket_ignores_incoherent_tiles(rule, diag):
+    grid = (2, 8, 16)
+    noisy = [1, 2]
+    Q, K = _ticket_field(grid, noisy, (1, 4, 16), seed=7)
+    wl = _TicketWL()
+    wl.rule, wl.diag, wl.mass = rule, diag, 0.95
+    wl.densities = lambda: np.full(1, 0.2, np.float32)
+    base = OT.tiles_workload_head(wl, Q, K)
+    assert base["pick"] == 0
+    assert np.all(base["eligible"])                   # no ticket: every tile
+    wl.sics_ticket = 0.5
+    ref = OT.tiles_workload_head(wl, Q, K)
+    assert np.allclose(ref["coh"][[0, 3]], 1.0) and np.all(ref["coh"][noisy] < 0.2)
+    assert np.array_equal(ref["eligible"], [True, False, False, True])
+    keep = ref["keepC"]
+    for a_ in range(4):
+        for t in noisy:
+            # a noisy tile is never kept, except as a row's own diagonal
+            assert keep[a_, t] == (diag and a_ == t)
+    # brute force: every row's selection equals the one made over the
+    # admitted tiles alone (re-indexed), plus its own tile with the diagonal
+    adm = [0, 3]
+    S, nk = base["S"], base["nk"]
+    for a_ in range(4):
+        row = S[a_:a_ + 1][:, adm]
+        want = OC.cluster_select(np.vstack([row, row]), nk[adm], Q.shape[0], rule,
+                                 density=0.2, tau=0.95)[0]
+        if diag and a_ in adm:
+            want[adm.index(a_)] = True
+        assert np.array_equal(keep[a_, adm], want), a_
+    # a ticket of -1 admits every tile and leaves the selection as it was
+    wl.sics_ticket = -1.0
+    same = OT.tiles_workload_head(wl, Q, K)
+    assert np.array_equal(same["keepC"], base["keepC"])
+
+
+def test_ticket_admitting_nothing_keeps_nothing_but_the_diagonal():
+    rng = np.random.default_rng(2)
+    S = rng.normal(size=(4, 4)).astype(np.float32)
+    nk = np.array([5, 5, 5, 0])
+    none = np.zeros(4, dtype=bool)
+    for rule in ("topk", "mass"):
+        assert not OC.cluster_select(S, nk, 15, rule, density=0.5, tau=0.9,
+                                     eligible=none).any()
+        k = OC.cluster_select(S, nk, 15, rule, density=0.5, tau=0.9, diag=True, eligible=none)
+        assert np.array_equal(k, np.diag([True, True, True, False]))

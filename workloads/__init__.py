@@ -88,6 +88,7 @@ class Workload:
     cluster_iters: int = 0
     tile_shapes: tuple = ()        # "tiles": the menu of (t, y, x) tile shapes
     aniso: bool = False            # head-dependent anisotropy of the smooth field
+    sics_ticket: Optional[float] = None  # "tiles": keep only tiles of key coherence >= this
 
     @property
     def N(self) -> int:
@@ -164,6 +165,11 @@ EXTRA = {
     "wan13b_sics": CONFIGS[2].replace(name="wan13b_sics", cluster="tiles",
                                       tile_shapes=SICS_MENU, n_clusters=352, rule="topk",
                                       density=0.15, aniso=True),
+    # the same with SICS's admission ticket: key tiles whose keys agree less
+    # (mean pairwise cosine below 0.72, about a third of them here) are ignored
+    "wan13b_sics_ticket": CONFIGS[2].replace(name="wan13b_sics_ticket", cluster="tiles",
+                                             tile_shapes=SICS_MENU, n_clusters=352, rule="topk",
+                                             density=0.15, aniso=True, sics_ticket=0.72),
 }
 
 
