@@ -27,9 +27,9 @@
 // 3 of the row index swapped), so W feeds the second product without any data
 // movement between lanes.
 //
-// One workgroup: 4 waves x 32 query blocks, a run of RJ KV blocks of one
-// (batch, head); K_j and V_j^T are staged in LDS once per KV block and shared
-// by the four waves.
+// One work item: 8 waves x 32 query blocks against one KV block j of one
+// (batch, head); K_j and V_j^T are staged in LDS once per item and shared by
+// the eight waves (see k_err for the persistent, double-buffered schedule).
 #include <math.h>
 
 #include "sa_internal.h"
@@ -39,33 +39,21 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kThreads = 256;
+constexpr int kWaves = 8;
+constexpr int kThreads = kWaves * 64;
 constexpr int kQPerWave = 32;
-constexpr int kQPerGroup = 4 * kQPerWave;
-constexpr int RJ = 4;                       // KV blocks per workgroup
+constexpr int kQPerGroup = kWaves * kQPerWave;   // query blocks per work item
 
-__device__ __forceinline__ uint16_t bf16_rne(float f) {
-    uint32_t u = __float_as_uint(f);
-    u += 0x7FFFu + ((u >> 16) & 1u);
-    return (uint16_t)(u >> 16);
-}
-
-__device__ __forceinline__ float bf16_val(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
-
-// Splits 8 fp32 values into bf16 hi and lo parts (x ~= hi + lo to 2^-16 relative).
+// Splits 8 finite fp32 values into bf16 hi and lo parts, both rounded to
+// nearest even (the conversion instruction): x ~= hi + lo to 2^-16 relative.
 __device__ __forceinline__ void split8(const float* x, bf16x8& hi, bf16x8& lo) {
-    uint32_t h[4], l[4];
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-        const uint16_t h0 = bf16_rne(x[2 * p]), h1 = bf16_rne(x[2 * p + 1]);
-        const uint16_t l0 = bf16_rne(x[2 * p] - bf16_val(h0));
-        const uint16_t l1 = bf16_rne(x[2 * p + 1] - bf16_val(h1));
-        h[p] = (uint32_t)h0 | ((uint32_t)h1 << 16);
-        l[p] = (uint32_t)l0 | ((uint32_t)l1 << 16);
+    for (int e = 0; e < 8; ++e) {
+        hi[e] = (__bf16)x[e];
+        lo[e] = (__bf16)(x[e] - (float)hi[e]);
     }
-    hi = __builtin_bit_cast(bf16x8, make_uint4(h[0], h[1], h[2], h[3]));
-    lo = __builtin_bit_cast(bf16x8, make_uint4(l[0], l[1], l[2], l[3]));
 }
 
 // K row order inside a 32-row tile: bits 2 and 3 of the row index swapped.
@@ -83,119 +71,211 @@ __device__ __forceinline__ float half_swap_sum(float x) {
 }
 
 template <int D, int BLK>
-__global__ __launch_bounds__(kThreads, 2) void k_err(const float* __restrict__ qm,
+struct ErrCfg {
+    static constexpr int KS = D / 16;            // channel steps of L^T
+    static constexpr int KT = BLK / 32;          // 32-key tiles
+    static constexpr int DT = D / 32;            // 32-channel tiles of A^T
+    static constexpr int KROW = D + 8;           // LDS row pitch of K (bf16)
+    static constexpr int VROW = BLK + 8;         // LDS row pitch of V^T (bf16)
+    static constexpr int K_ELEMS = BLK * KROW;
+    static constexpr int V_ELEMS = D * VROW;
+    static constexpr int KCH = BLK * (D / 8);    // 16-byte chunks of a K tile
+    static constexpr int VCH = D * (BLK / 8);    // and of a V^T tile
+    static constexpr int PK = KCH / kThreads;    // chunks per thread and tile
+    static constexpr int PV = VCH / kThreads;
+    // one stage: K tile, V^T tile (bf16) and the centroid values (fp32)
+    static constexpr int STAGE_BYTES = (K_ELEMS + V_ELEMS) * 2 + D * 4;
+    static constexpr int LDS_BYTES = 2 * STAGE_BYTES;
+    static_assert(PK * kThreads == KCH && PV * kThreads == VCH, "whole chunks per thread");
+    static_assert(STAGE_BYTES % 16 == 0, "16-byte aligned stages");
+};
+
+// Persistent grid over the work items (b*h, query group xg of 256 query
+// blocks, KV block j), item = ((bh * nxg) + xg) * nb + j; workgroup w takes a
+// contiguous range.  K_j and V_j^T of the next item are loaded into registers
+// while the current item is computed from LDS, and written to the other LDS
+// stage after it (one barrier per item), so each K/V tile is staged once for
+// all the query blocks of its head and its load overlaps the matrix work.
+template <int D, int BLK>
+__global__ __launch_bounds__(kThreads, 1) void k_err(const float* __restrict__ qm,
                                                     const uint16_t* __restrict__ K,
                                                     const uint16_t* __restrict__ Vt,
                                                     const float* __restrict__ v_sum,
                                                     const float* __restrict__ S,
                                                     float* __restrict__ keys, int N, int nb,
-                                                    float scale, const int32_t* __restrict__ order) {
-    constexpr int KS = D / 16;            // channel steps of L^T
-    constexpr int KT = BLK / 32;          // 32-key tiles
-    constexpr int DT = D / 32;            // 32-channel tiles of A^T
-    constexpr int KROW = D + 8;           // LDS row pitch of K (bf16)
-    constexpr int VROW = BLK + 8;         // LDS row pitch of V^T (bf16)
-    __shared__ uint16_t ks_lds[BLK * KROW];
-    __shared__ uint16_t vs_lds[D * VROW];
-    __shared__ float vbar[D];
-
+                                                    float scale, const int32_t* __restrict__ order,
+                                                    int64_t items, int nxg) {
+    using C = ErrCfg<D, BLK>;
+    extern __shared__ __attribute__((aligned(16))) unsigned char err_lds[];
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int col = lane & 31, h = lane >> 5;
-    const int64_t bh = blockIdx.z;
-    const int q = blockIdx.x * kQPerGroup + wave * kQPerWave + col;
-    const bool q_ok = q < nb;
-    const int j0 = blockIdx.y * RJ;
-    const int j1 = min(nb, j0 + RJ);
     const float c = scale * 1.44269504088896340736f;   // logits in log2 units
+    const int64_t beg = items * blockIdx.x / gridDim.x;
+    const int64_t end = items * (blockIdx.x + 1) / gridDim.x;
 
-    // query means as hi/lo bf16 B operands, held for the whole workgroup
-    bf16x8 qhi[KS], qlo[KS];
-    {
-        const float* qrow = qm + (bh * nb + (q_ok ? q : 0)) * (int64_t)D;
-#pragma unroll
-        for (int s = 0; s < KS; ++s) {
-            float x[8];
-            const float4 a = reinterpret_cast<const float4*>(qrow + s * 16 + 8 * h)[0];
-            const float4 b = reinterpret_cast<const float4*>(qrow + s * 16 + 8 * h)[1];
-            x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
-            x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
-            if (!q_ok) {
-#pragma unroll
-                for (int e = 0; e < 8; ++e) x[e] = 0.f;
-            }
-            split8(x, qhi[s], qlo[s]);
-        }
-    }
-
-    for (int j = j0; j < j1; ++j) {
+    auto k_tile = [&](int st) { return reinterpret_cast<uint16_t*>(err_lds + st * C::STAGE_BYTES); };
+    auto v_tile = [&](int st) { return k_tile(st) + C::K_ELEMS; };
+    auto vbar_of = [&](int st) {
+        return reinterpret_cast<float*>(err_lds + st * C::STAGE_BYTES + (C::K_ELEMS + C::V_ELEMS) * 2);
+    };
+    // staging registers of one item's tiles
+    u32x4 kreg[C::PK], vreg[C::PV];
+    float vb = 0.f;
+    auto load_k = [&](int64_t item) __attribute__((always_inline)) {
+        const int j = (int)(item % nb);
+        const int64_t bh = item / ((int64_t)nxg * nb);
         const int nj = min(BLK, N - j * BLK);
-        __syncthreads();   // the previous block's tiles are no longer read
-        {
-            // key r of block j: token j*BLK + r of the block order (through
-            // the token order when one is given)
-            const uint16_t* src = K + bh * N * (int64_t)D;
-            for (int p = tid; p < BLK * (D / 8); p += kThreads) {
-                const int r = p / (D / 8), ch = p % (D / 8);
-                uint4 v = make_uint4(0, 0, 0, 0);
-                if (r < nj) {
-                    const int t = order ? order[j * BLK + r] : j * BLK + r;
-                    v = *reinterpret_cast<const uint4*>(src + (int64_t)t * D + ch * 8);
-                }
-                *reinterpret_cast<uint4*>(&ks_lds[r * KROW + ch * 8]) = v;
+        // key r of block j: token j*BLK + r of the block order (through the
+        // token order when one is given); rows past the sequence are zero
+        const uint16_t* src = K + bh * N * (int64_t)D;
+#pragma unroll
+        for (int n = 0; n < C::PK; ++n) {
+            const int p = tid + n * kThreads;
+            const int r = p / (D / 8), ch = p % (D / 8);
+            u32x4 v = {0u, 0u, 0u, 0u};
+            if (r < nj) {
+                const int t = order ? order[j * BLK + r] : j * BLK + r;
+                v = *reinterpret_cast<const u32x4*>(src + (int64_t)t * D + ch * 8);
             }
-            const uint16_t* vsrc = Vt + (bh * nb + j) * (int64_t)D * BLK;
-            for (int p = tid; p < D * (BLK / 8); p += kThreads) {
-                const int d = p / (BLK / 8), kc = p % (BLK / 8);
-                *reinterpret_cast<uint4*>(&vs_lds[d * VROW + kc * 8]) =
-                    *reinterpret_cast<const uint4*>(vsrc + (int64_t)d * BLK + kc * 8);
-            }
-            for (int d = tid; d < D; d += kThreads)
-                vbar[d] = v_sum[(bh * nb + j) * (int64_t)D + d] / (float)nj;
+            kreg[n] = v;
         }
-        __syncthreads();
+    };
+    auto load_v = [&](int64_t item) __attribute__((always_inline)) {
+        const int j = (int)(item % nb);
+        const int64_t bh = item / ((int64_t)nxg * nb);
+        const int nj = min(BLK, N - j * BLK);
+        const uint16_t* vsrc = Vt + (bh * nb + j) * (int64_t)D * BLK;
+#pragma unroll
+        for (int n = 0; n < C::PV; ++n) {
+            const int p = tid + n * kThreads;
+            const int d = p / (BLK / 8), kc = p % (BLK / 8);
+            vreg[n] = *reinterpret_cast<const u32x4*>(vsrc + (int64_t)d * BLK + kc * 8);
+        }
+        // every thread loads a (clamped) channel; threads d < D keep theirs
+        vb = v_sum[(bh * nb + j) * (int64_t)D + (tid < D ? tid : 0)] / (float)nj;
+    };
+    auto store_k = [&](int st) __attribute__((always_inline)) {
+        uint16_t* kt = k_tile(st);
+#pragma unroll
+        for (int n = 0; n < C::PK; ++n) {
+            const int p = tid + n * kThreads;
+            const int r = p / (D / 8), ch = p % (D / 8);
+            *reinterpret_cast<u32x4*>(&kt[r * C::KROW + ch * 8]) = kreg[n];
+        }
+    };
+    auto store_v = [&](int st) __attribute__((always_inline)) {
+        uint16_t* vt = v_tile(st);
+#pragma unroll
+        for (int n = 0; n < C::PV; ++n) {
+            const int p = tid + n * kThreads;
+            const int d = p / (BLK / 8), kc = p % (BLK / 8);
+            *reinterpret_cast<u32x4*>(&vt[d * C::VROW + kc * 8]) = vreg[n];
+        }
+        if (tid < D) vbar_of(st)[tid] = vb;
+    };
+
+    if (beg < end) {
+        load_k(beg);
+        load_v(beg);
+        store_k(0);
+        store_v(0);
+    }
+    __syncthreads();
+
+    // query means as hi/lo bf16 B operands of the current (b*h, xg)
+    bf16x8 qhi[C::KS], qlo[C::KS];
+    int64_t cur_g = -1;
+    for (int64_t it = beg; it < end; ++it) {
+        const int st = (int)((it - beg) & 1);
+        const int j = (int)(it % nb);
+        const int64_t g = it / nb;                       // bh * nxg + xg
+        const int64_t bh = g / nxg;
+        const int q = (int)(g % nxg) * kQPerGroup + wave * kQPerWave + col;
+        const bool q_ok = q < nb;
+        // the next item's K and V^T are loaded during this item's score
+        // product and stored to the other stage (read by nobody since the last
+        // barrier) after it, before the value product needs the registers
+        const bool more = it + 1 < end;
+        if (more) {
+            load_k(it + 1);
+            load_v(it + 1);
+        }
+        if (g != cur_g) {
+            cur_g = g;
+            const float* qrow = qm + (bh * nb + (q_ok ? q : 0)) * (int64_t)D;
+#pragma unroll
+            for (int s2 = 0; s2 < C::KS; ++s2) {
+                float x[8];
+                const float4 a = reinterpret_cast<const float4*>(qrow + s2 * 16 + 8 * h)[0];
+                const float4 b = reinterpret_cast<const float4*>(qrow + s2 * 16 + 8 * h)[1];
+                x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+                x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+                if (!q_ok) {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) x[e] = 0.f;
+                }
+                split8(x, qhi[s2], qlo[s2]);
+            }
+        }
+        const int nj = min(BLK, N - j * BLK);
+        const uint16_t* ks_lds = k_tile(st);
+        const uint16_t* vs_lds = v_tile(st);
+        const float* vbar = vbar_of(st);
 
         // L^T = K_j qbar^T (raw dot products; the scale is applied in exp2)
-        f32x16 s[KT];
+        f32x16 s[C::KT];
 #pragma unroll
-        for (int kt = 0; kt < KT; ++kt) {
+        for (int kt = 0; kt < C::KT; ++kt) {
             s[kt] = f32x16{};
-            const uint16_t* krow = &ks_lds[(kt * 32 + swap23(col)) * KROW + 8 * h];
+            const uint16_t* krow = &ks_lds[(kt * 32 + swap23(col)) * C::KROW + 8 * h];
 #pragma unroll
-            for (int st = 0; st < KS; ++st) {
-                const bf16x8 a = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(krow + st * 16));
-                s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qhi[st], s[kt], 0, 0, 0);
-                s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qlo[st], s[kt], 0, 0, 0);
+            for (int st2 = 0; st2 < C::KS; ++st2) {
+                const bf16x8 a = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(krow + st2 * 16));
+                s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qhi[st2], s[kt], 0, 0, 0);
+                s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qlo[st2], s[kt], 0, 0, 0);
             }
         }
 
-        // keys past the end of the sequence take no part; max over the block
+        if (more) {
+            store_k(st ^ 1);
+            store_v(st ^ 1);
+        }
+
+        // keys past the end of the sequence take no part (a short last
+        // block only); max over the block
+        if (nj < BLK) {
+#pragma unroll
+            for (int kt = 0; kt < C::KT; ++kt) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int gg = r >> 2, e = r & 3;
+                    const int key = kt * 32 + 16 * (gg >> 1) + 8 * h + 4 * (gg & 1) + e;
+                    if (key >= nj) s[kt][r] = -__builtin_inff();
+                }
+            }
+        }
         float mx = -__builtin_inff();
 #pragma unroll
-        for (int kt = 0; kt < KT; ++kt) {
+        for (int kt = 0; kt < C::KT; ++kt) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int g = r >> 2, e = r & 3;
-                const int key = kt * 32 + 16 * (g >> 1) + 8 * h + 4 * (g & 1) + e;
-                if (key >= nj) s[kt][r] = -__builtin_inff();
-                mx = fmaxf(mx, s[kt][r]);
-            }
+            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kt][r]);
         }
         mx = half_swap_max(mx);
         const float nbase = -c * mx;
 #pragma unroll
-        for (int kt = 0; kt < KT; ++kt) {
+        for (int kt = 0; kt < C::KT; ++kt) {
 #pragma unroll
             for (int r = 0; r < 16; ++r)
                 s[kt][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kt][r], c, nbase));
         }
 
         // A^T = V_j^T W^T
-        f32x16 acc[DT];
+        f32x16 acc[C::DT];
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x16{};
+        for (int dt = 0; dt < C::DT; ++dt) acc[dt] = f32x16{};
 #pragma unroll
-        for (int kt = 0; kt < KT; ++kt) {
+        for (int kt = 0; kt < C::KT; ++kt) {
 #pragma unroll
             for (int s2 = 0; s2 < 2; ++s2) {
                 float w[8];
@@ -204,10 +284,10 @@ __global__ __launch_bounds__(kThreads, 2) void k_err(const float* __restrict__ q
                 bf16x8 whi, wlo;
                 split8(w, whi, wlo);
 #pragma unroll
-                for (int dt = 0; dt < DT; ++dt) {
+                for (int dt = 0; dt < C::DT; ++dt) {
                     const bf16x8 a = __builtin_bit_cast(
                         bf16x8, *reinterpret_cast<const uint4*>(
-                                    &vs_lds[(dt * 32 + col) * VROW + kt * 32 + 16 * s2 + 8 * h]));
+                                    &vs_lds[(dt * 32 + col) * C::VROW + kt * 32 + 16 * s2 + 8 * h]));
                     acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, whi, acc[dt], 0, 0, 0);
                     acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, wlo, acc[dt], 0, 0, 0);
                 }
@@ -219,7 +299,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_err(const float* __restrict__ q
         const float zhat = (float)nj * __builtin_amdgcn_exp2f(sij * 1.44269504088896340736f + nbase);
         float e2 = 0.f;
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
+        for (int dt = 0; dt < C::DT; ++dt) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int d = dt * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
@@ -230,16 +310,26 @@ __global__ __launch_bounds__(kThreads, 2) void k_err(const float* __restrict__ q
         e2 = half_swap_sum(e2);
         if (h == 0 && q_ok)
             keys[(bh * nb + q) * (int64_t)nb + j] = 0.5f * logf(e2) + scale * mx - logf((float)nj);
+
+        __syncthreads();
     }
 }
 
 template <int D, int BLK>
 sa_status launch_t(const Geometry& g, const float* qm, const uint16_t* K, const uint16_t* Vt,
                    const float* v_sum, const float* S, float* keys, hipStream_t stream) {
-    const dim3 grid((unsigned)ceil_div(g.nb, kQPerGroup), (unsigned)ceil_div(g.nb, RJ),
-                    (unsigned)g.BH());
-    hipLaunchKernelGGL((k_err<D, BLK>), grid, dim3(kThreads), 0, stream, qm, K, Vt, v_sum, S, keys,
-                       g.N, g.nb, g.scale, g.order);
+    using C = ErrCfg<D, BLK>;
+    const void* fn = (const void*)k_err<D, BLK>;
+    sa_status st = ensure_max_lds(fn, C::LDS_BYTES, "k_err");
+    if (st != SA_OK) return st;
+    int resident = 0;
+    if ((st = resident_workgroups(fn, kThreads, C::LDS_BYTES, &resident)) != SA_OK) return st;
+    const int nxg = (int)ceil_div(g.nb, kQPerGroup);
+    const int64_t items = g.BH() * nxg * (int64_t)g.nb;
+    const int64_t grid = items < resident ? items : resident;
+    if (grid <= 0) return SA_OK;
+    hipLaunchKernelGGL((k_err<D, BLK>), dim3((unsigned)grid), dim3(kThreads), C::LDS_BYTES, stream, qm,
+                       K, Vt, v_sum, S, keys, g.N, g.nb, g.scale, g.order, items, nxg);
     return hip_check(hipGetLastError(), "k_err launch");
 }
 
