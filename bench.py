@@ -137,7 +137,7 @@ def cpu_tiny_one_thread():
     import workloads as W
     from threadpoolctl import threadpool_limits
 
-    wl = W.CONFIGS[1]
+    wl = W.WORKLOADS[1]
     Q, K, V = W.make_qkv(wl)
     with threadpool_limits(limits=1):
         t0 = time.perf_counter()
@@ -231,7 +231,7 @@ def main():
         print(json.dumps({"calib_copy_bytes": n, "launches": 5}))
         return
 
-    wl = W.by_name(args.workload) if args.workload else W.CONFIGS[args.config]
+    wl = W.by_name(args.workload) if args.workload else W.WORKLOADS[args.config]
     log(f"[bench] workload {wl.name}: generating inputs")
     Q, K, V = W.make_qkv(wl)
 
@@ -364,8 +364,8 @@ def per_config_records(args, main_wl, main_res):
     import workloads as W
 
     recs = []
-    for c in sorted(W.CONFIGS):
-        wl = W.CONFIGS[c]
+    for c in sorted(W.WORKLOADS):
+        wl = W.WORKLOADS[c]
         if wl.name == main_wl.name:
             r = main_res
         else:
@@ -401,7 +401,7 @@ def bandwidth_legs():
     import block_sparse_attention_hilbert_amd as sa
     import workloads as W
 
-    wl = W.CONFIGS[2]
+    wl = W.WORKLOADS[2]
     prob = sa.problem_for(wl)
     dev = lambda x: torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).cuda()
     Q, K, V = W.make_qkv(wl)

@@ -419,7 +419,7 @@ def test_noalloc_select_rejects_beyond_its_scratch():
     selection that needs more (the 40-head 720p layer: ~78 MiB) is refused on
     the host, before any HIP call, with a message naming both sizes."""
     import workloads as W
-    wl = W.CONFIGS[3]
+    wl = W.WORKLOADS[3]
     prob = sa.problem_for(wl)
     spec = sa.spec_for(wl)
     need = sa.workspace_size(prob, spec)

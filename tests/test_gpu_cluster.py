@@ -47,7 +47,7 @@ def _pipe(wl, want_lse=True):
 
 
 # several clusters, ragged cluster sizes, both head dims and block sizes
-BASE = W.CONFIGS[2].replace(T=3, Hg=10, W=13, H=2)          # N = 390
+BASE = W.WORKLOADS[2].replace(T=3, Hg=10, W=13, H=2)          # N = 390
 SMALL = {
     "cocluster_mass_d128_b128": BASE.replace(cluster="cocluster", n_clusters=3, cluster_iters=2),
     "kmeans_topk_comp_d128_b64": BASE.replace(block=64, cluster="kmeans", n_clusters=6,
@@ -56,12 +56,12 @@ SMALL = {
     "cocluster_topk_comp_diag_d64_b64": BASE.replace(d=64, block=64, H=3, cluster="cocluster",
                                                      n_clusters=8, cluster_iters=4, rule="topk",
                                                      density=0.25, comp=True, diag=True),
-    "kmeans_mass_d64_b128_wide": W.CONFIGS[2].replace(T=5, Hg=9, W=29, H=2, d=64,
+    "kmeans_mass_d64_b128_wide": W.WORKLOADS[2].replace(T=5, Hg=9, W=29, H=2, d=64,
                                                       cluster="kmeans", n_clusters=10,
                                                       cluster_iters=2, mass=0.7),
     "kmeans_one_cluster": BASE.replace(block=64, cluster="kmeans", n_clusters=1,
                                        cluster_iters=1, rule="topk", density=0.5, comp=True),
-    "cocluster_iid_many": W.CONFIGS[1].replace(T=3, Hg=10, W=13, H=2, cluster="cocluster",
+    "cocluster_iid_many": W.WORKLOADS[1].replace(T=3, Hg=10, W=13, H=2, cluster="cocluster",
                                                n_clusters=40, cluster_iters=2, rule="mass",
                                                mass=0.8, diag=False, comp=True, topk=None),
     # SICS scheme generation over shaped tiles (SPADE parts 1-2), heads of
@@ -69,7 +69,7 @@ SMALL = {
     "tiles_topk_d128_b64": BASE.replace(H=4, block=64, cluster="tiles", aniso=True,
                                         tile_shapes=((1, 4, 16), (1, 8, 8), (2, 4, 8), (3, 2, 8)),
                                         n_clusters=12, rule="topk", density=0.3),
-    "tiles_mass_comp_diag_d64_b128": W.CONFIGS[2].replace(
+    "tiles_mass_comp_diag_d64_b128": W.WORKLOADS[2].replace(
         T=5, Hg=9, W=29, H=4, d=64, cluster="tiles", aniso=True,
         tile_shapes=((1, 4, 32), (1, 8, 16), (2, 4, 16), (5, 3, 8)), n_clusters=20,
         mass=0.8, comp=True, diag=True),
@@ -290,7 +290,7 @@ def test_counts_prepare_matches_fixed_layout():
     as fwd_prepare (with compensation), and counts below a block's extent mask
     exactly the keys past them (equal to attention on the shortened sequence)."""
     import block_sparse_attention_hilbert_amd as sa
-    wl = W.CONFIGS[2].replace(T=3, Hg=10, W=13, H=2, rule="topk", density=0.5, comp=True)
+    wl = W.WORKLOADS[2].replace(T=3, Hg=10, W=13, H=2, rule="topk", density=0.5, comp=True)
     prob = sa.problem_for(wl)
     Q, K, V = (to_dev(x) for x in W.make_qkv(wl))
     sel = sa.select(prob, sa.spec_for(wl), Q, K, V)

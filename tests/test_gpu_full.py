@@ -40,7 +40,7 @@ def _gpu():
 def test_full_workload(cfg):
     import block_sparse_attention_hilbert_amd as sa
     from block_sparse_attention_hilbert_amd.pipeline import BlockSparseAttention
-    wl = W.by_name(cfg) if isinstance(cfg, str) else W.CONFIGS[cfg]
+    wl = W.by_name(cfg) if isinstance(cfg, str) else W.WORKLOADS[cfg]
     log(f"[full] {wl.name}: B={wl.B} H={wl.H} N={wl.N} d={wl.d} block={wl.block} nb={wl.nb}")
     Q, K, V = W.make_qkv(wl, progress=None)
     log(f"[full] {wl.name}: inputs generated")

@@ -23,7 +23,7 @@ def _gpu():
     yield
 
 
-BASE = W.CONFIGS[2].replace(T=3, Hg=10, W=13, H=2)          # N = 390
+BASE = W.WORKLOADS[2].replace(T=3, Hg=10, W=13, H=2)          # N = 390
 CASES = {
     "fixed_mass_comp_b64": BASE.replace(block=64, comp=True),
     "fixed_hilbert_topk_b128": BASE.replace(hilbert=True, rule="topk", density=0.3),

@@ -43,31 +43,31 @@ def _pipeline(wl, want_scores=True, want_lse=True):
 
 # small workloads: several tiles and a ragged last block (390 = 3*128 + 6 = 6*64 + 6)
 SMALL = {
-    "mass_d128_b128": W.CONFIGS[2].replace(T=3, Hg=10, W=13, H=3),
-    "topk_d128_b128": W.CONFIGS[3].replace(T=3, Hg=10, W=13, H=4),
-    "topk_diag_d64_b64": W.CONFIGS[1].replace(T=3, Hg=10, W=13, H=2),
-    "window_anchor_d128_b128": W.CONFIGS[4].replace(T=6, Hg=10, W=13, H=2),
-    "hilbert_comp_d128_b64": W.CONFIGS[5].replace(T=3, Hg=10, W=13, H=3),
-    "mass_sub32_d64_b128": W.CONFIGS[2].replace(T=3, Hg=10, W=13, H=2, d=64, sub_block=32),
-    "mass_comp_d64_b128": W.CONFIGS[2].replace(T=5, Hg=7, W=11, H=2, d=64, comp=True, mass=0.5),
-    "topk_d128_b64_wide": W.CONFIGS[3].replace(T=5, Hg=9, W=29, H=2, block=64, density=0.3),
+    "mass_d128_b128": W.WORKLOADS[2].replace(T=3, Hg=10, W=13, H=3),
+    "topk_d128_b128": W.WORKLOADS[3].replace(T=3, Hg=10, W=13, H=4),
+    "topk_diag_d64_b64": W.WORKLOADS[1].replace(T=3, Hg=10, W=13, H=2),
+    "window_anchor_d128_b128": W.WORKLOADS[4].replace(T=6, Hg=10, W=13, H=2),
+    "hilbert_comp_d128_b64": W.WORKLOADS[5].replace(T=3, Hg=10, W=13, H=3),
+    "mass_sub32_d64_b128": W.WORKLOADS[2].replace(T=3, Hg=10, W=13, H=2, d=64, sub_block=32),
+    "mass_comp_d64_b128": W.WORKLOADS[2].replace(T=5, Hg=7, W=11, H=2, d=64, comp=True, mass=0.5),
+    "topk_d128_b64_wide": W.WORKLOADS[3].replace(T=5, Hg=9, W=29, H=2, block=64, density=0.3),
     # more heads than the per-head budgets passed inline with the launch
-    "topk_70heads_d64_b64": W.CONFIGS[5].replace(T=2, Hg=8, W=9, H=70, d=64, hilbert=False,
+    "topk_70heads_d64_b64": W.WORKLOADS[5].replace(T=2, Hg=8, W=9, H=70, d=64, hilbert=False,
                                                  comp=False, sub_block=0),
     # error-aware routing (keys ranked top-k, compensation on)
-    "err_d128_b128": W.CONFIGS[2].replace(T=3, Hg=10, W=13, H=3, rule="err", density=0.2,
+    "err_d128_b128": W.WORKLOADS[2].replace(T=3, Hg=10, W=13, H=3, rule="err", density=0.2,
                                           comp=True),
-    "err_hilbert_d128_b64": W.CONFIGS[5].replace(T=3, Hg=10, W=13, H=3, rule="err",
+    "err_hilbert_d128_b64": W.WORKLOADS[5].replace(T=3, Hg=10, W=13, H=3, rule="err",
                                                  sub_block=0),
-    "err_d64_b64_wide": W.CONFIGS[3].replace(T=5, Hg=9, W=29, H=2, d=64, block=64, rule="err",
+    "err_d64_b64_wide": W.WORKLOADS[3].replace(T=5, Hg=9, W=29, H=2, d=64, block=64, rule="err",
                                              density=0.3, comp=True),
-    "err_d64_b128_diag": W.CONFIGS[1].replace(T=3, Hg=10, W=13, H=2, block=128, rule="err",
+    "err_d64_b128_diag": W.WORKLOADS[1].replace(T=3, Hg=10, W=13, H=2, block=128, rule="err",
                                               comp=True, diag=True),
     # batches of two: every kernel indexes (batch, head) pairs
-    "mass_batch2": W.CONFIGS[2].replace(B=2, T=3, Hg=10, W=13, H=2),
-    "hilbert_comp_batch2": W.CONFIGS[5].replace(B=2, T=3, Hg=10, W=13, H=3),
-    "window_anchor_batch2": W.CONFIGS[4].replace(B=2, T=6, Hg=10, W=13, H=2),
-    "err_batch2": W.CONFIGS[2].replace(B=2, T=3, Hg=10, W=13, H=2, rule="err", density=0.3,
+    "mass_batch2": W.WORKLOADS[2].replace(B=2, T=3, Hg=10, W=13, H=2),
+    "hilbert_comp_batch2": W.WORKLOADS[5].replace(B=2, T=3, Hg=10, W=13, H=3),
+    "window_anchor_batch2": W.WORKLOADS[4].replace(B=2, T=6, Hg=10, W=13, H=2),
+    "err_batch2": W.WORKLOADS[2].replace(B=2, T=3, Hg=10, W=13, H=2, rule="err", density=0.3,
                                        comp=True),
 }
 
@@ -134,7 +134,7 @@ def test_small_workload_parity(name):
 
 def test_hilbert_permute_kernels():
     sa = _sa()
-    wl = W.CONFIGS[5].replace(H=2)
+    wl = W.WORKLOADS[5].replace(H=2)
     prob = sa.problem_for(wl)
     perm, _ = sa.hilbert_perm_build(wl.T, wl.Hg, wl.W)
     rng = np.random.default_rng(0)
@@ -150,13 +150,13 @@ def test_hilbert_permute_kernels():
 def test_edge_single_token_and_empty_rows():
     sa = _sa()
     # N = 1: one block of one token; attention to itself is exactly v
-    wl = W.CONFIGS[1].replace(T=1, Hg=1, W=1, H=1, rule="topk", topk=1, diag=False)
+    wl = W.WORKLOADS[1].replace(T=1, Hg=1, W=1, H=1, rule="topk", topk=1, diag=False)
     Q, K, V = W.make_qkv(wl)
     O = _pipeline(wl)(to_dev(Q), to_dev(K), to_dev(V))
     torch.cuda.synchronize()
     assert np.array_equal(from_dev(O), V)
     # structural rule with no structure: every row empty -> O = 0, lse = -inf
-    wl = W.CONFIGS[4].replace(T=2, Hg=8, W=8, H=2, window_frames=-1, n_anchors=0)
+    wl = W.WORKLOADS[4].replace(T=2, Hg=8, W=8, H=2, window_frames=-1, n_anchors=0)
     Q, K, V = W.make_qkv(wl)
     pipe = _pipeline(wl)
     O = pipe(to_dev(Q), to_dev(K), to_dev(V))
@@ -199,7 +199,7 @@ def test_edge_compensation_limits():
 
 def test_largest_sort_length():
     """nb = 4096 (the largest scored row) with the mass rule and sub-blocks."""
-    wl = W.CONFIGS[2].replace(T=64, Hg=64, W=64, H=1, block=64, d=64, sub_block=32, mass=0.5)
+    wl = W.WORKLOADS[2].replace(T=64, Hg=64, W=64, H=1, block=64, d=64, sub_block=32, mass=0.5)
     assert wl.nb == 4096
     Q, K, V = W.make_qkv(wl)
     case = OracleCase(wl, Q, K, V)
@@ -296,7 +296,7 @@ def test_largest_attention_window():
     (LVSA abstract: a temporal window) so that the oracle stays cheap: every
     row keeps the blocks of its own latent frame(s).  Every output row written;
     every 8th query block (and the first and last) against the oracle."""
-    wl = W.CONFIGS[4].replace(T=128, Hg=64, W=64, H=1, gen="iid", window_frames=0, n_anchors=0)
+    wl = W.WORKLOADS[4].replace(T=128, Hg=64, W=64, H=1, gen="iid", window_frames=0, n_anchors=0)
     assert wl.nb == 4096 and wl.d == 128 and wl.block == 128
     Q, K, V = W.make_qkv(wl)
     case = OracleCase(wl, Q, K, V)

@@ -184,7 +184,7 @@ def test_kept_flops_counts_true_block_sizes():
 
 
 def test_pipeline_on_tiny_workload_runs():
-    wl = W.CONFIGS[1]
+    wl = W.WORKLOADS[1]
     Q, K, V = W.make_qkv(wl)
     keep, S = oracle.select_workload(wl, Q, K)
     assert keep.shape == (1, 2, 4, 4)

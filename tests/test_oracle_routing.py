@@ -98,7 +98,7 @@ def test_constant_key_block_has_no_error():
 def test_routing_by_error_beats_routing_by_score():
     """SVG-EAR 2B / 4: at equal density, compensated attention with blocks kept
     by error is closer to dense attention than with blocks kept by score."""
-    wl = W.CONFIGS[2].replace(T=3, Hg=10, W=26, H=4, block=64, rule="topk", density=0.2)
+    wl = W.WORKLOADS[2].replace(T=3, Hg=10, W=26, H=4, block=64, rule="topk", density=0.2)
     Q, K, V = W.make_qkv(wl)
     n_better = 0
     for h in range(wl.H):

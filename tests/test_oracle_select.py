@@ -186,7 +186,7 @@ def test_csr_round_trip_and_ascending():
 
 def test_tiny_selection_keeps_topk_union_diagonal():
     import workloads as W
-    wl = W.CONFIGS[1]
+    wl = W.WORKLOADS[1]
     Q, K, V = W.make_qkv(wl)
     keep, S = oracle.select_workload(wl, Q, K)
     for h in range(wl.H):

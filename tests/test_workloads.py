@@ -21,7 +21,7 @@ def test_bf16_rounding_matches_torch():
 
 def test_geometry_matches_golden():
     rows = {r[0]: r for r in golden("block_geometry.txt")}
-    for wl in W.CONFIGS.values():
+    for wl in W.WORKLOADS.values():
         r = rows[wl.name]
         assert (wl.T, wl.Hg, wl.W, wl.block) == tuple(int(x) for x in r[1:5])
         assert wl.N == int(r[5]) and wl.nb == int(r[6])
@@ -31,7 +31,7 @@ def test_geometry_matches_golden():
 
 
 def test_generator_is_deterministic_and_per_head():
-    wl = W.CONFIGS[2].replace(T=3, Hg=6, W=10, H=3)
+    wl = W.WORKLOADS[2].replace(T=3, Hg=6, W=10, H=3)
     Q1, K1, V1 = W.make_qkv(wl)
     Q2, K2, V2 = W.make_qkv(wl, heads=[2])
     assert np.array_equal(Q1[:, 2:3], Q2) and np.array_equal(V1[:, 2:3], V2)
@@ -41,7 +41,7 @@ def test_generator_is_deterministic_and_per_head():
 
 
 def test_smooth_field_statistics():
-    wl = W.CONFIGS[2].replace(H=1)
+    wl = W.WORKLOADS[2].replace(H=1)
     Q, K, V = W.make_qkv(wl)
     q = W.bf16_bits_to_f32(Q[0, 0]).astype(np.float64)
     k = W.bf16_bits_to_f32(K[0, 0]).astype(np.float64)
@@ -75,11 +75,11 @@ def test_smooth_field_is_the_cosine_sum():
 def test_head_density_profile_range():
     rho = W.head_density_profile(12, 5)
     assert rho.dtype == np.float32 and np.all(rho >= 0.05) and np.all(rho <= 0.5)
-    assert np.array_equal(rho, W.CONFIGS[5].densities())
+    assert np.array_equal(rho, W.WORKLOADS[5].densities())
 
 
 def test_step_inputs_start_at_the_workload_and_drift():
-    wl = W.CONFIGS[1]
+    wl = W.WORKLOADS[1]
     steps = W.make_step_qkv(wl, 3, drift=0.1)
     Q, K, V = W.make_qkv(wl)
     assert all(np.array_equal(a, b) for a, b in zip(steps[0], (Q, K, V)))

@@ -43,7 +43,7 @@ def test_noalloc_select_equals_workspace_select(first, second):
     dev = torch.device("cuda:0")
     # the 64-token Hilbert workload at full size (sub-block scores, per-head
     # budgets, compensation statistics), then a smaller 1.3B-shaped layer
-    cases = [W.CONFIGS[first], W.CONFIGS[second].replace(T=7, Hg=10, W=13)]
+    cases = [W.WORKLOADS[first], W.WORKLOADS[second].replace(T=7, Hg=10, W=13)]
     for n, wl in enumerate(cases):
         prob, spec = sa.problem_for(wl), sa.spec_for(wl)
         Q, K, V = (to_dev(x) for x in W.make_qkv(wl))

@@ -120,7 +120,7 @@ class Workload:
         return dataclasses.replace(self, **kw)
 
 
-CONFIGS = {
+WORKLOADS = {
     1: Workload("tiny", 1, 2, 64, 4, 8, 8, 64, rule="topk", topk=2, diag=True,
                 gen="iid", seed=1),
     2: Workload("wan13b", 1, 12, 128, 21, 30, 52, 128, rule="mass", mass=0.9,
@@ -154,20 +154,20 @@ CONFIGS = {
 SICS_MENU = ((1, 4, 32), (1, 8, 16), (2, 4, 16), (2, 8, 8), (4, 4, 8), (8, 4, 4))
 
 EXTRA = {
-    "wan13b_err": CONFIGS[2].replace(name="wan13b_err", rule="err", density=0.2, comp=True),
-    "wan13b_topk_comp": CONFIGS[2].replace(name="wan13b_topk_comp", rule="topk", density=0.2,
+    "wan13b_err": WORKLOADS[2].replace(name="wan13b_err", rule="err", density=0.2, comp=True),
+    "wan13b_topk_comp": WORKLOADS[2].replace(name="wan13b_topk_comp", rule="topk", density=0.2,
                                            comp=True),
-    "wan13b_cocluster": CONFIGS[2].replace(name="wan13b_cocluster", cluster="cocluster",
+    "wan13b_cocluster": WORKLOADS[2].replace(name="wan13b_cocluster", cluster="cocluster",
                                            n_clusters=64, cluster_iters=3),
-    "wan13b_kmeans_comp": CONFIGS[2].replace(name="wan13b_kmeans_comp", cluster="kmeans",
+    "wan13b_kmeans_comp": WORKLOADS[2].replace(name="wan13b_kmeans_comp", cluster="kmeans",
                                              n_clusters=64, cluster_iters=3, rule="topk",
                                              density=0.2, comp=True),
-    "wan13b_sics": CONFIGS[2].replace(name="wan13b_sics", cluster="tiles",
+    "wan13b_sics": WORKLOADS[2].replace(name="wan13b_sics", cluster="tiles",
                                       tile_shapes=SICS_MENU, n_clusters=352, rule="topk",
                                       density=0.15, aniso=True),
     # the same with SICS's admission ticket: key tiles whose keys agree less
     # (mean pairwise cosine below 0.72, about a third of them here) are ignored
-    "wan13b_sics_ticket": CONFIGS[2].replace(name="wan13b_sics_ticket", cluster="tiles",
+    "wan13b_sics_ticket": WORKLOADS[2].replace(name="wan13b_sics_ticket", cluster="tiles",
                                              tile_shapes=SICS_MENU, n_clusters=352, rule="topk",
                                              density=0.15, aniso=True, sics_ticket=0.72),
 }
@@ -175,7 +175,7 @@ EXTRA = {
 
 def by_name(name: str) -> Workload:
     """Workload of the table above or of EXTRA by its name."""
-    for wl in list(CONFIGS.values()) + list(EXTRA.values()):
+    for wl in list(WORKLOADS.values()) + list(EXTRA.values()):
         if wl.name == name:
             return wl
     raise KeyError(name)
