@@ -96,3 +96,74 @@ def test_full_workload(cfg):
     log(f"[full] {wl.name}: attention on {n} query blocks max={emax:.2e} mean={emean:.2e} "
         f"lse={lmax:.2e}")
     assert emax <= ATOL_MAX and emean <= ATOL_MEAN and lmax <= LSE_ATOL
+
+
+@pytest.mark.parametrize("cfg", [2, 5])
+def test_full_size_runs_are_bitwise_identical(cfg):
+    """Two calls on the same inputs give the same bits: the persistent
+    scheduler hands rows to workgroups in a different order on every launch,
+    but each row is computed by one workgroup in a fixed order, so neither the
+    keep lists nor O nor lse may change."""
+    import block_sparse_attention_hilbert_amd as sa
+    from block_sparse_attention_hilbert_amd.pipeline import BlockSparseAttention
+    wl = W.WORKLOADS[cfg]
+    log(f"[full-det] {wl.name}: N={wl.N} H={wl.H}")
+    Q, K, V = W.make_qkv(wl, progress=None)
+    off = W.anchor_offset(wl.seed, 0, wl.nb)
+    pipe = BlockSparseAttention(sa.problem_for(wl), sa.spec_for(wl), hilbert=wl.hilbert,
+                                want_lse=True)
+    Qd, Kd, Vd = to_dev(Q), to_dev(K), to_dev(V)
+    runs = []
+    for _ in range(2):
+        poison(pipe.O, pipe.lse)
+        O = pipe(Qd, Kd, Vd, anchor_offset=off)
+        torch.cuda.synchronize()
+        runs.append((from_dev(O).copy(), pipe.lse.cpu().numpy().view(np.uint32).copy(),
+                     pipe.sel.row_ptr.cpu().numpy().copy(), pipe.sel.col_idx.cpu().numpy().copy()))
+    (o1, l1, r1, c1), (o2, l2, r2, c2) = runs
+    assert np.array_equal(r1, r2)
+    assert np.array_equal(c1[: r1[-1]], c2[: r2[-1]])
+    assert np.array_equal(o1, o2), "O differs between two identical calls"
+    assert np.array_equal(l1, l2), "lse differs between two identical calls"
+    log(f"[full-det] {wl.name}: identical")
+
+
+def test_concurrent_host_threads_on_separate_streams():
+    """Two host threads drive their own pipelines on their own streams at the
+    same time (the library's per-device launch memo is shared); each result
+    equals the same call made alone."""
+    import threading
+    import block_sparse_attention_hilbert_amd as sa
+    from block_sparse_attention_hilbert_amd.pipeline import BlockSparseAttention
+    wls = [W.WORKLOADS[2].replace(T=6, H=4), W.WORKLOADS[5].replace(T=6, H=4)]
+    inputs = [tuple(to_dev(x) for x in W.make_qkv(wl, progress=None)) for wl in wls]
+    ref = []
+    for wl, (Qd, Kd, Vd) in zip(wls, inputs):
+        pipe = BlockSparseAttention(sa.problem_for(wl), sa.spec_for(wl), hilbert=wl.hilbert)
+        ref.append(from_dev(pipe(Qd, Kd, Vd, anchor_offset=W.anchor_offset(wl.seed, 0, wl.nb))).copy())
+    torch.cuda.synchronize()
+    out = [None, None]
+    errors = []
+
+    def work(k):
+        try:
+            wl = wls[k]
+            stream = torch.cuda.Stream()
+            with torch.cuda.stream(stream):
+                pipe = BlockSparseAttention(sa.problem_for(wl), sa.spec_for(wl), hilbert=wl.hilbert)
+                res = None
+                for _ in range(5):
+                    res = pipe(*inputs[k], anchor_offset=W.anchor_offset(wl.seed, 0, wl.nb))
+                stream.synchronize()
+                out[k] = from_dev(res).copy()
+        except Exception as e:                      # reported on the main thread
+            errors.append(e)
+
+    threads = [threading.Thread(target=work, args=(k,)) for k in range(2)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join(timeout=120)
+    assert not errors, errors
+    for k in range(2):
+        assert out[k] is not None and np.array_equal(out[k], ref[k]), wls[k].name
