@@ -259,7 +259,7 @@ __device__ __forceinline__ void process_row(const FwdArgs& a, int64_t row, unsig
     // block order is token qtok of the caller's order
     bf16x8 qf[D / 16];
     const int qn = i * BLK + qg * 32 + r32;
-    const int qtok = qn < a.N ? (a.order ? a.order[qn] : qn) : 0;
+    const int qtok = qn < a.N ? (a.order ? clamp_token(a.order[qn], a.N) : qn) : 0;
 #pragma unroll
     for (int st = 0; st < D / 16; ++st) {
         uint4 v = make_uint4(0, 0, 0, 0);
@@ -762,7 +762,7 @@ __global__ __launch_bounds__(256) void k_vt_prep(const uint16_t* __restrict__ V,
 #pragma unroll
         for (int r = 0; r < 8; ++r) {
             const int key = kc * 8 + r;
-            tok[r] = key < n ? (order ? order[j * BLK + key] : j * BLK + key) : -1;
+            tok[r] = key < n ? (order ? clamp_token(order[j * BLK + key], N) : j * BLK + key) : -1;
         }
         uint32_t w[8][4];
 #pragma unroll

@@ -25,8 +25,7 @@ __global__ __launch_bounds__(kThreads) void k_permute(const uint4* __restrict__ 
         const int64_t t = e / CH;
         const int n = (int)(t % N);
         const int64_t bh = t / N;
-        const int p = perm[n];
-        if ((unsigned)p >= (unsigned)N) continue;
+        const int p = clamp_token(perm[n], N);
         const int64_t from = inverse ? n : p;
         const int64_t to = inverse ? p : n;
         dst[(bh * N + to) * CH + c] = src[(bh * N + from) * CH + c];

@@ -135,7 +135,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_err(const float* __restrict__ q
             const int r = p / (D / 8), ch = p % (D / 8);
             u32x4 v = {0u, 0u, 0u, 0u};
             if (r < nj) {
-                const int t = order ? order[j * BLK + r] : j * BLK + r;
+                const int t = order ? clamp_token(order[j * BLK + r], N) : j * BLK + r;
                 v = *reinterpret_cast<const u32x4*>(src + (int64_t)t * D + ch * 8);
             }
             kreg[n] = v;

@@ -77,7 +77,7 @@ __global__ __launch_bounds__(kThreads) void k_pool(PoolArgs a) {
 #pragma unroll
     for (int r = 0; r < SEGR; ++r) {
         const int row = sgi * SEGR + r;
-        tok[r] = row < n ? (a.order ? a.order[row0 + row] : row0 + row) : -1;
+        tok[r] = row < n ? (a.order ? clamp_token(a.order[row0 + row], a.N) : row0 + row) : -1;
     }
     uint4 v[SEGR];
 #pragma unroll

@@ -21,6 +21,11 @@ void clear_error();
 
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// A token index read from a caller's token order, clamped into [0, n): an
+// order that is not a permutation gives wrong rows, never an access outside
+// the tensors.
+__host__ __device__ inline int clamp_token(int t, int n) { return t < 0 ? 0 : (t >= n ? n - 1 : t); }
+
 // Launch set-up kept per device, safe to call from several host threads:
 // raises a kernel's dynamic-LDS limit to at least `bytes` on the current
 // device (one HIP call per kernel and device, repeated only for a larger

@@ -39,11 +39,14 @@
  *     N - (nb-1)*block tokens.
  *   - Ownership: the caller allocates and frees every buffer (device memory
  *     for tensors, masks and workspace; host memory for host arrays).  The
- *     library allocates no memory and never synchronises the stream.  Its
- *     only state between calls is host-side launch set-up, kept per device
+ *     library allocates no memory and never synchronises the stream; the
+ *     one exception is the fixed scratch array of sparse_attn_select_noalloc,
+ *     a static device array reserved when the library is loaded on a GPU.
+ *     Its only host state between calls is launch set-up, kept per device
  *     behind a mutex (safe from several host threads): a kernel's LDS limit
- *     raised once per device and the number of workgroups a device holds
- *     at once, queried once per kernel, device and size.
+ *     raised once per device, the number of workgroups a device holds at
+ *     once (queried once per kernel, device and size), and the device
+ *     address of that scratch array.
  *   - Ordering: device work is enqueued on `stream` (a hipStream_t; NULL is
  *     the default stream) and is asynchronous.  A workspace carries one
  *     call's intermediate state on the device (pooled means, scores, the
@@ -96,7 +99,11 @@ typedef struct {
                              block order, gathered by sparse_attn_fwd_run);
                              the other calls reject it (SA_ERR_UNSUPPORTED), as
                              does a latent-frame window (frames are runs of
-                             raster blocks).  Not checked to be a permutation. */
+                             raster blocks).  Not checked to be a permutation:
+                             every entry is clamped into [0, N), so a sequence
+                             that is not one gives wrong rows, never an access
+                             outside the tensors (the same holds for the perm
+                             of hilbert_permute / hilbert_unpermute).          */
 } sa_problem;
 
 enum {

@@ -362,3 +362,32 @@ def test_malformed_csr_is_contained():
     O_ref, _ = case.attention(0, 0, q_blocks=[1])
     e = np.abs(oracle.bf16_to_f64(Og[0, 0, bounds[1]:bounds[2]]) - O_ref[bounds[1]:bounds[2]])
     assert e.max() <= ATOL_MAX
+
+
+def test_token_order_out_of_range_is_contained():
+    """A token order with entries outside [0, N): every gathered index is
+    clamped into range, so the selection and the attention (with
+    compensation) end normally and every row the clamped order names is
+    written; rows it never names are left as they were."""
+    import dataclasses
+    sa = _sa()
+    wl = SMALL["hilbert_comp_d128_b64"].replace(hilbert=False)
+    N = wl.N
+    order = np.arange(N, dtype=np.int32)
+    order[[5, 77]] = [N + 1000, -3]                  # tokens 5 and 77 are never named
+    clamped = np.clip(order, 0, N - 1)
+    prob = dataclasses.replace(sa.problem_for(wl), token_order=torch.from_numpy(order).cuda())
+    Q, K, V = (to_dev(x) for x in W.make_qkv(wl))
+    spec = sa.spec_for(wl)
+    sel = sa.select(prob, spec, Q, K, V)
+    O = torch.empty_like(Q)
+    poison(O)
+    out, lse = sa.fwd(prob, Q, K, V, sel.row_ptr, sel.col_idx, O=O, want_lse=True,
+                      k_mean=sel.k_mean, v_sum=sel.v_sum)
+    torch.cuda.synchronize()
+    Og = from_dev(out)
+    named = np.zeros(N, dtype=bool)
+    named[clamped] = True
+    nan_rows = np.any((Og & 0x7F80) == 0x7F80, axis=-1)      # [B, H, N]
+    assert not np.any(nan_rows[..., named]), "a named row was not written"
+    assert np.all(~named[[5, 77]])
