@@ -83,7 +83,7 @@ def read_traffic(workload: str):
         return None
 
 
-def cpu_baseline(wl, Q, K, V, budget_s: float = 40.0):
+def cpu_baseline(wl, Q, K, V, budget_s: float = 40.0, tiny: bool = True):
     """The oracle (as it stands) on the workload: heads 0, 1, ... in turn,
     each one's full selection and float64 attention of all its query blocks,
     until done or the time budget is spent (the head in progress when it runs
@@ -126,7 +126,8 @@ def cpu_baseline(wl, Q, K, V, budget_s: float = 40.0):
                       f"{blocks} query blocks ({dt:.1f} s wall)" if whole else
                       f"{heads} of {wl.H} heads of batch 0: selection + float64 attention of "
                       f"{blocks} query blocks ({dt:.1f} s wall)")}
-    out["tiny_one_thread"] = cpu_tiny_one_thread()
+    if tiny:
+        out["tiny_one_thread"] = cpu_tiny_one_thread()
     return out
 
 
@@ -200,6 +201,8 @@ def main():
                     help="mask reuse: select on every r-th call only, the calls in between "
                          "keep the mask (compensation centroids still from their own K, V)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget-per-workload", type=float, default=5.0,
+                    help="seconds of oracle work per non-headline workload record")
     ap.add_argument("--cpu-budget", type=float, default=40.0,
                     help="seconds the CPU oracle baseline may take")
     ap.add_argument("--no-extra", action="store_true",
@@ -358,25 +361,35 @@ def time_calls(wl, Qd, Kd, Vd, steps, warmup, refresh_every=1, flush_bytes=0):
 
 
 def per_config_records(args, main_wl, main_res):
-    """One record per workload of the table (GPU timings only; inputs made and
-    freed one workload at a time)."""
+    """One record per workload of the table, plus the reported-only LVSA point
+    at a ±4-frame window (the structure closest to the page's ~8 % density):
+    GPU timings and, unless the CPU baseline is off, the oracle's rate on a
+    bounded sample of the same workload (inputs made and freed one workload at
+    a time)."""
     import torch
     import workloads as W
 
     recs = []
-    for c in sorted(W.WORKLOADS):
-        wl = W.WORKLOADS[c]
+    table = [(c, W.WORKLOADS[c]) for c in sorted(W.WORKLOADS)] + [(None, W.by_name("lvsa_6x_r4"))]
+    for c, wl in table:
+        Q, K, V = W.make_qkv(wl)
         if wl.name == main_wl.name:
             r = main_res
         else:
-            Q, K, V = W.make_qkv(wl)
             dev = lambda x: torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).cuda()
             Qd, Kd, Vd = dev(Q), dev(K), dev(V)
             r = time_calls(wl, Qd, Kd, Vd, 10, 2)
-            del Qd, Kd, Vd, Q, K, V
+            del Qd, Kd, Vd
             torch.cuda.empty_cache()
+        cpu = None
+        if not args.no_cpu_baseline and wl.name != main_wl.name:
+            # the headline workload's oracle runs whole in cpu_baseline
+            log(f"[bench] oracle sample: {wl.name}")
+            b = cpu_baseline(wl, Q, K, V, budget_s=args.cpu_budget_per_workload, tiny=False)
+            cpu = {k: b[k] for k in ("value", "unit", "cores", "wall_s", "whole_workload", "sample")}
+        del Q, K, V
         att = r["F_kept"] / (r["fwd_ms"] / 1e3) / 1e12
-        recs.append({"config": c, "workload": wl.name, "B": wl.B, "H": wl.H, "N": wl.N,
+        rec = {"config": c, "workload": wl.name, "B": wl.B, "H": wl.H, "N": wl.N,
                      "block": wl.block, "rule": wl.rule,
                      "density_kept": round(float(r["keep"].mean()), 4),
                      "ms_per_call": round(r["step_s"] * 1e3, 4),
@@ -386,7 +399,12 @@ def per_config_records(args, main_wl, main_res):
                      "kept_tflop_per_call": round(r["F_kept"] / 1e12, 4),
                      "tflops_call": round(r["F_kept"] / r["step_s"] / 1e12, 2),
                      "tflops_attention": round(att, 2),
-                     "frac": round(att / PEAK_BF16_TFLOPS, 4)})
+                     "frac": round(att / PEAK_BF16_TFLOPS, 4)}
+        if c is None:
+            rec["reported_only"] = "window ±4 latent frames + 4 anchors (the ±1-frame table entry keeps 2.7 %)"
+        if cpu is not None:
+            rec["cpu_oracle"] = cpu
+        recs.append(rec)
     return recs
 
 

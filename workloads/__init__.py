@@ -165,6 +165,9 @@ EXTRA = {
     "wan13b_sics": WORKLOADS[2].replace(name="wan13b_sics", cluster="tiles",
                                       tile_shapes=SICS_MENU, n_clusters=352, rule="topk",
                                       density=0.15, aniso=True),
+    # LVSA's structure at a ±4-frame window: the density closest to the page's
+    # ~8 % (reported beside the ±1-frame table entry, not a parity case)
+    "lvsa_6x_r4": WORKLOADS[4].replace(name="lvsa_6x_r4", window_frames=4),
     # the same with SICS's admission ticket: key tiles whose keys agree less
     # (mean pairwise cosine below 0.72, about a third of them here) are ignored
     "wan13b_sics_ticket": WORKLOADS[2].replace(name="wan13b_sics_ticket", cluster="tiles",
