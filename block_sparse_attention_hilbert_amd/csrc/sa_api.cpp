@@ -447,6 +447,8 @@ static sa_status check_cluster(const Geometry& g, const sa_cluster_spec* cs) {
                         cs->n_clusters, mt);
         if (cs->tile_coherence && !(cs->ticket >= -1.f && cs->ticket <= 1.f))
             return fail(SA_ERR_INVALID_ARG, "ticket = %g must be in [-1, 1]", (double)cs->ticket);
+        if (((uintptr_t)cs->tile_coherence & 7u) != 0 || ((uintptr_t)cs->shape_idx & 3u) != 0)
+            return fail(SA_ERR_INVALID_ARG, "tile_coherence must be 8-byte and shape_idx 4-byte aligned");
     } else {
         const int cmax = g.N < 1024 ? g.N : 1024;
         if (cs->n_clusters < 1 || cs->n_clusters > cmax)

@@ -238,6 +238,9 @@ def test_sics_ticket_validation():
     for t in (-1.0, 0.0, 0.72, 1.0):
         raw.ticket = t
         assert size(ctypes.byref(small.c()), ctypes.byref(raw), None, None, None) == sa.SA_OK, t
+    raw.tile_coherence = (1 << 20) + 4                # not 8-byte aligned
+    assert size(ctypes.byref(small.c()), ctypes.byref(raw), None, None, None) == sa.SA_ERR_INVALID_ARG
+    raw.tile_coherence = 1 << 20
     # the selection with a ticket but no shape_idx is refused before any launch
     raw.ticket, raw.shape_idx = 0.5, None
     fake = ctypes.c_void_p(1 << 20)
