@@ -61,6 +61,13 @@ __device__ __forceinline__ int swap23(int r) {
     return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1);
 }
 
+// Workgroup barrier after this wave's LDS writes have landed (global loads
+// and stores in flight are not waited for: their results are used only by
+// the wave that issued them, after the waits the compiler places).
+__device__ __forceinline__ void wg_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 __device__ __forceinline__ float half_swap_max(float x) {
     const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
     return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
@@ -92,10 +99,17 @@ struct ErrCfg {
 
 // Persistent grid over the work items (b*h, query group xg of 256 query
 // blocks, KV block j), item = ((bh * nxg) + xg) * nb + j; workgroup w takes a
-// contiguous range.  K_j and V_j^T of the next item are loaded into registers
-// while the current item is computed from LDS, and written to the other LDS
-// stage after it (one barrier per item), so each K/V tile is staged once for
-// all the query blocks of its head and its load overlaps the matrix work.
+// contiguous range, so each K/V tile is staged once for all the query blocks
+// of its head.  An item runs in four phases per wave: M1 (the score product,
+// matrix cores), V1 (mask, max, exp2 weights, hi/lo split), M2 (the value
+// product) and V2 (the error and the key).  The two groups of four waves run
+// one phase apart ("ping-pong"): the second group starts one barrier late,
+// so on every SIMD one wave's matrix phase overlaps the other wave's vector
+// phase and a barrier closes every phase.  Group 0 loads the next item's K
+// tile (and centroid values) during its M1 and stores it to the other LDS
+// stage in its V1, group 1 does the same with the V^T tile one phase later;
+// the other stage's last reader (group 1's M2 of the previous item) is past
+// by then, and both stores land before the next item's M1.
 template <int D, int BLK>
 __global__ __launch_bounds__(kThreads, 1) void k_err(const float* __restrict__ qm,
                                                     const uint16_t* __restrict__ K,
@@ -106,10 +120,16 @@ __global__ __launch_bounds__(kThreads, 1) void k_err(const float* __restrict__ q
                                                     float scale, const int32_t* __restrict__ order,
                                                     int64_t items, int nxg) {
     using C = ErrCfg<D, BLK>;
+    constexpr int GT = kThreads / 2;                 // threads of one wave group
+    constexpr int GK = C::KCH / GT;                  // K chunks per group-0 thread
+    constexpr int GV = C::VCH / GT;                  // V^T chunks per group-1 thread
+    static_assert(GK * GT == C::KCH && GV * GT == C::VCH, "whole chunks per thread");
     extern __shared__ __attribute__((aligned(16))) unsigned char err_lds[];
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int col = lane & 31, h = lane >> 5;
+    const bool lagging = wave >= kWaves / 2;
+    const int gt = tid & (GT - 1);                   // thread index inside the group
     const float c = scale * 1.44269504088896340736f;   // logits in log2 units
     const int64_t beg = items * blockIdx.x / gridDim.x;
     const int64_t end = items * (blockIdx.x + 1) / gridDim.x;
@@ -119,73 +139,62 @@ __global__ __launch_bounds__(kThreads, 1) void k_err(const float* __restrict__ q
     auto vbar_of = [&](int st) {
         return reinterpret_cast<float*>(err_lds + st * C::STAGE_BYTES + (C::K_ELEMS + C::V_ELEMS) * 2);
     };
-    // staging registers of one item's tiles
-    u32x4 kreg[C::PK], vreg[C::PV];
-    float vb = 0.f;
-    auto load_k = [&](int64_t item) __attribute__((always_inline)) {
+    // K chunk p of item `item`: key r of block j is token j*BLK + r of the
+    // block order (through the token order when one is given); rows past the
+    // sequence are zero
+    auto k_chunk = [&](int64_t item, int p) __attribute__((always_inline)) -> u32x4 {
         const int j = (int)(item % nb);
         const int64_t bh = item / ((int64_t)nxg * nb);
         const int nj = min(BLK, N - j * BLK);
-        // key r of block j: token j*BLK + r of the block order (through the
-        // token order when one is given); rows past the sequence are zero
-        const uint16_t* src = K + bh * N * (int64_t)D;
-#pragma unroll
-        for (int n = 0; n < C::PK; ++n) {
-            const int p = tid + n * kThreads;
-            const int r = p / (D / 8), ch = p % (D / 8);
-            u32x4 v = {0u, 0u, 0u, 0u};
-            if (r < nj) {
-                const int t = order ? clamp_token(order[j * BLK + r], N) : j * BLK + r;
-                v = *reinterpret_cast<const u32x4*>(src + (int64_t)t * D + ch * 8);
-            }
-            kreg[n] = v;
+        const int r = p / (D / 8), ch = p % (D / 8);
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (r < nj) {
+            const int t = order ? clamp_token(order[j * BLK + r], N) : j * BLK + r;
+            v = *reinterpret_cast<const u32x4*>(K + (bh * N + t) * (int64_t)D + ch * 8);
         }
+        return v;
     };
-    auto load_v = [&](int64_t item) __attribute__((always_inline)) {
+    auto v_chunk = [&](int64_t item, int p) __attribute__((always_inline)) -> u32x4 {
+        const int j = (int)(item % nb);
+        const int64_t bh = item / ((int64_t)nxg * nb);
+        const int d = p / (BLK / 8), kc = p % (BLK / 8);
+        return *reinterpret_cast<const u32x4*>(Vt + ((bh * nb + j) * (int64_t)D + d) * BLK + kc * 8);
+    };
+    auto vbar_val = [&](int64_t item, int d) __attribute__((always_inline)) -> float {
         const int j = (int)(item % nb);
         const int64_t bh = item / ((int64_t)nxg * nb);
         const int nj = min(BLK, N - j * BLK);
-        const uint16_t* vsrc = Vt + (bh * nb + j) * (int64_t)D * BLK;
-#pragma unroll
-        for (int n = 0; n < C::PV; ++n) {
-            const int p = tid + n * kThreads;
-            const int d = p / (BLK / 8), kc = p % (BLK / 8);
-            vreg[n] = *reinterpret_cast<const u32x4*>(vsrc + (int64_t)d * BLK + kc * 8);
-        }
-        // every thread loads a (clamped) channel; threads d < D keep theirs
-        vb = v_sum[(bh * nb + j) * (int64_t)D + (tid < D ? tid : 0)] / (float)nj;
+        return v_sum[(bh * nb + j) * (int64_t)D + d] / (float)nj;
     };
-    auto store_k = [&](int st) __attribute__((always_inline)) {
-        uint16_t* kt = k_tile(st);
-#pragma unroll
-        for (int n = 0; n < C::PK; ++n) {
-            const int p = tid + n * kThreads;
-            const int r = p / (D / 8), ch = p % (D / 8);
-            *reinterpret_cast<u32x4*>(&kt[r * C::KROW + ch * 8]) = kreg[n];
-        }
+    auto k_put = [&](int st, int p, u32x4 v) __attribute__((always_inline)) {
+        const int r = p / (D / 8), ch = p % (D / 8);
+        *reinterpret_cast<u32x4*>(&k_tile(st)[r * C::KROW + ch * 8]) = v;
     };
-    auto store_v = [&](int st) __attribute__((always_inline)) {
-        uint16_t* vt = v_tile(st);
-#pragma unroll
-        for (int n = 0; n < C::PV; ++n) {
-            const int p = tid + n * kThreads;
-            const int d = p / (BLK / 8), kc = p % (BLK / 8);
-            *reinterpret_cast<u32x4*>(&vt[d * C::VROW + kc * 8]) = vreg[n];
-        }
-        if (tid < D) vbar_of(st)[tid] = vb;
+    auto v_put = [&](int st, int p, u32x4 v) __attribute__((always_inline)) {
+        const int d = p / (BLK / 8), kc = p % (BLK / 8);
+        *reinterpret_cast<u32x4*>(&v_tile(st)[d * C::VROW + kc * 8]) = v;
     };
 
+    // the first item's tiles, by every thread
     if (beg < end) {
-        load_k(beg);
-        load_v(beg);
-        store_k(0);
-        store_v(0);
+        for (int p = tid; p < C::KCH; p += kThreads) k_put(0, p, k_chunk(beg, p));
+        for (int p = tid; p < C::VCH; p += kThreads) v_put(0, p, v_chunk(beg, p));
+        if (tid < D) vbar_of(0)[tid] = vbar_val(beg, tid);
     }
     __syncthreads();
 
-    // query means as hi/lo bf16 B operands of the current (b*h, xg)
+    // staging registers of this thread's share of the next item
+    u32x4 sreg[GK > GV ? GK : GV];
+    float vb = 0.f;
+
     bf16x8 qhi[C::KS], qlo[C::KS];
     int64_t cur_g = -1;
+    f32x16 s[C::KT];
+    bf16x8 whi[C::KT][2], wlo[C::KT][2];
+    f32x16 acc[C::DT];
+    float mx = 0.f, nbase = 0.f, sij = 0.f;
+
+    if (lagging) wg_barrier();
     for (int64_t it = beg; it < end; ++it) {
         const int st = (int)((it - beg) & 1);
         const int j = (int)(it % nb);
@@ -193,13 +202,27 @@ __global__ __launch_bounds__(kThreads, 1) void k_err(const float* __restrict__ q
         const int64_t bh = g / nxg;
         const int q = (int)(g % nxg) * kQPerGroup + wave * kQPerWave + col;
         const bool q_ok = q < nb;
-        // the next item's K and V^T are loaded during this item's score
-        // product and stored to the other stage (read by nobody since the last
-        // barrier) after it, before the value product needs the registers
         const bool more = it + 1 < end;
+        const int nj = min(BLK, N - j * BLK);
+        const uint16_t* ks_lds = k_tile(st);
+        const uint16_t* vs_lds = v_tile(st);
+
+        // ---- M1: L^T = K_j qbar^T (raw dot products; the scale is applied in exp2)
+        wg_barrier();
         if (more) {
-            load_k(it + 1);
-            load_v(it + 1);
+            // this group's share of the next item, into registers (the chunk
+            // indices are formed here: hoisted, they would hold registers
+            // across the whole loop)
+            int g0 = gt;
+            asm volatile("" : "+v"(g0));
+            if (!lagging) {
+#pragma unroll
+                for (int n = 0; n < GK; ++n) sreg[n] = k_chunk(it + 1, g0 + n * GT);
+                if (g0 < D) vb = vbar_val(it + 1, g0);
+            } else {
+#pragma unroll
+                for (int n = 0; n < GV; ++n) sreg[n] = v_chunk(it + 1, g0 + n * GT);
+            }
         }
         if (g != cur_g) {
             cur_g = g;
@@ -218,13 +241,6 @@ __global__ __launch_bounds__(kThreads, 1) void k_err(const float* __restrict__ q
                 split8(x, qhi[s2], qlo[s2]);
             }
         }
-        const int nj = min(BLK, N - j * BLK);
-        const uint16_t* ks_lds = k_tile(st);
-        const uint16_t* vs_lds = v_tile(st);
-        const float* vbar = vbar_of(st);
-
-        // L^T = K_j qbar^T (raw dot products; the scale is applied in exp2)
-        f32x16 s[C::KT];
 #pragma unroll
         for (int kt = 0; kt < C::KT; ++kt) {
             s[kt] = f32x16{};
@@ -237,13 +253,23 @@ __global__ __launch_bounds__(kThreads, 1) void k_err(const float* __restrict__ q
             }
         }
 
+        // ---- V1: the next item's share to the other stage; mask, max, weights
+        wg_barrier();
         if (more) {
-            store_k(st ^ 1);
-            store_v(st ^ 1);
+            int g0 = gt;
+            asm volatile("" : "+v"(g0));
+            if (!lagging) {
+#pragma unroll
+                for (int n = 0; n < GK; ++n) k_put(st ^ 1, g0 + n * GT, sreg[n]);
+                if (g0 < D) vbar_of(st ^ 1)[g0] = vb;
+            } else {
+#pragma unroll
+                for (int n = 0; n < GV; ++n) v_put(st ^ 1, g0 + n * GT, sreg[n]);
+            }
         }
-
+        sij = q_ok ? S[(bh * nb + q) * (int64_t)nb + j] : 0.f;
         // keys past the end of the sequence take no part (a short last
-        // block only); max over the block
+        // block only)
         if (nj < BLK) {
 #pragma unroll
             for (int kt = 0; kt < C::KT; ++kt) {
@@ -255,47 +281,48 @@ __global__ __launch_bounds__(kThreads, 1) void k_err(const float* __restrict__ q
                 }
             }
         }
-        float mx = -__builtin_inff();
+        mx = -__builtin_inff();
 #pragma unroll
         for (int kt = 0; kt < C::KT; ++kt) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kt][r]);
         }
         mx = half_swap_max(mx);
-        const float nbase = -c * mx;
-#pragma unroll
-        for (int kt = 0; kt < C::KT; ++kt) {
-#pragma unroll
-            for (int r = 0; r < 16; ++r)
-                s[kt][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kt][r], c, nbase));
-        }
-
-        // A^T = V_j^T W^T
-        f32x16 acc[C::DT];
-#pragma unroll
-        for (int dt = 0; dt < C::DT; ++dt) acc[dt] = f32x16{};
+        nbase = -c * mx;
 #pragma unroll
         for (int kt = 0; kt < C::KT; ++kt) {
 #pragma unroll
             for (int s2 = 0; s2 < 2; ++s2) {
                 float w[8];
 #pragma unroll
-                for (int t = 0; t < 8; ++t) w[t] = s[kt][8 * s2 + t];
-                bf16x8 whi, wlo;
-                split8(w, whi, wlo);
+                for (int t = 0; t < 8; ++t)
+                    w[t] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kt][8 * s2 + t], c, nbase));
+                split8(w, whi[kt][s2], wlo[kt][s2]);
+            }
+        }
+
+        // ---- M2: A^T = V_j^T W^T
+        wg_barrier();
+#pragma unroll
+        for (int dt = 0; dt < C::DT; ++dt) acc[dt] = f32x16{};
+#pragma unroll
+        for (int kt = 0; kt < C::KT; ++kt) {
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2) {
 #pragma unroll
                 for (int dt = 0; dt < C::DT; ++dt) {
                     const bf16x8 a = __builtin_bit_cast(
                         bf16x8, *reinterpret_cast<const uint4*>(
                                     &vs_lds[(dt * 32 + col) * C::VROW + kt * 32 + 16 * s2 + 8 * h]));
-                    acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, whi, acc[dt], 0, 0, 0);
-                    acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, wlo, acc[dt], 0, 0, 0);
+                    acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, whi[kt][s2], acc[dt], 0, 0, 0);
+                    acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, wlo[kt][s2], acc[dt], 0, 0, 0);
                 }
             }
         }
 
-        // || A - Ahat ||^2 over the channels, Ahat = n_j exp(S_ij - m) vbar_j
-        const float sij = q_ok ? S[(bh * nb + q) * (int64_t)nb + j] : 0.f;
+        // ---- V2: || A - Ahat ||^2 over the channels, Ahat = n_j exp(S_ij - m) vbar_j
+        wg_barrier();
+        const float* vbar = vbar_of(st);
         const float zhat = (float)nj * __builtin_amdgcn_exp2f(sij * 1.44269504088896340736f + nbase);
         float e2 = 0.f;
 #pragma unroll
@@ -310,9 +337,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_err(const float* __restrict__ q
         e2 = half_swap_sum(e2);
         if (h == 0 && q_ok)
             keys[(bh * nb + q) * (int64_t)nb + j] = 0.5f * logf(e2) + scale * mx - logf((float)nj);
-
-        __syncthreads();
     }
+    if (!lagging) wg_barrier();
 }
 
 template <int D, int BLK>
