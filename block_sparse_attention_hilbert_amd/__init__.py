@@ -66,7 +66,8 @@ class SaSelectSpec(ctypes.Structure):
                 ("density", ctypes.POINTER(ctypes.c_float)),
                 ("mass", ctypes.c_float), ("diag", ctypes.c_int32),
                 ("window_frames", ctypes.c_int32), ("n_anchors", ctypes.c_int32),
-                ("anchor_offset", ctypes.c_int64), ("want_comp", ctypes.c_int32)]
+                ("anchor_offset", ctypes.c_int64), ("want_comp", ctypes.c_int32),
+                ("v_blocks", ctypes.c_void_p)]
 
 
 class SaTileShape(ctypes.Structure):
@@ -183,8 +184,9 @@ class SelectSpec:
     anchor_offset: int = 0
     want_comp: bool = False
 
-    def c(self):
-        """ctypes struct plus the host arrays it points to (kept alive by the caller)."""
+    def c(self, v_blocks: int = 0):
+        """ctypes struct plus the host arrays it points to (kept alive by the
+        caller); ``v_blocks``: device address for the error rule's V layout (0: none)."""
         keep = []
         topk = density = None
         if self.topk is not None:
@@ -197,7 +199,7 @@ class SelectSpec:
             density = arr.ctypes.data_as(ctypes.POINTER(ctypes.c_float))
         s = SaSelectSpec(RULES[self.rule], self.sub_block, topk, density, self.mass,
                          int(self.diag), self.window_frames, self.n_anchors,
-                         int(self.anchor_offset), int(self.want_comp))
+                         int(self.anchor_offset), int(self.want_comp), v_blocks or None)
         return s, keep
 
 
@@ -269,12 +271,14 @@ class _Stream:
         return ctypes.c_void_p(s.cuda_stream)
 
 
-def workspace_size(prob: Problem, spec: Optional[SelectSpec] = None) -> int:
+def workspace_size(prob: Problem, spec: Optional[SelectSpec] = None, *, v_blocks: bool = False) -> int:
+    """sparse_attn_workspace_size; ``v_blocks``: the error rule's V layout goes
+    to the caller's buffer (the size query reads only whether it is given)."""
     n = ctypes.c_size_t(0)
     if spec is None:
         _check(lib.sparse_attn_workspace_size(ctypes.byref(prob.c()), None, ctypes.byref(n)))
     else:
-        cs, keep = spec.c()
+        cs, keep = spec.c(256 if v_blocks else 0)
         _check(lib.sparse_attn_workspace_size(ctypes.byref(prob.c()), ctypes.byref(cs),
                                               ctypes.byref(n)))
     return int(n.value)
@@ -334,8 +338,10 @@ class Selection:
 def select(prob: Problem, spec: SelectSpec, Q: torch.Tensor, K: torch.Tensor,
            V: Optional[torch.Tensor] = None, *, want_scores: bool = False,
            out: Optional[Selection] = None, workspace: Optional[torch.Tensor] = None,
-           stream=None) -> Selection:
-    """sparse_attn_select.  Output buffers are allocated unless ``out`` is given."""
+           v_blocks: Optional[torch.Tensor] = None, stream=None) -> Selection:
+    """sparse_attn_select.  Output buffers are allocated unless ``out`` is given.
+    ``v_blocks`` (error rule): a forward workspace whose start receives V in
+    block layout, for a following ``fwd_prepare(V=None)``."""
     A = _Args()
     dev = (Q if Q is not None else K).device
     nb, rows = prob.nb, prob.rows
@@ -347,9 +353,13 @@ def select(prob: Problem, spec: SelectSpec, Q: torch.Tensor, K: torch.Tensor,
         if spec.want_comp:
             out.k_mean = torch.empty(prob.B, prob.H, nb, prob.d, dtype=torch.float32, device=dev)
             out.v_sum = torch.empty_like(out.k_mean)
+    vb = 0
+    if v_blocks is not None:
+        need = prob.B * prob.H * nb * prob.d * prob.block * 2
+        vb = A(v_blocks, "v_blocks", _U8, numel=need).value
+    cs, keep = spec.c(vb)
     if workspace is None:
-        workspace = alloc_workspace(workspace_size(prob, spec), dev)
-    cs, keep = spec.c()
+        workspace = alloc_workspace(workspace_size(prob, spec, v_blocks=vb != 0), dev)
     tok, stat = _tokens(prob), (prob.B, prob.H, nb, prob.d)
     args = [A(Q, "Q", _BF16, shape=tok, optional=True),
             A(K, "K", _BF16, shape=tok, optional=True),
@@ -435,10 +445,11 @@ def fwd(prob: Problem, Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor,
 def fwd_prepare(prob: Problem, V: torch.Tensor, row_ptr: torch.Tensor,
                 k_mean: Optional[torch.Tensor] = None, v_sum: Optional[torch.Tensor] = None, *,
                 workspace: torch.Tensor, stream=None) -> None:
-    """sparse_attn_fwd_prepare: V (and the centroids) laid out in ``workspace``."""
+    """sparse_attn_fwd_prepare: V (and the centroids) laid out in ``workspace``.
+    V = None: the workspace already starts with V in block layout (written by
+    an error-rule ``select`` with ``v_blocks=workspace``)."""
     A = _Args()
-    pv = A(V, "V", _BF16, shape=_tokens(prob))
-    dev = V.device
+    pv = A(V, "V", _BF16, shape=_tokens(prob), optional=True)
     wp, ws_bytes = _ws(A, workspace)
     _check(A.call(lib.sparse_attn_fwd_prepare, ctypes.byref(prob.c()), pv,
                                        A(row_ptr, "row_ptr", _I32, numel=prob.rows + 1),

@@ -845,9 +845,11 @@ WsLayout ws_layout(const Geometry& g, bool comp) {
     WsLayout L{};
     const int64_t ntc = ceil_div(g.nb, g.block);
     size_t off = 0;
+    // V in block layout first: a selection with the error rule can write it
+    // there (the caller passes the workspace start)
+    L.vt = off; off = align_up(off + (size_t)g.BH() * g.nb * g.d * g.block * 2, 256);
     L.sched = off; off = align_up(off + 32 * sizeof(int32_t), 256);
     L.cnt = off; off = align_up(off + (size_t)g.BH() * g.nb * sizeof(int16_t), 256);
-    L.vt = off; off = align_up(off + (size_t)g.BH() * g.nb * g.d * g.block * 2, 256);
     if (g.order) {   // K in block order, [BH][N][D]
         L.kord = off; off = align_up(off + (size_t)g.BH() * g.N * g.d * 2, 256);
     }
@@ -874,9 +876,11 @@ sa_status prepare_t(const FwdArgs& a, const Geometry& g, const uint16_t* V, uint
                            kv_count, cnt, g.N, g.nb, BLK, ncnt);
         if ((st = hip_check(hipGetLastError(), "k_fill_counts launch")) != SA_OK) return st;
     }
-    hipLaunchKernelGGL((k_vt_prep<D, BLK>), dim3(g.nb, (unsigned)g.BH()), dim3(256), 0, stream, V,
-                       vt, g.N, g.nb, g.order);
-    if ((st = hip_check(hipGetLastError(), "k_vt_prep launch")) != SA_OK) return st;
+    if (V) {   // else the workspace already holds V in block layout
+        hipLaunchKernelGGL((k_vt_prep<D, BLK>), dim3(g.nb, (unsigned)g.BH()), dim3(256), 0, stream, V,
+                           vt, g.N, g.nb, g.order);
+        if ((st = hip_check(hipGetLastError(), "k_vt_prep launch")) != SA_OK) return st;
+    }
     if (COMP) {
         hipLaunchKernelGGL((k_comp_prep<D, BLK>), dim3(a.ntc * (BLK / kCompRun), (unsigned)g.BH()),
                            dim3(256), 0, stream, k_mean, v_sum, a.cnt, kbar, vbart, g.nb, a.ntc);

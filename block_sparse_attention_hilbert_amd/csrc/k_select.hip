@@ -784,8 +784,9 @@ SelectPlan make_select_plan(const Geometry& g, const sa_select_spec& s) {
     p.off_counts = off; off = align_up(off + (size_t)g.rows() * sizeof(int32_t), 256);
     p.off_k = off; off = align_up(off + (size_t)g.H * sizeof(int32_t), 256);
     const bool err = s.rule == SA_RULE_ERR;
+    p.v_blocks = err ? static_cast<uint16_t*>(s.v_blocks) : nullptr;
     p.off_vt = off;
-    off = align_up(off + (err ? (size_t)g.BH() * g.nb * g.d * g.block * 2 : 0), 256);
+    off = align_up(off + (err && !p.v_blocks ? (size_t)g.BH() * g.nb * g.d * g.block * 2 : 0), 256);
     p.off_keys = off;
     off = align_up(off + (err ? (size_t)g.rows() * g.nb * sizeof(float) : 0), 256);
     p.total = off;
@@ -878,7 +879,7 @@ sa_status launch_select(const Geometry& g, const SelectPlan& p, const int32_t* k
 
     // 2b. error-aware routing keys
     if (err) {
-        uint16_t* vt = reinterpret_cast<uint16_t*>(ws + p.off_vt);
+        uint16_t* vt = p.v_blocks ? p.v_blocks : reinterpret_cast<uint16_t*>(ws + p.off_vt);
         if ((st = launch_vt_layout(g, V, vt, stream)) != SA_OK) return st;
         if ((st = launch_route_keys(g, qm, K, vt, v_sum, S, keys, stream)) != SA_OK) return st;
     }

@@ -131,6 +131,10 @@ sa_status check_spec(const Geometry& g, const sa_select_spec* s) {
     if (s->rule != SA_RULE_NONE && s->rule != SA_RULE_TOPK && s->rule != SA_RULE_MASS &&
         s->rule != SA_RULE_ERR)
         return fail(SA_ERR_INVALID_ARG, "unknown rule %d", s->rule);
+    if (s->v_blocks && s->rule != SA_RULE_ERR)
+        return fail(SA_ERR_INVALID_ARG, "v_blocks is for SA_RULE_ERR only (must be NULL)");
+    if (s->v_blocks && ((uintptr_t)s->v_blocks & 255u) != 0)
+        return fail(SA_ERR_INVALID_ARG, "v_blocks must be 256-byte aligned");
     if (s->rule == SA_RULE_ERR) {
         if (s->want_comp != 1)
             return fail(SA_ERR_INVALID_ARG, "SA_RULE_ERR needs want_comp = 1");
@@ -347,8 +351,8 @@ SA_API sa_status sparse_attn_fwd_prepare(const sa_problem* prob, const void* V,
     Geometry g;
     sa_status st = check_problem(prob, &g);
     if (st != SA_OK) return st;
-    if (!V) return fail(SA_ERR_INVALID_ARG, "V is required");
-    if (!aligned16(V)) return fail(SA_ERR_INVALID_ARG, "V must be 16-byte aligned");
+    // V == NULL: the workspace already starts with V in block layout
+    if (V && !aligned16(V)) return fail(SA_ERR_INVALID_ARG, "V must be 16-byte aligned");
     if (!row_ptr) return fail(SA_ERR_INVALID_ARG, "row_ptr is required");
     if ((k_mean == nullptr) != (v_sum == nullptr))
         return fail(SA_ERR_INVALID_ARG, "k_mean and v_sum must be given together");

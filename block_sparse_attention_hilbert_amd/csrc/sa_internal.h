@@ -64,6 +64,7 @@ struct SelectPlan {
     // workspace carve-up (byte offsets); the error rule adds V re-laid out
     // per block and its routing keys
     size_t off_qm, off_km, off_scores, off_bits, off_counts, off_k, off_vt, off_keys, total;
+    uint16_t* v_blocks;      // the caller's destination of the V layout (error rule), or null
 };
 
 SelectPlan make_select_plan(const Geometry& g, const sa_select_spec& s);

@@ -79,7 +79,11 @@ class BlockSparseAttention:
             self.sel.k_mean = torch.empty(prob.B, prob.H, nb, prob.d, dtype=torch.float32,
                                           device=self.device)
             self.sel.v_sum = torch.empty_like(self.sel.k_mean)
-        self.ws_select = alloc_workspace(workspace_size(prob, spec), self.device)
+        # the error rule's selection writes V in block layout straight into the
+        # forward workspace, so the forward call does not lay it out again
+        self.share_v = spec.rule == "err"
+        self.v_ready = False       # the forward workspace holds V of the last selection
+        self.ws_select = alloc_workspace(workspace_size(prob, spec, v_blocks=self.share_v), self.device)
         self.ws_fwd = alloc_workspace(workspace_size(prob, None), self.device)
         # O and lse in the caller's token order (also with Hilbert blocks)
         self.O = torch.empty(shape, dtype=torch.bfloat16, device=self.device)
@@ -91,12 +95,16 @@ class BlockSparseAttention:
         if anchor_offset is not None:
             spec = SelectSpec(**{**spec.__dict__, "anchor_offset": int(anchor_offset)})
         sel = select(self.prob, spec, Q, K, V if spec.want_comp else None,
-                     out=self.sel, workspace=self.ws_select)
+                     out=self.sel, workspace=self.ws_select,
+                     v_blocks=self.ws_fwd if self.share_v else None)
         self.have_mask = True
+        self.v_ready = self.share_v
         return sel
 
     def run_centroids(self, K, V):
-        """Compensation statistics of the current K, V for a reused mask."""
+        """Compensation statistics of the current K, V for a reused mask (the
+        forward call then lays out this V itself)."""
+        self.v_ready = False
         if self.spec.want_comp:
             centroids(self.prob, K, V, self.sel.k_mean, self.sel.v_sum)
 
@@ -105,6 +113,10 @@ class BlockSparseAttention:
         return self.have_mask and self.calls % self.refresh_every != 0
 
     def run_fwd(self, Q, K, V, row_ptr=None, col_idx=None):
+        if self.v_ready:
+            # V is already in the workspace (written by the selection)
+            self.run_fwd_prepare(V, row_ptr)
+            return self.run_fwd_attention(Q, K, row_ptr, col_idx)
         rp = self.sel.row_ptr if row_ptr is None else row_ptr
         ci = self.sel.col_idx if col_idx is None else col_idx
         fwd(self.prob, Q, K, V, rp, ci, self.sel.k_mean, self.sel.v_sum, O=self.O, lse=self.lse,
@@ -112,9 +124,11 @@ class BlockSparseAttention:
         return self.O
 
     def run_fwd_prepare(self, V, row_ptr=None):
-        """First half of run_fwd: V (and the centroids) laid out in the workspace."""
+        """First half of run_fwd: V (and the centroids) laid out in the workspace
+        (V only if the last selection has not already put it there)."""
         rp = self.sel.row_ptr if row_ptr is None else row_ptr
-        fwd_prepare(self.prob, V, rp, self.sel.k_mean, self.sel.v_sum, workspace=self.ws_fwd)
+        fwd_prepare(self.prob, None if self.v_ready else V, rp, self.sel.k_mean, self.sel.v_sum,
+                    workspace=self.ws_fwd)
 
     def run_fwd_attention(self, Q, K, row_ptr=None, col_idx=None):
         """Second half of run_fwd: the attention kernel (with Hilbert blocks,

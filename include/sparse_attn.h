@@ -182,14 +182,27 @@ typedef struct {
                                 m*floor(nb/A)) mod nb kept for every row  [LVSA] */
     int64_t anchor_offset;   /* rotation of the anchors for this call (>= 0)      */
     int32_t want_comp;       /* 1: also write k_mean and v_sum for compensation   */
+    void* v_blocks;          /* SA_RULE_ERR only, optional (NULL for the other
+                                rules).  The error rule needs V re-laid out
+                                block by block ([B,H,nb,d,block] bf16, keys past
+                                N zero), the layout the forward call needs too.
+                                NULL: it is built in the selection workspace.
+                                Non-NULL (device, 256-byte aligned, room for
+                                B*H*nb*d*block bf16): it is written here and
+                                left for the caller; passing the start of a
+                                forward workspace lets sparse_attn_fwd_prepare
+                                skip its own re-layout (V = NULL there).
+                                sparse_attn_workspace_size reads only whether
+                                it is NULL.                                     */
 } sa_select_spec;
 
 /*
- * Workspace bytes needed by sparse_attn_select (spec != NULL) or by
- * sparse_attn_fwd (spec == NULL; the size covers calls with and without
- * compensation: 2*B*H*nb*d*block bytes for V re-laid out block by block, plus
- * the bf16 centroid tiles).  The same buffer may be reused by consecutive
- * calls on one stream.
+ * Workspace bytes needed by sparse_attn_select (spec != NULL; with the error
+ * rule and spec->v_blocks == NULL this includes V re-laid out block by block)
+ * or by sparse_attn_fwd (spec == NULL; the size covers calls with and without
+ * compensation: V re-laid out block by block in its first 2*B*H*nb*d*block
+ * bytes, then the bf16 centroid tiles and the work split).  The same buffer
+ * may be reused by consecutive calls on one stream.
  */
 sa_status sparse_attn_workspace_size(const sa_problem* prob,
                                      const sa_select_spec* spec, size_t* bytes);
@@ -334,9 +347,13 @@ sa_status sparse_attn_fwd(const sa_problem* prob, const void* Q, const void* K,
  * same stream, workspace and problem.
  *
  * sparse_attn_fwd_prepare: writes into the workspace V re-laid out block by
- *   block ([B,H,nb,d,block] bf16, keys past N zero), with compensation
- *   (k_mean, v_sum both non-NULL) the bf16 centroid keys and values, and the
- *   split of the rows into per-XCD work ranges (reads row_ptr).
+ *   block ([B,H,nb,d,block] bf16, keys past N zero; the workspace's first
+ *   2*B*H*nb*d*block bytes), with compensation (k_mean, v_sum both non-NULL)
+ *   the bf16 centroid keys and values, and the split of the rows into per-XCD
+ *   work ranges (reads row_ptr).  V = NULL skips the re-layout: the workspace
+ *   must then already start with this V in that layout, e.g. written by a
+ *   sparse_attn_select with SA_RULE_ERR and spec->v_blocks = workspace, on
+ *   the same stream, for the same problem and V.
  * sparse_attn_fwd_run: the attention kernel.  Reads the workspace written by
  *   the last sparse_attn_fwd_prepare on this stream, which must have had the
  *   same prob, the same row_ptr contents and with_comp = (k_mean != NULL);

@@ -155,7 +155,7 @@ def test_fwd_halves_reject_before_any_launch():
     fake = vp(1 << 20)
     odd = vp((1 << 20) + 8)
     prep, run = sa.lib.sparse_attn_fwd_prepare, sa.lib.sparse_attn_fwd_run
-    assert prep(ctypes.byref(p), None, fake, None, None, fake, 1 << 30, None) == sa.SA_ERR_INVALID_ARG
+    # (V = NULL is accepted: the workspace then already holds V in block layout)
     assert prep(ctypes.byref(p), odd, fake, None, None, fake, 1 << 30, None) == sa.SA_ERR_INVALID_ARG
     assert prep(ctypes.byref(p), fake, None, None, None, fake, 1 << 30, None) == sa.SA_ERR_INVALID_ARG
     assert prep(ctypes.byref(p), fake, fake, fake, None, fake, 1 << 30, None) == sa.SA_ERR_INVALID_ARG
@@ -216,6 +216,38 @@ def test_cluster_sizes_and_validation():
                                            None, None, None) == sa.SA_ERR_INVALID_ARG
     big = sa.Problem(1, 1, 4090 * 64, 64, 4090, 1, 64, 64)
     assert _err(sa.cluster_size, big, sa.ClusterSpec("kmeans", 16, 1)) == sa.SA_ERR_UNSUPPORTED
+
+
+def test_select_v_blocks_validation_and_sizes():
+    """The error rule's V layout can go to the caller's buffer (the start of a
+    forward workspace): the selection workspace then shrinks by exactly that
+    layout; v_blocks is rejected for the other rules and when misaligned, and
+    the forward workspace starts with the layout."""
+    p = _prob(N=1024, T=8, Hg=8, W=16, H=3)           # nb = 8
+    err = sa.SelectSpec(rule="err", topk=[2, 2, 2], want_comp=True)
+    layout = p.B * p.H * p.nb * p.d * p.block * 2
+    full = sa.workspace_size(p, err)
+    shared = sa.workspace_size(p, err, v_blocks=True)
+    assert full - shared == layout
+    # the forward workspace holds the layout first, so it is at least that big
+    assert sa.workspace_size(p) >= layout
+    vp = ctypes.c_void_p
+    fake = vp(1 << 20)
+    raw = p.c()
+    n = ctypes.c_size_t(0)
+    mass, keep = sa.SelectSpec(rule="mass").c(1 << 20)
+    assert sa.lib.sparse_attn_workspace_size(ctypes.byref(raw), ctypes.byref(mass),
+                                             ctypes.byref(n)) == sa.SA_ERR_INVALID_ARG
+    odd, keep2 = err.c((1 << 20) + 128)
+    assert sa.lib.sparse_attn_workspace_size(ctypes.byref(raw), ctypes.byref(odd),
+                                             ctypes.byref(n)) == sa.SA_ERR_INVALID_ARG
+    # the same checks on the selection call itself, before anything is launched
+    st = sa.lib.sparse_attn_select(ctypes.byref(raw), ctypes.byref(odd), fake, fake, fake,
+                                   fake, fake, None, fake, fake, fake, 1 << 30, None)
+    assert st == sa.SA_ERR_INVALID_ARG
+    st = sa.lib.sparse_attn_select(ctypes.byref(raw), ctypes.byref(mass), fake, fake, None,
+                                   fake, fake, None, None, None, fake, 1 << 30, None)
+    assert st == sa.SA_ERR_INVALID_ARG
 
 
 def test_sics_ticket_validation():

@@ -244,6 +244,33 @@ def test_fwd_halves_match_fwd(name):
         assert torch.equal(lse, ref_lse)
 
 
+@pytest.mark.parametrize("name", ["err_d128_b128", "err_hilbert_d128_b64", "err_d64_b64_wide"])
+def test_err_selection_shares_v_layout(name):
+    """The error rule's selection writes V in block layout into the forward
+    workspace (v_blocks), and the forward call then skips its own re-layout:
+    keys, CSR, O and lse are bit-identical to a selection that keeps the layout
+    in its own workspace followed by a forward call that lays V out again."""
+    sa = _sa()
+    wl = SMALL[name]
+    Q, K, V = (to_dev(x) for x in W.make_qkv(wl))
+    pipe = _pipeline(wl)
+    assert pipe.share_v
+    poison(pipe.O, pipe.lse)
+    O = pipe(Q, K, V, anchor_offset=0).clone()
+    lse = pipe.lse.clone()
+    prob, spec = pipe.prob, sa.spec_for(wl)
+    ref = sa.select(prob, spec, Q, K, V, want_scores=True)
+    O2, lse2 = sa.fwd(prob, Q, K, V, ref.row_ptr, ref.col_idx, ref.k_mean, ref.v_sum, want_lse=True)
+    torch.cuda.synchronize()
+    assert torch.equal(pipe.sel.row_ptr, ref.row_ptr)
+    n = int(ref.row_ptr[-1])
+    assert torch.equal(pipe.sel.col_idx[:n], ref.col_idx[:n])
+    assert torch.equal(pipe.sel.scores, ref.scores)
+    assert torch.equal(O.view(torch.int16), O2.view(torch.int16))
+    assert torch.equal(lse, lse2)
+    log(f"[share] {name}: shared V layout bit-identical ({n} kept blocks)")
+
+
 @pytest.mark.parametrize("name", ["hilbert_comp_d128_b64", "mass_d128_b128", "err_d128_b128"])
 def test_mask_reuse_across_steps(name):
     """Mask reuse (DFSAttn trick 3, SVOO 2B): step 0 selects, steps 1 and 2 keep
