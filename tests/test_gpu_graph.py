@@ -27,6 +27,9 @@ BASE = W.WORKLOADS[2].replace(T=3, Hg=10, W=13, H=2)          # N = 390
 CASES = {
     "fixed_mass_comp_b64": BASE.replace(block=64, comp=True),
     "fixed_hilbert_topk_b128": BASE.replace(hilbert=True, rule="topk", density=0.3),
+    # error-aware routing: the selection writes V in block layout into the
+    # forward workspace, and the forming graph skips the second re-layout
+    "fixed_err_comp_b128": BASE.replace(rule="err", density=0.3, comp=True),
     "cocluster_mass_b128": BASE.replace(cluster="cocluster", n_clusters=3, cluster_iters=2),
     "kmeans_topk_comp_b64": BASE.replace(block=64, cluster="kmeans", n_clusters=6,
                                          cluster_iters=3, rule="topk", density=0.3, comp=True),
