@@ -88,7 +88,13 @@ __device__ __forceinline__ float xsum32(float x) {
 // in flight.  The memory clobber keeps the compiler from moving LDS accesses
 // across it.
 __device__ __forceinline__ void wg_barrier() { asm volatile("s_barrier" ::: "memory"); }
-__device__ __forceinline__ void copies_done() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// The scheduling fence keeps the compiler from hoisting the wait above the
+// vector work before it (which touches no memory): the copies in flight then
+// land while the softmax runs instead of stalling it.
+__device__ __forceinline__ void copies_done() {
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
 
 struct FwdArgs {
     const uint16_t* Q;
