@@ -91,6 +91,10 @@ class BlockSparseAttention:
                                device=self.device) if want_lse else None
 
     def run_select(self, Q, K, V, anchor_offset: Optional[int] = None) -> Selection:
+        """The selection.  With the error rule it also leaves this V in block
+        layout in the forward workspace, and the next run_fwd /
+        run_fwd_prepare use that layout instead of laying out their V again:
+        pass them the same V (run_centroids, the mask-reuse path, drops it)."""
         spec = self.spec
         if anchor_offset is not None:
             spec = SelectSpec(**{**spec.__dict__, "anchor_offset": int(anchor_offset)})
