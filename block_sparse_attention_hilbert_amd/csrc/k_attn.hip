@@ -57,6 +57,9 @@ constexpr float kLazy = 8.0f;      // log2 headroom before the running max moves
 #ifndef SA_SGB
 #define SA_SGB 1
 #endif
+#ifndef SA_VPRIO
+#define SA_VPRIO 1                 // wave priority of the vector phase (4-wave workgroups)
+#endif
 
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
     uint32_t u = __float_as_uint(f);
@@ -524,7 +527,13 @@ __device__ __forceinline__ void process_row(const FwdArgs& a, int64_t row, unsig
             }
             matrix_phase(yes{}, yes{}, t);
             if (C::PING) wg_barrier();
+            // 4-wave workgroups (64-token blocks) run free beside a second
+            // workgroup on the CU: the vector phase takes issue priority over
+            // the other workgroup's matrix work on the SIMD, whose queued
+            // matrix instructions keep the matrix core busy meanwhile
+            if constexpr (!C::PING) __builtin_amdgcn_s_setprio(SA_VPRIO);
             vector_phase(t + 1);
+            if constexpr (!C::PING) __builtin_amdgcn_s_setprio(0);
             copies_done();
         }
         // step T-1: P_{T-1} V_{T-1}
