@@ -25,6 +25,8 @@
 //                   per-block compensation statistics
 #include <math.h>
 
+#include <algorithm>
+
 #include "sa_internal.h"
 
 namespace sa {
@@ -136,19 +138,29 @@ __global__ __launch_bounds__(kAsgThreads) void k_assign(const uint16_t* __restri
 // s~[c, t] = x_t . c on v_mfma_f32_32x32x16_bf16: x is bf16 (exact operand),
 // the fp32 centroid is split into bf16 hi + lo; |s~ - seqfma| <= 2^-14.7
 // sum_d |x_d c_d| (split remainder 2^-16, fp32 accumulation of 256 terms, the
-// chain's own 128 roundings).  With B = 2^-12 (|x| |c| + |bias_c|), a
+// chain's own 128 roundings).  With B = 2^-12 (|x| |c| + |bias|), a
 // centroid can win only if s~ + bias + B >= the token's best s~ + bias - B;
 // those candidates (about one per token) get the exact decision arithmetic
 // of k_assign, and the exact winner among them is the winner among all.
-// One wave = 32 tokens (two lanes per token); the workgroup's centroids sit in
-// LDS (fp32; the hi / lo operands are split from them).  Each token's
-// candidates are evaluated by its own two lanes in ascending index order.
+//
+// A workgroup (8 waves) serves one head and many 32-token groups: it stages
+// the head's centroids once (fp32 rows for the exact chains, the split hi / lo
+// operands in the lane order of the matrix instruction, the decision bias and
+// the bound terms per centroid), then each wave takes groups of 32 tokens
+// (two lanes per token) in turn.  Each token's candidates are evaluated by its
+// own two lanes in ascending index order.
 // ----------------------------------------------------------------------------
 typedef __bf16 amx_bf16x8 __attribute__((ext_vector_type(8)));
 typedef float amx_f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 amx_bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kAmxC = 64;                  // centroid slots (C <= 64)
+constexpr int kAmxWaves = 8;               // waves per workgroup
 constexpr float kAmxEps = 1.0f / 4096.0f;  // bound factor 2^-12
+// added to both squared norms: it covers squares and products lost below the
+// fp32 / bf16 normal range (flushed or underflowed), so that the bound holds
+// for arbitrarily small tokens and centroids
+constexpr float kAmxTiny = 0x1p-118f;
 
 __device__ __forceinline__ uint16_t amx_bf16(float f) {
     uint32_t u = __float_as_uint(f);
@@ -156,28 +168,35 @@ __device__ __forceinline__ uint16_t amx_bf16(float f) {
     return (uint16_t)(u >> 16);
 }
 
-__device__ __forceinline__ uint32_t amx_ordered(float f) {
-    const uint32_t u = __float_as_uint(f);
-    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+// the value of lane (l & 31) + 32 h, for both lanes l of a pair (h constant)
+template <int HALF>
+__device__ __forceinline__ float amx_pair_take(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(HALF == 0 ? r[0] : r[1]);
 }
 
 template <int D>
-__global__ __launch_bounds__(256) void k_assign_mx(const uint16_t* __restrict__ X,
-                                                   const float* __restrict__ cent,
-                                                   int32_t* __restrict__ assign, int N, int C,
-                                                   int kmeans) {
+__global__ __launch_bounds__(64 * kAmxWaves) __attribute__((amdgpu_waves_per_eu(4))) void k_assign_mx(const uint16_t* __restrict__ X,
+                                                              const float* __restrict__ cent,
+                                                              int32_t* __restrict__ assign, int N,
+                                                              int C, int kmeans) {
     constexpr int ROW = D + 4;                     // floats per centroid row in LDS
-    __shared__ float cs[kAmxC * ROW];              // the head's centroids (fp32)
-    __shared__ float sb[kAmxC], sn[kAmxC];         // bias and norm bound
+    constexpr int NST = D / 16;                    // k-steps of the matrix instruction
+    constexpr int NT = 64 * kAmxWaves;
+    __shared__ __align__(16) float cs[kAmxC * ROW];     // the head's centroids (fp32)
+    __shared__ uint4 aop[2][NST][2][64];                // A operands [tile][k-step][hi, lo][lane]
+    __shared__ float sb[kAmxC];                         // decision bias
+    __shared__ __align__(16) float sbl[kAmxC];          // bias - its bound share
+    __shared__ __align__(16) float sbh[kAmxC];          // bias + its bound share
+    __shared__ __align__(16) float sn[kAmxC];           // norm upper bound
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int r32 = lane & 31, hf = lane >> 5;
     const int64_t bh = blockIdx.y;
-    const int tok0 = blockIdx.x * 128 + wave * 32;
     const int nct = (C + 31) / 32;                 // centroid tiles
     const uint16_t* Xh = X + bh * (int64_t)N * D;
     {
         const float* ch = cent + bh * (int64_t)C * D;
-        for (int p = threadIdx.x; p < kAmxC * (D / 4); p += 256) {
+        for (int p = threadIdx.x; p < kAmxC * (D / 4); p += NT) {
             const int c = p / (D / 4), o = p % (D / 4);
             float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
             if (c < C) v = reinterpret_cast<const float4*>(ch + (int64_t)c * D)[o];
@@ -185,142 +204,184 @@ __global__ __launch_bounds__(256) void k_assign_mx(const uint16_t* __restrict__ 
         }
     }
     __syncthreads();
-    if (threadIdx.x < kAmxC) {
+    // A operand of lane l in tile ct, k-step st: centroid ct*32 + (l & 31),
+    // channels 16 st + 8 (l >> 5) .. + 7, as bf16 hi and the bf16 of the rest
+    for (int p = threadIdx.x; p < 2 * NST * 64; p += NT) {
+        const int l = p & 63, st = (p >> 6) % NST, ct = p / (64 * NST);
+        const float* cr = cs + (ct * 32 + (l & 31)) * ROW + 16 * st + 8 * (l >> 5);
+        float v[8];
+        *reinterpret_cast<float4*>(v) = *reinterpret_cast<const float4*>(cr);
+        *reinterpret_cast<float4*>(v + 4) = *reinterpret_cast<const float4*>(cr + 4);
+        uint32_t h[4], lo[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const uint16_t h0 = amx_bf16(v[2 * e]), h1 = amx_bf16(v[2 * e + 1]);
+            const uint16_t l0 = amx_bf16(v[2 * e] - __uint_as_float((uint32_t)h0 << 16));
+            const uint16_t l1 = amx_bf16(v[2 * e + 1] - __uint_as_float((uint32_t)h1 << 16));
+            h[e] = h0 | ((uint32_t)h1 << 16);
+            lo[e] = l0 | ((uint32_t)l1 << 16);
+        }
+        aop[ct][st][0][l] = make_uint4(h[0], h[1], h[2], h[3]);
+        aop[ct][st][1][l] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+    }
+    if (threadIdx.x >= NT - kAmxC) {
         // decision bias, as k_cent_prep: fl32(-0.5 seqfma(c, c)) for k-means,
         // 0 for co-clustering, -inf for unused slots; a norm upper bound
-        const int c = threadIdx.x;
+        const int c = threadIdx.x - (NT - kAmxC);
         float acc = 0.f;
+#pragma unroll 8
         for (int k = 0; k < D; ++k) acc = __builtin_fmaf(cs[c * ROW + k], cs[c * ROW + k], acc);
-        sb[c] = c < C ? (kmeans ? -0.5f * acc : 0.f) : -INFINITY;
-        sn[c] = sqrtf(acc) * (1.0f + 1.0f / 1024.0f);
-    }
-
-    // B operand (x^T) of the wave's 32 tokens: lane (r32, hf) holds channels
-    // 16 st + 8 hf .. + 7 of token r32, for st = 0 .. D/16 - 1
-    amx_bf16x8 xf[D / 16];
-    float nx;
-    {
-        const int t = min(tok0 + r32, N - 1);
-        const uint4* row = reinterpret_cast<const uint4*>(Xh + (int64_t)t * D);
-        float ss = 0.f;
-#pragma unroll
-        for (int st = 0; st < D / 16; ++st) {
-            const uint4 v = row[2 * st + hf];
-            xf[st] = __builtin_bit_cast(amx_bf16x8, v);
-            const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const float a = __uint_as_float(w[e] << 16), b = __uint_as_float(w[e] & 0xffff0000u);
-                ss = __builtin_fmaf(a, a, ss);
-                ss = __builtin_fmaf(b, b, ss);
-            }
-        }
-        ss += __shfl_xor(ss, 32, 64);
-        nx = sqrtf(ss) * (1.0f + 1.0f / 1024.0f);
+        const float b = c < C ? (kmeans ? -0.5f * acc : 0.f) : -INFINITY;
+        sb[c] = b;
+        sbl[c] = c < C ? b - kAmxEps * fabsf(b) : -INFINITY;
+        sbh[c] = c < C ? b + kAmxEps * fabsf(b) : -INFINITY;
+        sn[c] = sqrtf(acc + kAmxTiny) * (1.0f + 1.0f / 1024.0f);
     }
     __syncthreads();
 
-    amx_f32x16 acc[2] = {amx_f32x16{}, amx_f32x16{}};
+    const int ngr = (N + 31) / 32;
+    for (int g = blockIdx.x * kAmxWaves + wave; g < ngr; g += gridDim.x * kAmxWaves) {
+        const int tok0 = g * 32;
+        // B operand (x^T) of the group's 32 tokens: lane (r32, hf) holds
+        // channels 16 st + 8 hf .. + 7 of token r32, for st = 0 .. NST - 1
+        amx_bf16x8 xf[NST];
+        {
+            const int t = min(tok0 + r32, N - 1);
+            const uint4* row = reinterpret_cast<const uint4*>(Xh + (int64_t)t * D);
 #pragma unroll
-    for (int st = 0; st < D / 16; ++st) {
+            for (int st = 0; st < NST; ++st) xf[st] = __builtin_bit_cast(amx_bf16x8, row[2 * st + hf]);
+        }
+        amx_f32x16 acc[2] = {amx_f32x16{}, amx_f32x16{}};
+#pragma unroll
+        for (int st = 0; st < NST; ++st) {
+#pragma unroll
+            for (int ct = 0; ct < 2; ++ct) {
+                if (ct >= nct) break;
+                const amx_bf16x8 ah = __builtin_bit_cast(amx_bf16x8, aop[ct][st][0][lane]);
+                const amx_bf16x8 al = __builtin_bit_cast(amx_bf16x8, aop[ct][st][1][lane]);
+                acc[ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, xf[st], acc[ct], 0, 0, 0);
+                acc[ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, xf[st], acc[ct], 0, 0, 0);
+            }
+        }
+        // the token's norm bound (two-term dot products: only the bound reads
+        // it, and the 2^-10 factor covers their rounding)
+        float ss = 0.f;
+#pragma unroll
+        for (int st = 0; st < NST; ++st) {
+            const uint4 v = __builtin_bit_cast(uint4, xf[st]);
+            const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const amx_bf16x2 p = __builtin_bit_cast(amx_bf16x2, w[e]);
+                ss = __builtin_amdgcn_fdot2_f32_bf16(p, p, ss, false);
+            }
+        }
+        ss = amx_pair_take<0>(ss) + amx_pair_take<1>(ss);
+        const float enx = kAmxEps * (sqrtf(ss + kAmxTiny) * (1.0f + 1.0f / 1024.0f));
+
+        // element r of tile ct: centroid ct*32 + 8 (r / 4) + 4 hf + r % 4, token r32.
+        // The token's best lower bound, then the mask of its candidates.
+        float thr = -INFINITY;
 #pragma unroll
         for (int ct = 0; ct < 2; ++ct) {
             if (ct >= nct) break;
-            const float* cr = cs + (ct * 32 + r32) * ROW + 16 * st + 8 * hf;
-            float v[8];
-            *reinterpret_cast<float4*>(v) = *reinterpret_cast<const float4*>(cr);
-            *reinterpret_cast<float4*>(v + 4) = *reinterpret_cast<const float4*>(cr + 4);
-            uint32_t h[4], l[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int c0 = ct * 32 + 8 * q + 4 * hf;
+                const float4 bl = *reinterpret_cast<const float4*>(sbl + c0);
+                const float4 nn = *reinterpret_cast<const float4*>(sn + c0);
+                thr = fmaxf(thr, __builtin_fmaf(-enx, nn.x, acc[ct][4 * q + 0] + bl.x));
+                thr = fmaxf(thr, __builtin_fmaf(-enx, nn.y, acc[ct][4 * q + 1] + bl.y));
+                thr = fmaxf(thr, __builtin_fmaf(-enx, nn.z, acc[ct][4 * q + 2] + bl.z));
+                thr = fmaxf(thr, __builtin_fmaf(-enx, nn.w, acc[ct][4 * q + 3] + bl.w));
+            }
+        }
+        thr = fmaxf(amx_pair_take<0>(thr), amx_pair_take<1>(thr));
+        // unused slots have -inf bounds and never pass (thr is finite)
+        uint32_t cm[2] = {0u, 0u};
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) {
+            if (ct >= nct) break;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int c0 = ct * 32 + 8 * q + 4 * hf;
+                const float4 bu = *reinterpret_cast<const float4*>(sbh + c0);
+                const float4 nn = *reinterpret_cast<const float4*>(sn + c0);
+                const float u[4] = {__builtin_fmaf(enx, nn.x, acc[ct][4 * q + 0] + bu.x),
+                                    __builtin_fmaf(enx, nn.y, acc[ct][4 * q + 1] + bu.y),
+                                    __builtin_fmaf(enx, nn.z, acc[ct][4 * q + 2] + bu.z),
+                                    __builtin_fmaf(enx, nn.w, acc[ct][4 * q + 3] + bu.w)};
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (u[e] >= thr) cm[ct] |= 1u << (8 * q + 4 * hf + e);
+            }
+        }
+        // both lanes of the token take the union of their halves' masks
+        uint64_t cand = 0;
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) {
+            const float m = __uint_as_float(cm[ct]);
+            const uint32_t both = __float_as_uint(amx_pair_take<0>(m)) | __float_as_uint(amx_pair_take<1>(m));
+            cand |= (uint64_t)both << (32 * ct);
+        }
+
+        // the token's channels as fp32 (exact)
+        float xu[NST][8];
+#pragma unroll
+        for (int st = 0; st < NST; ++st) {
+            const uint4 v = __builtin_bit_cast(uint4, xf[st]);
+            const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const uint16_t h0 = amx_bf16(v[2 * e]), h1 = amx_bf16(v[2 * e + 1]);
-                const uint16_t l0 = amx_bf16(v[2 * e] - __uint_as_float((uint32_t)h0 << 16));
-                const uint16_t l1 = amx_bf16(v[2 * e + 1] - __uint_as_float((uint32_t)h1 << 16));
-                h[e] = h0 | ((uint32_t)h1 << 16);
-                l[e] = l0 | ((uint32_t)l1 << 16);
+                xu[st][2 * e] = __uint_as_float(w[e] << 16);
+                xu[st][2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
             }
-            const amx_bf16x8 ah = __builtin_bit_cast(amx_bf16x8, make_uint4(h[0], h[1], h[2], h[3]));
-            const amx_bf16x8 al = __builtin_bit_cast(amx_bf16x8, make_uint4(l[0], l[1], l[2], l[3]));
-            acc[ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, xf[st], acc[ct], 0, 0, 0);
-            acc[ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, xf[st], acc[ct], 0, 0, 0);
         }
-    }
 
-    // element r of tile ct: centroid ct*32 + 8 (r / 4) + 4 hf + r % 4, token r32.
-    // The token's best lower bound, then the mask of its candidates.
-    float thr = -INFINITY;
+        // Exact decision arithmetic for the candidates, in ascending centroid
+        // order: the token's two lanes run the chain over the channels in order,
+        // 8 channels at a time, handing the partial sum across (lane hf = 0 holds
+        // channel groups 0, 2, 4, ...; hf = 1 groups 1, 3, 5, ...).
+        float best = -INFINITY;
+        int arg = 0;
+        for (;;) {
+            const uint64_t any = __ballot(cand != 0);
+            if (any == 0) break;
+            const bool act = cand != 0;
+            const int c = act ? __ffsll((long long)cand) - 1 : 0;
+            if (act) cand &= cand - 1;
+            const float* cr = cs + c * ROW + 8 * hf;
+            float a = 0.f;
 #pragma unroll
-    for (int ct = 0; ct < 2; ++ct) {
-        if (ct >= nct) break;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int c = ct * 32 + 8 * (r / 4) + 4 * hf + (r % 4);
-            const float b = sb[c];
-            thr = fmaxf(thr, (acc[ct][r] + b) - kAmxEps * (nx * sn[c] + fabsf(b)));
-        }
-    }
-    thr = fmaxf(thr, __shfl_xor(thr, 32, 64));
-    uint64_t cand = 0;
-#pragma unroll
-    for (int ct = 0; ct < 2; ++ct) {
-        if (ct >= nct) break;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int c = ct * 32 + 8 * (r / 4) + 4 * hf + (r % 4);
-            const float b = sb[c];
-            const float hi = (acc[ct][r] + b) + kAmxEps * (nx * sn[c] + fabsf(b));
-            if (c < C && hi >= thr) cand |= 1ull << c;
-        }
-    }
-    cand |= __shfl_xor(cand, 32, 64);
-
-    // Exact decision arithmetic for the candidates, in ascending centroid
-    // order: the token's two lanes run the chain over the channels in order,
-    // 8 channels at a time, handing the partial sum across (lane hf = 0 holds
-    // channel groups 0, 2, 4, ...; hf = 1 groups 1, 3, 5, ...).
-    float best = -INFINITY;
-    int arg = 0;
-    for (;;) {
-        const uint64_t any = __ballot(cand != 0);
-        if (any == 0) break;
-        const bool act = cand != 0;
-        const int c = act ? __ffsll((long long)cand) - 1 : 0;
-        if (act) cand &= cand - 1;
-        const float* cr = cs + c * ROW + 8 * hf;
-        float a = 0.f;
-#pragma unroll
-        for (int st = 0; st < D / 16; ++st) {
-            const uint4 xv = __builtin_bit_cast(uint4, xf[st]);
-            const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
-            const float4 c0 = *reinterpret_cast<const float4*>(cr + 16 * st);
-            const float4 c1 = *reinterpret_cast<const float4*>(cr + 16 * st + 4);
-            const float cc[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
-            // group 2 st (lane hf = 0), then group 2 st + 1 (lane hf = 1)
-#pragma unroll
-            for (int half = 0; half < 2; ++half) {
+            for (int st = 0; st < NST; ++st) {
+                const float4 c0 = *reinterpret_cast<const float4*>(cr + 16 * st);
+                const float4 c1 = *reinterpret_cast<const float4*>(cr + 16 * st + 4);
+                const float cc[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+                // channels 16 st .. + 7 (lane hf = 0), then 16 st + 8 .. + 15 (hf = 1)
                 float t = a;
-                if (hf == half) {
+                if (hf == 0) {
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        t = __builtin_fmaf(__uint_as_float(xw[e] << 16), cc[2 * e], t);
-                        t = __builtin_fmaf(__uint_as_float(xw[e] & 0xffff0000u), cc[2 * e + 1], t);
-                    }
+                    for (int e = 0; e < 8; ++e) t = __builtin_fmaf(xu[st][e], cc[e], t);
                 }
-                // both lanes take the sum of the lane that just worked
-                const float o = __shfl_xor(t, 32, 64);
-                a = hf == half ? t : o;
+                a = amx_pair_take<0>(t);
+                t = a;
+                if (hf == 1) {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) t = __builtin_fmaf(xu[st][e], cc[e], t);
+                }
+                a = amx_pair_take<1>(t);
+            }
+            if (act) {
+                const float sc = a + sb[c];
+                if (sc > best) {
+                    best = sc;
+                    arg = c;
+                }
             }
         }
-        if (act) {
-            const float sc = a + sb[c];
-            if (sc > best) {
-                best = sc;
-                arg = c;
-            }
-        }
+        const int t = tok0 + r32;
+        if (hf == 0 && t < N) assign[bh * N + t] = arg;
     }
-    const int t = tok0 + r32;
-    if (hf == 0 && t < N) assign[bh * N + t] = arg;
 }
 
 // ----------------------------------------------------------------------------
@@ -877,8 +938,17 @@ sa_status assign_side(const Geometry& g, int C, char* ws, const ClusterWs& w, in
                       const uint16_t* X, const float* cent, int kmeans, hipStream_t st) {
     int32_t* assign = reinterpret_cast<int32_t*>(ws + w.assign[s]);
     if (C <= kAmxC) {
-        hipLaunchKernelGGL((k_assign_mx<D>), dim3((unsigned)ceil_div(g.N, 128), (unsigned)g.BH()),
-                           dim3(256), 0, st, X, cent, assign, g.N, C, kmeans);
+        // one resident round of workgroups, spread over the heads; each
+        // stages its head's centroids once and serves many token groups
+        int resident = 0;
+        sa_status e = resident_workgroups(reinterpret_cast<const void*>(&k_assign_mx<D>),
+                                          64 * kAmxWaves, 0, &resident);
+        if (e != SA_OK) return e;
+        const int64_t groups = ceil_div(g.N, 32);
+        const int64_t per_head = std::max<int64_t>(1, resident / std::max<int64_t>(1, g.BH()));
+        const unsigned gx = (unsigned)std::min(per_head, ceil_div(groups, kAmxWaves));
+        hipLaunchKernelGGL((k_assign_mx<D>), dim3(gx, (unsigned)g.BH()), dim3(64 * kAmxWaves), 0, st,
+                           X, cent, assign, g.N, C, kmeans);
         return hip_check(hipGetLastError(), "k_assign_mx launch");
     }
     float* centT = reinterpret_cast<float*>(ws + w.centT);
