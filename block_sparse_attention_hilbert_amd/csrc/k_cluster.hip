@@ -10,11 +10,17 @@
 //                   each dot product a sequential fp32 FMA chain over the
 //                   channels, ties to the lower index -- the integer decision
 //                   is taken in one fixed arithmetic
+//   k_sum_assigned, k_clmean (C <= 64)
+//                   cluster means without sorting: k_assign_mx (and, for the
+//                   initial partition, k_sum_assigned) leave per-workgroup
+//                   exact fp64 cluster sums, k_clmean adds them up; an empty
+//                   cluster keeps its previous centroid
 //   k_hist, k_hist_scan, k_sort_scatter
 //                   stable counting sort of the tokens by cluster (tiles of
-//                   1024 tokens; LDS bitonic sort inside a tile)
-//   k_segmean       cluster means from exact fp64 sums (an empty cluster keeps
-//                   its previous centroid)
+//                   1024 tokens; LDS bitonic sort inside a tile): every round
+//                   for C > 64, once at the end otherwise
+//   k_segmean       cluster means from exact fp64 sums over the sorted order
+//                   (rounds with C > 64, value means, tile partitions)
 //   k_layout        the padded layout: each cluster takes whole blocks
 //                   (its tokens in ascending order, then padding); per-block
 //                   cluster and token count
@@ -155,7 +161,8 @@ typedef float amx_f32x16 __attribute__((ext_vector_type(16)));
 typedef __bf16 amx_bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kAmxC = 64;                  // centroid slots (C <= 64)
-constexpr int kAmxWaves = 8;               // waves per workgroup
+constexpr int kAmxWaves = 16;              // waves per workgroup
+constexpr int kAmxWgTarget = 256;          // workgroups per launch, over all heads
 constexpr float kAmxEps = 1.0f / 4096.0f;  // bound factor 2^-12
 // added to both squared norms: it covers squares and products lost below the
 // fp32 / bf16 normal range (flushed or underflowed), so that the bound holds
@@ -175,10 +182,86 @@ __device__ __forceinline__ float amx_pair_take(float x) {
     return __uint_as_float(HALF == 0 ? r[0] : r[1]);
 }
 
+// Cluster sums without sorting.  A cluster mean is fl32(exact sum / n): the
+// fp64 sums of bf16 rows are exact, so they may be formed in any order.  Each
+// workgroup sums its tokens per cluster in LDS and writes one partial row per
+// cluster it touched; k_clmean adds the partials of a head.
+//
+// Adds the rows of tokens tok0 .. tok0 + 31 (those below N) to their
+// clusters' LDS sums; lane j < 32 holds the cluster of token tok0 + j.  Lane l
+// takes channels D/64 l .. of every row; a run of tokens of one cluster is
+// summed in registers and added to LDS when the cluster changes.
+template <int D>
+__device__ __forceinline__ void amx_accumulate(const uint16_t* __restrict__ Xh, int tok0, int N,
+                                               int cl, double* ssum, int* scnt, int lane) {
+    constexpr int CPL = D / 64;
+    static_assert(CPL == 1 || CPL == 2, "D is 64 or 128");
+    const int nt = min(32, N - tok0);
+    uint32_t v[32];                        // channel 2l | 2l+1 (D = 128), or channel l in the high half
+#pragma unroll
+    for (int j = 0; j < 32; ++j) {
+        const int64_t row = (int64_t)(tok0 + min(j, nt - 1)) * D;
+        if constexpr (CPL == 2)
+            v[j] = reinterpret_cast<const uint32_t*>(Xh + row)[lane];
+        else
+            v[j] = (uint32_t)Xh[row + lane] << 16;
+    }
+    auto flush = [&](int c, double a0, double a1, int run) {
+        __hip_atomic_fetch_add(ssum + c * D + CPL * lane, a0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        if constexpr (CPL == 2)
+            __hip_atomic_fetch_add(ssum + c * D + 2 * lane + 1, a1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        if (lane == 0) __hip_atomic_fetch_add(scnt + c, run, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    };
+    int cur = __builtin_amdgcn_readlane(cl, 0);
+    double a0 = 0.0, a1 = 0.0;
+    int run = 0;
+#pragma unroll
+    for (int j = 0; j < 32; ++j) {
+        if (j < nt) {
+            const int c = __builtin_amdgcn_readlane(cl, j);
+            if (c != cur) {
+                flush(cur, a0, a1, run);
+                cur = c;
+                a0 = a1 = 0.0;
+                run = 0;
+            }
+            if constexpr (CPL == 2) {
+                a0 += (double)__uint_as_float(v[j] << 16);
+                a1 += (double)__uint_as_float(v[j] & 0xffff0000u);
+            } else {
+                a0 += (double)__uint_as_float(v[j]);
+            }
+            ++run;
+        }
+    }
+    flush(cur, a0, a1, run);
+}
+
+// zeroes the workgroup's LDS sums (before the first accumulation)
+template <int D, int NT>
+__device__ __forceinline__ void amx_sums_clear(double* ssum, int* scnt) {
+    for (int p = threadIdx.x; p < kAmxC * D; p += NT) ssum[p] = 0.0;
+    for (int p = threadIdx.x; p < kAmxC; p += NT) scnt[p] = 0;
+}
+
+// writes the workgroup's partial sums: the count of every slot, the row of
+// every slot with tokens (k_clmean reads only those)
+template <int D, int NT>
+__device__ __forceinline__ void amx_sums_store(const double* ssum, const int* scnt,
+                                               double* __restrict__ psum,
+                                               int32_t* __restrict__ pcnt, int64_t part) {
+    __syncthreads();
+    for (int p = threadIdx.x; p < kAmxC * D; p += NT)
+        if (scnt[p / D] > 0) psum[part * kAmxC * D + p] = ssum[p];
+    for (int p = threadIdx.x; p < kAmxC; p += NT) pcnt[part * kAmxC + p] = scnt[p];
+}
+
 template <int D>
 __global__ __launch_bounds__(64 * kAmxWaves) __attribute__((amdgpu_waves_per_eu(4))) void k_assign_mx(const uint16_t* __restrict__ X,
                                                               const float* __restrict__ cent,
-                                                              int32_t* __restrict__ assign, int N,
+                                                              int32_t* __restrict__ assign,
+                                                              double* __restrict__ psum,
+                                                              int32_t* __restrict__ pcnt, int N,
                                                               int C, int kmeans) {
     constexpr int ROW = D + 4;                     // floats per centroid row in LDS
     constexpr int NST = D / 16;                    // k-steps of the matrix instruction
@@ -189,7 +272,9 @@ __global__ __launch_bounds__(64 * kAmxWaves) __attribute__((amdgpu_waves_per_eu(
     __shared__ __align__(16) float sbl[kAmxC];          // bias - its bound share
     __shared__ __align__(16) float sbh[kAmxC];          // bias + its bound share
     __shared__ __align__(16) float sn[kAmxC];           // norm upper bound
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    __shared__ double ssum[kAmxC * D];                  // cluster sums (fp64, exact)
+    __shared__ int scnt[kAmxC];                         // cluster token counts
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int r32 = lane & 31, hf = lane >> 5;
     const int64_t bh = blockIdx.y;
     const int nct = (C + 31) / 32;                 // centroid tiles
@@ -203,6 +288,7 @@ __global__ __launch_bounds__(64 * kAmxWaves) __attribute__((amdgpu_waves_per_eu(
             *reinterpret_cast<float4*>(cs + c * ROW + 4 * o) = v;
         }
     }
+    amx_sums_clear<D, NT>(ssum, scnt);
     __syncthreads();
     // A operand of lane l in tile ct, k-step st: centroid ct*32 + (l & 31),
     // channels 16 st + 8 (l >> 5) .. + 7, as bf16 hi and the bf16 of the rest
@@ -381,7 +467,65 @@ __global__ __launch_bounds__(64 * kAmxWaves) __attribute__((amdgpu_waves_per_eu(
         }
         const int t = tok0 + r32;
         if (hf == 0 && t < N) assign[bh * N + t] = arg;
+        amx_accumulate<D>(Xh, tok0, N, arg, ssum, scnt, lane);
     }
+    amx_sums_store<D, NT>(ssum, scnt, psum, pcnt, bh * gridDim.x + blockIdx.x);
+}
+
+// the cluster sums of a given assignment (the initial partition)
+template <int D>
+__global__ __launch_bounds__(64 * kAmxWaves) void k_sum_assigned(const uint16_t* __restrict__ X,
+                                                                 const int32_t* __restrict__ assign,
+                                                                 double* __restrict__ psum,
+                                                                 int32_t* __restrict__ pcnt, int N) {
+    constexpr int NT = 64 * kAmxWaves;
+    __shared__ double ssum[kAmxC * D];
+    __shared__ int scnt[kAmxC];
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    const int64_t bh = blockIdx.y;
+    const uint16_t* Xh = X + bh * (int64_t)N * D;
+    amx_sums_clear<D, NT>(ssum, scnt);
+    __syncthreads();
+    const int ngr = (N + 31) / 32;
+    for (int g = blockIdx.x * kAmxWaves + wave; g < ngr; g += gridDim.x * kAmxWaves) {
+        const int tok0 = g * 32;
+        const int t = tok0 + (lane & 31);
+        const int cl = t < N ? assign[bh * N + t] : 0;
+        amx_accumulate<D>(Xh, tok0, N, cl, ssum, scnt, lane);
+    }
+    amx_sums_store<D, NT>(ssum, scnt, psum, pcnt, bh * gridDim.x + blockIdx.x);
+}
+
+// cluster means from the partial sums of G <= kAmxWgTarget workgroups per
+// head; an empty cluster keeps its previous centroid
+template <int D>
+__global__ __launch_bounds__(D) void k_clmean(const double* __restrict__ psum,
+                                              const int32_t* __restrict__ pcnt, int G,
+                                              float* __restrict__ cent, int32_t* __restrict__ count,
+                                              int C) {
+    __shared__ int pc[kAmxWgTarget];
+    const int c = blockIdx.x, tid = threadIdx.x;
+    const int64_t p0 = (int64_t)blockIdx.y * G;
+    for (int g = tid; g < G; g += D) pc[g] = pcnt[(p0 + g) * kAmxC + c];
+    __syncthreads();
+    int n = 0;
+    for (int g = 0; g < G; ++g) n += pc[g];
+    if (tid == 0) count[blockIdx.y * C + c] = n;
+    if (n == 0) return;
+    // eight partial rows in flight at a time (the sums are exact: any order)
+    const double* col = psum + (p0 * kAmxC + c) * D + tid;
+    double s = 0.0;
+    int g = 0;
+    for (; g + 8 <= G; g += 8) {
+        double t[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) t[u] = pc[g + u] > 0 ? col[(int64_t)(g + u) * kAmxC * D] : 0.0;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) s += t[u];
+    }
+    for (; g < G; ++g)
+        if (pc[g] > 0) s += col[(int64_t)g * kAmxC * D];
+    cent[((int64_t)blockIdx.y * C + c) * D + tid] = (float)(s / (double)n);
 }
 
 // ----------------------------------------------------------------------------
@@ -878,12 +1022,28 @@ __global__ void k_block_comp(const float* __restrict__ k_cent, const float* __re
 // host side
 // ----------------------------------------------------------------------------
 struct ClusterWs {
-    size_t assign[2], sorted[2], hist, off, cstart[2], centT, bias, total;
+    size_t assign[2], sorted[2], hist, off, cstart[2], centT, bias, psum, pcnt, total;
 };
 
 inline int padded_c(int C) { return (C + kAsgIlp - 1) / kAsgIlp * kAsgIlp; }
 
-ClusterWs cluster_ws(const Geometry& g, int C) {
+// workgroups per head of k_assign_mx (about one per CU over all heads: its
+// LDS holds one per CU) or of k_sum_assigned (two per CU), at least 16 token
+// groups each; never more than kAmxWgTarget
+inline int amx_wg_per_head(const Geometry& g, bool sum_only = false) {
+    const int64_t groups = ceil_div(g.N, 32);
+    const int64_t wgs = sum_only ? 2 * kAmxWgTarget : kAmxWgTarget;
+    const int64_t target = std::max<int64_t>(1, wgs / std::max<int64_t>(1, g.BH()));
+    return (int)std::min<int64_t>({target, ceil_div(groups, kAmxWaves), (int64_t)kAmxWgTarget});
+}
+
+// the rounds form their means from unsorted partial sums (C <= 64)
+inline bool fused_means(const sa_cluster_spec& cs) {
+    return cs.mode != SA_CLUSTER_TILES && cs.n_clusters <= kAmxC;
+}
+
+ClusterWs cluster_ws(const Geometry& g, const sa_cluster_spec& cs) {
+    const int C = cs.n_clusters;
     ClusterWs w{};
     const int64_t ntiles = ceil_div(g.N, kTok);
     size_t o = 0;
@@ -896,6 +1056,11 @@ ClusterWs cluster_ws(const Geometry& g, int C) {
     w.off = o; o = align_up(o + (size_t)g.BH() * ntiles * C * 4, 256);
     w.centT = o; o = align_up(o + (size_t)g.BH() * g.d * padded_c(C) * 4, 256);
     w.bias = o; o = align_up(o + (size_t)g.BH() * padded_c(C) * 4, 256);
+    if (fused_means(cs)) {
+        const size_t parts = (size_t)g.BH() * std::max(amx_wg_per_head(g), amx_wg_per_head(g, true));
+        w.psum = o; o = align_up(o + parts * kAmxC * g.d * 8, 256);
+        w.pcnt = o; o = align_up(o + parts * kAmxC * 4, 256);
+    }
     w.total = o;
     return w;
 }
@@ -909,11 +1074,9 @@ sa_status segmean(const Geometry& g, int C, const uint16_t* X, const int32_t* so
     return hip_check(hipGetLastError(), "k_segmean launch");
 }
 
-// sorts side s by its assignment and refreshes its centroids
-template <int D>
-sa_status sort_and_mean(const Geometry& g, int C, char* ws, const ClusterWs& w, int s,
-                        const uint16_t* X, int32_t* count, float* cent, hipStream_t st,
-                        int zero_empty = 0) {
+// sorts side s by its assignment (sorted order, counts, cluster starts)
+sa_status sort_side(const Geometry& g, int C, char* ws, const ClusterWs& w, int s, int32_t* count,
+                    hipStream_t st) {
     const int ntiles = (int)ceil_div(g.N, kTok);
     const int32_t* assign = reinterpret_cast<const int32_t*>(ws + w.assign[s]);
     int32_t* sorted = reinterpret_cast<int32_t*>(ws + w.sorted[s]);
@@ -929,8 +1092,43 @@ sa_status sort_and_mean(const Geometry& g, int C, char* ws, const ClusterWs& w, 
     if ((e = hip_check(hipGetLastError(), "k_hist_scan launch")) != SA_OK) return e;
     hipLaunchKernelGGL(k_sort_scatter, dim3(ntiles, (unsigned)g.BH()), dim3(kTok), 0, st, assign,
                        off, sorted, g.N, C, ntiles);
-    if ((e = hip_check(hipGetLastError(), "k_sort_scatter launch")) != SA_OK) return e;
-    return segmean<D>(g, C, X, sorted, count, cstart, cent, st, zero_empty);
+    return hip_check(hipGetLastError(), "k_sort_scatter launch");
+}
+
+// sorts side s by its assignment and refreshes its centroids
+template <int D>
+sa_status sort_and_mean(const Geometry& g, int C, char* ws, const ClusterWs& w, int s,
+                        const uint16_t* X, int32_t* count, float* cent, hipStream_t st,
+                        int zero_empty = 0) {
+    sa_status e = sort_side(g, C, ws, w, s, count, st);
+    if (e != SA_OK) return e;
+    return segmean<D>(g, C, X, reinterpret_cast<const int32_t*>(ws + w.sorted[s]), count,
+                      reinterpret_cast<const int32_t*>(ws + w.cstart[s]), cent, st, zero_empty);
+}
+
+// means of side s from the partial sums of the last assignment (C <= 64)
+template <int D>
+sa_status partial_means(const Geometry& g, int C, char* ws, const ClusterWs& w, int32_t* count,
+                        float* cent, hipStream_t st, bool sum_only = false) {
+    hipLaunchKernelGGL((k_clmean<D>), dim3((unsigned)C, (unsigned)g.BH()), dim3(D), 0, st,
+                       reinterpret_cast<const double*>(ws + w.psum),
+                       reinterpret_cast<const int32_t*>(ws + w.pcnt), amx_wg_per_head(g, sum_only), cent,
+                       count, C);
+    return hip_check(hipGetLastError(), "k_clmean launch");
+}
+
+// means of the assignment already in side s's workspace (C <= 64)
+template <int D>
+sa_status assigned_means(const Geometry& g, int C, char* ws, const ClusterWs& w, int s,
+                         const uint16_t* X, int32_t* count, float* cent, hipStream_t st) {
+    hipLaunchKernelGGL((k_sum_assigned<D>), dim3((unsigned)amx_wg_per_head(g, true), (unsigned)g.BH()),
+                       dim3(64 * kAmxWaves), 0, st, X,
+                       reinterpret_cast<const int32_t*>(ws + w.assign[s]),
+                       reinterpret_cast<double*>(ws + w.psum), reinterpret_cast<int32_t*>(ws + w.pcnt),
+                       g.N);
+    sa_status e = hip_check(hipGetLastError(), "k_sum_assigned launch");
+    if (e != SA_OK) return e;
+    return partial_means<D>(g, C, ws, w, count, cent, st, true);
 }
 
 template <int D>
@@ -938,17 +1136,13 @@ sa_status assign_side(const Geometry& g, int C, char* ws, const ClusterWs& w, in
                       const uint16_t* X, const float* cent, int kmeans, hipStream_t st) {
     int32_t* assign = reinterpret_cast<int32_t*>(ws + w.assign[s]);
     if (C <= kAmxC) {
-        // one resident round of workgroups, spread over the heads; each
-        // stages its head's centroids once and serves many token groups
-        int resident = 0;
-        sa_status e = resident_workgroups(reinterpret_cast<const void*>(&k_assign_mx<D>),
-                                          64 * kAmxWaves, 0, &resident);
-        if (e != SA_OK) return e;
-        const int64_t groups = ceil_div(g.N, 32);
-        const int64_t per_head = std::max<int64_t>(1, resident / std::max<int64_t>(1, g.BH()));
-        const unsigned gx = (unsigned)std::min(per_head, ceil_div(groups, kAmxWaves));
-        hipLaunchKernelGGL((k_assign_mx<D>), dim3(gx, (unsigned)g.BH()), dim3(64 * kAmxWaves), 0, st,
-                           X, cent, assign, g.N, C, kmeans);
+        // about one workgroup per CU, spread over the heads; each stages its
+        // head's centroids once, serves many token groups and leaves the
+        // partial cluster sums of its tokens
+        hipLaunchKernelGGL((k_assign_mx<D>), dim3((unsigned)amx_wg_per_head(g), (unsigned)g.BH()),
+                           dim3(64 * kAmxWaves), 0, st, X, cent, assign,
+                           reinterpret_cast<double*>(ws + w.psum),
+                           reinterpret_cast<int32_t*>(ws + w.pcnt), g.N, C, kmeans);
         return hip_check(hipGetLastError(), "k_assign_mx launch");
     }
     float* centT = reinterpret_cast<float*>(ws + w.centT);
@@ -967,7 +1161,8 @@ template <int D>
 sa_status cluster_t(const Geometry& g, const sa_cluster_spec& cs, const uint16_t* Q,
                     const uint16_t* K, const uint16_t* V, ClusterOut o, char* ws, hipStream_t st) {
     const int C = cs.n_clusters;
-    const ClusterWs w = cluster_ws(g, C);
+    const ClusterWs w = cluster_ws(g, cs);
+    const bool fused = fused_means(cs);
     sa_status e;
     if (cs.mode == SA_CLUSTER_TILES) {
         // the partition is geometric: the tiles of each head's chosen shape,
@@ -985,28 +1180,38 @@ sa_status cluster_t(const Geometry& g, const sa_cluster_spec& cs, const uint16_t
         hipLaunchKernelGGL(k_chunk_assign, dim3((unsigned)ceil_div(g.N, 256), (unsigned)g.BH()),
                            dim3(256), 0, st, reinterpret_cast<int32_t*>(ws + w.assign[s]), g.N, C);
         if ((e = hip_check(hipGetLastError(), "k_chunk_assign launch")) != SA_OK) return e;
-        if ((e = sort_and_mean<D>(g, C, ws, w, s, s ? K : Q, s ? o.k_count : o.q_count,
-                                  s ? o.k_cent : o.q_cent, st)) != SA_OK)
-            return e;
+        e = fused ? assigned_means<D>(g, C, ws, w, s, s ? K : Q, s ? o.k_count : o.q_count,
+                                      s ? o.k_cent : o.q_cent, st)
+                  : sort_and_mean<D>(g, C, ws, w, s, s ? K : Q, s ? o.k_count : o.q_count,
+                                     s ? o.k_cent : o.q_cent, st);
+        if (e != SA_OK) return e;
     }
+    // a side's means after its assignment: from the partial sums the
+    // assignment left (C <= 64), else by sorting
+    auto means = [&](int s, const uint16_t* X, int32_t* count, float* cent) -> sa_status {
+        return fused ? partial_means<D>(g, C, ws, w, count, cent, st)
+                     : sort_and_mean<D>(g, C, ws, w, s, X, count, cent, st);
+    };
     for (int it = 0; it < (cs.mode == SA_CLUSTER_TILES ? 0 : cs.iters); ++it) {
         if (cs.mode == SA_CLUSTER_COCLUSTER) {
             // keys by affinity to the query centroids, then queries by affinity
             // to the refreshed key centroids
             if ((e = assign_side<D>(g, C, ws, w, 1, K, o.q_cent, 0, st)) != SA_OK) return e;
-            if ((e = sort_and_mean<D>(g, C, ws, w, 1, K, o.k_count, o.k_cent, st)) != SA_OK) return e;
+            if ((e = means(1, K, o.k_count, o.k_cent)) != SA_OK) return e;
             if ((e = assign_side<D>(g, C, ws, w, 0, Q, o.k_cent, 0, st)) != SA_OK) return e;
-            if ((e = sort_and_mean<D>(g, C, ws, w, 0, Q, o.q_count, o.q_cent, st)) != SA_OK) return e;
+            if ((e = means(0, Q, o.q_count, o.q_cent)) != SA_OK) return e;
         } else {
             for (int s = 0; s < 2; ++s) {
                 const uint16_t* X = s ? K : Q;
                 float* cent = s ? o.k_cent : o.q_cent;
                 if ((e = assign_side<D>(g, C, ws, w, s, X, cent, 1, st)) != SA_OK) return e;
-                if ((e = sort_and_mean<D>(g, C, ws, w, s, X, s ? o.k_count : o.q_count, cent, st)) != SA_OK)
-                    return e;
+                if ((e = means(s, X, s ? o.k_count : o.q_count, cent)) != SA_OK) return e;
             }
         }
     }
+    // the final partition in sorted order (the layout and the value means read it)
+    for (int s = 0; s < 2 && fused; ++s)
+        if ((e = sort_side(g, C, ws, w, s, s ? o.k_count : o.q_count, st)) != SA_OK) return e;
     if (o.v_cent) {
         if ((e = segmean<D>(g, C, V, reinterpret_cast<const int32_t*>(ws + w.sorted[1]), o.k_count,
                             reinterpret_cast<const int32_t*>(ws + w.cstart[1]), o.v_cent, st,
@@ -1035,7 +1240,7 @@ int padded_block_count(const Geometry& g, const sa_cluster_spec& cs) {
 }
 
 size_t cluster_workspace_bytes(const Geometry& g, const sa_cluster_spec& cs) {
-    const size_t a = cluster_ws(g, cs.n_clusters).total;
+    const size_t a = cluster_ws(g, cs).total;
     if (cs.mode != SA_CLUSTER_TILES) return a;
     const size_t b = sics_workspace_bytes(g, cs);     // sparse_attn_sics shares the buffer
     return a > b ? a : b;
