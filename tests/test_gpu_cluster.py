@@ -73,6 +73,15 @@ SMALL = {
         T=5, Hg=9, W=29, H=4, d=64, cluster="tiles", aniso=True,
         tile_shapes=((1, 4, 32), (1, 8, 16), (2, 4, 16), (5, 3, 8)), n_clusters=20,
         mass=0.8, comp=True, diag=True),
+    # 64 clusters (the most the matrix-core assignment and the partial-sum
+    # means take) on a few hundred tokens: small and empty clusters, both
+    # centroid tiles, both head dims
+    "kmeans_c64_mass_comp_d64_iid": W.WORKLOADS[1].replace(T=3, Hg=10, W=13, H=2, d=64,
+                                                         cluster="kmeans", n_clusters=64,
+                                                         cluster_iters=3, rule="mass", mass=0.8,
+                                                         diag=False, comp=True, topk=None),
+    "cocluster_c64_topk_d128": BASE.replace(cluster="cocluster", n_clusters=64, cluster_iters=3,
+                                            rule="topk", density=0.3),
     # more than 64 clusters: the assignment's vector-unit path
     "kmeans_c100_mass_comp": BASE.replace(block=64, cluster="kmeans", n_clusters=100,
                                           cluster_iters=2, mass=0.9, comp=True),
