@@ -898,16 +898,32 @@ __global__ __launch_bounds__(kSelThreads) void k_cselect(CSelArgs a) {
     for (int r = tid; r < live; r += kSelThreads) ord[r] = (int32_t)(key[r] & 0xffffffffu);
     __syncthreads();
     if (a.rule == SA_RULE_TOPK) {
-        if (tid == 0) {
+        // the shortest rank prefix whose token count reaches the budget (all
+        // of them if none does): counts in rank order to LDS, then one wave
+        // scans them in 64 consecutive chunks (integer sums: exact in any order)
+        int64_t* wc = reinterpret_cast<int64_t*>(smem);        // the keys are dead
+        for (int r = tid; r < live; r += kSelThreads) wc[r] = nk[ord[r]];
+        __syncthreads();
+        if (tid < 64) {
             const int64_t budget = a.budget[h];
-            int64_t run = 0;
-            int m = 0;
-            while (m < live) {
-                run += nk[ord[m]];
-                ++m;
-                if (run >= budget) break;
+            const int per = (live + 63) / 64;
+            const int r0 = min(tid * per, live), r1 = min(r0 + per, live);
+            int64_t own = 0;
+            for (int r = r0; r < r1; ++r) own += wc[r];
+            // exclusive prefix of the chunk sums over the lanes
+            int64_t incl = own;
+            for (int off = 1; off < 64; off <<= 1) {
+                const int64_t o = __shfl_up(incl, off, 64);
+                if (tid >= off) incl += o;
             }
-            s_cut = m;
+            int64_t run = incl - own;
+            int m = live;
+            for (int r = r0; r < r1; ++r) {
+                run += wc[r];
+                if (run >= budget) { m = r + 1; break; }
+            }
+            for (int off = 32; off > 0; off >>= 1) m = min(m, __shfl_xor(m, off, 64));
+            if (tid == 0) s_cut = m;
         }
     } else {
         // weight n_b exp(S_b - S_max) in fp64, summed sequentially in rank order
