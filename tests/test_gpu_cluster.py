@@ -370,3 +370,30 @@ def test_partition_reuse_across_steps(name):
         assert e.max() <= ATOL_MAX and e.mean() <= ATOL_MEAN and le.max() <= LSE_ATOL
     log(f"[cluster-reuse] {name}: tokens a fresh clustering would move: {moved}")
     assert moved > 0
+
+
+@pytest.mark.parametrize("name", ["wan13b_cocluster", "wan13b_kmeans_comp"])
+def test_full_size_cluster_runs_are_bitwise_identical(name):
+    """Two clustered calls on the same inputs give the same bits.  The cluster
+    sums are added up in LDS and across workgroups in an order that changes
+    from launch to launch; they are exact, so the centroids, the partition,
+    the keep lists and the output may not change."""
+    wl = W.by_name(name)
+    log(f"[cluster-det] {name}: N={wl.N} H={wl.H} C={wl.n_clusters}")
+    pipe = _pipe(wl)
+    Q, K, V = W.make_qkv(wl)
+    Qd, Kd, Vd = to_dev(Q), to_dev(K), to_dev(V)
+    runs = []
+    for _ in range(2):
+        poison(pipe.O, pipe.lse)
+        O = pipe(Qd, Kd, Vd, reuse=False)
+        torch.cuda.synchronize()
+        cl = pipe.cl
+        runs.append([from_dev(O).copy(), pipe.lse.cpu().numpy().view(np.uint32).copy()] +
+                    [getattr(cl, f).cpu().numpy().copy() for f in
+                     ("q_order", "k_order", "q_cnt", "k_cnt", "q_count", "k_count")] +
+                    [getattr(cl, f).cpu().numpy().view(np.uint32).copy() for f in ("q_cent", "k_cent")] +
+                    [pipe.sel.row_ptr.cpu().numpy().copy(), pipe.sel.col_idx.cpu().numpy().copy()])
+    for k, (a, b) in enumerate(zip(*runs)):
+        assert np.array_equal(a, b), f"output {k} differs between two identical calls"
+    log(f"[cluster-det] {name}: identical")
