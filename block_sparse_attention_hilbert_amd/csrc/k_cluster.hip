@@ -10,11 +10,11 @@
 //                   each dot product a sequential fp32 FMA chain over the
 //                   channels, ties to the lower index -- the integer decision
 //                   is taken in one fixed arithmetic
-//   k_sum_assigned, k_clmean (C <= 64)
-//                   cluster means without sorting: k_assign_mx (and, for the
-//                   initial partition, k_sum_assigned) leave per-workgroup
-//                   exact fp64 cluster sums, k_clmean adds them up; an empty
-//                   cluster keeps its previous centroid
+//   k_chunkmean, k_clmean (C <= 64)
+//                   cluster means without sorting: the initial chunks' means
+//                   from contiguous rows; in every round k_assign_mx leaves
+//                   per-workgroup exact fp64 cluster sums and k_clmean adds
+//                   them up (an empty cluster keeps its previous centroid)
 //   k_hist, k_hist_scan, k_sort_scatter
 //                   stable counting sort of the tokens by cluster (tiles of
 //                   1024 tokens; LDS bitonic sort inside a tile): every round
@@ -472,30 +472,6 @@ __global__ __launch_bounds__(64 * kAmxWaves) __attribute__((amdgpu_waves_per_eu(
     amx_sums_store<D, NT>(ssum, scnt, psum, pcnt, bh * gridDim.x + blockIdx.x);
 }
 
-// the cluster sums of a given assignment (the initial partition)
-template <int D>
-__global__ __launch_bounds__(64 * kAmxWaves) void k_sum_assigned(const uint16_t* __restrict__ X,
-                                                                 const int32_t* __restrict__ assign,
-                                                                 double* __restrict__ psum,
-                                                                 int32_t* __restrict__ pcnt, int N) {
-    constexpr int NT = 64 * kAmxWaves;
-    __shared__ double ssum[kAmxC * D];
-    __shared__ int scnt[kAmxC];
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-    const int64_t bh = blockIdx.y;
-    const uint16_t* Xh = X + bh * (int64_t)N * D;
-    amx_sums_clear<D, NT>(ssum, scnt);
-    __syncthreads();
-    const int ngr = (N + 31) / 32;
-    for (int g = blockIdx.x * kAmxWaves + wave; g < ngr; g += gridDim.x * kAmxWaves) {
-        const int tok0 = g * 32;
-        const int t = tok0 + (lane & 31);
-        const int cl = t < N ? assign[bh * N + t] : 0;
-        amx_accumulate<D>(Xh, tok0, N, cl, ssum, scnt, lane);
-    }
-    amx_sums_store<D, NT>(ssum, scnt, psum, pcnt, bh * gridDim.x + blockIdx.x);
-}
-
 // cluster means from the partial sums of G <= kAmxWgTarget workgroups per
 // head; an empty cluster keeps its previous centroid
 template <int D>
@@ -617,6 +593,54 @@ __global__ __launch_bounds__(kTok) void k_sort_scatter(const int32_t* __restrict
     const int rank = tid - lo;
     const int dst = tile_off[(bh * ntiles + tile) * (int64_t)C + c] + rank;
     sorted[bh * N + dst] = tile * kTok + (int)(k & 1023u);
+}
+
+// ----------------------------------------------------------------------------
+// means and sizes of the initial partition: C equal chunks of the token order,
+// chunk c = tokens [floor(c N / C), floor((c + 1) N / C)) (C <= N: none empty);
+// exact fp64 sums of contiguous rows, one fp32 rounding
+// ----------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void k_chunkmean(const uint16_t* __restrict__ X,
+                                                   float* __restrict__ cent,
+                                                   int32_t* __restrict__ count, int N, int C) {
+    constexpr int CH = D / 8;                 // 16-byte chunks per row
+    constexpr int ST = 256 / CH;              // token streams
+    __shared__ double red[ST][D];
+    const int c = blockIdx.x;
+    const int64_t bh = blockIdx.y;
+    const int tid = threadIdx.x;
+    const int s0 = (int)((int64_t)c * N / C), n = (int)((int64_t)(c + 1) * N / C) - s0;
+    if (tid == 0) count[bh * C + c] = n;
+    const int ch = tid % CH, st = tid / CH;
+    const uint16_t* Xh = X + (bh * N + s0) * (int64_t)D + ch * 8;
+    double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    auto add = [&](uint4 v) {
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            acc[2 * e] += (double)__uint_as_float(w[e] << 16);
+            acc[2 * e + 1] += (double)__uint_as_float(w[e] & 0xffff0000u);
+        }
+    };
+    constexpr int U = 4;                      // rows in flight per thread
+    int r = st;
+    for (; r + (U - 1) * ST < n; r += U * ST) {
+        uint4 v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) v[u] = *reinterpret_cast<const uint4*>(Xh + (int64_t)(r + u * ST) * D);
+#pragma unroll
+        for (int u = 0; u < U; ++u) add(v[u]);
+    }
+    for (; r < n; r += ST) add(*reinterpret_cast<const uint4*>(Xh + (int64_t)r * D));
+#pragma unroll
+    for (int e = 0; e < 8; ++e) red[st][ch * 8 + e] = acc[e];
+    __syncthreads();
+    if (tid < D) {
+        double sum = 0.0;
+        for (int k = 0; k < ST; ++k) sum += red[k][tid];
+        cent[(bh * C + c) * (int64_t)D + tid] = (float)(sum / (double)n);
+    }
 }
 
 // ----------------------------------------------------------------------------
@@ -1043,13 +1067,11 @@ struct ClusterWs {
 
 inline int padded_c(int C) { return (C + kAsgIlp - 1) / kAsgIlp * kAsgIlp; }
 
-// workgroups per head of k_assign_mx (about one per CU over all heads: its
-// LDS holds one per CU) or of k_sum_assigned (two per CU), at least 16 token
-// groups each; never more than kAmxWgTarget
-inline int amx_wg_per_head(const Geometry& g, bool sum_only = false) {
+// workgroups per head of k_assign_mx: about one per CU over all heads (its
+// LDS holds one per CU), at least 16 token groups each, at most kAmxWgTarget
+inline int amx_wg_per_head(const Geometry& g) {
     const int64_t groups = ceil_div(g.N, 32);
-    const int64_t wgs = sum_only ? 2 * kAmxWgTarget : kAmxWgTarget;
-    const int64_t target = std::max<int64_t>(1, wgs / std::max<int64_t>(1, g.BH()));
+    const int64_t target = std::max<int64_t>(1, kAmxWgTarget / std::max<int64_t>(1, g.BH()));
     return (int)std::min<int64_t>({target, ceil_div(groups, kAmxWaves), (int64_t)kAmxWgTarget});
 }
 
@@ -1073,7 +1095,7 @@ ClusterWs cluster_ws(const Geometry& g, const sa_cluster_spec& cs) {
     w.centT = o; o = align_up(o + (size_t)g.BH() * g.d * padded_c(C) * 4, 256);
     w.bias = o; o = align_up(o + (size_t)g.BH() * padded_c(C) * 4, 256);
     if (fused_means(cs)) {
-        const size_t parts = (size_t)g.BH() * std::max(amx_wg_per_head(g), amx_wg_per_head(g, true));
+        const size_t parts = (size_t)g.BH() * amx_wg_per_head(g);
         w.psum = o; o = align_up(o + parts * kAmxC * g.d * 8, 256);
         w.pcnt = o; o = align_up(o + parts * kAmxC * 4, 256);
     }
@@ -1125,26 +1147,21 @@ sa_status sort_and_mean(const Geometry& g, int C, char* ws, const ClusterWs& w, 
 // means of side s from the partial sums of the last assignment (C <= 64)
 template <int D>
 sa_status partial_means(const Geometry& g, int C, char* ws, const ClusterWs& w, int32_t* count,
-                        float* cent, hipStream_t st, bool sum_only = false) {
+                        float* cent, hipStream_t st) {
     hipLaunchKernelGGL((k_clmean<D>), dim3((unsigned)C, (unsigned)g.BH()), dim3(D), 0, st,
                        reinterpret_cast<const double*>(ws + w.psum),
-                       reinterpret_cast<const int32_t*>(ws + w.pcnt), amx_wg_per_head(g, sum_only), cent,
+                       reinterpret_cast<const int32_t*>(ws + w.pcnt), amx_wg_per_head(g), cent,
                        count, C);
     return hip_check(hipGetLastError(), "k_clmean launch");
 }
 
-// means of the assignment already in side s's workspace (C <= 64)
+// means and sizes of the initial chunk partition (no assignment needed)
 template <int D>
-sa_status assigned_means(const Geometry& g, int C, char* ws, const ClusterWs& w, int s,
-                         const uint16_t* X, int32_t* count, float* cent, hipStream_t st) {
-    hipLaunchKernelGGL((k_sum_assigned<D>), dim3((unsigned)amx_wg_per_head(g, true), (unsigned)g.BH()),
-                       dim3(64 * kAmxWaves), 0, st, X,
-                       reinterpret_cast<const int32_t*>(ws + w.assign[s]),
-                       reinterpret_cast<double*>(ws + w.psum), reinterpret_cast<int32_t*>(ws + w.pcnt),
-                       g.N);
-    sa_status e = hip_check(hipGetLastError(), "k_sum_assigned launch");
-    if (e != SA_OK) return e;
-    return partial_means<D>(g, C, ws, w, count, cent, st, true);
+sa_status chunk_means(const Geometry& g, int C, const uint16_t* X, int32_t* count, float* cent,
+                      hipStream_t st) {
+    hipLaunchKernelGGL((k_chunkmean<D>), dim3((unsigned)C, (unsigned)g.BH()), dim3(256), 0, st, X,
+                       cent, count, g.N, C);
+    return hip_check(hipGetLastError(), "k_chunkmean launch");
 }
 
 template <int D>
@@ -1191,15 +1208,19 @@ sa_status cluster_t(const Geometry& g, const sa_cluster_spec& cs, const uint16_t
                 return e;
         }
     }
-    // initial partition of both sides and its centroids
+    // initial partition of both sides and its centroids: C equal chunks of
+    // the token order (with partial-sum means every round reassigns both
+    // sides before anything reads an assignment, so none is written)
     for (int s = 0; s < 2 && cs.mode != SA_CLUSTER_TILES; ++s) {
-        hipLaunchKernelGGL(k_chunk_assign, dim3((unsigned)ceil_div(g.N, 256), (unsigned)g.BH()),
-                           dim3(256), 0, st, reinterpret_cast<int32_t*>(ws + w.assign[s]), g.N, C);
-        if ((e = hip_check(hipGetLastError(), "k_chunk_assign launch")) != SA_OK) return e;
-        e = fused ? assigned_means<D>(g, C, ws, w, s, s ? K : Q, s ? o.k_count : o.q_count,
-                                      s ? o.k_cent : o.q_cent, st)
-                  : sort_and_mean<D>(g, C, ws, w, s, s ? K : Q, s ? o.k_count : o.q_count,
-                                     s ? o.k_cent : o.q_cent, st);
+        if (fused) {
+            e = chunk_means<D>(g, C, s ? K : Q, s ? o.k_count : o.q_count, s ? o.k_cent : o.q_cent, st);
+        } else {
+            hipLaunchKernelGGL(k_chunk_assign, dim3((unsigned)ceil_div(g.N, 256), (unsigned)g.BH()),
+                               dim3(256), 0, st, reinterpret_cast<int32_t*>(ws + w.assign[s]), g.N, C);
+            if ((e = hip_check(hipGetLastError(), "k_chunk_assign launch")) != SA_OK) return e;
+            e = sort_and_mean<D>(g, C, ws, w, s, s ? K : Q, s ? o.k_count : o.q_count,
+                                 s ? o.k_cent : o.q_cent, st);
+        }
         if (e != SA_OK) return e;
     }
     // a side's means after its assignment: from the partial sums the
