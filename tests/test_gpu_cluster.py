@@ -82,6 +82,11 @@ SMALL = {
                                                          diag=False, comp=True, topk=None),
     "cocluster_c64_topk_d128": BASE.replace(cluster="cocluster", n_clusters=64, cluster_iters=3,
                                             rule="topk", density=0.3),
+    # fewer tokens than one 32-token group of the assignment (N = 21)
+    "kmeans_tiny_d64": BASE.replace(T=1, Hg=3, W=7, H=3, d=64, block=64, cluster="kmeans",
+                                    n_clusters=4, cluster_iters=2, rule="topk", density=0.5),
+    "cocluster_tiny_d128": BASE.replace(T=1, Hg=3, W=7, H=2, cluster="cocluster", n_clusters=21,
+                                        cluster_iters=2, mass=0.9),
     # more than 64 clusters: the assignment's vector-unit path
     "kmeans_c100_mass_comp": BASE.replace(block=64, cluster="kmeans", n_clusters=100,
                                           cluster_iters=2, mass=0.9, comp=True),
