@@ -149,7 +149,8 @@ __global__ __launch_bounds__(kAsgThreads) void k_assign(const uint16_t* __restri
 // those candidates (about one per token) get the exact decision arithmetic
 // of k_assign, and the exact winner among them is the winner among all.
 //
-// A workgroup (8 waves) serves one head and many 32-token groups: it stages
+// A workgroup (16 waves; its LDS, which also holds the cluster sums below,
+// fits one per CU) serves one head and many 32-token groups: it stages
 // the head's centroids once (fp32 rows for the exact chains, the split hi / lo
 // operands in the lane order of the matrix instruction, the decision bias and
 // the bound terms per centroid), then each wave takes groups of 32 tokens
@@ -182,8 +183,10 @@ __device__ __forceinline__ float amx_pair_take(float x) {
     return __uint_as_float(HALF == 0 ? r[0] : r[1]);
 }
 
-// Cluster sums without sorting.  A cluster mean is fl32(exact sum / n): the
-// fp64 sums of bf16 rows are exact, so they may be formed in any order.  Each
+// Cluster sums without sorting.  A cluster mean is fl32(exact sum / n): fp64
+// sums of bf16 values are exact while their significands span fewer than 53
+// bits (the means' definition takes them as exact), so they may be formed in
+// any order.  Each
 // workgroup sums its tokens per cluster in LDS and writes one partial row per
 // cluster it touched; k_clmean adds the partials of a head.
 //
