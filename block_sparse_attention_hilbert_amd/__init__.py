@@ -50,7 +50,7 @@ EXPORTS = ("sparse_attn_workspace_size", "hilbert_perm_build", "hilbert_permute"
            "sparse_attn_fwd_prepare_counts", "sparse_attn_cluster_size", "sparse_attn_cluster",
            "sparse_attn_cluster_gather", "sparse_attn_cluster_scatter",
            "sparse_attn_cluster_select", "sparse_attn_cluster_centroids", "sparse_attn_sics",
-           "sparse_attn_select_noalloc", "sparse_attn_last_error")
+           "sparse_attn_select_noalloc", "sparse_attn_cluster_fwd_run", "sparse_attn_last_error")
 
 
 class SaProblem(ctypes.Structure):
@@ -116,6 +116,8 @@ def _load():
     lib.sparse_attn_cluster.argtypes = [P(SaProblem), P(SaClusterSpec)] + [vp] * 15 + [sz, vp]
     lib.sparse_attn_cluster_gather.argtypes = [P(SaProblem), P(SaClusterSpec), vp, vp, vp, vp]
     lib.sparse_attn_cluster_scatter.argtypes = [P(SaProblem), P(SaClusterSpec)] + [vp] * 6
+    lib.sparse_attn_cluster_fwd_run.argtypes = ([P(SaProblem), P(SaClusterSpec), vp, vp, vp, vp, vp,
+                                                 ctypes.c_int32, vp, vp, vp, sz, vp])
     lib.sparse_attn_cluster_select.argtypes = ([P(SaProblem), P(SaClusterSpec), P(SaSelectSpec)]
                                                + [vp] * 13 + [sz, vp])
     lib.sparse_attn_cluster_centroids.argtypes = [P(SaProblem), P(SaClusterSpec)] + [vp] * 10
@@ -644,6 +646,27 @@ def cluster_scatter(prob: Problem, cspec: ClusterSpec, order: torch.Tensor, src:
         A(lse_dst, "lse_dst", _F32, shape=(prob.B, prob.H, prob.N), optional=True),
         _Stream(stream)))
     return dst
+
+
+def cluster_fwd_run(prob: Problem, cspec: ClusterSpec, q_order: torch.Tensor, Q: torch.Tensor,
+                    Kp: torch.Tensor, row_ptr: torch.Tensor, col_idx: torch.Tensor,
+                    with_comp: bool, *, O: torch.Tensor, lse: Optional[torch.Tensor] = None,
+                    workspace: torch.Tensor, stream=None) -> torch.Tensor:
+    """sparse_attn_cluster_fwd_run: the attention over the padded clustered
+    layout (Kp gathered, the workspace prepared for the padded problem) with Q
+    read and O, lse written in token order through q_order."""
+    A = _Args()
+    Np = _padded_rows(prob, cspec)
+    tok = _tokens(prob)
+    wp, ws_bytes = _ws(A, workspace)
+    _check(A.call(lib.sparse_attn_cluster_fwd_run, ctypes.byref(prob.c()), ctypes.byref(cspec.c()),
+        A(q_order, "q_order", _I32, shape=(prob.B * prob.H, Np)),
+        A(Q, "Q", _BF16, shape=tok), A(Kp, "Kp", _BF16, shape=_tokens(prob, Np)),
+        A(row_ptr, "row_ptr", _I32, numel=prob.B * prob.H * (Np // prob.block) + 1),
+        A(col_idx, "col_idx", _I32), int(bool(with_comp)),
+        A(O, "O", _BF16, shape=tok), A(lse, "lse", _F32, shape=tok[:3], optional=True),
+        wp, ws_bytes, _Stream(stream)))
+    return O
 
 
 def cluster_select(prob: Problem, cspec: ClusterSpec, spec: SelectSpec, cl: Clusters, *,

@@ -118,6 +118,11 @@ struct FwdArgs {
     int32_t N, nb, ntc;
     int64_t rows;
     float c;                 // scale * log2(e)
+    // row-map kernels only (MAP): order is a per-head map [BH][N] from the rows
+    // of the block layout to the tokens of Q, O and lse (a negative entry: no
+    // token, the row is skipped), qmap_stride = N, qN tokens per head of Q, O, lse
+    int64_t qmap_stride;
+    int32_t qN;
 };
 
 template <int D, int BLK>
@@ -234,7 +239,7 @@ __device__ __forceinline__ void dma_tile_fast(unsigned char* tile, const unsigne
 
 // One row = one (batch, head, query block): all its kept tiles, then (with
 // compensation) the centroid tiles, then the merge of the two key halves.
-template <int D, int BLK, bool COMP>
+template <int D, int BLK, bool COMP, bool MAP>
 __device__ __forceinline__ void process_row(const FwdArgs& a, int64_t row, unsigned char* smem,
                                             bool var_cnt) {
     using C = Cfg<D, BLK>;
@@ -258,7 +263,8 @@ __device__ __forceinline__ void process_row(const FwdArgs& a, int64_t row, unsig
     const bool issuer = wave < C::NWI;
     const bool lagging = C::PING && wave >= C::NWI;
     const int r32 = lane & 31, h = lane >> 5;
-    const int64_t head_off = bh * (int64_t)a.N * D;
+    const int64_t head_off = bh * (int64_t)a.N * D;           // K (block layout)
+    const int64_t q_head_off = MAP ? bh * (int64_t)a.qN * D : head_off;   // Q, O (token layout)
     const unsigned char* Kh = reinterpret_cast<const unsigned char*>(a.K + head_off);
     const unsigned char* Vth =
         reinterpret_cast<const unsigned char*>(a.Vt + bh * (int64_t)a.nb * D * BLK);
@@ -268,11 +274,21 @@ __device__ __forceinline__ void process_row(const FwdArgs& a, int64_t row, unsig
     // block order is token qtok of the caller's order
     bf16x8 qf[D / 16];
     const int qn = i * BLK + qg * 32 + r32;
-    const int qtok = qn < a.N ? (a.order ? clamp_token(a.order[qn], a.N) : qn) : 0;
+    // (through a per-head map, a row with no token is skipped: zero queries,
+    // nothing stored)
+    int qtok = 0;
+    bool qvalid = qn < a.N;
+    if constexpr (MAP) {
+        const int t = qvalid ? a.order[bh * a.qmap_stride + qn] : -1;
+        qvalid = t >= 0;
+        qtok = qvalid ? clamp_token(t, a.qN) : 0;
+    } else {
+        qtok = qvalid ? (a.order ? clamp_token(a.order[qn], a.N) : qn) : 0;
+    }
 #pragma unroll
     for (int st = 0; st < D / 16; ++st) {
         uint4 v = make_uint4(0, 0, 0, 0);
-        if (qn < a.N) v = *reinterpret_cast<const uint4*>(a.Q + head_off + (int64_t)qtok * D + st * 16 + h * 8);
+        if (qvalid) v = *reinterpret_cast<const uint4*>(a.Q + q_head_off + (int64_t)qtok * D + st * 16 + h * 8);
         qf[st] = as_bf16x8(v);
     }
 
@@ -586,7 +602,7 @@ __device__ __forceinline__ void process_row(const FwdArgs& a, int64_t row, unsig
     const float inv = l > 0.f ? 1.f / l : 0.f;
     auto finish = [&](auto KHC) {
         constexpr int K = decltype(KHC)::value;
-        uint16_t* orow = a.O + head_off + (int64_t)qtok * D;
+        uint16_t* orow = a.O + q_head_off + (int64_t)qtok * D;
 #pragma unroll
         for (int t = 0; t < HD; ++t) {
             constexpr int OK = 1 - K;
@@ -622,13 +638,13 @@ __device__ __forceinline__ void process_row(const FwdArgs& a, int64_t row, unsig
             }
         }
     };
-    if (qn < a.N) {
+    if (qvalid) {
         if (kh == 0)
             finish(std::integral_constant<int, 0>{});
         else
             finish(std::integral_constant<int, 1>{});
         if (a.lse && kh == 0 && h == 0)
-            a.lse[bh * (int64_t)a.N + qtok] = l > 0.f ? (m + __log2f(l)) * kLn2 : -INFINITY;
+            a.lse[bh * (int64_t)(MAP ? a.qN : a.N) + qtok] = l > 0.f ? (m + __log2f(l)) * kLn2 : -INFINITY;
     }
 }
 
@@ -637,7 +653,7 @@ __device__ __forceinline__ void process_row(const FwdArgs& a, int64_t row, unsig
 // in order, so concurrently running rows of one XCD are neighbouring query
 // blocks that share K/V blocks in that XCD's L2.  A workgroup whose range is
 // exhausted takes rows from the other ranges.
-template <int D, int BLK, bool COMP>
+template <int D, int BLK, bool COMP, bool MAP>
 __global__ __launch_bounds__(BLK * 4) __attribute__((amdgpu_waves_per_eu(2)))
 void k_bsattn_fwd(FwdArgs a) {
     extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
@@ -667,7 +683,7 @@ void k_bsattn_fwd(FwdArgs a) {
             const int row = s_row;
             __syncthreads();
             if (row < 0) break;
-            process_row<D, BLK, COMP>(a, row, smem, var_cnt);
+            process_row<D, BLK, COMP, MAP>(a, row, smem, var_cnt);
         }
     }
     // The last workgroup to finish re-arms the pull counters for the next
@@ -908,21 +924,21 @@ sa_status prepare_t(const FwdArgs& a, const Geometry& g, const uint16_t* V, uint
 }
 
 // The attention kernel on a persistent grid.
-template <int D, int BLK, bool COMP>
+template <int D, int BLK, bool COMP, bool MAP>
 sa_status run_t(const FwdArgs& a, const Geometry& g, hipStream_t stream) {
     using C = Cfg<D, BLK>;
     sa_status st = SA_OK;
     const size_t lds = 256 + C::BASE + C::MAX_NB + 4 * (size_t)g.nb + (COMP ? 4 * (BLK + 1) : 0);
     const int most = 256 + C::BASE + C::MAX_NB + 4 * C::MAX_NB + 4 * (BLK + 1);
-    st = ensure_max_lds((const void*)k_bsattn_fwd<D, BLK, COMP>, most, "k_bsattn_fwd shared memory");
+    st = ensure_max_lds((const void*)k_bsattn_fwd<D, BLK, COMP, MAP>, most, "k_bsattn_fwd shared memory");
     if (st != SA_OK) return st;
     if (a.rows == 0) return SA_OK;
     // as many workgroups as the chip holds at once (LDS per workgroup depends on nb)
     int resident = 0;
-    st = resident_workgroups((const void*)k_bsattn_fwd<D, BLK, COMP>, C::NT, lds, &resident);
+    st = resident_workgroups((const void*)k_bsattn_fwd<D, BLK, COMP, MAP>, C::NT, lds, &resident);
     if (st != SA_OK) return st;
     const int64_t grid = a.rows < resident ? a.rows : resident;
-    hipLaunchKernelGGL((k_bsattn_fwd<D, BLK, COMP>), dim3((unsigned)grid), dim3(C::NT), lds, stream, a);
+    hipLaunchKernelGGL((k_bsattn_fwd<D, BLK, COMP, MAP>), dim3((unsigned)grid), dim3(C::NT), lds, stream, a);
     return hip_check(hipGetLastError(), "k_bsattn_fwd launch");
 }
 
@@ -934,6 +950,8 @@ FwdArgs make_args(const Geometry& g, bool comp, const uint16_t* Q, const uint16_
     a.order = g.order;
     a.row_ptr = row_ptr; a.col_idx = col_idx;
     a.O = O; a.lse = lse; a.N = g.N; a.nb = g.nb; a.rows = g.rows();
+    a.qmap_stride = 0;
+    a.qN = g.N;
     a.ntc = (int32_t)ceil_div(g.nb, g.block);
     a.c = g.scale * kLog2e;
     a.Vt = reinterpret_cast<uint16_t*>(ws + L.vt);
@@ -991,6 +1009,21 @@ sa_status launch_fwd_prepare(const Geometry& g, const uint16_t* V, const int32_t
 #undef SA_PREP
 }
 
+sa_status launch_fwd_run_mapped(const Geometry& g, bool comp, const uint16_t* Q, const uint16_t* K,
+                                const int32_t* row_ptr, const int32_t* col_idx,
+                                const int32_t* qmap, int32_t qN, uint16_t* O, float* lse, char* ws,
+                                hipStream_t stream) {
+    if (g.nb > 4096) return fail(SA_ERR_UNSUPPORTED, "attention supports nb <= 4096 (got %d)", g.nb);
+    if (g.order) return fail(SA_ERR_UNSUPPORTED, "a row map and a token order do not combine");
+    FwdArgs a = make_args(g, comp, Q, K, row_ptr, col_idx, O, lse, ws);
+    a.order = qmap;
+    a.qmap_stride = g.N;
+    a.qN = qN;
+#define SA_RUN(D_, B_, C_) run_t<D_, B_, C_, true>(a, g, stream)
+    SA_DISPATCH(SA_RUN)
+#undef SA_RUN
+}
+
 sa_status launch_fwd_run(const Geometry& g, bool comp, const uint16_t* Q, const uint16_t* K,
                          const int32_t* row_ptr, const int32_t* col_idx, uint16_t* O, float* lse,
                          char* ws, hipStream_t stream) {
@@ -1001,7 +1034,7 @@ sa_status launch_fwd_run(const Geometry& g, bool comp, const uint16_t* Q, const 
         const sa_status st = launch_permute(g, K, const_cast<uint16_t*>(a.K), g.order, false, stream);
         if (st != SA_OK) return st;
     }
-#define SA_RUN(D_, B_, C_) run_t<D_, B_, C_>(a, g, stream)
+#define SA_RUN(D_, B_, C_) run_t<D_, B_, C_, false>(a, g, stream)
     SA_DISPATCH(SA_RUN)
 #undef SA_RUN
 }

@@ -590,6 +590,37 @@ SA_API sa_status sparse_attn_cluster_scatter(const sa_problem* prob, const sa_cl
                                   (uint16_t*)dst, lse_src, lse_dst, (hipStream_t)stream);
 }
 
+SA_API sa_status sparse_attn_cluster_fwd_run(const sa_problem* prob, const sa_cluster_spec* cspec,
+                                             const int32_t* q_order, const void* Q, const void* Kp,
+                                             const int32_t* row_ptr, const int32_t* col_idx,
+                                             int32_t with_comp, void* O, float* lse,
+                                             void* workspace, size_t ws_bytes, void* stream) {
+    clear_error();
+    Geometry g;
+    sa_status st = check_problem(prob, &g);
+    if (st != SA_OK) return st;
+    if ((st = no_token_order(g, "sparse_attn_cluster_fwd_run")) != SA_OK) return st;
+    if ((st = check_cluster(g, cspec)) != SA_OK) return st;
+    if (!q_order || !Q || !Kp || !O) return fail(SA_ERR_INVALID_ARG, "q_order, Q, Kp and O are required");
+    if (!aligned16(Q) || !aligned16(Kp) || !aligned16(O))
+        return fail(SA_ERR_INVALID_ARG, "Q, Kp, O must be 16-byte aligned");
+    if (!row_ptr || !col_idx) return fail(SA_ERR_INVALID_ARG, "row_ptr and col_idx are required");
+    if (with_comp != 0 && with_comp != 1) return fail(SA_ERR_INVALID_ARG, "with_comp must be 0 or 1");
+    // the attention problem of the padded layout: one flat frame of nbp blocks
+    sa_problem pp = *prob;
+    pp.N = padded_block_count(g, *cspec) * g.block;
+    pp.T = 1;
+    pp.Hg = 1;
+    pp.W = pp.N;
+    pp.token_order = nullptr;
+    Geometry gp;
+    if ((st = check_problem(&pp, &gp)) != SA_OK) return st;
+    if ((st = check_fwd_workspace(gp, with_comp != 0, workspace, ws_bytes)) != SA_OK) return st;
+    return launch_fwd_run_mapped(gp, with_comp != 0, (const uint16_t*)Q, (const uint16_t*)Kp, row_ptr,
+                                 col_idx, q_order, g.N, (uint16_t*)O, lse, (char*)workspace,
+                                 (hipStream_t)stream);
+}
+
 SA_API sa_status sparse_attn_cluster_select(const sa_problem* prob, const sa_cluster_spec* cspec,
                                             const sa_select_spec* spec, const float* q_cent,
                                             const float* k_cent, const float* v_cent,

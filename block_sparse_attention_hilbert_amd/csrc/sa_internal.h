@@ -183,6 +183,12 @@ size_t fwd_workspace_bytes(const Geometry& g, bool comp);
 sa_status launch_fwd_prepare(const Geometry& g, const uint16_t* V, const int32_t* row_ptr,
                              const float* k_mean, const float* v_sum, const int32_t* kv_count,
                              char* ws, hipStream_t stream);
+// the attention on a block layout whose rows map to the tokens of Q, O, lse
+// through qmap ([BH][g.N], negative: no token) with qN tokens per head
+sa_status launch_fwd_run_mapped(const Geometry& g, bool comp, const uint16_t* Q, const uint16_t* K,
+                                const int32_t* row_ptr, const int32_t* col_idx,
+                                const int32_t* qmap, int32_t qN, uint16_t* O, float* lse, char* ws,
+                                hipStream_t stream);
 sa_status launch_fwd_run(const Geometry& g, bool comp, const uint16_t* Q, const uint16_t* K,
                          const int32_t* row_ptr, const int32_t* col_idx, uint16_t* O, float* lse,
                          char* ws, hipStream_t stream);

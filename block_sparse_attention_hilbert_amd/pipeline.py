@@ -40,8 +40,8 @@ import numpy as np
 import torch
 
 from . import (Clusters, ClusterSpec, Problem, Selection, SelectSpec, alloc_workspace,
-               centroids, cluster, cluster_centroids, cluster_gather, cluster_scatter,
-               cluster_select, sics,
+               centroids, cluster, cluster_centroids, cluster_gather,
+               cluster_fwd_run, cluster_select, sics,
                cluster_size, fwd, fwd_prepare, fwd_prepare_counts, fwd_run,
                hilbert_perm_build, padded_problem, select, workspace_size)
 
@@ -217,18 +217,18 @@ class ClusteredAttention:
         self.ws_cluster = alloc_workspace(ws_c, self.device)
         self.ws_select = alloc_workspace(ws_s, self.device)
         self.ws_fwd = alloc_workspace(workspace_size(pp, None), self.device)
+        # K and V are gathered into the padded layout; Q is read and O, lse
+        # written in token order by the attention call itself
         pshape = (pp.B, pp.H, pp.N, pp.d)
-        self.Qp = torch.empty(pshape, dtype=torch.bfloat16, device=self.device)
-        self.Kp = torch.empty_like(self.Qp)
-        self.Vp = torch.empty_like(self.Qp)
-        self.Op = torch.empty_like(self.Qp)
+        self.Kp = torch.empty(pshape, dtype=torch.bfloat16, device=self.device)
+        self.Vp = torch.empty_like(self.Kp)
         self.O = torch.empty(prob.B, prob.H, prob.N, prob.d, dtype=torch.bfloat16,
                              device=self.device)
-        self.lsep = self.lse = None
+        self.lse = None
         if want_lse:
-            self.lsep = torch.empty(pp.B, pp.H, pp.N, dtype=torch.float32, device=self.device)
             self.lse = torch.empty(prob.B, prob.H, prob.N, dtype=torch.float32,
                                    device=self.device)
+        self._Q = None             # this call's Q (read by the attention)
 
     def run_cluster(self, Q, K, V, choose_shapes: bool = True):
         """Form the partition.  In tile mode SICS first picks each head's tile
@@ -253,7 +253,9 @@ class ClusteredAttention:
                               self.sel.v_sum)
 
     def run_gather(self, Q, K, V):
-        cluster_gather(self.prob, self.cspec, self.cl.q_order, Q, self.Qp)
+        """K and V into the padded layout (Q stays in token order: the
+        attention reads it through q_order)."""
+        self._Q = Q
         cluster_gather(self.prob, self.cspec, self.cl.k_order, K, self.Kp)
         cluster_gather(self.prob, self.cspec, self.cl.k_order, V, self.Vp)
 
@@ -266,13 +268,15 @@ class ClusteredAttention:
                            self.sel.k_mean, self.sel.v_sum, workspace=self.ws_fwd)
 
     def run_fwd_attention(self):
-        fwd_run(self.pprob, self.Qp, self.Kp, self.sel.row_ptr, self.sel.col_idx,
-                self.spec.want_comp, O=self.Op, lse=self.lsep, workspace=self.ws_fwd)
-        return self.Op
+        """The attention over the padded layout, Q read and O, lse written in
+        token order (this call's Q, from run_gather)."""
+        cluster_fwd_run(self.prob, self.cspec, self.cl.q_order, self._Q, self.Kp,
+                        self.sel.row_ptr, self.sel.col_idx, self.spec.want_comp, O=self.O,
+                        lse=self.lse, workspace=self.ws_fwd)
+        return self.O
 
     def run_scatter(self):
-        cluster_scatter(self.prob, self.cspec, self.cl.q_order, self.Op, self.O, self.lsep,
-                        self.lse)
+        """O (and lse) in token order: written there by run_fwd_attention."""
         return self.O
 
     def __call__(self, Q, K, V, reuse: Optional[bool] = None,

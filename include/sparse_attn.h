@@ -527,6 +527,31 @@ sa_status sparse_attn_fwd_prepare_counts(const sa_problem* prob, const void* V,
                                          const float* v_sum, const int32_t* kv_count,
                                          void* workspace, size_t ws_bytes, void* stream);
 
+/*
+ * sparse_attn_fwd_run over the padded clustered layout with Q read and O, lse
+ * written in the caller's token order [SVOO 2B: attention within the
+ * clusters' blocks; SVG-EAR 2A: the permutation that makes clusters
+ * contiguous]: the attention problem is that of the padded layout (N_p =
+ * nbp * block tokens in one flat frame, as the workspace was prepared for by
+ * sparse_attn_fwd_prepare_counts); the query row of padded slot p of head
+ * (b, h) is Q[b, h, q_order[b*H+h, p], :], its output row and lse go to the
+ * same token, and slots with q_order = -1 (padding) are skipped.  This is
+ * sparse_attn_cluster_gather of Q, sparse_attn_fwd_run and
+ * sparse_attn_cluster_scatter of O and lse in one pass.
+ * prob, cspec: the token-order problem and the clustering (prob without a
+ * token order).  q_order: device int32 [B*H, N_p] as written by
+ * sparse_attn_cluster (entries in [0, N) or -1).  Q, O: device bf16
+ * [B,H,N,d]; lse: optional device fp32 [B,H,N]; rows of tokens that no slot
+ * maps to are left untouched.  Kp: device bf16 [B,H,N_p,d] (K gathered by
+ * k_order).  row_ptr, col_idx, with_comp, workspace: as for
+ * sparse_attn_fwd_run on the padded problem.  All tensors 16-byte aligned.
+ */
+sa_status sparse_attn_cluster_fwd_run(const sa_problem* prob, const sa_cluster_spec* cspec,
+                                      const int32_t* q_order, const void* Q, const void* Kp,
+                                      const int32_t* row_ptr, const int32_t* col_idx,
+                                      int32_t with_comp, void* O, float* lse,
+                                      void* workspace, size_t ws_bytes, void* stream);
+
 /* Text of the last failure on the calling thread ("" after success). */
 const char* sparse_attn_last_error(void);
 

@@ -333,6 +333,16 @@ def test_cluster_calls_reject_before_any_launch():
     c, keep = sa.SelectSpec(rule="mass").c()
     assert sel(ctypes.byref(p), ctypes.byref(cs), ctypes.byref(c), *ptrs, None, None, None,
                fake, 8, None) == sa.SA_ERR_WORKSPACE
+    # attention over the padded layout through q_order: map, operands, flags, workspace
+    run = sa.lib.sparse_attn_cluster_fwd_run
+    assert run(ctypes.byref(p), ctypes.byref(cs), None, fake, fake, fake, fake, 0, fake, None,
+               fake, 1 << 30, None) == sa.SA_ERR_INVALID_ARG                 # no q_order
+    assert run(ctypes.byref(p), ctypes.byref(cs), fake, odd, fake, fake, fake, 0, fake, None,
+               fake, 1 << 30, None) == sa.SA_ERR_INVALID_ARG                 # misaligned Q
+    assert run(ctypes.byref(p), ctypes.byref(cs), fake, fake, fake, fake, fake, 2, fake, None,
+               fake, 1 << 30, None) == sa.SA_ERR_INVALID_ARG                 # with_comp
+    assert run(ctypes.byref(p), ctypes.byref(cs), fake, fake, fake, fake, fake, 0, fake, None,
+               fake, 16, None) == sa.SA_ERR_WORKSPACE
     # prepare with counts needs the counts
     prep = sa.lib.sparse_attn_fwd_prepare_counts
     assert prep(ctypes.byref(p), fake, fake, None, None, None, fake, 1 << 30, None) == \

@@ -140,7 +140,7 @@ def check_case(wl, Q, K, V, heads, q_clusters_per_head=None, seed=0):
     forced in, so the partition, selection and attention are checked against
     the oracle's own choice (the oracle never takes a value from the GPU)."""
     pipe = _pipe(wl)
-    poison(pipe.O, pipe.Op, pipe.lse, pipe.lsep)
+    poison(pipe.O, pipe.lse)
     Qd, Kd, Vd = to_dev(Q), to_dev(K), to_dev(V)
     O = pipe(Qd, Kd, Vd)
     torch.cuda.synchronize()
@@ -171,7 +171,7 @@ def check_case(wl, Q, K, V, heads, q_clusters_per_head=None, seed=0):
         if excused:
             log(f"[cluster] {wl.name}: {excused} near-tie shape picks; rerun with the oracle's")
             pipe.shape_idx.copy_(torch.from_numpy(forced))
-            poison(pipe.O, pipe.Op, pipe.lse, pipe.lsep)
+            poison(pipe.O, pipe.lse)
             O = pipe(Qd, Kd, Vd, reuse=False, choose_shapes=False)
             torch.cuda.synchronize()
             assert np.array_equal(pipe.shape_idx.cpu().numpy(), forced)
