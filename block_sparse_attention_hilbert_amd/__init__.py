@@ -50,7 +50,8 @@ EXPORTS = ("sparse_attn_workspace_size", "hilbert_perm_build", "hilbert_permute"
            "sparse_attn_fwd_prepare_counts", "sparse_attn_cluster_size", "sparse_attn_cluster",
            "sparse_attn_cluster_gather", "sparse_attn_cluster_scatter",
            "sparse_attn_cluster_select", "sparse_attn_cluster_centroids", "sparse_attn_sics",
-           "sparse_attn_select_noalloc", "sparse_attn_cluster_fwd_run", "sparse_attn_last_error")
+           "sparse_attn_select_noalloc", "sparse_attn_cluster_fwd_run",
+           "sparse_attn_cluster_fwd_prepare", "sparse_attn_last_error")
 
 
 class SaProblem(ctypes.Structure):
@@ -118,6 +119,8 @@ def _load():
     lib.sparse_attn_cluster_scatter.argtypes = [P(SaProblem), P(SaClusterSpec)] + [vp] * 6
     lib.sparse_attn_cluster_fwd_run.argtypes = ([P(SaProblem), P(SaClusterSpec), vp, vp, vp, vp, vp,
                                                  ctypes.c_int32, vp, vp, vp, sz, vp])
+    lib.sparse_attn_cluster_fwd_prepare.argtypes = ([P(SaProblem), P(SaClusterSpec)] + [vp] * 7 +
+                                                    [sz, vp])
     lib.sparse_attn_cluster_select.argtypes = ([P(SaProblem), P(SaClusterSpec), P(SaSelectSpec)]
                                                + [vp] * 13 + [sz, vp])
     lib.sparse_attn_cluster_centroids.argtypes = [P(SaProblem), P(SaClusterSpec)] + [vp] * 10
@@ -646,6 +649,25 @@ def cluster_scatter(prob: Problem, cspec: ClusterSpec, order: torch.Tensor, src:
         A(lse_dst, "lse_dst", _F32, shape=(prob.B, prob.H, prob.N), optional=True),
         _Stream(stream)))
     return dst
+
+
+def cluster_fwd_prepare(prob: Problem, cspec: ClusterSpec, k_order: torch.Tensor, V: torch.Tensor,
+                        row_ptr: torch.Tensor, kv_count: torch.Tensor,
+                        k_mean: Optional[torch.Tensor] = None, v_sum: Optional[torch.Tensor] = None,
+                        *, workspace: torch.Tensor, stream=None) -> None:
+    """sparse_attn_cluster_fwd_prepare: fwd_prepare_counts over the padded
+    clustered layout with V read in token order through k_order."""
+    A = _Args()
+    Np = _padded_rows(prob, cspec)
+    pp = padded_problem(prob, Np // prob.block)
+    wp, ws_bytes = _ws(A, workspace)
+    _check(A.call(lib.sparse_attn_cluster_fwd_prepare, ctypes.byref(prob.c()), ctypes.byref(cspec.c()),
+        A(k_order, "k_order", _I32, shape=(prob.B * prob.H, Np)),
+        A(V, "V", _BF16, shape=_tokens(prob)),
+        A(row_ptr, "row_ptr", _I32, numel=pp.rows + 1),
+        *_comp_args(A, pp, k_mean, v_sum),
+        A(kv_count, "kv_count", _I32, numel=pp.B * pp.H * pp.nb),
+        wp, ws_bytes, _Stream(stream)))
 
 
 def cluster_fwd_run(prob: Problem, cspec: ClusterSpec, q_order: torch.Tensor, Q: torch.Tensor,

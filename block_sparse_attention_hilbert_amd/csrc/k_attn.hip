@@ -775,15 +775,20 @@ __global__ __launch_bounds__(kSchedThreads) void k_sched(const int32_t* __restri
 // stores of 8 consecutive keys of one channel.  Consecutive lanes take
 // consecutive key groups, so 16 (8) lanes write one whole 256-byte (128-byte)
 // row of the transposed block.
+// With a per-head map (map_stride = N: order is [BH][N], slot -> token of V,
+// negative: no token, a zero row; V holds vN tokens per head) the same for a
+// layout whose rows map to the tokens of V.
 template <int D, int BLK>
 __global__ __launch_bounds__(256) void k_vt_prep(const uint16_t* __restrict__ V,
                                                  uint16_t* __restrict__ Vt, int N, int nb,
-                                                 const int32_t* __restrict__ order) {
+                                                 const int32_t* __restrict__ order,
+                                                 int64_t map_stride = 0, int vN = 0) {
     constexpr int KC = BLK / 8, DC = D / 8;
     const int j = blockIdx.x;
     const int64_t bh = blockIdx.y;
     const int n = min(BLK, N - j * BLK);
-    const uint16_t* src = V + bh * N * (int64_t)D;
+    const int NV = map_stride ? vN : N;       // tokens per head of V
+    const uint16_t* src = V + bh * NV * (int64_t)D;
     uint16_t* dst = Vt + (bh * nb + j) * (int64_t)D * BLK;
     for (int p = threadIdx.x; p < KC * DC; p += 256) {
         const int kc = p % KC, dc = p / KC;
@@ -793,7 +798,16 @@ __global__ __launch_bounds__(256) void k_vt_prep(const uint16_t* __restrict__ V,
 #pragma unroll
         for (int r = 0; r < 8; ++r) {
             const int key = kc * 8 + r;
-            tok[r] = key < n ? (order ? clamp_token(order[j * BLK + key], N) : j * BLK + key) : -1;
+            int t = -1;
+            if (key < n) {
+                if (map_stride) {
+                    t = order[bh * map_stride + j * BLK + key];
+                    t = t < 0 ? -1 : clamp_token(t, NV);
+                } else {
+                    t = order ? clamp_token(order[j * BLK + key], N) : j * BLK + key;
+                }
+            }
+            tok[r] = t;
         }
         uint32_t w[8][4];
 #pragma unroll
@@ -897,7 +911,8 @@ WsLayout ws_layout(const Geometry& g, bool comp) {
 template <int D, int BLK, bool COMP>
 sa_status prepare_t(const FwdArgs& a, const Geometry& g, const uint16_t* V, uint16_t* vt,
                     const float* k_mean, const float* v_sum, const int32_t* kv_count,
-                    uint16_t* kbar, uint16_t* vbart, hipStream_t stream) {
+                    uint16_t* kbar, uint16_t* vbart, hipStream_t stream,
+                    const int32_t* vmap = nullptr, int vN = 0) {
     // the block counts are read only with the caller's counts or compensation
     sa_status st = SA_OK;
     if (COMP || kv_count) {
@@ -908,8 +923,12 @@ sa_status prepare_t(const FwdArgs& a, const Geometry& g, const uint16_t* V, uint
         if ((st = hip_check(hipGetLastError(), "k_fill_counts launch")) != SA_OK) return st;
     }
     if (V) {   // else the workspace already holds V in block layout
-        hipLaunchKernelGGL((k_vt_prep<D, BLK>), dim3(g.nb, (unsigned)g.BH()), dim3(256), 0, stream, V,
-                           vt, g.N, g.nb, g.order);
+        if (vmap)
+            hipLaunchKernelGGL((k_vt_prep<D, BLK>), dim3(g.nb, (unsigned)g.BH()), dim3(256), 0, stream, V,
+                               vt, g.N, g.nb, vmap, (int64_t)g.N, vN);
+        else
+            hipLaunchKernelGGL((k_vt_prep<D, BLK>), dim3(g.nb, (unsigned)g.BH()), dim3(256), 0, stream, V,
+                               vt, g.N, g.nb, g.order, (int64_t)0, 0);
         if ((st = hip_check(hipGetLastError(), "k_vt_prep launch")) != SA_OK) return st;
     }
     if (COMP) {
@@ -997,14 +1016,15 @@ sa_status launch_vt_layout(const Geometry& g, const uint16_t* V, uint16_t* Vt, h
 
 sa_status launch_fwd_prepare(const Geometry& g, const uint16_t* V, const int32_t* row_ptr,
                              const float* k_mean, const float* v_sum, const int32_t* kv_count,
-                             char* ws, hipStream_t stream) {
+                             char* ws, hipStream_t stream, const int32_t* vmap, int vN) {
     const bool comp = k_mean != nullptr;
+    if (vmap && g.order) return fail(SA_ERR_UNSUPPORTED, "a row map and a token order do not combine");
     if (g.nb > 4096) return fail(SA_ERR_UNSUPPORTED, "attention supports nb <= 4096 (got %d)", g.nb);
     const FwdArgs a = make_args(g, comp, nullptr, nullptr, row_ptr, nullptr, nullptr, nullptr, ws);
     uint16_t* vt = const_cast<uint16_t*>(a.Vt);
     uint16_t* kbar = const_cast<uint16_t*>(a.kbar);
     uint16_t* vbart = const_cast<uint16_t*>(a.vbart);
-#define SA_PREP(D_, B_, C_) prepare_t<D_, B_, C_>(a, g, V, vt, k_mean, v_sum, kv_count, kbar, vbart, stream)
+#define SA_PREP(D_, B_, C_) prepare_t<D_, B_, C_>(a, g, V, vt, k_mean, v_sum, kv_count, kbar, vbart, stream, vmap, vN)
     SA_DISPATCH(SA_PREP)
 #undef SA_PREP
 }

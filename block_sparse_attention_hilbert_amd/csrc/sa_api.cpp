@@ -590,6 +590,37 @@ SA_API sa_status sparse_attn_cluster_scatter(const sa_problem* prob, const sa_cl
                                   (uint16_t*)dst, lse_src, lse_dst, (hipStream_t)stream);
 }
 
+SA_API sa_status sparse_attn_cluster_fwd_prepare(const sa_problem* prob,
+                                                 const sa_cluster_spec* cspec,
+                                                 const int32_t* k_order, const void* V,
+                                                 const int32_t* row_ptr, const float* k_mean,
+                                                 const float* v_sum, const int32_t* kv_count,
+                                                 void* workspace, size_t ws_bytes, void* stream) {
+    clear_error();
+    Geometry g;
+    sa_status st = check_problem(prob, &g);
+    if (st != SA_OK) return st;
+    if ((st = no_token_order(g, "sparse_attn_cluster_fwd_prepare")) != SA_OK) return st;
+    if ((st = check_cluster(g, cspec)) != SA_OK) return st;
+    if (!k_order || !V) return fail(SA_ERR_INVALID_ARG, "k_order and V are required");
+    if (!aligned16(V)) return fail(SA_ERR_INVALID_ARG, "V must be 16-byte aligned");
+    if (!row_ptr) return fail(SA_ERR_INVALID_ARG, "row_ptr is required");
+    if (!kv_count) return fail(SA_ERR_INVALID_ARG, "kv_count is required");
+    if ((k_mean == nullptr) != (v_sum == nullptr))
+        return fail(SA_ERR_INVALID_ARG, "k_mean and v_sum must be given together");
+    sa_problem pp = *prob;
+    pp.N = padded_block_count(g, *cspec) * g.block;
+    pp.T = 1;
+    pp.Hg = 1;
+    pp.W = pp.N;
+    pp.token_order = nullptr;
+    Geometry gp;
+    if ((st = check_problem(&pp, &gp)) != SA_OK) return st;
+    if ((st = check_fwd_workspace(gp, k_mean != nullptr, workspace, ws_bytes)) != SA_OK) return st;
+    return launch_fwd_prepare(gp, (const uint16_t*)V, row_ptr, k_mean, v_sum, kv_count,
+                              (char*)workspace, (hipStream_t)stream, k_order, g.N);
+}
+
 SA_API sa_status sparse_attn_cluster_fwd_run(const sa_problem* prob, const sa_cluster_spec* cspec,
                                              const int32_t* q_order, const void* Q, const void* Kp,
                                              const int32_t* row_ptr, const int32_t* col_idx,

@@ -180,9 +180,12 @@ size_t fwd_workspace_bytes(const Geometry& g, bool comp);
 
 // kv_count: device int32 [BH, nb] token counts per KV block, or null for the
 // fixed layout (block, the last one N - (nb - 1) block).
+// vmap (optional, [BH][g.N], negative: no token): V holds vN tokens per head
+// and the layout's rows read them through the map
 sa_status launch_fwd_prepare(const Geometry& g, const uint16_t* V, const int32_t* row_ptr,
                              const float* k_mean, const float* v_sum, const int32_t* kv_count,
-                             char* ws, hipStream_t stream);
+                             char* ws, hipStream_t stream, const int32_t* vmap = nullptr,
+                             int vN = 0);
 // the attention on a block layout whose rows map to the tokens of Q, O, lse
 // through qmap ([BH][g.N], negative: no token) with qN tokens per head
 sa_status launch_fwd_run_mapped(const Geometry& g, bool comp, const uint16_t* Q, const uint16_t* K,

@@ -41,7 +41,7 @@ import torch
 
 from . import (Clusters, ClusterSpec, Problem, Selection, SelectSpec, alloc_workspace,
                centroids, cluster, cluster_centroids, cluster_gather,
-               cluster_fwd_run, cluster_select, sics,
+               cluster_fwd_prepare, cluster_fwd_run, cluster_select, sics,
                cluster_size, fwd, fwd_prepare, fwd_prepare_counts, fwd_run,
                hilbert_perm_build, padded_problem, select, workspace_size)
 
@@ -217,8 +217,9 @@ class ClusteredAttention:
         self.ws_cluster = alloc_workspace(ws_c, self.device)
         self.ws_select = alloc_workspace(ws_s, self.device)
         self.ws_fwd = alloc_workspace(workspace_size(pp, None), self.device)
-        # K and V are gathered into the padded layout; Q is read and O, lse
-        # written in token order by the attention call itself
+        # K is gathered into the padded layout (V too when a kept partition's
+        # centroids are recomputed); V is laid out and Q read, O and lse
+        # written in token order by the forward calls themselves
         pshape = (pp.B, pp.H, pp.N, pp.d)
         self.Kp = torch.empty(pshape, dtype=torch.bfloat16, device=self.device)
         self.Vp = torch.empty_like(self.Kp)
@@ -228,7 +229,7 @@ class ClusteredAttention:
         if want_lse:
             self.lse = torch.empty(prob.B, prob.H, prob.N, dtype=torch.float32,
                                    device=self.device)
-        self._Q = None             # this call's Q (read by the attention)
+        self._Q = self._V = None   # this call's Q and V (read by the forward calls)
 
     def run_cluster(self, Q, K, V, choose_shapes: bool = True):
         """Form the partition.  In tile mode SICS first picks each head's tile
@@ -247,25 +248,26 @@ class ClusteredAttention:
         return self.have_partition and self.calls % self.refresh_every != 0
 
     def run_centroids(self):
-        """Compensation statistics of this call's (gathered) K, V for a kept partition."""
+        """Compensation statistics of this call's K, V for a kept partition
+        (V gathered into the padded layout for them)."""
         if self.spec.want_comp:
+            cluster_gather(self.prob, self.cspec, self.cl.k_order, self._V, self.Vp)
             cluster_centroids(self.prob, self.cspec, self.Kp, self.Vp, self.cl, self.sel.k_mean,
                               self.sel.v_sum)
 
     def run_gather(self, Q, K, V):
-        """K and V into the padded layout (Q stays in token order: the
-        attention reads it through q_order)."""
-        self._Q = Q
+        """K into the padded layout (Q and V stay in token order: the forward
+        calls read them through q_order and k_order)."""
+        self._Q, self._V = Q, V
         cluster_gather(self.prob, self.cspec, self.cl.k_order, K, self.Kp)
-        cluster_gather(self.prob, self.cspec, self.cl.k_order, V, self.Vp)
 
     def run_select(self) -> Selection:
         return cluster_select(self.prob, self.cspec, self.spec, self.cl, out=self.sel,
                               workspace=self.ws_select)
 
     def run_fwd_prepare(self):
-        fwd_prepare_counts(self.pprob, self.Vp, self.sel.row_ptr, self.cl.k_cnt,
-                           self.sel.k_mean, self.sel.v_sum, workspace=self.ws_fwd)
+        cluster_fwd_prepare(self.prob, self.cspec, self.cl.k_order, self._V, self.sel.row_ptr,
+                            self.cl.k_cnt, self.sel.k_mean, self.sel.v_sum, workspace=self.ws_fwd)
 
     def run_fwd_attention(self):
         """The attention over the padded layout, Q read and O, lse written in

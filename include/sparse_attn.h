@@ -528,6 +528,24 @@ sa_status sparse_attn_fwd_prepare_counts(const sa_problem* prob, const void* V,
                                          void* workspace, size_t ws_bytes, void* stream);
 
 /*
+ * sparse_attn_fwd_prepare_counts over the padded clustered layout with V read
+ * in the caller's token order: the padded slot p of head (b, h) holds the
+ * value row V[b, h, k_order[b*H+h, p], :] (zeros where k_order = -1).  This
+ * is sparse_attn_cluster_gather of V followed by
+ * sparse_attn_fwd_prepare_counts on the padded problem (N_p = nbp * block
+ * tokens in one flat frame), in one pass.  prob, cspec: the token-order
+ * problem and the clustering.  k_order: device int32 [B*H, N_p] as written by
+ * sparse_attn_cluster.  V: device bf16 [B,H,N,d], 16-byte aligned.  row_ptr,
+ * k_mean, v_sum, kv_count, workspace: as for sparse_attn_fwd_prepare_counts
+ * on the padded problem.
+ */
+sa_status sparse_attn_cluster_fwd_prepare(const sa_problem* prob, const sa_cluster_spec* cspec,
+                                          const int32_t* k_order, const void* V,
+                                          const int32_t* row_ptr, const float* k_mean,
+                                          const float* v_sum, const int32_t* kv_count,
+                                          void* workspace, size_t ws_bytes, void* stream);
+
+/*
  * sparse_attn_fwd_run over the padded clustered layout with Q read and O, lse
  * written in the caller's token order [SVOO 2B: attention within the
  * clusters' blocks; SVG-EAR 2A: the permutation that makes clusters
