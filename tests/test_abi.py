@@ -343,6 +343,16 @@ def test_cluster_calls_reject_before_any_launch():
                fake, 1 << 30, None) == sa.SA_ERR_INVALID_ARG                 # with_comp
     assert run(ctypes.byref(p), ctypes.byref(cs), fake, fake, fake, fake, fake, 0, fake, None,
                fake, 16, None) == sa.SA_ERR_WORKSPACE
+    # its preparation with V through k_order: map, V, counts, workspace
+    cprep = sa.lib.sparse_attn_cluster_fwd_prepare
+    assert cprep(ctypes.byref(p), ctypes.byref(cs), None, fake, fake, None, None, fake,
+                 fake, 1 << 30, None) == sa.SA_ERR_INVALID_ARG               # no k_order
+    assert cprep(ctypes.byref(p), ctypes.byref(cs), fake, odd, fake, None, None, fake,
+                 fake, 1 << 30, None) == sa.SA_ERR_INVALID_ARG               # misaligned V
+    assert cprep(ctypes.byref(p), ctypes.byref(cs), fake, fake, fake, None, None, None,
+                 fake, 1 << 30, None) == sa.SA_ERR_INVALID_ARG               # no counts
+    assert cprep(ctypes.byref(p), ctypes.byref(cs), fake, fake, fake, None, None, fake,
+                 fake, 16, None) == sa.SA_ERR_WORKSPACE
     # prepare with counts needs the counts
     prep = sa.lib.sparse_attn_fwd_prepare_counts
     assert prep(ctypes.byref(p), fake, fake, None, None, None, fake, 1 << 30, None) == \
