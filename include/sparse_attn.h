@@ -535,7 +535,8 @@ sa_status sparse_attn_fwd_prepare_counts(const sa_problem* prob, const void* V,
  * sparse_attn_fwd_prepare_counts on the padded problem (N_p = nbp * block
  * tokens in one flat frame), in one pass.  prob, cspec: the token-order
  * problem and the clustering.  k_order: device int32 [B*H, N_p] as written by
- * sparse_attn_cluster.  V: device bf16 [B,H,N,d], 16-byte aligned.  row_ptr,
+ * sparse_attn_cluster (not checked: an entry >= N is clamped to N - 1, a
+ * negative one gives a zero row).  V: device bf16 [B,H,N,d], 16-byte aligned.  row_ptr,
  * k_mean, v_sum, kv_count, workspace: as for sparse_attn_fwd_prepare_counts
  * on the padded problem.
  */
@@ -558,7 +559,8 @@ sa_status sparse_attn_cluster_fwd_prepare(const sa_problem* prob, const sa_clust
  * sparse_attn_cluster_scatter of O and lse in one pass.
  * prob, cspec: the token-order problem and the clustering (prob without a
  * token order).  q_order: device int32 [B*H, N_p] as written by
- * sparse_attn_cluster (entries in [0, N) or -1).  Q, O: device bf16
+ * sparse_attn_cluster (entries in [0, N) or -1; not checked: an entry >= N
+ * is clamped to N - 1, any negative one skips its slot).  Q, O: device bf16
  * [B,H,N,d]; lse: optional device fp32 [B,H,N]; rows of tokens that no slot
  * maps to are left untouched.  Kp: device bf16 [B,H,N_p,d] (K gathered by
  * k_order).  row_ptr, col_idx, with_comp, workspace: as for
