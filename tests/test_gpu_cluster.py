@@ -402,3 +402,43 @@ def test_full_size_cluster_runs_are_bitwise_identical(name):
     for k, (a, b) in enumerate(zip(*runs)):
         assert np.array_equal(a, b), f"output {k} differs between two identical calls"
     log(f"[cluster-det] {name}: identical")
+
+
+def test_slot_maps_out_of_range_are_contained():
+    """Slot maps with entries outside [0, N): the clustered forward calls clamp
+    positive ones into range and skip (queries) or zero (values) negative
+    ones, so they end normally; every token the clamped query map names gets
+    its output row, tokens it never names keep what they held."""
+    import block_sparse_attention_hilbert_amd as sa
+    wl = SMALL["kmeans_topk_comp_d128_b64"].replace(name="kmeans_topk_comp_d128_b64")
+    pipe = _pipe(wl)
+    Q, K, V = (to_dev(x) for x in W.make_qkv(wl))
+    pipe(Q, K, V)
+    torch.cuda.synchronize()
+    N = wl.N
+    qo = pipe.cl.q_order.clone()
+    ko = pipe.cl.k_order.clone()
+    hit = (qo[0] >= 0).nonzero().flatten()[:3]
+    moved = [int(qo[0, s]) for s in hit]
+    qo[0, hit[0]] = N + 1000
+    qo[0, hit[1]] = -7
+    qo[0, hit[2]] = -(1 << 30)
+    ko[0, (ko[0] >= 0).nonzero().flatten()[:2]] = N + 5
+    sa.cluster_fwd_prepare(pipe.prob, pipe.cspec, ko, V, pipe.sel.row_ptr, pipe.cl.k_cnt,
+                           pipe.sel.k_mean, pipe.sel.v_sum, workspace=pipe.ws_fwd)
+    O = torch.empty_like(Q)
+    poison(O)
+    sa.cluster_fwd_run(pipe.prob, pipe.cspec, qo, Q, pipe.Kp, pipe.sel.row_ptr, pipe.sel.col_idx,
+                       True, O=O, workspace=pipe.ws_fwd)
+    torch.cuda.synchronize()
+    Og = from_dev(O)
+    named = np.zeros((wl.B * wl.H, N), dtype=bool)
+    q = qo.cpu().numpy()
+    for bh in range(wl.B * wl.H):
+        t = q[bh][q[bh] >= 0]
+        named[bh, np.minimum(t, N - 1)] = True
+    nan_rows = np.any((Og & 0x7F80) == 0x7F80, axis=-1).reshape(wl.B * wl.H, N)
+    assert not np.any(nan_rows & named), "a named row was not written"
+    for t in moved[1:]:
+        assert nan_rows[0, t], "a token no slot names was written"
+    log(f"[cluster-maps] malformed slot maps contained ({int(named.sum())} rows written)")
