@@ -99,6 +99,9 @@ __device__ __forceinline__ void copies_done() {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
+// int32 entries of the scheduling header before the row list
+constexpr int kSchedHead = 32;
+
 struct FwdArgs {
     const uint16_t* Q;
     const uint16_t* K;
@@ -112,9 +115,11 @@ struct FwdArgs {
     float* lse;
     const int32_t* order;    // token order of the blocks ([N]) or null: Q, O, lse rows go
                              // through it (K comes already in block order)
-    int32_t* sched;          // [3][8] per-XCD row range start, end and pull counter;
+    int32_t* sched;          // [0..7] / [8..15] start / end of each range's part of the
+                             // row list, [16..23] pull counters;
                              // [24] = 1 when the block counts come from the caller;
-                             // [25] workgroups of the launch that are done
+                             // [25] workgroups of the launch that are done;
+                             // [kSchedHead ..) the rows, longest first
     int32_t N, nb, ntc;
     int64_t rows;
     float c;                 // scale * log2(e)
@@ -648,11 +653,14 @@ __device__ __forceinline__ void process_row(const FwdArgs& a, int64_t row, unsig
     }
 }
 
-// Persistent grid.  The rows are split into 8 contiguous ranges of equal work
-// (k_sched); workgroup w pulls rows of range w % 8 -- the XCD it is dealt to --
-// in order, so concurrently running rows of one XCD are neighbouring query
-// blocks that share K/V blocks in that XCD's L2.  A workgroup whose range is
-// exhausted takes rows from the other ranges.
+// Persistent grid.  k_sched splits the rows into 8 contiguous ranges of equal
+// work and lists each range's rows long ones first (by length class, in row
+// order within a class); workgroup w pulls rows of range w % 8 -- the XCD it
+// is dealt to -- in that order, so concurrently running rows of one XCD are
+// mostly neighbouring query blocks that share K/V blocks in that XCD's L2,
+// and the last rows handed out are short ones.  A workgroup whose range is
+// exhausted takes rows from the other ranges.  Which workgroup runs a row
+// does not change its result.
 template <int D, int BLK, bool COMP, bool MAP>
 __global__ __launch_bounds__(BLK * 4) __attribute__((amdgpu_waves_per_eu(2)))
 void k_bsattn_fwd(FwdArgs a) {
@@ -673,11 +681,11 @@ void k_bsattn_fwd(FwdArgs a) {
     const int x0 = blockIdx.x % 8;
     for (int k = 0; k < 8; ++k) {
         const int x = (x0 + k) % 8;
-        const int start = a.sched[x], stop = a.sched[8 + x];
+        const int start = a.sched[x], stop = a.sched[8 + x];   // list positions of range x
         for (;;) {
             if (threadIdx.x == 0) {
                 const int idx = start < stop ? atomicAdd(&a.sched[16 + x], 1) : 0;
-                s_row = start + idx < stop ? start + idx : -1;
+                s_row = start + idx < stop ? a.sched[kSchedHead + start + idx] : -1;
             }
             __syncthreads();
             const int row = s_row;
@@ -698,28 +706,49 @@ void k_bsattn_fwd(FwdArgs a) {
     }
 }
 
-// Splits the R rows into 8 contiguous ranges of (nearly) equal work, where a
-// row costs its number of tiles plus a fixed overhead; resets the pull counters.
 constexpr int kSchedThreads = 1024;
 constexpr int kSchedItems = 8;
+constexpr int kSchedCls = 9;                    // length classes
+constexpr int kSchedSlots = 256;                // 128-token rows running at once (one per CU)
 
+// The row list of the persistent grid.  The rows are split into 8 contiguous
+// ranges of (nearly) equal work, a row costing its tiles (kept blocks clamped
+// to [0, nb], the attention kernel's own clamp) plus a fixed overhead.  Inside
+// a range the rows are listed by length class, longest first -- class
+// min(8, floor(4 len / mean len)) -- and in row order within a class, so rows
+// of equal length keep their order (neighbouring query blocks run together
+// and share K/V blocks in the XCD's L2) while long rows do not start last.
+// Class k = min(8, floor(len / w)) with w = max(mean len / 2, 1/32 of the work
+// per concurrently running workgroup (`slots` of them)): where every row is
+// short against that share (many rows per workgroup) there is one class and
+// the rows keep their order.  One workgroup.
 __global__ __launch_bounds__(kSchedThreads) void k_sched(const int32_t* __restrict__ row_ptr,
                                                          int32_t* __restrict__ sched, int64_t R,
-                                                         int nb, int extra, int cnt_flag) {
+                                                         int nb, int extra, int slots,
+                                                         int cnt_flag) {
     __shared__ long long wsum[kSchedThreads / 64];
     __shared__ long long s_total, s_carry;
+    __shared__ int s_bound[9];
+    __shared__ int s_cnt[8][kSchedCls];          // rows per (range, class)
+    __shared__ int s_off[8][kSchedCls];          // list position of a class's first row, less
+                                                 // that class's rows in earlier ranges
+    __shared__ int s_wcnt[kSchedThreads / 64][kSchedCls];
+    __shared__ int s_seen[kSchedCls];            // rows per class in earlier chunks
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-    // a row's tiles as the attention kernel counts them (length clamped to [0, nb])
-    auto cost = [&](int64_t r) -> long long {
+    auto len = [&](int64_t r) -> int {
         const int n = row_ptr[r + 1] - row_ptr[r];
-        return (long long)(n < 0 ? 0 : (n > nb ? nb : n)) + extra;
+        return n < 0 ? 0 : (n > nb ? nb : n);
     };
+    auto cost = [&](int64_t r) -> long long { return (long long)len(r) + extra; };
     // total work
     long long part = 0;
     for (int64_t r = tid; r < R; r += kSchedThreads) part += cost(r);
     for (int off = 32; off > 0; off >>= 1) part += __shfl_xor(part, off, 64);
     if (lane == 0) wsum[wid] = part;
-    if (tid < 8) { sched[tid] = (int32_t)R; sched[8 + tid] = (int32_t)R; sched[16 + tid] = 0; }
+    if (tid < 8) { sched[16 + tid] = 0; }
+    if (tid < 9) s_bound[tid] = (int)R;
+    if (tid < 8 * kSchedCls) s_cnt[tid / kSchedCls][tid % kSchedCls] = 0;
+    if (tid < kSchedCls) s_seen[tid] = 0;
     if (tid == 0) { sched[24] = cnt_flag; sched[25] = 0; }
     __syncthreads();
     if (tid == 0) {
@@ -727,7 +756,7 @@ __global__ __launch_bounds__(kSchedThreads) void k_sched(const int32_t* __restri
         for (int k = 0; k < kSchedThreads / 64; ++k) t += wsum[k];
         s_total = t;
         s_carry = 0;
-        sched[0] = 0;
+        s_bound[0] = 0;
     }
     __syncthreads();
     const long long total = s_total;
@@ -756,7 +785,7 @@ __global__ __launch_bounds__(kSchedThreads) void k_sched(const int32_t* __restri
             if (my + k < R) {
                 for (int x = 1; x < 8; ++x) {
                     const long long tgt = (long long)x * total;      // 8 * (x/8 of the total)
-                    if (run * 8 <= tgt && tgt < (run + c[k]) * 8) sched[x] = (int32_t)(my + k);
+                    if (run * 8 <= tgt && tgt < (run + c[k]) * 8) s_bound[x] = (int)(my + k);
                 }
             }
             run += c[k];
@@ -765,8 +794,63 @@ __global__ __launch_bounds__(kSchedThreads) void k_sched(const int32_t* __restri
         if (tid == kSchedThreads - 1) s_carry = run;
         __syncthreads();
     }
+    // a boundary no row interval contains (costs of 0 cannot occur: extra >= 1)
+    // stays at R; boundaries are non-decreasing
+    if (tid < 8) {
+        sched[tid] = s_bound[tid];
+        sched[8 + tid] = s_bound[tid + 1];
+    }
+    // len / w = len min(2 R, 32 slots) / (sum of the lengths)
+    const long long sumlen = total - (long long)R * extra;
+    const long long per = 2 * R < 32LL * slots ? 2 * R : 32LL * slots;
+    auto cls = [&](int64_t r) -> int {
+        if (sumlen <= 0) return 0;
+        const long long k = (long long)len(r) * per / sumlen;
+        return k < kSchedCls - 1 ? (int)k : kSchedCls - 1;
+    };
+    auto range_of = [&](int64_t r) -> int {
+        int x = 0;
+        for (int y = 1; y < 8; ++y) x += r >= s_bound[y] ? 1 : 0;
+        return x;
+    };
+    for (int64_t r = tid; r < R; r += kSchedThreads) atomicAdd(&s_cnt[range_of(r)][cls(r)], 1);
     __syncthreads();
-    if (tid < 8) sched[8 + tid] = tid < 7 ? sched[tid + 1] : (int32_t)R;
+    if (tid < 8 * kSchedCls) {
+        const int x = tid / kSchedCls, k = tid % kSchedCls;
+        int o = s_bound[x];
+        for (int q = k + 1; q < kSchedCls; ++q) o += s_cnt[x][q];
+        for (int y = 0; y < x; ++y) o -= s_cnt[y][k];
+        s_off[x][k] = o;
+    }
+    __syncthreads();
+    // stable scatter, 1024 rows a round: a row's place among the rows of its
+    // class before it = ballot rank in its wave + earlier waves + earlier rounds
+    int32_t* list = sched + kSchedHead;
+    const unsigned long long below = (1ull << lane) - 1ull;
+    for (int64_t c0 = 0; c0 < R; c0 += kSchedThreads) {
+        const int64_t r = c0 + tid;
+        const int k = r < R ? cls(r) : -1;
+        int rank = 0;
+#pragma unroll
+        for (int q = 0; q < kSchedCls; ++q) {
+            const unsigned long long m = __ballot(k == q);
+            if (k == q) rank = __popcll(m & below);
+            if (lane == 0) s_wcnt[wid][q] = __popcll(m);
+        }
+        __syncthreads();
+        if (k >= 0) {
+            int before = s_seen[k] + rank;
+            for (int w = 0; w < wid; ++w) before += s_wcnt[w][k];
+            list[s_off[range_of(r)][k] + before] = (int32_t)r;
+        }
+        __syncthreads();
+        if (tid < kSchedCls) {
+            int t = 0;
+            for (int w = 0; w < kSchedThreads / 64; ++w) t += s_wcnt[w][tid];
+            s_seen[tid] += t;
+        }
+        __syncthreads();
+    }
 }
 
 // V blocks transposed to [D][BLK] (keys past the end of the sequence are 0).
@@ -893,7 +977,7 @@ WsLayout ws_layout(const Geometry& g, bool comp) {
     // V in block layout first: a selection with the error rule can write it
     // there (the caller passes the workspace start)
     L.vt = off; off = align_up(off + (size_t)g.BH() * g.nb * g.d * g.block * 2, 256);
-    L.sched = off; off = align_up(off + 32 * sizeof(int32_t), 256);
+    L.sched = off; off = align_up(off + (kSchedHead + (size_t)g.rows()) * sizeof(int32_t), 256);
     L.cnt = off; off = align_up(off + (size_t)g.BH() * g.nb * sizeof(int16_t), 256);
     if (g.order) {   // K in block order, [BH][N][D]
         L.kord = off; off = align_up(off + (size_t)g.BH() * g.N * g.d * 2, 256);
@@ -938,7 +1022,8 @@ sa_status prepare_t(const FwdArgs& a, const Geometry& g, const uint16_t* V, uint
     }
     if (a.rows == 0) return SA_OK;
     hipLaunchKernelGGL(k_sched, dim3(1), dim3(kSchedThreads), 0, stream, a.row_ptr, a.sched,
-                       a.rows, g.nb, (COMP ? a.ntc : 0) + 2, kv_count != nullptr ? 1 : 0);
+                       a.rows, g.nb, (COMP ? a.ntc : 0) + 2, kSchedSlots * (128 / BLK),
+                       kv_count != nullptr ? 1 : 0);
     return hip_check(hipGetLastError(), "k_sched launch");
 }
 
